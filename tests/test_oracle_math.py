@@ -1,0 +1,367 @@
+"""Pins for the verification oracle: values, laws and special cases fixed by the pages and
+by mathematics, independent of the oracle's own formulas.
+
+Sources: "Speculative decoding: accelerate LLM generation without changing its answers"
+(sections 2, 3, 5 and its variations, 6) and "Walk through KV-cache updates when
+speculative decoding rejects some draft tokens" (paragraph 1).
+"""
+
+import itertools
+import json
+import math
+import os
+import random
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from oracle.verify import (accept, inverse_cdf, inverse_cdf_np, residual_weights, transform,
+                           verify_probs, bf16_bits_to_f64)
+
+
+def _grid(n):
+    """Midpoints of n equal cells of [0, 1): exact when every breakpoint is a multiple of 1/n."""
+    return [F(2 * i + 1, 2 * n) for i in range(n)]
+
+
+def _accept_measure(P, Q, n):
+    """Lebesgue measure of {u in [0,1): oracle accepts}, evaluated on an exact grid."""
+    return F(sum(1 for u in _grid(n) if accept(P, Q, u)), n)
+
+
+# ---------------------------------------------------------------------------------------
+# Section 5 toy lab: printed values.
+# ---------------------------------------------------------------------------------------
+
+def test_toy_lab_printed_values(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "toy_lab.json")))
+    p = [F(x) for x in g["p"]]
+    q = [F(x) for x in g["q"]]
+    # ratios p/q are 5/2, 3/5, 2/3: every breakpoint is a multiple of 1/15
+    accepted = [q[x] * _accept_measure(p[x], q[x], 15) for x in range(3)]
+    assert accepted == [F(x) for x in g["accepted_mass"]]
+    resid = residual_weights(p, q)
+    assert resid == [F(x) for x in g["residual"]]
+    reject_prob = sum(resid)
+    assert reject_prob == F(g["reject_probability"])
+    assert [r / reject_prob for r in resid] == [F(x) for x in g["corrected"]]
+    assert [a + r for a, r in zip(accepted, resid)] == [F(x) for x in g["reconstructed"]]
+
+
+def test_toy_lab_fp64_decimals():
+    # The page's script runs in Python floats; the printed values reproduce in fp64.
+    p, q = np.array([0.50, 0.30, 0.20]), np.array([0.20, 0.50, 0.30])
+    r = residual_weights(p, q)
+    assert r.tolist() == [0.5 - 0.2, 0.0, 0.0] and abs(r.sum() - 0.3) < 1e-16
+    x, W, _ = inverse_cdf_np(r, 0.999)
+    assert x == 0 and abs(W - 0.3) < 1e-16
+
+
+# ---------------------------------------------------------------------------------------
+# Section 3: min(q,p) + max(0,p-q) = p per token, acceptance probability 1 - W.
+# ---------------------------------------------------------------------------------------
+
+def _rand_dist(rng, V, den):
+    cuts = sorted(rng.randint(0, den) for _ in range(V - 1))
+    parts = [b - a for a, b in zip([0] + cuts, cuts + [den])]
+    return [F(x, den) for x in parts]
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_accepted_plus_residual_is_target(seed):
+    rng = random.Random(seed)
+    V = rng.randint(2, 7)
+    p, q = _rand_dist(rng, V, 6), _rand_dist(rng, V, 6)
+    n = 60  # ratios i/j with i, j <= 6 are multiples of 1/60
+    accepted = [q[x] * _accept_measure(p[x], q[x], n) if q[x] else F(0) for x in range(V)]
+    resid = residual_weights(p, q)
+    assert [a + r for a, r in zip(accepted, resid)] == p
+    # probability of accepting a proposal drawn from q equals 1 - residual mass
+    assert sum(accepted) == 1 - sum(resid)
+
+
+# ---------------------------------------------------------------------------------------
+# Section 5 variations.
+# ---------------------------------------------------------------------------------------
+
+def test_variation_q_equals_p_always_accepts_and_bonus_from_p():
+    p = [F(1, 2), F(1, 4), F(1, 8), F(1, 8)]
+    for u in [F(0), F(1, 3), F(1) - F(1, 2 ** 24)]:
+        for y in range(4):
+            assert accept(p[y], p[y], u)
+    assert sum(residual_weights(p, p)) == 0
+    # k = 2, q = p: bonus is always drawn, from p_{k+1}
+    counts = {}
+    for u in _grid(8):
+        r = verify_probs([p, p, p], [p, p], [0, 1], [F(9, 10), F(9, 10)], u)
+        assert r.a == 2 and r.mode == "bonus"
+        counts[r.emitted[-1]] = counts.get(r.emitted[-1], 0) + 1
+    assert {x: F(c, 8) for x, c in counts.items()} == {x: p[x] for x in range(4)}
+
+
+def test_variation_zero_draft_mass_is_carried_by_residual():
+    p = [F(1, 2), F(1, 2), F(0)]
+    q = [F(0), F(1, 2), F(1, 2)]
+    r = residual_weights(p, q)
+    assert r == [F(1, 2), F(0), F(0)]
+    # token 0 has q = 0 so it is never proposed; rejection of token 2 (p = 0) always
+    # happens and the replacement is token 0 for every u
+    for u in _grid(10):
+        res = verify_probs([p, p], [q], [2], [u], u)
+        assert res.a == 0 and res.emitted == [0]
+    # the accept rule never divides by q: a q = 0 proposal with p > 0 is accepted
+    assert accept(F(1, 2), F(0), F(1, 2))
+
+
+# ---------------------------------------------------------------------------------------
+# Exact joint law: speculative output over all draws equals autoregressive sampling from p.
+# ---------------------------------------------------------------------------------------
+
+def _exact_law_case(seed):
+    rng = random.Random(seed)
+    V, den = 4, 4
+    p1 = _rand_dist(rng, V, den)
+    p2 = {x1: _rand_dist(rng, V, den) for x1 in range(V)}
+    p3 = {(x1, x2): _rand_dist(rng, V, den) for x1 in range(V) for x2 in range(V)}
+    q1 = _rand_dist(rng, V, den)
+    q2 = {y1: _rand_dist(rng, V, den) for y1 in range(V)}
+    grid = _grid(12)  # all breakpoints are i/j with i, j <= 4 (or multiples of 1/4)
+    w = F(1, 12)
+    law = {}
+    for y1 in range(V):
+        if q1[y1] == 0:
+            continue
+        for y2 in range(V):
+            if q2[y1][y2] == 0:
+                continue
+            P_rows = [p1, p2[y1], p3[(y1, y2)]]
+            Q_rows = [q1, q2[y1]]
+            base = q1[y1] * q2[y1][y2] * w * w * w
+            for u1 in grid:
+                for u2 in grid:
+                    for us in grid:
+                        r = verify_probs(P_rows, Q_rows, [y1, y2], [u1, u2], us)
+                        seq = r.emitted
+                        assert len(seq) == r.a + 1
+                        # complete to length 3 by exact autoregressive sampling from p
+                        if len(seq) == 1:
+                            for x2 in range(V):
+                                for x3 in range(V):
+                                    key = (seq[0], x2, x3)
+                                    law[key] = law.get(key, 0) + base * p2[seq[0]][x2] * p3[(seq[0], x2)][x3]
+                        elif len(seq) == 2:
+                            for x3 in range(V):
+                                key = (seq[0], seq[1], x3)
+                                law[key] = law.get(key, 0) + base * p3[(seq[0], seq[1])][x3]
+                        else:
+                            key = tuple(seq)
+                            law[key] = law.get(key, 0) + base
+    target = {}
+    for x1, x2, x3 in itertools.product(range(V), repeat=3):
+        pr = p1[x1] * p2[x1][x2] * p3[(x1, x2)][x3]
+        if pr:
+            target[(x1, x2, x3)] = pr
+    law = {k: v for k, v in law.items() if v}
+    return law, target
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_exact_joint_law_V4_k2(seed):
+    law, target = _exact_law_case(seed)
+    assert sum(law.values()) == 1
+    assert law == target
+
+
+# ---------------------------------------------------------------------------------------
+# Inverse CDF: the set of u mapping to x has measure w(x)/W; NumPy form agrees with loop.
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(10))
+def test_inverse_cdf_interval_lengths(seed):
+    rng = random.Random(seed)
+    V = rng.randint(1, 9)
+    w = _rand_dist(rng, V, 8)
+    scale = F(rng.choice([1, 2, 4]), 4)   # W in {1/4, 1/2, 1}: breakpoints stay on 1/8 grid
+    w = [x * scale for x in w]
+    counts = [0] * V
+    for u in _grid(8):
+        x, W, margin = inverse_cdf(w, u)
+        assert W == sum(w) and w[x] > 0 and margin > 0
+        counts[x] += 1
+    assert [F(c, 8) for c in counts] == [x / sum(w) for x in w]
+
+
+def test_inverse_cdf_ascending_order_and_boundaries():
+    w = [F(1, 4), F(0), F(1, 4), F(1, 2)]
+    assert inverse_cdf(w, F(0))[0] == 0
+    assert inverse_cdf(w, F(1, 4))[0] == 2       # C(0) = 1/4 is not > t = 1/4
+    assert inverse_cdf(w, F(1, 2))[0] == 3
+    assert inverse_cdf([F(0)] * 3, F(1, 2))[0] is None
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_inverse_cdf_numpy_matches_loop(seed):
+    rng = np.random.default_rng(seed)
+    w = np.maximum(rng.standard_normal(500), 0.0)
+    for u in rng.random(50):
+        a = inverse_cdf(list(w), float(u))
+        b = inverse_cdf_np(w, float(u))
+        assert a[0] == b[0] and a[1] == b[1] and a[2] == b[2]
+
+
+# ---------------------------------------------------------------------------------------
+# Transform: textbook softmax, logistic closed form, top-k by brute force, bf16 decode.
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1.0, 0.7, 2.5])
+def test_transform_is_softmax(T):
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal(1000) * 3
+    t = transform(z, T, 0)
+    ref = scipy.special.softmax(z / T)
+    assert np.max(np.abs(t.p - ref) / ref) < 1e-13
+    assert t.m == z.max() and t.nkept == 1000 and t.thr == -math.inf
+
+
+def test_transform_two_tokens_logistic():
+    for z0, z1, T in [(0.3, -1.2, 1.0), (5.0, 4.0, 0.5), (-2.0, 3.0, 3.0)]:
+        t = transform(np.array([z0, z1]), T, 0)
+        assert abs(t.p[0] - 1.0 / (1.0 + math.exp((z1 - z0) / T))) < 1e-15
+
+
+def test_transform_topk_brute_force_with_ties():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        V = int(rng.integers(2, 16))
+        z = rng.integers(-3, 4, size=V).astype(np.float64)   # many planted ties
+        k = int(rng.integers(1, V + 1))
+        t = transform(z, 0.9, k)
+        # kept iff fewer than k tokens are strictly larger (ties at the threshold kept)
+        kept = np.array([np.sum(z > z[x]) < k for x in range(V)])
+        assert np.array_equal(t.p > 0, kept)
+        assert t.nkept == kept.sum() >= min(k, V)
+        ref = scipy.special.softmax(np.where(kept, z / 0.9, -np.inf))
+        assert np.allclose(t.p, ref, rtol=1e-13, atol=0)
+
+
+def test_transform_topk_is_temperature_invariant_selection():
+    rng = np.random.default_rng(5)
+    z = np.round(rng.standard_normal(300) * 4) / 4
+    s = [(transform(z, T, 10).p > 0) for T in (0.1, 1.0, 7.0)]
+    assert np.array_equal(s[0], s[1]) and np.array_equal(s[1], s[2])
+
+
+def test_transform_rejects_nonfinite_and_handles_neg_inf():
+    assert not transform(np.array([0.0, np.nan]), 1.0, 0).valid
+    assert not transform(np.array([0.0, np.inf]), 1.0, 0).valid
+    assert not transform(np.array([-np.inf, -np.inf]), 1.0, 0).valid
+    t = transform(np.array([0.0, -np.inf, 0.0]), 1.0, 0)
+    assert t.valid and t.p.tolist() == [0.5, 0.0, 0.5] and t.nkept == 2
+    # fewer finite entries than k: all finite entries kept
+    t = transform(np.array([1.0, -np.inf, -np.inf, 0.0]), 1.0, 3)
+    assert t.valid and t.nkept == 2 and t.thr == -np.inf
+
+
+def test_bf16_decode_matches_torch():
+    import torch
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = bf16_bits_to_f64(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_transform_underflow_small_temperature():
+    # T near 0: fp64 stable softmax keeps the max token at p = 1 without overflow
+    z = np.array([10.0, 9.0, -5.0])
+    t = transform(z, 1e-3, 0)
+    assert t.p[0] == 1.0 and t.p[1] == 0.0 and np.isfinite(t.S)
+
+
+# ---------------------------------------------------------------------------------------
+# Worked flows and forced rejection positions.
+# ---------------------------------------------------------------------------------------
+
+def _forced(k, reject_at):
+    """Rows that force acceptance of positions < reject_at (u = 0, P > 0) and rejection at
+    reject_at (P = 0 < Q); reject_at = k means all accepted."""
+    V = 6
+    P_rows, Q_rows, toks, us = [], [], [], []
+    for i in range(k):
+        y = i % 3
+        q = [F(1, V)] * V
+        if i == reject_at:
+            p = [F(0)] * V
+            p[5] = F(1)          # p(y) = 0 -> always rejected; residual is all on token 5
+        else:
+            p = [F(1, V)] * V
+        P_rows.append(p)
+        Q_rows.append(q)
+        toks.append(y)
+        us.append(F(0) if i < reject_at else F(1, 2))
+    P_rows.append([F(0)] * 4 + [F(1), F(0)])   # bonus row: token 4
+    return P_rows, Q_rows, toks, us
+
+
+def test_worked_flows(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "worked_flows.json")))
+    for f in g["flows"]:
+        k, j = f["k"], f["rejected_position"] - 1
+        P_rows, Q_rows, toks, us = _forced(k, j)
+        r = verify_probs(P_rows, Q_rows, toks, us, F(1, 3))
+        assert r.a == f["expect_num_accepted"]
+        assert len(r.emitted) == f["expect_num_emitted"]
+        assert r.emitted[:r.a] == toks[:r.a] and r.emitted[-1] == 5
+        discarded = [i + 1 for i in range(r.a + 1, k)]
+        assert discarded == f["expect_discarded_positions"]
+
+
+@pytest.mark.parametrize("k", [1, 2, 5, 8])
+def test_forced_rejection_first_middle_last_and_bonus(k):
+    for j in sorted({0, k // 2, k - 1, k}):
+        P_rows, Q_rows, toks, us = _forced(k, j)
+        r = verify_probs(P_rows, Q_rows, toks, us, F(1, 3))
+        assert r.a == j
+        assert r.emitted == toks[:j] + [5 if j < k else 4]
+        assert r.mode == ("resid" if j < k else "bonus")
+
+
+def test_k_zero_is_plain_sampling_from_p():
+    p = [F(1, 4), F(3, 4)]
+    r = verify_probs([p], [], [], [], F(1, 2))
+    assert r.a == 0 and r.emitted == [1] and r.mode == "bonus"
+
+
+# ---------------------------------------------------------------------------------------
+# Batch wrapper: error bits and ragged layout.
+# ---------------------------------------------------------------------------------------
+
+def test_batch_errors_and_layout():
+    V = 8
+    rng = np.random.default_rng(0)
+    cu = np.array([0, 2, 2, 5, 9], dtype=np.int32)     # k = 2, 0, 3, 4
+    K, B = int(cu[-1]), 4
+    tgt = rng.standard_normal((K + B, V)).astype(np.float32)
+    dft = rng.standard_normal((K, V)).astype(np.float32)
+    toks = rng.integers(0, V, size=K).astype(np.int32)
+    ua = rng.random(K, dtype=np.float32)
+    us = rng.random(B, dtype=np.float32)
+    toks[3] = V                 # request 2 token out of range
+    tgt[9 + 3, 0] = np.nan      # request 3 (rows 9..13 for target -> row cu[3]+3+.. = 8..12)
+    r = oracle.verify_batch(tgt, dft, toks, cu, ua, us, 1.0, 0, 4, "f32")
+    assert r.err[2] & oracle.ERR_TOKEN and r.num_accepted[2] == -1 and r.num_emitted[2] == 0
+    assert r.err[3] & oracle.ERR_NONFINITE and r.num_accepted[3] == -1
+    for b in (0, 1):
+        assert r.num_accepted[b] >= 0 and r.num_emitted[b] == r.num_accepted[b] + 1
+        lo = cu[b] + b
+        assert list(r.out_tokens[lo:lo + r.num_accepted[b]]) == list(toks[cu[b]:cu[b] + r.num_accepted[b]])
+    assert r.num_accepted[1] == 0 and r.num_emitted[1] == 1   # k = 0: one bonus token
+    bad = oracle.verify_batch(tgt, dft, toks, cu, ua, us, 1.0, 0, 3, "f32")
+    assert bad.err[3] == oracle.ERR_K
+    ua2 = ua.copy()
+    ua2[0] = 1.0
+    r2 = oracle.verify_batch(tgt, dft, toks, cu, ua2, us, 1.0, 0, 4, "f32")
+    assert r2.err[0] & oracle.ERR_UNIFORM
