@@ -1,0 +1,213 @@
+"""Benchmark: one speculative cycle (paged append -> verify -> rollback) per step.
+
+Default workload: B=256 requests, k=5 proposals, V=128256, bf16 logits (target N(0,3),
+draft = target + N(0,1.5)), T=0.7, paged KV of 32 layers x 8 KV heads x 128 bf16 with
+16-slot blocks and prefix lengths U[512,4096]. Inputs are synthetic, seeded and resident
+in HBM before timing. Steps run back to back on one stream; the cache grows by 1 + a_b
+per request per step, as in steady-state decoding.
+
+Prints one JSON line with the throughput (verified draft positions per second), the
+achieved HBM bandwidth of the whole cycle and, under "roofline", of the row-statistics
+kernel (timed with HIP events recorded around it inside the timed steps), plus a CPU
+baseline: the fp64 oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "verified draft positions/sec + achieved HBM GB/s (% peak), B=256 k=5 V=128256 bf16"
+PEAK_GBPS = 8000.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "row_stats_c2_traffic.json")
+STATS_SRC = os.path.join(ROOT, "rejection_sampling_verify_specdec_amd", "csrc", "verify.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c2")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-requests", type=int, default=96,
+                   help="requests of the workload the oracle runs for the CPU baseline")
+    return p.parse_args()
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(STATS_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_bytes_alg: float):
+    """HBM bytes per launch of the row-statistics kernel from committed rocprofv3 counter
+    summaries, if they were taken on the current kernel source."""
+    try:
+        d = json.load(open(PROFILE_TRAFFIC))
+    except Exception:
+        return None
+    if d.get("source_sha256_16") != source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(vin, kv, nreq: int):
+    """The oracle as it stands on nreq requests of the same cycle, one core."""
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(1)
+    except Exception:
+        limiter = None
+    import oracle
+    rng = np.random.default_rng(1234)
+    reqs = sorted(rng.choice(vin.B, size=min(nreq, vin.B), replace=False).tolist())
+    t0 = time.perf_counter()
+    res = oracle.verify_batch(vin.target, vin.draft, vin.draft_tokens, vin.cu_draft,
+                              vin.u_accept, vin.u_sample, vin.T, vin.top_k, vin.max_k,
+                              vin.dtype, requests=reqs, keep_probs=False)
+    t_verify = time.perf_counter() - t0
+    o = oracle.PagedKV(kv.L, kv.H, kv.D, kv.block_size, kv.num_blocks, kv.block_tables,
+                       kv.seq_lens, kv.refcount, kv.free_list, kv.free_count, kv.blocks)
+    acc = np.where(res.num_accepted >= 0, res.num_accepted, 0)
+    t0 = time.perf_counter()
+    o.append(kv.k_new, kv.v_new, kv.cu_new)
+    o.rollback(acc, vin.cu_draft)
+    t_kv = time.perf_counter() - t0
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    k_sample = int(sum(vin.k_b[b] for b in reqs))
+    # KV bookkeeping ran for the whole batch: charge the sample its share
+    t = t_verify + t_kv * (k_sample / max(vin.K, 1))
+    return {"value": k_sample / t, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{len(reqs)} of {vin.B} requests ({k_sample} positions) verified by "
+                       f"the fp64 oracle in {t_verify:.2f} s; paged append+rollback of the "
+                       f"whole batch {t_kv:.2f} s, charged pro rata")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the verification path shards by request with no "
+              "cross-GPU exchange, and runs on more than one GPU are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from rejection_sampling_verify_specdec_amd import binding, synth
+
+    if not os.path.exists(binding.LIB_PATH):
+        from rejection_sampling_verify_specdec_amd import build as _b
+        _b.build()
+    binding.load_library()
+    d = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    vin = synth.make_verify(wl, seed=args.seed)
+    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + args.steps + 2)
+    print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
+          f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(d)
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(d)
+
+    logits = bf if vin.dtype == "bf16" else (lambda x: t(x.astype(np.float32)))
+    tgt, dft = logits(vin.target), logits(vin.draft)
+    tokens, cu = t(vin.draft_tokens), t(vin.cu_draft)
+    u_acc, u_smp = t(vin.u_accept), t(vin.u_sample)
+    pool = torch.empty((kv.L, 2, kv.num_blocks, kv.block_size, kv.H, kv.D), dtype=torch.bfloat16, device=d)
+    if kv.blocks:
+        ids = sorted(kv.blocks)
+        pool[:, :, torch.tensor(ids, device=d)] = bf(np.stack([kv.blocks[X][0] for X in ids], axis=2))
+    cache = binding.PagedKVCache(pool, t(kv.block_tables), t(kv.seq_lens), t(kv.refcount),
+                                 t(kv.free_list), torch.tensor([kv.free_count], dtype=torch.int32, device=d),
+                                 torch.zeros(1, dtype=torch.int32, device=d))
+    k_new, v_new, cu_new = bf(kv.k_new), bf(kv.v_new), t(kv.cu_new)
+    B, K, V = vin.B, vin.K, vin.V
+    out = torch.empty(K + B, dtype=torch.int32, device=d)
+    nacc = torch.empty(B, dtype=torch.int32, device=d)
+    nemit = torch.empty(B, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+    ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
+    kws = torch.empty(binding.kv_paged_append_workspace_size(B), dtype=torch.uint8, device=d)
+    n = args.warmup + args.steps
+    evs = [(binding.HipEvent(), binding.HipEvent()) for _ in range(n)]
+
+    def step(i):
+        dbg = binding.SpecdecDebug()
+        dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
+        binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
+        binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
+                               temperature=vin.T, top_k=vin.top_k, out_tokens=out,
+                               num_accepted=nacc, num_emitted=nemit, err_word=err,
+                               workspace=ws, debug=dbg)
+        binding.kv_rollback(cache, nacc, cu)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st = int(cache.state.item())
+    if st:
+        print(f"# warning: cache state word {st:#x}", file=sys.stderr)
+    if int(err.item()) & (binding.ERR_TOKEN | binding.ERR_K | binding.ERR_NONFINITE | binding.ERR_UNIFORM):
+        print(f"# warning: verify error word {int(err.item()):#x}", file=sys.stderr)
+    stats_ms = [evs[i][0].elapsed_ms(evs[i][1]) for i in range(args.warmup, n)]
+    stats_avg_s = float(np.mean(stats_ms)) / 1e3
+    ms_per_step = elapsed / args.steps * 1e3
+    es = 2 if vin.dtype == "bf16" else 4
+    rows = 2 * K + B
+    logit_bytes = rows * V * es
+    kv_bytes = 2 * (K + B) * kv.L * 2 * kv.H * kv.D * 2      # read + write, K and V
+    small = 4 * (3 * K + 6 * B + 2)                         # tokens, uniforms, offsets, outputs
+    cycle_bytes = logit_bytes + kv_bytes + small
+    positions_per_s = K * args.steps / elapsed
+    cycle_gbps = cycle_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = logit_bytes / stats_avg_s / 1e9
+    res = {
+        "metric": METRIC,
+        "value": positions_per_s,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": vin.dtype,
+        "data": "synthetic",
+        "config": {"workload": (f"{wl.name}: B={B} k={'U{%d..%d}' % wl.k_range if wl.k_range else wl.k} "
+                                f"V={V} {vin.dtype} T={vin.T:g} top_k={vin.top_k}; paged KV "
+                                f"{kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
+                   "global_batch": B, "positions_per_step": K, "parallelism": "single GPU"},
+        "achieved_hbm_gbps": cycle_gbps,
+        "pct_peak_hbm": 100.0 * cycle_gbps / PEAK_GBPS,
+        "cycle_bytes": cycle_bytes,
+        "roofline": {"bound": "hbm", "kernel": "k_row_stats", "achieved": achieved,
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": achieved / PEAK_GBPS,
+                     "traffic": traffic_from_profile(logit_bytes),
+                     "algorithmic_bytes": logit_bytes,
+                     "avg_launch_us": stats_avg_s * 1e6},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_requests)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

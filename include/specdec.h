@@ -1,0 +1,227 @@
+/*
+ * specdec.h - batched speculative-decoding verification and paged KV append / rollback
+ * on AMD Instinct MI355X (gfx950). C ABI, plain pointers and sizes.
+ *
+ * One speculative cycle, as the pages describe it, is three stream-ordered calls:
+ *
+ *   kv_paged_append  - provisional append of the K/V the target pass produced for the
+ *                      pending token and the k_b proposals of every request
+ *                      ("Walk through KV-cache updates when speculative decoding rejects
+ *                      some draft tokens", both paragraphs: K/V are appended as part of
+ *                      the verifying forward pass, before the accept test);
+ *   specdec_verify   - left-to-right modified rejection sampling with replacement /
+ *                      bonus sampling ("Speculative decoding: accelerate LLM generation
+ *                      without changing its answers", section 2 "Draft, verify, correct");
+ *   kv_rollback      - truncate every request back to its committed prefix, freeing the
+ *                      blocks past it ("Walk through KV-cache updates ...", paragraph 1;
+ *                      "Keep cache validity aligned with the committed token history",
+ *                      paragraphs 1-4).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named device are device memory owned by the caller; the library never
+ *     allocates, never frees, never synchronizes the stream and keeps no global mutable
+ *     state. All work is enqueued on `stream`; outputs are valid once the stream reaches
+ *     that point.
+ *   - Arguments the host can see are checked before anything is enqueued; on failure the
+ *     call returns SPECDEC_EINVAL and no device memory is touched.
+ *   - Problems only the device can see (bad token ids, non-finite logits, too few free
+ *     blocks, ...) set sticky bits in a caller-owned device word (OR-ed, never cleared by
+ *     the library) and are handled per request as documented below.
+ *   - No random numbers are drawn inside: every random decision uses the caller's
+ *     uniforms, so results are a deterministic function of the inputs.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------------------ */
+#define SPECDEC_OK          0
+#define SPECDEC_EINVAL     (-1)   /* a host-visible argument is invalid; nothing enqueued */
+#define SPECDEC_EHIP       (-3)   /* a HIP launch / runtime call failed                    */
+#define SPECDEC_EWORKSPACE (-4)   /* workspace missing, misaligned or too small            */
+
+/* ---- logits element type ----------------------------------------------------------- */
+#define SPECDEC_F32  0
+#define SPECDEC_BF16 1
+
+/* ---- device-side bits of specdec_verify's err_word and req_flags --------------------- */
+#define SPECDEC_ERR_TOKEN      1   /* a draft token id outside [0, V)                      */
+#define SPECDEC_ERR_K          2   /* cu_draft inconsistent: k_b<0, k_b>max_k, cu[0]!=0,
+                                      cu[B]!=K                                            */
+#define SPECDEC_ERR_NONFINITE  4   /* NaN / +inf logit in one of the request's rows, or a
+                                      row with no finite kept logit                       */
+#define SPECDEC_ERR_QZERO      8   /* flag only: q_i(y_i) == 0 at an evaluated position    */
+#define SPECDEC_ERR_ZFALLBACK 16   /* flag only: residual mass was 0 after a rejection;
+                                      the replacement was drawn from p_i                   */
+#define SPECDEC_ERR_UNIFORM   32   /* a uniform outside [0, 1) (or NaN)                   */
+
+/* ---- device-side bits of kv_paged_cache.state --------------------------------------- */
+#define KV_ERR_NOMEM       64        /* append needed more blocks than free: not applied   */
+#define KV_ERR_APPEND     128        /* append argument invalid on device: not applied     */
+#define KV_ERR_ROLLBACK   256        /* rollback request invalid (skipped) or corrupt meta */
+#define KV_APPEND_REJECTED (1 << 16) /* not sticky: the latest append was not applied, so
+                                        the next kv_rollback is a no-op                    */
+
+/* Largest proposal count per request, batch size for the KV calls, and vocabulary. */
+#define SPECDEC_MAX_K      64
+#define SPECDEC_MAX_KV_BATCH 4096
+
+/* Short English text for a return code. Never NULL. */
+const char* specdec_status_string(int status);
+
+/* =====================================================================================
+ * Verification
+ * ===================================================================================== */
+
+/* Optional per-call diagnostics; any field may be NULL / 0. Row arrays are indexed with
+ * the target rows first (0 .. K+B-1) and then the draft rows (K+B .. 2K+B-1). */
+typedef struct specdec_debug {
+    double*  p_y;          /* [K]  p_i(y_i) after the transform                           */
+    double*  q_y;          /* [K]  q_i(y_i)                                               */
+    float*   row_max;      /* [2K+B] max kept logit of the row                            */
+    double*  row_sum;      /* [2K+B] S = sum over kept x of exp((z(x) - max) / T)         */
+    float*   row_thr;      /* [2K+B] top-k threshold logit (-inf when top-k is off)       */
+    int32_t* row_nkept;    /* [2K+B] kept tokens with finite logit                        */
+    double*  resid_mass;   /* [B]  W the final token was drawn from: residual mass, or
+                                   sum of p for the bonus                                  */
+    double*  picked_prob;  /* [B]  w(x*) / W                                               */
+    int32_t* req_flags;    /* [B]  SPECDEC_ERR_* bits of the request                       */
+    hipEvent_t ev_stats_begin;  /* recorded on `stream` right before / after the kernel  */
+    hipEvent_t ev_stats_end;    /* that streams the logit rows (for timing)              */
+} specdec_debug;
+
+/* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned). */
+size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
+                                     int32_t top_k);
+
+/*
+ * specdec_verify - one verification step for a batch of B requests.
+ *
+ * For request b with k_b = cu_draft[b+1] - cu_draft[b] proposals y_1..y_k (draft_tokens
+ * [cu_draft[b] .. cu_draft[b+1])):
+ *   p_i = transform(target row i), i = 0..k_b (row k_b is the position after the block),
+ *   q_i = transform(draft row i),  i = 0..k_b-1,
+ * where transform keeps the tokens whose logit is >= the top_k-th largest logit of the row
+ * (ties inclusive; all finite tokens when top_k <= 0 or top_k >= V) and applies a
+ * max-subtracted softmax at temperature T ("Speculative decoding ...", section 6: stable
+ * softmax, identical transform on both sides). Proposal i is accepted iff
+ * u_accept[cu_draft[b]+i] * q_i(y_i) < p_i(y_i), i.e. with probability
+ * min(1, p_i(y_i)/q_i(y_i)) (section 2). The first rejection j ends the run; the
+ * replacement is drawn from normalize(max(0, p_j - q_j)), or, when all k_b are accepted,
+ * the bonus token from p_{k_b}; both by inverse CDF over ascending token ids with
+ * u_sample[b]: the smallest x whose running sum exceeds u * W (section 2; section 3
+ * shows the emitted token then has law p).
+ *
+ * Layout (all device, row-major, packed ragged):
+ *   target_logits [K+B][V] dtype: rows of request b are cu_draft[b] + b + i, i = 0..k_b
+ *   draft_logits  [K][V]   dtype: rows cu_draft[b] + i, i < k_b
+ *   draft_tokens  [K] int32,  cu_draft [B+1] int32 (exclusive prefix of k_b)
+ *   u_accept [K] fp32, u_sample [B] fp32, caller-drawn uniforms in [0, 1)
+ * Outputs (device):
+ *   out_tokens   [K+B] int32: request b writes num_emitted[b] tokens at cu_draft[b] + b
+ *                (the accepted proposals, then the replacement or bonus token); other
+ *                entries are left untouched
+ *   num_accepted [B] int32 (-1 on a request error), num_emitted [B] int32 (0 on error)
+ *   err_word     [1] int32, SPECDEC_ERR_* bits OR-ed in (not cleared)
+ * Host scalars: B >= 1, K = cu_draft[B] (the packed row count the caller allocated),
+ * 0 <= max_k <= SPECDEC_MAX_K, V >= 1, dtype SPECDEC_F32 or SPECDEC_BF16,
+ * temperature > 0 and finite, top_k any value (<= 0 or >= V disables it).
+ * workspace: device, 16-byte aligned, >= specdec_verify_workspace_size(B, K, V, dtype,
+ * top_k) bytes, owned by the caller; its contents need no initialization and are
+ * scratch between calls. Calls that share a workspace must not overlap.
+ * Returns SPECDEC_OK once enqueued, or SPECDEC_EINVAL / SPECDEC_EWORKSPACE /
+ * SPECDEC_EHIP without enqueuing anything that writes outputs.
+ */
+int specdec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                   const int32_t* draft_tokens, const int32_t* cu_draft,
+                   const float* u_accept, const float* u_sample,
+                   int32_t B, int32_t K, int32_t max_k, int32_t V,
+                   float temperature, int32_t top_k,
+                   int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                   int32_t* err_word, const specdec_debug* dbg,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* =====================================================================================
+ * Paged KV cache
+ * ===================================================================================== */
+
+/* Cache metadata and storage, all device memory owned by the caller. Physical block X of
+ * layer l holds block_size slots of K then V: pool[l][0][X] and pool[l][1][X], each slot
+ * num_kv_heads * head_dim bf16 values. Logical block lb of request b is
+ * block_tables[b][lb]; it is valid iff lb < ceil(seq_lens[b] / block_size), and entries
+ * past that are -1. refcount[X] counts the table entries that reference X; a block is on
+ * the free list iff its refcount is 0. The free list is a stack: free_list[0 ..
+ * *free_count) with the top at *free_count - 1 ("Keep cache validity ...", paragraph 3:
+ * block tables, ownership and reference counts decide which physical memory is valid). */
+typedef struct kv_paged_cache {
+    void*    pool;            /* bf16 [L][2][num_blocks][block_size][H][D]             */
+    int32_t  num_layers;      /* L >= 1                                                */
+    int32_t  num_kv_heads;    /* H >= 1                                                */
+    int32_t  head_dim;        /* D >= 1; H*D*2 bytes must be a multiple of 16          */
+    int32_t  block_size;      /* slots per block, >= 1                                 */
+    int32_t  num_blocks;      /* NB >= 1                                               */
+    int32_t  max_blocks_per_req;  /* MBR: columns of block_tables                      */
+    int32_t* block_tables;    /* [B][MBR] int32                                        */
+    int32_t* seq_lens;        /* [B] valid K/V entries; the committed length is one more
+                                 (the last committed token is pending)                  */
+    int32_t* refcount;        /* [NB]                                                  */
+    int32_t* free_list;       /* [NB]                                                  */
+    int32_t* free_count;      /* [1]                                                   */
+    int32_t* state;           /* [1] KV_ERR_* sticky bits and KV_APPEND_REJECTED       */
+} kv_paged_cache;
+
+/* Bytes of device workspace kv_paged_append needs for a batch of B requests. */
+size_t kv_paged_append_workspace_size(int32_t B);
+
+/*
+ * kv_paged_append - provisional append of n_b = cu_new[b+1] - cu_new[b] entries per
+ * request (in a cycle: the pending token and the k_b proposals, n_b = k_b + 1) at slots
+ * seq_lens[b] .. seq_lens[b] + n_b - 1.
+ * k_new, v_new: device bf16 [L][N][H][D] with N = cu_new[B]; entry t of request b is row
+ * cu_new[b] + t. cu_new: device int32 [B+1].
+ * Blocks are popped from the top of the free list in ascending request order, then
+ * ascending logical block. When the receiving partial block is shared (refcount > 1) it
+ * is first copied into a fresh block (copy-on-write, slots below seq_len) and the old
+ * block is released ("Keep cache validity ...", paragraph 4: shared-prefix isolation).
+ * All-or-nothing: if the batch needs more blocks than are free (KV_ERR_NOMEM) or an
+ * argument is invalid on device (KV_ERR_APPEND: n_b < 0, cu_new[0] != 0, cu_new[B] != N,
+ * capacity MBR * block_size exceeded, no block for a partial tail), no request changes
+ * and KV_APPEND_REJECTED is set; a successful append clears KV_APPEND_REJECTED.
+ * Host checks: 1 <= B <= SPECDEC_MAX_KV_BATCH, N >= 0, pointers non-NULL, geometry > 0.
+ * workspace: device, 16-byte aligned, >= kv_paged_append_workspace_size(B) bytes.
+ */
+int kv_paged_append(const kv_paged_cache* cache, int32_t B,
+                    const void* k_new, const void* v_new, const int32_t* cu_new, int32_t N,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kv_rollback - truncate every request to its committed prefix after verification:
+ * drop_b = k_b - num_accepted[b] trailing entries (k_b = cu_draft[b+1] - cu_draft[b]),
+ * so that after a cycle seq_lens[b] = old length + 1 + num_accepted[b] (the pending token
+ * and the accepted proposals stay; the replacement / bonus token becomes the new pending
+ * token: "Keep cache validity ...", paragraphs 1-2). For every logical block from
+ * ceil(new / block_size) to ceil(old / block_size) - 1 the refcount is decremented, the
+ * block is pushed on the free list when it reaches 0 (ascending request, then logical
+ * block order), and the table entry becomes -1. Only metadata changes: slots past the new
+ * length inside a retained block keep their bytes ("rejected speculative tokens remain in
+ * KV", paragraph 2). A request with num_accepted < 0, num_accepted > k_b or drop > seq_len
+ * is skipped and KV_ERR_ROLLBACK set; a table entry out of range or a refcount already 0
+ * sets KV_ERR_ROLLBACK and that entry is only cleared. The call is a no-op when the
+ * latest append was rejected (KV_APPEND_REJECTED). B <= SPECDEC_MAX_KV_BATCH.
+ * num_accepted [B] and cu_draft [B+1]: device int32 (specdec_verify's outputs / inputs).
+ */
+int kv_rollback(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                const int32_t* cu_draft, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECDEC_H */

@@ -236,8 +236,9 @@ def _u_ok(u) -> bool:
 
 
 def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: int,
-                   V: int) -> RequestResult:
-    """Validate and verify one request from logits (float64 rows)."""
+                   V: int, keep_probs: bool = True) -> RequestResult:
+    """Validate and verify one request from logits (float64 rows). With keep_probs=False
+    the normalized rows are dropped from the result once used (large vocabularies)."""
     k = len(tokens)
     err = 0
     if any((int(y) < 0 or int(y) >= V) for y in tokens):
@@ -249,10 +250,16 @@ def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: 
     if not all(r.valid for r in rows_t) or not all(r.valid for r in rows_d):
         err |= ERR_NONFINITE
     if err & ERROR_BITS:
+        res = None
+    else:
+        res = verify_probs([r.p for r in rows_t], [r.p for r in rows_d],
+                           [int(y) for y in tokens],
+                           [float(u) for u in u_accept], float(u_sample))
+    if not keep_probs:
+        for r in rows_t + rows_d:
+            r.p = None
+    if res is None:
         return RequestResult(-1, [], err, None, rows_t, rows_d)
-    res = verify_probs([r.p for r in rows_t], [r.p for r in rows_d],
-                       [int(y) for y in tokens],
-                       [float(u) for u in u_accept], float(u_sample))
     return RequestResult(res.a, res.emitted, err | res.flags, res, rows_t, rows_d)
 
 
@@ -274,7 +281,8 @@ def _decode_rows(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
                  T: float, top_k: int, max_k: int, dtype: str,
-                 requests: Optional[Sequence[int]] = None) -> BatchResult:
+                 requests: Optional[Sequence[int]] = None,
+                 keep_probs: bool = True) -> BatchResult:
     """Batched verification over packed ragged rows.
 
     target: [K+B, V] (fp32 values, or bf16 bit patterns as uint16); the rows of request b
@@ -301,7 +309,7 @@ def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
         t_rows = _decode_rows(target[lo + b: lo + b + k + 1], dtype)
         d_rows = _decode_rows(draft[lo: hi], dtype)
         r = verify_request(t_rows, d_rows, np.asarray(draft_tokens[lo:hi]),
-                           np.asarray(u_accept[lo:hi]), u_sample[b], T, top_k, V)
+                           np.asarray(u_accept[lo:hi]), u_sample[b], T, top_k, V, keep_probs)
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

@@ -1,0 +1,287 @@
+"""Thin ctypes binding of ``libspecdec.so`` (see ``include/specdec.h``).
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape and
+contiguity, and their device pointers plus torch's current HIP stream are passed to the C
+entry points of the same names. Every step of the path runs in the library's kernels.
+The library must have been built (``python -m rejection_sampling_verify_specdec_amd.build``);
+calls fail loudly otherwise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecdec.so")
+
+SPECDEC_OK = 0
+SPECDEC_EINVAL = -1
+SPECDEC_EHIP = -3
+SPECDEC_EWORKSPACE = -4
+SPECDEC_F32 = 0
+SPECDEC_BF16 = 1
+
+ERR_TOKEN = 1
+ERR_K = 2
+ERR_NONFINITE = 4
+ERR_QZERO = 8
+ERR_ZFALLBACK = 16
+ERR_UNIFORM = 32
+KV_ERR_NOMEM = 64
+KV_ERR_APPEND = 128
+KV_ERR_ROLLBACK = 256
+KV_APPEND_REJECTED = 1 << 16
+
+MAX_K = 64
+MAX_KV_BATCH = 4096
+
+EXPORTED = [
+    "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
+    "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback",
+]
+
+
+class SpecdecError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+class SpecdecDebug(ctypes.Structure):
+    _fields_ = [
+        ("p_y", ctypes.c_void_p), ("q_y", ctypes.c_void_p),
+        ("row_max", ctypes.c_void_p), ("row_sum", ctypes.c_void_p),
+        ("row_thr", ctypes.c_void_p), ("row_nkept", ctypes.c_void_p),
+        ("resid_mass", ctypes.c_void_p), ("picked_prob", ctypes.c_void_p),
+        ("req_flags", ctypes.c_void_p),
+        ("ev_stats_begin", ctypes.c_void_p), ("ev_stats_end", ctypes.c_void_p),
+    ]
+
+
+class KvPagedCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("pool", ctypes.c_void_p),
+        ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32), ("max_blocks_per_req", ctypes.c_int32),
+        ("block_tables", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("refcount", ctypes.c_void_p), ("free_list", ctypes.c_void_p),
+        ("free_count", ctypes.c_void_p), ("state", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m rejection_sampling_verify_specdec_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.specdec_status_string.argtypes = [ctypes.c_int]
+    lib.specdec_status_string.restype = ctypes.c_char_p
+    lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.specdec_verify_workspace_size.restype = sz
+    lib.specdec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                   ctypes.c_float, i32, vp, vp, vp, vp,
+                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
+    lib.specdec_verify.restype = ctypes.c_int
+    lib.kv_paged_append_workspace_size.argtypes = [i32]
+    lib.kv_paged_append_workspace_size.restype = sz
+    lib.kv_paged_append.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32,
+                                    vp, sz, vp]
+    lib.kv_paged_append.restype = ctypes.c_int
+    lib.kv_rollback.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
+    lib.kv_rollback.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().specdec_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, numel: Optional[int] = None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, is on {t.device}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+
+
+def _logits_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SPECDEC_BF16
+    if t.dtype == torch.float32:
+        return SPECDEC_F32
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def specdec_verify_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int) -> int:
+    return int(load_library().specdec_verify_workspace_size(B, K, V, dtype, top_k))
+
+
+def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                   draft_tokens: torch.Tensor, cu_draft: torch.Tensor,
+                   u_accept: torch.Tensor, u_sample: torch.Tensor, *, max_k: int,
+                   temperature: float, top_k: int, out_tokens: torch.Tensor,
+                   num_accepted: torch.Tensor, num_emitted: torch.Tensor,
+                   err_word: torch.Tensor, workspace: torch.Tensor,
+                   debug: Optional[SpecdecDebug] = None) -> None:
+    """Enqueue one verification step on torch's current stream (shapes as in the header)."""
+    lib = load_library()
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    dtype = _logits_dtype(target_logits)
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [K+B, V]")
+    B = cu_draft.numel() - 1
+    R, V = target_logits.shape
+    K = R - B
+    _check(target_logits, "target_logits", target_logits.dtype, device=dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, K * V, dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, K, dev)
+    _check(cu_draft, "cu_draft", torch.int32, B + 1, dev)
+    _check(u_accept, "u_accept", torch.float32, K, dev)
+    _check(u_sample, "u_sample", torch.float32, B, dev)
+    _check(out_tokens, "out_tokens", torch.int32, K + B, dev)
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(num_emitted, "num_emitted", torch.int32, B, dev)
+    _check(err_word, "err_word", torch.int32, 1, dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    st = lib.specdec_verify(
+        _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(cu_draft),
+        _ptr(u_accept), _ptr(u_sample), B, K, max_k, V, float(temperature), int(top_k),
+        _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
+        ctypes.byref(debug) if debug is not None else None,
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_verify", st)
+
+
+class PagedKVCache:
+    """Device tensors of one paged cache plus the C struct that points at them."""
+
+    def __init__(self, pool: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                 refcount: torch.Tensor, free_list: torch.Tensor, free_count: torch.Tensor,
+                 state: torch.Tensor):
+        if pool.dtype != torch.bfloat16 or pool.dim() != 6:
+            raise ValueError("pool must be bf16 [L][2][NB][block_size][H][D]")
+        L, two, NB, bs, H, D = pool.shape
+        if two != 2:
+            raise ValueError("pool dim 1 must be 2 (K, V)")
+        dev = pool.device
+        _check(pool, "pool", torch.bfloat16, device=dev)
+        _check(block_tables, "block_tables", torch.int32, device=dev)
+        _check(seq_lens, "seq_lens", torch.int32, device=dev)
+        _check(refcount, "refcount", torch.int32, NB, dev)
+        _check(free_list, "free_list", torch.int32, NB, dev)
+        _check(free_count, "free_count", torch.int32, 1, dev)
+        _check(state, "state", torch.int32, 1, dev)
+        self.pool, self.block_tables, self.seq_lens = pool, block_tables, seq_lens
+        self.refcount, self.free_list, self.free_count, self.state = refcount, free_list, free_count, state
+        self.device = dev
+        self.struct = KvPagedCacheStruct(
+            pool.data_ptr(), L, H, D, bs, NB, block_tables.shape[1],
+            block_tables.data_ptr(), seq_lens.data_ptr(), refcount.data_ptr(),
+            free_list.data_ptr(), free_count.data_ptr(), state.data_ptr())
+
+
+def kv_paged_append_workspace_size(B: int) -> int:
+    return int(load_library().kv_paged_append_workspace_size(B))
+
+
+def kv_paged_append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                    cu_new: torch.Tensor, workspace: torch.Tensor) -> None:
+    """Enqueue the provisional append of k_new / v_new ([L][N][H][D] bf16)."""
+    lib = load_library()
+    dev = cache.device
+    B = cu_new.numel() - 1
+    N = k_new.shape[1]
+    s = cache.struct
+    shape = (s.num_layers, N, s.num_kv_heads, s.head_dim)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    _check(k_new, "k_new", torch.bfloat16, device=dev)
+    _check(v_new, "v_new", torch.bfloat16, device=dev)
+    _check(cu_new, "cu_new", torch.int32, B + 1, dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    st = lib.kv_paged_append(ctypes.byref(s), B, _ptr(k_new), _ptr(v_new), _ptr(cu_new), N,
+                             _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("kv_paged_append", st)
+
+
+def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch.Tensor) -> None:
+    """Enqueue the rollback of every request to its committed prefix."""
+    lib = load_library()
+    dev = cache.device
+    B = cu_draft.numel() - 1
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(cu_draft, "cu_draft", torch.int32, B + 1, dev)
+    st = lib.kv_rollback(ctypes.byref(cache.struct), B, _ptr(num_accepted), _ptr(cu_draft),
+                         _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("kv_rollback", st)
+
+
+# --- HIP events through the runtime (for timing the row-statistics kernel) -------------
+
+_hip = None
+
+
+def _hip_rt() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                             ctypes.c_void_p]
+    return _hip
+
+
+class HipEvent:
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        if _hip_rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        rt = _hip_rt()
+        rt.hipEventSynchronize(end.handle)
+        ms = ctypes.c_float()
+        if rt.hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _hip_rt().hipEventDestroy(self.handle)
+        except Exception:
+            pass

@@ -1,0 +1,364 @@
+"""Shared helpers for GPU parity tests: upload seeded inputs, run the HIP library through
+the binding, and compare with the oracle under the flagged-margin rule.
+
+Parity rule: accepted counts, emitted tokens, lengths, tables, free lists and K/V bits are
+compared exactly, except decisions whose oracle margin (|u - p/q| for an accept test,
+distance of u*W to the nearer CDF edge as a fraction of W for a sampled token) is below
+1e-6: those are flagged and counted; a flagged mismatch is followed up by re-deriving the
+oracle's result from the GPU's decision. Probabilities match within 1e-5 relative.
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+from oracle.verify import residual_weights, inverse_cdf_np, transform, _decode_rows
+from rejection_sampling_verify_specdec_amd import binding
+from rejection_sampling_verify_specdec_amd.synth import VerifyInputs, KVInputs
+
+MARGIN = 1e-6
+RTOL = 1e-5
+ATOL = 1e-30
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev() -> torch.device:
+    return torch.device("cuda:0")
+
+
+def _logits_t(x: np.ndarray, dtype: str, device) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+@dataclass
+class GpuVerify:
+    num_accepted: np.ndarray
+    num_emitted: np.ndarray
+    out_tokens: np.ndarray
+    err_word: int
+    p_y: np.ndarray
+    q_y: np.ndarray
+    row_max: np.ndarray
+    row_sum: np.ndarray
+    row_thr: np.ndarray
+    row_nkept: np.ndarray
+    resid_mass: np.ndarray
+    picked_prob: np.ndarray
+    req_flags: np.ndarray
+
+
+class VerifyOnDevice:
+    """Inputs of one verification batch resident on the GPU, plus outputs and workspace."""
+
+    def __init__(self, vin: VerifyInputs, device=None, max_k: Optional[int] = None,
+                 top_k: Optional[int] = None, T: Optional[float] = None):
+        d = device or dev()
+        self.vin = vin
+        self.max_k = vin.max_k if max_k is None else max_k
+        self.top_k = vin.top_k if top_k is None else top_k
+        self.T = vin.T if T is None else T
+        self.tgt = _logits_t(vin.target, vin.dtype, d)
+        self.dft = _logits_t(vin.draft.reshape(vin.K, vin.V), vin.dtype, d)
+        self.tokens = torch.from_numpy(vin.draft_tokens.astype(np.int32)).to(d)
+        self.cu = torch.from_numpy(vin.cu_draft.astype(np.int32)).to(d)
+        self.u_acc = torch.from_numpy(vin.u_accept.astype(np.float32)).to(d)
+        self.u_smp = torch.from_numpy(vin.u_sample.astype(np.float32)).to(d)
+        B, K = vin.B, vin.K
+        R = 2 * K + B
+        self.out_tokens = torch.full((K + B,), -7, dtype=torch.int32, device=d)
+        self.num_acc = torch.full((B,), -9, dtype=torch.int32, device=d)
+        self.num_emit = torch.full((B,), -9, dtype=torch.int32, device=d)
+        self.err = torch.zeros(1, dtype=torch.int32, device=d)
+        dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+        ws = binding.specdec_verify_workspace_size(B, K, vin.V, dt, self.top_k)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=d)
+        self.p_y = torch.full((max(K, 1),), -1.0, dtype=torch.float64, device=d)
+        self.q_y = torch.full((max(K, 1),), -1.0, dtype=torch.float64, device=d)
+        self.row_max = torch.zeros(R, dtype=torch.float32, device=d)
+        self.row_sum = torch.zeros(R, dtype=torch.float64, device=d)
+        self.row_thr = torch.zeros(R, dtype=torch.float32, device=d)
+        self.row_nkept = torch.zeros(R, dtype=torch.int32, device=d)
+        self.resid_mass = torch.full((B,), -1.0, dtype=torch.float64, device=d)
+        self.picked = torch.full((B,), -1.0, dtype=torch.float64, device=d)
+        self.req_flags = torch.full((B,), -1, dtype=torch.int32, device=d)
+        self.dbg = binding.SpecdecDebug(
+            self.p_y.data_ptr(), self.q_y.data_ptr(), self.row_max.data_ptr(),
+            self.row_sum.data_ptr(), self.row_thr.data_ptr(), self.row_nkept.data_ptr(),
+            self.resid_mass.data_ptr(), self.picked.data_ptr(), self.req_flags.data_ptr(),
+            None, None)
+
+    def run(self, debug: bool = True) -> None:
+        binding.specdec_verify(
+            self.tgt, self.dft, self.tokens, self.cu, self.u_acc, self.u_smp,
+            max_k=self.max_k, temperature=self.T, top_k=self.top_k,
+            out_tokens=self.out_tokens, num_accepted=self.num_acc, num_emitted=self.num_emit,
+            err_word=self.err, workspace=self.ws, debug=self.dbg if debug else None)
+
+    def result(self) -> GpuVerify:
+        torch.cuda.synchronize()
+        c = lambda t: t.cpu().numpy()
+        return GpuVerify(c(self.num_acc), c(self.num_emit), c(self.out_tokens), int(self.err.item()),
+                         c(self.p_y), c(self.q_y), c(self.row_max), c(self.row_sum), c(self.row_thr),
+                         c(self.row_nkept), c(self.resid_mass), c(self.picked), c(self.req_flags))
+
+
+def run_verify(vin: VerifyInputs, **kw) -> GpuVerify:
+    v = VerifyOnDevice(vin, **kw)
+    v.run()
+    return v.result()
+
+
+def oracle_verify(vin: VerifyInputs, requests=None, keep_probs=False, max_k=None, top_k=None,
+                  T=None):
+    return oracle.verify_batch(vin.target, vin.draft, vin.draft_tokens, vin.cu_draft,
+                               vin.u_accept, vin.u_sample, vin.T if T is None else T,
+                               vin.top_k if top_k is None else top_k,
+                               vin.max_k if max_k is None else max_k, vin.dtype,
+                               requests=requests, keep_probs=keep_probs)
+
+
+@dataclass
+class Report:
+    decisions: int = 0
+    samples: int = 0
+    flagged: int = 0
+    flagged_mismatch: int = 0
+    max_rel_p: float = 0.0
+    max_rel_S: float = 0.0
+    max_rel_W: float = 0.0
+    errors: List[str] = field(default_factory=list)
+
+    def fail(self, msg: str) -> None:
+        if len(self.errors) < 20:
+            self.errors.append(msg)
+
+    def __str__(self) -> str:
+        return (f"decisions={self.decisions} samples={self.samples} flagged={self.flagged} "
+                f"flagged_mismatch={self.flagged_mismatch} max_rel_p={self.max_rel_p:.2e} "
+                f"max_rel_S={self.max_rel_S:.2e} max_rel_W={self.max_rel_W:.2e}")
+
+
+def _rel(a: float, b: float) -> float:
+    if a == b:
+        return 0.0
+    return abs(a - b) / (abs(b) + ATOL)
+
+
+def _close(a: float, b: float, rtol: float = RTOL) -> bool:
+    if math.isinf(b) or math.isnan(b):
+        return a == b or (math.isnan(a) and math.isnan(b))
+    return abs(a - b) <= rtol * abs(b) + ATOL
+
+
+def _resample(vin: VerifyInputs, b: int, a: int, T: float, top_k: int):
+    """Oracle token drawn at the GPU's decision a (after a flagged accept mismatch)."""
+    lo, hi = int(vin.cu_draft[b]), int(vin.cu_draft[b + 1])
+    k = hi - lo
+    t_rows = _decode_rows(vin.target[lo + b: lo + b + k + 1], vin.dtype)
+    d_rows = _decode_rows(vin.draft[lo:hi], vin.dtype)
+    if a < k:
+        p = transform(t_rows[a], T, top_k).p
+        q = transform(d_rows[a], T, top_k).p
+        w = residual_weights(p, q)
+        x, W, m = inverse_cdf_np(w, float(vin.u_sample[b]))
+        if x is None:
+            x, W, m = inverse_cdf_np(p, float(vin.u_sample[b]))
+    else:
+        p = transform(t_rows[k], T, top_k).p
+        x, W, m = inverse_cdf_np(p, float(vin.u_sample[b]))
+    return x, W, m
+
+
+def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, top_k=None,
+                   check_debug: bool = True) -> Report:
+    T = vin.T if T is None else T
+    top_k = vin.top_k if top_k is None else top_k
+    rep = Report()
+    B, K = vin.B, vin.K
+    reqs = range(B) if requests is None else requests
+    for b in reqs:
+        lo, hi = int(vin.cu_draft[b]), int(vin.cu_draft[b + 1])
+        k = hi - lo
+        r = o.requests[b]
+        oa = int(o.num_accepted[b])
+        ga = int(g.num_accepted[b])
+        if int(o.err[b]) != int(g.req_flags[b]) and check_debug:
+            # flags of a flagged mismatch may differ only in QZERO at the moved position
+            if not (oa != ga and ((int(o.err[b]) ^ int(g.req_flags[b])) & ~oracle.ERR_QZERO) == 0):
+                rep.fail(f"req {b}: flags oracle={o.err[b]} gpu={g.req_flags[b]}")
+        if oa < 0 or ga < 0:
+            if oa != ga or int(g.num_emitted[b]) != 0:
+                rep.fail(f"req {b}: error status oracle a={oa} gpu a={ga}")
+            continue
+        # probabilities at every proposal position
+        if check_debug:
+            for i in range(k):
+                P, Q = float(r.probs.P[i]), float(r.probs.Q[i])
+                gp, gq = float(g.p_y[lo + i]), float(g.q_y[lo + i])
+                rep.max_rel_p = max(rep.max_rel_p, _rel(gp, P), _rel(gq, Q))
+                if not (_close(gp, P) and _close(gq, Q)):
+                    rep.fail(f"req {b} pos {i}: p {gp} vs {P}, q {gq} vs {Q}")
+            for i, row in enumerate(r.rows_t):
+                R = lo + b + i
+                _cmp_row(rep, f"req {b} target row {i}", row, g, R, top_k)
+            for i, row in enumerate(r.rows_d):
+                R = K + B + lo + i
+                _cmp_row(rep, f"req {b} draft row {i}", row, g, R, top_k)
+        margins = r.probs.accept_margin
+        first = min(oa, ga)
+        rep.decisions += min(max(oa, ga) + 1, k)
+        flagged_dec = any(float(margins[i]) < MARGIN for i in range(min(first + 1, k)))
+        rep.flagged += flagged_dec
+        if oa != ga:
+            if float(margins[first]) < MARGIN:
+                rep.flagged_mismatch += 1
+                x, W, m = _resample(vin, b, ga, T, top_k)
+                gx = int(g.out_tokens[lo + b + ga])
+                if gx != x and not (m is not None and m < MARGIN):
+                    rep.fail(f"req {b}: after flagged accept mismatch token {gx} vs {x}")
+            else:
+                rep.fail(f"req {b}: accepted {ga} vs oracle {oa} (margin {float(margins[first]):.3e})")
+            continue
+        if int(g.num_emitted[b]) != oa + 1:
+            rep.fail(f"req {b}: num_emitted {g.num_emitted[b]} vs {oa + 1}")
+        got = [int(x) for x in g.out_tokens[lo + b: lo + b + oa + 1]]
+        exp = r.emitted
+        rep.samples += 1
+        if got[:oa] != exp[:oa]:
+            rep.fail(f"req {b}: accepted tokens {got[:oa]} vs {exp[:oa]}")
+        sm = float(r.probs.sample_margin)
+        if sm < MARGIN:
+            rep.flagged += 1
+        if got[oa] != exp[oa]:
+            if sm < MARGIN:
+                rep.flagged_mismatch += 1
+            else:
+                rep.fail(f"req {b}: sampled token {got[oa]} vs {exp[oa]} (margin {sm:.3e})")
+        if check_debug:
+            W = float(r.probs.W)
+            rep.max_rel_W = max(rep.max_rel_W, _rel(float(g.resid_mass[b]), W))
+            if not _close(float(g.resid_mass[b]), W):
+                rep.fail(f"req {b}: W {g.resid_mass[b]} vs {W}")
+            if got[oa] == exp[oa] and not _close(float(g.picked_prob[b]), float(r.probs.picked), 1e-4):
+                rep.fail(f"req {b}: picked prob {g.picked_prob[b]} vs {r.probs.picked}")
+    return rep
+
+
+def _cmp_row(rep: Report, what: str, row, g: GpuVerify, R: int, top_k: int) -> None:
+    if not row.valid:
+        return
+    if float(g.row_max[R]) != row.m:
+        rep.fail(f"{what}: max {g.row_max[R]} vs {row.m}")
+    rep.max_rel_S = max(rep.max_rel_S, _rel(float(g.row_sum[R]), row.S))
+    if not _close(float(g.row_sum[R]), row.S):
+        rep.fail(f"{what}: S {g.row_sum[R]} vs {row.S}")
+    if float(g.row_thr[R]) != row.thr:
+        rep.fail(f"{what}: thr {g.row_thr[R]} vs {row.thr}")
+    if top_k and 0 < top_k and int(g.row_nkept[R]) != row.nkept and row.thr != -math.inf:
+        rep.fail(f"{what}: nkept {g.row_nkept[R]} vs {row.nkept}")
+
+
+# --------------------------------------------------------------------------------------
+# Paged KV on the device
+# --------------------------------------------------------------------------------------
+
+def pool_tensor(kv: KVInputs, device, fill_bits: int = 0x7FAA) -> torch.Tensor:
+    """Pool filled with a marker pattern, then the prefix contents the cycle may read."""
+    pool = torch.empty((kv.L, 2, kv.num_blocks, kv.block_size, kv.H, kv.D),
+                       dtype=torch.bfloat16, device=device)
+    pool.view(torch.int16).fill_(np.int16(np.uint16(fill_bits).view(np.int16)))
+    if kv.blocks:
+        ids = sorted(kv.blocks)
+        data = np.stack([kv.blocks[X][0] for X in ids], axis=2)   # [L][2][n][bs][H][D]
+        t = torch.from_numpy(data.view(np.int16)).view(torch.bfloat16).to(device)
+        pool[:, :, torch.tensor(ids, device=device)] = t
+    return pool
+
+
+class KVOnDevice:
+    def __init__(self, kv: KVInputs, B: int, device=None, fill_bits: int = 0x7FAA):
+        d = device or dev()
+        self.kv = kv
+        self.pool = pool_tensor(kv, d, fill_bits)
+        self.cache = binding.PagedKVCache(
+            self.pool,
+            torch.from_numpy(kv.block_tables.astype(np.int32)).to(d),
+            torch.from_numpy(kv.seq_lens.astype(np.int32)).to(d),
+            torch.from_numpy(kv.refcount.astype(np.int32)).to(d),
+            torch.from_numpy(kv.free_list.astype(np.int32)).to(d),
+            torch.tensor([kv.free_count], dtype=torch.int32, device=d),
+            torch.zeros(1, dtype=torch.int32, device=d))
+        self.k_new = torch.from_numpy(kv.k_new.view(np.int16)).view(torch.bfloat16).to(d)
+        self.v_new = torch.from_numpy(kv.v_new.view(np.int16)).view(torch.bfloat16).to(d)
+        self.cu_new = torch.from_numpy(kv.cu_new.astype(np.int32)).to(d)
+        self.ws = torch.empty(binding.kv_paged_append_workspace_size(B), dtype=torch.uint8,
+                              device=d)
+
+    def append(self, k_new=None, v_new=None, cu_new=None):
+        binding.kv_paged_append(self.cache, self.k_new if k_new is None else k_new,
+                                self.v_new if v_new is None else v_new,
+                                self.cu_new if cu_new is None else cu_new, self.ws)
+
+    def rollback(self, num_accepted: torch.Tensor, cu_draft: torch.Tensor):
+        binding.kv_rollback(self.cache, num_accepted, cu_draft)
+
+    def meta(self):
+        torch.cuda.synchronize()
+        c = self.cache
+        return dict(tables=c.block_tables.cpu().numpy(), seq_lens=c.seq_lens.cpu().numpy(),
+                    refcount=c.refcount.cpu().numpy(), free_list=c.free_list.cpu().numpy(),
+                    free_count=int(c.free_count.item()), state=int(c.state.item()))
+
+
+def oracle_kv(kv: KVInputs) -> oracle.PagedKV:
+    return oracle.PagedKV(kv.L, kv.H, kv.D, kv.block_size, kv.num_blocks, kv.block_tables,
+                          kv.seq_lens, kv.refcount, kv.free_list, kv.free_count, kv.blocks)
+
+
+def compare_kv_meta(o: oracle.PagedKV, m: Dict, what: str = "") -> List[str]:
+    errs = []
+    if not np.array_equal(m["tables"], o.tables):
+        bad = np.argwhere(m["tables"] != o.tables)[:5]
+        errs.append(f"{what} block tables differ at {bad.tolist()}")
+    if list(m["seq_lens"]) != o.seq_lens:
+        errs.append(f"{what} seq_lens differ")
+    if list(m["refcount"]) != o.refcount:
+        bad = np.nonzero(np.array(m["refcount"]) != np.array(o.refcount))[0][:5]
+        errs.append(f"{what} refcounts differ at {bad.tolist()}")
+    if m["free_count"] != o.free_count:
+        errs.append(f"{what} free_count {m['free_count']} vs {o.free_count}")
+    elif list(m["free_list"][:o.free_count]) != o.free:
+        errs.append(f"{what} free list differs")
+    if m["state"] != (o.err | o.state):
+        errs.append(f"{what} state {m['state']} vs {o.err | o.state}")
+    return errs
+
+
+def compare_kv_data(o: oracle.PagedKV, pool: torch.Tensor, blocks=None) -> List[str]:
+    """Every slot the oracle has defined contents for must match bit for bit."""
+    errs = []
+    ids = sorted(o.data) if blocks is None else sorted(blocks)
+    if not ids:
+        return errs
+    idx = torch.tensor(ids, device=pool.device)
+    got = pool[:, :, idx].view(torch.int16).cpu().numpy().view(np.uint16)   # [L][2][n][bs][H][D]
+    for j, X in enumerate(ids):
+        m = o.defined[X]
+        if not np.array_equal(got[:, :, j][:, :, m], o.data[X][:, :, m]):
+            errs.append(f"block {X}: K/V bits differ")
+            if len(errs) > 10:
+                break
+    return errs
