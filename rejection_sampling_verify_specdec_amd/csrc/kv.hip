@@ -74,18 +74,23 @@ SD_DEV void copy_slots(const KvArgs& a, int src, int dst, int nslots, int tid, i
     }
 }
 
+// Requests are spread over the workgroup with stride kKvNT (request b = round * kKvNT +
+// thread), so a batch of up to kKvNT requests costs one pass of dependent loads; ordered
+// quantities (pop positions) come from per-round exclusive scans with a running carry.
 __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restrict__ cu_new,
                                                     int B, int N, int* __restrict__ ws) {
     __shared__ int redi[kKvNT / kWave];
     __shared__ int s_pot_b[SPECDEC_MAX_KV_BATCH];
     __shared__ int s_pot_X[SPECDEC_MAX_KV_BATCH];
     const int tid = threadIdx.x;
+    const int rounds = (B + kKvNT - 1) / kKvNT;
+    const int fc = *a.free_count;
     int s[kKvRPT], n[kKvRPT], X[kKvRPT], r0[kKvRPT];
-    int bad = 0, npot = 0;
+    int bad = 0;
     if (tid == 0 && (cu_new[0] != 0 || cu_new[B] != N)) bad = 1;
 #pragma unroll
     for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
+        const int b = i * kKvNT + tid;
         s[i] = n[i] = 0;
         X[i] = -1;
         r0[i] = 0;
@@ -103,7 +108,6 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
                 continue;
             }
             r0[i] = a.refcount[X[i]];
-            npot += r0[i] > 1;
         }
     }
     bad = block_max_i<kKvNT>(bad, redi);
@@ -115,18 +119,17 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
         }
         return;
     }
-    // shared partial blocks receiving entries: list them in request order
-    int total;
-    int pos = block_excl_scan_i<kKvNT>(npot, redi, &total);
-    const int P = total;
-#pragma unroll
-    for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
-        if (b < B && X[i] >= 0 && r0[i] > 1) {
-            s_pot_b[pos] = b;
+    // shared partial blocks receiving entries, listed in request order
+    int P = 0;
+    for (int i = 0; i < rounds; ++i) {
+        const int pot = (X[i] >= 0 && r0[i] > 1) ? 1 : 0;
+        int tot;
+        const int pos = P + block_excl_scan_i<kKvNT>(pot, redi, &tot);
+        if (pot) {
+            s_pot_b[pos] = i * kKvNT + tid;
             s_pot_X[pos] = X[i];
-            ++pos;
         }
+        P += tot;
     }
     if (tid == 0) {
         ws[1] = 0;
@@ -135,11 +138,11 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
     __syncthreads();
     // copy-on-write: the i-th sharer (in request order) of block X copies iff i < r0 - 1,
     // which is what processing the batch in order with live refcounts gives
-    int cow[kKvRPT], conflict[kKvRPT], need = 0;
+    int cow[kKvRPT], conflict[kKvRPT], need[kKvRPT];
 #pragma unroll
     for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
-        cow[i] = conflict[i] = 0;
+        const int b = i * kKvNT + tid;
+        cow[i] = conflict[i] = need[i] = 0;
         if (b >= B) continue;
         if (X[i] >= 0 && r0[i] > 1) {
             int rank = 0, cnt = 0;
@@ -153,11 +156,15 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
             // another sharer writes X in place in this batch: copy before the scatter
             conflict[i] = cow[i] && cnt > r0[i] - 1;
         }
-        if (n[i] > 0) need += ceil_div(s[i] + n[i], a.bs) - ceil_div(s[i], a.bs) + cow[i];
+        if (n[i] > 0) need[i] = ceil_div(s[i] + n[i], a.bs) - ceil_div(s[i], a.bs) + cow[i];
     }
-    int T;
-    const int base = block_excl_scan_i<kKvNT>(need, redi, &T);
-    const int fc = *a.free_count;
+    int base[kKvRPT];
+    int T = 0;
+    for (int i = 0; i < rounds; ++i) {
+        int tot;
+        base[i] = T + block_excl_scan_i<kKvNT>(need[i], redi, &tot);
+        T += tot;
+    }
     if (T > fc) {
         if (tid == 0) {
             ws[0] = 1;
@@ -165,11 +172,10 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
         }
         return;
     }
-    int p = base;
-#pragma unroll
-    for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
+    for (int i = 0; i < rounds; ++i) {
+        const int b = i * kKvNT + tid;
         if (b >= B || n[i] == 0) continue;
+        int p = base[i];
         int* tab = a.tables + (size_t)b * a.MBR;
         if (cow[i]) {
             const int nb = a.free_list[fc - 1 - p++];
@@ -279,46 +285,46 @@ __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __re
     __shared__ int s_lb[kEvCap];
     if (*a.state & KV_APPEND_REJECTED) return;
     const int tid = threadIdx.x;
-    int err = 0, nev = 0;
-    int newlen[kKvRPT], ev[kKvRPT], valid[kKvRPT];
+    const int rounds = (B + kKvNT - 1) / kKvNT;
+    int fc = *a.free_count;
+    int err = 0;
+    int newlen[kKvRPT], valid[kKvRPT];
+    int E = 0;
 #pragma unroll
     for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
+        const int b = i * kKvNT + tid;
         valid[i] = 0;
-        ev[i] = 0;
         newlen[i] = 0;
-        if (b >= B) continue;
-        const int k = cu[b + 1] - cu[b], acc = num_acc[b], s = a.seq_lens[b];
-        if (k < 0 || acc < 0 || acc > k || k - acc > s ||
-            (long long)s > (long long)a.MBR * a.bs) {
-            err = 1;
-            continue;
-        }
-        valid[i] = 1;
-        newlen[i] = s - (k - acc);
-        ev[i] = ceil_div(s, a.bs) - ceil_div(newlen[i], a.bs);
-        nev += ev[i];
-    }
-    int E;
-    int off = block_excl_scan_i<kKvNT>(nev, redi, &E);
-#pragma unroll
-    for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
+        int ev = 0;
         if (b < B) {
-            s_off[b] = off;
-            s_lb0[b] = ceil_div(newlen[i], a.bs);
-            off += ev[i];
+            const int k = cu[b + 1] - cu[b], acc = num_acc[b], s = a.seq_lens[b];
+            if (k < 0 || acc < 0 || acc > k || k - acc > s ||
+                (long long)s > (long long)a.MBR * a.bs) {
+                err = 1;
+            } else {
+                valid[i] = 1;
+                newlen[i] = s - (k - acc);
+                ev = ceil_div(s, a.bs) - ceil_div(newlen[i], a.bs);
+            }
+        }
+        if (i < rounds) {
+            int tot;
+            const int off = E + block_excl_scan_i<kKvNT>(ev, redi, &tot);
+            if (b < B) {
+                s_off[b] = off;
+                s_lb0[b] = ceil_div(newlen[i], a.bs);
+            }
+            E += tot;
         }
     }
     if (tid == 0) s_off[B] = E;
-    int fc = *a.free_count;
     __syncthreads();
     for (int w0 = 0; w0 < E; w0 += kEvCap) {
         const int nw = min(kEvCap, E - w0);
         // gather this window's events in (request, logical block) order
 #pragma unroll
         for (int i = 0; i < kEvPT; ++i) {
-            const int el = tid * kEvPT + i;
+            const int el = i * kKvNT + tid;
             if (el >= nw) continue;
             const int e = w0 + el;
             int lo = 0, hi = B;               // largest b with s_off[b] <= e
@@ -327,17 +333,16 @@ __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __re
                 if (s_off[mid] <= e) lo = mid;
                 else hi = mid;
             }
-            while (lo + 1 < B && s_off[lo + 1] <= e) ++lo;   // skip requests without events
             const int lb = s_lb0[lo] + (e - s_off[lo]);
             s_b[el] = lo;
             s_lb[el] = lb;
             s_X[el] = a.tables[(size_t)lo * a.MBR + lb];
         }
         __syncthreads();
-        int push[kEvPT], newrc[kEvPT], first[kEvPT], npush = 0;
+        int push[kEvPT], newrc[kEvPT], first[kEvPT];
 #pragma unroll
         for (int i = 0; i < kEvPT; ++i) {
-            const int el = tid * kEvPT + i;
+            const int el = i * kKvNT + tid;
             push[i] = first[i] = 0;
             newrc[i] = 0;
             if (el >= nw) continue;
@@ -360,21 +365,26 @@ __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __re
             push[i] = rc >= 1 && rank == rc - 1;
             first[i] = rank == 0;
             newrc[i] = rc - min(cnt, max(rc, 0));
-            npush += push[i];
         }
-        int ptot;
-        int pp = block_excl_scan_i<kKvNT>(npush, redi, &ptot);   // also orders the reads
+        // push positions follow event order (the scans also separate reads from writes)
+        int pbase[kEvPT];
+        int ptot = 0;
 #pragma unroll
         for (int i = 0; i < kEvPT; ++i) {
-            const int el = tid * kEvPT + i;
+            int tot;
+            pbase[i] = ptot + block_excl_scan_i<kKvNT>(push[i], redi, &tot);
+            ptot += tot;
+        }
+#pragma unroll
+        for (int i = 0; i < kEvPT; ++i) {
+            const int el = i * kKvNT + tid;
             if (el >= nw) continue;
             const int X = s_X[el];
             if (X >= 0 && X < a.NB) {
                 if (first[i]) a.refcount[X] = newrc[i];
                 if (push[i]) {
-                    if (fc + pp < a.NB) a.free_list[fc + pp] = X;
+                    if (fc + pbase[i] < a.NB) a.free_list[fc + pbase[i]] = X;
                     else err = 1;                     // more frees than blocks: corrupt
-                    ++pp;
                 }
             }
             a.tables[(size_t)s_b[el] * a.MBR + s_lb[el]] = -1;
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __re
     }
 #pragma unroll
     for (int i = 0; i < kKvRPT; ++i) {
-        const int b = tid * kKvRPT + i;
+        const int b = i * kKvNT + tid;
         if (b < B && valid[i]) a.seq_lens[b] = newlen[i];
     }
     err = block_max_i<kKvNT>(err, redi);

@@ -7,23 +7,21 @@
 // decoding transform (temperature, top-k) applied identically to target and draft rows
 // and a max-subtracted (stable) softmax (same page, section 6).
 //
-// Pipeline on one stream, per call:
-//   k_row_stats   every target and draft row is streamed once in 16 KB-32 KB chunks with
+// Pipeline on one stream, per call (two kernels):
+//   k_row_stats   every target and draft row is streamed once in 16K-element chunks with
 //                 128-bit loads; each workgroup writes the chunk max m_c and
 //                 S_c = sum exp2((z - m_c) * c), c = log2(e) / T, as an fp32/fp64 pair.
-//   k_topk_rows   (top-k only) one workgroup per row: exact top-k threshold, max and
-//                 kept-set sum (replaces k_row_stats).
-//   k_decide      one wave per request: combines the row partials in fp64, evaluates
-//                 p_i(y_i), q_i(y_i) in fp64, the accept test u * q < p, finds the first
-//                 rejection, writes accepted tokens and the parameters of the one row
-//                 pair (or bonus row) still to be sampled.
-//   k_resid_part  per (request, chunk): partial sums of the sampling weights w(x) =
-//                 max(0, p_j(x) - q_j(x)) (or p_{k+1}(x) for the bonus), fp64.
-//   k_resid_pick  per request: total W, t = u * W, locates the chunk holding t, then an
-//                 LDS prefix scan over that chunk in ascending token order finds the
-//                 smallest x with C(x) > t. Rows after the first rejection are never
-//                 re-read (ragged early exit).
+//   k_topk_rows   (top-k only, replaces k_row_stats) one workgroup per row: exact top-k
+//                 threshold, max, kept count and kept-set sum.
+//   k_sample      one workgroup per (request, chunk): combines the row partials in fp64,
+//                 evaluates p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p, finds
+//                 the first rejection; sums the sampling weights of its chunk of the one
+//                 row pair (or bonus row) still to be sampled; the request's last workgroup
+//                 locates t = u * W among the chunk sums and scans that chunk in ascending
+//                 token order for the smallest x with C(x) > t. Rows after the first
+//                 rejection are never re-read (ragged early exit).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stddef.h>
@@ -45,17 +43,6 @@ struct alignas(16) RowPartial {
     float m;      // max logit of the chunk (-inf if none)
     int nkept;    // kept tokens (top-k rows only)
     double s;     // sum over the chunk of exp2((z - m) * c)
-};
-
-// What k_decide leaves for the sampling kernels, per request.
-struct alignas(16) SampleRec {
-    int mode, row_t, row_d, out_pos;
-    float mc_t, mc_d;      // fp32(m * c): the exponent offset used elementwise
-    float thr_t, thr_d;    // top-k thresholds (-inf when off)
-    double al_t, al_d;     // 2^(m*c - mc) / S: turns exp2(z*c - mc) into a probability
-    float u;
-    int flags;
-    int pad0, pad1;
 };
 
 template <bool BF16, bool VEC>
@@ -137,13 +124,15 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ tgt,
                                                    const uint8_t* __restrict__ dft,
                                                    int rows_t, int V, int nchunks, float c,
-                                                   RowPartial* __restrict__ part) {
+                                                   RowPartial* __restrict__ part, int B,
+                                                   int* __restrict__ cnt) {
     using Lt = Layout<BF16, VEC>;
     __shared__ float redf[kNT / kWave];
     __shared__ double redd[kNT / kWave];
     __shared__ int redi[kNT / kWave];
     const int row = blockIdx.x / nchunks;
     const int chunk = blockIdx.x - row * nchunks;
+    if (chunk == 0 && row < B && threadIdx.x == 0) cnt[row] = 0;   // sampling counters
     const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, Lt::ES);
     float z[Lt::EPT];
     load_chunk<BF16, VEC>(base, V, chunk * Lt::CH, z);
@@ -205,7 +194,8 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
                                                        const uint8_t* __restrict__ dft,
                                                        int rows_t, int V, int top_k, float c,
                                                        RowPartial* __restrict__ part,
-                                                       float* __restrict__ row_thr) {
+                                                       float* __restrict__ row_thr, int B,
+                                                       int* __restrict__ cnt) {
     constexpr int NT = kTopkNT;
     constexpr int ES = BF16 ? 2 : 4;
     __shared__ unsigned hist[256];
@@ -217,6 +207,7 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
     const int row = blockIdx.x;
     const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, ES);
     const int tid = threadIdx.x;
+    if (row < B && tid == 0) cnt[row] = 0;   // sampling counters
 
     // pass 0: max, invalid entries (NaN, +inf)
     float mx = -INFINITY;
@@ -267,20 +258,20 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
     const float mc = m * c;
     const float emc = fmaf(m, c, -mc);
     float acc = 0.f;
-    int cnt = 0;
+    int kept = 0;
     for (int i = tid; i < V; i += NT) {
         const float z = load_elem(base, i, BF16);
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
-            ++cnt;
+            ++kept;
         }
     }
     const double tot = block_sum<NT>((double)acc, redd);
-    cnt = block_sum_i<NT>(cnt, redi);
+    kept = block_sum_i<NT>(kept, redi);
     if (tid == 0) {
         RowPartial rp;
         rp.m = m;
-        rp.nkept = cnt;
+        rp.nkept = kept;
         rp.s = bad ? (double)NAN : (m == -INFINITY ? 0.0 : tot * exp2(-(double)emc));
         part[row] = rp;
         row_thr[row] = thr;
@@ -288,165 +279,50 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------------------
-// Per-request decision: one wave per request.
+// Decision and sampling, fused: one kernel over (request, chunk) workgroups.
+//   1. every workgroup of request b re-derives b's decision from the row partials (cheap:
+//      2k+1 rows x a few partials, k fp64 exponentials) so no separate launch is needed;
+//      the chunk-0 workgroup publishes the outputs;
+//   2. each workgroup sums the sampling weights of its chunk of the row(s) still to be
+//      sampled (rows after the first rejection are never touched);
+//   3. the last workgroup of the request to finish (device-scope counter) turns the chunk
+//      sums into W, finds the chunk holding t = u * W and scans it in ascending token order.
 // ---------------------------------------------------------------------------------------
-struct DecideArgs {
+struct SampleArgs {
     const uint8_t* tgt;
     const uint8_t* dft;
-    int bf16;
     const int* tokens;
     const int* cu;
     const float* u_acc;
     const float* u_smp;
     int B, K, max_k, V;
-    int nparts;              // partials per row
+    int nparts;              // statistics partials per row
+    int nchunks;             // sampling chunks per row
     int topk;                // 1 when rows carry a top-k threshold
     float c;
     const RowPartial* part;
     const float* row_thr;
+    double* wpart;           // [B][nchunks] chunk sums of the weights
+    int* cnt;                // [B] finished chunks (zeroed by the statistics kernel)
     int* out_tokens;
     int* num_acc;
     int* num_emit;
     int* err_word;
-    SampleRec* rec;
     specdec_debug dbg;
 };
 
-__global__ __launch_bounds__(kWave) void k_decide(DecideArgs a) {
-    __shared__ float s_m[2 * SPECDEC_MAX_K + 1];
-    __shared__ double s_S[2 * SPECDEC_MAX_K + 1];
-    __shared__ float s_thr[2 * SPECDEC_MAX_K + 1];
-    const int b = blockIdx.x;
-    const int lane = threadIdx.x;
-    const int rows_t = a.K + a.B;
-    const int lo = a.cu[b], hi = a.cu[b + 1];
-    const int k = hi - lo;
-    const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
-                       hi > a.K;
-    if (bad_k) {
-        if (lane == 0) {
-            a.num_acc[b] = -1;
-            a.num_emit[b] = 0;
-            a.rec[b].mode = MODE_NONE;
-            atomicOr(a.err_word, SPECDEC_ERR_K);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = SPECDEC_ERR_K;
-        }
-        return;
-    }
-    const double cd = (double)a.c;
-    const int nrows = 2 * k + 1;
-    int row_bad = 0;
-    for (int r = lane; r < nrows; r += kWave) {
-        const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
-        const RowPartial* pp = a.part + (size_t)prow * a.nparts;
-        float m = -INFINITY;
-        for (int q = 0; q < a.nparts; ++q) m = fmaxf(m, pp[q].m);
-        double S = 0.0;
-        int nk = 0;
-        for (int q = 0; q < a.nparts; ++q) {
-            const RowPartial x = pp[q];
-            // chunks with no finite entry carry 0 (or NaN, which must propagate)
-            S += x.m == -INFINITY ? x.s : x.s * exp2((double)(x.m - m) * cd);
-            nk += x.nkept;
-        }
-        const float thr = a.topk ? a.row_thr[prow] : -INFINITY;
-        s_m[r] = m;
-        s_S[r] = S;
-        s_thr[r] = thr;
-        row_bad |= !(S > 0.0 && S < INFINITY && m > -INFINITY);
-        if (a.dbg.row_max) a.dbg.row_max[prow] = m;
-        if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
-        if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
-        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
-    }
-    __syncthreads();
+struct Decision {
+    int flags, err, a, k, lo, mode, row_t, row_d;
+    float mc_t, mc_d, thr_t, thr_d;
+    double al_t, al_d;
+    float u;
+};
 
-    // proposals: lane i handles position i (k <= SPECDEC_MAX_K = kWave)
-    int flags = 0;
-    bool acc = true;
-    double P = 0.0, Q = 0.0;
-    int y = 0;
-    if (lane < k) {
-        y = a.tokens[lo + lane];
-        const double u = (double)a.u_acc[lo + lane];
-        if (!(u >= 0.0 && u < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-        if (y < 0 || y >= a.V) {
-            flags |= SPECDEC_ERR_TOKEN;
-        } else {
-            const int es = a.bf16 ? 2 : 4;
-            const float zt = load_elem(a.tgt + (size_t)(lo + b + lane) * a.V * es, y, a.bf16);
-            const float zd = load_elem(a.dft + (size_t)(lo + lane) * a.V * es, y, a.bf16);
-            const int rt = lane, rd = k + 1 + lane;
-            if (zt >= s_thr[rt] && zt > -INFINITY)
-                P = exp2(((double)zt - (double)s_m[rt]) * cd) / s_S[rt];
-            if (zd >= s_thr[rd] && zd > -INFINITY)
-                Q = exp2(((double)zd - (double)s_m[rd]) * cd) / s_S[rd];
-            acc = u * Q < P;
-        }
-    }
-    const double us = (double)a.u_smp[b];
-    if (lane == 0 && !(us >= 0.0 && us < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-    if (row_bad) flags |= SPECDEC_ERR_NONFINITE;
-    const unsigned long long rej = __ballot(lane < k && !acc);
-    const int j = rej ? (__ffsll((long long)rej) - 1) : k;
-    if (lane < k && lane <= j && Q == 0.0 && !(flags & SPECDEC_ERR_TOKEN)) flags |= SPECDEC_ERR_QZERO;
-    // OR the flags over the wave
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
+constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
 
-    if (lane < k) {
-        if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
-        if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
-    }
-    const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
-    if (err) {
-        if (lane == 0) {
-            a.num_acc[b] = -1;
-            a.num_emit[b] = 0;
-            a.rec[b].mode = MODE_NONE;
-            atomicOr(a.err_word, flags);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
-        }
-        return;
-    }
-    if (lane < j) a.out_tokens[lo + b + lane] = y;
-    if (lane == 0) {
-        a.num_acc[b] = j;
-        a.num_emit[b] = j + 1;
-        SampleRec r;
-        r.mode = j < k ? MODE_RESID : MODE_BONUS;
-        r.row_t = lo + b + j;
-        r.row_d = j < k ? lo + j : 0;
-        r.out_pos = lo + b + j;
-        const float mt = s_m[j];
-        r.mc_t = mt * a.c;
-        r.al_t = exp2(-(double)fmaf(mt, a.c, -r.mc_t)) / s_S[j];
-        r.thr_t = s_thr[j];
-        if (j < k) {
-            const float md = s_m[k + 1 + j];
-            r.mc_d = md * a.c;
-            r.al_d = exp2(-(double)fmaf(md, a.c, -r.mc_d)) / s_S[k + 1 + j];
-            r.thr_d = s_thr[k + 1 + j];
-        } else {
-            r.mc_d = 0.f;
-            r.al_d = 0.0;
-            r.thr_d = INFINITY;
-        }
-        r.u = a.u_smp[b];
-        r.flags = flags;
-        r.pad0 = r.pad1 = 0;
-        a.rec[b] = r;
-        if (flags) atomicOr(a.err_word, flags);
-        if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Sampling weights and the inverse CDF.
-// ---------------------------------------------------------------------------------------
-// w(x) = max(0, p(x) - q(x)) for a replacement, p(x) for the bonus; p and q in fp64 from
-// fp32 exponentials of the same form the statistics used.
-SD_DEV double weight(float zt, float zd, const SampleRec& r, float c, bool resid) {
+// Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection, p(x) for the
+// bonus; p and q in fp64 from fp32 exponentials of the same form the statistics used.
+SD_DEV double weight(float zt, float zd, const Decision& r, float c, bool resid) {
     const double pt = zt >= r.thr_t
                           ? (double)__builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * r.al_t
                           : 0.0;
@@ -457,63 +333,267 @@ SD_DEV double weight(float zt, float zd, const SampleRec& r, float c, bool resid
     return fmax(pt - pd, 0.0);
 }
 
+// Eight consecutive elements starting at i0 (a multiple of 8); -inf at or past V.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kNT) void k_resid_part(const uint8_t* __restrict__ tgt,
-                                                    const uint8_t* __restrict__ dft, int V,
-                                                    int nchunks, float c,
-                                                    const SampleRec* __restrict__ rec,
-                                                    double* __restrict__ wpart) {
-    using Lt = Layout<BF16, VEC>;
-    __shared__ double redd[kNT / kWave];
-    const int b = blockIdx.x / nchunks;
-    const int chunk = blockIdx.x - b * nchunks;
-    const SampleRec r = rec[b];
-    if (r.mode == MODE_NONE) return;
-    const bool resid = r.mode == MODE_RESID;
-    float zt[Lt::EPT], zd[Lt::EPT];
-    load_chunk<BF16, VEC>(tgt + (size_t)r.row_t * V * Lt::ES, V, chunk * Lt::CH, zt);
-    if (resid) {
-        load_chunk<BF16, VEC>(dft + (size_t)r.row_d * V * Lt::ES, V, chunk * Lt::CH, zd);
+SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8]) {
+    if constexpr (VEC && BF16) {
+        if (i0 < V) {
+            const uint4 w = reinterpret_cast<const uint4*>(row)[i0 / 8];
+            const uint32_t q[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                z[2 * j] = bf16_lo(q[j]);
+                z[2 * j + 1] = bf16_hi(q[j]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
+        }
+    } else if constexpr (VEC) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (i0 + 4 * h < V) {
+                const uint4 w = reinterpret_cast<const uint4*>(row)[i0 / 4 + h];
+                z[4 * h] = __uint_as_float(w.x);
+                z[4 * h + 1] = __uint_as_float(w.y);
+                z[4 * h + 2] = __uint_as_float(w.z);
+                z[4 * h + 3] = __uint_as_float(w.w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[4 * h + j] = -INFINITY;
+            }
+        }
     } else {
 #pragma unroll
-        for (int i = 0; i < Lt::EPT; ++i) zd[i] = -INFINITY;
+        for (int j = 0; j < 8; ++j) z[j] = i0 + j < V ? load_elem(row, i0 + j, BF16) : -INFINITY;
     }
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 0; i < Lt::EPT; ++i) acc += weight(zt[i], zd[i], r, c, resid);
-    acc = block_sum<kNT>(acc, redd);
-    if (threadIdx.x == 0) wpart[blockIdx.x] = acc;
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kNT) void k_resid_pick(const uint8_t* __restrict__ tgt,
-                                                    const uint8_t* __restrict__ dft, int V,
-                                                    int nchunks, float c,
-                                                    SampleRec* __restrict__ rec,
-                                                    const double* __restrict__ wpart,
-                                                    int* __restrict__ out_tokens,
-                                                    int* __restrict__ err_word,
-                                                    double* __restrict__ dbg_mass,
-                                                    double* __restrict__ dbg_pick,
-                                                    int* __restrict__ dbg_flags) {
+__global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
     using Lt = Layout<BF16, VEC>;
+    __shared__ float s_m[kMaxRows];
+    __shared__ double s_S[kMaxRows];
+    __shared__ float s_thr[kMaxRows];
+    __shared__ int s_rowbad;
+    __shared__ Decision D;
     __shared__ double redd[kNT / kWave];
     __shared__ int redi[kNT / kWave];
     __shared__ double s_part[1024];
     __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_chunk;
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x;
-    SampleRec r = rec[b];
-    if (r.mode == MODE_NONE) return;
-    bool resid = r.mode == MODE_RESID;
+    __shared__ int s_chunk, s_last;
 
-    // chunk weights (recomputed here for the fallback, where W = 0 after a rejection)
-    for (int q = tid; q < nchunks; q += kNT) s_part[q] = wpart[(size_t)b * nchunks + q];
+    const int b = blockIdx.x / a.nchunks;
+    const int chunk = blockIdx.x - b * a.nchunks;
+    const bool publish = chunk == 0;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int rows_t = a.K + a.B;
+    const double cd = (double)a.c;
+
+    // ---- 1. decision ------------------------------------------------------------------
+    const int lo = a.cu[b], hi = a.cu[b + 1];
+    const int k = hi - lo;
+    const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
+                       hi > a.K;
+    if (bad_k) {
+        if (publish && tid == 0) {
+            a.num_acc[b] = -1;
+            a.num_emit[b] = 0;
+            atomicOr(a.err_word, SPECDEC_ERR_K);
+            if (a.dbg.req_flags) a.dbg.req_flags[b] = SPECDEC_ERR_K;
+        }
+        return;
+    }
+    if (tid == 0) s_rowbad = 0;
+    __syncthreads();
+    const int nrows = 2 * k + 1;   // <= kMaxRows <= kNT
+    if (tid < nrows) {
+        const int r = tid;
+        const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
+        const RowPartial* pp = a.part + (size_t)prow * a.nparts;
+        float m = -INFINITY;
+        double S = 0.0;
+        int nk = 0;
+        // batches of 8 partials: their loads are issued together
+        for (int q0 = 0; q0 < a.nparts; q0 += 8) {
+            RowPartial x[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (q0 + q < a.nparts) x[q] = pp[q0 + q];
+                else x[q] = RowPartial{-INFINITY, 0, 0.0};
+            }
+            float mb = -INFINITY;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) mb = fmaxf(mb, x[q].m);
+            const float mn = fmaxf(m, mb);
+            // rescale what was summed so far to the new max, then add this batch
+            if (m != -INFINITY && mn != m) S *= exp2((double)(m - mn) * cd);
+            m = mn;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                // chunks with no finite entry carry 0 (or NaN, which must propagate)
+                S += x[q].m == -INFINITY ? x[q].s : x[q].s * exp2((double)(x[q].m - m) * cd);
+                nk += x[q].nkept;
+            }
+        }
+        const float thr = a.topk ? a.row_thr[prow] : -INFINITY;
+        s_m[r] = m;
+        s_S[r] = S;
+        s_thr[r] = thr;
+        if (!(S > 0.0 && S < INFINITY && m > -INFINITY)) atomicOr(&s_rowbad, 1);
+        if (publish) {
+            if (a.dbg.row_max) a.dbg.row_max[prow] = m;
+            if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
+            if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
+            if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
+        }
+    }
+    __syncthreads();
+    if (tid < kWave) {
+        // lane i: proposal i (k <= SPECDEC_MAX_K = kWave)
+        int flags = 0;
+        bool acc = true;
+        double P = 0.0, Q = 0.0;
+        int y = 0;
+        if (lane < k) {
+            y = a.tokens[lo + lane];
+            const double u = (double)a.u_acc[lo + lane];
+            if (!(u >= 0.0 && u < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
+            if (y < 0 || y >= a.V) {
+                flags |= SPECDEC_ERR_TOKEN;
+            } else {
+                const float zt = load_elem(a.tgt + (size_t)(lo + b + lane) * a.V * Lt::ES, y, BF16);
+                const float zd = load_elem(a.dft + (size_t)(lo + lane) * a.V * Lt::ES, y, BF16);
+                const int rt = lane, rd = k + 1 + lane;
+                if (zt >= s_thr[rt] && zt > -INFINITY)
+                    P = exp2(((double)zt - (double)s_m[rt]) * cd) / s_S[rt];
+                if (zd >= s_thr[rd] && zd > -INFINITY)
+                    Q = exp2(((double)zd - (double)s_m[rd]) * cd) / s_S[rd];
+                acc = u * Q < P;
+            }
+        }
+        const double us = (double)a.u_smp[b];
+        if (lane == 0 && !(us >= 0.0 && us < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
+        if (lane == 0 && s_rowbad) flags |= SPECDEC_ERR_NONFINITE;
+        const unsigned long long rej = __ballot(lane < k && !acc);
+        const int j = rej ? (__ffsll((long long)rej) - 1) : k;
+        if (lane < k && lane <= j && Q == 0.0 && !(flags & SPECDEC_ERR_TOKEN)) flags |= SPECDEC_ERR_QZERO;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
+        const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
+        if (publish) {
+            if (lane < k) {
+                if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
+                if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
+            }
+            if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
+            if (lane == 0) {
+                a.num_acc[b] = err ? -1 : j;
+                a.num_emit[b] = err ? 0 : j + 1;
+                if (flags) atomicOr(a.err_word, flags);
+                if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
+            }
+        }
+        if (lane == 0) {
+            Decision d;
+            d.flags = flags;
+            d.err = err;
+            d.a = j;
+            d.k = k;
+            d.lo = lo;
+            d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
+            d.row_t = lo + b + j;
+            d.row_d = j < k ? lo + j : 0;
+            const float mt = s_m[j];
+            d.mc_t = mt * a.c;
+            d.al_t = exp2(-(double)fmaf(mt, a.c, -d.mc_t)) / s_S[j];
+            d.thr_t = s_thr[j];
+            if (j < k) {
+                const float md = s_m[k + 1 + j];
+                d.mc_d = md * a.c;
+                d.al_d = exp2(-(double)fmaf(md, a.c, -d.mc_d)) / s_S[k + 1 + j];
+                d.thr_d = s_thr[k + 1 + j];
+            } else {
+                d.mc_d = 0.f;
+                d.al_d = 0.0;
+                d.thr_d = INFINITY;
+            }
+            d.u = a.u_smp[b];
+            D = d;
+        }
+    }
+    __syncthreads();
+    if (D.mode == MODE_NONE) return;
+    Decision r = D;
+    bool resid = r.mode == MODE_RESID;
+    const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
+    const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
+
+    // ---- 2. weights of this chunk (coalesced strided layout) --------------------------
+    {
+        double acc = 0.0;
+        const int c0 = chunk * Lt::CH;
+        constexpr int HALF = Lt::COLS / 2;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float zt[HALF * Lt::PER], zd[HALF * Lt::PER];
+#pragma unroll
+            for (int cc = 0; cc < HALF; ++cc) {
+                const int i0 = c0 + ((h * HALF + cc) * kNT + tid) * Lt::PER;
+                if constexpr (VEC) {
+                    float t8[8], d8[8];
+                    // PER is 8 (bf16) or 4 (fp32) elements per 16-byte vector
+                    if constexpr (Lt::PER == 8) {
+                        load8<BF16, VEC>(trow, a.V, i0, t8);
+                        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            zt[cc * 8 + q] = t8[q];
+                            zd[cc * 8 + q] = resid ? d8[q] : -INFINITY;
+                        }
+                    } else {
+                        const uint4* tp = reinterpret_cast<const uint4*>(trow);
+                        const uint4* dp = reinterpret_cast<const uint4*>(drow);
+                        const bool in = i0 < a.V;
+                        const uint4 wt = in ? tp[i0 / 4] : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                        const uint4 wd = (in && resid) ? dp[i0 / 4] : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                        zt[cc * 4 + 0] = __uint_as_float(wt.x);
+                        zt[cc * 4 + 1] = __uint_as_float(wt.y);
+                        zt[cc * 4 + 2] = __uint_as_float(wt.z);
+                        zt[cc * 4 + 3] = __uint_as_float(wt.w);
+                        zd[cc * 4 + 0] = __uint_as_float(wd.x);
+                        zd[cc * 4 + 1] = __uint_as_float(wd.y);
+                        zd[cc * 4 + 2] = __uint_as_float(wd.z);
+                        zd[cc * 4 + 3] = __uint_as_float(wd.w);
+                    }
+                } else {
+                    zt[cc] = i0 < a.V ? load_elem(trow, i0, BF16) : -INFINITY;
+                    zd[cc] = (resid && i0 < a.V) ? load_elem(drow, i0, BF16) : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < HALF * Lt::PER; ++i) acc += weight(zt[i], zd[i], r, a.c, resid);
+        }
+        acc = block_sum<kNT>(acc, redd);
+        if (tid == 0) {
+            a.wpart[(size_t)b * a.nchunks + chunk] = acc;
+            __threadfence();
+            s_last = atomicAdd(&a.cnt[b], 1) == a.nchunks - 1;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+    }
+
+    // ---- 3. the last workgroup of the request draws the token -------------------------
+    for (int q = tid; q < a.nchunks; q += kNT)
+        s_part[q] = __hip_atomic_load(&a.wpart[(size_t)b * a.nchunks + q], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) a.cnt[b] = 0;   // ready for the next call
     __syncthreads();
     if (tid == 0) {
         double W = 0.0;
-        for (int q = 0; q < nchunks; ++q) W += s_part[q];
+        for (int q = 0; q < a.nchunks; ++q) W += s_part[q];
         s_W = W;
     }
     __syncthreads();
@@ -521,21 +601,23 @@ __global__ __launch_bounds__(kNT) void k_resid_pick(const uint8_t* __restrict__ 
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
-        for (int q = 0; q < nchunks; ++q) {
-            float zt[Lt::EPT];
-            load_chunk<BF16, VEC>(tgt + (size_t)r.row_t * V * Lt::ES, V, q * Lt::CH, zt);
+        for (int q = 0; q < a.nchunks; ++q) {
             double acc = 0.0;
+            for (int i0 = q * Lt::CH + tid * 8; i0 < (q + 1) * Lt::CH; i0 += kNT * 8) {
+                float z8[8];
+                load8<BF16, VEC>(trow, a.V, i0, z8);
 #pragma unroll
-            for (int i = 0; i < Lt::EPT; ++i) acc += weight(zt[i], -INFINITY, r, c, false);
+                for (int e = 0; e < 8; ++e) acc += weight(z8[e], -INFINITY, r, a.c, false);
+            }
             acc = block_sum<kNT>(acc, redd);
             if (tid == 0) s_part[q] = acc;
         }
         __syncthreads();
         if (tid == 0) {
             double W = 0.0;
-            for (int q = 0; q < nchunks; ++q) W += s_part[q];
+            for (int q = 0; q < a.nchunks; ++q) W += s_part[q];
             s_W = W;
-            atomicOr(err_word, SPECDEC_ERR_ZFALLBACK);
+            atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
         }
         __syncthreads();
     }
@@ -544,12 +626,12 @@ __global__ __launch_bounds__(kNT) void k_resid_pick(const uint8_t* __restrict__ 
     if (tid == 0) {
         double C = 0.0;
         int q = 0;
-        for (; q < nchunks; ++q) {
+        for (; q < a.nchunks; ++q) {
             if (C + s_part[q] > t) break;
             C += s_part[q];
         }
-        if (q == nchunks) {   // unreachable while t < W; keep the last non-empty chunk
-            q = nchunks - 1;
+        if (q == a.nchunks) {   // unreachable while t < W; keep the last non-empty chunk
+            q = a.nchunks - 1;
             while (q > 0 && !(s_part[q] > 0.0)) --q;
             C = 0.0;
             for (int i = 0; i < q; ++i) C += s_part[i];
@@ -558,60 +640,51 @@ __global__ __launch_bounds__(kNT) void k_resid_pick(const uint8_t* __restrict__ 
         s_base = C;
     }
     __syncthreads();
-    const int chunk = s_chunk;
-    const int c0 = chunk * Lt::CH;
-    float zt[Lt::EPT], zd[Lt::EPT];
-    load_chunk<BF16, VEC>(tgt + (size_t)r.row_t * V * Lt::ES, V, c0, zt);
-    if (resid) {
-        load_chunk<BF16, VEC>(dft + (size_t)r.row_d * V * Lt::ES, V, c0, zd);
+    // contiguous runs: thread tid scans elements [c0 + tid*EPT, c0 + (tid+1)*EPT)
+    const int e0 = s_chunk * Lt::CH + tid * Lt::EPT;
+    double run = 0.0;
+    for (int i0 = e0; i0 < e0 + Lt::EPT; i0 += 8) {
+        float t8[8], d8[8];
+        load8<BF16, VEC>(trow, a.V, i0, t8);
+        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) run += weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+    }
+    double tot;
+    double C = s_base + block_excl_scan_d<kNT>(run, redd, &tot);
+    int mine = 0x7fffffff, lastpos = -1;
+    double wmine = 0.0, wlast = 0.0;
+    for (int i0 = e0; i0 < e0 + Lt::EPT; i0 += 8) {
+        float t8[8], d8[8];
+        load8<BF16, VEC>(trow, a.V, i0, t8);
+        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double w = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+            C += w;
+            if (mine == 0x7fffffff && C > t) {
+                mine = i0 + e;
+                wmine = w;
+            }
+            if (w > 0.0) {
+                lastpos = i0 + e;
+                wlast = w;
+            }
+        }
+    }
+    int found = block_min_i<kNT>(mine, redi);
+    if (found != 0x7fffffff) {
+        if (mine == found) s_wpick = wmine;
     } else {
-#pragma unroll
-        for (int i = 0; i < Lt::EPT; ++i) zd[i] = -INFINITY;
-    }
-    double carry = s_base;
-    int found = 0x7fffffff;
-    int lastpos = -1;
-#pragma unroll
-    for (int col = 0; col < Lt::COLS; ++col) {
-        double w[Lt::PER], lp[Lt::PER];
-        double run = 0.0;
-#pragma unroll
-        for (int q = 0; q < Lt::PER; ++q) {
-            w[q] = weight(zt[col * Lt::PER + q], zd[col * Lt::PER + q], r, c, resid);
-            run += w[q];
-            lp[q] = run;
-        }
-        double coltot;
-        const double ex = block_excl_scan_d<kNT>(run, redd, &coltot);
-        const int i0 = c0 + (col * kNT + tid) * Lt::PER;
-        int mine = 0x7fffffff;
-#pragma unroll
-        for (int q = Lt::PER - 1; q >= 0; --q) {
-            if (carry + (ex + lp[q]) > t) mine = i0 + q;
-            if (w[q] > 0.0 && i0 + q > lastpos) lastpos = i0 + q;
-        }
-        found = block_min_i<kNT>(mine, redi);
-        if (found != 0x7fffffff) {
-            if (i0 <= found && found < i0 + Lt::PER) s_wpick = w[found - i0];
-            break;
-        }
-        carry += coltot;
-    }
-    if (found == 0x7fffffff) {
         found = block_max_i<kNT>(lastpos, redi);
-        if (found >= 0 && tid == 0) {
-            s_wpick = weight(load_elem(tgt + (size_t)r.row_t * V * Lt::ES, found, BF16),
-                             resid ? load_elem(dft + (size_t)r.row_d * V * Lt::ES, found, BF16)
-                                   : -INFINITY,
-                             r, c, resid);
-        }
+        if (found >= 0 && lastpos == found) s_wpick = wlast;
     }
     __syncthreads();
     if (tid == 0) {
-        out_tokens[r.out_pos] = found;
-        if (dbg_mass) dbg_mass[b] = W;
-        if (dbg_pick) dbg_pick[b] = s_wpick / W;
-        if (dbg_flags) dbg_flags[b] = r.flags;
+        a.out_tokens[lo + b + r.a] = found;
+        if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W;
+        if (a.dbg.picked_prob) a.dbg.picked_prob[b] = s_wpick / W;
+        if (a.dbg.req_flags) a.dbg.req_flags[b] = r.flags;
     }
 }
 
@@ -621,30 +694,26 @@ __global__ __launch_bounds__(kNT) void k_resid_pick(const uint8_t* __restrict__ 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, rec, wpart, thr, total;
+    size_t part, wpart, cnt, thr, total;
     int nparts, nchunks;
 };
-
-static int chunk_elems(int dtype, bool vec) {
-    if (dtype == SPECDEC_BF16) return vec ? Layout<true, true>::CH : Layout<true, false>::CH;
-    return vec ? Layout<false, true>::CH : Layout<false, false>::CH;
-}
 
 static bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
 
 static WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     WsPlan p{};
     // the vector and scalar layouts use the same chunk length
-    p.nchunks = (V + chunk_elems(dtype, true) - 1) / chunk_elems(dtype, true);
+    const int ch = dtype == SPECDEC_BF16 ? Layout<true, true>::CH : Layout<false, true>::CH;
+    p.nchunks = (V + ch - 1) / ch;
     p.nparts = topk_active(top_k, V) ? 1 : p.nchunks;
     const size_t rows = (size_t)2 * K + B;
     size_t off = 0;
     p.part = off;
     off = align256(off + rows * p.nparts * sizeof(RowPartial));
-    p.rec = off;
-    off = align256(off + (size_t)B * sizeof(SampleRec));
     p.wpart = off;
     off = align256(off + (size_t)B * p.nchunks * sizeof(double));
+    p.cnt = off;
+    off = align256(off + (size_t)B * sizeof(int));
     p.thr = off;
     off = align256(off + rows * sizeof(float));
     p.total = off;
@@ -653,29 +722,23 @@ static WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
 
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
-                       int top_k, float c, const WsPlan& p, uint8_t* ws, DecideArgs da,
+                       int top_k, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
                        const specdec_debug* dbg, hipStream_t st) {
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
     float* thr = reinterpret_cast<float*>(ws + p.thr);
-    if (dbg && dbg->ev_stats_begin) hipEventRecord(dbg->ev_stats_begin, st);
+    int* cnt = reinterpret_cast<int*>(ws + p.cnt);
+    // optional timing events are attached to the statistics launch itself
+    hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
+    hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
-        hipLaunchKernelGGL((k_topk_rows<BF16, VEC>), dim3(rows), dim3(kTopkNT), 0, st, tgt, dft,
-                           K + B, V, top_k, c, part, thr);
-    } else if (rows > 0) {
-        hipLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
-                           0, st, tgt, dft, K + B, V, p.nchunks, c, part);
+        hipExtLaunchKernelGGL((k_topk_rows<BF16, VEC>), dim3(rows), dim3(kTopkNT), 0, st, e0, e1, 0,
+                              tgt, dft, K + B, V, top_k, c, part, thr, B, cnt);
+    } else {
+        hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
+                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part, B, cnt);
     }
-    if (dbg && dbg->ev_stats_end) hipEventRecord(dbg->ev_stats_end, st);
-    hipLaunchKernelGGL(k_decide, dim3(B), dim3(kWave), 0, st, da);
-    SampleRec* rec = reinterpret_cast<SampleRec*>(ws + p.rec);
-    double* wpart = reinterpret_cast<double*>(ws + p.wpart);
-    hipLaunchKernelGGL((k_resid_part<BF16, VEC>), dim3((unsigned)B * p.nchunks), dim3(kNT), 0, st,
-                       tgt, dft, V, p.nchunks, c, rec, wpart);
-    hipLaunchKernelGGL((k_resid_pick<BF16, VEC>), dim3(B), dim3(kNT), 0, st, tgt, dft, V,
-                       p.nchunks, c, rec, wpart, da.out_tokens, da.err_word,
-                       dbg ? dbg->resid_mass : nullptr, dbg ? dbg->picked_prob : nullptr,
-                       dbg ? dbg->req_flags : nullptr);
+    hipLaunchKernelGGL((k_sample<BF16, VEC>), dim3((unsigned)B * p.nchunks), dim3(kNT), 0, st, sa);
 }
 
 }  // namespace sd
@@ -718,43 +781,42 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     const uint8_t* tgt = reinterpret_cast<const uint8_t*>(target_logits);
     const uint8_t* dft = reinterpret_cast<const uint8_t*>(K > 0 ? draft_logits : target_logits);
 
-    DecideArgs da;
-    da.tgt = tgt;
-    da.dft = dft;
-    da.bf16 = dtype == SPECDEC_BF16;
-    da.tokens = draft_tokens;
-    da.cu = cu_draft;
-    da.u_acc = u_accept;
-    da.u_smp = u_sample;
-    da.B = B;
-    da.K = K;
-    da.max_k = max_k;
-    da.V = V;
-    da.nparts = p.nparts;
-    da.topk = topk_active(top_k, V);
-    da.c = c;
-    da.part = reinterpret_cast<const RowPartial*>(ws + p.part);
-    da.row_thr = reinterpret_cast<const float*>(ws + p.thr);
-    da.out_tokens = out_tokens;
-    da.num_acc = num_accepted;
-    da.num_emit = num_emitted;
-    da.err_word = err_word;
-    da.rec = reinterpret_cast<SampleRec*>(ws + p.rec);
+    SampleArgs sa;
+    sa.tgt = tgt;
+    sa.dft = dft;
+    sa.tokens = draft_tokens;
+    sa.cu = cu_draft;
+    sa.u_acc = u_accept;
+    sa.u_smp = u_sample;
+    sa.B = B;
+    sa.K = K;
+    sa.max_k = max_k;
+    sa.V = V;
+    sa.nparts = p.nparts;
+    sa.nchunks = p.nchunks;
+    sa.topk = topk_active(top_k, V);
+    sa.c = c;
+    sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
+    sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
+    sa.wpart = reinterpret_cast<double*>(ws + p.wpart);
+    sa.cnt = reinterpret_cast<int*>(ws + p.cnt);
+    sa.out_tokens = out_tokens;
+    sa.num_acc = num_accepted;
+    sa.num_emit = num_emitted;
+    sa.err_word = err_word;
     if (dbg) {
-        da.dbg = *dbg;
+        sa.dbg = *dbg;
     } else {
-        da.dbg = specdec_debug{};
+        sa.dbg = specdec_debug{};
     }
-    // the sampling kernel reports flags itself
-    da.dbg.req_flags = dbg ? dbg->req_flags : nullptr;
 
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_k, c, p, ws, da, dbg, stream);
-        else launch_all<true, false>(tgt, dft, B, K, V, top_k, c, p, ws, da, dbg, stream);
+        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
+        else launch_all<true, false>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
     } else {
-        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_k, c, p, ws, da, dbg, stream);
-        else launch_all<false, false>(tgt, dft, B, K, V, top_k, c, p, ws, da, dbg, stream);
+        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
+        else launch_all<false, false>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }
