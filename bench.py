@@ -37,6 +37,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--schedule", choices=["serial", "overlap"], default="overlap",
+                   help="serial: append, verify, rollback on one stream; overlap: the K/V "
+                        "scatter runs on a second stream once the logit rows are streamed, "
+                        "beside the sampling kernel")
+    p.add_argument("--timing-every", type=int, default=4,
+                   help="attach HIP timing events to the row-statistics launch of every "
+                        "n-th step (they add a few microseconds to those steps)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time the oracle baseline runs for")
@@ -138,18 +145,36 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
     ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
-    kws = torch.empty(binding.kv_paged_append_workspace_size(B), dtype=torch.uint8, device=d)
+    kws = torch.empty(binding.kv_paged_append_workspace_size(B, K + B), dtype=torch.uint8, device=d)
     n = args.warmup + args.steps
-    evs = [(binding.HipEvent(), binding.HipEvent()) for _ in range(n)]
+    timed = [i for i in range(args.warmup, n) if (i - args.warmup) % max(args.timing_every, 1) == 0]
+    evs = {i: (binding.HipEvent(), binding.HipEvent()) for i in timed}
+    main_s = torch.cuda.current_stream(d)
+    side_s = torch.cuda.Stream(d)                      # default priority
+    ev_stats = [binding.HipEvent(timing=False) for _ in range(n)]
+    ev_kv = [binding.HipEvent(timing=False) for _ in range(n)]
 
     def step(i):
         dbg = binding.SpecdecDebug()
-        dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
-        binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
-        binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
-                               temperature=vin.T, top_k=vin.top_k, out_tokens=out,
-                               num_accepted=nacc, num_emitted=nemit, err_word=err,
-                               workspace=ws, debug=dbg)
+        if i in evs:
+            dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
+        if args.schedule == "serial":
+            binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
+            binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
+                                   temperature=vin.T, top_k=vin.top_k, out_tokens=out,
+                                   num_accepted=nacc, num_emitted=nemit, err_word=err,
+                                   workspace=ws, debug=dbg)
+        else:
+            dbg.ev_stats_done = ev_stats[i].handle
+            binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
+                                   temperature=vin.T, top_k=vin.top_k, out_tokens=out,
+                                   num_accepted=nacc, num_emitted=nemit, err_word=err,
+                                   workspace=ws, debug=dbg)
+            ev_stats[i].wait_on(side_s)
+            with torch.cuda.stream(side_s):
+                binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
+            ev_kv[i].record(side_s)
+            ev_kv[i].wait_on(main_s)
         binding.kv_rollback(cache, nacc, cu)
 
     for i in range(args.warmup):
@@ -165,7 +190,7 @@ def main():
         print(f"# warning: cache state word {st:#x}", file=sys.stderr)
     if int(err.item()) & (binding.ERR_TOKEN | binding.ERR_K | binding.ERR_NONFINITE | binding.ERR_UNIFORM):
         print(f"# warning: verify error word {int(err.item()):#x}", file=sys.stderr)
-    stats_ms = [evs[i][0].elapsed_ms(evs[i][1]) for i in range(args.warmup, n)]
+    stats_ms = [evs[i][0].elapsed_ms(evs[i][1]) for i in timed]
     stats_avg_s = float(np.mean(stats_ms)) / 1e3
     ms_per_step = elapsed / args.steps * 1e3
     es = 2 if vin.dtype == "bf16" else 4
@@ -193,7 +218,8 @@ def main():
         "config": {"workload": (f"{wl.name}: B={B} k={'U{%d..%d}' % wl.k_range if wl.k_range else wl.k} "
                                 f"V={V} {vin.dtype} T={vin.T:g} top_k={vin.top_k}; paged KV "
                                 f"{kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
-                   "global_batch": B, "positions_per_step": K, "parallelism": "single GPU"},
+                   "global_batch": B, "positions_per_step": K, "parallelism": "single GPU",
+                   "schedule": args.schedule},
         "achieved_hbm_gbps": cycle_gbps,
         "pct_peak_hbm": 100.0 * cycle_gbps / PEAK_GBPS,
         "cycle_bytes": cycle_bytes,

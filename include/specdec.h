@@ -80,21 +80,26 @@ const char* specdec_status_string(int status);
  * Verification
  * ===================================================================================== */
 
-/* Optional per-call diagnostics; any field may be NULL / 0. Row arrays are indexed with
- * the target rows first (0 .. K+B-1) and then the draft rows (K+B .. 2K+B-1). */
+/* Optional per-call diagnostics and scheduling hooks; any field may be NULL / 0. Row
+ * arrays are indexed with the target rows first (0 .. K+B-1) and then the draft rows
+ * (K+B .. 2K+B-1). */
 typedef struct specdec_debug {
     double*  p_y;          /* [K]  p_i(y_i) after the transform                           */
     double*  q_y;          /* [K]  q_i(y_i)                                               */
     float*   row_max;      /* [2K+B] max kept logit of the row                            */
     double*  row_sum;      /* [2K+B] S = sum over kept x of exp((z(x) - max) / T)         */
     float*   row_thr;      /* [2K+B] top-k threshold logit (-inf when top-k is off)       */
-    int32_t* row_nkept;    /* [2K+B] kept tokens with finite logit                        */
+    int32_t* row_nkept;    /* [2K+B] kept tokens with finite logit (-1 when top-k is off) */
     double*  resid_mass;   /* [B]  W the final token was drawn from: residual mass, or
                                    sum of p for the bonus                                  */
     double*  picked_prob;  /* [B]  w(x*) / W                                               */
     int32_t* req_flags;    /* [B]  SPECDEC_ERR_* bits of the request                       */
-    hipEvent_t ev_stats_begin;  /* recorded on `stream` right before / after the kernel  */
-    hipEvent_t ev_stats_end;    /* that streams the logit rows (for timing)              */
+    hipEvent_t ev_stats_begin;  /* timing events attached to the launch of the kernel    */
+    hipEvent_t ev_stats_end;    /* that streams the logit rows (both or neither)         */
+    hipEvent_t ev_stats_done;   /* recorded on `stream` once the logit rows have been
+                                   streamed: independent bandwidth-bound work (the K/V
+                                   scatter) can start on another stream while the
+                                   latency-bound sampling kernel runs                     */
 } specdec_debug;
 
 /* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned). */
@@ -177,8 +182,8 @@ typedef struct kv_paged_cache {
     int32_t* state;           /* [1] KV_ERR_* sticky bits and KV_APPEND_REJECTED       */
 } kv_paged_cache;
 
-/* Bytes of device workspace kv_paged_append needs for a batch of B requests. */
-size_t kv_paged_append_workspace_size(int32_t B);
+/* Bytes of device workspace kv_paged_append needs for B requests and N new entries. */
+size_t kv_paged_append_workspace_size(int32_t B, int32_t N);
 
 /*
  * kv_paged_append - provisional append of n_b = cu_new[b+1] - cu_new[b] entries per
@@ -195,7 +200,8 @@ size_t kv_paged_append_workspace_size(int32_t B);
  * capacity MBR * block_size exceeded, no block for a partial tail), no request changes
  * and KV_APPEND_REJECTED is set; a successful append clears KV_APPEND_REJECTED.
  * Host checks: 1 <= B <= SPECDEC_MAX_KV_BATCH, N >= 0, pointers non-NULL, geometry > 0.
- * workspace: device, 16-byte aligned, >= kv_paged_append_workspace_size(B) bytes.
+ * workspace: device, 16-byte aligned, >= kv_paged_append_workspace_size(B, N) bytes;
+ * scratch between calls, no initialization needed; calls sharing it must not overlap.
  */
 int kv_paged_append(const kv_paged_cache* cache, int32_t B,
                     const void* k_new, const void* v_new, const int32_t* cu_new, int32_t N,

@@ -59,6 +59,7 @@ class SpecdecDebug(ctypes.Structure):
         ("resid_mass", ctypes.c_void_p), ("picked_prob", ctypes.c_void_p),
         ("req_flags", ctypes.c_void_p),
         ("ev_stats_begin", ctypes.c_void_p), ("ev_stats_end", ctypes.c_void_p),
+        ("ev_stats_done", ctypes.c_void_p),
     ]
 
 
@@ -95,7 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    ctypes.c_float, i32, vp, vp, vp, vp,
                                    ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_verify.restype = ctypes.c_int
-    lib.kv_paged_append_workspace_size.argtypes = [i32]
+    lib.kv_paged_append_workspace_size.argtypes = [i32, i32]
     lib.kv_paged_append_workspace_size.restype = sz
     lib.kv_paged_append.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32,
                                     vp, sz, vp]
@@ -210,8 +211,8 @@ class PagedKVCache:
             free_list.data_ptr(), free_count.data_ptr(), state.data_ptr())
 
 
-def kv_paged_append_workspace_size(B: int) -> int:
-    return int(load_library().kv_paged_append_workspace_size(B))
+def kv_paged_append_workspace_size(B: int, N: int) -> int:
+    return int(load_library().kv_paged_append_workspace_size(B, N))
 
 
 def kv_paged_append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -248,7 +249,7 @@ def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch
         raise SpecdecError("kv_rollback", st)
 
 
-# --- HIP events through the runtime (for timing the row-statistics kernel) -------------
+# --- HIP events and stream waits through the runtime (timing, cross-stream ordering) -----
 
 _hip = None
 
@@ -257,19 +258,33 @@ def _hip_rt() -> ctypes.CDLL:
     global _hip
     if _hip is None:
         _hip = ctypes.CDLL("libamdhip64.so")
-        _hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                              ctypes.c_void_p]
     return _hip
 
 
 class HipEvent:
-    def __init__(self):
+    """A hipEvent_t; timing=False creates a synchronization-only event."""
+
+    def __init__(self, timing: bool = True):
         self.handle = ctypes.c_void_p()
-        if _hip_rt().hipEventCreate(ctypes.byref(self.handle)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        flags = 0 if timing else 0x2   # hipEventDisableTiming
+        if _hip_rt().hipEventCreateWithFlags(ctypes.byref(self.handle), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream: "torch.cuda.Stream") -> None:
+        if _hip_rt().hipEventRecord(self.handle, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def wait_on(self, stream: "torch.cuda.Stream") -> None:
+        """Make `stream` wait until this event has completed."""
+        if _hip_rt().hipStreamWaitEvent(ctypes.c_void_p(stream.cuda_stream), self.handle, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
 
     def elapsed_ms(self, end: "HipEvent") -> float:
         rt = _hip_rt()

@@ -34,7 +34,7 @@ namespace sd {
 constexpr int kKvNT = 1024;      // single-workgroup bookkeeping kernels
 constexpr int kKvRPT = SPECDEC_MAX_KV_BATCH / kKvNT;   // requests per thread
 constexpr int kScNT = 256;       // scatter workgroup
-constexpr int kScTok = 8;        // tokens per scatter workgroup
+constexpr int kScMaxTok = 16;    // tokens per scatter workgroup (for small rows)
 constexpr int kEvCap = 2048;     // rollback events per window
 constexpr int kEvPT = kEvCap / kKvNT;
 
@@ -53,7 +53,8 @@ struct KvArgs {
 // for the scatter (stored from the front of the entry array), [2] entries whose source
 // block another request writes in place in the same batch (stored from the back; copied
 // by k_kv_alloc itself so the copy reads before the scatter writes), [3] unused, then
-// B entries (src block, dst block, slots, b).
+// B entries (src block, dst block, slots, b), then N int64 destination rows (physical
+// block * block_size + slot) of the new entries, -1 where the block id is corrupt.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct CowEntry {
@@ -191,12 +192,22 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
                 atomicOr(a.state, KV_ERR_APPEND);    // corrupt free list
             }
         }
+        const int lb_first = ceil_div(s[i], a.bs);
         const int lb_end = ceil_div(s[i] + n[i], a.bs);
-        for (int lb = ceil_div(s[i], a.bs); lb < lb_end; ++lb) {
+        for (int lb = lb_first; lb < lb_end; ++lb) {
             const int nb = a.free_list[fc - 1 - p++];
             tab[lb] = nb;
             if ((unsigned)nb < (unsigned)a.NB) a.refcount[nb] = 1;
             else atomicOr(a.state, KV_ERR_APPEND);  // corrupt free list
+        }
+        // destination rows of the request's new entries, read by the scatter
+        long long* drow = reinterpret_cast<long long*>(ws + 4 + 4 * B);
+        const int part_blk = (s[i] % a.bs != 0) ? tab[s[i] / a.bs] : -1;
+        for (int t = 0; t < n[i]; ++t) {
+            const int pos = s[i] + t;
+            const int lb = pos / a.bs;
+            const int blk = (lb < lb_first) ? part_blk : a.free_list[fc - 1 - (base[i] + cow[i] + (lb - lb_first))];
+            drow[cu_new[b] + t] = (unsigned)blk < (unsigned)a.NB ? (long long)blk * a.bs + pos % a.bs : -1;
         }
         a.seq_lens[b] = s[i] + n[i];
     }
@@ -216,44 +227,28 @@ __global__ __launch_bounds__(kKvNT) void k_kv_alloc(KvArgs a, const int* __restr
     }
 }
 
+// tpw tokens per workgroup (tpw * lanes <= kScNT when a token row is small); each thread
+// moves 16-byte pieces of token rows, reading the destination row the alloc kernel wrote.
 __global__ __launch_bounds__(kScNT) void k_kv_scatter(KvArgs a, const uint8_t* __restrict__ knew,
-                                                      const uint8_t* __restrict__ vnew,
-                                                      const int* __restrict__ cu_new, int B,
-                                                      int N, const int* __restrict__ ws) {
-    __shared__ long long s_dst[kScTok];
+                                                      const uint8_t* __restrict__ vnew, int B, int N,
+                                                      int tpw, const int* __restrict__ ws) {
     if (ws[0] != 0) return;
     const int tid = threadIdx.x;
     const int lk = blockIdx.y;                 // layer * 2 + (0: K, 1: V)
     const int l = lk >> 1;
     const size_t ub = (size_t)a.H * a.D * 2;   // bytes of one token's row
     const int lanes = (int)(ub / 16);
-    const int t0 = blockIdx.x * kScTok;
-    if (tid < kScTok) {
-        const int t = t0 + tid;
-        long long d = -1;
-        if (t < N) {
-            int lo = 0, hi = B;                // largest b with cu_new[b] <= t
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (cu_new[mid] <= t) lo = mid;
-                else hi = mid;
-            }
-            const int b = lo;
-            const int nb = cu_new[b + 1] - cu_new[b];
-            const int pos = a.seq_lens[b] - nb + (t - cu_new[b]);
-            const int blk = a.tables[(size_t)b * a.MBR + pos / a.bs];
-            if ((unsigned)blk < (unsigned)a.NB) d = (long long)blk * a.bs + pos % a.bs;
-        }
-        s_dst[tid] = d;
-    }
-    __syncthreads();
+    const int t0 = blockIdx.x * tpw;
+    const long long* drow = reinterpret_cast<const long long*>(ws + 4 + 4 * B);
     const uint8_t* src_base = (lk & 1) ? vnew : knew;
     uint8_t* dst_base = a.pool + (size_t)lk * a.NB * a.bs * ub;
-    for (int idx = tid; idx < kScTok * lanes; idx += kScNT) {
+    for (int idx = tid; idx < tpw * lanes; idx += kScNT) {
         const int tok = idx / lanes, q = idx - tok * lanes;
-        const long long d = s_dst[tok];
+        const int t = t0 + tok;
+        if (t >= N) break;
+        const long long d = drow[t];
         if (d < 0) continue;
-        const u32x4* src = reinterpret_cast<const u32x4*>(src_base + ((size_t)l * N + t0 + tok) * ub) + q;
+        const u32x4* src = reinterpret_cast<const u32x4*>(src_base + ((size_t)l * N + t) * ub) + q;
         u32x4* dst = reinterpret_cast<u32x4*>(dst_base + (size_t)d * ub) + q;
         __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
     }
@@ -437,9 +432,9 @@ static KvArgs args_of(const kv_paged_cache* c) {
 
 }  // namespace sd
 
-extern "C" size_t kv_paged_append_workspace_size(int32_t B) {
-    if (B < 1) return 0;
-    return 16 + (size_t)B * sizeof(sd::CowEntry);
+extern "C" size_t kv_paged_append_workspace_size(int32_t B, int32_t N) {
+    if (B < 1 || N < 0) return 0;
+    return 16 + (size_t)B * sizeof(sd::CowEntry) + (size_t)N * sizeof(long long);
 }
 
 extern "C" int kv_paged_append(const kv_paged_cache* cache, int32_t B, const void* k_new,
@@ -450,17 +445,20 @@ extern "C" int kv_paged_append(const kv_paged_cache* cache, int32_t B, const voi
         return SPECDEC_EINVAL;
     if (N > 0 && (!k_new || !v_new || ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15)))
         return SPECDEC_EINVAL;
-    if (!workspace || workspace_bytes < kv_paged_append_workspace_size(B) ||
+    if (!workspace || workspace_bytes < kv_paged_append_workspace_size(B, N) ||
         ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;
     const KvArgs a = args_of(cache);
     int* ws = reinterpret_cast<int*>(workspace);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_kv_alloc, dim3(1), dim3(kKvNT), 0, stream, a, cu_new, B, N, ws);
-    const unsigned tiles = (unsigned)((N + kScTok - 1) / kScTok);
-    hipLaunchKernelGGL(k_kv_scatter, dim3(tiles > 0 ? tiles : 1, (unsigned)a.L * 2), dim3(kScNT),
-                       0, stream, a, reinterpret_cast<const uint8_t*>(k_new),
-                       reinterpret_cast<const uint8_t*>(v_new), cu_new, B, N, ws);
+    const int lanes = (int)((size_t)a.H * a.D * 2 / 16);
+    const int tpw = lanes >= kScNT ? 1 : min(kScMaxTok, kScNT / lanes);
+    const unsigned tiles = (unsigned)((N + tpw - 1) / tpw);
+    if (tiles > 0)
+        hipLaunchKernelGGL(k_kv_scatter, dim3(tiles, (unsigned)a.L * 2), dim3(kScNT), 0, stream, a,
+                           reinterpret_cast<const uint8_t*>(k_new),
+                           reinterpret_cast<const uint8_t*>(v_new), B, N, tpw, ws);
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }
 

@@ -32,6 +32,8 @@
 
 namespace sd {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kNT = 256;        // threads per workgroup of the streaming kernels
 constexpr int kVPT = 8;         // 16-byte vectors per thread per chunk
 constexpr int kTopkNT = 1024;   // threads per workgroup of the top-k row kernel
@@ -68,16 +70,17 @@ SD_DEV void load_chunk(const uint8_t* __restrict__ row, int V, int c0,
     using Lt = Layout<BF16, VEC>;
     const int tid = threadIdx.x;
     if constexpr (VEC) {
-        const uint4* p = reinterpret_cast<const uint4*>(row);
-        uint4 raw[Lt::COLS];
+        // streamed once: non-temporal loads keep the rows from displacing other lines
+        const u32x4* p = reinterpret_cast<const u32x4*>(row);
+        u32x4 raw[Lt::COLS];
+        const uint32_t fill = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
         for (int col = 0; col < Lt::COLS; ++col) {
             const int i0 = c0 + (col * kNT + tid) * Lt::PER;
             if (i0 < V) {
-                raw[col] = p[i0 / Lt::EPV];
+                raw[col] = __builtin_nontemporal_load(p + i0 / Lt::EPV);
             } else {
-                raw[col] = BF16 ? make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u)
-                                : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                raw[col] = (u32x4){fill, fill, fill, fill};
             }
         }
 #pragma unroll
@@ -124,15 +127,13 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ tgt,
                                                    const uint8_t* __restrict__ dft,
                                                    int rows_t, int V, int nchunks, float c,
-                                                   RowPartial* __restrict__ part, int B,
-                                                   int* __restrict__ cnt) {
+                                                   RowPartial* __restrict__ part) {
     using Lt = Layout<BF16, VEC>;
     __shared__ float redf[kNT / kWave];
     __shared__ double redd[kNT / kWave];
     __shared__ int redi[kNT / kWave];
     const int row = blockIdx.x / nchunks;
     const int chunk = blockIdx.x - row * nchunks;
-    if (chunk == 0 && row < B && threadIdx.x == 0) cnt[row] = 0;   // sampling counters
     const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, Lt::ES);
     float z[Lt::EPT];
     load_chunk<BF16, VEC>(base, V, chunk * Lt::CH, z);
@@ -194,8 +195,7 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
                                                        const uint8_t* __restrict__ dft,
                                                        int rows_t, int V, int top_k, float c,
                                                        RowPartial* __restrict__ part,
-                                                       float* __restrict__ row_thr, int B,
-                                                       int* __restrict__ cnt) {
+                                                       float* __restrict__ row_thr) {
     constexpr int NT = kTopkNT;
     constexpr int ES = BF16 ? 2 : 4;
     __shared__ unsigned hist[256];
@@ -207,7 +207,6 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
     const int row = blockIdx.x;
     const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, ES);
     const int tid = threadIdx.x;
-    if (row < B && tid == 0) cnt[row] = 0;   // sampling counters
 
     // pass 0: max, invalid entries (NaN, +inf)
     float mx = -INFINITY;
@@ -279,15 +278,22 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------------------
-// Decision and sampling, fused: one kernel over (request, chunk) workgroups.
-//   1. every workgroup of request b re-derives b's decision from the row partials (cheap:
-//      2k+1 rows x a few partials, k fp64 exponentials) so no separate launch is needed;
-//      the chunk-0 workgroup publishes the outputs;
-//   2. each workgroup sums the sampling weights of its chunk of the row(s) still to be
-//      sampled (rows after the first rejection are never touched);
-//   3. the last workgroup of the request to finish (device-scope counter) turns the chunk
-//      sums into W, finds the chunk holding t = u * W and scans it in ascending token order.
+// Decision and sampling, fused: one workgroup of 1024 threads per request.
+//   1. combine the row partials in fp64, evaluate p_i(y_i), q_i(y_i) and the accept test
+//      left to right, find the first rejection, publish the accepted tokens;
+//   2. stream the one row pair (or bonus row) still to be sampled in 8192-element chunks
+//      (four chunks in flight per thread) and keep per-chunk weight sums in LDS;
+//   3. W = sum of the chunk sums, t = u * W, locate the chunk holding t and scan it in
+//      ascending token order (each thread owns 8 consecutive tokens) for the smallest x
+//      with C(x) > t.
+// Nothing crosses workgroups, so no device-scope fence is needed; rows after the first
+// rejection are never read.
 // ---------------------------------------------------------------------------------------
+constexpr int kSNT = 1024;                 // threads of the sampling workgroup
+constexpr int kSW = kSNT / kWave;          // its waves
+constexpr int kSChunk = kSNT * 8;          // tokens per sampling chunk
+constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
+
 struct SampleArgs {
     const uint8_t* tgt;
     const uint8_t* dft;
@@ -297,13 +303,10 @@ struct SampleArgs {
     const float* u_smp;
     int B, K, max_k, V;
     int nparts;              // statistics partials per row
-    int nchunks;             // sampling chunks per row
     int topk;                // 1 when rows carry a top-k threshold
     float c;
     const RowPartial* part;
     const float* row_thr;
-    double* wpart;           // [B][nchunks] chunk sums of the weights
-    int* cnt;                // [B] finished chunks (zeroed by the statistics kernel)
     int* out_tokens;
     int* num_acc;
     int* num_emit;
@@ -312,7 +315,7 @@ struct SampleArgs {
 };
 
 struct Decision {
-    int flags, err, a, k, lo, mode, row_t, row_d;
+    int flags, err, a, k, mode, row_t, row_d, pad;
     float mc_t, mc_d, thr_t, thr_d;
     double al_t, al_d;
     float u;
@@ -338,7 +341,7 @@ template <bool BF16, bool VEC>
 SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8]) {
     if constexpr (VEC && BF16) {
         if (i0 < V) {
-            const uint4 w = reinterpret_cast<const uint4*>(row)[i0 / 8];
+            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 8);
             const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -353,7 +356,7 @@ SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8])
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             if (i0 + 4 * h < V) {
-                const uint4 w = reinterpret_cast<const uint4*>(row)[i0 / 4 + h];
+                const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 4 + h);
                 z[4 * h] = __uint_as_float(w.x);
                 z[4 * h + 1] = __uint_as_float(w.y);
                 z[4 * h + 2] = __uint_as_float(w.z);
@@ -369,23 +372,57 @@ SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8])
     }
 }
 
+// Per-chunk weight sums of the row (pair) into s_cs[0 .. nch): wave sums in LDS, then a
+// fixed-order sum over the 16 waves.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
+SD_DEV void chunk_sums(const uint8_t* trow, const uint8_t* drow, int V, int nch,
+                       const Decision& r, float c, bool resid, double (*s_wp)[kSW],
+                       double* s_cs) {
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    for (int c0 = 0; c0 < nch; c0 += 4) {
+        float zt[4][8], zd[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i0 = (c0 + u) * kSChunk + tid * 8;
+            load8<BF16, VEC>(trow, (c0 + u) < nch ? V : 0, i0, zt[u]);
+            if (resid) load8<BF16, VEC>(drow, (c0 + u) < nch ? V : 0, i0, zd[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            double acc = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc += weight(zt[u][e], resid ? zd[u][e] : -INFINITY, r, c, resid);
+            acc = wave_sum(acc);
+            if (lane == 0 && c0 + u < nch) s_wp[c0 + u][wave] = acc;
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < nch; q += kSNT) {
+        double x = 0.0;
+#pragma unroll
+        for (int w = 0; w < kSW; ++w) x += s_wp[q][w];
+        s_cs[q] = x;
+    }
+    __syncthreads();
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kSNT) void k_sample(SampleArgs a) {
     using Lt = Layout<BF16, VEC>;
     __shared__ float s_m[kMaxRows];
     __shared__ double s_S[kMaxRows];
     __shared__ float s_thr[kMaxRows];
     __shared__ int s_rowbad;
     __shared__ Decision D;
-    __shared__ double redd[kNT / kWave];
-    __shared__ int redi[kNT / kWave];
-    __shared__ double s_part[1024];
+    __shared__ double redd[kSW];
+    __shared__ int redi[kSW];
+    __shared__ double s_wp[kSMaxChunks][kSW];
+    __shared__ double s_cs[kSMaxChunks];
     __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_chunk, s_last;
+    __shared__ int s_chunk;
 
-    const int b = blockIdx.x / a.nchunks;
-    const int chunk = blockIdx.x - b * a.nchunks;
-    const bool publish = chunk == 0;
+    const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid % kWave;
     const int rows_t = a.K + a.B;
     const double cd = (double)a.c;
@@ -396,7 +433,7 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
     const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
                        hi > a.K;
     if (bad_k) {
-        if (publish && tid == 0) {
+        if (tid == 0) {
             a.num_acc[b] = -1;
             a.num_emit[b] = 0;
             atomicOr(a.err_word, SPECDEC_ERR_K);
@@ -406,7 +443,7 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
     }
     if (tid == 0) s_rowbad = 0;
     __syncthreads();
-    const int nrows = 2 * k + 1;   // <= kMaxRows <= kNT
+    const int nrows = 2 * k + 1;   // <= kMaxRows <= kSNT
     if (tid < nrows) {
         const int r = tid;
         const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
@@ -441,12 +478,10 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
         s_S[r] = S;
         s_thr[r] = thr;
         if (!(S > 0.0 && S < INFINITY && m > -INFINITY)) atomicOr(&s_rowbad, 1);
-        if (publish) {
-            if (a.dbg.row_max) a.dbg.row_max[prow] = m;
-            if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
-            if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
-            if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
-        }
+        if (a.dbg.row_max) a.dbg.row_max[prow] = m;
+        if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
+        if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
+        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
     }
     __syncthreads();
     if (tid < kWave) {
@@ -481,26 +516,22 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
         const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
-        if (publish) {
-            if (lane < k) {
-                if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
-                if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
-            }
-            if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
-            if (lane == 0) {
-                a.num_acc[b] = err ? -1 : j;
-                a.num_emit[b] = err ? 0 : j + 1;
-                if (flags) atomicOr(a.err_word, flags);
-                if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
-            }
+        if (lane < k) {
+            if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
+            if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
         }
+        if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
         if (lane == 0) {
+            a.num_acc[b] = err ? -1 : j;
+            a.num_emit[b] = err ? 0 : j + 1;
+            if (flags) atomicOr(a.err_word, flags);
+            if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
             Decision d;
             d.flags = flags;
             d.err = err;
             d.a = j;
             d.k = k;
-            d.lo = lo;
+            d.pad = 0;
             d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
             d.row_t = lo + b + j;
             d.row_d = j < k ? lo + j : 0;
@@ -528,72 +559,13 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
     bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
+    const int nch = (a.V + kSChunk - 1) / kSChunk;
 
-    // ---- 2. weights of this chunk (coalesced strided layout) --------------------------
-    {
-        double acc = 0.0;
-        const int c0 = chunk * Lt::CH;
-        constexpr int HALF = Lt::COLS / 2;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float zt[HALF * Lt::PER], zd[HALF * Lt::PER];
-#pragma unroll
-            for (int cc = 0; cc < HALF; ++cc) {
-                const int i0 = c0 + ((h * HALF + cc) * kNT + tid) * Lt::PER;
-                if constexpr (VEC) {
-                    float t8[8], d8[8];
-                    // PER is 8 (bf16) or 4 (fp32) elements per 16-byte vector
-                    if constexpr (Lt::PER == 8) {
-                        load8<BF16, VEC>(trow, a.V, i0, t8);
-                        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            zt[cc * 8 + q] = t8[q];
-                            zd[cc * 8 + q] = resid ? d8[q] : -INFINITY;
-                        }
-                    } else {
-                        const uint4* tp = reinterpret_cast<const uint4*>(trow);
-                        const uint4* dp = reinterpret_cast<const uint4*>(drow);
-                        const bool in = i0 < a.V;
-                        const uint4 wt = in ? tp[i0 / 4] : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-                        const uint4 wd = (in && resid) ? dp[i0 / 4] : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-                        zt[cc * 4 + 0] = __uint_as_float(wt.x);
-                        zt[cc * 4 + 1] = __uint_as_float(wt.y);
-                        zt[cc * 4 + 2] = __uint_as_float(wt.z);
-                        zt[cc * 4 + 3] = __uint_as_float(wt.w);
-                        zd[cc * 4 + 0] = __uint_as_float(wd.x);
-                        zd[cc * 4 + 1] = __uint_as_float(wd.y);
-                        zd[cc * 4 + 2] = __uint_as_float(wd.z);
-                        zd[cc * 4 + 3] = __uint_as_float(wd.w);
-                    }
-                } else {
-                    zt[cc] = i0 < a.V ? load_elem(trow, i0, BF16) : -INFINITY;
-                    zd[cc] = (resid && i0 < a.V) ? load_elem(drow, i0, BF16) : -INFINITY;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < HALF * Lt::PER; ++i) acc += weight(zt[i], zd[i], r, a.c, resid);
-        }
-        acc = block_sum<kNT>(acc, redd);
-        if (tid == 0) {
-            a.wpart[(size_t)b * a.nchunks + chunk] = acc;
-            __threadfence();
-            s_last = atomicAdd(&a.cnt[b], 1) == a.nchunks - 1;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-    }
-
-    // ---- 3. the last workgroup of the request draws the token -------------------------
-    for (int q = tid; q < a.nchunks; q += kNT)
-        s_part[q] = __hip_atomic_load(&a.wpart[(size_t)b * a.nchunks + q], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    if (tid == 0) a.cnt[b] = 0;   // ready for the next call
-    __syncthreads();
+    // ---- 2. chunk sums of the weights -------------------------------------------------
+    chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, resid, s_wp, s_cs);
     if (tid == 0) {
         double W = 0.0;
-        for (int q = 0; q < a.nchunks; ++q) W += s_part[q];
+        for (int q = 0; q < nch; ++q) W += s_cs[q];
         s_W = W;
     }
     __syncthreads();
@@ -601,82 +573,67 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
-        for (int q = 0; q < a.nchunks; ++q) {
-            double acc = 0.0;
-            for (int i0 = q * Lt::CH + tid * 8; i0 < (q + 1) * Lt::CH; i0 += kNT * 8) {
-                float z8[8];
-                load8<BF16, VEC>(trow, a.V, i0, z8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc += weight(z8[e], -INFINITY, r, a.c, false);
-            }
-            acc = block_sum<kNT>(acc, redd);
-            if (tid == 0) s_part[q] = acc;
-        }
-        __syncthreads();
+        chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, false, s_wp, s_cs);
         if (tid == 0) {
             double W = 0.0;
-            for (int q = 0; q < a.nchunks; ++q) W += s_part[q];
+            for (int q = 0; q < nch; ++q) W += s_cs[q];
             s_W = W;
             atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
         }
         __syncthreads();
     }
+
+    // ---- 3. inverse CDF ---------------------------------------------------------------
     const double W = s_W;
     const double t = (double)r.u * W;
     if (tid == 0) {
         double C = 0.0;
         int q = 0;
-        for (; q < a.nchunks; ++q) {
-            if (C + s_part[q] > t) break;
-            C += s_part[q];
+        for (; q < nch; ++q) {
+            if (C + s_cs[q] > t) break;
+            C += s_cs[q];
         }
-        if (q == a.nchunks) {   // unreachable while t < W; keep the last non-empty chunk
-            q = a.nchunks - 1;
-            while (q > 0 && !(s_part[q] > 0.0)) --q;
+        if (q == nch) {   // unreachable while t < W; keep the last non-empty chunk
+            q = nch - 1;
+            while (q > 0 && !(s_cs[q] > 0.0)) --q;
             C = 0.0;
-            for (int i = 0; i < q; ++i) C += s_part[i];
+            for (int i = 0; i < q; ++i) C += s_cs[i];
         }
         s_chunk = q;
         s_base = C;
     }
     __syncthreads();
-    // contiguous runs: thread tid scans elements [c0 + tid*EPT, c0 + (tid+1)*EPT)
-    const int e0 = s_chunk * Lt::CH + tid * Lt::EPT;
-    double run = 0.0;
-    for (int i0 = e0; i0 < e0 + Lt::EPT; i0 += 8) {
-        float t8[8], d8[8];
-        load8<BF16, VEC>(trow, a.V, i0, t8);
-        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+    const int i0 = s_chunk * kSChunk + tid * 8;
+    float t8[8], d8[8];
+    load8<BF16, VEC>(trow, a.V, i0, t8);
+    if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+    double w[8], run = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) run += weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+    for (int e = 0; e < 8; ++e) {
+        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+        run += w[e];
     }
     double tot;
-    double C = s_base + block_excl_scan_d<kNT>(run, redd, &tot);
+    double C = s_base + block_excl_scan_d<kSNT>(run, redd, &tot);
     int mine = 0x7fffffff, lastpos = -1;
     double wmine = 0.0, wlast = 0.0;
-    for (int i0 = e0; i0 < e0 + Lt::EPT; i0 += 8) {
-        float t8[8], d8[8];
-        load8<BF16, VEC>(trow, a.V, i0, t8);
-        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double w = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
-            C += w;
-            if (mine == 0x7fffffff && C > t) {
-                mine = i0 + e;
-                wmine = w;
-            }
-            if (w > 0.0) {
-                lastpos = i0 + e;
-                wlast = w;
-            }
+    for (int e = 0; e < 8; ++e) {
+        C += w[e];
+        if (mine == 0x7fffffff && C > t) {
+            mine = i0 + e;
+            wmine = w[e];
+        }
+        if (w[e] > 0.0) {
+            lastpos = i0 + e;
+            wlast = w[e];
         }
     }
-    int found = block_min_i<kNT>(mine, redi);
+    int found = block_min_i<kSNT>(mine, redi);
     if (found != 0x7fffffff) {
         if (mine == found) s_wpick = wmine;
     } else {
-        found = block_max_i<kNT>(lastpos, redi);
+        found = block_max_i<kSNT>(lastpos, redi);
         if (found >= 0 && lastpos == found) s_wpick = wlast;
     }
     __syncthreads();
@@ -694,7 +651,7 @@ __global__ __launch_bounds__(kNT) void k_sample(SampleArgs a) {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, wpart, cnt, thr, total;
+    size_t part, thr, total;
     int nparts, nchunks;
 };
 
@@ -710,10 +667,6 @@ static WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     size_t off = 0;
     p.part = off;
     off = align256(off + rows * p.nparts * sizeof(RowPartial));
-    p.wpart = off;
-    off = align256(off + (size_t)B * p.nchunks * sizeof(double));
-    p.cnt = off;
-    off = align256(off + (size_t)B * sizeof(int));
     p.thr = off;
     off = align256(off + rows * sizeof(float));
     p.total = off;
@@ -727,18 +680,18 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
     float* thr = reinterpret_cast<float*>(ws + p.thr);
-    int* cnt = reinterpret_cast<int*>(ws + p.cnt);
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
         hipExtLaunchKernelGGL((k_topk_rows<BF16, VEC>), dim3(rows), dim3(kTopkNT), 0, st, e0, e1, 0,
-                              tgt, dft, K + B, V, top_k, c, part, thr, B, cnt);
+                              tgt, dft, K + B, V, top_k, c, part, thr);
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
-                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part, B, cnt);
+                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);
     }
-    hipLaunchKernelGGL((k_sample<BF16, VEC>), dim3((unsigned)B * p.nchunks), dim3(kNT), 0, st, sa);
+    if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
+    hipLaunchKernelGGL((k_sample<BF16, VEC>), dim3(B), dim3(kSNT), 0, st, sa);
 }
 
 }  // namespace sd
@@ -766,7 +719,8 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
         return SPECDEC_EINVAL;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k);
-    if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu || p.nchunks > 1024)
+    if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
+        V > kSChunk * kSMaxChunks)
         return SPECDEC_EINVAL;
     if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;
@@ -793,13 +747,10 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.max_k = max_k;
     sa.V = V;
     sa.nparts = p.nparts;
-    sa.nchunks = p.nchunks;
     sa.topk = topk_active(top_k, V);
     sa.c = c;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
-    sa.wpart = reinterpret_cast<double*>(ws + p.wpart);
-    sa.cnt = reinterpret_cast<int*>(ws + p.cnt);
     sa.out_tokens = out_tokens;
     sa.num_acc = num_accepted;
     sa.num_emit = num_emitted;

@@ -304,13 +304,15 @@ class KVOnDevice:
         self.k_new = torch.from_numpy(kv.k_new.view(np.int16)).view(torch.bfloat16).to(d)
         self.v_new = torch.from_numpy(kv.v_new.view(np.int16)).view(torch.bfloat16).to(d)
         self.cu_new = torch.from_numpy(kv.cu_new.astype(np.int32)).to(d)
-        self.ws = torch.empty(binding.kv_paged_append_workspace_size(B), dtype=torch.uint8,
-                              device=d)
+        self.B = B
+        self.device = d
 
     def append(self, k_new=None, v_new=None, cu_new=None):
-        binding.kv_paged_append(self.cache, self.k_new if k_new is None else k_new,
-                                self.v_new if v_new is None else v_new,
-                                self.cu_new if cu_new is None else cu_new, self.ws)
+        k_new = self.k_new if k_new is None else k_new
+        ws = torch.empty(binding.kv_paged_append_workspace_size(self.B, k_new.shape[1]),
+                         dtype=torch.uint8, device=self.device)
+        binding.kv_paged_append(self.cache, k_new, self.v_new if v_new is None else v_new,
+                                self.cu_new if cu_new is None else cu_new, ws)
 
     def rollback(self, num_accepted: torch.Tensor, cu_draft: torch.Tensor):
         binding.kv_rollback(self.cache, num_accepted, cu_draft)

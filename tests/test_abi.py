@@ -46,7 +46,8 @@ def test_workspace_sizes(lib):
     assert n > 0 and n % 256 == 0
     assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 64) < n
     assert binding.specdec_verify_workspace_size(0, 0, 10, 0, 0) == 0
-    assert binding.kv_paged_append_workspace_size(512) >= 16 + 512 * 16
+    assert binding.kv_paged_append_workspace_size(512, 3000) >= 16 + 512 * 16 + 3000 * 8
+    assert binding.kv_paged_append_workspace_size(0, 10) == 0
 
 
 def test_host_validation_returns_einval_without_gpu(lib):
