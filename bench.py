@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--schedule", choices=["serial", "overlap"], default="overlap",
+    p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
                    help="serial: append, verify, rollback on one stream; overlap: the K/V "
                         "scatter runs on a second stream once the logit rows are streamed, "
                         "beside the sampling kernel")
@@ -45,6 +45,9 @@ def parse():
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="run one plain device-to-device copy of this many MiB before timing "
+                        "(a known-size reference for HBM traffic counters)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time the oracle baseline runs for")
     return p.parse_args()
@@ -177,6 +180,13 @@ def main():
             ev_kv[i].wait_on(main_s)
         binding.kv_rollback(cache, nacc, cu)
 
+    if args.calibrate_copy_mib:
+        nb = args.calibrate_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=d).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

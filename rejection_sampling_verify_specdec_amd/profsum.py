@@ -1,0 +1,92 @@
+"""Summaries of rocprofv3 output databases (kernel trace, PMC counters) as short text.
+
+    python -m rejection_sampling_verify_specdec_amd.profsum trace DB [--cmd "..."]
+    python -m rejection_sampling_verify_specdec_amd.profsum traffic FETCH_DB WRITE_DB \
+        --kernel k_row_stats --calib-kernel copyBuffer --calib-bytes N --alg-bytes A
+
+``trace`` prints count / average / min / max duration per kernel. ``traffic`` turns the
+FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of a kernel into HBM bytes per
+launch, scaled by what the same counters read for a plain copy kernel of known size.
+"""
+
+import argparse
+import sqlite3
+import sys
+
+
+def _kernels(db):
+    con = sqlite3.connect(db)
+    return con.execute("select name, count(*), avg(end-start), min(end-start), max(end-start) "
+                       "from kernels group by name order by sum(end-start) desc").fetchall()
+
+
+def trace(db, cmd=None, top=12):
+    out = []
+    if cmd:
+        out.append(f"command: {cmd}")
+    out.append(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
+    for name, n, avg, mn, mx in _kernels(db)[:top]:
+        out.append(f"{name[:64]:64s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}")
+    return "\n".join(out)
+
+
+def _pmc(db, counter):
+    """Per-dispatch counter values: list of (kernel name, value)."""
+    con = sqlite3.connect(db)
+    views = {r[0] for r in con.execute("select name from sqlite_master")}
+    if "counters_collection" in views:
+        cols = [c[1] for c in con.execute("pragma table_info(counters_collection)")]
+        name_col = "kernel_name" if "kernel_name" in cols else "name"
+        val_col = "value" if "value" in cols else "counter_value"
+        cnt_col = "counter_name" if "counter_name" in cols else "counter"
+        rows = con.execute(f"select {name_col}, dispatch_id, sum({val_col}) from counters_collection "
+                           f"where {cnt_col} = ? group by dispatch_id", (counter,)).fetchall()
+        return [(r[0], r[2]) for r in rows]
+    raise RuntimeError("no counters_collection view in " + db)
+
+
+def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes, alg_bytes=None):
+    f = _pmc(fetch_db, "FETCH_SIZE")
+    w = _pmc(write_db, "WRITE_SIZE")
+    sel = lambda rows, key: [v for n, v in rows if key in n]
+    cf, cw = sel(f, calib_kernel), sel(w, calib_kernel)
+    kf, kw = sel(f, kernel), sel(w, kernel)
+    if not (cf and cw and kf and kw):
+        raise RuntimeError("kernel or calibration copy not found in the counter databases")
+    # the copy reads and writes calib_bytes: KiB reported -> bytes scale factors
+    sf = calib_bytes / (sum(cf) / len(cf) * 1024.0)
+    sw = calib_bytes / (sum(cw) / len(cw) * 1024.0)
+    fetch = sum(kf) / len(kf) * 1024.0 * sf
+    write = sum(kw) / len(kw) * 1024.0 * sw
+    lines = [f"kernel {kernel}: {len(kf)} dispatches",
+             f"calibration copy {calib_kernel}: {calib_bytes} bytes read and written; "
+             f"FETCH_SIZE scale {sf:.4f}, WRITE_SIZE scale {sw:.4f}",
+             f"FETCH bytes/launch {fetch:.4e}", f"WRITE bytes/launch {write:.4e}",
+             f"total HBM bytes/launch {fetch + write:.4e}"]
+    if alg_bytes:
+        lines.append(f"algorithmic bytes/launch {alg_bytes:.4e}  ratio {(fetch + write) / alg_bytes:.4f}")
+    return "\n".join(lines), fetch + write
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--cmd")
+    p = sub.add_parser("traffic")
+    p.add_argument("fetch_db")
+    p.add_argument("write_db")
+    p.add_argument("--kernel", required=True)
+    p.add_argument("--calib-kernel", required=True)
+    p.add_argument("--calib-bytes", type=float, required=True)
+    p.add_argument("--alg-bytes", type=float)
+    a = ap.parse_args(argv)
+    if a.what == "trace":
+        print(trace(a.db, a.cmd))
+    else:
+        print(traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes, a.alg_bytes)[0])
+
+
+if __name__ == "__main__":
+    sys.exit(main())
