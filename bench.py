@@ -26,8 +26,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% peak), B=256 k=5 V=128256 bf16"
 PEAK_GBPS = 8000.0
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "row_stats_c2_traffic.json")
-STATS_SRC = os.path.join(ROOT, "rejection_sampling_verify_specdec_amd", "csrc", "verify.hip")
+CSRC = os.path.join(ROOT, "rejection_sampling_verify_specdec_amd", "csrc")
 
 
 def parse():
@@ -37,10 +36,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--schedule", choices=["serial", "overlap"], default="serial",
-                   help="serial: append, verify, rollback on one stream; overlap: the K/V "
-                        "scatter runs on a second stream once the logit rows are streamed, "
-                        "beside the sampling kernel")
+    p.add_argument("--schedule", choices=["fused", "serial", "overlap"], default="fused",
+                   help="fused: specdec_cycle (allocation inside the logit-streaming launch, "
+                        "K/V scatter beside the sampling workgroups); serial: append, verify, "
+                        "rollback as three calls on one stream; overlap: the three calls with "
+                        "the append on a second stream after the logit rows are streamed")
     p.add_argument("--timing-every", type=int, default=4,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
@@ -54,14 +54,19 @@ def parse():
 
 
 def source_hash() -> str:
-    return hashlib.sha256(open(STATS_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of every kernel source file: counters taken on other sources do not apply."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_bytes_alg: float):
-    """HBM bytes per launch of the row-statistics kernel from committed rocprofv3 counter
-    summaries, if they were taken on the current kernel source."""
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
     try:
-        d = json.load(open(PROFILE_TRAFFIC))
+        d = json.load(open(os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")))
     except Exception:
         return None
     if d.get("source_sha256_16") != source_hash():
@@ -148,6 +153,7 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
     ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
+    cws = torch.empty(binding.specdec_cycle_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
     kws = torch.empty(binding.kv_paged_append_workspace_size(B, K + B), dtype=torch.uint8, device=d)
     n = args.warmup + args.steps
     timed = [i for i in range(args.warmup, n) if (i - args.warmup) % max(args.timing_every, 1) == 0]
@@ -161,6 +167,12 @@ def main():
         dbg = binding.SpecdecDebug()
         if i in evs:
             dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
+        if args.schedule == "fused":
+            binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
+                                  max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
+                                  out_tokens=out, num_accepted=nacc, num_emitted=nemit,
+                                  err_word=err, workspace=cws, debug=dbg)
+            return
         if args.schedule == "serial":
             binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
@@ -212,6 +224,7 @@ def main():
     positions_per_s = K * args.steps / elapsed
     cycle_gbps = cycle_bytes / (ms_per_step / 1e3) / 1e9
     achieved = logit_bytes / stats_avg_s / 1e9
+    stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
     res = {
         "metric": METRIC,
         "value": positions_per_s,
@@ -233,9 +246,9 @@ def main():
         "achieved_hbm_gbps": cycle_gbps,
         "pct_peak_hbm": 100.0 * cycle_gbps / PEAK_GBPS,
         "cycle_bytes": cycle_bytes,
-        "roofline": {"bound": "hbm", "kernel": "k_row_stats", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": stats_kernel, "achieved": achieved,
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": achieved / PEAK_GBPS,
-                     "traffic": traffic_from_profile(logit_bytes),
+                     "traffic": traffic_from_profile(stats_kernel, wl.name),
                      "algorithmic_bytes": logit_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
     }

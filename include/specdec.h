@@ -226,6 +226,40 @@ int kv_paged_append(const kv_paged_cache* cache, int32_t B,
 int kv_rollback(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
                 const int32_t* cu_draft, hipStream_t stream);
 
+/* =====================================================================================
+ * One whole cycle
+ * ===================================================================================== */
+
+/* Bytes of device workspace specdec_cycle needs (16-byte aligned). */
+size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
+                                    int32_t top_k);
+
+/*
+ * specdec_cycle - one speculative cycle with the same effect as the three calls
+ *   kv_paged_append(cache, B, k_new, v_new, cu_new, K + B, ...)   with cu_new[b] = cu_draft[b] + b
+ *   specdec_verify(target_logits, ..., num_accepted, ...)
+ *   kv_rollback(cache, B, num_accepted, cu_draft)
+ * on `stream`: the pending token and the k_b proposals of every request are appended
+ * (entry t of request b is row cu_draft[b] + b + t of k_new / v_new, bf16 [L][K+B][H][D]),
+ * verified, and the cache truncated to the pending token plus the accepted proposals
+ * ("Walk through KV-cache updates when speculative decoding rejects some draft tokens",
+ * paragraph 1; "Keep cache validity aligned with the committed token history",
+ * paragraphs 1-2). Outputs, error bits and cache state are bit-identical to the three
+ * calls. The launches are fused so that block allocation overlaps the logit stream and the
+ * K/V scatter overlaps the per-request sampling. Arguments and their checks are those of
+ * the three calls (B <= SPECDEC_MAX_KV_BATCH); workspace >=
+ * specdec_cycle_workspace_size(B, K, V, dtype, top_k) bytes, 16-byte aligned.
+ */
+int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
+                  const void* target_logits, const void* draft_logits, int32_t dtype,
+                  const int32_t* draft_tokens, const int32_t* cu_draft,
+                  const float* u_accept, const float* u_sample,
+                  int32_t B, int32_t K, int32_t max_k, int32_t V,
+                  float temperature, int32_t top_k,
+                  int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                  int32_t* err_word, const specdec_debug* dbg,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -42,6 +42,7 @@ MAX_KV_BATCH = 4096
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback",
+    "specdec_cycle_workspace_size", "specdec_cycle",
 ]
 
 
@@ -103,6 +104,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_paged_append.restype = ctypes.c_int
     lib.kv_rollback.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
     lib.kv_rollback.restype = ctypes.c_int
+    lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.specdec_cycle_workspace_size.restype = sz
+    lib.specdec_cycle.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp,
+                                  vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, vp, vp,
+                                  ctypes.POINTER(SpecdecDebug), vp, sz, vp]
+    lib.specdec_cycle.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -247,6 +254,54 @@ def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch
                          _stream(dev))
     if st != SPECDEC_OK:
         raise SpecdecError("kv_rollback", st)
+
+
+def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int) -> int:
+    return int(load_library().specdec_cycle_workspace_size(B, K, V, dtype, top_k))
+
+
+def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                  target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                  draft_tokens: torch.Tensor, cu_draft: torch.Tensor,
+                  u_accept: torch.Tensor, u_sample: torch.Tensor, *, max_k: int,
+                  temperature: float, top_k: int, out_tokens: torch.Tensor,
+                  num_accepted: torch.Tensor, num_emitted: torch.Tensor,
+                  err_word: torch.Tensor, workspace: torch.Tensor,
+                  debug: Optional[SpecdecDebug] = None) -> None:
+    """Enqueue append -> verify -> rollback of one cycle as fused launches."""
+    lib = load_library()
+    dev = target_logits.device
+    dtype = _logits_dtype(target_logits)
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [K+B, V]")
+    B = cu_draft.numel() - 1
+    R, V = target_logits.shape
+    K = R - B
+    s = cache.struct
+    shape = (s.num_layers, K + B, s.num_kv_heads, s.head_dim)
+    if tuple(k_new.shape) != shape or tuple(v_new.shape) != shape:
+        raise ValueError(f"k_new / v_new must be {shape}")
+    _check(k_new, "k_new", torch.bfloat16, device=dev)
+    _check(v_new, "v_new", torch.bfloat16, device=dev)
+    _check(target_logits, "target_logits", target_logits.dtype, device=dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, K * V, dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, K, dev)
+    _check(cu_draft, "cu_draft", torch.int32, B + 1, dev)
+    _check(u_accept, "u_accept", torch.float32, K, dev)
+    _check(u_sample, "u_sample", torch.float32, B, dev)
+    _check(out_tokens, "out_tokens", torch.int32, K + B, dev)
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(num_emitted, "num_emitted", torch.int32, B, dev)
+    _check(err_word, "err_word", torch.int32, 1, dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    st = lib.specdec_cycle(
+        ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
+        dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,
+        V, float(temperature), int(top_k), _ptr(out_tokens), _ptr(num_accepted),
+        _ptr(num_emitted), _ptr(err_word), ctypes.byref(debug) if debug is not None else None,
+        _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_cycle", st)
 
 
 # --- HIP events and stream waits through the runtime (timing, cross-stream ordering) -----

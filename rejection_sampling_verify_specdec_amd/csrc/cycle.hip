@@ -1,0 +1,193 @@
+// One whole speculative cycle in three launches (gfx950): the same work and results as
+// kv_paged_append -> specdec_verify -> kv_rollback on one stream, scheduled so that
+// latency-bound work rides along with bandwidth-bound work.
+//
+//   k_cycle_stats   workgroup 0 allocates the cycle's blocks (copy-on-write, LIFO pops,
+//                   destination rows) while every other workgroup streams logit rows
+//                   (row statistics, or the top-k row kernel);
+//   k_cycle_sample  workgroups [0, B) decide and draw each request's tokens; the rest
+//                   scatter the candidate K/V into their slots meanwhile;
+//   k_kv_rollback   truncates every request to its committed prefix.
+//
+// The cycle is the one the pages describe ("Walk through KV-cache updates when
+// speculative decoding rejects some draft tokens": K/V for the candidates are appended by
+// the verifying pass, the accept test runs left to right, pages past the committed prefix
+// are freed): the pending token and the k_b proposals are appended (n_b = k_b + 1, new
+// entry t of request b is row cu_draft[b] + b + t of k_new / v_new), then verified, then
+// rolled back to the pending token plus the accepted proposals.
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kv_dev.h"
+#include "verify_dev.h"
+
+namespace sd {
+
+constexpr int kCycAllocNT = kNT;   // allocation workgroup inside the statistics launch
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __restrict__ cu,
+                                                     int B, int N, uint8_t* __restrict__ aws,
+                                                     const uint8_t* __restrict__ tgt,
+                                                     const uint8_t* __restrict__ dft,
+                                                     int rows_t, int V, int nchunks, float c,
+                                                     RowPartial* __restrict__ part) {
+    if (blockIdx.x == 0) {
+        alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
+        return;
+    }
+    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTopkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
+                                                        int B, int N, uint8_t* __restrict__ aws,
+                                                        const uint8_t* __restrict__ tgt,
+                                                        const uint8_t* __restrict__ dft,
+                                                        int rows_t, int V, int top_k, float c,
+                                                        RowPartial* __restrict__ part,
+                                                        float* __restrict__ row_thr) {
+    if (blockIdx.x == 0) {
+        alloc_body<kTopkNT>(kv, cu, 1, B, N, aws);
+        return;
+    }
+    topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kSNT) void k_cycle_sample(SampleArgs sa, KvArgs kv,
+                                                       const uint8_t* __restrict__ knew,
+                                                       const uint8_t* __restrict__ vnew, int N,
+                                                       int tpw, int ntiles,
+                                                       const uint8_t* __restrict__ aws) {
+    const int bid = blockIdx.x;
+    if (bid < sa.B) {
+        sample_body<BF16, VEC>(sa, bid);
+        return;
+    }
+    const int s = bid - sa.B;
+    const int planes = kv.L * 2;
+    scatter_body(kv, knew, vnew, sa.B, N, tpw, aws, s / planes, s % planes, s, ntiles * planes,
+                 kSNT);
+}
+
+__global__ __launch_bounds__(kKvNT) void k_cycle_rollback(KvArgs a, const int* __restrict__ num_acc,
+                                                          const int* __restrict__ cu, int B) {
+    rollback_body(a, num_acc, cu, B);
+}
+
+template <bool BF16, bool VEC>
+static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
+                         const uint8_t* tgt, const uint8_t* dft, const int* cu, int B, int K,
+                         int V, int top_k, float c, const WsPlan& p, uint8_t* vws, uint8_t* aws,
+                         const SampleArgs& sa, const specdec_debug* dbg, hipStream_t st) {
+    const int rows = 2 * K + B;
+    const int N = K + B;
+    RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
+    float* thr = reinterpret_cast<float*>(vws + p.thr);
+    hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
+    hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
+    if (topk_active(top_k, V)) {
+        hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC>), dim3(rows + 1), dim3(kTopkNT), 0, st, e0,
+                              e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V, top_k, c, part, thr);
+    } else {
+        hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
+                              dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,
+                              p.nchunks, c, part);
+    }
+    if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
+    const int tpw = scatter_tokens_per_wg(kv, kSNT);
+    const int ntiles = (N + tpw - 1) / tpw;
+    hipLaunchKernelGGL((k_cycle_sample<BF16, VEC>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
+                       dim3(kSNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
+    hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, kv, sa.num_acc, cu, B);
+}
+
+}  // namespace sd
+
+extern "C" size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
+                                               int32_t top_k) {
+    if (B < 1 || K < 0 || V < 1 || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16)) return 0;
+    return sd::align256(sd::plan_ws(B, K, V, dtype, top_k).total) + sd::append_ws_bytes(B, K + B);
+}
+
+extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
+                             const void* target_logits, const void* draft_logits, int32_t dtype,
+                             const int32_t* draft_tokens, const int32_t* cu_draft,
+                             const float* u_accept, const float* u_sample, int32_t B, int32_t K,
+                             int32_t max_k, int32_t V, float temperature, int32_t top_k,
+                             int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                             int32_t* err_word, const specdec_debug* dbg, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    using namespace sd;
+    // verification arguments: the same checks as specdec_verify
+    if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
+    if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
+    if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SPECDEC_EINVAL;
+    if (!target_logits || !cu_draft || !u_sample || !out_tokens || !num_accepted ||
+        !num_emitted || !err_word)
+        return SPECDEC_EINVAL;
+    if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
+    // cache arguments: the same checks as kv_paged_append / kv_rollback
+    if (!geometry_ok(cache) || B > SPECDEC_MAX_KV_BATCH || !k_new || !v_new ||
+        ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
+        return SPECDEC_EINVAL;
+    const WsPlan p = plan_ws(B, K, V, dtype, top_k);
+    if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > kSChunk * kSMaxChunks)
+        return SPECDEC_EINVAL;
+    const size_t vbytes = align256(p.total);
+    if (!workspace || workspace_bytes < vbytes + append_ws_bytes(B, K + B) ||
+        ((uintptr_t)workspace & 15))
+        return SPECDEC_EWORKSPACE;
+
+    const double c64 = 1.4426950408889634074 / (double)temperature;   // log2(e) / T
+    const float c = (float)c64;
+    if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
+    const int es = dtype == SPECDEC_BF16 ? 2 : 4;
+    const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)target_logits & 15) == 0 &&
+                     (K == 0 || ((uintptr_t)draft_logits & 15) == 0);
+    uint8_t* vws = reinterpret_cast<uint8_t*>(workspace);
+    uint8_t* aws = vws + vbytes;
+    const uint8_t* tgt = reinterpret_cast<const uint8_t*>(target_logits);
+    const uint8_t* dft = reinterpret_cast<const uint8_t*>(K > 0 ? draft_logits : target_logits);
+    const uint8_t* knew = reinterpret_cast<const uint8_t*>(k_new);
+    const uint8_t* vnew = reinterpret_cast<const uint8_t*>(v_new);
+
+    SampleArgs sa;
+    sa.tgt = tgt;
+    sa.dft = dft;
+    sa.tokens = draft_tokens;
+    sa.cu = cu_draft;
+    sa.u_acc = u_accept;
+    sa.u_smp = u_sample;
+    sa.B = B;
+    sa.K = K;
+    sa.max_k = max_k;
+    sa.V = V;
+    sa.nparts = p.nparts;
+    sa.topk = topk_active(top_k, V);
+    sa.c = c;
+    sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
+    sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
+    sa.out_tokens = out_tokens;
+    sa.num_acc = num_accepted;
+    sa.num_emit = num_emitted;
+    sa.err_word = err_word;
+    sa.dbg = dbg ? *dbg : specdec_debug{};
+
+    const KvArgs kv = args_of(cache);
+    (void)hipGetLastError();
+    if (dtype == SPECDEC_BF16) {
+        if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+        else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+    } else {
+        if (vec) launch_cycle<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+        else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+    }
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}

@@ -27,167 +27,16 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "common.h"
-#include "specdec.h"
+#include "verify_dev.h"
 
 namespace sd {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kNT = 256;        // threads per workgroup of the streaming kernels
-constexpr int kVPT = 8;         // 16-byte vectors per thread per chunk
-constexpr int kTopkNT = 1024;   // threads per workgroup of the top-k row kernel
-
-enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_BONUS = 2 };
-
-// Partial statistics of one row chunk (or of a whole row for top-k rows).
-struct alignas(16) RowPartial {
-    float m;      // max logit of the chunk (-inf if none)
-    int nkept;    // kept tokens (top-k rows only)
-    double s;     // sum over the chunk of exp2((z - m) * c)
-};
-
-template <bool BF16, bool VEC>
-struct Layout {
-    static constexpr int ES = BF16 ? 2 : 4;          // element bytes
-    static constexpr int EPV = 16 / ES;              // elements per 16-byte vector
-    static constexpr int PER = VEC ? EPV : 1;        // elements per thread per column
-    static constexpr int COLS = VEC ? kVPT : kVPT * EPV;
-    static constexpr int EPT = COLS * PER;           // elements per thread per chunk
-    static constexpr int CH = kNT * EPT;             // elements per chunk
-};
-
-SD_DEV float load_elem(const uint8_t* row, long i, bool bf16) {
-    if (bf16) return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
-    return reinterpret_cast<const float*>(row)[i];
-}
-
-// Element z[col * PER + e] of the calling thread is index c0 + (col * kNT + tid) * PER + e
-// of the row; elements at or past V read as -inf.
-template <bool BF16, bool VEC>
-SD_DEV void load_chunk(const uint8_t* __restrict__ row, int V, int c0,
-                       float (&z)[Layout<BF16, VEC>::EPT]) {
-    using Lt = Layout<BF16, VEC>;
-    const int tid = threadIdx.x;
-    if constexpr (VEC) {
-        // streamed once: non-temporal loads keep the rows from displacing other lines
-        const u32x4* p = reinterpret_cast<const u32x4*>(row);
-        u32x4 raw[Lt::COLS];
-        const uint32_t fill = BF16 ? 0xff80ff80u : 0xff800000u;
-#pragma unroll
-        for (int col = 0; col < Lt::COLS; ++col) {
-            const int i0 = c0 + (col * kNT + tid) * Lt::PER;
-            if (i0 < V) {
-                raw[col] = __builtin_nontemporal_load(p + i0 / Lt::EPV);
-            } else {
-                raw[col] = (u32x4){fill, fill, fill, fill};
-            }
-        }
-#pragma unroll
-        for (int col = 0; col < Lt::COLS; ++col) {
-            const uint32_t w[4] = {raw[col].x, raw[col].y, raw[col].z, raw[col].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (BF16) {
-                    z[col * Lt::PER + 2 * q] = bf16_lo(w[q]);
-                    z[col * Lt::PER + 2 * q + 1] = bf16_hi(w[q]);
-                } else {
-                    z[col * Lt::PER + q] = __uint_as_float(w[q]);
-                }
-            }
-        }
-    } else {
-#pragma unroll
-        for (int col = 0; col < Lt::COLS; ++col) {
-            const int i = c0 + col * kNT + tid;
-            z[col] = i < V ? load_elem(row, i, BF16) : -INFINITY;
-        }
-    }
-}
-
-template <int N>
-SD_DEV float tree_sum(float (&a)[N]) {
-#pragma unroll
-    for (int s = 1; s < N; s <<= 1) {
-#pragma unroll
-        for (int i = 0; i + s < N; i += 2 * s) a[i] += a[i + s];
-    }
-    return a[0];
-}
-
-SD_DEV const uint8_t* row_ptr(const uint8_t* tgt, const uint8_t* dft, int rows_t, int row,
-                              int V, int es) {
-    return row < rows_t ? tgt + (size_t)row * V * es : dft + (size_t)(row - rows_t) * V * es;
-}
-
-// ---------------------------------------------------------------------------------------
-// Row statistics, chunked: max and sum of exp2((z - m_c) * c) per chunk.
-// ---------------------------------------------------------------------------------------
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ tgt,
                                                    const uint8_t* __restrict__ dft,
                                                    int rows_t, int V, int nchunks, float c,
                                                    RowPartial* __restrict__ part) {
-    using Lt = Layout<BF16, VEC>;
-    __shared__ float redf[kNT / kWave];
-    __shared__ double redd[kNT / kWave];
-    __shared__ int redi[kNT / kWave];
-    const int row = blockIdx.x / nchunks;
-    const int chunk = blockIdx.x - row * nchunks;
-    const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, Lt::ES);
-    float z[Lt::EPT];
-    load_chunk<BF16, VEC>(base, V, chunk * Lt::CH, z);
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < Lt::EPT; ++i) mx = fmaxf(mx, z[i]);
-    const float m = block_max<kNT>(mx, redf);
-
-    double s;
-    if (m == -INFINITY) {
-        // nothing finite: the chunk contributes 0, unless it holds a NaN
-        int nan = 0;
-#pragma unroll
-        for (int i = 0; i < Lt::EPT; ++i) nan |= (z[i] != z[i]);
-        nan = block_max_i<kNT>(nan, redi);
-        s = nan ? (double)NAN : 0.0;
-    } else {
-        const float mc = m * c;
-        const float emc = fmaf(m, c, -mc);    // exact: m * c = mc + emc
-        float vs[Lt::COLS];
-#pragma unroll
-        for (int col = 0; col < Lt::COLS; ++col) {
-            float e[Lt::PER];
-#pragma unroll
-            for (int q = 0; q < Lt::PER; ++q)
-                e[q] = __builtin_amdgcn_exp2f(fmaf(z[col * Lt::PER + q], c, -mc));
-            vs[col] = tree_sum(e);
-        }
-        const double tot = block_sum<kNT>((double)tree_sum(vs), redd);
-        // exp2(z*c - mc) = exp2((z - m)*c) * 2^emc, so rescale by 2^-emc
-        s = tot * exp2(-(double)emc);
-    }
-    if (threadIdx.x == 0) {
-        RowPartial rp;
-        rp.m = m;
-        rp.nkept = 0;
-        rp.s = s;
-        part[blockIdx.x] = rp;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Top-k rows: one workgroup of 1024 threads per row. The row is walked in segments of
-// 1024 * 8 vectors. Exact k-th largest value by a 4-pass radix select on
-// order-preserving 32-bit keys (2 passes suffice for bf16, whose low 16 key bits are
-// constant), then kept-set max / count / sum in a final pass.
-// ---------------------------------------------------------------------------------------
-SD_DEV uint32_t f2key(float f) {
-    const uint32_t b = __float_as_uint(f);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-SD_DEV float key2f(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x);
 }
 
 template <bool BF16, bool VEC>
@@ -196,481 +45,12 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
                                                        int rows_t, int V, int top_k, float c,
                                                        RowPartial* __restrict__ part,
                                                        float* __restrict__ row_thr) {
-    constexpr int NT = kTopkNT;
-    constexpr int ES = BF16 ? 2 : 4;
-    __shared__ unsigned hist[256];
-    __shared__ float redf[NT / kWave];
-    __shared__ double redd[NT / kWave];
-    __shared__ int redi[NT / kWave];
-    __shared__ uint32_t s_prefix;
-    __shared__ int s_krem;
-    const int row = blockIdx.x;
-    const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, ES);
-    const int tid = threadIdx.x;
-
-    // pass 0: max, invalid entries (NaN, +inf)
-    float mx = -INFINITY;
-    int bad = 0;
-    for (int i = tid; i < V; i += NT) {
-        const float z = load_elem(base, i, BF16);
-        mx = fmaxf(mx, z);
-        bad |= (z != z) | (z == INFINITY);
-    }
-    const float m = block_max<NT>(mx, redf);
-    bad = block_max_i<NT>(bad, redi);
-
-    // radix select of the top_k-th largest key
-    if (tid == 0) {
-        s_prefix = 0;
-        s_krem = top_k;
-    }
-    __syncthreads();
-    const int npass = BF16 ? 2 : 4;
-    for (int pass = 0; pass < npass; ++pass) {
-        const int shift = 24 - 8 * pass;
-        for (int i = tid; i < 256; i += NT) hist[i] = 0;
-        __syncthreads();
-        const uint32_t prefix = s_prefix;
-        const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < V; i += NT) {
-            const uint32_t k = f2key(load_elem(base, i, BF16));
-            if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xff], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int krem = s_krem;
-            int d = 255;
-            for (; d > 0; --d) {
-                if ((int)hist[d] >= krem) break;
-                krem -= hist[d];
-            }
-            s_prefix = prefix | ((uint32_t)d << shift);
-            s_krem = krem;
-        }
-        __syncthreads();
-    }
-    uint32_t tkey = s_prefix;
-    if (BF16) tkey |= (tkey & 0x80000000u) ? 0u : 0xffffu;   // negatives' low key bits are 1s
-    const float thr = key2f(tkey);
-
-    // kept set: z >= thr (and finite); max is the row max; count and sum
-    const float mc = m * c;
-    const float emc = fmaf(m, c, -mc);
-    float acc = 0.f;
-    int kept = 0;
-    for (int i = tid; i < V; i += NT) {
-        const float z = load_elem(base, i, BF16);
-        if (z >= thr && z > -INFINITY) {
-            acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
-            ++kept;
-        }
-    }
-    const double tot = block_sum<NT>((double)acc, redd);
-    kept = block_sum_i<NT>(kept, redi);
-    if (tid == 0) {
-        RowPartial rp;
-        rp.m = m;
-        rp.nkept = kept;
-        rp.s = bad ? (double)NAN : (m == -INFINITY ? 0.0 : tot * exp2(-(double)emc));
-        part[row] = rp;
-        row_thr[row] = thr;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Decision and sampling, fused: one workgroup of 1024 threads per request.
-//   1. combine the row partials in fp64, evaluate p_i(y_i), q_i(y_i) and the accept test
-//      left to right, find the first rejection, publish the accepted tokens;
-//   2. stream the one row pair (or bonus row) still to be sampled in 8192-element chunks
-//      (four chunks in flight per thread) and keep per-chunk weight sums in LDS;
-//   3. W = sum of the chunk sums, t = u * W, locate the chunk holding t and scan it in
-//      ascending token order (each thread owns 8 consecutive tokens) for the smallest x
-//      with C(x) > t.
-// Nothing crosses workgroups, so no device-scope fence is needed; rows after the first
-// rejection are never read.
-// ---------------------------------------------------------------------------------------
-constexpr int kSNT = 1024;                 // threads of the sampling workgroup
-constexpr int kSW = kSNT / kWave;          // its waves
-constexpr int kSChunk = kSNT * 8;          // tokens per sampling chunk
-constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
-
-struct SampleArgs {
-    const uint8_t* tgt;
-    const uint8_t* dft;
-    const int* tokens;
-    const int* cu;
-    const float* u_acc;
-    const float* u_smp;
-    int B, K, max_k, V;
-    int nparts;              // statistics partials per row
-    int topk;                // 1 when rows carry a top-k threshold
-    float c;
-    const RowPartial* part;
-    const float* row_thr;
-    int* out_tokens;
-    int* num_acc;
-    int* num_emit;
-    int* err_word;
-    specdec_debug dbg;
-};
-
-struct Decision {
-    int flags, err, a, k, mode, row_t, row_d, pad;
-    float mc_t, mc_d, thr_t, thr_d;
-    double al_t, al_d;
-    float u;
-};
-
-constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
-
-// Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection, p(x) for the
-// bonus; p and q in fp64 from fp32 exponentials of the same form the statistics used.
-SD_DEV double weight(float zt, float zd, const Decision& r, float c, bool resid) {
-    const double pt = zt >= r.thr_t
-                          ? (double)__builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * r.al_t
-                          : 0.0;
-    if (!resid) return pt;
-    const double pd = zd >= r.thr_d
-                          ? (double)__builtin_amdgcn_exp2f(fmaf(zd, c, -r.mc_d)) * r.al_d
-                          : 0.0;
-    return fmax(pt - pd, 0.0);
-}
-
-// Eight consecutive elements starting at i0 (a multiple of 8); -inf at or past V.
-template <bool BF16, bool VEC>
-SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8]) {
-    if constexpr (VEC && BF16) {
-        if (i0 < V) {
-            const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 8);
-            const uint32_t q[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                z[2 * j] = bf16_lo(q[j]);
-                z[2 * j + 1] = bf16_hi(q[j]);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
-        }
-    } else if constexpr (VEC) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (i0 + 4 * h < V) {
-                const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 4 + h);
-                z[4 * h] = __uint_as_float(w.x);
-                z[4 * h + 1] = __uint_as_float(w.y);
-                z[4 * h + 2] = __uint_as_float(w.z);
-                z[4 * h + 3] = __uint_as_float(w.w);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) z[4 * h + j] = -INFINITY;
-            }
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = i0 + j < V ? load_elem(row, i0 + j, BF16) : -INFINITY;
-    }
-}
-
-// Per-chunk weight sums of the row (pair) into s_cs[0 .. nch): wave sums in LDS, then a
-// fixed-order sum over the 16 waves.
-template <bool BF16, bool VEC>
-SD_DEV void chunk_sums(const uint8_t* trow, const uint8_t* drow, int V, int nch,
-                       const Decision& r, float c, bool resid, double (*s_wp)[kSW],
-                       double* s_cs) {
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-        float zt[4][8], zd[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i0 = (c0 + u) * kSChunk + tid * 8;
-            load8<BF16, VEC>(trow, (c0 + u) < nch ? V : 0, i0, zt[u]);
-            if (resid) load8<BF16, VEC>(drow, (c0 + u) < nch ? V : 0, i0, zd[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            double acc = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc += weight(zt[u][e], resid ? zd[u][e] : -INFINITY, r, c, resid);
-            acc = wave_sum(acc);
-            if (lane == 0 && c0 + u < nch) s_wp[c0 + u][wave] = acc;
-        }
-    }
-    __syncthreads();
-    for (int q = tid; q < nch; q += kSNT) {
-        double x = 0.0;
-#pragma unroll
-        for (int w = 0; w < kSW; ++w) x += s_wp[q][w];
-        s_cs[q] = x;
-    }
-    __syncthreads();
+    topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
 }
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kSNT) void k_sample(SampleArgs a) {
-    using Lt = Layout<BF16, VEC>;
-    __shared__ float s_m[kMaxRows];
-    __shared__ double s_S[kMaxRows];
-    __shared__ float s_thr[kMaxRows];
-    __shared__ int s_rowbad;
-    __shared__ Decision D;
-    __shared__ double redd[kSW];
-    __shared__ int redi[kSW];
-    __shared__ double s_wp[kSMaxChunks][kSW];
-    __shared__ double s_cs[kSMaxChunks];
-    __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_chunk;
-
-    const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid % kWave;
-    const int rows_t = a.K + a.B;
-    const double cd = (double)a.c;
-
-    // ---- 1. decision ------------------------------------------------------------------
-    const int lo = a.cu[b], hi = a.cu[b + 1];
-    const int k = hi - lo;
-    const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
-                       hi > a.K;
-    if (bad_k) {
-        if (tid == 0) {
-            a.num_acc[b] = -1;
-            a.num_emit[b] = 0;
-            atomicOr(a.err_word, SPECDEC_ERR_K);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = SPECDEC_ERR_K;
-        }
-        return;
-    }
-    if (tid == 0) s_rowbad = 0;
-    __syncthreads();
-    const int nrows = 2 * k + 1;   // <= kMaxRows <= kSNT
-    if (tid < nrows) {
-        const int r = tid;
-        const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
-        const RowPartial* pp = a.part + (size_t)prow * a.nparts;
-        float m = -INFINITY;
-        double S = 0.0;
-        int nk = 0;
-        // batches of 8 partials: their loads are issued together
-        for (int q0 = 0; q0 < a.nparts; q0 += 8) {
-            RowPartial x[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (q0 + q < a.nparts) x[q] = pp[q0 + q];
-                else x[q] = RowPartial{-INFINITY, 0, 0.0};
-            }
-            float mb = -INFINITY;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) mb = fmaxf(mb, x[q].m);
-            const float mn = fmaxf(m, mb);
-            // rescale what was summed so far to the new max, then add this batch
-            if (m != -INFINITY && mn != m) S *= exp2((double)(m - mn) * cd);
-            m = mn;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                // chunks with no finite entry carry 0 (or NaN, which must propagate)
-                S += x[q].m == -INFINITY ? x[q].s : x[q].s * exp2((double)(x[q].m - m) * cd);
-                nk += x[q].nkept;
-            }
-        }
-        const float thr = a.topk ? a.row_thr[prow] : -INFINITY;
-        s_m[r] = m;
-        s_S[r] = S;
-        s_thr[r] = thr;
-        if (!(S > 0.0 && S < INFINITY && m > -INFINITY)) atomicOr(&s_rowbad, 1);
-        if (a.dbg.row_max) a.dbg.row_max[prow] = m;
-        if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
-        if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
-        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
-    }
-    __syncthreads();
-    if (tid < kWave) {
-        // lane i: proposal i (k <= SPECDEC_MAX_K = kWave)
-        int flags = 0;
-        bool acc = true;
-        double P = 0.0, Q = 0.0;
-        int y = 0;
-        if (lane < k) {
-            y = a.tokens[lo + lane];
-            const double u = (double)a.u_acc[lo + lane];
-            if (!(u >= 0.0 && u < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-            if (y < 0 || y >= a.V) {
-                flags |= SPECDEC_ERR_TOKEN;
-            } else {
-                const float zt = load_elem(a.tgt + (size_t)(lo + b + lane) * a.V * Lt::ES, y, BF16);
-                const float zd = load_elem(a.dft + (size_t)(lo + lane) * a.V * Lt::ES, y, BF16);
-                const int rt = lane, rd = k + 1 + lane;
-                if (zt >= s_thr[rt] && zt > -INFINITY)
-                    P = exp2(((double)zt - (double)s_m[rt]) * cd) / s_S[rt];
-                if (zd >= s_thr[rd] && zd > -INFINITY)
-                    Q = exp2(((double)zd - (double)s_m[rd]) * cd) / s_S[rd];
-                acc = u * Q < P;
-            }
-        }
-        const double us = (double)a.u_smp[b];
-        if (lane == 0 && !(us >= 0.0 && us < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-        if (lane == 0 && s_rowbad) flags |= SPECDEC_ERR_NONFINITE;
-        const unsigned long long rej = __ballot(lane < k && !acc);
-        const int j = rej ? (__ffsll((long long)rej) - 1) : k;
-        if (lane < k && lane <= j && Q == 0.0 && !(flags & SPECDEC_ERR_TOKEN)) flags |= SPECDEC_ERR_QZERO;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
-        const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
-        if (lane < k) {
-            if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
-            if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
-        }
-        if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
-        if (lane == 0) {
-            a.num_acc[b] = err ? -1 : j;
-            a.num_emit[b] = err ? 0 : j + 1;
-            if (flags) atomicOr(a.err_word, flags);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
-            Decision d;
-            d.flags = flags;
-            d.err = err;
-            d.a = j;
-            d.k = k;
-            d.pad = 0;
-            d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
-            d.row_t = lo + b + j;
-            d.row_d = j < k ? lo + j : 0;
-            const float mt = s_m[j];
-            d.mc_t = mt * a.c;
-            d.al_t = exp2(-(double)fmaf(mt, a.c, -d.mc_t)) / s_S[j];
-            d.thr_t = s_thr[j];
-            if (j < k) {
-                const float md = s_m[k + 1 + j];
-                d.mc_d = md * a.c;
-                d.al_d = exp2(-(double)fmaf(md, a.c, -d.mc_d)) / s_S[k + 1 + j];
-                d.thr_d = s_thr[k + 1 + j];
-            } else {
-                d.mc_d = 0.f;
-                d.al_d = 0.0;
-                d.thr_d = INFINITY;
-            }
-            d.u = a.u_smp[b];
-            D = d;
-        }
-    }
-    __syncthreads();
-    if (D.mode == MODE_NONE) return;
-    Decision r = D;
-    bool resid = r.mode == MODE_RESID;
-    const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
-    const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
-    const int nch = (a.V + kSChunk - 1) / kSChunk;
-
-    // ---- 2. chunk sums of the weights -------------------------------------------------
-    chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, resid, s_wp, s_cs);
-    if (tid == 0) {
-        double W = 0.0;
-        for (int q = 0; q < nch; ++q) W += s_cs[q];
-        s_W = W;
-    }
-    __syncthreads();
-    if (resid && !(s_W > 0.0)) {
-        // residual mass 0 after a rejection: draw the replacement from p_j instead
-        resid = false;
-        r.flags |= SPECDEC_ERR_ZFALLBACK;
-        chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, false, s_wp, s_cs);
-        if (tid == 0) {
-            double W = 0.0;
-            for (int q = 0; q < nch; ++q) W += s_cs[q];
-            s_W = W;
-            atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
-        }
-        __syncthreads();
-    }
-
-    // ---- 3. inverse CDF ---------------------------------------------------------------
-    const double W = s_W;
-    const double t = (double)r.u * W;
-    if (tid == 0) {
-        double C = 0.0;
-        int q = 0;
-        for (; q < nch; ++q) {
-            if (C + s_cs[q] > t) break;
-            C += s_cs[q];
-        }
-        if (q == nch) {   // unreachable while t < W; keep the last non-empty chunk
-            q = nch - 1;
-            while (q > 0 && !(s_cs[q] > 0.0)) --q;
-            C = 0.0;
-            for (int i = 0; i < q; ++i) C += s_cs[i];
-        }
-        s_chunk = q;
-        s_base = C;
-    }
-    __syncthreads();
-    const int i0 = s_chunk * kSChunk + tid * 8;
-    float t8[8], d8[8];
-    load8<BF16, VEC>(trow, a.V, i0, t8);
-    if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
-    double w[8], run = 0.0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
-        run += w[e];
-    }
-    double tot;
-    double C = s_base + block_excl_scan_d<kSNT>(run, redd, &tot);
-    int mine = 0x7fffffff, lastpos = -1;
-    double wmine = 0.0, wlast = 0.0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        C += w[e];
-        if (mine == 0x7fffffff && C > t) {
-            mine = i0 + e;
-            wmine = w[e];
-        }
-        if (w[e] > 0.0) {
-            lastpos = i0 + e;
-            wlast = w[e];
-        }
-    }
-    int found = block_min_i<kSNT>(mine, redi);
-    if (found != 0x7fffffff) {
-        if (mine == found) s_wpick = wmine;
-    } else {
-        found = block_max_i<kSNT>(lastpos, redi);
-        if (found >= 0 && lastpos == found) s_wpick = wlast;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        a.out_tokens[lo + b + r.a] = found;
-        if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W;
-        if (a.dbg.picked_prob) a.dbg.picked_prob[b] = s_wpick / W;
-        if (a.dbg.req_flags) a.dbg.req_flags[b] = r.flags;
-    }
-}
-
-// ---------------------------------------------------------------------------------------
-// Host side.
-// ---------------------------------------------------------------------------------------
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-struct WsPlan {
-    size_t part, thr, total;
-    int nparts, nchunks;
-};
-
-static bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
-
-static WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
-    WsPlan p{};
-    // the vector and scalar layouts use the same chunk length
-    const int ch = dtype == SPECDEC_BF16 ? Layout<true, true>::CH : Layout<false, true>::CH;
-    p.nchunks = (V + ch - 1) / ch;
-    p.nparts = topk_active(top_k, V) ? 1 : p.nchunks;
-    const size_t rows = (size_t)2 * K + B;
-    size_t off = 0;
-    p.part = off;
-    off = align256(off + rows * p.nparts * sizeof(RowPartial));
-    p.thr = off;
-    off = align256(off + rows * sizeof(float));
-    p.total = off;
-    return p;
+    sample_body<BF16, VEC>(a, blockIdx.x);
 }
 
 template <bool BF16, bool VEC>

@@ -9,23 +9,36 @@ import pytest
 
 from gpu_harness import (KVOnDevice, VerifyOnDevice, compare_kv_data, compare_kv_meta,
                          compare_verify, log, oracle_kv, oracle_verify)
-from rejection_sampling_verify_specdec_amd import synth
+import torch
+
+from rejection_sampling_verify_specdec_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("mode", ["calls", "fused"])
 @pytest.mark.parametrize("wl", ["c1", "c2", "c3", "c4"])
-def test_cycle(wl):
+def test_cycle(wl, mode):
     vin = synth.make_verify(wl, seed=0)
     log(f"[cycle] {wl}: B={vin.B} K={vin.K} V={vin.V}; oracle verify")
     o = oracle_verify(vin, keep_probs=False)
     kv = synth.make_kv(wl, vin, seed=0, a_hint=o.num_accepted)
-    log(f"[cycle] {wl}: NB={kv.num_blocks} L={kv.L}; GPU cycle")
+    log(f"[cycle] {wl}: NB={kv.num_blocks} L={kv.L}; GPU cycle ({mode})")
     g_kv = KVOnDevice(kv, vin.B)
     g_v = VerifyOnDevice(vin)
-    g_kv.append()
-    g_v.run()
-    g_kv.rollback(g_v.num_acc, g_v.cu)
+    if mode == "calls":
+        g_kv.append()
+        g_v.run()
+        g_kv.rollback(g_v.num_acc, g_v.cu)
+    else:
+        dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+        ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, vin.top_k),
+                         dtype=torch.uint8, device=g_v.tgt.device)
+        binding.specdec_cycle(g_kv.cache, g_kv.k_new, g_kv.v_new, g_v.tgt, g_v.dft, g_v.tokens,
+                              g_v.cu, g_v.u_acc, g_v.u_smp, max_k=vin.max_k, temperature=vin.T,
+                              top_k=vin.top_k, out_tokens=g_v.out_tokens,
+                              num_accepted=g_v.num_acc, num_emitted=g_v.num_emit,
+                              err_word=g_v.err, workspace=ws, debug=g_v.dbg)
     g = g_v.result()
     rep = compare_verify(vin, g, o)
     log(f"[cycle] {wl}: {rep}")
@@ -41,3 +54,58 @@ def test_cycle(wl):
         # rejected requests end exactly on a block boundary
         rej = [b for b in range(vin.B) if 0 <= g.num_accepted[b] < vin.k_b[b]]
         assert all(o_kv.seq_lens[b] % kv.block_size == 0 for b in rej)
+
+
+def _run_mode(vin, kv, mode, free_count=None, cu_override=None):
+    g_kv = KVOnDevice(kv, vin.B)
+    if free_count is not None:
+        g_kv.cache.free_count.fill_(free_count)
+    g_v = VerifyOnDevice(vin)
+    if cu_override is not None:
+        g_v.cu.copy_(torch.tensor(cu_override, dtype=torch.int32))
+    if mode == "calls":
+        g_kv.append(cu_new=g_v.cu + torch.arange(vin.B + 1, dtype=torch.int32, device=g_v.cu.device))
+        g_v.run()
+        g_kv.rollback(g_v.num_acc, g_v.cu)
+    else:
+        dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+        ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, vin.top_k),
+                         dtype=torch.uint8, device=g_v.tgt.device)
+        binding.specdec_cycle(g_kv.cache, g_kv.k_new, g_kv.v_new, g_v.tgt, g_v.dft, g_v.tokens,
+                              g_v.cu, g_v.u_acc, g_v.u_smp, max_k=vin.max_k, temperature=vin.T,
+                              top_k=vin.top_k, out_tokens=g_v.out_tokens,
+                              num_accepted=g_v.num_acc, num_emitted=g_v.num_emit,
+                              err_word=g_v.err, workspace=ws, debug=g_v.dbg)
+    g = g_v.result()
+    return g, g_kv.meta(), g_kv.pool.view(torch.int16).cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["normal", "nomem", "bad_offsets", "topk"])
+def test_fused_cycle_equals_three_calls(case):
+    # small geometry, shared prefixes and a fragmented pool; the fused launches must give
+    # bit-identical outputs, metadata and pool contents
+    over = dict(top_k=8) if case == "topk" else {}
+    vin = synth.make_verify("c4", seed=31, B=12, V=2048, **over)
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=520, prefix_hi=700, share_group=4,
+                         share_blocks=32)
+    kv = synth.make_kv("c4", vin, seed=31, recipe=rec)
+    kw = {}
+    if case == "nomem":
+        kw["free_count"] = 3
+    if case == "bad_offsets":
+        cu = vin.cu_draft.copy()
+        cu[-1] += 1
+        kw["cu_override"] = cu
+    log(f"[fused-vs-calls] {case}")
+    a = _run_mode(vin, kv, "calls", **kw)
+    b = _run_mode(vin, kv, "fused", **kw)
+    for f in ("num_accepted", "num_emitted", "out_tokens", "err_word", "p_y", "q_y", "row_sum",
+              "resid_mass", "picked_prob", "req_flags"):
+        assert np.array_equal(np.asarray(getattr(a[0], f)), np.asarray(getattr(b[0], f))), f
+    for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
+        assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
+    assert np.array_equal(a[2], b[2])
+    if case == "nomem":
+        assert a[1]["state"] & binding.KV_ERR_NOMEM
+    if case == "bad_offsets":
+        assert a[1]["state"] & binding.KV_ERR_APPEND and (a[0].num_accepted == -1).all()
