@@ -22,9 +22,9 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra=None) -> str:
+def build(verbose: bool = False, extra=None, out: str = LIB) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, "-o", tmp,
            *[os.path.join(CSRC, s) for s in SOURCES]]
     if verbose:
@@ -33,8 +33,8 @@ def build(verbose: bool = False, extra=None) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError(f"hipcc failed with exit code {r.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,13 +1,15 @@
-// One whole speculative cycle in three launches (gfx950): the same work and results as
-// kv_paged_append -> specdec_verify -> kv_rollback on one stream, scheduled so that
-// latency-bound work rides along with bandwidth-bound work.
+// One whole speculative cycle in four launches (gfx950): the same work and results as
+// kv_paged_append -> specdec_verify -> kv_rollback on one stream, with the latency-bound
+// pieces folded into launches that are busy streaming memory anyway.
 //
 //   k_cycle_stats   workgroup 0 allocates the cycle's blocks (copy-on-write, LIFO pops,
 //                   destination rows) while every other workgroup streams logit rows
 //                   (row statistics, or the top-k row kernel);
-//   k_cycle_sample  workgroups [0, B) decide and draw each request's tokens; the rest
-//                   scatter the candidate K/V into their slots meanwhile;
-//   k_kv_rollback   truncates every request to its committed prefix.
+//   k_cycle_decide  K/V scatter workgroups, then one workgroup per request for its
+//                   accept / reject decisions;
+//   k_part          (request, chunk) workgroups sum the sampling weights chunk by chunk;
+//   k_cycle_pick    workgroup 0 truncates every request to its committed prefix while the
+//                   others draw each request's replacement / bonus token.
 //
 // The cycle is the one the pages describe ("Walk through KV-cache updates when
 // speculative decoding rejects some draft tokens": K/V for the candidates are appended by
@@ -28,6 +30,7 @@
 namespace sd {
 
 constexpr int kCycAllocNT = kNT;   // allocation workgroup inside the statistics launch
+constexpr int kCycScatterPPT = 1;  // 16-byte pieces per scatter thread (many small groups)
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __restrict__ cu,
@@ -58,26 +61,40 @@ __global__ __launch_bounds__(kTopkNT) void k_cycle_topk(KvArgs kv, const int* __
     topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
 }
 
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kSNT) void k_cycle_sample(SampleArgs sa, KvArgs kv,
-                                                       const uint8_t* __restrict__ knew,
-                                                       const uint8_t* __restrict__ vnew, int N,
-                                                       int tpw, int ntiles,
-                                                       const uint8_t* __restrict__ aws) {
+static_assert(kDecideNT == kScNT, "decision and scatter workgroups share one launch");
+
+template <bool BF16>
+__global__ __launch_bounds__(kDecideNT) void k_cycle_decide(SampleArgs sa, KvArgs kv,
+                                                            const uint8_t* __restrict__ knew,
+                                                            const uint8_t* __restrict__ vnew,
+                                                            int N, int tpw, int ntiles,
+                                                            const uint8_t* __restrict__ aws) {
+    // scatter workgroups are dispatched first; the short decision workgroups come last and
+    // finish in the scatter's tail
+    const int planes = kv.L * 2;
+    const int nscat = ntiles * planes;
     const int bid = blockIdx.x;
-    if (bid < sa.B) {
-        sample_body<BF16, VEC>(sa, bid);
+    if (bid >= nscat) {
+        decide_kernel_body<BF16, kDecideNT>(sa, bid - nscat);
         return;
     }
-    const int s = bid - sa.B;
-    const int planes = kv.L * 2;
-    scatter_body(kv, knew, vnew, sa.B, N, tpw, aws, s / planes, s % planes, s, ntiles * planes,
-                 kSNT);
+    const int s = bid;
+    scatter_body<kCycScatterPPT>(kv, knew, vnew, sa.B, N, tpw, aws, s / planes, s % planes, s,
+                                 ntiles * planes, kScNT);
 }
 
-__global__ __launch_bounds__(kKvNT) void k_cycle_rollback(KvArgs a, const int* __restrict__ num_acc,
-                                                          const int* __restrict__ cu, int B) {
-    rollback_body(a, num_acc, cu, B);
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa) {
+    part_body<BF16, VEC, kPartNT>(sa, blockIdx.x / sa.nch, blockIdx.x % sa.nch);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa, KvArgs kv) {
+    if (blockIdx.x == 0) {
+        rollback_body(kv, sa.num_acc, sa.cu, sa.B);
+        return;
+    }
+    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x - 1);
 }
 
 template <bool BF16, bool VEC>
@@ -100,11 +117,13 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
                               p.nchunks, c, part);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
-    const int tpw = scatter_tokens_per_wg(kv, kSNT);
+    const int tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);
     const int ntiles = (N + tpw - 1) / tpw;
-    hipLaunchKernelGGL((k_cycle_sample<BF16, VEC>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
-                       dim3(kSNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
-    hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, kv, sa.num_acc, cu, B);
+    hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
+                       dim3(kDecideNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
+    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch), dim3(kPartNT), 0, st,
+                       sa);
+    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B + 1), dim3(kPickNT), 0, st, sa, kv);
 }
 
 }  // namespace sd
@@ -170,10 +189,13 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.max_k = max_k;
     sa.V = V;
     sa.nparts = p.nparts;
+    sa.nch = p.nch;
     sa.topk = topk_active(top_k, V);
     sa.c = c;
     sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
+    sa.rec = reinterpret_cast<Decision*>(vws + p.rec);
+    sa.wsum = reinterpret_cast<double*>(vws + p.wsum);
     sa.out_tokens = out_tokens;
     sa.num_acc = num_accepted;
     sa.num_emit = num_emitted;

@@ -232,6 +232,7 @@ SD_DEV void alloc_body(const KvArgs& a, const int* __restrict__ cu, int derive, 
 // layer / K-V plane lk; each thread moves 16-byte pieces of token rows to the
 // destination rows the allocation wrote. Then the copy-on-write copies, grid-stride over
 // (entry, layer, K/V).
+template <int P>
 SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
                          const uint8_t* __restrict__ vnew, int B, int N, int tpw,
                          const uint8_t* __restrict__ wsb, int tile, int lk, int wg, int nwg,
@@ -246,15 +247,32 @@ SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
     const long long* drow = reinterpret_cast<const long long*>(wsb + 16 + (size_t)40 * B);
     const uint8_t* src_base = (lk & 1) ? vnew : knew;
     uint8_t* dst_base = a.pool + (size_t)lk * a.NB * a.bs * ub;
-    for (int idx = tid; idx < tpw * lanes; idx += nt) {
-        const int tok = idx / lanes, q = idx - tok * lanes;
-        const int t = t0 + tok;
-        if (t >= N) break;
-        const long long d = drow[t];
-        if (d < 0) continue;
-        const u32x4* src = reinterpret_cast<const u32x4*>(src_base + ((size_t)l * N + t) * ub) + q;
-        u32x4* dst = reinterpret_cast<u32x4*>(dst_base + (size_t)d * ub) + q;
-        __builtin_nontemporal_store(__builtin_nontemporal_load(src), dst);
+    // P 16-byte pieces per thread in flight: all loads first, then the stores (the
+    // destination row is re-read at store time to keep registers for the data)
+    const int pieces = tpw * lanes;
+    for (int base = 0; base < pieces; base += P * nt) {
+        u32x4 v[P];
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int idx = base + u * nt + tid;
+            const int tok = idx / lanes;
+            const int t = t0 + tok;
+            if (idx < pieces && t < N && drow[t] >= 0)
+                v[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4*>(src_base + ((size_t)l * N + t) * ub) + (idx - tok * lanes));
+        }
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int idx = base + u * nt + tid;
+            const int tok = idx / lanes;
+            const int t = t0 + tok;
+            if (idx < pieces && t < N) {
+                const long long d = drow[t];
+                if (d >= 0)
+                    __builtin_nontemporal_store(
+                        v[u], reinterpret_cast<u32x4*>(dst_base + (size_t)d * ub) + (idx - tok * lanes));
+            }
+        }
     }
     const int ncow = ws[1];
     if (ncow > 0) {
@@ -431,9 +449,11 @@ static inline KvArgs args_of(const kv_paged_cache* c) {
     return a;
 }
 
-static inline int scatter_tokens_per_wg(const KvArgs& a, int nt) {
+// Tokens per scatter workgroup for about `ppt` 16-byte pieces per thread.
+static inline int scatter_tokens_per_wg(const KvArgs& a, int nt, int ppt) {
     const int lanes = (int)((size_t)a.H * a.D * 2 / 16);
-    return lanes >= nt ? 1 : (nt / lanes < kScMaxTok ? nt / lanes : kScMaxTok);
+    const int t = (ppt * nt) / lanes;
+    return t < 1 ? 1 : (t > kScMaxTok * 8 ? kScMaxTok * 8 : t);
 }
 
 }  // namespace sd

@@ -7,19 +7,22 @@
 // decoding transform (temperature, top-k) applied identically to target and draft rows
 // and a max-subtracted (stable) softmax (same page, section 6).
 //
-// Pipeline on one stream, per call (two kernels):
+// Pipeline on one stream, per call (four kernels):
 //   k_row_stats   every target and draft row is streamed once in 16K-element chunks with
 //                 128-bit loads; each workgroup writes the chunk max m_c and
 //                 S_c = sum exp2((z - m_c) * c), c = log2(e) / T, as an fp32/fp64 pair.
 //   k_topk_rows   (top-k only, replaces k_row_stats) one workgroup per row: exact top-k
 //                 threshold, max, kept count and kept-set sum.
-//   k_sample      one workgroup per (request, chunk): combines the row partials in fp64,
-//                 evaluates p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p, finds
-//                 the first rejection; sums the sampling weights of its chunk of the one
-//                 row pair (or bonus row) still to be sampled; the request's last workgroup
-//                 locates t = u * W among the chunk sums and scans that chunk in ascending
-//                 token order for the smallest x with C(x) > t. Rows after the first
-//                 rejection are never re-read (ragged early exit).
+//   k_decide      one workgroup per request: combines the row partials in fp64, evaluates
+//                 p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p left to right,
+//                 finds the first rejection, publishes the accepted tokens and stores the
+//                 parameters of the one row pair (or bonus row) still to be sampled.
+//   k_part        one workgroup per (request, 8192-token chunk): sum of the sampling
+//                 weights over its chunk of that row (pair). Rows after the first
+//                 rejection are never read again (ragged early exit).
+//   k_pick        one workgroup per request: W from the chunk sums, t = u * W, the chunk
+//                 holding t scanned in ascending token order (LDS prefix scan) for the
+//                 smallest x with C(x) > t.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -48,9 +51,19 @@ __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict
     topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
 }
 
+template <bool BF16>
+__global__ __launch_bounds__(kDecideNT) void k_decide(SampleArgs a) {
+    decide_kernel_body<BF16, kDecideNT>(a, blockIdx.x);
+}
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kSNT) void k_sample(SampleArgs a) {
-    sample_body<BF16, VEC>(a, blockIdx.x);
+__global__ __launch_bounds__(kPartNT) void k_part(SampleArgs a) {
+    part_body<BF16, VEC, kPartNT>(a, blockIdx.x / a.nch, blockIdx.x % a.nch);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kPickNT) void k_pick(SampleArgs a) {
+    pick_body<BF16, VEC, kPickNT>(a, blockIdx.x);
 }
 
 template <bool BF16, bool VEC>
@@ -71,7 +84,9 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                               0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
-    hipLaunchKernelGGL((k_sample<BF16, VEC>), dim3(B), dim3(kSNT), 0, st, sa);
+    hipLaunchKernelGGL((k_decide<BF16>), dim3(B), dim3(kDecideNT), 0, st, sa);
+    hipLaunchKernelGGL((k_part<BF16, VEC>), dim3((unsigned)B * p.nch), dim3(kPartNT), 0, st, sa);
+    hipLaunchKernelGGL((k_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
 }
 
 }  // namespace sd
@@ -127,10 +142,13 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.max_k = max_k;
     sa.V = V;
     sa.nparts = p.nparts;
+    sa.nch = p.nch;
     sa.topk = topk_active(top_k, V);
     sa.c = c;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
+    sa.rec = reinterpret_cast<Decision*>(ws + p.rec);
+    sa.wsum = reinterpret_cast<double*>(ws + p.wsum);
     sa.out_tokens = out_tokens;
     sa.num_acc = num_accepted;
     sa.num_emit = num_emitted;

@@ -54,13 +54,19 @@ SD_DEV void load_chunk(const uint8_t* __restrict__ row, int V, int c0,
         const u32x4* p = reinterpret_cast<const u32x4*>(row);
         u32x4 raw[Lt::COLS];
         const uint32_t fill = BF16 ? 0xff80ff80u : 0xff800000u;
+        if (c0 + Lt::CH <= V) {                // whole chunk inside the row
 #pragma unroll
-        for (int col = 0; col < Lt::COLS; ++col) {
-            const int i0 = c0 + (col * kNT + tid) * Lt::PER;
-            if (i0 < V) {
-                raw[col] = __builtin_nontemporal_load(p + i0 / Lt::EPV);
-            } else {
-                raw[col] = (u32x4){fill, fill, fill, fill};
+            for (int col = 0; col < Lt::COLS; ++col)
+                raw[col] = __builtin_nontemporal_load(p + (c0 + (col * kNT + tid) * Lt::PER) / Lt::EPV);
+        } else {
+#pragma unroll
+            for (int col = 0; col < Lt::COLS; ++col) {
+                const int i0 = c0 + (col * kNT + tid) * Lt::PER;
+                if (i0 < V) {
+                    raw[col] = __builtin_nontemporal_load(p + i0 / Lt::EPV);
+                } else {
+                    raw[col] = (u32x4){fill, fill, fill, fill};
+                }
             }
         }
 #pragma unroll
@@ -265,10 +271,19 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // Nothing crosses workgroups, so no device-scope fence is needed; rows after the first
 // rejection are never read.
 // ---------------------------------------------------------------------------------------
-constexpr int kSNT = 1024;                 // threads of the sampling workgroup
-constexpr int kSW = kSNT / kWave;          // its waves
-constexpr int kSChunk = kSNT * 8;          // tokens per sampling chunk
+constexpr int kDecideNT = 256;             // threads of a decision workgroup (>= 2*64+1 rows)
+constexpr int kPartNT = 256;               // threads of a chunk-sum workgroup
+constexpr int kPickNT = 1024;              // threads of a pick workgroup
+constexpr int kSChunk = 8192;              // tokens per sampling chunk
 constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
+
+struct Decision {
+    int flags, err, a, k, mode, row_t, row_d, pad;
+    float mc_t, mc_d, thr_t, thr_d;
+    double al_t, al_d;
+    float u;
+    int pad2, pad3, pad4;
+};
 
 struct SampleArgs {
     const uint8_t* tgt;
@@ -280,9 +295,12 @@ struct SampleArgs {
     int B, K, max_k, V;
     int nparts;              // statistics partials per row
     int topk;                // 1 when rows carry a top-k threshold
+    int nch;                 // sampling chunks per row
     float c;
     const RowPartial* part;
     const float* row_thr;
+    Decision* rec;           // [B] each request's decision, for the draw
+    double* wsum;            // [B][nch] chunk sums of the sampling weights
     int* out_tokens;
     int* num_acc;
     int* num_emit;
@@ -290,33 +308,32 @@ struct SampleArgs {
     specdec_debug dbg;
 };
 
-struct Decision {
-    int flags, err, a, k, mode, row_t, row_d, pad;
-    float mc_t, mc_d, thr_t, thr_d;
-    double al_t, al_d;
-    float u;
-};
-
 constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
 
-// Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection, p(x) for the
-// bonus; p and q in fp64 from fp32 exponentials of the same form the statistics used.
-SD_DEV double weight(float zt, float zd, const Decision& r, float c, bool resid) {
-    const double pt = zt >= r.thr_t
-                          ? (double)__builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * r.al_t
-                          : 0.0;
-    if (!resid) return pt;
-    const double pd = zd >= r.thr_d
-                          ? (double)__builtin_amdgcn_exp2f(fmaf(zd, c, -r.mc_d)) * r.al_d
-                          : 0.0;
+// Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection (RESID), p(x)
+// for the bonus; p and q in fp64 from fp32 exponentials of the same form the statistics
+// used. TOPK masks tokens below the rows' thresholds.
+template <bool RESID, bool TOPK>
+SD_DEV double weight_t(float zt, float zd, const Decision& r, float c) {
+    double pt = (double)__builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * r.al_t;
+    if (TOPK && !(zt >= r.thr_t)) pt = 0.0;
+    if (!RESID) return pt;
+    double pd = (double)__builtin_amdgcn_exp2f(fmaf(zd, c, -r.mc_d)) * r.al_d;
+    if (TOPK && !(zd >= r.thr_d)) pd = 0.0;
     return fmax(pt - pd, 0.0);
 }
 
-// Eight consecutive elements starting at i0 (a multiple of 8); -inf at or past V.
-template <bool BF16, bool VEC>
+SD_DEV double weight(float zt, float zd, const Decision& r, float c, bool resid) {
+    if (resid) return weight_t<true, true>(zt, zd, r, c);
+    return weight_t<false, true>(zt, zd, r, c);
+}
+
+// Eight consecutive elements starting at i0 (a multiple of 8); -inf at or past V. FULL
+// promises i0 + 8 <= V (no bounds test).
+template <bool BF16, bool VEC, bool FULL = false>
 SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8]) {
     if constexpr (VEC && BF16) {
-        if (i0 < V) {
+        if (FULL || i0 < V) {
             const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 8);
             const uint32_t q[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -331,7 +348,7 @@ SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8])
     } else if constexpr (VEC) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            if (i0 + 4 * h < V) {
+            if (FULL || i0 + 4 * h < V) {
                 const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + i0 / 4 + h);
                 z[4 * h] = __uint_as_float(w.x);
                 z[4 * h + 1] = __uint_as_float(w.y);
@@ -344,81 +361,47 @@ SD_DEV void load8(const uint8_t* __restrict__ row, int V, int i0, float (&z)[8])
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[j] = i0 + j < V ? load_elem(row, i0 + j, BF16) : -INFINITY;
+        for (int j = 0; j < 8; ++j) z[j] = (FULL || i0 + j < V) ? load_elem(row, i0 + j, BF16) : -INFINITY;
     }
 }
 
-// Per-chunk weight sums of the row (pair) into s_cs[0 .. nch): wave sums in LDS, then a
-// fixed-order sum over the 16 waves.
-template <bool BF16, bool VEC>
-SD_DEV void chunk_sums(const uint8_t* trow, const uint8_t* drow, int V, int nch,
-                       const Decision& r, float c, bool resid, double (*s_wp)[kSW],
-                       double* s_cs) {
-    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    for (int c0 = 0; c0 < nch; c0 += 4) {
-        float zt[4][8], zd[4][8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i0 = (c0 + u) * kSChunk + tid * 8;
-            load8<BF16, VEC>(trow, (c0 + u) < nch ? V : 0, i0, zt[u]);
-            if (resid) load8<BF16, VEC>(drow, (c0 + u) < nch ? V : 0, i0, zd[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            double acc = 0.0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc += weight(zt[u][e], resid ? zd[u][e] : -INFINITY, r, c, resid);
-            acc = wave_sum(acc);
-            if (lane == 0 && c0 + u < nch) s_wp[c0 + u][wave] = acc;
-        }
-    }
-    __syncthreads();
-    for (int q = tid; q < nch; q += kSNT) {
-        double x = 0.0;
-#pragma unroll
-        for (int w = 0; w < kSW; ++w) x += s_wp[q][w];
-        s_cs[q] = x;
-    }
-    __syncthreads();
-}
-
-template <bool BF16, bool VEC>
-SD_DEV void sample_body(const SampleArgs& a, int b) {
-    using Lt = Layout<BF16, VEC>;
+// Decision of request b, computed by one workgroup of NT threads (all threads call): the
+// row partials are combined in fp64, p_i(y_i) and q_i(y_i) evaluated in fp64, proposals
+// accepted left to right while u * q < p. The result lands in D (LDS). With `publish` the
+// workgroup also writes num_accepted / num_emitted, the accepted tokens, the error word
+// and the diagnostics.
+template <bool BF16, int NT>
+SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
+    using Lt = Layout<BF16, true>;
     __shared__ float s_m[kMaxRows];
     __shared__ double s_S[kMaxRows];
     __shared__ float s_thr[kMaxRows];
     __shared__ int s_rowbad;
-    __shared__ Decision D;
-    __shared__ double redd[kSW];
-    __shared__ int redi[kSW];
-    __shared__ double s_wp[kSMaxChunks][kSW];
-    __shared__ double s_cs[kSMaxChunks];
-    __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_chunk;
-
     const int tid = threadIdx.x, lane = tid % kWave;
     const int rows_t = a.K + a.B;
     const double cd = (double)a.c;
 
-    // ---- 1. decision ------------------------------------------------------------------
     const int lo = a.cu[b], hi = a.cu[b + 1];
     const int k = hi - lo;
     const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
                        hi > a.K;
     if (bad_k) {
         if (tid == 0) {
-            a.num_acc[b] = -1;
-            a.num_emit[b] = 0;
-            atomicOr(a.err_word, SPECDEC_ERR_K);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = SPECDEC_ERR_K;
+            D.mode = MODE_NONE;
+            D.flags = SPECDEC_ERR_K;
+            if (publish) {
+                a.num_acc[b] = -1;
+                a.num_emit[b] = 0;
+                atomicOr(a.err_word, SPECDEC_ERR_K);
+                if (a.dbg.req_flags) a.dbg.req_flags[b] = SPECDEC_ERR_K;
+            }
         }
+        __syncthreads();
         return;
     }
     if (tid == 0) s_rowbad = 0;
     __syncthreads();
-    const int nrows = 2 * k + 1;   // <= kMaxRows <= kSNT
+    const int nrows = 2 * k + 1;   // <= kMaxRows <= NT
     if (tid < nrows) {
         const int r = tid;
         const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
@@ -453,10 +436,12 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
         s_S[r] = S;
         s_thr[r] = thr;
         if (!(S > 0.0 && S < INFINITY && m > -INFINITY)) atomicOr(&s_rowbad, 1);
-        if (a.dbg.row_max) a.dbg.row_max[prow] = m;
-        if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
-        if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
-        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
+        if (publish) {
+            if (a.dbg.row_max) a.dbg.row_max[prow] = m;
+            if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
+            if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
+            if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = a.topk ? nk : -1;
+        }
     }
     __syncthreads();
     if (tid < kWave) {
@@ -491,22 +476,26 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
         const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
-        if (lane < k) {
-            if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
-            if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
+        if (publish) {
+            if (lane < k) {
+                if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
+                if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
+            }
+            if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
+            if (lane == 0) {
+                a.num_acc[b] = err ? -1 : j;
+                a.num_emit[b] = err ? 0 : j + 1;
+                if (flags) atomicOr(a.err_word, flags);
+                if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
+            }
         }
-        if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
         if (lane == 0) {
-            a.num_acc[b] = err ? -1 : j;
-            a.num_emit[b] = err ? 0 : j + 1;
-            if (flags) atomicOr(a.err_word, flags);
-            if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
             Decision d;
             d.flags = flags;
             d.err = err;
             d.a = j;
             d.k = k;
-            d.pad = 0;
+            d.pad = d.pad2 = d.pad3 = d.pad4 = 0;
             d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
             d.row_t = lo + b + j;
             d.row_d = j < k ? lo + j : 0;
@@ -529,15 +518,99 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
         }
     }
     __syncthreads();
-    if (D.mode == MODE_NONE) return;
-    Decision r = D;
+}
+
+// Sum of the sampling weights over one chunk (kSChunk tokens) of the row (pair) still to
+// be sampled, by a workgroup of NT threads; every group of 8 tokens of the thread is in
+// flight at once. Fixed reduction order.
+template <bool BF16, bool VEC, int NT, bool RESID, bool TOPK>
+SD_DEV double chunk_weight_sum_t(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
+                                 const Decision& r, float c, double* redd) {
+    constexpr int PT = kSChunk / (NT * 8);     // groups of 8 tokens per thread
+    const int tid = threadIdx.x;
+    float zt[PT][8], zd[PT][8];
+    if ((chunk + 1) * kSChunk <= V) {          // whole chunk inside the row
+#pragma unroll
+        for (int g = 0; g < PT; ++g) {
+            const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
+            load8<BF16, VEC, true>(trow, V, i0, zt[g]);
+            if (RESID) load8<BF16, VEC, true>(drow, V, i0, zd[g]);
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < PT; ++g) {
+            const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
+            load8<BF16, VEC>(trow, V, i0, zt[g]);
+            if (RESID) load8<BF16, VEC>(drow, V, i0, zd[g]);
+        }
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int g = 0; g < PT; ++g) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += weight_t<RESID, TOPK>(zt[g][e], zd[g][e], r, c);
+    }
+    return block_sum<NT>(acc, redd);
+}
+
+template <bool BF16, bool VEC, int NT>
+SD_DEV double chunk_weight_sum(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
+                               const Decision& r, float c, bool resid, bool topk, double* redd) {
+    if (resid) {
+        if (topk) return chunk_weight_sum_t<BF16, VEC, NT, true, true>(trow, drow, V, chunk, r, c, redd);
+        return chunk_weight_sum_t<BF16, VEC, NT, true, false>(trow, drow, V, chunk, r, c, redd);
+    }
+    if (topk) return chunk_weight_sum_t<BF16, VEC, NT, false, true>(trow, drow, V, chunk, r, c, redd);
+    return chunk_weight_sum_t<BF16, VEC, NT, false, false>(trow, drow, V, chunk, r, c, redd);
+}
+
+// Decision kernel body: one workgroup per request publishes its decision and stores it
+// for the sampling workgroups.
+template <bool BF16, int NT>
+SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
+    __shared__ Decision D;
+    decide_body<BF16, NT>(a, b, true, D);
+    if (threadIdx.x == 0) a.rec[b] = D;
+}
+
+// Sampling, part 1: workgroup (b, chunk) writes the chunk sum of the weights of the row
+// (pair) b still has to sample. Rows after the first rejection are never read.
+template <bool BF16, bool VEC, int NT>
+SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
+    using Lt = Layout<BF16, VEC>;
+    __shared__ double redd[NT / kWave];
+    const Decision r = a.rec[b];
+    if (r.mode == MODE_NONE) return;
+    const bool resid = r.mode == MODE_RESID;
+    const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
+    const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
+    const double s = chunk_weight_sum<BF16, VEC, NT>(trow, drow, a.V, chunk, r, a.c, resid,
+                                                     a.topk != 0, redd);
+    if (threadIdx.x == 0) a.wsum[(size_t)b * a.nch + chunk] = s;
+}
+
+// Sampling, part 2: workgroup b turns the chunk sums into W, finds the chunk holding
+// t = u * W and scans it in ascending token order (each thread owns kSChunk / NT
+// consecutive tokens) for the smallest x with C(x) > t.
+template <bool BF16, bool VEC, int NT>
+SD_DEV void pick_body(const SampleArgs& a, int b) {
+    using Lt = Layout<BF16, VEC>;
+    constexpr int NW = NT / kWave;
+    constexpr int RUN = kSChunk / NT;
+    __shared__ double redd[NW];
+    __shared__ int redi[NW];
+    __shared__ double s_cs[kSMaxChunks];
+    __shared__ double s_W, s_base, s_wpick;
+    __shared__ int s_chunk;
+    const int tid = threadIdx.x;
+    Decision r = a.rec[b];
+    if (r.mode == MODE_NONE) return;
     bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
-    const int nch = (a.V + kSChunk - 1) / kSChunk;
-
-    // ---- 2. chunk sums of the weights -------------------------------------------------
-    chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, resid, s_wp, s_cs);
+    const int nch = a.nch;
+    for (int q = tid; q < nch; q += NT) s_cs[q] = a.wsum[(size_t)b * nch + q];
+    __syncthreads();
     if (tid == 0) {
         double W = 0.0;
         for (int q = 0; q < nch; ++q) W += s_cs[q];
@@ -548,7 +621,12 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
-        chunk_sums<BF16, VEC>(trow, drow, a.V, nch, r, a.c, false, s_wp, s_cs);
+        for (int q = 0; q < nch; ++q) {
+            const double x = chunk_weight_sum<BF16, VEC, NT>(trow, drow, a.V, q, r, a.c, false,
+                                                             a.topk != 0, redd);
+            if (tid == 0) s_cs[q] = x;
+        }
+        __syncthreads();
         if (tid == 0) {
             double W = 0.0;
             for (int q = 0; q < nch; ++q) W += s_cs[q];
@@ -557,8 +635,6 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
         }
         __syncthreads();
     }
-
-    // ---- 3. inverse CDF ---------------------------------------------------------------
     const double W = s_W;
     const double t = (double)r.u * W;
     if (tid == 0) {
@@ -578,42 +654,50 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
         s_base = C;
     }
     __syncthreads();
-    const int i0 = s_chunk * kSChunk + tid * 8;
-    float t8[8], d8[8];
-    load8<BF16, VEC>(trow, a.V, i0, t8);
-    if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
-    double w[8], run = 0.0;
+    // thread tid scans tokens [c0 + tid * RUN, c0 + (tid + 1) * RUN) of the chunk: a first
+    // pass for its total, an exclusive scan over threads, a second pass for the crossing
+    const int e0 = s_chunk * kSChunk + tid * RUN;
+    double run = 0.0;
+    for (int i0 = e0; i0 < e0 + RUN; i0 += 8) {
+        float t8[8], d8[8];
+        load8<BF16, VEC>(trow, a.V, i0, t8);
+        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
-        run += w[e];
+        for (int e = 0; e < 8; ++e) run += weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
     }
+    // (one chunk per request: the generic weight with its run-time branches is enough here)
     double tot;
-    double C = s_base + block_excl_scan_d<kSNT>(run, redd, &tot);
+    double C = s_base + block_excl_scan_d<NT>(run, redd, &tot);
     int mine = 0x7fffffff, lastpos = -1;
     double wmine = 0.0, wlast = 0.0;
+    for (int i0 = e0; i0 < e0 + RUN; i0 += 8) {
+        float t8[8], d8[8];
+        load8<BF16, VEC>(trow, a.V, i0, t8);
+        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        C += w[e];
-        if (mine == 0x7fffffff && C > t) {
-            mine = i0 + e;
-            wmine = w[e];
-        }
-        if (w[e] > 0.0) {
-            lastpos = i0 + e;
-            wlast = w[e];
+        for (int e = 0; e < 8; ++e) {
+            const double w = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+            C += w;
+            if (mine == 0x7fffffff && C > t) {
+                mine = i0 + e;
+                wmine = w;
+            }
+            if (w > 0.0) {
+                lastpos = i0 + e;
+                wlast = w;
+            }
         }
     }
-    int found = block_min_i<kSNT>(mine, redi);
+    int found = block_min_i<NT>(mine, redi);
     if (found != 0x7fffffff) {
         if (mine == found) s_wpick = wmine;
     } else {
-        found = block_max_i<kSNT>(lastpos, redi);
+        found = block_max_i<NT>(lastpos, redi);
         if (found >= 0 && lastpos == found) s_wpick = wlast;
     }
     __syncthreads();
     if (tid == 0) {
-        a.out_tokens[lo + b + r.a] = found;
+        a.out_tokens[a.cu[b] + b + r.a] = found;
         if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W;
         if (a.dbg.picked_prob) a.dbg.picked_prob[b] = s_wpick / W;
         if (a.dbg.req_flags) a.dbg.req_flags[b] = r.flags;
@@ -626,8 +710,8 @@ SD_DEV void sample_body(const SampleArgs& a, int b) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, total;
-    int nparts, nchunks;
+    size_t part, thr, rec, wsum, total;
+    int nparts, nchunks, nch;
 };
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
@@ -644,6 +728,11 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     off = align256(off + rows * p.nparts * sizeof(RowPartial));
     p.thr = off;
     off = align256(off + rows * sizeof(float));
+    p.nch = (V + kSChunk - 1) / kSChunk;
+    p.rec = off;
+    off = align256(off + (size_t)B * sizeof(Decision));
+    p.wsum = off;
+    off = align256(off + (size_t)B * p.nch * sizeof(double));
     p.total = off;
     return p;
 }
