@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, int R>
 __global__ __launch_bounds__(kTopkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
                                                         int B, int N, uint8_t* __restrict__ aws,
                                                         const uint8_t* __restrict__ tgt,
@@ -58,7 +58,10 @@ __global__ __launch_bounds__(kTopkNT) void k_cycle_topk(KvArgs kv, const int* __
         alloc_body<kTopkNT>(kv, cu, 1, B, N, aws);
         return;
     }
-    topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
+    if constexpr (R == 0)
+        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
+    else
+        topk_reg_body<BF16, R>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
 }
 
 static_assert(kDecideNT == kScNT, "decision and scatter workgroups share one launch");
@@ -109,8 +112,15 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
-        hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC>), dim3(rows + 1), dim3(kTopkNT), 0, st, e0,
-                              e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V, top_k, c, part, thr);
+#define SD_TOPK(R_)                                                                        \
+    hipExtLaunchKernelGGL((k_cycle_topk<BF16, R_>), dim3(rows + 1), dim3(kTopkNT), 0, st, e0,   \
+                          e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V, top_k, c, part, thr)
+        switch (topk_reg_vectors(V, BF16 ? 2 : 4, VEC, top_k)) {
+            case 8: SD_TOPK(8); break;
+            case 16: SD_TOPK(16); break;
+            default: SD_TOPK(0); break;
+        }
+#undef SD_TOPK
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,

@@ -42,13 +42,16 @@ __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ t
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, int R>
 __global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict__ tgt,
                                                        const uint8_t* __restrict__ dft,
                                                        int rows_t, int V, int top_k, float c,
                                                        RowPartial* __restrict__ part,
                                                        float* __restrict__ row_thr) {
-    topk_rows_body<BF16, VEC>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
+    if constexpr (R == 0)
+        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
+    else
+        topk_reg_body<BF16, R>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
 }
 
 template <bool BF16>
@@ -77,8 +80,15 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
-        hipExtLaunchKernelGGL((k_topk_rows<BF16, VEC>), dim3(rows), dim3(kTopkNT), 0, st, e0, e1, 0,
-                              tgt, dft, K + B, V, top_k, c, part, thr);
+#define SD_TOPK(R_)                                                                        \
+    hipExtLaunchKernelGGL((k_topk_rows<BF16, R_>), dim3(rows), dim3(kTopkNT), 0, st, e0, e1, 0, \
+                          tgt, dft, K + B, V, top_k, c, part, thr)
+        switch (topk_reg_vectors(V, BF16 ? 2 : 4, VEC, top_k)) {
+            case 8: SD_TOPK(8); break;
+            case 16: SD_TOPK(16); break;
+            default: SD_TOPK(0); break;
+        }
+#undef SD_TOPK
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
                               0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);

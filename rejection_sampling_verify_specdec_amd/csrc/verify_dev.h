@@ -260,6 +260,255 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 }
 
 // ---------------------------------------------------------------------------------------
+// Top-k row statistics with the row held in registers: one HBM read per row. For rows of
+// 16-byte vectors that fit R vectors per thread of a 1024-thread workgroup.
+//   1. every thread loads its R vectors, turns them in place into order-preserving keys
+//      (16-bit keys two to a register for bf16) and keeps its own max and min key;
+//   2. t0 = the top_k-th largest of the 1024 per-thread max keys (two-digit radix select
+//      in LDS). At least top_k threads hold an element >= t0, so the row's top_k-th
+//      largest element is >= t0;
+//   3. the elements with key >= t0 (for i.i.d. logits only a little over top_k of them)
+//      are appended to an LDS list, and an exact radix select over the list gives the
+//      threshold key;
+//   4. row max, kept count and the exp-sum over kept tokens come from the list alone.
+// Rows holding NaN or +inf, and rows whose list overflows (heavy ties at the threshold),
+// take the generic multi-pass body instead. -0 and +0 compare equal as floats but not as
+// keys; t0 is lowered from key(+0) to key(-0) so that every token the float test keeps
+// is on the list.
+// ---------------------------------------------------------------------------------------
+constexpr int kCandCap = 4096;   // LDS list capacity of the register-resident top-k body
+
+template <bool BF16>
+struct TopkKeys {
+    static constexpr uint32_t KEY_NINF = BF16 ? 0x007fu : 0x007fffffu;     // key(-inf)
+    static constexpr uint32_t KEY_PINF = BF16 ? 0xff80u : 0xff800000u;     // key(+inf)
+    static constexpr uint32_t KEY_PZERO = BF16 ? 0x8000u : 0x80000000u;    // key(+0)
+    static constexpr uint32_t KEY_NZERO = BF16 ? 0x7fffu : 0x7fffffffu;    // key(-0)
+    static constexpr uint32_t RAW_NINF = BF16 ? 0xff80ff80u : 0xff800000u;
+    static constexpr int KBITS = BF16 ? 16 : 32;
+};
+
+typedef short sd_i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short sd_u16x2 __attribute__((ext_vector_type(2)));
+
+// keys of one register: two bf16 (flip all bits of negatives, set the sign of the rest)
+// or one fp32
+template <bool BF16>
+SD_DEV uint32_t reg_keys(uint32_t d) {
+    if constexpr (BF16) {
+        const sd_i16x2 s = __builtin_bit_cast(sd_i16x2, d) >> (sd_i16x2){15, 15};
+        return d ^ (__builtin_bit_cast(uint32_t, s) | 0x80008000u);
+    } else {
+        return d ^ (uint32_t((int)d >> 31) | 0x80000000u);
+    }
+}
+template <bool BF16>
+SD_DEV uint32_t reg_max(uint32_t a, uint32_t b) {
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(sd_u16x2, a),
+                                                                      __builtin_bit_cast(sd_u16x2, b)));
+    else
+        return a > b ? a : b;
+}
+template <bool BF16>
+SD_DEV uint32_t reg_min(uint32_t a, uint32_t b) {
+    if constexpr (BF16)
+        return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(sd_u16x2, a),
+                                                                      __builtin_bit_cast(sd_u16x2, b)));
+    else
+        return a < b ? a : b;
+}
+template <bool BF16>
+SD_DEV float key_to_float(uint32_t k) {
+    if constexpr (BF16) {
+        const uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
+        return __uint_as_float(b << 16);
+    } else {
+        return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    }
+}
+
+// Called by the 64 threads of wave 0. hist holds 256 bins with at least *krem entries;
+// finds the bin d holding the *krem-th largest entry (counting down from bin 255), stores
+// d in *dig and *krem minus the entries in bins above d in *krem.
+SD_DEV void hist_select(const unsigned* hist, int* dig, int* krem) {
+    const int l = threadIdx.x;
+    const int k = *krem;
+    const unsigned h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+    const int s = int(h0 + h1 + h2 + h3);
+    int S = s;                                   // entries in the bins of lanes l..63
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_down(S, o, kWave);
+        if (l + o < kWave) S += v;
+    }
+    int above = S - s;
+    if (S >= k && above < k) {
+        const unsigned h[4] = {h0, h1, h2, h3};
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+            if (above + int(h[b]) >= k) {
+                *dig = 4 * l + b;
+                *krem = k - above;
+                break;
+            }
+            above += int(h[b]);
+        }
+    }
+}
+
+template <bool BF16, int R>
+SD_DEV void topk_reg_body(const uint8_t* __restrict__ tgt, const uint8_t* __restrict__ dft,
+                          int rows_t, int V, int top_k, float c, RowPartial* __restrict__ part,
+                          float* __restrict__ row_thr, int row) {
+    constexpr int NT = kTopkNT;
+    constexpr int ES = BF16 ? 2 : 4;
+    constexpr int EPV = 16 / ES;
+    using Kt = TopkKeys<BF16>;
+    __shared__ unsigned hist_a[256], hist_b[256];
+    __shared__ uint32_t ckey[kCandCap];
+    __shared__ int redi[NT / kWave];
+    __shared__ double redd[NT / kWave];
+    __shared__ int s_cnt, s_dig, s_krem;
+    const int tid = threadIdx.x;
+    const u32x4* p = reinterpret_cast<const u32x4*>(row_ptr(tgt, dft, rows_t, row, V, ES));
+    const int nvec = V / EPV;
+
+    // 1. load, key, per-thread max / min (padding reads as -inf)
+    u32x4 r[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int s = j * NT + tid;
+        r[j] = s < nvec ? __builtin_nontemporal_load(p + s)
+                        : (u32x4){Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF};
+    }
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        r[j].x = reg_keys<BF16>(r[j].x);
+        r[j].y = reg_keys<BF16>(r[j].y);
+        r[j].z = reg_keys<BF16>(r[j].z);
+        r[j].w = reg_keys<BF16>(r[j].w);
+        kmax = reg_max<BF16>(kmax, reg_max<BF16>(reg_max<BF16>(r[j].x, r[j].y),
+                                                 reg_max<BF16>(r[j].z, r[j].w)));
+        kmin = reg_min<BF16>(kmin, reg_min<BF16>(reg_min<BF16>(r[j].x, r[j].y),
+                                                 reg_min<BF16>(r[j].z, r[j].w)));
+    }
+    if constexpr (BF16) {
+        kmax = max(kmax & 0xffffu, kmax >> 16);
+        kmin = min(kmin & 0xffffu, kmin >> 16);
+    }
+    for (int i = tid; i < 512; i += NT) (i < 256 ? hist_a[i] : hist_b[i - 256]) = 0u;
+    if (tid == 0) {
+        s_cnt = 0;
+        s_krem = top_k;
+    }
+    // order-preserving map of unsigned keys onto int for the signed block reductions
+    const uint32_t rmax = uint32_t(block_max_i<NT>(int(kmax ^ 0x80000000u), redi)) ^ 0x80000000u;
+    const uint32_t rmin = uint32_t(block_min_i<NT>(int(kmin ^ 0x80000000u), redi)) ^ 0x80000000u;
+    if (rmax >= Kt::KEY_PINF || rmin < Kt::KEY_NINF) {     // NaN or +inf in the row
+        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, row);
+        return;
+    }
+
+    // 2. t0 = top_k-th largest per-thread max (upper 16 key bits for fp32)
+    const uint32_t tv = BF16 ? kmax : kmax >> 16;
+    atomicAdd(&hist_a[tv >> 8], 1u);
+    __syncthreads();
+    if (tid < kWave) hist_select(hist_a, &s_dig, &s_krem);
+    __syncthreads();
+    const uint32_t d1 = (uint32_t)s_dig;
+    if ((tv >> 8) == d1) atomicAdd(&hist_b[tv & 0xffu], 1u);
+    __syncthreads();
+    if (tid < kWave) hist_select(hist_b, &s_dig, &s_krem);
+    __syncthreads();
+    uint32_t t0 = (d1 << 8) | (uint32_t)s_dig;
+    if constexpr (!BF16) t0 <<= 16;
+    if (t0 == Kt::KEY_PZERO) t0 = Kt::KEY_NZERO;
+
+    // 3. list of keys >= t0
+    const uint32_t below = BF16 ? (t0 - 1u) * 0x10001u : t0 - 1u;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * NT + tid < nvec) {
+            const uint32_t m4 = reg_max<BF16>(reg_max<BF16>(r[j].x, r[j].y),
+                                              reg_max<BF16>(r[j].z, r[j].w));
+            if (reg_max<BF16>(m4, below) != below) {
+                const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+#pragma unroll
+                for (int e = 0; e < 4 * (BF16 ? 2 : 1); ++e) {
+                    const uint32_t k = BF16 ? (w[e >> 1] >> (16 * (e & 1))) & 0xffffu : w[e];
+                    if (k >= t0) {
+                        const int pos = atomicAdd(&s_cnt, 1);
+                        if (pos < kCandCap) ckey[pos] = k;
+                    }
+                }
+            }
+        }
+    }
+    if (tid == 0) s_krem = top_k;
+    __syncthreads();
+    const int C = s_cnt;
+    if (C > kCandCap) {
+        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, row);
+        return;
+    }
+
+    // exact top_k-th largest key of the list, one 8-bit digit at a time
+    uint32_t prefix = 0u;
+#pragma unroll
+    for (int shift = Kt::KBITS - 8; shift >= 0; shift -= 8) {
+        unsigned* h = ((shift / 8) & 1) ? hist_a : hist_b;
+        const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
+        for (int i = tid; i < 256; i += NT) h[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < C; i += NT) {
+            const uint32_t k = ckey[i];
+            if ((k & hmask) == prefix) atomicAdd(&h[(k >> shift) & 0xffu], 1u);
+        }
+        __syncthreads();
+        if (tid < kWave) hist_select(h, &s_dig, &s_krem);
+        __syncthreads();
+        prefix |= (uint32_t)s_dig << shift;
+    }
+    const float thr = key_to_float<BF16>(prefix);
+
+    // 4. max, kept count and exp-sum over the list
+    const float m = key_to_float<BF16>(rmax);
+    const float mc = m * c;
+    const float emc = fmaf(m, c, -mc);
+    float acc = 0.f;
+    int kept = 0;
+    for (int i = tid; i < C; i += NT) {
+        const float z = key_to_float<BF16>(ckey[i]);
+        if (z >= thr && z > -INFINITY) {
+            acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
+            ++kept;
+        }
+    }
+    const double tot = block_sum<NT>((double)acc, redd);
+    kept = block_sum_i<NT>(kept, redi);
+    if (tid == 0) {
+        RowPartial rp;
+        rp.m = m;
+        rp.nkept = kept;
+        rp.s = m == -INFINITY ? 0.0 : tot * exp2(-(double)emc);
+        part[row] = rp;
+        row_thr[row] = thr;
+    }
+}
+
+// Register capacity (16-byte vectors per thread) of the top-k body for a row, 0 when the
+// generic multi-pass body must be used.
+static inline int topk_reg_vectors(int V, int es, bool vec, int top_k) {
+    if (!vec || top_k > kTopkNT) return 0;
+    const long nvec = (long)V * es / 16;
+    for (int r : {8, 16})
+        if (nvec <= (long)r * kTopkNT) return r;
+    return 0;
+}
+
+// ---------------------------------------------------------------------------------------
 // Decision and sampling, fused: one workgroup of 1024 threads per request.
 //   1. combine the row partials in fp64, evaluate p_i(y_i), q_i(y_i) and the accept test
 //      left to right, find the first rejection, publish the accepted tokens;
