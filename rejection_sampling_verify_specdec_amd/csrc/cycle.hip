@@ -1,10 +1,11 @@
-// One whole speculative cycle in four launches (gfx950): the same work and results as
+// One whole speculative cycle in four launches (five with top-k) (gfx950): the same work and results as
 // kv_paged_append -> specdec_verify -> kv_rollback on one stream, with the latency-bound
 // pieces folded into launches that are busy streaming memory anyway.
 //
 //   k_cycle_stats   workgroup 0 allocates the cycle's blocks (copy-on-write, LIFO pops,
 //                   destination rows) while every other workgroup streams logit rows
-//                   (row statistics, or the top-k row kernel);
+//                   (row statistics, or top-k chunk candidates followed by a short
+//                   per-row merge launch);
 //   k_cycle_decide  K/V scatter workgroups, then one workgroup per request for its
 //                   accept / reject decisions;
 //   k_part          (request, chunk) workgroups sum the sampling weights chunk by chunk;
@@ -46,22 +47,23 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1);
 }
 
-template <bool BF16, int R>
-__global__ __launch_bounds__(kTopkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
-                                                        int B, int N, uint8_t* __restrict__ aws,
-                                                        const uint8_t* __restrict__ tgt,
-                                                        const uint8_t* __restrict__ dft,
-                                                        int rows_t, int V, int top_k, float c,
-                                                        RowPartial* __restrict__ part,
-                                                        float* __restrict__ row_thr) {
+static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
+                                                      int B, int N, uint8_t* __restrict__ aws,
+                                                      TopkArgs a) {
     if (blockIdx.x == 0) {
-        alloc_body<kTopkNT>(kv, cu, 1, B, N, aws);
+        alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
         return;
     }
-    if constexpr (R == 0)
-        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
-    else
-        topk_reg_body<BF16, R>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x - 1);
+    const int w = blockIdx.x - 1;
+    topk_chunk_body<BF16, VEC>(a, w / a.nchunks, w % a.nchunks);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kMergeNT) void k_cycle_topk_merge(TopkArgs a) {
+    topk_merge_body<BF16>(a, blockIdx.x);
 }
 
 static_assert(kDecideNT == kScNT, "decision and scatter workgroups share one launch");
@@ -112,15 +114,11 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
-#define SD_TOPK(R_)                                                                        \
-    hipExtLaunchKernelGGL((k_cycle_topk<BF16, R_>), dim3(rows + 1), dim3(kTopkNT), 0, st, e0,   \
-                          e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V, top_k, c, part, thr)
-        switch (topk_reg_vectors(V, BF16 ? 2 : 4, VEC, top_k)) {
-            case 8: SD_TOPK(8); break;
-            case 16: SD_TOPK(16); break;
-            default: SD_TOPK(0); break;
-        }
-#undef SD_TOPK
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_k, c, p, vws);
+        const unsigned nchunk_wg = ta.generic ? 0u : (unsigned)rows * p.nchunks;
+        hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC>), dim3(nchunk_wg + 1), dim3(kTkNT), 0, st,
+                              e0, e1, 0, kv, cu, B, N, aws, ta);
+        hipLaunchKernelGGL((k_cycle_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, ta);
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,

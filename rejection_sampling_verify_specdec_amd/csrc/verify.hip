@@ -7,12 +7,15 @@
 // decoding transform (temperature, top-k) applied identically to target and draft rows
 // and a max-subtracted (stable) softmax (same page, section 6).
 //
-// Pipeline on one stream, per call (four kernels):
+// Pipeline on one stream, per call (four kernels, five with top-k):
 //   k_row_stats   every target and draft row is streamed once in 16K-element chunks with
 //                 128-bit loads; each workgroup writes the chunk max m_c and
 //                 S_c = sum exp2((z - m_c) * c), c = log2(e) / T, as an fp32/fp64 pair.
-//   k_topk_rows   (top-k only, replaces k_row_stats) one workgroup per row: exact top-k
-//                 threshold, max, kept count and kept-set sum.
+//   k_topk_chunks (top-k only, replaces k_row_stats) the same chunks, held in registers as
+//                 order-preserving keys: each workgroup writes the few tokens that can be
+//                 in the row's top-k set (a bound from its per-thread maxima).
+//   k_topk_merge  one workgroup per row: exact top-k threshold over the chunks'
+//                 candidates, max, kept count and kept-set sum.
 //   k_decide      one workgroup per request: combines the row partials in fp64, evaluates
 //                 p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p left to right,
 //                 finds the first rejection, publishes the accepted tokens and stores the
@@ -42,16 +45,14 @@ __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ t
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x);
 }
 
-template <bool BF16, int R>
-__global__ __launch_bounds__(kTopkNT) void k_topk_rows(const uint8_t* __restrict__ tgt,
-                                                       const uint8_t* __restrict__ dft,
-                                                       int rows_t, int V, int top_k, float c,
-                                                       RowPartial* __restrict__ part,
-                                                       float* __restrict__ row_thr) {
-    if constexpr (R == 0)
-        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
-    else
-        topk_reg_body<BF16, R>(tgt, dft, rows_t, V, top_k, c, part, row_thr, blockIdx.x);
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
+    topk_chunk_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kMergeNT) void k_topk_merge(TopkArgs a) {
+    topk_merge_body<BF16>(a, blockIdx.x);
 }
 
 template <bool BF16>
@@ -80,15 +81,14 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (topk_active(top_k, V)) {
-#define SD_TOPK(R_)                                                                        \
-    hipExtLaunchKernelGGL((k_topk_rows<BF16, R_>), dim3(rows), dim3(kTopkNT), 0, st, e0, e1, 0, \
-                          tgt, dft, K + B, V, top_k, c, part, thr)
-        switch (topk_reg_vectors(V, BF16 ? 2 : 4, VEC, top_k)) {
-            case 8: SD_TOPK(8); break;
-            case 16: SD_TOPK(16); break;
-            default: SD_TOPK(0); break;
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_k, c, p, ws);
+        if (!ta.generic) {
+            hipExtLaunchKernelGGL((k_topk_chunks<BF16, VEC>), dim3((unsigned)rows * p.nchunks),
+                                  dim3(kTkNT), 0, st, e0, e1, 0, ta);
+            e0 = e1 = nullptr;
         }
-#undef SD_TOPK
+        hipExtLaunchKernelGGL((k_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, e0, e1, 0,
+                              ta);
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
                               0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);

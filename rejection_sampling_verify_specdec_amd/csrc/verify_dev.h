@@ -16,7 +16,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNT = 256;        // threads per workgroup of the streaming kernels
 constexpr int kVPT = 8;         // 16-byte vectors per thread per chunk
-constexpr int kTopkNT = 1024;   // threads per workgroup of the top-k row kernel
 
 enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_BONUS = 2 };
 
@@ -175,11 +174,10 @@ SD_DEV float key2f(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, int NT>
 SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __restrict__ dft,
                            int rows_t, int V, int top_k, float c, RowPartial* __restrict__ part,
                            float* __restrict__ row_thr, int row) {
-    constexpr int NT = kTopkNT;
     constexpr int ES = BF16 ? 2 : 4;
     __shared__ unsigned hist[256];
     __shared__ float redf[NT / kWave];
@@ -260,23 +258,43 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 }
 
 // ---------------------------------------------------------------------------------------
-// Top-k row statistics with the row held in registers: one HBM read per row. For rows of
-// 16-byte vectors that fit R vectors per thread of a 1024-thread workgroup.
-//   1. every thread loads its R vectors, turns them in place into order-preserving keys
-//      (16-bit keys two to a register for bf16) and keeps its own max and min key;
-//   2. t0 = the top_k-th largest of the 1024 per-thread max keys (two-digit radix select
-//      in LDS). At least top_k threads hold an element >= t0, so the row's top_k-th
-//      largest element is >= t0;
-//   3. the elements with key >= t0 (for i.i.d. logits only a little over top_k of them)
-//      are appended to an LDS list, and an exact radix select over the list gives the
-//      threshold key;
-//   4. row max, kept count and the exp-sum over kept tokens come from the list alone.
-// Rows holding NaN or +inf, and rows whose list overflows (heavy ties at the threshold),
-// take the generic multi-pass body instead. -0 and +0 compare equal as floats but not as
-// keys; t0 is lowered from key(+0) to key(-0) so that every token the float test keeps
-// is on the list.
+// Top-k row statistics in two launches, one HBM read per row.
+//  chunks: one 256-thread workgroup per 16K-element chunk (8K for fp32), the chunking of the
+//    plain statistics kernel. The chunk sits in registers as order-preserving keys (two
+//    16-bit keys a register for bf16). t_c = the top_k-th largest of the per-thread max keys
+//    (per-16-element-group max keys when top_k > 256), by a two-digit radix select in LDS.
+//    At least top_k chunk elements are >= t_c, so the row's top_k-th largest element is
+//    >= t_c too; the elements >= t_c (for i.i.d. logits a little over top_k per chunk) go
+//    to the workspace in thread order, (key << 32 | token) each.
+//  merge: one workgroup per row selects the exact top_k-th largest key among the chunks'
+//    candidates (their union holds every token the row keeps) and takes max, kept count and
+//    exp-sum from the candidates alone.
+// Rows holding NaN or +inf, rows with a chunk that overflows its candidate capacity (heavy
+// ties at the threshold) and top_k above 1024 take the generic multi-pass select in the
+// merge launch instead. -0 and +0 compare equal as floats but not as keys: t_c is lowered
+// from key(+0) to key(-0) so that every token the float test keeps is a candidate.
 // ---------------------------------------------------------------------------------------
-constexpr int kCandCap = 4096;   // LDS list capacity of the register-resident top-k body
+constexpr int kTkNT = kNT;         // threads of a chunk workgroup
+constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-byte vectors)
+constexpr int kMergeNT = 256;      // threads of a merge workgroup
+constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
+constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
+
+struct TopkArgs {
+    const uint8_t* tgt;
+    const uint8_t* dft;
+    int rows_t, V, nchunks, top_k;
+    int cap;                 // candidates per chunk
+    int generic;             // 1: every row takes the generic select
+    float c;
+    int* cnt;                // [rows][nchunks] candidates found (-1: NaN / +inf in the chunk)
+    uint64_t* cand;          // [rows][nchunks][cap]
+    RowPartial* part;        // [rows]
+    float* row_thr;          // [rows]
+};
+
+static inline int topk_cap(int top_k) { return top_k <= 128 ? 512 : 4 * top_k; }
+static inline bool topk_generic(int top_k) { return top_k > kTkMaxK; }
 
 template <bool BF16>
 struct TopkKeys {
@@ -357,68 +375,103 @@ SD_DEV void hist_select(const unsigned* hist, int* dig, int* krem) {
     }
 }
 
-template <bool BF16, int R>
-SD_DEV void topk_reg_body(const uint8_t* __restrict__ tgt, const uint8_t* __restrict__ dft,
-                          int rows_t, int V, int top_k, float c, RowPartial* __restrict__ part,
-                          float* __restrict__ row_thr, int row) {
-    constexpr int NT = kTopkNT;
-    constexpr int ES = BF16 ? 2 : 4;
-    constexpr int EPV = 16 / ES;
+template <bool BF16, bool VEC>
+SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
+    constexpr int NT = kTkNT;
+    constexpr int NR = kTkRegs;
+    constexpr int EPR = BF16 ? 2 : 1;                 // elements per register
+    using Lt = Layout<BF16, VEC>;
     using Kt = TopkKeys<BF16>;
+    static_assert(NR * EPR == Lt::EPT, "a chunk is NT threads x NR registers");
     __shared__ unsigned hist_a[256], hist_b[256];
-    __shared__ uint32_t ckey[kCandCap];
     __shared__ int redi[NT / kWave];
-    __shared__ double redd[NT / kWave];
-    __shared__ int s_cnt, s_dig, s_krem;
+    __shared__ int s_dig, s_krem;
     const int tid = threadIdx.x;
-    const u32x4* p = reinterpret_cast<const u32x4*>(row_ptr(tgt, dft, rows_t, row, V, ES));
-    const int nvec = V / EPV;
+    const int V = a.V;
+    const uint8_t* base = row_ptr(a.tgt, a.dft, a.rows_t, row, V, Lt::ES);
+    const int c0 = chunk * Lt::CH;
+    // token of element h of register w
+    auto token = [&](int w, int h) {
+        if constexpr (VEC) return c0 + ((w / 4) * NT + tid) * Lt::EPV + (w % 4) * EPR + h;
+        else return c0 + (w * EPR + h) * NT + tid;
+    };
 
-    // 1. load, key, per-thread max / min (padding reads as -inf)
-    u32x4 r[R];
+    // 1. load (tokens past V read as -inf), keys in place, group max / thread min
+    uint32_t r[NR];
+    if constexpr (VEC) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(base);
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const int s = j * NT + tid;
-        r[j] = s < nvec ? __builtin_nontemporal_load(p + s)
-                        : (u32x4){Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF};
-    }
-    uint32_t kmax = 0u, kmin = 0xffffffffu;
+        for (int j = 0; j < NR / 4; ++j) {
+            const int i0 = token(4 * j, 0);
+            const u32x4 v = i0 < V ? __builtin_nontemporal_load(p + i0 / Lt::EPV)
+                                   : (u32x4){Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF, Kt::RAW_NINF};
+            r[4 * j] = v.x;
+            r[4 * j + 1] = v.y;
+            r[4 * j + 2] = v.z;
+            r[4 * j + 3] = v.w;
+        }
+    } else {
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        r[j].x = reg_keys<BF16>(r[j].x);
-        r[j].y = reg_keys<BF16>(r[j].y);
-        r[j].z = reg_keys<BF16>(r[j].z);
-        r[j].w = reg_keys<BF16>(r[j].w);
-        kmax = reg_max<BF16>(kmax, reg_max<BF16>(reg_max<BF16>(r[j].x, r[j].y),
-                                                 reg_max<BF16>(r[j].z, r[j].w)));
-        kmin = reg_min<BF16>(kmin, reg_min<BF16>(reg_min<BF16>(r[j].x, r[j].y),
-                                                 reg_min<BF16>(r[j].z, r[j].w)));
+        for (int w = 0; w < NR; ++w) {
+            if constexpr (BF16) {
+                const uint16_t* q = reinterpret_cast<const uint16_t*>(base);
+                const int i0 = token(w, 0), i1 = token(w, 1);
+                const uint32_t lo = i0 < V ? q[i0] : 0xff80u;
+                const uint32_t hi = i1 < V ? q[i1] : 0xff80u;
+                r[w] = lo | (hi << 16);
+            } else {
+                const uint32_t* q = reinterpret_cast<const uint32_t*>(base);
+                const int i0 = token(w, 0);
+                r[w] = i0 < V ? q[i0] : Kt::RAW_NINF;
+            }
+        }
     }
-    if constexpr (BF16) {
-        kmax = max(kmax & 0xffffu, kmax >> 16);
-        kmin = min(kmin & 0xffffu, kmin >> 16);
+    uint32_t gm[4];
+    uint32_t kmin = 0xffffffffu;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int w = g * (NR / 4); w < (g + 1) * (NR / 4); ++w) {
+            r[w] = reg_keys<BF16>(r[w]);
+            m = reg_max<BF16>(m, r[w]);
+            kmin = reg_min<BF16>(kmin, r[w]);
+        }
+        gm[g] = BF16 ? max(m & 0xffffu, m >> 16) : m;
     }
-    for (int i = tid; i < 512; i += NT) (i < 256 ? hist_a[i] : hist_b[i - 256]) = 0u;
-    if (tid == 0) {
-        s_cnt = 0;
-        s_krem = top_k;
-    }
-    // order-preserving map of unsigned keys onto int for the signed block reductions
-    const uint32_t rmax = uint32_t(block_max_i<NT>(int(kmax ^ 0x80000000u), redi)) ^ 0x80000000u;
-    const uint32_t rmin = uint32_t(block_min_i<NT>(int(kmin ^ 0x80000000u), redi)) ^ 0x80000000u;
-    if (rmax >= Kt::KEY_PINF || rmin < Kt::KEY_NINF) {     // NaN or +inf in the row
-        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, row);
+    if constexpr (BF16) kmin = min(kmin & 0xffffu, kmin >> 16);
+    const uint32_t kmax = max(max(gm[0], gm[1]), max(gm[2], gm[3]));
+    for (int i = tid; i < 256; i += NT) hist_a[i] = hist_b[i] = 0u;
+    if (tid == 0) s_krem = a.top_k;
+    const int bad = block_max_i<NT>(kmax >= Kt::KEY_PINF || kmin < Kt::KEY_NINF, redi);
+    if (bad) {
+        if (tid == 0) a.cnt[(size_t)row * a.nchunks + chunk] = -1;
         return;
     }
 
-    // 2. t0 = top_k-th largest per-thread max (upper 16 key bits for fp32)
-    const uint32_t tv = BF16 ? kmax : kmax >> 16;
-    atomicAdd(&hist_a[tv >> 8], 1u);
+    // 2. t_c: top_k-th largest per-thread (or per-group) max, upper 16 key bits for fp32
+    const bool groups = a.top_k > NT;
+    uint32_t tv[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) tv[g] = BF16 ? gm[g] : gm[g] >> 16;
+    if (groups) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) atomicAdd(&hist_a[tv[g] >> 8], 1u);
+    } else {
+        atomicAdd(&hist_a[(BF16 ? kmax : kmax >> 16) >> 8], 1u);
+    }
     __syncthreads();
     if (tid < kWave) hist_select(hist_a, &s_dig, &s_krem);
     __syncthreads();
     const uint32_t d1 = (uint32_t)s_dig;
-    if ((tv >> 8) == d1) atomicAdd(&hist_b[tv & 0xffu], 1u);
+    if (groups) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            if ((tv[g] >> 8) == d1) atomicAdd(&hist_b[tv[g] & 0xffu], 1u);
+    } else {
+        const uint32_t t = BF16 ? kmax : kmax >> 16;
+        if ((t >> 8) == d1) atomicAdd(&hist_b[t & 0xffu], 1u);
+    }
     __syncthreads();
     if (tid < kWave) hist_select(hist_b, &s_dig, &s_krem);
     __syncthreads();
@@ -426,64 +479,107 @@ SD_DEV void topk_reg_body(const uint8_t* __restrict__ tgt, const uint8_t* __rest
     if constexpr (!BF16) t0 <<= 16;
     if (t0 == Kt::KEY_PZERO) t0 = Kt::KEY_NZERO;
 
-    // 3. list of keys >= t0
+    // 3. candidates (key >= t0), written in thread order
     const uint32_t below = BF16 ? (t0 - 1u) * 0x10001u : t0 - 1u;
+    unsigned hit = 0u;
+    int nh = 0;
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-        if (j * NT + tid < nvec) {
-            const uint32_t m4 = reg_max<BF16>(reg_max<BF16>(r[j].x, r[j].y),
-                                              reg_max<BF16>(r[j].z, r[j].w));
-            if (reg_max<BF16>(m4, below) != below) {
-                const uint32_t w[4] = {r[j].x, r[j].y, r[j].z, r[j].w};
+    for (int j = 0; j < NR / 4; ++j) {
+        const uint32_t m4 = reg_max<BF16>(reg_max<BF16>(r[4 * j], r[4 * j + 1]),
+                                          reg_max<BF16>(r[4 * j + 2], r[4 * j + 3]));
+        if (reg_max<BF16>(m4, below) != below) {
+            hit |= 1u << j;
 #pragma unroll
-                for (int e = 0; e < 4 * (BF16 ? 2 : 1); ++e) {
-                    const uint32_t k = BF16 ? (w[e >> 1] >> (16 * (e & 1))) & 0xffffu : w[e];
-                    if (k >= t0) {
-                        const int pos = atomicAdd(&s_cnt, 1);
-                        if (pos < kCandCap) ckey[pos] = k;
+            for (int w = 4 * j; w < 4 * j + 4; ++w)
+#pragma unroll
+                for (int h = 0; h < EPR; ++h) nh += ((r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u)) >= t0;
+        }
+    }
+    int total;
+    int off = block_excl_scan_i<NT>(nh, redi, &total);
+    uint64_t* out = a.cand + ((size_t)row * a.nchunks + chunk) * a.cap;
+    if (nh) {
+#pragma unroll
+        for (int j = 0; j < NR / 4; ++j) {
+            if (hit & (1u << j)) {
+#pragma unroll
+                for (int w = 4 * j; w < 4 * j + 4; ++w)
+#pragma unroll
+                    for (int h = 0; h < EPR; ++h) {
+                        const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+                        if (k >= t0) {
+                            if (off < a.cap) out[off] = ((uint64_t)k << 32) | (uint32_t)token(w, h);
+                            ++off;
+                        }
                     }
-                }
             }
         }
     }
-    if (tid == 0) s_krem = top_k;
-    __syncthreads();
-    const int C = s_cnt;
-    if (C > kCandCap) {
-        topk_rows_body<BF16, false>(tgt, dft, rows_t, V, top_k, c, part, row_thr, row);
+    if (tid == 0) a.cnt[(size_t)row * a.nchunks + chunk] = total;
+}
+
+template <bool BF16>
+SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
+    constexpr int NT = kMergeNT;
+    using Kt = TopkKeys<BF16>;
+    __shared__ unsigned hist[256];
+    __shared__ int s_cnt[kTkMaxChunks];
+    __shared__ int redi[NT / kWave];
+    __shared__ double redd[NT / kWave];
+    __shared__ int s_dig, s_krem;
+    const int tid = threadIdx.x;
+    const int nch = a.nchunks;
+    int flag = a.generic;
+    if (!a.generic) {
+        for (int ch = tid; ch < nch; ch += NT) {
+            const int n = a.cnt[(size_t)row * nch + ch];
+            s_cnt[ch] = n;
+            flag |= n < 0 || n > a.cap;
+        }
+    }
+    if (tid == 0) s_krem = a.top_k;
+    flag = block_max_i<NT>(flag, redi);
+    if (flag) {
+        topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.top_k, a.c, a.part, a.row_thr, row);
         return;
     }
+    const uint64_t* cand = a.cand + (size_t)row * nch * a.cap;
 
-    // exact top_k-th largest key of the list, one 8-bit digit at a time
-    uint32_t prefix = 0u;
+    // exact top_k-th largest candidate key, one 8-bit digit at a time; the row max on the way
+    uint32_t prefix = 0u, kmax = 0u;
 #pragma unroll
     for (int shift = Kt::KBITS - 8; shift >= 0; shift -= 8) {
-        unsigned* h = ((shift / 8) & 1) ? hist_a : hist_b;
         const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
-        for (int i = tid; i < 256; i += NT) h[i] = 0u;
+        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < C; i += NT) {
-            const uint32_t k = ckey[i];
-            if ((k & hmask) == prefix) atomicAdd(&h[(k >> shift) & 0xffu], 1u);
+        for (int ch = 0; ch < nch; ++ch) {
+            const int n = s_cnt[ch];
+            for (int i = tid; i < n; i += NT) {
+                const uint32_t k = uint32_t(cand[(size_t)ch * a.cap + i] >> 32);
+                if (shift == Kt::KBITS - 8) kmax = max(kmax, k);
+                if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+            }
         }
         __syncthreads();
-        if (tid < kWave) hist_select(h, &s_dig, &s_krem);
+        if (tid < kWave) hist_select(hist, &s_dig, &s_krem);
         __syncthreads();
         prefix |= (uint32_t)s_dig << shift;
     }
+    const uint32_t rmax = uint32_t(block_max_i<NT>(int(kmax ^ 0x80000000u), redi)) ^ 0x80000000u;
     const float thr = key_to_float<BF16>(prefix);
-
-    // 4. max, kept count and exp-sum over the list
     const float m = key_to_float<BF16>(rmax);
-    const float mc = m * c;
-    const float emc = fmaf(m, c, -mc);
+    const float mc = m * a.c;
+    const float emc = fmaf(m, a.c, -mc);
     float acc = 0.f;
     int kept = 0;
-    for (int i = tid; i < C; i += NT) {
-        const float z = key_to_float<BF16>(ckey[i]);
-        if (z >= thr && z > -INFINITY) {
-            acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
-            ++kept;
+    for (int ch = 0; ch < nch; ++ch) {
+        const int n = s_cnt[ch];
+        for (int i = tid; i < n; i += NT) {
+            const float z = key_to_float<BF16>(uint32_t(cand[(size_t)ch * a.cap + i] >> 32));
+            if (z >= thr && z > -INFINITY) {
+                acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
+                ++kept;
+            }
         }
     }
     const double tot = block_sum<NT>((double)acc, redd);
@@ -493,19 +589,9 @@ SD_DEV void topk_reg_body(const uint8_t* __restrict__ tgt, const uint8_t* __rest
         rp.m = m;
         rp.nkept = kept;
         rp.s = m == -INFINITY ? 0.0 : tot * exp2(-(double)emc);
-        part[row] = rp;
-        row_thr[row] = thr;
+        a.part[row] = rp;
+        a.row_thr[row] = thr;
     }
-}
-
-// Register capacity (16-byte vectors per thread) of the top-k body for a row, 0 when the
-// generic multi-pass body must be used.
-static inline int topk_reg_vectors(int V, int es, bool vec, int top_k) {
-    if (!vec || top_k > kTopkNT) return 0;
-    const long nvec = (long)V * es / 16;
-    for (int r : {8, 16})
-        if (nvec <= (long)r * kTopkNT) return r;
-    return 0;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -959,8 +1045,8 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, rec, wsum, total;
-    int nparts, nchunks, nch;
+    size_t part, thr, rec, wsum, tk_cnt, tk_cand, total;
+    int nparts, nchunks, nch, tk_cap;
 };
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
@@ -982,8 +1068,34 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     off = align256(off + (size_t)B * sizeof(Decision));
     p.wsum = off;
     off = align256(off + (size_t)B * p.nch * sizeof(double));
+    p.tk_cnt = p.tk_cand = off;
+    if (topk_active(top_k, V) && !topk_generic(top_k)) {
+        p.tk_cap = topk_cap(top_k);
+        off = align256(off + rows * p.nchunks * sizeof(int));
+        p.tk_cand = off;
+        off = align256(off + rows * p.nchunks * (size_t)p.tk_cap * sizeof(uint64_t));
+    }
     p.total = off;
     return p;
+}
+
+static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int rows_t, int V,
+                                 int top_k, float c, const WsPlan& p, uint8_t* ws) {
+    TopkArgs a;
+    a.tgt = tgt;
+    a.dft = dft;
+    a.rows_t = rows_t;
+    a.V = V;
+    a.nchunks = p.nchunks;
+    a.top_k = top_k;
+    a.cap = p.tk_cap;
+    a.generic = topk_generic(top_k);
+    a.c = c;
+    a.cnt = reinterpret_cast<int*>(ws + p.tk_cnt);
+    a.cand = reinterpret_cast<uint64_t*>(ws + p.tk_cand);
+    a.part = reinterpret_cast<RowPartial*>(ws + p.part);
+    a.row_thr = reinterpret_cast<float*>(ws + p.thr);
+    return a;
 }
 
 }  // namespace sd

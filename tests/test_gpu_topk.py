@@ -1,10 +1,10 @@
 """GPU parity of the top-k transform against the oracle.
 
-Rows of 16-byte vectors that fit 16 vectors per thread take the register-resident select
-(one HBM read per row); larger or unaligned rows, top_k above 1024, rows holding NaN/+inf
-and rows whose candidate list overflows (heavy ties at the threshold) take the generic
-multi-pass select. Both must give the oracle's threshold, kept count, max and exp-sum on
-every row, and the same decisions and tokens.
+Rows take the chunked select (per-chunk candidate lists, then a per-row merge); top_k
+above 1024, rows holding NaN/+inf and rows with a chunk whose candidates overflow its
+capacity (heavy ties at the threshold) take the generic multi-pass select. Both must give
+the oracle's threshold, kept count, max and exp-sum on every row, and the same decisions
+and tokens.
 """
 
 import numpy as np
@@ -43,7 +43,7 @@ def test_topk_fp32_rows():
 
 @pytest.mark.parametrize("top_k", [1, 2, 1000, 1024, 1025])
 def test_topk_values(top_k):
-    # 1024 is the largest top_k of the register-resident select; 1025 takes the generic one
+    # 1000 and 1024 bound the chunk threshold by per-group maxima; 1025 is generic
     _check(synth.make_verify("c4", seed=43, B=4, V=16384, top_k=top_k))
 
 
@@ -119,6 +119,13 @@ def test_topk_planted_rows_small_vocab():
     vin = synth.make_verify("c4", seed=45, B=6, V=4096, k=3)
     pats = [_signed_zero_threshold, _few_finite, _integer_ties, _ascending, _constant, None]
     _check(_plant(vin, pats, seed=46))
+
+
+def test_topk_planted_rows_one_chunk():
+    # every token a candidate (threshold -inf, signed zeros) without overflowing the chunk
+    vin = synth.make_verify("c4", seed=50, B=3, V=512, k=2)
+    pats = [_few_finite, _signed_zero_threshold, _integer_ties]
+    _check(_plant(vin, pats, seed=51))
 
 
 def test_topk_planted_rows_large_vocab():
