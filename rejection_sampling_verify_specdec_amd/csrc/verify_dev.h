@@ -261,11 +261,12 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // Top-k row statistics in two launches, one HBM read per row.
 //  chunks: one 256-thread workgroup per 16K-element chunk (8K for fp32), the chunking of the
 //    plain statistics kernel. The chunk sits in registers as order-preserving keys (two
-//    16-bit keys a register for bf16). t_c = the top_k-th largest of the per-thread max keys
-//    (per-16-element-group max keys when top_k > 256), by a two-digit radix select in LDS.
-//    At least top_k chunk elements are >= t_c, so the row's top_k-th largest element is
-//    >= t_c too; the elements >= t_c (for i.i.d. logits a little over top_k per chunk) go
-//    to the workspace in thread order, (key << 32 | token) each.
+//    16-bit keys a register for bf16). Each wave finds the ceil(top_k/4)-th largest of its
+//    per-thread max keys (per-16-element-group max keys when top_k > 256) by a ballot radix
+//    select, and t_c is the smallest of the four. At least top_k chunk elements are >= t_c,
+//    so the row's top_k-th largest element is >= t_c too; the elements >= t_c (for i.i.d. logits a little over top_k per chunk) go
+//    to the workspace as (key << 32 | token), one list per wave compacted with ballots
+//    (fixed order: register, then lane).
 //  merge: one workgroup per row selects the exact top_k-th largest key among the chunks'
 //    candidates (their union holds every token the row keeps) and takes max, kept count and
 //    exp-sum from the candidates alone.
@@ -279,21 +280,27 @@ constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-b
 constexpr int kMergeNT = 256;      // threads of a merge workgroup
 constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
 constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
+constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
+constexpr int kMergeCap = 4096;  // candidates of a row the merge holds in LDS
+constexpr int kTkWcapMax = kTkMaxK;   // list capacity at the largest top_k
 
 struct TopkArgs {
     const uint8_t* tgt;
     const uint8_t* dft;
     int rows_t, V, nchunks, top_k;
-    int cap;                 // candidates per chunk
+    int wcap;                // candidates a wave of a chunk may contribute
+    int cstride;             // keys between the lists of consecutive chunks
     int generic;             // 1: every row takes the generic select
     float c;
-    int* cnt;                // [rows][nchunks] candidates found (-1: NaN / +inf in the chunk)
-    uint64_t* cand;          // [rows][nchunks][cap]
+    int* cnt;                // [rows][nchunks] candidates (-1: NaN / +inf; > 4 * wcap: overflow)
+    uint32_t* cand;          // [rows][nchunks] lists of cstride keys
     RowPartial* part;        // [rows]
     float* row_thr;          // [rows]
 };
 
-static inline int topk_cap(int top_k) { return top_k <= 128 ? 512 : 4 * top_k; }
+static inline int topk_wcap(int top_k) { return top_k <= 256 ? 256 : top_k; }
+static inline int topk_cstride(int wcap) { return kTkWaves * wcap + 16; }
+static_assert(kTkMaxK <= kTkWcapMax, "a list holds top_k keys");
 static inline bool topk_generic(int top_k) { return top_k > kTkMaxK; }
 
 template <bool BF16>
@@ -383,9 +390,10 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     using Lt = Layout<BF16, VEC>;
     using Kt = TopkKeys<BF16>;
     static_assert(NR * EPR == Lt::EPT, "a chunk is NT threads x NR registers");
-    __shared__ unsigned hist_a[256], hist_b[256];
-    __shared__ int redi[NT / kWave];
-    __shared__ int s_dig, s_krem;
+    static_assert(kTkWaves == 4, "t_c takes the minimum of four wave bounds");
+    __shared__ uint32_t s_tw[kTkWaves];
+    __shared__ int s_wn[kTkWaves];
+    __shared__ uint32_t s_list[kTkWaves * kTkWcapMax];
     const int tid = threadIdx.x;
     const int V = a.V;
     const uint8_t* base = row_ptr(a.tgt, a.dft, a.rows_t, row, V, Lt::ES);
@@ -441,153 +449,202 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     }
     if constexpr (BF16) kmin = min(kmin & 0xffffu, kmin >> 16);
     const uint32_t kmax = max(max(gm[0], gm[1]), max(gm[2], gm[3]));
-    for (int i = tid; i < 256; i += NT) hist_a[i] = hist_b[i] = 0u;
-    if (tid == 0) s_krem = a.top_k;
-    const int bad = block_max_i<NT>(kmax >= Kt::KEY_PINF || kmin < Kt::KEY_NINF, redi);
-    if (bad) {
-        if (tid == 0) a.cnt[(size_t)row * a.nchunks + chunk] = -1;
-        return;
-    }
+    const int lane = tid % kWave, wv = tid / kWave;
+    const bool wbad = __ballot(kmax >= Kt::KEY_PINF || kmin < Kt::KEY_NINF) != 0ull;
 
-    // 2. t_c: top_k-th largest per-thread (or per-group) max, upper 16 key bits for fp32
+    // 2. t_c: every wave takes the ceil(top_k / 4)-th largest of its per-thread (or, when
+    //    top_k > 256, per-group) max keys; t_c = the smallest of the four, so each wave, and
+    //    the chunk, holds at least top_k elements >= t_c. Upper 16 key bits for fp32.
     const bool groups = a.top_k > NT;
+    const int mth = (a.top_k + kTkWaves - 1) / kTkWaves;
     uint32_t tv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) tv[g] = BF16 ? gm[g] : gm[g] >> 16;
-    if (groups) {
+    const uint32_t tt = BF16 ? kmax : kmax >> 16;
+    uint32_t tw = 0u;
+    int krem = mth;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) atomicAdd(&hist_a[tv[g] >> 8], 1u);
-    } else {
-        atomicAdd(&hist_a[(BF16 ? kmax : kmax >> 16) >> 8], 1u);
-    }
-    __syncthreads();
-    if (tid < kWave) hist_select(hist_a, &s_dig, &s_krem);
-    __syncthreads();
-    const uint32_t d1 = (uint32_t)s_dig;
-    if (groups) {
+    for (int b = 15; b >= 0; --b) {
+        const uint32_t probe = (tw | (1u << b)) >> b;
+        int n;
+        if (groups) {
+            n = 0;
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-            if ((tv[g] >> 8) == d1) atomicAdd(&hist_b[tv[g] & 0xffu], 1u);
-    } else {
-        const uint32_t t = BF16 ? kmax : kmax >> 16;
-        if ((t >> 8) == d1) atomicAdd(&hist_b[t & 0xffu], 1u);
+            for (int g = 0; g < 4; ++g) n += __popcll(__ballot((tv[g] >> b) == probe));
+        } else {
+            n = __popcll(__ballot((tt >> b) == probe));
+        }
+        if (n >= krem) tw |= 1u << b;
+        else krem -= n;
     }
+    if (lane == 0) s_tw[wv] = tw;
     __syncthreads();
-    if (tid < kWave) hist_select(hist_b, &s_dig, &s_krem);
-    __syncthreads();
-    uint32_t t0 = (d1 << 8) | (uint32_t)s_dig;
+    uint32_t t0 = min(min(s_tw[0], s_tw[1]), min(s_tw[2], s_tw[3]));
     if constexpr (!BF16) t0 <<= 16;
     if (t0 == Kt::KEY_PZERO) t0 = Kt::KEY_NZERO;
 
-    // 3. candidates (key >= t0), written in thread order
-    const uint32_t below = BF16 ? (t0 - 1u) * 0x10001u : t0 - 1u;
-    unsigned hit = 0u;
-    int nh = 0;
+    // 3. candidates (key >= t0): each wave appends to its own list, ballot-compacted in
+    //    LDS, then copied out with coalesced stores
+    const uint64_t below_me = __lanemask_lt();
+    uint32_t* lst = s_list + wv * a.wcap;
+    int woff = 0;
 #pragma unroll
-    for (int j = 0; j < NR / 4; ++j) {
-        const uint32_t m4 = reg_max<BF16>(reg_max<BF16>(r[4 * j], r[4 * j + 1]),
-                                          reg_max<BF16>(r[4 * j + 2], r[4 * j + 3]));
-        if (reg_max<BF16>(m4, below) != below) {
-            hit |= 1u << j;
+    for (int w = 0; w < NR; ++w)
 #pragma unroll
-            for (int w = 4 * j; w < 4 * j + 4; ++w)
-#pragma unroll
-                for (int h = 0; h < EPR; ++h) nh += ((r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u)) >= t0;
-        }
-    }
-    int total;
-    int off = block_excl_scan_i<NT>(nh, redi, &total);
-    uint64_t* out = a.cand + ((size_t)row * a.nchunks + chunk) * a.cap;
-    if (nh) {
-#pragma unroll
-        for (int j = 0; j < NR / 4; ++j) {
-            if (hit & (1u << j)) {
-#pragma unroll
-                for (int w = 4 * j; w < 4 * j + 4; ++w)
-#pragma unroll
-                    for (int h = 0; h < EPR; ++h) {
-                        const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
-                        if (k >= t0) {
-                            if (off < a.cap) out[off] = ((uint64_t)k << 32) | (uint32_t)token(w, h);
-                            ++off;
-                        }
-                    }
+        for (int h = 0; h < EPR; ++h) {
+            const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+            const bool f = k >= t0;
+            const uint64_t bal = __ballot(f);
+            if (bal) {
+                const int pos = woff + __popcll(bal & below_me);
+                if (f && pos < a.wcap) lst[pos] = k;
+                woff += __popcll(bal);
             }
         }
+    if (lane == 0) s_wn[wv] = wbad ? -1 : woff;
+    __syncthreads();
+    int before = 0, total = 0, bad = 0, over = 0;
+#pragma unroll
+    for (int i = 0; i < kTkWaves; ++i) {
+        const int n = s_wn[i];
+        before += i < wv ? n : 0;
+        total += n;
+        bad |= n < 0;
+        over |= n > a.wcap;
     }
-    if (tid == 0) a.cnt[(size_t)row * a.nchunks + chunk] = total;
+    const size_t ci = (size_t)row * a.nchunks + chunk;
+    if (!bad && !over) {
+        uint32_t* out = a.cand + ci * a.cstride + before;
+        for (int i = lane; i < woff; i += kWave) out[i] = lst[i];
+    }
+    if (tid == 0) a.cnt[ci] = bad ? -1 : (over ? kTkWaves * a.wcap + 1 : total);
 }
 
 template <bool BF16>
 SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     constexpr int NT = kMergeNT;
+    constexpr int LPT = kTkMaxChunks / NT;              // lists per thread at most
+    constexpr int UNR = 4;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
     __shared__ unsigned hist[256];
-    __shared__ int s_cnt[kTkMaxChunks];
+    __shared__ int s_off[kTkMaxChunks + 1];
+    __shared__ uint32_t keys[kMergeCap];
     __shared__ int redi[NT / kWave];
-    __shared__ double redd[NT / kWave];
+    __shared__ double redd[2 * (NT / kWave)];
     __shared__ int s_dig, s_krem;
+    __shared__ unsigned s_kmax;
     const int tid = threadIdx.x;
-    const int nch = a.nchunks;
-    int flag = a.generic;
-    if (!a.generic) {
-        for (int ch = tid; ch < nch; ch += NT) {
-            const int n = a.cnt[(size_t)row * nch + ch];
-            s_cnt[ch] = n;
-            flag |= n < 0 || n > a.cap;
-        }
+    const int nl = a.nchunks;
+    const int lcap = kTkWaves * a.wcap;
+    // list counts (thread t owns lists t*LPT ..); a bad or overflowing list pushes the
+    // total past the LDS capacity, which sends the row to the generic select
+    int cnt[LPT];
+    int mine = 0;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+        const int l = tid * LPT + q;
+        cnt[q] = (!a.generic && l < nl) ? a.cnt[(size_t)row * nl + l] : 0;
+        mine += (cnt[q] < 0 || cnt[q] > lcap) ? kMergeCap + 1 : cnt[q];
     }
-    if (tid == 0) s_krem = a.top_k;
-    flag = block_max_i<NT>(flag, redi);
-    if (flag) {
+    if (a.generic) mine = kMergeCap + 1;
+    if (tid == 0) {
+        s_krem = a.top_k;
+        s_kmax = 0u;
+    }
+    int total;
+    int off = block_excl_scan_i<NT>(mine, redi, &total);
+    if (total > kMergeCap) {
         topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.top_k, a.c, a.part, a.row_thr, row);
         return;
     }
-    const uint64_t* cand = a.cand + (size_t)row * nch * a.cap;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+        const int l = tid * LPT + q;
+        if (l < nl) s_off[l] = off;
+        off += cnt[q];
+    }
+    if (tid == 0) s_off[nl] = total;
+    __syncthreads();
 
-    // exact top_k-th largest candidate key, one 8-bit digit at a time; the row max on the way
-    uint32_t prefix = 0u, kmax = 0u;
+    // candidate keys into LDS: entry e of the row lives in the list l with
+    // s_off[l] <= e < s_off[l + 1]
+    const uint32_t* cand = a.cand + (size_t)row * nl * a.cstride;
+    uint32_t kmax = 0u;
+    for (int e0 = 0; e0 < total; e0 += UNR * NT) {
+        uint32_t v[UNR];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int e = e0 + u * NT + tid;
+            v[u] = 0u;
+            if (e < total) {
+                int lo = 0, hi = nl;                 // largest l with s_off[l] <= e
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_off[mid] <= e) lo = mid;
+                    else hi = mid;
+                }
+                v[u] = cand[(size_t)lo * a.cstride + (e - s_off[lo])];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int e = e0 + u * NT + tid;
+            if (e < total) {
+                keys[e] = v[u];
+                kmax = max(kmax, v[u]);
+            }
+        }
+    }
+    if (kmax) atomicMax(&s_kmax, kmax);
+    __syncthreads();
+
+    // exact top_k-th largest candidate key, one 8-bit digit at a time
+    uint32_t prefix = 0u;
 #pragma unroll
     for (int shift = Kt::KBITS - 8; shift >= 0; shift -= 8) {
         const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
         for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();
-        for (int ch = 0; ch < nch; ++ch) {
-            const int n = s_cnt[ch];
-            for (int i = tid; i < n; i += NT) {
-                const uint32_t k = uint32_t(cand[(size_t)ch * a.cap + i] >> 32);
-                if (shift == Kt::KBITS - 8) kmax = max(kmax, k);
-                if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
-            }
+        for (int i = tid; i < total; i += NT) {
+            const uint32_t k = keys[i];
+            if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
         }
         __syncthreads();
         if (tid < kWave) hist_select(hist, &s_dig, &s_krem);
         __syncthreads();
         prefix |= (uint32_t)s_dig << shift;
     }
-    const uint32_t rmax = uint32_t(block_max_i<NT>(int(kmax ^ 0x80000000u), redi)) ^ 0x80000000u;
     const float thr = key_to_float<BF16>(prefix);
-    const float m = key_to_float<BF16>(rmax);
+    const float m = key_to_float<BF16>(s_kmax);
     const float mc = m * a.c;
     const float emc = fmaf(m, a.c, -mc);
     float acc = 0.f;
     int kept = 0;
-    for (int ch = 0; ch < nch; ++ch) {
-        const int n = s_cnt[ch];
-        for (int i = tid; i < n; i += NT) {
-            const float z = key_to_float<BF16>(uint32_t(cand[(size_t)ch * a.cap + i] >> 32));
-            if (z >= thr && z > -INFINITY) {
-                acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
-                ++kept;
-            }
+    for (int i = tid; i < total; i += NT) {
+        const float z = key_to_float<BF16>(keys[i]);
+        if (z >= thr && z > -INFINITY) {
+            acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
+            ++kept;
         }
     }
-    const double tot = block_sum<NT>((double)acc, redd);
-    kept = block_sum_i<NT>(kept, redi);
+    // kept count and sum in one reduction (a count below 2^53 is exact in fp64)
+    double sum = wave_sum((double)acc), kd = wave_sum((double)kept);
+    const int w = tid / kWave, l = tid % kWave;
+    if (l == 0) {
+        redd[w] = sum;
+        redd[NT / kWave + w] = kd;
+    }
+    __syncthreads();
     if (tid == 0) {
+        double tot = 0.0, kt = 0.0;
+#pragma unroll
+        for (int i = 0; i < NT / kWave; ++i) {
+            tot += redd[i];
+            kt += redd[NT / kWave + i];
+        }
         RowPartial rp;
         rp.m = m;
-        rp.nkept = kept;
+        rp.nkept = (int)kt;
         rp.s = m == -INFINITY ? 0.0 : tot * exp2(-(double)emc);
         a.part[row] = rp;
         a.row_thr[row] = thr;
@@ -1046,7 +1103,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
     size_t part, thr, rec, wsum, tk_cnt, tk_cand, total;
-    int nparts, nchunks, nch, tk_cap;
+    int nparts, nchunks, nch, tk_wcap;
 };
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
@@ -1070,10 +1127,11 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     off = align256(off + (size_t)B * p.nch * sizeof(double));
     p.tk_cnt = p.tk_cand = off;
     if (topk_active(top_k, V) && !topk_generic(top_k)) {
-        p.tk_cap = topk_cap(top_k);
-        off = align256(off + rows * p.nchunks * sizeof(int));
+        p.tk_wcap = topk_wcap(top_k);
+        const size_t lists = rows * p.nchunks;
+        off = align256(off + lists * sizeof(int));
         p.tk_cand = off;
-        off = align256(off + rows * p.nchunks * (size_t)p.tk_cap * sizeof(uint64_t));
+        off = align256(off + lists * (size_t)topk_cstride(p.tk_wcap) * sizeof(uint32_t));
     }
     p.total = off;
     return p;
@@ -1088,11 +1146,12 @@ static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int row
     a.V = V;
     a.nchunks = p.nchunks;
     a.top_k = top_k;
-    a.cap = p.tk_cap;
+    a.wcap = p.tk_wcap;
+    a.cstride = topk_cstride(p.tk_wcap);
     a.generic = topk_generic(top_k);
     a.c = c;
     a.cnt = reinterpret_cast<int*>(ws + p.tk_cnt);
-    a.cand = reinterpret_cast<uint64_t*>(ws + p.tk_cand);
+    a.cand = reinterpret_cast<uint32_t*>(ws + p.tk_cand);
     a.part = reinterpret_cast<RowPartial*>(ws + p.part);
     a.row_thr = reinterpret_cast<float*>(ws + p.thr);
     return a;

@@ -44,9 +44,9 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     n = binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 0)
     assert n > 0 and n % 256 == 0
-    # top-k rows keep per-chunk candidate lists: 2816 rows x 8 chunks x 512 x 8 bytes
+    # top-k rows keep per-chunk candidate lists: 2816 rows x 8 chunks x 1040 keys x 4 bytes
     assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 64) >= \
-        2816 * 8 * 512 * 8
+        2816 * 8 * 1040 * 4
     # above the chunked select's top_k limit only the generic select runs: no lists
     assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 2000) < n
     assert binding.specdec_verify_workspace_size(0, 0, 10, 0, 0) == 0

@@ -123,7 +123,7 @@ def test_topk_planted_rows_small_vocab():
 
 def test_topk_planted_rows_one_chunk():
     # every token a candidate (threshold -inf, signed zeros) without overflowing the chunk
-    vin = synth.make_verify("c4", seed=50, B=3, V=512, k=2)
+    vin = synth.make_verify("c4", seed=50, B=3, V=256, k=2)
     pats = [_few_finite, _signed_zero_threshold, _integer_ties]
     _check(_plant(vin, pats, seed=51))
 
