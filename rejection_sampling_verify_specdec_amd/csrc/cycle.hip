@@ -31,7 +31,7 @@
 namespace sd {
 
 constexpr int kCycAllocNT = kNT;   // allocation workgroup inside the statistics launch
-constexpr int kCycScatterPPT = 1;  // 16-byte pieces per scatter thread (many small groups)
+constexpr int kCycScatterPPT = kScPPT;   // token rows per scatter thread in flight
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __restrict__ cu,

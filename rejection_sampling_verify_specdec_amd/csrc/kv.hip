@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kScNT) void k_kv_scatter(KvArgs a, const uint8_t* _
                                                       const uint8_t* __restrict__ vnew, int B,
                                                       int N, int tpw,
                                                       const uint8_t* __restrict__ ws) {
-    scatter_body<1>(a, knew, vnew, B, N, tpw, ws, blockIdx.x, blockIdx.y,
+    scatter_body<kScPPT>(a, knew, vnew, B, N, tpw, ws, blockIdx.x, blockIdx.y,
                  blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y, kScNT);
 }
 
@@ -70,7 +70,7 @@ extern "C" int kv_paged_append(const kv_paged_cache* cache, int32_t B, const voi
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_kv_alloc, dim3(1), dim3(kKvNT), 0, stream, a, cu_new, B, N, ws);
-    const int tpw = scatter_tokens_per_wg(a, kScNT, 1);   // many small workgroups
+    const int tpw = scatter_tokens_per_wg(a, kScNT, kScPPT);
     const unsigned tiles = (unsigned)((N + tpw - 1) / tpw);
     if (tiles > 0)
         hipLaunchKernelGGL(k_kv_scatter, dim3(tiles, (unsigned)a.L * 2), dim3(kScNT), 0, stream, a,

@@ -14,7 +14,7 @@ namespace sd {
 constexpr int kKvNT = 1024;      // rollback workgroup (and the standalone allocation)
 constexpr int kKvRPT = SPECDEC_MAX_KV_BATCH / kKvNT;   // rollback requests per thread
 constexpr int kScNT = 256;       // standalone scatter workgroup
-constexpr int kScMaxTok = 16;    // tokens per scatter workgroup (for small rows)
+constexpr int kScPPT = 8;        // token rows per scatter thread in flight
 constexpr int kEvCap = 2048;     // rollback events per window
 constexpr int kEvPT = kEvCap / kKvNT;
 
@@ -229,8 +229,11 @@ SD_DEV void alloc_body(const KvArgs& a, const int* __restrict__ cu, int derive, 
 }
 
 // Scatter of the new entries: workgroup `wg` of `nwg` handles tokens [tile * tpw, ...) of
-// layer / K-V plane lk; each thread moves 16-byte pieces of token rows to the
-// destination rows the allocation wrote. Then the copy-on-write copies, grid-stride over
+// layer / K-V plane lk and moves their rows (H*D bf16, 16-byte pieces) to the destination
+// rows the allocation wrote. Thread tid owns piece column tid % lanes of every tpp-th
+// token (tpp = nt / lanes tokens per pass when a row has fewer pieces than the group has
+// threads), so no per-piece division is needed; P rows per thread are in flight (all
+// loads, then all stores). Then the copy-on-write copies, grid-stride over
 // (entry, layer, K/V).
 template <int P>
 SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
@@ -243,35 +246,35 @@ SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
     const int l = lk >> 1;
     const size_t ub = (size_t)a.H * a.D * 2;   // bytes of one token's row
     const int lanes = (int)(ub / 16);
+    const int tpp = lanes >= nt ? 1 : nt / lanes;            // tokens per pass
+    const int rounds = lanes >= nt ? (lanes + nt - 1) / nt : 1;
+    const int my_tok = lanes >= nt ? 0 : tid / lanes;
+    const int my_q = lanes >= nt ? tid : tid - my_tok * lanes;
     const int t0 = tile * tpw;
+    const int ntok = min(tpw, N - t0);
+    const int jmax = my_tok < tpp ? (ntok - my_tok + tpp - 1) / tpp : 0;   // tokens of mine
     const long long* drow = reinterpret_cast<const long long*>(wsb + 16 + (size_t)40 * B);
-    const uint8_t* src_base = (lk & 1) ? vnew : knew;
+    const uint8_t* src_base = ((lk & 1) ? vnew : knew) + (size_t)l * N * ub;
     uint8_t* dst_base = a.pool + (size_t)lk * a.NB * a.bs * ub;
-    // P 16-byte pieces per thread in flight: all loads first, then the stores (the
-    // destination row is re-read at store time to keep registers for the data)
-    const int pieces = tpw * lanes;
-    for (int base = 0; base < pieces; base += P * nt) {
-        u32x4 v[P];
+    for (int j0 = 0; j0 < jmax; j0 += P) {
+        long long d[P];
 #pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int idx = base + u * nt + tid;
-            const int tok = idx / lanes;
-            const int t = t0 + tok;
-            if (idx < pieces && t < N && drow[t] >= 0)
-                v[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4*>(src_base + ((size_t)l * N + t) * ub) + (idx - tok * lanes));
-        }
+        for (int u = 0; u < P; ++u) d[u] = j0 + u < jmax ? drow[t0 + my_tok + (j0 + u) * tpp] : -1;
+        for (int r = 0; r < rounds; ++r) {
+            const int q = my_q + r * nt;
+            if (q >= lanes) break;
+            u32x4 v[P];
 #pragma unroll
-        for (int u = 0; u < P; ++u) {
-            const int idx = base + u * nt + tid;
-            const int tok = idx / lanes;
-            const int t = t0 + tok;
-            if (idx < pieces && t < N) {
-                const long long d = drow[t];
-                if (d >= 0)
-                    __builtin_nontemporal_store(
-                        v[u], reinterpret_cast<u32x4*>(dst_base + (size_t)d * ub) + (idx - tok * lanes));
+            for (int u = 0; u < P; ++u) {
+                const int t = t0 + my_tok + (j0 + u) * tpp;
+                if (d[u] >= 0)
+                    v[u] = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x4*>(src_base + (size_t)t * ub) + q);
             }
+#pragma unroll
+            for (int u = 0; u < P; ++u)
+                if (d[u] >= 0)
+                    __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(dst_base + (size_t)d[u] * ub) + q);
         }
     }
     const int ncow = ws[1];
@@ -450,10 +453,11 @@ static inline KvArgs args_of(const kv_paged_cache* c) {
 }
 
 // Tokens per scatter workgroup for about `ppt` 16-byte pieces per thread.
+// Tokens per scatter workgroup of nt threads with ppt rows per thread in flight.
 static inline int scatter_tokens_per_wg(const KvArgs& a, int nt, int ppt) {
     const int lanes = (int)((size_t)a.H * a.D * 2 / 16);
-    const int t = (ppt * nt) / lanes;
-    return t < 1 ? 1 : (t > kScMaxTok * 8 ? kScMaxTok * 8 : t);
+    const int tpp = lanes >= nt ? 1 : nt / lanes;
+    return tpp * ppt;
 }
 
 }  // namespace sd
