@@ -13,7 +13,6 @@ baseline: the fp64 oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -24,9 +23,10 @@ sys.path.insert(0, ROOT)
 
 import numpy as np  # noqa: E402
 
+from rejection_sampling_verify_specdec_amd.profsum import source_hash  # noqa: E402
+
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% peak), B=256 k=5 V=128256 bf16"
 PEAK_GBPS = 8000.0
-CSRC = os.path.join(ROOT, "rejection_sampling_verify_specdec_amd", "csrc")
 
 
 def parse():
@@ -51,15 +51,6 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time the oracle baseline runs for")
     return p.parse_args()
-
-
-def source_hash() -> str:
-    """Hash of every kernel source file: counters taken on other sources do not apply."""
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
-    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(kernel: str, workload: str):

@@ -2,16 +2,33 @@
 
     python -m rejection_sampling_verify_specdec_amd.profsum trace DB [--cmd "..."]
     python -m rejection_sampling_verify_specdec_amd.profsum traffic FETCH_DB WRITE_DB \
-        --kernel k_row_stats --calib-kernel copyBuffer --calib-bytes N --alg-bytes A
+        --kernel k_cycle_stats --calib-kernel copyBuffer --calib-bytes N --alg-bytes A \
+        [--json profiles/KERNEL_WORKLOAD_traffic.json --workload c2 --cmd "..."]
 
 ``trace`` prints count / average / min / max duration per kernel. ``traffic`` turns the
 FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of a kernel into HBM bytes per
-launch, scaled by what the same counters read for a plain copy kernel of known size.
+launch, scaled by what the same counters read for a plain copy kernel of known size (the
+largest dispatch of the calibration kernel: the copy of N bytes), and optionally writes
+the JSON summary that bench.py reads, stamped with the hash of the kernel sources.
 """
 
 import argparse
+import hashlib
+import json
+import os
 import sqlite3
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_hash() -> str:
+    """Hash of every kernel source file: counters taken on other sources do not apply."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _kernels(db):
@@ -54,8 +71,8 @@ def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes, alg_bytes=Non
     if not (cf and cw and kf and kw):
         raise RuntimeError("kernel or calibration copy not found in the counter databases")
     # the copy reads and writes calib_bytes: KiB reported -> bytes scale factors
-    sf = calib_bytes / (sum(cf) / len(cf) * 1024.0)
-    sw = calib_bytes / (sum(cw) / len(cw) * 1024.0)
+    sf = calib_bytes / (max(cf) * 1024.0)
+    sw = calib_bytes / (max(cw) * 1024.0)
     fetch = sum(kf) / len(kf) * 1024.0 * sf
     write = sum(kw) / len(kw) * 1024.0 * sw
     lines = [f"kernel {kernel}: {len(kf)} dispatches",
@@ -65,7 +82,10 @@ def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes, alg_bytes=Non
              f"total HBM bytes/launch {fetch + write:.4e}"]
     if alg_bytes:
         lines.append(f"algorithmic bytes/launch {alg_bytes:.4e}  ratio {(fetch + write) / alg_bytes:.4f}")
-    return "\n".join(lines), fetch + write
+    info = {"kernel": kernel, "dispatches": len(kf), "fetch_scale": sf, "write_scale": sw,
+            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+            "bytes_per_launch": fetch + write, "algorithmic_bytes_per_launch": alg_bytes}
+    return "\n".join(lines), info
 
 
 def main(argv=None):
@@ -81,11 +101,21 @@ def main(argv=None):
     p.add_argument("--calib-kernel", required=True)
     p.add_argument("--calib-bytes", type=float, required=True)
     p.add_argument("--alg-bytes", type=float)
+    p.add_argument("--json", help="write the summary bench.py reads")
+    p.add_argument("--workload")
+    p.add_argument("--cmd", help="the profiling command, recorded in the JSON")
     a = ap.parse_args(argv)
     if a.what == "trace":
         print(trace(a.db, a.cmd))
     else:
-        print(traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes, a.alg_bytes)[0])
+        text, info = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes,
+                             a.alg_bytes)
+        print(text)
+        if a.json:
+            info.update(workload=a.workload, command=a.cmd, source_sha256_16=source_hash())
+            with open(a.json, "w") as f:
+                json.dump(info, f, indent=1)
+                f.write("\n")
 
 
 if __name__ == "__main__":
