@@ -88,18 +88,28 @@ __global__ __launch_bounds__(kDecideNT) void k_cycle_decide(SampleArgs sa, KvArg
                                  ntiles * planes, kScNT);
 }
 
+// Up to kCycRbMaxB requests the rollback runs as workgroup 0 of the chunk-sum launch (its
+// LDS then stays small), otherwise as workgroup 0 of the pick launch.
+constexpr int kCycRbMaxB = 512;
+constexpr int kCycRbEv = 512;
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa) {
-    part_body<BF16, VEC, kPartNT>(sa, blockIdx.x / sa.nch, blockIdx.x % sa.nch);
+__global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa, KvArgs kv, int rb) {
+    if (rb && blockIdx.x == 0) {
+        rollback_body<kPartNT, kCycRbMaxB, kCycRbEv>(kv, sa.num_acc, sa.cu, sa.B);
+        return;
+    }
+    const int w = blockIdx.x - rb;
+    part_body<BF16, VEC, kPartNT>(sa, w / sa.nch, w % sa.nch);
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa, KvArgs kv) {
-    if (blockIdx.x == 0) {
+__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa, KvArgs kv, int rb) {
+    if (!rb && blockIdx.x == 0) {
         rollback_body(kv, sa.num_acc, sa.cu, sa.B);
         return;
     }
-    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x - 1);
+    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x - !rb);
 }
 
 template <bool BF16, bool VEC>
@@ -129,9 +139,10 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     const int ntiles = (N + tpw - 1) / tpw;
     hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
                        dim3(kDecideNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
-    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch), dim3(kPartNT), 0, st,
-                       sa);
-    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B + 1), dim3(kPickNT), 0, st, sa, kv);
+    const int rb = B <= kCycRbMaxB;
+    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
+                       st, sa, kv, rb);
+    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B + !rb), dim3(kPickNT), 0, st, sa, kv, rb);
 }
 
 }  // namespace sd

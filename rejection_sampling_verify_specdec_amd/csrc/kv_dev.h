@@ -12,11 +12,9 @@
 namespace sd {
 
 constexpr int kKvNT = 1024;      // rollback workgroup (and the standalone allocation)
-constexpr int kKvRPT = SPECDEC_MAX_KV_BATCH / kKvNT;   // rollback requests per thread
 constexpr int kScNT = 256;       // standalone scatter workgroup
 constexpr int kScPPT = 8;        // token rows per scatter thread in flight
 constexpr int kEvCap = 2048;     // rollback events per window
-constexpr int kEvPT = kEvCap / kKvNT;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -292,24 +290,30 @@ SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
     }
 }
 
+// Rollback of every request by one workgroup of NT threads, for B <= MAXB requests;
+// events (freed logical blocks) are processed in windows of EVCAP.
+template <int NT = kKvNT, int MAXB = SPECDEC_MAX_KV_BATCH, int EVCAP = kEvCap>
 SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
                           const int* __restrict__ cu, int B) {
-    __shared__ int redi[kKvNT / kWave];
-    __shared__ int s_off[SPECDEC_MAX_KV_BATCH + 1];
-    __shared__ int s_lb0[SPECDEC_MAX_KV_BATCH];
-    __shared__ int s_X[kEvCap];
-    __shared__ int s_b[kEvCap];
-    __shared__ int s_lb[kEvCap];
+    constexpr int RPT = MAXB / NT;    // requests per thread
+    constexpr int EPT = EVCAP / NT;   // window events per thread
+    static_assert(RPT * NT == MAXB && EPT * NT == EVCAP, "whole rounds per thread");
+    __shared__ int redi[NT / kWave];
+    __shared__ int s_off[MAXB + 1];
+    __shared__ int s_lb0[MAXB];
+    __shared__ int s_X[EVCAP];
+    __shared__ int s_b[EVCAP];
+    __shared__ int s_lb[EVCAP];
     if (*a.state & KV_APPEND_REJECTED) return;
     const int tid = threadIdx.x;
-    const int rounds = (B + kKvNT - 1) / kKvNT;
+    const int rounds = (B + NT - 1) / NT;
     int fc = *a.free_count;
     int err = 0;
-    int newlen[kKvRPT], valid[kKvRPT];
+    int newlen[RPT], valid[RPT];
     int E = 0;
 #pragma unroll
-    for (int i = 0; i < kKvRPT; ++i) {
-        const int b = i * kKvNT + tid;
+    for (int i = 0; i < RPT; ++i) {
+        const int b = i * NT + tid;
         valid[i] = 0;
         newlen[i] = 0;
         int ev = 0;
@@ -326,7 +330,7 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
         }
         if (i < rounds) {
             int tot;
-            const int off = E + block_excl_scan_i<kKvNT>(ev, redi, &tot);
+            const int off = E + block_excl_scan_i<NT>(ev, redi, &tot);
             if (b < B) {
                 s_off[b] = off;
                 s_lb0[b] = ceil_div(newlen[i], a.bs);
@@ -336,12 +340,12 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
     }
     if (tid == 0) s_off[B] = E;
     __syncthreads();
-    for (int w0 = 0; w0 < E; w0 += kEvCap) {
-        const int nw = min(kEvCap, E - w0);
+    for (int w0 = 0; w0 < E; w0 += EVCAP) {
+        const int nw = min(EVCAP, E - w0);
         // gather this window's events in (request, logical block) order
 #pragma unroll
-        for (int i = 0; i < kEvPT; ++i) {
-            const int el = i * kKvNT + tid;
+        for (int i = 0; i < EPT; ++i) {
+            const int el = i * NT + tid;
             if (el >= nw) continue;
             const int e = w0 + el;
             int lo = 0, hi = B;               // largest b with s_off[b] <= e
@@ -356,10 +360,10 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
             s_X[el] = a.tables[(size_t)lo * a.MBR + lb];
         }
         __syncthreads();
-        int push[kEvPT], newrc[kEvPT], first[kEvPT];
+        int push[EPT], newrc[EPT], first[EPT];
 #pragma unroll
-        for (int i = 0; i < kEvPT; ++i) {
-            const int el = i * kKvNT + tid;
+        for (int i = 0; i < EPT; ++i) {
+            const int el = i * NT + tid;
             push[i] = first[i] = 0;
             newrc[i] = 0;
             if (el >= nw) continue;
@@ -384,17 +388,17 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
             newrc[i] = rc - min(cnt, max(rc, 0));
         }
         // push positions follow event order (the scans also separate reads from writes)
-        int pbase[kEvPT];
+        int pbase[EPT];
         int ptot = 0;
 #pragma unroll
-        for (int i = 0; i < kEvPT; ++i) {
+        for (int i = 0; i < EPT; ++i) {
             int tot;
-            pbase[i] = ptot + block_excl_scan_i<kKvNT>(push[i], redi, &tot);
+            pbase[i] = ptot + block_excl_scan_i<NT>(push[i], redi, &tot);
             ptot += tot;
         }
 #pragma unroll
-        for (int i = 0; i < kEvPT; ++i) {
-            const int el = i * kKvNT + tid;
+        for (int i = 0; i < EPT; ++i) {
+            const int el = i * NT + tid;
             if (el >= nw) continue;
             const int X = s_X[el];
             if (X >= 0 && X < a.NB) {
@@ -410,11 +414,11 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < kKvRPT; ++i) {
-        const int b = i * kKvNT + tid;
+    for (int i = 0; i < RPT; ++i) {
+        const int b = i * NT + tid;
         if (b < B && valid[i]) a.seq_lens[b] = newlen[i];
     }
-    err = block_max_i<kKvNT>(err, redi);
+    err = block_max_i<NT>(err, redi);
     if (tid == 0) {
         *a.free_count = min(fc, a.NB);
         if (err) atomicOr(a.state, KV_ERR_ROLLBACK);

@@ -109,3 +109,31 @@ def test_fused_cycle_equals_three_calls(case):
         assert a[1]["state"] & binding.KV_ERR_NOMEM
     if case == "bad_offsets":
         assert a[1]["state"] & binding.KV_ERR_APPEND and (a[0].num_accepted == -1).all()
+
+
+@pytest.mark.parametrize("B,k", [(600, 3), (300, 40)])
+def test_fused_cycle_batch_shapes(B, k):
+    # 600 requests: the truncation runs in the pick launch; 300 requests x 40 proposals with
+    # early rejections free more blocks than one window of the chunk-sum launch holds
+    vin = synth.make_verify("c4", seed=35, B=B, V=1024, k=k, top_k=0,
+                            classes=((1.0, "noise", 4.0),))
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=60, prefix_hi=400, share_group=3,
+                         share_blocks=2)
+    kv = synth.make_kv("c4", vin, seed=35, recipe=rec)
+    log(f"[fused-vs-calls] B={B} k={k}")
+    a = _run_mode(vin, kv, "calls")
+    b = _run_mode(vin, kv, "fused")
+    dropped = int((vin.k_b - a[0].num_accepted).sum())
+    log(f"[fused-vs-calls]   entries dropped by the rollback: {dropped}")
+    for f in ("num_accepted", "num_emitted", "out_tokens", "err_word"):
+        assert np.array_equal(np.asarray(getattr(a[0], f)), np.asarray(getattr(b[0], f))), f
+    for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
+        assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
+    assert np.array_equal(a[2], b[2])
+    assert a[1]["state"] == 0
+    # and both equal the oracle's append + rollback with these accepted counts
+    o_kv = oracle_kv(kv)
+    o_kv.append(kv.k_new, kv.v_new, kv.cu_new)
+    o_kv.rollback(a[0].num_accepted, vin.cu_draft)
+    errs = compare_kv_meta(o_kv, b[1], f"B={B}")
+    assert not errs, "\n".join(errs)
