@@ -277,11 +277,11 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // ---------------------------------------------------------------------------------------
 constexpr int kTkNT = kNT;         // threads of a chunk workgroup
 constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-byte vectors)
-constexpr int kMergeNT = 256;      // threads of a merge workgroup
+constexpr int kMergeNT = 128;      // threads of a merge workgroup
 constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
 constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
-constexpr int kMergeCap = 4096;  // candidates of a row the merge holds in LDS
+constexpr int kMergeCap = 3072;  // candidates of a row the merge holds in LDS
 constexpr int kTkWcapMax = kTkMaxK;   // list capacity at the largest top_k
 
 struct TopkArgs {
@@ -524,7 +524,7 @@ template <bool BF16>
 SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     constexpr int NT = kMergeNT;
     constexpr int LPT = kTkMaxChunks / NT;              // lists per thread at most
-    constexpr int UNR = 4;                              // candidate loads in flight per thread
+    constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
     __shared__ unsigned hist[256];
     __shared__ int s_off[kTkMaxChunks + 1];
