@@ -215,6 +215,9 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
     sa.rec = reinterpret_cast<Decision*>(vws + p.rec);
     sa.wsum = reinterpret_cast<double*>(vws + p.wsum);
+    sa.kn = p.tk_listed ? reinterpret_cast<const int*>(vws + p.tk_kn) : nullptr;
+    sa.ktok = p.tk_listed ? reinterpret_cast<const uint32_t*>(vws + p.tk_ktok) : nullptr;
+    sa.kkey = p.tk_listed ? reinterpret_cast<const uint16_t*>(vws + p.tk_kkey) : nullptr;
     sa.out_tokens = out_tokens;
     sa.num_acc = num_accepted;
     sa.num_emit = num_emitted;

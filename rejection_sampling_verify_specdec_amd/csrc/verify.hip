@@ -159,6 +159,9 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
     sa.rec = reinterpret_cast<Decision*>(ws + p.rec);
     sa.wsum = reinterpret_cast<double*>(ws + p.wsum);
+    sa.kn = p.tk_listed ? reinterpret_cast<const int*>(ws + p.tk_kn) : nullptr;
+    sa.ktok = p.tk_listed ? reinterpret_cast<const uint32_t*>(ws + p.tk_ktok) : nullptr;
+    sa.kkey = p.tk_listed ? reinterpret_cast<const uint16_t*>(ws + p.tk_kkey) : nullptr;
     sa.out_tokens = out_tokens;
     sa.num_acc = num_accepted;
     sa.num_emit = num_emitted;

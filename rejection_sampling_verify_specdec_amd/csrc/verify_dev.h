@@ -269,7 +269,9 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 //    (fixed order: register, then lane).
 //  merge: one workgroup per row selects the exact top_k-th largest key among the chunks'
 //    candidates (their union holds every token the row keeps) and takes max, kept count and
-//    exp-sum from the candidates alone.
+//    exp-sum from the candidates alone. For bf16 target rows it also lists the kept tokens
+//    in ascending order (at most kKeptCap): the draw then scans that list instead of the
+//    vocabulary.
 // Rows holding NaN or +inf, rows with a chunk that overflows its candidate capacity (heavy
 // ties at the threshold) and top_k above 1024 take the generic multi-pass select in the
 // merge launch instead. -0 and +0 compare equal as floats but not as keys: t_c is lowered
@@ -283,6 +285,7 @@ constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
 constexpr int kMergeCap = 3072;  // candidates of a row the merge holds in LDS
 constexpr int kTkWcapMax = kTkMaxK;   // list capacity at the largest top_k
+constexpr int kKeptCap = 512;   // kept tokens of a bf16 target row listed for the draw
 
 struct TopkArgs {
     const uint8_t* tgt;
@@ -293,7 +296,11 @@ struct TopkArgs {
     int generic;             // 1: every row takes the generic select
     float c;
     int* cnt;                // [rows][nchunks] candidates (-1: NaN / +inf; > 4 * wcap: overflow)
-    uint32_t* cand;          // [rows][nchunks] lists of cstride keys
+    uint32_t* cand;          // [rows][nchunks] lists of cstride entries: keys (fp32), or
+                             // key << 16 | token - chunk start (bf16)
+    int* kn;                 // bf16: [rows_t] kept tokens listed (-1: none), else null
+    uint32_t* ktok;          // [rows_t][kKeptCap] kept tokens, ascending
+    uint16_t* kkey;          // [rows_t][kKeptCap] their keys
     RowPartial* part;        // [rows]
     float* row_thr;          // [rows]
 };
@@ -497,7 +504,8 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
             const uint64_t bal = __ballot(f);
             if (bal) {
                 const int pos = woff + __popcll(bal & below_me);
-                if (f && pos < a.wcap) lst[pos] = k;
+                if (f && pos < a.wcap)
+                    lst[pos] = BF16 ? (k << 16) | (uint32_t)(token(w, h) - c0) : k;
                 woff += __popcll(bal);
             }
         }
@@ -526,13 +534,20 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     constexpr int LPT = kTkMaxChunks / NT;              // lists per thread at most
     constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
-    __shared__ unsigned hist[256];
+    static_assert(kKeptCap >= 256, "the histogram and the kept-token list share LDS");
+    __shared__ uint32_t s_u32[kKeptCap];    // radix histogram, then the kept tokens
+    unsigned* hist = s_u32;
+    uint32_t* s_ktok = s_u32;
     __shared__ int s_off[kTkMaxChunks + 1];
-    __shared__ uint32_t keys[kMergeCap];
+    __shared__ uint32_t keys[kMergeCap];    // entries as the chunks wrote them
+    __shared__ uint16_t s_kkey[BF16 ? kKeptCap : 1];
     __shared__ int redi[NT / kWave];
     __shared__ double redd[2 * (NT / kWave)];
-    __shared__ int s_dig, s_krem;
+    __shared__ int s_dig, s_krem, s_nk;
     __shared__ unsigned s_kmax;
+    // an entry's key
+    auto key_of = [](uint32_t e) { return BF16 ? e >> 16 : e; };
+    const bool listed = BF16 && a.kn && row < a.rows_t;
     const int tid = threadIdx.x;
     const int nl = a.nchunks;
     const int lcap = kTkWaves * a.wcap;
@@ -550,10 +565,12 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     if (tid == 0) {
         s_krem = a.top_k;
         s_kmax = 0u;
+        s_nk = 0;
     }
     int total;
     int off = block_excl_scan_i<NT>(mine, redi, &total);
     if (total > kMergeCap) {
+        if (listed && tid == 0) a.kn[row] = -1;
         topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.top_k, a.c, a.part, a.row_thr, row);
         return;
     }
@@ -569,6 +586,15 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     // candidate keys into LDS: entry e of the row lives in the list l with
     // s_off[l] <= e < s_off[l + 1]
     const uint32_t* cand = a.cand + (size_t)row * nl * a.cstride;
+    auto list_of = [&](int e) {        // largest l with s_off[l] <= e
+        int lo = 0, hi = nl;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
     uint32_t kmax = 0u;
     for (int e0 = 0; e0 < total; e0 += UNR * NT) {
         uint32_t v[UNR];
@@ -577,12 +603,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
             const int e = e0 + u * NT + tid;
             v[u] = 0u;
             if (e < total) {
-                int lo = 0, hi = nl;                 // largest l with s_off[l] <= e
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_off[mid] <= e) lo = mid;
-                    else hi = mid;
-                }
+                const int lo = list_of(e);
                 v[u] = cand[(size_t)lo * a.cstride + (e - s_off[lo])];
             }
         }
@@ -591,7 +612,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
             const int e = e0 + u * NT + tid;
             if (e < total) {
                 keys[e] = v[u];
-                kmax = max(kmax, v[u]);
+                kmax = max(kmax, key_of(v[u]));
             }
         }
     }
@@ -606,7 +627,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
         for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();
         for (int i = tid; i < total; i += NT) {
-            const uint32_t k = keys[i];
+            const uint32_t k = key_of(keys[i]);
             if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
         }
         __syncthreads();
@@ -621,11 +642,35 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     float acc = 0.f;
     int kept = 0;
     for (int i = tid; i < total; i += NT) {
-        const float z = key_to_float<BF16>(keys[i]);
+        const uint32_t k = key_of(keys[i]);
+        const float z = key_to_float<BF16>(k);
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
             ++kept;
+            if (listed) {
+                const int pos = atomicAdd(&s_nk, 1);
+                if (pos < kKeptCap) {
+                    s_ktok[pos] = (uint32_t)list_of(i) * (uint32_t)Layout<BF16, true>::CH +
+                                  (keys[i] & 0xffffu);
+                    s_kkey[pos] = (uint16_t)k;
+                }
+            }
         }
+    }
+    if (listed) {
+        // the kept tokens in ascending order: each one's rank among them
+        __syncthreads();
+        const int nk = s_nk;
+        if (nk <= kKeptCap) {
+            for (int i = tid; i < nk; i += NT) {
+                const uint32_t x = s_ktok[i];
+                int rank = 0;
+                for (int j = 0; j < nk; ++j) rank += s_ktok[j] < x;
+                a.ktok[(size_t)row * kKeptCap + rank] = x;
+                a.kkey[(size_t)row * kKeptCap + rank] = s_kkey[i];
+            }
+        }
+        if (tid == 0) a.kn[row] = nk <= kKeptCap ? nk : -1;
     }
     // kept count and sum in one reduction (a count below 2^53 is exact in fp64)
     double sum = wave_sum((double)acc), kd = wave_sum((double)kept);
@@ -693,6 +738,9 @@ struct SampleArgs {
     const float* row_thr;
     Decision* rec;           // [B] each request's decision, for the draw
     double* wsum;            // [B][nch] chunk sums of the sampling weights
+    const int* kn;           // bf16 top-k: [K+B] kept tokens listed per target row, or null
+    const uint32_t* ktok;    // [K+B][kKeptCap] kept tokens, ascending
+    const uint16_t* kkey;    // [K+B][kKeptCap] their keys
     int* out_tokens;
     int* num_acc;
     int* num_emit;
@@ -965,6 +1013,89 @@ SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
     if (threadIdx.x == 0) a.rec[b] = D;
 }
 
+// Draw from the target row's kept-token list (bf16 top-k rows). Tokens outside the list
+// have p = 0 and so weight 0 in both the residual and the bonus draw, so scanning the list
+// in ascending token order finds the same smallest x with C(x) > u * W as scanning the
+// vocabulary; the weights are the streaming draw's, token by token. One workgroup of NT
+// threads, kKeptCap / NT consecutive list entries per thread.
+template <bool BF16, int NT>
+SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
+    constexpr int EPT = kKeptCap / NT;
+    static_assert(EPT * NT == kKeptCap, "whole list entries per thread");
+    __shared__ double redd[NT / kWave];
+    __shared__ int redi[NT / kWave];
+    __shared__ double s_wpick;
+    const int tid = threadIdx.x;
+    const uint32_t* tok = a.ktok + (size_t)r.row_t * kKeptCap;
+    const uint16_t* key = a.kkey + (size_t)r.row_t * kKeptCap;
+    const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * (BF16 ? 2 : 4);
+    bool resid = r.mode == MODE_RESID;
+    int x[EPT];
+    float zt[EPT], zd[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = tid * EPT + e;
+        x[e] = -1;
+        zt[e] = zd[e] = -INFINITY;
+        if (i < n) {
+            x[e] = (int)tok[i];
+            zt[e] = key_to_float<BF16>(key[i]);
+            if (resid) zd[e] = load_elem(drow, x[e], BF16);
+        }
+    }
+    double w[EPT];
+    double run = 0.0, W;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, a.c, resid) : 0.0;
+        run += w[e];
+    }
+    double C = block_excl_scan_d<NT>(run, redd, &W);
+    if (resid && !(W > 0.0)) {
+        // residual mass 0 after a rejection: draw the replacement from p_j instead
+        resid = false;
+        r.flags |= SPECDEC_ERR_ZFALLBACK;
+        run = 0.0;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, a.c, false) : 0.0;
+            run += w[e];
+        }
+        C = block_excl_scan_d<NT>(run, redd, &W);
+        if (tid == 0) atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
+    }
+    const double t = (double)r.u * W;
+    int mine = 0x7fffffff, lastpos = -1;
+    double wmine = 0.0, wlast = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        if (x[e] < 0) continue;
+        C += w[e];
+        if (mine == 0x7fffffff && C > t) {
+            mine = x[e];
+            wmine = w[e];
+        }
+        if (w[e] > 0.0) {
+            lastpos = x[e];
+            wlast = w[e];
+        }
+    }
+    int found = block_min_i<NT>(mine, redi);
+    if (found != 0x7fffffff) {
+        if (mine == found) s_wpick = wmine;
+    } else {
+        found = block_max_i<NT>(lastpos, redi);
+        if (found >= 0 && lastpos == found) s_wpick = wlast;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        a.out_tokens[a.cu[b] + b + r.a] = found;
+        if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W;
+        if (a.dbg.picked_prob) a.dbg.picked_prob[b] = s_wpick / W;
+        if (a.dbg.req_flags) a.dbg.req_flags[b] = r.flags;
+    }
+}
+
 // Sampling, part 1: workgroup (b, chunk) writes the chunk sum of the weights of the row
 // (pair) b still has to sample. Rows after the first rejection are never read.
 template <bool BF16, bool VEC, int NT>
@@ -973,6 +1104,15 @@ SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
     __shared__ double redd[NT / kWave];
     const Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
+    if constexpr (BF16) {
+        if (a.kn) {
+            const int n = a.kn[r.row_t];
+            if (n >= 0) {             // the whole draw from the kept-token list
+                if (chunk == 0) listed_pick_body<BF16, NT>(a, b, r, n);
+                return;
+            }
+        }
+    }
     const bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
@@ -997,6 +1137,9 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     const int tid = threadIdx.x;
     Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
+    if constexpr (BF16) {
+        if (a.kn && a.kn[r.row_t] >= 0) return;   // drawn from the kept-token list
+    }
     bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
@@ -1102,8 +1245,8 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, rec, wsum, tk_cnt, tk_cand, total;
-    int nparts, nchunks, nch, tk_wcap;
+    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, total;
+    int nparts, nchunks, nch, tk_wcap, tk_listed;
 };
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
@@ -1132,6 +1275,16 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
         off = align256(off + lists * sizeof(int));
         p.tk_cand = off;
         off = align256(off + lists * (size_t)topk_cstride(p.tk_wcap) * sizeof(uint32_t));
+        if (dtype == SPECDEC_BF16) {       // kept-token lists of the target rows
+            const size_t rows_t = (size_t)K + B;
+            p.tk_listed = 1;
+            p.tk_kn = off;
+            off = align256(off + rows_t * sizeof(int));
+            p.tk_ktok = off;
+            off = align256(off + rows_t * kKeptCap * sizeof(uint32_t));
+            p.tk_kkey = off;
+            off = align256(off + rows_t * kKeptCap * sizeof(uint16_t));
+        }
     }
     p.total = off;
     return p;
@@ -1152,6 +1305,9 @@ static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int row
     a.c = c;
     a.cnt = reinterpret_cast<int*>(ws + p.tk_cnt);
     a.cand = reinterpret_cast<uint32_t*>(ws + p.tk_cand);
+    a.kn = p.tk_listed ? reinterpret_cast<int*>(ws + p.tk_kn) : nullptr;
+    a.ktok = p.tk_listed ? reinterpret_cast<uint32_t*>(ws + p.tk_ktok) : nullptr;
+    a.kkey = p.tk_listed ? reinterpret_cast<uint16_t*>(ws + p.tk_kkey) : nullptr;
     a.part = reinterpret_cast<RowPartial*>(ws + p.part);
     a.row_thr = reinterpret_cast<float*>(ws + p.thr);
     return a;
