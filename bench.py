@@ -32,8 +32,9 @@ PEAK_GBPS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=30,
+                   help="untimed cycles first: the GPU clock settles over the first ~10 ms")
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--schedule", choices=["fused", "serial", "overlap"], default="fused",

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kDecideNT) void k_cycle_decide(SampleArgs sa, KvArg
 }
 
 // Up to kCycRbMaxB requests the rollback runs as workgroup 0 of the chunk-sum launch (its
-// LDS then stays small), otherwise as workgroup 0 of the pick launch.
+// LDS then stays small), otherwise as a launch of its own after the draws.
 constexpr int kCycRbMaxB = 512;
 constexpr int kCycRbEv = 512;
 
@@ -104,12 +104,12 @@ __global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa, KvArgs kv
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa, KvArgs kv, int rb) {
-    if (!rb && blockIdx.x == 0) {
-        rollback_body(kv, sa.num_acc, sa.cu, sa.B);
-        return;
-    }
-    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x - !rb);
+__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa) {
+    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x);
+}
+
+__global__ __launch_bounds__(kKvNT) void k_cycle_rollback(SampleArgs sa, KvArgs kv) {
+    rollback_body(kv, sa.num_acc, sa.cu, sa.B);
 }
 
 template <bool BF16, bool VEC>
@@ -142,7 +142,8 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     const int rb = B <= kCycRbMaxB;
     hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
                        st, sa, kv, rb);
-    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B + !rb), dim3(kPickNT), 0, st, sa, kv, rb);
+    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
+    if (!rb) hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, sa, kv);
 }
 
 }  // namespace sd

@@ -20,12 +20,13 @@
 //                 p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p left to right,
 //                 finds the first rejection, publishes the accepted tokens and stores the
 //                 parameters of the one row pair (or bonus row) still to be sampled.
-//   k_part        one workgroup per (request, 8192-token chunk): sum of the sampling
-//                 weights over its chunk of that row (pair). Rows after the first
-//                 rejection are never read again (ragged early exit).
-//   k_pick        one workgroup per request: W from the chunk sums, t = u * W, the chunk
-//                 holding t scanned in ascending token order (LDS prefix scan) for the
-//                 smallest x with C(x) > t.
+//   k_part        one workgroup per (request, 8192-token chunk): sums of the sampling
+//                 weights over the four 2048-token sub-chunks of that row (pair). Rows
+//                 after the first rejection are never read again (ragged early exit).
+//                 A bf16 top-k request draws here, from its row's kept-token list.
+//   k_pick        one workgroup per request: W from the sub-chunk sums, t = u * W, the
+//                 sub-chunk holding t scanned in ascending token order (LDS prefix scan)
+//                 for the smallest x with C(x) > t.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>

@@ -710,8 +710,10 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
 // ---------------------------------------------------------------------------------------
 constexpr int kDecideNT = 256;             // threads of a decision workgroup (>= 2*64+1 rows)
 constexpr int kPartNT = 256;               // threads of a chunk-sum workgroup
-constexpr int kPickNT = 1024;              // threads of a pick workgroup
+constexpr int kPickNT = 256;               // threads of a pick workgroup
 constexpr int kSChunk = 8192;              // tokens per sampling chunk
+constexpr int kSSub = 4;                   // weight sums per chunk, one per sub-chunk
+constexpr int kSSubLen = kSChunk / kSSub;  // tokens per sub-chunk
 constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
 
 struct Decision {
@@ -737,7 +739,7 @@ struct SampleArgs {
     const RowPartial* part;
     const float* row_thr;
     Decision* rec;           // [B] each request's decision, for the draw
-    double* wsum;            // [B][nch] chunk sums of the sampling weights
+    double* wsum;            // [B][nch][kSSub] sub-chunk sums of the sampling weights
     const int* kn;           // bf16 top-k: [K+B] kept tokens listed per target row, or null
     const uint32_t* ktok;    // [K+B][kKeptCap] kept tokens, ascending
     const uint16_t* kkey;    // [K+B][kKeptCap] their keys
@@ -960,48 +962,63 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
     __syncthreads();
 }
 
-// Sum of the sampling weights over one chunk (kSChunk tokens) of the row (pair) still to
-// be sampled, by a workgroup of NT threads; every group of 8 tokens of the thread is in
-// flight at once. Fixed reduction order.
+// Sums of the sampling weights over the kSSub sub-chunks (kSSubLen consecutive tokens
+// each) of one chunk of the row (pair) still to be sampled, by a workgroup of NT threads:
+// group g of every thread lies in sub-chunk g, and all of them are in flight at once.
+// Fixed reduction order (lanes, then waves in index order). Thread s < kSSub writes
+// out[s]; `red` holds kSSub * NT / 64 doubles.
 template <bool BF16, bool VEC, int NT, bool RESID, bool TOPK>
-SD_DEV double chunk_weight_sum_t(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
-                                 const Decision& r, float c, double* redd) {
-    constexpr int PT = kSChunk / (NT * 8);     // groups of 8 tokens per thread
+SD_DEV void chunk_weight_sums_t(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
+                                const Decision& r, float c, double* red, double* out) {
+    constexpr int NW = NT / kWave;
+    static_assert(NT * 8 * kSSub == kSChunk, "group g of every thread is sub-chunk g");
     const int tid = threadIdx.x;
-    float zt[PT][8], zd[PT][8];
+    float zt[kSSub][8], zd[kSSub][8];
     if ((chunk + 1) * kSChunk <= V) {          // whole chunk inside the row
 #pragma unroll
-        for (int g = 0; g < PT; ++g) {
+        for (int g = 0; g < kSSub; ++g) {
             const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
             load8<BF16, VEC, true>(trow, V, i0, zt[g]);
             if (RESID) load8<BF16, VEC, true>(drow, V, i0, zd[g]);
         }
     } else {
 #pragma unroll
-        for (int g = 0; g < PT; ++g) {
+        for (int g = 0; g < kSSub; ++g) {
             const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
             load8<BF16, VEC>(trow, V, i0, zt[g]);
             if (RESID) load8<BF16, VEC>(drow, V, i0, zd[g]);
         }
     }
-    double acc = 0.0;
+    const int w = tid / kWave, l = tid % kWave;
 #pragma unroll
-    for (int g = 0; g < PT; ++g) {
+    for (int g = 0; g < kSSub; ++g) {
+        double acc = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += weight_t<RESID, TOPK>(zt[g][e], zd[g][e], r, c);
+        acc = wave_sum(acc);
+        if (l == 0) red[g * NW + w] = acc;
     }
-    return block_sum<NT>(acc, redd);
+    __syncthreads();
+    if (tid < kSSub) {
+        double sum = 0.0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) sum += red[tid * NW + i];
+        out[tid] = sum;
+    }
+    __syncthreads();
 }
 
 template <bool BF16, bool VEC, int NT>
-SD_DEV double chunk_weight_sum(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
-                               const Decision& r, float c, bool resid, bool topk, double* redd) {
+SD_DEV void chunk_weight_sums(const uint8_t* trow, const uint8_t* drow, int V, int chunk,
+                              const Decision& r, float c, bool resid, bool topk, double* red,
+                              double* out) {
     if (resid) {
-        if (topk) return chunk_weight_sum_t<BF16, VEC, NT, true, true>(trow, drow, V, chunk, r, c, redd);
-        return chunk_weight_sum_t<BF16, VEC, NT, true, false>(trow, drow, V, chunk, r, c, redd);
+        if (topk) chunk_weight_sums_t<BF16, VEC, NT, true, true>(trow, drow, V, chunk, r, c, red, out);
+        else chunk_weight_sums_t<BF16, VEC, NT, true, false>(trow, drow, V, chunk, r, c, red, out);
+    } else {
+        if (topk) chunk_weight_sums_t<BF16, VEC, NT, false, true>(trow, drow, V, chunk, r, c, red, out);
+        else chunk_weight_sums_t<BF16, VEC, NT, false, false>(trow, drow, V, chunk, r, c, red, out);
     }
-    if (topk) return chunk_weight_sum_t<BF16, VEC, NT, false, true>(trow, drow, V, chunk, r, c, redd);
-    return chunk_weight_sum_t<BF16, VEC, NT, false, false>(trow, drow, V, chunk, r, c, redd);
 }
 
 // Decision kernel body: one workgroup per request publishes its decision and stores it
@@ -1096,12 +1113,12 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
     }
 }
 
-// Sampling, part 1: workgroup (b, chunk) writes the chunk sum of the weights of the row
-// (pair) b still has to sample. Rows after the first rejection are never read.
+// Sampling, part 1: workgroup (b, chunk) writes the sub-chunk sums of the weights of the
+// row (pair) b still has to sample. Rows after the first rejection are never read.
 template <bool BF16, bool VEC, int NT>
 SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
     using Lt = Layout<BF16, VEC>;
-    __shared__ double redd[NT / kWave];
+    __shared__ double red[kSSub * (NT / kWave)];
     const Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
     if constexpr (BF16) {
@@ -1116,24 +1133,24 @@ SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
     const bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
-    const double s = chunk_weight_sum<BF16, VEC, NT>(trow, drow, a.V, chunk, r, a.c, resid,
-                                                     a.topk != 0, redd);
-    if (threadIdx.x == 0) a.wsum[(size_t)b * a.nch + chunk] = s;
+    chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, chunk, r, a.c, resid, a.topk != 0, red,
+                                     a.wsum + ((size_t)b * a.nch + chunk) * kSSub);
 }
 
-// Sampling, part 2: workgroup b turns the chunk sums into W, finds the chunk holding
-// t = u * W and scans it in ascending token order (each thread owns kSChunk / NT
-// consecutive tokens) for the smallest x with C(x) > t.
+// Sampling, part 2: workgroup b turns the sub-chunk sums into W, finds the sub-chunk holding
+// t = u * W and scans it in ascending token order (each thread owns 8 consecutive tokens,
+// an exclusive scan over threads gives each its running sum) for the smallest x with
+// C(x) > t.
 template <bool BF16, bool VEC, int NT>
 SD_DEV void pick_body(const SampleArgs& a, int b) {
     using Lt = Layout<BF16, VEC>;
     constexpr int NW = NT / kWave;
-    constexpr int RUN = kSChunk / NT;
-    __shared__ double redd[NW];
+    static_assert(NT * 8 == kSSubLen, "8 tokens per thread cover a sub-chunk");
+    __shared__ double red[kSSub * NW];
     __shared__ int redi[NW];
-    __shared__ double s_cs[kSMaxChunks];
+    __shared__ double s_cs[kSMaxChunks * kSSub];
     __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_chunk;
+    __shared__ int s_sub;
     const int tid = threadIdx.x;
     Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
@@ -1143,12 +1160,12 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
-    const int nch = a.nch;
-    for (int q = tid; q < nch; q += NT) s_cs[q] = a.wsum[(size_t)b * nch + q];
+    const int nch = a.nch, nsub = nch * kSSub;
+    for (int q = tid; q < nsub; q += NT) s_cs[q] = a.wsum[(size_t)b * nsub + q];
     __syncthreads();
     if (tid == 0) {
         double W = 0.0;
-        for (int q = 0; q < nch; ++q) W += s_cs[q];
+        for (int q = 0; q < nsub; ++q) W += s_cs[q];
         s_W = W;
     }
     __syncthreads();
@@ -1156,15 +1173,12 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
-        for (int q = 0; q < nch; ++q) {
-            const double x = chunk_weight_sum<BF16, VEC, NT>(trow, drow, a.V, q, r, a.c, false,
-                                                             a.topk != 0, redd);
-            if (tid == 0) s_cs[q] = x;
-        }
-        __syncthreads();
+        for (int q = 0; q < nch; ++q)
+            chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, q, r, a.c, false, a.topk != 0, red,
+                                             s_cs + q * kSSub);
         if (tid == 0) {
             double W = 0.0;
-            for (int q = 0; q < nch; ++q) W += s_cs[q];
+            for (int q = 0; q < nsub; ++q) W += s_cs[q];
             s_W = W;
             atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
         }
@@ -1175,52 +1189,45 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     if (tid == 0) {
         double C = 0.0;
         int q = 0;
-        for (; q < nch; ++q) {
+        for (; q < nsub; ++q) {
             if (C + s_cs[q] > t) break;
             C += s_cs[q];
         }
-        if (q == nch) {   // unreachable while t < W; keep the last non-empty chunk
-            q = nch - 1;
+        if (q == nsub) {   // unreachable while t < W; keep the last non-empty sub-chunk
+            q = nsub - 1;
             while (q > 0 && !(s_cs[q] > 0.0)) --q;
             C = 0.0;
             for (int i = 0; i < q; ++i) C += s_cs[i];
         }
-        s_chunk = q;
+        s_sub = q;
         s_base = C;
     }
     __syncthreads();
-    // thread tid scans tokens [c0 + tid * RUN, c0 + (tid + 1) * RUN) of the chunk: a first
-    // pass for its total, an exclusive scan over threads, a second pass for the crossing
-    const int e0 = s_chunk * kSChunk + tid * RUN;
+    const int i0 = s_sub * kSSubLen + tid * 8;
+    float t8[8], d8[8];
+    load8<BF16, VEC>(trow, a.V, i0, t8);
+    if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
+    double w[8];
     double run = 0.0;
-    for (int i0 = e0; i0 < e0 + RUN; i0 += 8) {
-        float t8[8], d8[8];
-        load8<BF16, VEC>(trow, a.V, i0, t8);
-        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) run += weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+    for (int e = 0; e < 8; ++e) {
+        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+        run += w[e];
     }
-    // (one chunk per request: the generic weight with its run-time branches is enough here)
     double tot;
-    double C = s_base + block_excl_scan_d<NT>(run, redd, &tot);
+    double C = s_base + block_excl_scan_d<NT>(run, red, &tot);
     int mine = 0x7fffffff, lastpos = -1;
     double wmine = 0.0, wlast = 0.0;
-    for (int i0 = e0; i0 < e0 + RUN; i0 += 8) {
-        float t8[8], d8[8];
-        load8<BF16, VEC>(trow, a.V, i0, t8);
-        if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const double w = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
-            C += w;
-            if (mine == 0x7fffffff && C > t) {
-                mine = i0 + e;
-                wmine = w;
-            }
-            if (w > 0.0) {
-                lastpos = i0 + e;
-                wlast = w;
-            }
+    for (int e = 0; e < 8; ++e) {
+        C += w[e];
+        if (mine == 0x7fffffff && C > t) {
+            mine = i0 + e;
+            wmine = w[e];
+        }
+        if (w[e] > 0.0) {
+            lastpos = i0 + e;
+            wlast = w[e];
         }
     }
     int found = block_min_i<NT>(mine, redi);
@@ -1267,7 +1274,7 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     p.rec = off;
     off = align256(off + (size_t)B * sizeof(Decision));
     p.wsum = off;
-    off = align256(off + (size_t)B * p.nch * sizeof(double));
+    off = align256(off + (size_t)B * p.nch * kSSub * sizeof(double));
     p.tk_cnt = p.tk_cand = off;
     if (topk_active(top_k, V) && !topk_generic(top_k)) {
         p.tk_wcap = topk_wcap(top_k);
