@@ -973,30 +973,64 @@ SD_DEV void chunk_weight_sums_t(const uint8_t* trow, const uint8_t* drow, int V,
     constexpr int NW = NT / kWave;
     static_assert(NT * 8 * kSSub == kSChunk, "group g of every thread is sub-chunk g");
     const int tid = threadIdx.x;
-    float zt[kSSub][8], zd[kSSub][8];
-    if ((chunk + 1) * kSChunk <= V) {          // whole chunk inside the row
+    const int w = tid / kWave, l = tid % kWave;
+    if constexpr (BF16 && VEC) {
+        // packed bf16 stays packed until used: fewer registers, more workgroups per CU
+        const u32x4* tv = reinterpret_cast<const u32x4*>(trow);
+        const u32x4* dv = reinterpret_cast<const u32x4*>(drow);
+        const u32x4 ninf = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
+        u32x4 rt[kSSub], rd[kSSub];
+        const bool full = (chunk + 1) * kSChunk <= V;
 #pragma unroll
         for (int g = 0; g < kSSub; ++g) {
             const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
-            load8<BF16, VEC, true>(trow, V, i0, zt[g]);
-            if (RESID) load8<BF16, VEC, true>(drow, V, i0, zd[g]);
+            rt[g] = full || i0 < V ? __builtin_nontemporal_load(tv + i0 / 8) : ninf;
+            if (RESID) rd[g] = full || i0 < V ? __builtin_nontemporal_load(dv + i0 / 8) : ninf;
+        }
+#pragma unroll
+        for (int g = 0; g < kSSub; ++g) {
+            const uint32_t qt[4] = {rt[g].x, rt[g].y, rt[g].z, rt[g].w};
+            uint32_t qd[4] = {0u, 0u, 0u, 0u};
+            if (RESID) {
+                qd[0] = rd[g].x;
+                qd[1] = rd[g].y;
+                qd[2] = rd[g].z;
+                qd[3] = rd[g].w;
+            }
+            double acc = 0.0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc += weight_t<RESID, TOPK>(bf16_lo(qt[j]), bf16_lo(qd[j]), r, c);
+                acc += weight_t<RESID, TOPK>(bf16_hi(qt[j]), bf16_hi(qd[j]), r, c);
+            }
+            acc = wave_sum(acc);
+            if (l == 0) red[g * NW + w] = acc;
         }
     } else {
+        float zt[kSSub][8], zd[kSSub][8];
+        if ((chunk + 1) * kSChunk <= V) {          // whole chunk inside the row
+#pragma unroll
+            for (int g = 0; g < kSSub; ++g) {
+                const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
+                load8<BF16, VEC, true>(trow, V, i0, zt[g]);
+                if (RESID) load8<BF16, VEC, true>(drow, V, i0, zd[g]);
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < kSSub; ++g) {
+                const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
+                load8<BF16, VEC>(trow, V, i0, zt[g]);
+                if (RESID) load8<BF16, VEC>(drow, V, i0, zd[g]);
+            }
+        }
 #pragma unroll
         for (int g = 0; g < kSSub; ++g) {
-            const int i0 = chunk * kSChunk + (g * NT + tid) * 8;
-            load8<BF16, VEC>(trow, V, i0, zt[g]);
-            if (RESID) load8<BF16, VEC>(drow, V, i0, zd[g]);
+            double acc = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += weight_t<RESID, TOPK>(zt[g][e], zd[g][e], r, c);
+            acc = wave_sum(acc);
+            if (l == 0) red[g * NW + w] = acc;
         }
-    }
-    const int w = tid / kWave, l = tid % kWave;
-#pragma unroll
-    for (int g = 0; g < kSSub; ++g) {
-        double acc = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += weight_t<RESID, TOPK>(zt[g][e], zd[g][e], r, c);
-        acc = wave_sum(acc);
-        if (l == 0) red[g * NW + w] = acc;
     }
     __syncthreads();
     if (tid < kSSub) {
