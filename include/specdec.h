@@ -72,6 +72,7 @@ extern "C" {
 /* Largest proposal count per request, batch size for the KV calls, and vocabulary. */
 #define SPECDEC_MAX_K      64
 #define SPECDEC_MAX_KV_BATCH 4096
+#define SPECDEC_MAX_V      2097152
 
 /* Short English text for a return code. Never NULL. */
 const char* specdec_status_string(int status);
@@ -102,7 +103,8 @@ typedef struct specdec_debug {
                                    latency-bound sampling kernel runs                     */
 } specdec_debug;
 
-/* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned). */
+/* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned); 0
+ * for sizes the call rejects (B < 1, K < 0, V outside [1, SPECDEC_MAX_V], bad dtype). */
 size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
                                      int32_t top_k);
 
@@ -136,7 +138,7 @@ size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dt
  *   num_accepted [B] int32 (-1 on a request error), num_emitted [B] int32 (0 on error)
  *   err_word     [1] int32, SPECDEC_ERR_* bits OR-ed in (not cleared)
  * Host scalars: B >= 1, K = cu_draft[B] (the packed row count the caller allocated),
- * 0 <= max_k <= SPECDEC_MAX_K, V >= 1, dtype SPECDEC_F32 or SPECDEC_BF16,
+ * 0 <= max_k <= SPECDEC_MAX_K, 1 <= V <= SPECDEC_MAX_V, dtype SPECDEC_F32 or SPECDEC_BF16,
  * temperature > 0 and finite, top_k any value (<= 0 or >= V disables it).
  * workspace: device, 16-byte aligned, >= specdec_verify_workspace_size(B, K, V, dtype,
  * top_k) bytes, owned by the caller; its contents need no initialization and are

@@ -38,6 +38,7 @@ KV_APPEND_REJECTED = 1 << 16
 
 MAX_K = 64
 MAX_KV_BATCH = 4096
+MAX_V = 2097152
 
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",

@@ -150,7 +150,8 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
 
 extern "C" size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
                                                int32_t top_k) {
-    if (B < 1 || K < 0 || V < 1 || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16)) return 0;
+    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16))
+        return 0;
     return sd::align256(sd::plan_ws(B, K, V, dtype, top_k).total) + sd::append_ws_bytes(B, K + B);
 }
 
@@ -177,7 +178,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
         ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
         return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k);
-    if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > kSChunk * kSMaxChunks)
+    if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     const size_t vbytes = align256(p.total);
     if (!workspace || workspace_bytes < vbytes + append_ws_bytes(B, K + B) ||

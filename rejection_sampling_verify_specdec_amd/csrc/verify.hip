@@ -104,7 +104,8 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
 
 extern "C" size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
                                                 int32_t top_k) {
-    if (B < 1 || K < 0 || V < 1 || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16)) return 0;
+    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16))
+        return 0;
     return sd::plan_ws(B, K, V, dtype, top_k).total;
 }
 
@@ -126,7 +127,7 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
-        V > kSChunk * kSMaxChunks)
+        V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;

@@ -715,6 +715,7 @@ constexpr int kSChunk = 8192;              // tokens per sampling chunk
 constexpr int kSSub = 4;                   // weight sums per chunk, one per sub-chunk
 constexpr int kSSubLen = kSChunk / kSSub;  // tokens per sub-chunk
 constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
+static_assert(kSChunk * kSMaxChunks == SPECDEC_MAX_V, "sampling chunks cover the largest V");
 
 struct Decision {
     int flags, err, a, k, mode, row_t, row_d, pad;

@@ -52,6 +52,10 @@ def test_workspace_sizes(lib):
     assert binding.specdec_verify_workspace_size(0, 0, 10, 0, 0) == 0
     assert binding.kv_paged_append_workspace_size(512, 3000) >= 16 + 512 * 16 + 3000 * 8
     assert binding.kv_paged_append_workspace_size(0, 10) == 0
+    # the largest vocabulary is accepted, one more token is not
+    assert binding.specdec_verify_workspace_size(1, 1, binding.MAX_V, binding.SPECDEC_BF16, 64) > 0
+    assert binding.specdec_verify_workspace_size(1, 1, binding.MAX_V + 1, binding.SPECDEC_BF16, 0) == 0
+    assert binding.specdec_cycle_workspace_size(1, 1, binding.MAX_V + 1, binding.SPECDEC_F32, 0) == 0
 
 
 def test_host_validation_returns_einval_without_gpu(lib):

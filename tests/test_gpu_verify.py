@@ -171,3 +171,30 @@ def test_host_validation_einval():
                                temperature=1.0, top_k=0, out_tokens=v.out_tokens,
                                num_accepted=v.num_acc, num_emitted=v.num_emit, err_word=v.err,
                                workspace=small)
+
+
+@pytest.mark.parametrize("dtype,top_k", [("bf16", 0), ("bf16", 64), ("f32", 0), ("f32", 50)])
+def test_largest_vocabulary(dtype, top_k):
+    # V = 2,097,152: 256 sampling chunks; 128 (bf16) or 256 (fp32) statistics chunks
+    vin = synth.make_verify("c2", seed=27, B=2, V=binding.MAX_V, k=2, dtype=dtype,
+                            top_k=top_k)
+    _check(vin)
+
+
+@pytest.mark.parametrize("top_k", ["V-1", "V"])
+def test_top_k_at_the_vocabulary_size(top_k):
+    V = 3000
+    vin = synth.make_verify("c4", seed=28, B=4, V=V, top_k=V - 1 if top_k == "V-1" else V)
+    _check(vin)
+
+
+def test_vocabulary_past_the_limit_is_einval():
+    vin = synth.make_verify("tiny", seed=29, B=1, V=16)
+    v = VerifyOnDevice(vin)
+    lib = binding.load_library()
+    st = lib.specdec_verify(v.tgt.data_ptr(), v.dft.data_ptr(), 1, v.tokens.data_ptr(),
+                            v.cu.data_ptr(), v.u_acc.data_ptr(), v.u_smp.data_ptr(), 1, vin.K,
+                            vin.max_k, binding.MAX_V + 1, 1.0, 0, v.out_tokens.data_ptr(),
+                            v.num_acc.data_ptr(), v.num_emit.data_ptr(), v.err.data_ptr(), None,
+                            v.ws.data_ptr(), v.ws.numel(), None)
+    assert st == binding.SPECDEC_EINVAL
