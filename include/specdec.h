@@ -16,6 +16,8 @@
  *                      blocks past it ("Walk through KV-cache updates ...", paragraph 1;
  *                      "Keep cache validity aligned with the committed token history",
  *                      paragraphs 1-4).
+ *   kv_rollback_draft - the same for the draft model's cache under its own processed-
+ *                      state convention ("Keep cache validity ...", paragraph 5).
  *
  * Conventions for every entry point:
  *   - Pointers named device are device memory owned by the caller; the library never
@@ -227,6 +229,20 @@ int kv_paged_append(const kv_paged_cache* cache, int32_t B,
  */
 int kv_rollback(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
                 const int32_t* cu_draft, hipStream_t stream);
+
+/*
+ * kv_rollback_draft - realign the draft model's cache with the committed history after
+ * verification ("Keep cache validity aligned with the committed token history",
+ * paragraph 5: the draft advanced along its own proposals and is realigned under its own
+ * processed-state convention). To propose k_b tokens the draft processed its pending
+ * token(s) and y_1 .. y_{k_b-1}, never y_{k_b}, which it only sampled; so it keeps the
+ * states of y_1 .. y_{min(a_b, k_b-1)} and drops max(0, k_b - 1 - num_accepted[b]) trailing
+ * entries (none when k_b = 0). Its pending tokens are then the replacement, or y_{k_b} and
+ * the bonus token after a fully accepted round. Block release, error handling and the
+ * no-op after a rejected append are those of kv_rollback; arguments likewise.
+ */
+int kv_rollback_draft(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                      const int32_t* cu_draft, hipStream_t stream);
 
 /* =====================================================================================
  * One whole cycle

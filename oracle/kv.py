@@ -34,7 +34,14 @@ Readings taken (the pages give the principle only):
 * rollback only edits metadata (lengths, tables, refcounts, free list); stale slots keep
   their bytes;
 * a shared partial block (refcount > 1) that receives new entries is first copied into a
-  freshly popped block (slots below the valid length), and the old block is decref'ed.
+  freshly popped block (slots below the valid length), and the old block is decref'ed;
+* the draft's cache follows the draft's own processed-state convention ("Keep cache
+  validity ...", paragraph 5: the draft has advanced along its own proposals and must be
+  realigned with the corrected history): to propose k_b tokens the draft processed its
+  pending token(s) and y_1 .. y_{k_b-1} (never y_{k_b}, which it only sampled), so after
+  a_b acceptances it keeps the states of y_1 .. y_{min(a_b, k_b-1)} and drops
+  max(0, k_b - 1 - a_b) entries; its pending tokens are then the correction (a_b < k_b)
+  or y_{k_b} and the bonus (a_b = k_b).
 """
 
 from __future__ import annotations
@@ -163,11 +170,13 @@ class PagedKV:
         return 0
 
     # -- rollback to the committed prefix ----------------------------------------------
-    def rollback(self, num_accepted: Sequence[int], cu_draft: Sequence[int]) -> int:
-        """Drop k_b - a_b trailing entries per request; free blocks past the new end.
-
-        After a cycle that appended k_b + 1 entries, the new length is the old committed
-        prefix plus 1 + a_b (the pending token and the accepted proposals)."""
+    def rollback(self, num_accepted: Sequence[int], cu_draft: Sequence[int],
+                 draft: bool = False) -> int:
+        """Drop trailing entries per request and free blocks past the new end: k_b - a_b for
+        the target's cache (after a cycle that appended k_b + 1 entries the new length is
+        the old committed prefix plus 1 + a_b: the pending token and the accepted
+        proposals), max(0, k_b - 1 - a_b) for the draft's (the draft never processed
+        y_{k_b})."""
         if self.state & KV_APPEND_REJECTED:
             return 0
         cu = [int(c) for c in cu_draft]
@@ -179,7 +188,7 @@ class PagedKV:
                 err |= KV_ERR_ROLLBACK
                 continue
             s = self.seq_lens[b]
-            new = s - (k - a)
+            new = s - (max(0, k - 1 - a) if draft else k - a)
             if new < 0:
                 err |= KV_ERR_ROLLBACK
                 continue
@@ -255,10 +264,11 @@ class ContiguousKV:
             self.buf[b] = np.concatenate([self.buf[b][:, :, :self.len[b]], ent], axis=2)
             self.len[b] += hi - lo
 
-    def rollback(self, num_accepted: Sequence[int], cu_draft: Sequence[int]) -> None:
+    def rollback(self, num_accepted: Sequence[int], cu_draft: Sequence[int],
+                 draft: bool = False) -> None:
         for b in range(len(self.buf)):
-            k = int(cu_draft[b + 1]) - int(cu_draft[b])
-            self.len[b] -= k - int(num_accepted[b])
+            k, a = int(cu_draft[b + 1]) - int(cu_draft[b]), int(num_accepted[b])
+            self.len[b] -= max(0, k - 1 - a) if draft else k - a
 
     def view(self, b: int, start: int = 0) -> np.ndarray:
         return self.buf[b][:, :, start:self.len[b]]

@@ -42,7 +42,7 @@ MAX_V = 2097152
 
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
-    "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback",
+    "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
     "specdec_cycle_workspace_size", "specdec_cycle",
 ]
 
@@ -103,8 +103,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kv_paged_append.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32,
                                     vp, sz, vp]
     lib.kv_paged_append.restype = ctypes.c_int
-    lib.kv_rollback.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
-    lib.kv_rollback.restype = ctypes.c_int
+    for fn in (lib.kv_rollback, lib.kv_rollback_draft):
+        fn.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
+        fn.restype = ctypes.c_int
     lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.specdec_cycle_workspace_size.restype = sz
     lib.specdec_cycle.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp,
@@ -244,17 +245,20 @@ def kv_paged_append(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tenso
         raise SpecdecError("kv_paged_append", st)
 
 
-def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch.Tensor) -> None:
-    """Enqueue the rollback of every request to its committed prefix."""
+def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch.Tensor,
+                draft: bool = False) -> None:
+    """Enqueue the rollback of every request to its committed prefix (kv_rollback), or of
+    the draft model's cache under the draft's convention (kv_rollback_draft)."""
     lib = load_library()
     dev = cache.device
     B = cu_draft.numel() - 1
     _check(num_accepted, "num_accepted", torch.int32, B, dev)
     _check(cu_draft, "cu_draft", torch.int32, B + 1, dev)
-    st = lib.kv_rollback(ctypes.byref(cache.struct), B, _ptr(num_accepted), _ptr(cu_draft),
-                         _stream(dev))
+    fn = "kv_rollback_draft" if draft else "kv_rollback"
+    st = getattr(lib, fn)(ctypes.byref(cache.struct), B, _ptr(num_accepted), _ptr(cu_draft),
+                          _stream(dev))
     if st != SPECDEC_OK:
-        raise SpecdecError("kv_rollback", st)
+        raise SpecdecError(fn, st)
 
 
 def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int) -> int:

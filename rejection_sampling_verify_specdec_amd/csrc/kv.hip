@@ -44,8 +44,9 @@ __global__ __launch_bounds__(kScNT) void k_kv_scatter(KvArgs a, const uint8_t* _
 }
 
 __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __restrict__ num_acc,
-                                                       const int* __restrict__ cu, int B) {
-    rollback_body(a, num_acc, cu, B);
+                                                       const int* __restrict__ cu, int B,
+                                                       int draft) {
+    rollback_body(a, num_acc, cu, B, draft);
 }
 
 }  // namespace sd
@@ -79,13 +80,25 @@ extern "C" int kv_paged_append(const kv_paged_cache* cache, int32_t B, const voi
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }
 
-extern "C" int kv_rollback(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
-                           const int32_t* cu_draft, hipStream_t stream) {
+static int rollback_call(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                         const int32_t* cu_draft, hipStream_t stream, int draft) {
     using namespace sd;
     if (!geometry_ok(cache) || B < 1 || B > SPECDEC_MAX_KV_BATCH || !num_accepted || !cu_draft)
         return SPECDEC_EINVAL;
     const KvArgs a = args_of(cache);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_kv_rollback, dim3(1), dim3(kKvNT), 0, stream, a, num_accepted, cu_draft, B);
+    hipLaunchKernelGGL(k_kv_rollback, dim3(1), dim3(kKvNT), 0, stream, a, num_accepted, cu_draft,
+                       B, draft);
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}
+
+extern "C" int kv_rollback(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                           const int32_t* cu_draft, hipStream_t stream) {
+    return rollback_call(cache, B, num_accepted, cu_draft, stream, 0);
+}
+
+extern "C" int kv_rollback_draft(const kv_paged_cache* cache, int32_t B,
+                                 const int32_t* num_accepted, const int32_t* cu_draft,
+                                 hipStream_t stream) {
+    return rollback_call(cache, B, num_accepted, cu_draft, stream, 1);
 }

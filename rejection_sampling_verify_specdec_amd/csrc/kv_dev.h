@@ -292,9 +292,10 @@ SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
 
 // Rollback of every request by one workgroup of NT threads, for B <= MAXB requests;
 // events (freed logical blocks) are processed in windows of EVCAP.
+// draft = 1: the draft model's convention, drop max(0, k_b - 1 - a_b) instead of k_b - a_b.
 template <int NT = kKvNT, int MAXB = SPECDEC_MAX_KV_BATCH, int EVCAP = kEvCap>
 SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
-                          const int* __restrict__ cu, int B) {
+                          const int* __restrict__ cu, int B, int draft = 0) {
     constexpr int RPT = MAXB / NT;    // requests per thread
     constexpr int EPT = EVCAP / NT;   // window events per thread
     static_assert(RPT * NT == MAXB && EPT * NT == EVCAP, "whole rounds per thread");
@@ -319,12 +320,13 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
         int ev = 0;
         if (b < B) {
             const int k = cu[b + 1] - cu[b], acc = num_acc[b], s = a.seq_lens[b];
-            if (k < 0 || acc < 0 || acc > k || k - acc > s ||
+            const int drop = draft ? max(0, k - 1 - acc) : k - acc;
+            if (k < 0 || acc < 0 || acc > k || drop > s ||
                 (long long)s > (long long)a.MBR * a.bs) {
                 err = 1;
             } else {
                 valid[i] = 1;
-                newlen[i] = s - (k - acc);
+                newlen[i] = s - drop;
                 ev = ceil_div(s, a.bs) - ceil_div(newlen[i], a.bs);
             }
         }

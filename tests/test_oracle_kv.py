@@ -242,3 +242,71 @@ def test_repeated_cycles_do_not_leak_with_sharing():
         assert kv.rollback(a, cu) == 0
         kv.check_invariants()
     assert all(kv.refcount[X] == 4 for X in shared)
+
+
+# ---------------------------------------------------------------------------------------
+# Target and draft caches over many rounds ("Keep cache validity aligned with the committed
+# token history", paragraphs 1-2 and 5-6): after every round each cache must hold exactly
+# the states its model computes for the committed history (no contamination), as long a
+# prefix of it as that model has processed (no lost state), and no block may leak.
+# ---------------------------------------------------------------------------------------
+
+def _state(model, b, pos, tok):
+    """K/V a model computes at position pos of request b for token tok (stand-in values)."""
+    r = np.random.default_rng([model, b, pos, tok])
+    return r.integers(0, 0x7f00, size=(L, 2, H, D), dtype=np.uint16)
+
+
+def _entries(model, b, pos0, toks):
+    return np.stack([_state(model, b, pos0 + i, t) for i, t in enumerate(toks)], axis=2) \
+        if toks else np.zeros((L, 2, 0, H, D), np.uint16)
+
+
+def _append_all(cache, ents):
+    """Append per-request entry stacks [L][2][n][H][D] in one batched call."""
+    n = [e.shape[2] for e in ents]
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    k = np.concatenate([e[:, 0] for e in ents], axis=1) if cu[-1] else np.zeros((L, 0, H, D), np.uint16)
+    v = np.concatenate([e[:, 1] for e in ents], axis=1) if cu[-1] else np.zeros((L, 0, H, D), np.uint16)
+    assert cache.append(k, v, cu) == 0
+    return cu
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_target_and_draft_caches_track_the_committed_history(seed):
+    rng = np.random.default_rng(100 + seed)
+    B, NB, MBR, bs, V = 6, 4000, 400, 4, 50
+    tgt = _empty(B, NB, bs, MBR, order=rng.permutation(NB))
+    dft = _empty(B, NB, bs, MBR, order=rng.permutation(NB))
+    hist = [[int(rng.integers(V))] for _ in range(B)]     # the prompt's last token is pending
+    for rnd in range(40):
+        k = rng.integers(0, 6, size=B)
+        y = [list(rng.integers(V, size=int(k[b]))) for b in range(B)]
+        a = np.array([int(rng.integers(0, k[b] + 1)) for b in range(B)])
+        # drafting: the draft processes its pending tokens, then y_1 .. y_{k-1}
+        d0 = list(dft.seq_lens)
+        _append_all(dft, [_entries(1, b, d0[b], hist[b][d0[b]:] + y[b][:-1]) if k[b] else
+                          _entries(1, b, d0[b], []) for b in range(B)])
+        # verification pass: the target processes the pending token and y_1 .. y_k
+        t0 = list(tgt.seq_lens)
+        _append_all(tgt, [_entries(0, b, t0[b], [hist[b][-1]] + y[b]) for b in range(B)])
+        cu = np.concatenate([[0], np.cumsum(k)])
+        assert tgt.rollback(a, cu) == 0
+        assert dft.rollback(a, cu, draft=True) == 0
+        for b in range(B):
+            hist[b] += y[b][:a[b]] + [int(rng.integers(V))]     # accepted, then x*
+        for b in range(B):
+            n = len(hist[b])
+            assert tgt.seq_lens[b] == n - 1                      # one token pending
+            want = _entries(0, b, 0, hist[b][:n - 1])
+            assert np.array_equal(tgt.logical_view(b), want)
+            # the draft keeps every state it computed on the committed history
+            if k[b]:
+                keep = d0[b] + (t0[b] + 1 - d0[b]) + min(a[b], k[b] - 1)
+            else:
+                keep = d0[b]
+            assert dft.seq_lens[b] == keep, (rnd, b)
+            assert keep <= n - 1
+            assert np.array_equal(dft.logical_view(b), _entries(1, b, 0, hist[b][:keep]))
+        tgt.check_invariants()
+        dft.check_invariants()
