@@ -29,6 +29,12 @@ Readings taken where the pages leave a step open (each is listed in the design n
 * top-k keeps every token whose logit is >= the k-th largest logit of the row, counting
   multiplicity (ties inclusive), and selects on the raw logits, which is the same set for
   any temperature T > 0.
+* top-p (the pages name it among the transforms that must be applied identically to both
+  distributions, section 3 closing paragraph and section 4, without defining it) is the
+  nucleus rule, applied after temperature and top-k to the renormalized kept
+  distribution: keep every token whose probability is >= the largest value v for which
+  the tokens with probability >= v carry at least top_p of the mass (ties inclusive, like
+  top-k); top_p <= 0 or >= 1 leaves the row unchanged.
 * the bonus token is emitted only when all proposals are accepted (section 2, section 6
   "Bad bonus-token logic").
 """
@@ -70,13 +76,16 @@ class Transformed:
     p: Optional[np.ndarray]   # normalized probabilities, float64 [V]; None if invalid
     m: float                  # max kept logit
     S: float                  # sum over kept x of exp((z(x) - m) / T)
-    thr: float                # top-k threshold logit (-inf when top-k is off)
+    thr: float                # smallest kept logit under top-k / top-p (-inf when both are off)
     nkept: int                # number of kept tokens with finite logit
     valid: bool
+    # top-p: distance of the nucleus mass decision from top_p (the mass through the
+    # boundary value minus top_p, and top_p minus the mass above it), inf when off
+    nucleus_margin: float = math.inf
 
 
-def transform(z: np.ndarray, T: float, top_k: int) -> Transformed:
-    """Temperature + top-k transform of one logit row, stable softmax in fp64.
+def transform(z: np.ndarray, T: float, top_k: int, top_p: float = 1.0) -> Transformed:
+    """Temperature + top-k + top-p transform of one logit row, stable softmax in fp64.
 
     Section 6 of the speculative-decoding lesson asks for stable softmax and for the same
     transform on both distributions; section 4 ("When it wins") lists temperature and
@@ -99,7 +108,31 @@ def transform(z: np.ndarray, T: float, top_k: int) -> Transformed:
     with np.errstate(invalid="ignore", over="ignore"):
         e = np.where(kept, np.exp((z - m) / T), 0.0)
     S = float(e.sum())
-    return Transformed(e / S, m, S, thr, nkept, True)
+    margin = math.inf
+    if 0.0 < top_p < 1.0:
+        thr, margin = nucleus(z[kept], e[kept] / S, top_p)
+        kept = (z >= thr) & (z > -math.inf)
+        nkept = int(kept.sum())
+        e = np.where(kept, e, 0.0)
+        S = float(e.sum())
+    return Transformed(e / S, m, S, thr, nkept, True, margin)
+
+
+def nucleus(zk: np.ndarray, pk: np.ndarray, top_p: float):
+    """Smallest kept logit of the nucleus and the margin of its mass decision.
+
+    zk, pk: logits and normalized probabilities of the kept tokens. Equal logits have equal
+    probability, so the values are walked in descending order, one group of equal values
+    at a time, until the mass of the groups taken reaches top_p."""
+    vals = np.unique(zk)[::-1]                 # distinct kept logits, descending
+    before = 0.0
+    for v in vals:
+        through = before + float(pk[zk == v].sum())
+        if through >= top_p:
+            return float(v), min(through - top_p, top_p - before)
+        before = through
+    # rounding left the total short of top_p: keep every kept token
+    return float(vals[-1]), 0.0
 
 
 # --------------------------------------------------------------------------------------
@@ -236,7 +269,7 @@ def _u_ok(u) -> bool:
 
 
 def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: int,
-                   V: int, keep_probs: bool = True) -> RequestResult:
+                   V: int, keep_probs: bool = True, top_p: float = 1.0) -> RequestResult:
     """Validate and verify one request from logits (float64 rows). With keep_probs=False
     the normalized rows are dropped from the result once used (large vocabularies)."""
     k = len(tokens)
@@ -245,8 +278,8 @@ def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: 
         err |= ERR_TOKEN
     if not all(_u_ok(u) for u in u_accept) or not _u_ok(u_sample):
         err |= ERR_UNIFORM
-    rows_t = [transform(t_rows[i], T, top_k) for i in range(k + 1)]
-    rows_d = [transform(d_rows[i], T, top_k) for i in range(k)]
+    rows_t = [transform(t_rows[i], T, top_k, top_p) for i in range(k + 1)]
+    rows_d = [transform(d_rows[i], T, top_k, top_p) for i in range(k)]
     if not all(r.valid for r in rows_t) or not all(r.valid for r in rows_d):
         err |= ERR_NONFINITE
     if err & ERROR_BITS:
@@ -282,7 +315,7 @@ def _decode_rows(x: np.ndarray, dtype: str) -> np.ndarray:
 def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
                  T: float, top_k: int, max_k: int, dtype: str,
                  requests: Optional[Sequence[int]] = None,
-                 keep_probs: bool = True) -> BatchResult:
+                 keep_probs: bool = True, top_p: float = 1.0) -> BatchResult:
     """Batched verification over packed ragged rows.
 
     target: [K+B, V] (fp32 values, or bf16 bit patterns as uint16); the rows of request b
@@ -294,6 +327,7 @@ def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
     K = int(np.asarray(draft_tokens).shape[0])
     V = int(target.shape[1])
     T = float(np.float32(T))
+    top_p = float(np.float32(top_p))
     num_acc = np.full(B, -1, dtype=np.int32)
     num_emit = np.zeros(B, dtype=np.int32)
     out = np.full(K + B, -1, dtype=np.int32)
@@ -309,7 +343,8 @@ def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
         t_rows = _decode_rows(target[lo + b: lo + b + k + 1], dtype)
         d_rows = _decode_rows(draft[lo: hi], dtype)
         r = verify_request(t_rows, d_rows, np.asarray(draft_tokens[lo:hi]),
-                           np.asarray(u_accept[lo:hi]), u_sample[b], T, top_k, V, keep_probs)
+                           np.asarray(u_accept[lo:hi]), u_sample[b], T, top_k, V, keep_probs,
+                           top_p)
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

@@ -254,6 +254,70 @@ def test_transform_topk_is_temperature_invariant_selection():
     assert np.array_equal(s[0], s[1]) and np.array_equal(s[1], s[2])
 
 
+def _nucleus_brute(p, top_p):
+    """Kept set of the nucleus rule by brute force over candidate thresholds: the largest
+    probability value v whose upper set {x : p(x) >= v} carries at least top_p."""
+    best = None
+    for v in sorted(set(p[p > 0].tolist())):
+        if p[p >= v].sum() >= top_p:
+            best = v
+    return p >= best
+
+
+def test_transform_topp_brute_force_with_ties():
+    rng = np.random.default_rng(12)
+    for _ in range(300):
+        V = int(rng.integers(2, 14))
+        z = rng.integers(-3, 4, size=V).astype(np.float64) * 0.7   # planted ties
+        T = float(rng.choice([0.5, 1.0, 2.0]))
+        k = int(rng.integers(0, V + 1))
+        top_p = float(rng.choice([0.05, 0.3, 0.5, 0.77, 0.9, 0.999]))
+        t = transform(z, T, k, top_p)
+        # top-k by brute force, then the nucleus on the renormalized kept distribution
+        kept_k = np.array([k <= 0 or k >= V or np.sum(z > z[x]) < k for x in range(V)])
+        base = scipy.special.softmax(np.where(kept_k, z / T, -np.inf))
+        kept = _nucleus_brute(base, top_p)
+        assert np.array_equal(t.p > 0, kept), (z, T, k, top_p)
+        ref = scipy.special.softmax(np.where(kept, z / T, -np.inf))
+        assert np.allclose(t.p, ref, rtol=1e-12, atol=0)
+        assert t.nkept == kept.sum() and t.thr == z[kept].min()
+        # the kept mass reaches top_p; without the smallest kept value it would not
+        assert base[kept].sum() >= top_p - 1e-12
+        assert base[kept & (z > t.thr)].sum() < top_p + 1e-12
+
+
+def test_transform_topp_limits():
+    rng = np.random.default_rng(13)
+    z = rng.standard_normal(200) * 2
+    full = transform(z, 0.8, 0)
+    for top_p in (1.0, 1.5, 0.0, -1.0):        # off: the row is unchanged
+        t = transform(z, 0.8, 0, top_p)
+        assert np.array_equal(t.p, full.p) and t.nucleus_margin == math.inf
+    # a tiny top_p keeps the largest value only, with its ties
+    zt = np.array([1.0, 3.0, -2.0, 3.0, 0.5])
+    t = transform(zt, 1.3, 0, 1e-9)
+    assert t.p.tolist() == [0.0, 0.5, 0.0, 0.5, 0.0] and t.thr == 3.0
+    # two tokens: the first alone suffices iff its probability reaches top_p
+    p0 = 1.0 / (1.0 + math.exp(-1.0))
+    assert transform(np.array([1.0, 0.0]), 1.0, 0, p0 - 1e-9).nkept == 1
+    assert transform(np.array([1.0, 0.0]), 1.0, 0, p0 + 1e-9).nkept == 2
+
+
+def test_verify_batch_applies_topp_to_both_sides():
+    # with q = p after the same nucleus, every proposal is accepted (section 5, variation 1)
+    rng = np.random.default_rng(14)
+    V, k = 50, 4
+    z = rng.standard_normal((k + 1, V)) * 2
+    cu = np.array([0, k])
+    toks = np.array([int(np.argmax(z[i])) for i in range(k)])
+    res = oracle.verify_batch(z.astype(np.float32), z[:k].astype(np.float32), toks, cu,
+                              np.full(k, 0.999, np.float32), np.array([0.3], np.float32),
+                              1.0, 0, k, "f32", top_p=0.6)
+    assert res.num_accepted[0] == k
+    p = res.requests[0].rows_t[k].p
+    assert res.out_tokens[k] in np.flatnonzero(p > 0)
+
+
 def test_transform_rejects_nonfinite_and_handles_neg_inf():
     assert not transform(np.array([0.0, np.nan]), 1.0, 0).valid
     assert not transform(np.array([0.0, np.inf]), 1.0, 0).valid
