@@ -37,6 +37,10 @@ def parse():
                    help="untimed cycles first: the GPU clock settles over the first ~10 ms")
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--top-k", type=int, default=None,
+                   help="override the workload's top_k (0 = off)")
+    p.add_argument("--top-p", type=float, default=1.0,
+                   help="nucleus mass after temperature and top-k (<= 0 or >= 1 = off)")
     p.add_argument("--schedule", choices=["fused", "serial", "overlap"], default="fused",
                    help="fused: specdec_cycle (allocation inside the logit-streaming launch, "
                         "K/V scatter beside the sampling workgroups); serial: append, verify, "
@@ -66,7 +70,7 @@ def traffic_from_profile(kernel: str, workload: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(vin, kv, min_seconds: float):
+def cpu_baseline(vin, kv, min_seconds: float, top_p: float):
     """The oracle as it stands, one core: whole cycles of the same workload (verify of every
     request, then the paged append and rollback), repeated until min_seconds have passed."""
     try:
@@ -80,7 +84,7 @@ def cpu_baseline(vin, kv, min_seconds: float):
         t0 = time.perf_counter()
         res = oracle.verify_batch(vin.target, vin.draft, vin.draft_tokens, vin.cu_draft,
                                   vin.u_accept, vin.u_sample, vin.T, vin.top_k, vin.max_k,
-                                  vin.dtype, keep_probs=False)
+                                  vin.dtype, keep_probs=False, top_p=top_p)
         t1 = time.perf_counter()
         o = oracle.PagedKV(kv.L, kv.H, kv.D, kv.block_size, kv.num_blocks, kv.block_tables,
                            kv.seq_lens, kv.refcount, kv.free_list, kv.free_count, kv.blocks)
@@ -115,7 +119,9 @@ def main():
     d = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     t0 = time.time()
-    vin = synth.make_verify(wl, seed=args.seed)
+    vin = synth.make_verify(wl, seed=args.seed,
+                            **({} if args.top_k is None else {"top_k": args.top_k}))
+    top_p = args.top_p
     kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + args.steps + 2)
     print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
           f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
@@ -144,8 +150,10 @@ def main():
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-    ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
-    cws = torch.empty(binding.specdec_cycle_workspace_size(B, K, V, dt, vin.top_k), dtype=torch.uint8, device=d)
+    ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k, top_p),
+                     dtype=torch.uint8, device=d)
+    cws = torch.empty(binding.specdec_cycle_workspace_size(B, K, V, dt, vin.top_k, top_p),
+                      dtype=torch.uint8, device=d)
     kws = torch.empty(binding.kv_paged_append_workspace_size(B, K + B), dtype=torch.uint8, device=d)
     n = args.warmup + args.steps
     timed = [i for i in range(args.warmup, n) if (i - args.warmup) % max(args.timing_every, 1) == 0]
@@ -163,20 +171,20 @@ def main():
             binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
                                   max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
                                   out_tokens=out, num_accepted=nacc, num_emitted=nemit,
-                                  err_word=err, workspace=cws, debug=dbg)
+                                  err_word=err, workspace=cws, debug=dbg, top_p=top_p)
             return
         if args.schedule == "serial":
             binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
                                    temperature=vin.T, top_k=vin.top_k, out_tokens=out,
                                    num_accepted=nacc, num_emitted=nemit, err_word=err,
-                                   workspace=ws, debug=dbg)
+                                   workspace=ws, debug=dbg, top_p=top_p)
         else:
             dbg.ev_stats_done = ev_stats[i].handle
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
                                    temperature=vin.T, top_k=vin.top_k, out_tokens=out,
                                    num_accepted=nacc, num_emitted=nemit, err_word=err,
-                                   workspace=ws, debug=dbg)
+                                   workspace=ws, debug=dbg, top_p=top_p)
             ev_stats[i].wait_on(side_s)
             with torch.cuda.stream(side_s):
                 binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
@@ -216,7 +224,11 @@ def main():
     positions_per_s = K * args.steps / elapsed
     cycle_gbps = cycle_bytes / (ms_per_step / 1e3) / 1e9
     achieved = logit_bytes / stats_avg_s / 1e9
-    stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
+    filtered = 0 < vin.top_k < V or 0.0 < top_p < 1.0
+    if filtered:      # the first launch holds the rows as keys and gathers candidates
+        stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
+    else:
+        stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
     res = {
         "metric": METRIC,
         "value": positions_per_s,
@@ -231,7 +243,8 @@ def main():
         "dtype": vin.dtype,
         "data": "synthetic",
         "config": {"workload": (f"{wl.name}: B={B} k={'U{%d..%d}' % wl.k_range if wl.k_range else wl.k} "
-                                f"V={V} {vin.dtype} T={vin.T:g} top_k={vin.top_k}; paged KV "
+                                f"V={V} {vin.dtype} T={vin.T:g} top_k={vin.top_k}"
+                                + (f" top_p={top_p:g}" if 0.0 < top_p < 1.0 else "") + "; paged KV "
                                 f"{kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
                    "global_batch": B, "positions_per_step": K, "parallelism": "single GPU",
                    "schedule": args.schedule},
@@ -245,7 +258,7 @@ def main():
                      "avg_launch_us": stats_avg_s * 1e6},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
     print(json.dumps(res))
 
 

@@ -92,7 +92,8 @@ typedef struct specdec_debug {
     float*   row_max;      /* [2K+B] max kept logit of the row                            */
     double*  row_sum;      /* [2K+B] S = sum over kept x of exp((z(x) - max) / T)         */
     float*   row_thr;      /* [2K+B] top-k threshold logit (-inf when top-k is off)       */
-    int32_t* row_nkept;    /* [2K+B] kept tokens with finite logit (-1 when top-k is off) */
+    int32_t* row_nkept;    /* [2K+B] kept tokens with finite logit (-1 when top-k and
+                                   top-p are off)                                         */
     double*  resid_mass;   /* [B]  W the final token was drawn from: residual mass, or
                                    sum of p for the bonus                                  */
     double*  picked_prob;  /* [B]  w(x*) / W                                               */
@@ -106,9 +107,10 @@ typedef struct specdec_debug {
 } specdec_debug;
 
 /* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned); 0
- * for sizes the call rejects (B < 1, K < 0, V outside [1, SPECDEC_MAX_V], bad dtype). */
+ * for sizes the call rejects (B < 1, K < 0, V outside [1, SPECDEC_MAX_V], bad dtype,
+ * top_p NaN). */
 size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                     int32_t top_k);
+                                     int32_t top_k, float top_p);
 
 /*
  * specdec_verify - one verification step for a batch of B requests.
@@ -120,7 +122,11 @@ size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dt
  * where transform keeps the tokens whose logit is >= the top_k-th largest logit of the row
  * (ties inclusive; all finite tokens when top_k <= 0 or top_k >= V) and applies a
  * max-subtracted softmax at temperature T ("Speculative decoding ...", section 6: stable
- * softmax, identical transform on both sides). Proposal i is accepted iff
+ * softmax, identical transform on both sides); then, when 0 < top_p < 1, keeps only the
+ * nucleus: the tokens whose probability is >= the largest v such that the tokens of
+ * probability >= v carry at least top_p of the mass (ties inclusive), and renormalizes
+ * (sections 3 and 4 name temperature, top-k and top-p truncation among the transforms
+ * applied alike to p and q). Proposal i is accepted iff
  * u_accept[cu_draft[b]+i] * q_i(y_i) < p_i(y_i), i.e. with probability
  * min(1, p_i(y_i)/q_i(y_i)) (section 2). The first rejection j ends the run; the
  * replacement is drawn from normalize(max(0, p_j - q_j)), or, when all k_b are accepted,
@@ -141,9 +147,13 @@ size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dt
  *   err_word     [1] int32, SPECDEC_ERR_* bits OR-ed in (not cleared)
  * Host scalars: B >= 1, K = cu_draft[B] (the packed row count the caller allocated),
  * 0 <= max_k <= SPECDEC_MAX_K, 1 <= V <= SPECDEC_MAX_V, dtype SPECDEC_F32 or SPECDEC_BF16,
- * temperature > 0 and finite, top_k any value (<= 0 or >= V disables it).
+ * temperature > 0 and finite, top_k any value (<= 0 or >= V disables it), top_p any
+ * value but NaN (<= 0 or >= 1 disables it). The nucleus mass decision is made with fp32
+ * exponentials summed in fixed point (2^-42 units): a row whose boundary mass lies within
+ * about 1e-6 of top_p may keep one group of equal logits more or less than exact
+ * arithmetic would.
  * workspace: device, 16-byte aligned, >= specdec_verify_workspace_size(B, K, V, dtype,
- * top_k) bytes, owned by the caller; its contents need no initialization and are
+ * top_k, top_p) bytes, owned by the caller; its contents need no initialization and are
  * scratch between calls. Calls that share a workspace must not overlap.
  * Returns SPECDEC_OK once enqueued, or SPECDEC_EINVAL / SPECDEC_EWORKSPACE /
  * SPECDEC_EHIP without enqueuing anything that writes outputs.
@@ -152,7 +162,7 @@ int specdec_verify(const void* target_logits, const void* draft_logits, int32_t 
                    const int32_t* draft_tokens, const int32_t* cu_draft,
                    const float* u_accept, const float* u_sample,
                    int32_t B, int32_t K, int32_t max_k, int32_t V,
-                   float temperature, int32_t top_k,
+                   float temperature, int32_t top_k, float top_p,
                    int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                    int32_t* err_word, const specdec_debug* dbg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -248,9 +258,10 @@ int kv_rollback_draft(const kv_paged_cache* cache, int32_t B, const int32_t* num
  * One whole cycle
  * ===================================================================================== */
 
-/* Bytes of device workspace specdec_cycle needs (16-byte aligned). */
+/* Bytes of device workspace specdec_cycle needs (16-byte aligned); 0 where
+ * specdec_verify_workspace_size gives 0. */
 size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                    int32_t top_k);
+                                    int32_t top_k, float top_p);
 
 /*
  * specdec_cycle - one speculative cycle with the same effect as the three calls
@@ -266,14 +277,14 @@ size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dty
  * calls. The launches are fused so that block allocation overlaps the logit stream and the
  * K/V scatter overlaps the per-request sampling. Arguments and their checks are those of
  * the three calls (B <= SPECDEC_MAX_KV_BATCH); workspace >=
- * specdec_cycle_workspace_size(B, K, V, dtype, top_k) bytes, 16-byte aligned.
+ * specdec_cycle_workspace_size(B, K, V, dtype, top_k, top_p) bytes, 16-byte aligned.
  */
 int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
                   const void* target_logits, const void* draft_logits, int32_t dtype,
                   const int32_t* draft_tokens, const int32_t* cu_draft,
                   const float* u_accept, const float* u_sample,
                   int32_t B, int32_t K, int32_t max_k, int32_t V,
-                  float temperature, int32_t top_k,
+                  float temperature, int32_t top_k, float top_p,
                   int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                   int32_t* err_word, const specdec_debug* dbg,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -92,10 +92,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.specdec_status_string.argtypes = [ctypes.c_int]
     lib.specdec_status_string.restype = ctypes.c_char_p
-    lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    f32 = ctypes.c_float
+    lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
     lib.specdec_verify_workspace_size.restype = sz
     lib.specdec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
-                                   ctypes.c_float, i32, vp, vp, vp, vp,
+                                   f32, i32, f32, vp, vp, vp, vp,
                                    ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_verify.restype = ctypes.c_int
     lib.kv_paged_append_workspace_size.argtypes = [i32, i32]
@@ -106,10 +107,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in (lib.kv_rollback, lib.kv_rollback_draft):
         fn.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
         fn.restype = ctypes.c_int
-    lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
     lib.specdec_cycle_workspace_size.restype = sz
     lib.specdec_cycle.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp,
-                                  vp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, vp, vp,
+                                  vp, vp, i32, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_cycle.restype = ctypes.c_int
     _lib = lib
@@ -149,8 +150,9 @@ def _logits_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
 
 
-def specdec_verify_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int) -> int:
-    return int(load_library().specdec_verify_workspace_size(B, K, V, dtype, top_k))
+def specdec_verify_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int,
+                                  top_p: float = 1.0) -> int:
+    return int(load_library().specdec_verify_workspace_size(B, K, V, dtype, top_k, float(top_p)))
 
 
 def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
@@ -159,7 +161,7 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                    temperature: float, top_k: int, out_tokens: torch.Tensor,
                    num_accepted: torch.Tensor, num_emitted: torch.Tensor,
                    err_word: torch.Tensor, workspace: torch.Tensor,
-                   debug: Optional[SpecdecDebug] = None) -> None:
+                   debug: Optional[SpecdecDebug] = None, top_p: float = 1.0) -> None:
     """Enqueue one verification step on torch's current stream (shapes as in the header)."""
     lib = load_library()
     dev = target_logits.device
@@ -185,7 +187,7 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     st = lib.specdec_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(cu_draft),
         _ptr(u_accept), _ptr(u_sample), B, K, max_k, V, float(temperature), int(top_k),
-        _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
+        float(top_p), _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
         ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
@@ -261,8 +263,9 @@ def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch
         raise SpecdecError(fn, st)
 
 
-def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int) -> int:
-    return int(load_library().specdec_cycle_workspace_size(B, K, V, dtype, top_k))
+def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int,
+                                 top_p: float = 1.0) -> int:
+    return int(load_library().specdec_cycle_workspace_size(B, K, V, dtype, top_k, float(top_p)))
 
 
 def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -272,7 +275,7 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
                   temperature: float, top_k: int, out_tokens: torch.Tensor,
                   num_accepted: torch.Tensor, num_emitted: torch.Tensor,
                   err_word: torch.Tensor, workspace: torch.Tensor,
-                  debug: Optional[SpecdecDebug] = None) -> None:
+                  debug: Optional[SpecdecDebug] = None, top_p: float = 1.0) -> None:
     """Enqueue append -> verify -> rollback of one cycle as fused launches."""
     lib = load_library()
     dev = target_logits.device
@@ -302,7 +305,7 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
     st = lib.specdec_cycle(
         ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
         dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,
-        V, float(temperature), int(top_k), _ptr(out_tokens), _ptr(num_accepted),
+        V, float(temperature), int(top_k), float(top_p), _ptr(out_tokens), _ptr(num_accepted),
         _ptr(num_emitted), _ptr(err_word), ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:

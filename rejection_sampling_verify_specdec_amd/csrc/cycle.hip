@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
 
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool P2>
 __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
                                                       int B, int N, uint8_t* __restrict__ aws,
                                                       TopkArgs a) {
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __re
         return;
     }
     const int w = blockIdx.x - 1;
-    topk_chunk_body<BF16, VEC>(a, w / a.nchunks, w % a.nchunks);
+    topk_chunk_body<BF16, VEC, P2>(a, w / a.nchunks, w % a.nchunks);
 }
 
 template <bool BF16>
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kKvNT) void k_cycle_rollback(SampleArgs sa, KvArgs 
 template <bool BF16, bool VEC>
 static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
                          const uint8_t* tgt, const uint8_t* dft, const int* cu, int B, int K,
-                         int V, int top_k, float c, const WsPlan& p, uint8_t* vws, uint8_t* aws,
+                         int V, float top_p, float c, const WsPlan& p, uint8_t* vws, uint8_t* aws,
                          const SampleArgs& sa, const specdec_debug* dbg, hipStream_t st) {
     const int rows = 2 * K + B;
     const int N = K + B;
@@ -123,11 +123,15 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     float* thr = reinterpret_cast<float*>(vws + p.thr);
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (topk_active(top_k, V)) {
-        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_k, c, p, vws);
+    if (p.filter) {
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         const unsigned nchunk_wg = ta.generic ? 0u : (unsigned)rows * p.nchunks;
-        hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC>), dim3(nchunk_wg + 1), dim3(kTkNT), 0, st,
-                              e0, e1, 0, kv, cu, B, N, aws, ta);
+        if (p.topp_mode == 2)
+            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, true>), dim3(nchunk_wg + 1), dim3(kTkNT),
+                                  0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
+        else
+            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, false>), dim3(nchunk_wg + 1), dim3(kTkNT),
+                                  0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
         hipLaunchKernelGGL((k_cycle_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, ta);
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
@@ -149,10 +153,12 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
 }  // namespace sd
 
 extern "C" size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                               int32_t top_k) {
-    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16))
+                                               int32_t top_k, float top_p) {
+    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) ||
+        top_p != top_p)
         return 0;
-    return sd::align256(sd::plan_ws(B, K, V, dtype, top_k).total) + sd::append_ws_bytes(B, K + B);
+    return sd::align256(sd::plan_ws(B, K, V, dtype, top_k, top_p).total) +
+           sd::append_ws_bytes(B, K + B);
 }
 
 extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
@@ -160,7 +166,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
                              const int32_t* draft_tokens, const int32_t* cu_draft,
                              const float* u_accept, const float* u_sample, int32_t B, int32_t K,
                              int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                             int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                             float top_p, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                              int32_t* err_word, const specdec_debug* dbg, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
     using namespace sd;
@@ -168,7 +174,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SPECDEC_EINVAL;
+    if (!(temperature > 0.0f) || !isfinite(temperature) || top_p != top_p) return SPECDEC_EINVAL;
     if (!target_logits || !cu_draft || !u_sample || !out_tokens || !num_accepted ||
         !num_emitted || !err_word)
         return SPECDEC_EINVAL;
@@ -177,7 +183,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     if (!geometry_ok(cache) || B > SPECDEC_MAX_KV_BATCH || !k_new || !v_new ||
         ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
         return SPECDEC_EINVAL;
-    const WsPlan p = plan_ws(B, K, V, dtype, top_k);
+    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     const size_t vbytes = align256(p.total);
@@ -211,7 +217,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.V = V;
     sa.nparts = p.nparts;
     sa.nch = p.nch;
-    sa.topk = topk_active(top_k, V);
+    sa.topk = p.filter;
     sa.c = c;
     sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
@@ -229,11 +235,11 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     const KvArgs kv = args_of(cache);
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
-        else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+        if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
+        else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
     } else {
-        if (vec) launch_cycle<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
-        else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_k, c, p, vws, aws, sa, dbg, stream);
+        if (vec) launch_cycle<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
+        else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

@@ -46,9 +46,9 @@ __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ t
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x);
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool P2>
 __global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
-    topk_chunk_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+    topk_chunk_body<BF16, VEC, P2>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
 }
 
 template <bool BF16>
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kPickNT) void k_pick(SampleArgs a) {
 
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
-                       int top_k, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
+                       float top_p, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
                        const specdec_debug* dbg, hipStream_t st) {
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
@@ -81,11 +81,17 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (topk_active(top_k, V)) {
-        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_k, c, p, ws);
+    if (p.filter) {
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         if (!ta.generic) {
-            hipExtLaunchKernelGGL((k_topk_chunks<BF16, VEC>), dim3((unsigned)rows * p.nchunks),
-                                  dim3(kTkNT), 0, st, e0, e1, 0, ta);
+            if (p.topp_mode == 2)
+                hipExtLaunchKernelGGL((k_topk_chunks<BF16, VEC, true>),
+                                      dim3((unsigned)rows * p.nchunks), dim3(kTkNT), 0, st, e0, e1,
+                                      0, ta);
+            else
+                hipExtLaunchKernelGGL((k_topk_chunks<BF16, VEC, false>),
+                                      dim3((unsigned)rows * p.nchunks), dim3(kTkNT), 0, st, e0, e1,
+                                      0, ta);
             e0 = e1 = nullptr;
         }
         hipExtLaunchKernelGGL((k_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, e0, e1, 0,
@@ -103,29 +109,30 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
 }  // namespace sd
 
 extern "C" size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                                int32_t top_k) {
-    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16))
+                                                int32_t top_k, float top_p) {
+    if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) ||
+        top_p != top_p)
         return 0;
-    return sd::plan_ws(B, K, V, dtype, top_k).total;
+    return sd::plan_ws(B, K, V, dtype, top_k, top_p).total;
 }
 
 extern "C" int specdec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
                               const int32_t* draft_tokens, const int32_t* cu_draft,
                               const float* u_accept, const float* u_sample, int32_t B, int32_t K,
                               int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                              int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                              float top_p, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                               int32_t* err_word, const specdec_debug* dbg, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
     using namespace sd;
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SPECDEC_EINVAL;
+    if (!(temperature > 0.0f) || !isfinite(temperature) || top_p != top_p) return SPECDEC_EINVAL;
     if (!target_logits || !cu_draft || !u_sample || !out_tokens || !num_accepted ||
         !num_emitted || !err_word)
         return SPECDEC_EINVAL;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
-    const WsPlan p = plan_ws(B, K, V, dtype, top_k);
+    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
         V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
@@ -155,7 +162,7 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.V = V;
     sa.nparts = p.nparts;
     sa.nch = p.nch;
-    sa.topk = topk_active(top_k, V);
+    sa.topk = p.filter;
     sa.c = c;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
@@ -176,11 +183,11 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
 
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
-        else launch_all<true, false>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
+        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
+        else launch_all<true, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
     } else {
-        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
-        else launch_all<false, false>(tgt, dft, B, K, V, top_k, c, p, ws, sa, dbg, stream);
+        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
+        else launch_all<false, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

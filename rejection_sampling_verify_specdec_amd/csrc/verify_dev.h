@@ -303,7 +303,15 @@ struct TopkArgs {
     uint16_t* kkey;          // [rows_t][kKeptCap] their keys
     RowPartial* part;        // [rows]
     float* row_thr;          // [rows]
+    int topp_mode;           // 0: no top-p; 1: top-p inside the top-k set; 2: top-p alone
+    float top_p;
+    RowPartial* cpart;       // mode 2: [rows][nchunks] each chunk's max and exp-sum
+    uint32_t* ctc;           // mode 2: [rows][nchunks] each chunk's candidate bound t_c
 };
+
+// Candidates per row gathered for a top-p row without top-k: the nucleus comes from them
+// when the complete upper set they hold carries top_p of the mass, else from full passes.
+constexpr int kToppCand = 1536;          // top-p alone: candidates per row, about
 
 static inline int topk_wcap(int top_k) { return top_k <= 256 ? 256 : top_k; }
 static inline int topk_cstride(int wcap) { return kTkWaves * wcap + 16; }
@@ -389,7 +397,9 @@ SD_DEV void hist_select(const unsigned* hist, int* dig, int* krem) {
     }
 }
 
-template <bool BF16, bool VEC>
+// P2: top-p without top-k; the chunk also writes its max and exp-sum (cpart) and its bound
+// t_c (ctc), from which the merge knows the row's exp-sum and which candidates are complete.
+template <bool BF16, bool VEC, bool P2>
 SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     constexpr int NT = kTkNT;
     constexpr int NR = kTkRegs;
@@ -399,6 +409,8 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     static_assert(NR * EPR == Lt::EPT, "a chunk is NT threads x NR registers");
     static_assert(kTkWaves == 4, "t_c takes the minimum of four wave bounds");
     __shared__ uint32_t s_tw[kTkWaves];
+    __shared__ float s_mw[kTkWaves];
+    __shared__ double s_sw[kTkWaves];
     __shared__ int s_wn[kTkWaves];
     __shared__ uint32_t s_list[kTkWaves * kTkWcapMax];
     const int tid = threadIdx.x;
@@ -485,10 +497,50 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
         else krem -= n;
     }
     if (lane == 0) s_tw[wv] = tw;
+    if constexpr (P2) {
+        // top-p without top-k also needs the row's exp-sum: each wave sums exp2((z - m_w) c)
+        // over its elements with its own max m_w; thread 0 combines the four in fp64
+        const uint32_t wk = uint32_t(wave_max_i(int(kmax ^ 0x80000000u))) ^ 0x80000000u;
+        const float mw = key_to_float<BF16>(BF16 ? (wk & 0xffffu) : wk);
+        double sw = 0.0;
+        if (mw > -INFINITY && !wbad) {
+            const float mc = mw * a.c;
+            const float emc = fmaf(mw, a.c, -mc);
+            double acc = 0.0;             // fp64: the nucleus test divides by this sum
+#pragma unroll
+            for (int w = 0; w < NR; ++w)
+#pragma unroll
+                for (int h = 0; h < EPR; ++h) {
+                    const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+                    acc += (double)__builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), a.c, -mc));
+                }
+            sw = wave_sum(acc) * exp2(-(double)emc);
+        }
+        if (lane == 0) {
+            s_mw[wv] = mw;
+            s_sw[wv] = sw;
+        }
+    }
     __syncthreads();
     uint32_t t0 = min(min(s_tw[0], s_tw[1]), min(s_tw[2], s_tw[3]));
     if constexpr (!BF16) t0 <<= 16;
     if (t0 == Kt::KEY_PZERO) t0 = Kt::KEY_NZERO;
+    if (P2 && tid == 0) {
+        float mcx = s_mw[0];
+        for (int i = 1; i < kTkWaves; ++i) mcx = fmaxf(mcx, s_mw[i]);
+        double sc = 0.0;
+        if (mcx > -INFINITY)
+            for (int i = 0; i < kTkWaves; ++i)
+                if (s_mw[i] > -INFINITY)
+                    sc += s_sw[i] * exp2(((double)s_mw[i] - (double)mcx) * (double)a.c);
+        RowPartial rp;
+        rp.m = mcx;
+        rp.nkept = 0;
+        rp.s = sc;
+        const size_t ci = (size_t)row * a.nchunks + chunk;
+        a.cpart[ci] = rp;
+        a.ctc[ci] = t0;
+    }
 
     // 3. candidates (key >= t0): each wave appends to its own list, ballot-compacted in
     //    LDS, then copied out with coalesced stores
@@ -528,6 +580,124 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     if (tid == 0) a.cnt[ci] = bad ? -1 : (over ? kTkWaves * a.wcap + 1 : total);
 }
 
+// Top-p mass in fixed point: exp2(z c - m c) in units of 2^-42, rounded, so that sums do
+// not depend on the order of the adds (a row of 2^21 weights <= 1 stays below 2^63).
+constexpr double kMassFix = 4398046511104.0;
+
+SD_DEV unsigned long long mass_fix(float w) { return (unsigned long long)((double)w * kMassFix + 0.5); }
+
+// Called by the 64 threads of wave 0. hist holds 256 bins of fixed-point mass. The mass to
+// reach is frac * (all of hist) when frac > 0, else *need. Finds the largest bin d whose
+// suffix mass (bins d..255) reaches it; leaves d in *dig and the mass still to reach inside
+// bin d in *need; *dig = -1 when the whole histogram is short of it.
+SD_DEV void hist_select_mass(const unsigned long long* hist, int* dig, double* need, double frac) {
+    const int l = threadIdx.x;
+    const unsigned long long h[4] = {hist[4 * l], hist[4 * l + 1], hist[4 * l + 2], hist[4 * l + 3]};
+    const unsigned long long own = h[0] + h[1] + h[2] + h[3];
+    unsigned long long S = own;                  // mass of the bins of lanes l..63
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long v = __shfl_down(S, o, kWave);
+        if (l + o < kWave) S += v;
+    }
+    const double nd = frac > 0.0 ? frac * (double)__shfl(S, 0, kWave) : *need;
+    unsigned long long above = S - own;
+    if (l == 0 && (double)S < nd) *dig = -1;
+    if ((double)S >= nd && (double)above < nd) {
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+            if ((double)(above + h[b]) >= nd) {
+                *dig = 4 * l + b;
+                *need = nd - (double)above;
+                break;
+            }
+            above += h[b];
+        }
+    }
+}
+
+// Nucleus boundary key over a set of keys: the largest key K such that the keys >= K carry
+// frac of the mass of the keys >= lo (frac > 0), or need0 of it in fixed point (frac = 0).
+// One 8-bit digit per pass over the set; each(f) calls f(key) for this thread's share of
+// it (canonical keys: -0 as +0). Returns false (K undefined) when the mass of the keys
+// >= lo is short of need0. All NT threads call it; h64: 256 u64 of LDS.
+template <int NT, int KBITS, class Each>
+SD_DEV bool nucleus_key(Each each, uint32_t lo, float c, float mc, double frac, double need0,
+                        unsigned long long* h64, uint32_t* K) {
+    __shared__ int s_dig;
+    __shared__ double s_need;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_need = need0;
+    uint32_t prefix = 0u;
+    for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
+        const uint32_t hmask = shift + 8 >= KBITS ? 0u : ~0u << (shift + 8);
+        for (int i = tid; i < 256; i += NT) h64[i] = 0ull;
+        __syncthreads();
+        each([&](uint32_t k, float z) {
+            if (k >= lo && (k & hmask) == prefix)
+                atomicAdd(&h64[(k >> shift) & 0xffu], mass_fix(__builtin_amdgcn_exp2f(fmaf(z, c, -mc))));
+        });
+        __syncthreads();
+        if (tid < kWave) hist_select_mass(h64, &s_dig, &s_need, shift == KBITS - 8 ? frac : 0.0);
+        __syncthreads();
+        const int d = s_dig;
+        if (d < 0) return false;
+        prefix |= (uint32_t)d << shift;
+    }
+    *K = prefix;
+    return true;
+}
+
+// Nucleus of one row by full passes over it (rows that took the generic top-k select, or
+// whose nucleus reaches below the gathered candidates): the boundary over the tokens with
+// logit >= thr_lo (finite), then the kept count and exp-sum in a last pass. m: the row max.
+template <bool BF16, int NT>
+SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
+                           unsigned long long* h64) {
+    using Kt = TopkKeys<BF16>;
+    constexpr int ES = BF16 ? 2 : 4;
+    __shared__ double redd[NT / kWave];
+    __shared__ int redi[NT / kWave];
+    const int tid = threadIdx.x;
+    const uint8_t* base = row_ptr(a.tgt, a.dft, a.rows_t, row, a.V, ES);
+    const float mc = m * a.c;
+    const float emc = fmaf(m, a.c, -mc);
+    auto keyz = [](float z) {                    // canonical key of a logit (-0 as +0)
+        const uint32_t k = BF16 ? f2key(z) >> 16 : f2key(z);
+        return k == Kt::KEY_NZERO ? Kt::KEY_PZERO : k;
+    };
+    const uint32_t lo = max(thr_lo > -INFINITY ? keyz(thr_lo) : 0u, Kt::KEY_NINF + 1u);
+    uint32_t K = lo;
+    const bool ok = nucleus_key<NT, Kt::KBITS>(
+        [&](auto f) {
+            for (int i = tid; i < a.V; i += NT) {
+                const float z = load_elem(base, i, BF16);
+                if (z > -INFINITY) f(keyz(z), z);
+            }
+        },
+        lo, a.c, mc, (double)a.top_p, 0.0, h64, &K);
+    const float thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
+    float acc = 0.f;
+    int kept = 0;
+    for (int i = tid; i < a.V; i += NT) {
+        const float z = load_elem(base, i, BF16);
+        if (z >= thr && z > -INFINITY) {
+            acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
+            ++kept;
+        }
+    }
+    const double tot = block_sum<NT>((double)acc, redd);
+    kept = block_sum_i<NT>(kept, redi);
+    if (tid == 0) {
+        RowPartial rp;
+        rp.m = m;
+        rp.nkept = kept;
+        rp.s = tot * exp2(-(double)emc);
+        a.part[row] = rp;
+        a.row_thr[row] = thr;
+    }
+}
+
 template <bool BF16>
 SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     constexpr int NT = kMergeNT;
@@ -535,11 +705,13 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
     static_assert(kKeptCap >= 256, "the histogram and the kept-token list share LDS");
-    __shared__ uint32_t s_u32[kKeptCap];    // radix histogram, then the kept tokens
+    __shared__ __attribute__((aligned(16))) uint32_t s_u32[kKeptCap];   // histograms, then
+                                                                       // the kept tokens
     unsigned* hist = s_u32;
     uint32_t* s_ktok = s_u32;
     __shared__ int s_off[kTkMaxChunks + 1];
-    __shared__ uint32_t keys[kMergeCap];    // entries as the chunks wrote them
+    __shared__ __attribute__((aligned(16))) uint32_t keys[kMergeCap];   // entries as the chunks
+                                                                     // wrote them
     __shared__ uint16_t s_kkey[BF16 ? kKeptCap : 1];
     __shared__ int redi[NT / kWave];
     __shared__ double redd[2 * (NT / kWave)];
@@ -571,7 +743,25 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     int off = block_excl_scan_i<NT>(mine, redi, &total);
     if (total > kMergeCap) {
         if (listed && tid == 0) a.kn[row] = -1;
-        topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.top_k, a.c, a.part, a.row_thr, row);
+        // generic select (all of the row's finite tokens for top-p alone), then the nucleus
+        topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.topp_mode == 2 ? a.V : a.top_k,
+                                 a.c, a.part, a.row_thr, row);
+        if (a.topp_mode) {
+            // the row max and validity as the select left them (tid 0 wrote them)
+            if (tid == 0) {
+                const RowPartial rp = a.part[row];
+                s_kmax = (rp.s == rp.s && rp.m > -INFINITY) ? 1u : 0u;
+                redd[0] = rp.m;
+                redd[1] = a.row_thr[row];
+            }
+            __syncthreads();
+            const bool run = s_kmax != 0u;
+            const float rm = (float)redd[0], tk = (float)redd[1];
+            __syncthreads();
+            if (run)
+                topp_rows_body<BF16, NT>(a, row, rm, a.topp_mode == 1 ? tk : -INFINITY,
+                                         reinterpret_cast<unsigned long long*>(keys));
+        }
         return;
     }
 #pragma unroll
@@ -619,10 +809,10 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     if (kmax) atomicMax(&s_kmax, kmax);
     __syncthreads();
 
-    // exact top_k-th largest candidate key, one 8-bit digit at a time
+    // exact top_k-th largest candidate key, one 8-bit digit at a time (no top-k: none)
     uint32_t prefix = 0u;
 #pragma unroll
-    for (int shift = Kt::KBITS - 8; shift >= 0; shift -= 8) {
+    for (int shift = Kt::KBITS - 8; shift >= 0 && a.topp_mode != 2; shift -= 8) {
         const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
         for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();
@@ -635,10 +825,61 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
         __syncthreads();
         prefix |= (uint32_t)s_dig << shift;
     }
-    const float thr = key_to_float<BF16>(prefix);
+    float thr = a.topp_mode == 2 ? -INFINITY : key_to_float<BF16>(prefix);
     const float m = key_to_float<BF16>(s_kmax);
     const float mc = m * a.c;
     const float emc = fmaf(m, a.c, -mc);
+    if (a.topp_mode && m > -INFINITY) {
+        // top-p: the nucleus boundary among the candidates (-0 ranks with +0, as the float
+        // comparisons do)
+        auto canon = [](uint32_t k) { return k == Kt::KEY_NZERO ? Kt::KEY_PZERO : k; };
+        uint32_t lo;
+        double frac = 0.0, need = 0.0;
+        if (a.topp_mode == 1) {
+            // with top-k: the kept set is every candidate >= the top-k threshold
+            lo = max(canon(prefix), Kt::KEY_NINF + 1u);
+            frac = (double)a.top_p;
+        } else {
+            // no top-k: the row's exp-sum from the chunk partials; the candidates hold the
+            // complete upper set above every chunk's bound t_c
+            double sp = 0.0;
+            uint32_t tg = 0u;
+#pragma unroll
+            for (int q = 0; q < LPT; ++q) {
+                const int l = tid * LPT + q;
+                if (l < nl) {
+                    const RowPartial cp = a.cpart[(size_t)row * nl + l];
+                    if (cp.m > -INFINITY)
+                        sp += cp.s * exp2(((double)cp.m - (double)m) * (double)a.c);
+                    tg = max(tg, a.ctc[(size_t)row * nl + l]);
+                }
+            }
+            const double S = block_sum<NT>(sp, redd);
+            tg = uint32_t(block_max_i<NT>(int(tg ^ 0x80000000u), redi)) ^ 0x80000000u;
+            lo = (tg == Kt::KEY_PZERO || tg == Kt::KEY_NZERO) ? Kt::KEY_PZERO + 1u : canon(tg);
+            lo = max(lo, Kt::KEY_NINF + 1u);
+            need = (double)a.top_p * S * exp2((double)emc) * kMassFix;
+        }
+        unsigned long long* h64 = reinterpret_cast<unsigned long long*>(s_u32);
+        uint32_t K = lo;
+        const bool ok = nucleus_key<NT, Kt::KBITS>(
+            [&](auto f) {
+                for (int i = tid; i < total; i += NT) {
+                    const uint32_t k = canon(key_of(keys[i]));
+                    f(k, key_to_float<BF16>(k));
+                }
+            },
+            lo, a.c, mc, frac, need, h64, &K);
+        if (!ok && a.topp_mode == 2) {
+            // the nucleus reaches below the candidates: full passes over the row
+            if (listed && tid == 0) a.kn[row] = -1;
+            __syncthreads();
+            topp_rows_body<BF16, NT>(a, row, m, -INFINITY, h64);
+            return;
+        }
+        thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
+        __syncthreads();                    // the histogram memory holds kept tokens next
+    }
     float acc = 0.f;
     int kept = 0;
     for (int i = tid; i < total; i += NT) {
@@ -1287,18 +1528,44 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, total;
-    int nparts, nchunks, nch, tk_wcap, tk_listed;
+    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc, total;
+    int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
 };
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
+static inline bool topp_active(float top_p) { return top_p > 0.0f && top_p < 1.0f; }
+// 0: no top-p; 1: top-p inside the top-k set; 2: top-p alone
+static inline int topp_mode(int top_k, float top_p, int V) {
+    return !topp_active(top_p) ? 0 : (topk_active(top_k, V) ? 1 : 2);
+}
+// rows carry a threshold (top-k, top-p or both)
+static inline bool filter_active(int top_k, float top_p, int V) {
+    return topk_active(top_k, V) || topp_active(top_p);
+}
+// the k the chunk select runs with. Top-p alone gathers about kToppCand candidates per row
+// over all chunks (each chunk's top k_c, a multiple of 4 in [16, 256]), so that the merge's
+// LDS holds them: the complete upper set above the largest chunk bound is then the part of
+// the row the nucleus is searched in.
+static inline int select_k(int top_k, float top_p, int V, int nchunks) {
+    if (topp_mode(top_k, top_p, V) != 2) return top_k;
+    const int kc = (kToppCand / nchunks) & ~3;
+    return kc < 16 ? 16 : (kc > 256 ? 256 : kc);
+}
+static inline bool select_generic(int top_k, float top_p, int V, int nchunks) {
+    const int k = select_k(top_k, top_p, V, nchunks);
+    return topk_generic(k) || k >= V;
+}
 
-static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
+static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float top_p) {
     WsPlan p{};
     // the vector and scalar layouts use the same chunk length
     const int ch = dtype == SPECDEC_BF16 ? Layout<true, true>::CH : Layout<false, true>::CH;
     p.nchunks = (V + ch - 1) / ch;
-    p.nparts = topk_active(top_k, V) ? 1 : p.nchunks;
+    p.filter = filter_active(top_k, top_p, V);
+    p.topp_mode = topp_mode(top_k, top_p, V);
+    p.sel_k = select_k(top_k, top_p, V, p.nchunks);
+    p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
+    p.nparts = p.filter ? 1 : p.nchunks;
     const size_t rows = (size_t)2 * K + B;
     size_t off = 0;
     p.part = off;
@@ -1310,13 +1577,19 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
     off = align256(off + (size_t)B * sizeof(Decision));
     p.wsum = off;
     off = align256(off + (size_t)B * p.nch * kSSub * sizeof(double));
-    p.tk_cnt = p.tk_cand = off;
-    if (topk_active(top_k, V) && !topk_generic(top_k)) {
-        p.tk_wcap = topk_wcap(top_k);
+    p.tk_cnt = p.tk_cand = p.tk_cpart = p.tk_ctc = off;
+    if (p.filter && !p.sel_generic) {
+        p.tk_wcap = topk_wcap(p.sel_k);
         const size_t lists = rows * p.nchunks;
         off = align256(off + lists * sizeof(int));
         p.tk_cand = off;
         off = align256(off + lists * (size_t)topk_cstride(p.tk_wcap) * sizeof(uint32_t));
+        if (p.topp_mode == 2) {            // per-chunk max / exp-sum and bound
+            p.tk_cpart = off;
+            off = align256(off + lists * sizeof(RowPartial));
+            p.tk_ctc = off;
+            off = align256(off + lists * sizeof(uint32_t));
+        }
         if (dtype == SPECDEC_BF16) {       // kept-token lists of the target rows
             const size_t rows_t = (size_t)K + B;
             p.tk_listed = 1;
@@ -1333,17 +1606,17 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k) {
 }
 
 static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int rows_t, int V,
-                                 int top_k, float c, const WsPlan& p, uint8_t* ws) {
+                                 float top_p, float c, const WsPlan& p, uint8_t* ws) {
     TopkArgs a;
     a.tgt = tgt;
     a.dft = dft;
     a.rows_t = rows_t;
     a.V = V;
     a.nchunks = p.nchunks;
-    a.top_k = top_k;
+    a.top_k = p.sel_k;
     a.wcap = p.tk_wcap;
     a.cstride = topk_cstride(p.tk_wcap);
-    a.generic = topk_generic(top_k);
+    a.generic = p.sel_generic;
     a.c = c;
     a.cnt = reinterpret_cast<int*>(ws + p.tk_cnt);
     a.cand = reinterpret_cast<uint32_t*>(ws + p.tk_cand);
@@ -1352,6 +1625,10 @@ static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int row
     a.kkey = p.tk_listed ? reinterpret_cast<uint16_t*>(ws + p.tk_kkey) : nullptr;
     a.part = reinterpret_cast<RowPartial*>(ws + p.part);
     a.row_thr = reinterpret_cast<float*>(ws + p.thr);
+    a.topp_mode = p.topp_mode;
+    a.top_p = top_p;
+    a.cpart = p.topp_mode == 2 ? reinterpret_cast<RowPartial*>(ws + p.tk_cpart) : nullptr;
+    a.ctc = p.topp_mode == 2 ? reinterpret_cast<uint32_t*>(ws + p.tk_ctc) : nullptr;
     return a;
 }
 

@@ -56,11 +56,11 @@ def test_cycle(wl, mode):
         assert all(o_kv.seq_lens[b] % kv.block_size == 0 for b in rej)
 
 
-def _run_mode(vin, kv, mode, free_count=None, cu_override=None):
+def _run_mode(vin, kv, mode, free_count=None, cu_override=None, top_p=1.0):
     g_kv = KVOnDevice(kv, vin.B)
     if free_count is not None:
         g_kv.cache.free_count.fill_(free_count)
-    g_v = VerifyOnDevice(vin)
+    g_v = VerifyOnDevice(vin, top_p=top_p)
     if cu_override is not None:
         g_v.cu.copy_(torch.tensor(cu_override, dtype=torch.int32))
     if mode == "calls":
@@ -69,27 +69,31 @@ def _run_mode(vin, kv, mode, free_count=None, cu_override=None):
         g_kv.rollback(g_v.num_acc, g_v.cu)
     else:
         dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-        ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, vin.top_k),
+        ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, vin.top_k,
+                                                              top_p),
                          dtype=torch.uint8, device=g_v.tgt.device)
         binding.specdec_cycle(g_kv.cache, g_kv.k_new, g_kv.v_new, g_v.tgt, g_v.dft, g_v.tokens,
                               g_v.cu, g_v.u_acc, g_v.u_smp, max_k=vin.max_k, temperature=vin.T,
                               top_k=vin.top_k, out_tokens=g_v.out_tokens,
                               num_accepted=g_v.num_acc, num_emitted=g_v.num_emit,
-                              err_word=g_v.err, workspace=ws, debug=g_v.dbg)
+                              err_word=g_v.err, workspace=ws, debug=g_v.dbg, top_p=top_p)
     g = g_v.result()
     return g, g_kv.meta(), g_kv.pool.view(torch.int16).cpu().numpy()
 
 
-@pytest.mark.parametrize("case", ["normal", "nomem", "bad_offsets", "topk"])
+@pytest.mark.parametrize("case", ["normal", "nomem", "bad_offsets", "topk", "topp", "topk_topp"])
 def test_fused_cycle_equals_three_calls(case):
     # small geometry, shared prefixes and a fragmented pool; the fused launches must give
     # bit-identical outputs, metadata and pool contents
-    over = dict(top_k=8) if case == "topk" else {}
-    vin = synth.make_verify("c4", seed=31, B=12, V=2048, **over)
+    over = dict(top_k=8) if case in ("topk", "topk_topp") else {}
+    V = 40000 if case == "topp" else 2048
+    vin = synth.make_verify("c4", seed=31, B=12, V=V, **over)
     rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=520, prefix_hi=700, share_group=4,
                          share_blocks=32)
     kv = synth.make_kv("c4", vin, seed=31, recipe=rec)
     kw = {}
+    if case in ("topp", "topk_topp"):
+        kw["top_p"] = 0.8
     if case == "nomem":
         kw["free_count"] = 3
     if case == "bad_offsets":
@@ -100,7 +104,7 @@ def test_fused_cycle_equals_three_calls(case):
     a = _run_mode(vin, kv, "calls", **kw)
     b = _run_mode(vin, kv, "fused", **kw)
     for f in ("num_accepted", "num_emitted", "out_tokens", "err_word", "p_y", "q_y", "row_sum",
-              "resid_mass", "picked_prob", "req_flags"):
+              "row_thr", "row_nkept", "resid_mass", "picked_prob", "req_flags"):
         assert np.array_equal(np.asarray(getattr(a[0], f)), np.asarray(getattr(b[0], f))), f
     for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
         assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
