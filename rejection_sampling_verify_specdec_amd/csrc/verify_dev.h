@@ -41,6 +41,45 @@ SD_DEV float load_elem(const uint8_t* row, long i, bool bf16) {
     return reinterpret_cast<const float*>(row)[i];
 }
 
+// Calls f(z) for this thread's share of a row's V elements, in a fixed order: U 16-byte
+// vectors in flight per thread when the row starts 16-byte aligned (the whole vectors),
+// single elements otherwise and for the tail. For passes that walk whole rows.
+template <bool BF16, int NT, int U, class F>
+SD_DEV void walk_row(const uint8_t* __restrict__ row, int V, F&& f) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    const int tid = threadIdx.x;
+    int done = 0;
+    if (((uintptr_t)row & 15) == 0) {
+        const int nv = V / EPV;
+        const u32x4* p = reinterpret_cast<const u32x4*>(row);
+        for (int v0 = 0; v0 < nv; v0 += U * NT) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int v = v0 + u * NT + tid;
+                x[u] = v < nv ? p[v] : (u32x4){0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (v0 + u * NT + tid < nv) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t w = x[u][q];
+                        if constexpr (BF16) {
+                            f(__uint_as_float(w << 16));
+                            f(__uint_as_float(w & 0xffff0000u));
+                        } else {
+                            f(__uint_as_float(w));
+                        }
+                    }
+                }
+            }
+        }
+        done = nv * EPV;
+    }
+    for (int i = done + tid; i < V; i += NT) f(load_elem(row, i, BF16));
+}
+
 // Element z[col * PER + e] of the calling thread is index c0 + (col * kNT + tid) * PER + e
 // of the row; elements at or past V read as -inf.
 template <bool BF16, bool VEC>
@@ -191,11 +230,10 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
     // pass 0: max, invalid entries (NaN, +inf)
     float mx = -INFINITY;
     int bad = 0;
-    for (int i = tid; i < V; i += NT) {
-        const float z = load_elem(base, i, BF16);
+    walk_row<BF16, NT, 4>(base, V, [&](float z) {
         mx = fmaxf(mx, z);
         bad |= (z != z) | (z == INFINITY);
-    }
+    });
     const float m = block_max<NT>(mx, redf);
     bad = block_max_i<NT>(bad, redi);
 
@@ -212,10 +250,10 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
         __syncthreads();
         const uint32_t prefix = s_prefix;
         const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        for (int i = tid; i < V; i += NT) {
-            const uint32_t k = f2key(load_elem(base, i, BF16));
+        walk_row<BF16, NT, 4>(base, V, [&](float z) {
+            const uint32_t k = f2key(z);
             if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xff], 1u);
-        }
+        });
         __syncthreads();
         if (tid == 0) {
             int krem = s_krem;
@@ -238,13 +276,12 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
     const float emc = fmaf(m, c, -mc);
     float acc = 0.f;
     int kept = 0;
-    for (int i = tid; i < V; i += NT) {
-        const float z = load_elem(base, i, BF16);
+    walk_row<BF16, NT, 4>(base, V, [&](float z) {
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
             ++kept;
         }
-    }
+    });
     const double tot = block_sum<NT>((double)acc, redd);
     kept = block_sum_i<NT>(kept, redi);
     if (tid == 0) {
@@ -311,7 +348,7 @@ struct TopkArgs {
 
 // Candidates per row gathered for a top-p row without top-k: the nucleus comes from them
 // when the complete upper set they hold carries top_p of the mass, else from full passes.
-constexpr int kToppCand = 1536;          // top-p alone: candidates per row, about
+constexpr int kToppCand = 1024;          // top-p alone: upper-set size per row, about
 
 static inline int topk_wcap(int top_k) { return top_k <= 256 ? 256 : top_k; }
 static inline int topk_cstride(int wcap) { return kTkWaves * wcap + 16; }
@@ -506,15 +543,22 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
         if (mw > -INFINITY && !wbad) {
             const float mc = mw * a.c;
             const float emc = fmaf(mw, a.c, -mc);
-            double acc = 0.0;             // fp64: the nucleus test divides by this sum
+            // fp32 trees of 16 (8) terms per register group, then across the groups
+            float gs[4];
 #pragma unroll
-            for (int w = 0; w < NR; ++w)
+            for (int g = 0; g < 4; ++g) {
+                float e[NR / 4 * EPR];
 #pragma unroll
-                for (int h = 0; h < EPR; ++h) {
-                    const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
-                    acc += (double)__builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), a.c, -mc));
-                }
-            sw = wave_sum(acc) * exp2(-(double)emc);
+                for (int w = 0; w < NR / 4; ++w)
+#pragma unroll
+                    for (int h = 0; h < EPR; ++h) {
+                        const uint32_t k = (r[g * (NR / 4) + w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+                        e[w * EPR + h] =
+                            __builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), a.c, -mc));
+                    }
+                gs[g] = tree_sum(e);
+            }
+            sw = wave_sum((double)tree_sum(gs)) * exp2(-(double)emc);
         }
         if (lane == 0) {
             s_mw[wv] = mw;
@@ -586,14 +630,18 @@ constexpr double kMassFix = 4398046511104.0;
 
 SD_DEV unsigned long long mass_fix(float w) { return (unsigned long long)((double)w * kMassFix + 0.5); }
 
-// Called by the 64 threads of wave 0. hist holds 256 bins of fixed-point mass. The mass to
-// reach is frac * (all of hist) when frac > 0, else *need. Finds the largest bin d whose
-// suffix mass (bins d..255) reaches it; leaves d in *dig and the mass still to reach inside
-// bin d in *need; *dig = -1 when the whole histogram is short of it.
+// Called by the 64 threads of wave 0. hist holds NB bins of fixed-point mass (NB / 64 per
+// lane). The mass to reach is frac * (all of hist) when frac > 0, else *need. Finds the
+// largest bin d whose suffix mass (bins d..NB-1) reaches it; leaves d in *dig and the mass
+// still to reach inside bin d in *need; *dig = -1 when the whole histogram is short of it.
+template <int NB>
 SD_DEV void hist_select_mass(const unsigned long long* hist, int* dig, double* need, double frac) {
+    constexpr int BPL = NB / kWave;
+    static_assert(BPL * kWave == NB, "whole bins per lane");
     const int l = threadIdx.x;
-    const unsigned long long h[4] = {hist[4 * l], hist[4 * l + 1], hist[4 * l + 2], hist[4 * l + 3]};
-    const unsigned long long own = h[0] + h[1] + h[2] + h[3];
+    unsigned long long own = 0ull;
+#pragma unroll
+    for (int b = 0; b < BPL; ++b) own += hist[BPL * l + b];
     unsigned long long S = own;                  // mass of the bins of lanes l..63
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -604,45 +652,50 @@ SD_DEV void hist_select_mass(const unsigned long long* hist, int* dig, double* n
     unsigned long long above = S - own;
     if (l == 0 && (double)S < nd) *dig = -1;
     if ((double)S >= nd && (double)above < nd) {
-#pragma unroll
-        for (int b = 3; b >= 0; --b) {
-            if ((double)(above + h[b]) >= nd) {
-                *dig = 4 * l + b;
+        for (int b = BPL - 1; b >= 0; --b) {
+            const unsigned long long h = hist[BPL * l + b];
+            if ((double)(above + h) >= nd) {
+                *dig = BPL * l + b;
                 *need = nd - (double)above;
                 break;
             }
-            above += h[b];
+            above += h;
         }
     }
 }
 
 // Nucleus boundary key over a set of keys: the largest key K such that the keys >= K carry
 // frac of the mass of the keys >= lo (frac > 0), or need0 of it in fixed point (frac = 0).
-// One 8-bit digit per pass over the set; each(f) calls f(key) for this thread's share of
-// it (canonical keys: -0 as +0). Returns false (K undefined) when the mass of the keys
-// >= lo is short of need0. All NT threads call it; h64: 256 u64 of LDS.
-template <int NT, int KBITS, class Each>
+// One digit of up to DBITS bits per pass over the set, most significant first, from a
+// histogram of NB >= 2^DBITS bins; each(f) calls f(key, z) for this thread's share of the
+// set (canonical keys: -0 as +0). Returns false (K undefined) when the mass of the keys
+// >= lo is short of need0. All NT threads call it; h64: NB u64 of LDS.
+template <int NT, int KBITS, int DBITS, int NB, class Each>
 SD_DEV bool nucleus_key(Each each, uint32_t lo, float c, float mc, double frac, double need0,
                         unsigned long long* h64, uint32_t* K) {
+    static_assert((1 << DBITS) <= NB, "a digit's bins fit the histogram");
     __shared__ int s_dig;
     __shared__ double s_need;
     const int tid = threadIdx.x;
     if (tid == 0) s_need = need0;
     uint32_t prefix = 0u;
-    for (int shift = KBITS - 8; shift >= 0; shift -= 8) {
-        const uint32_t hmask = shift + 8 >= KBITS ? 0u : ~0u << (shift + 8);
-        for (int i = tid; i < 256; i += NT) h64[i] = 0ull;
+    for (int hi = KBITS; hi > 0; hi -= DBITS) {
+        const int lb = hi > DBITS ? hi - DBITS : 0;
+        const uint32_t hmask = hi >= KBITS ? 0u : ~0u << hi;
+        const uint32_t dmask = (1u << (hi - lb)) - 1u;
+        for (int i = tid; i < NB; i += NT) h64[i] = 0ull;
         __syncthreads();
         each([&](uint32_t k, float z) {
             if (k >= lo && (k & hmask) == prefix)
-                atomicAdd(&h64[(k >> shift) & 0xffu], mass_fix(__builtin_amdgcn_exp2f(fmaf(z, c, -mc))));
+                atomicAdd(&h64[(k >> lb) & dmask],
+                          mass_fix(__builtin_amdgcn_exp2f(fmaf(z, c, -mc))));
         });
         __syncthreads();
-        if (tid < kWave) hist_select_mass(h64, &s_dig, &s_need, shift == KBITS - 8 ? frac : 0.0);
+        if (tid < kWave) hist_select_mass<NB>(h64, &s_dig, &s_need, hi == KBITS ? frac : 0.0);
         __syncthreads();
         const int d = s_dig;
         if (d < 0) return false;
-        prefix |= (uint32_t)d << shift;
+        prefix |= (uint32_t)d << lb;
     }
     *K = prefix;
     return true;
@@ -651,6 +704,10 @@ SD_DEV bool nucleus_key(Each each, uint32_t lo, float c, float mc, double frac, 
 // Nucleus of one row by full passes over it (rows that took the generic top-k select, or
 // whose nucleus reaches below the gathered candidates): the boundary over the tokens with
 // logit >= thr_lo (finite), then the kept count and exp-sum in a last pass. m: the row max.
+// The first digit has 10 bits (sign, exponent, one mantissa bit for bf16) so that the
+// histogram adds of a wave spread over many bins. h64: kToppRowBins u64 of LDS.
+constexpr int kToppRowDigit = 10;
+constexpr int kToppRowBins = 1024;
 template <bool BF16, int NT>
 SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
                            unsigned long long* h64) {
@@ -668,24 +725,22 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
     };
     const uint32_t lo = max(thr_lo > -INFINITY ? keyz(thr_lo) : 0u, Kt::KEY_NINF + 1u);
     uint32_t K = lo;
-    const bool ok = nucleus_key<NT, Kt::KBITS>(
+    const bool ok = nucleus_key<NT, Kt::KBITS, kToppRowDigit, kToppRowBins>(
         [&](auto f) {
-            for (int i = tid; i < a.V; i += NT) {
-                const float z = load_elem(base, i, BF16);
+            walk_row<BF16, NT, 4>(base, a.V, [&](float z) {
                 if (z > -INFINITY) f(keyz(z), z);
-            }
+            });
         },
         lo, a.c, mc, (double)a.top_p, 0.0, h64, &K);
     const float thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
     float acc = 0.f;
     int kept = 0;
-    for (int i = tid; i < a.V; i += NT) {
-        const float z = load_elem(base, i, BF16);
+    walk_row<BF16, NT, 4>(base, a.V, [&](float z) {
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
             ++kept;
         }
-    }
+    });
     const double tot = block_sum<NT>((double)acc, redd);
     kept = block_sum_i<NT>(kept, redi);
     if (tid == 0) {
@@ -712,6 +767,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     __shared__ int s_off[kTkMaxChunks + 1];
     __shared__ __attribute__((aligned(16))) uint32_t keys[kMergeCap];   // entries as the chunks
                                                                      // wrote them
+    static_assert(kMergeCap * 4 >= kToppRowBins * 8, "the full-row nucleus histogram fits");
     __shared__ uint16_t s_kkey[BF16 ? kKeptCap : 1];
     __shared__ int redi[NT / kWave];
     __shared__ double redd[2 * (NT / kWave)];
@@ -862,7 +918,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
         }
         unsigned long long* h64 = reinterpret_cast<unsigned long long*>(s_u32);
         uint32_t K = lo;
-        const bool ok = nucleus_key<NT, Kt::KBITS>(
+        const bool ok = nucleus_key<NT, Kt::KBITS, 8, 256>(
             [&](auto f) {
                 for (int i = tid; i < total; i += NT) {
                     const uint32_t k = canon(key_of(keys[i]));
@@ -874,7 +930,8 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
             // the nucleus reaches below the candidates: full passes over the row
             if (listed && tid == 0) a.kn[row] = -1;
             __syncthreads();
-            topp_rows_body<BF16, NT>(a, row, m, -INFINITY, h64);
+            topp_rows_body<BF16, NT>(a, row, m, -INFINITY,
+                                     reinterpret_cast<unsigned long long*>(keys));
             return;
         }
         thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
@@ -1542,14 +1599,15 @@ static inline int topp_mode(int top_k, float top_p, int V) {
 static inline bool filter_active(int top_k, float top_p, int V) {
     return topk_active(top_k, V) || topp_active(top_p);
 }
-// the k the chunk select runs with. Top-p alone gathers about kToppCand candidates per row
-// over all chunks (each chunk's top k_c, a multiple of 4 in [16, 256]), so that the merge's
-// LDS holds them: the complete upper set above the largest chunk bound is then the part of
-// the row the nucleus is searched in.
+// the k the chunk select runs with. Top-p alone asks each chunk for its top k_c tokens,
+// k_c = kToppCand / nchunks (a multiple of 4 in [8, 128]); the per-thread-max bound then
+// gathers about 1.5 kToppCand candidates per row on unstructured rows, within the merge's
+// LDS, and the complete upper set above the largest chunk bound (about kToppCand tokens)
+// is where the nucleus is searched.
 static inline int select_k(int top_k, float top_p, int V, int nchunks) {
     if (topp_mode(top_k, top_p, V) != 2) return top_k;
     const int kc = (kToppCand / nchunks) & ~3;
-    return kc < 16 ? 16 : (kc > 256 ? 256 : kc);
+    return kc < 8 ? 8 : (kc > 128 ? 128 : kc);
 }
 static inline bool select_generic(int top_k, float top_p, int V, int nchunks) {
     const int k = select_k(top_k, top_p, V, nchunks);
