@@ -225,6 +225,9 @@ def main():
     cycle_gbps = cycle_bytes / (ms_per_step / 1e3) / 1e9
     achieved = logit_bytes / stats_avg_s / 1e9
     filtered = 0 < vin.top_k < V or 0.0 < top_p < 1.0
+    # top_k above 1024 runs the multi-pass select inside the merge launch: no launch
+    # streams the rows once
+    generic = 0 < vin.top_k < V and vin.top_k > 1024
     if filtered:      # the first launch holds the rows as keys and gathers candidates
         stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
     else:
@@ -257,6 +260,8 @@ def main():
                      "algorithmic_bytes": logit_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
     }
+    if generic:
+        res["roofline"] = None
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
     print(json.dumps(res))

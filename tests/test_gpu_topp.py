@@ -76,7 +76,8 @@ def test_topp_inside_topk(wl, top_k):
 
 @pytest.mark.parametrize("V", [100, 256, 300, 4001])
 def test_topp_small_and_unaligned_vocab(V):
-    # V <= 256: generic select; 300: one chunk, candidate lists overflow (padding)
+    # V = 100: generic select; 256 and 300: one chunk whose candidate lists overflow (its
+    # padding is -inf), then the generic select; 4001: unaligned rows
     vin = synth.make_verify("c4", seed=66, B=4, V=V, top_k=0)
     _check(_redraw(vin, 0.8, 67), 0.8)
 
