@@ -1,16 +1,18 @@
-// One whole speculative cycle in four launches (five with top-k) (gfx950): the same work and results as
-// kv_paged_append -> specdec_verify -> kv_rollback on one stream, with the latency-bound
-// pieces folded into launches that are busy streaming memory anyway.
+// One whole speculative cycle in four launches (five with top-k or top-p; one more above
+// 512 requests) (gfx950): the same work and results as kv_paged_append -> specdec_verify ->
+// kv_rollback on one stream, with the latency-bound pieces folded into launches that are
+// busy streaming memory anyway.
 //
 //   k_cycle_stats   workgroup 0 allocates the cycle's blocks (copy-on-write, LIFO pops,
 //                   destination rows) while every other workgroup streams logit rows
-//                   (row statistics, or top-k chunk candidates followed by a short
-//                   per-row merge launch);
+//                   (row statistics; with top-k or top-p, k_cycle_topk gathers chunk
+//                   candidates and a short per-row merge launch follows);
 //   k_cycle_decide  K/V scatter workgroups, then one workgroup per request for its
 //                   accept / reject decisions;
-//   k_part          (request, chunk) workgroups sum the sampling weights chunk by chunk;
-//   k_cycle_pick    workgroup 0 truncates every request to its committed prefix while the
-//                   others draw each request's replacement / bonus token.
+//   k_cycle_part    workgroup 0 truncates every request to its committed prefix (up to 512
+//                   requests; beyond that k_cycle_rollback runs after the pick) while the
+//                   others sum the sampling weights chunk by chunk;
+//   k_cycle_pick    one workgroup per request draws its replacement / bonus token.
 //
 // The cycle is the one the pages describe ("Walk through KV-cache updates when
 // speculative decoding rejects some draft tokens": K/V for the candidates are appended by

@@ -4,18 +4,21 @@
 // changing its answers", section 2 "Draft, verify, correct" (accept y_i with probability
 // min(1, p_i(y_i)/q_i(y_i)) left to right, replacement from normalize(max(0, p_j - q_j))
 // at the first rejection j, bonus token from p_{k+1} when all are accepted), with the
-// decoding transform (temperature, top-k) applied identically to target and draft rows
-// and a max-subtracted (stable) softmax (same page, section 6).
+// decoding transform (temperature, top-k, top-p) applied identically to target and draft
+// rows (sections 3 and 4) and a max-subtracted (stable) softmax (same page, section 6).
 //
-// Pipeline on one stream, per call (four kernels, five with top-k):
+// Pipeline on one stream, per call (four kernels, five with top-k or top-p):
 //   k_row_stats   every target and draft row is streamed once in 16K-element chunks with
 //                 128-bit loads; each workgroup writes the chunk max m_c and
 //                 S_c = sum exp2((z - m_c) * c), c = log2(e) / T, as an fp32/fp64 pair.
-//   k_topk_chunks (top-k only, replaces k_row_stats) the same chunks, held in registers as
-//                 order-preserving keys: each workgroup writes the few tokens that can be
-//                 in the row's top-k set (a bound from its per-thread maxima).
+//   k_topk_chunks (top-k or top-p, replaces k_row_stats) the same chunks, held in
+//                 registers as order-preserving keys: each workgroup writes the few tokens
+//                 that can be in the row's top-k set (a bound from its per-thread maxima);
+//                 for top-p alone, the chunk's top k_c tokens plus its max and exp-sum.
 //   k_topk_merge  one workgroup per row: exact top-k threshold over the chunks'
-//                 candidates, max, kept count and kept-set sum.
+//                 candidates, then the nucleus boundary (top-p) from fixed-point mass
+//                 histograms, max, kept count and kept-set sum; rows the candidates do not
+//                 cover take full passes over the row.
 //   k_decide      one workgroup per request: combines the row partials in fp64, evaluates
 //                 p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p left to right,
 //                 finds the first rejection, publishes the accepted tokens and stores the
