@@ -41,6 +41,9 @@ def parse():
                    help="override the workload's top_k (0 = off)")
     p.add_argument("--top-p", type=float, default=1.0,
                    help="nucleus mass after temperature and top-k (<= 0 or >= 1 = off)")
+    p.add_argument("--per-request", action="store_true",
+                   help="pass the transform as per-request arrays (same values for every "
+                        "request): measures the per-request path")
     p.add_argument("--schedule", choices=["fused", "serial", "overlap"], default="fused",
                    help="fused: specdec_cycle (allocation inside the logit-streaming launch, "
                         "K/V scatter beside the sampling workgroups); serial: append, verify, "
@@ -150,9 +153,19 @@ def main():
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-    ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k, top_p),
+    pr = {}
+    if args.per_request:
+        pr["temperatures"] = torch.full((B,), vin.T, dtype=torch.float32, device=d)
+        if 0 < vin.top_k < V:
+            pr["top_ks"] = torch.full((B,), vin.top_k, dtype=torch.int32, device=d)
+            pr["top_k_max"] = vin.top_k
+        if 0.0 < top_p < 1.0:
+            pr["top_ps"] = torch.full((B,), top_p, dtype=torch.float32, device=d)
+    prm = binding._params(B, d, pr.get("temperatures"), pr.get("top_ks"), pr.get("top_ps"),
+                          pr.get("top_k_max"))
+    ws = torch.empty(binding.specdec_verify_workspace_size(B, K, V, dt, vin.top_k, top_p, prm),
                      dtype=torch.uint8, device=d)
-    cws = torch.empty(binding.specdec_cycle_workspace_size(B, K, V, dt, vin.top_k, top_p),
+    cws = torch.empty(binding.specdec_cycle_workspace_size(B, K, V, dt, vin.top_k, top_p, prm),
                       dtype=torch.uint8, device=d)
     kws = torch.empty(binding.kv_paged_append_workspace_size(B, K + B), dtype=torch.uint8, device=d)
     n = args.warmup + args.steps
@@ -171,20 +184,20 @@ def main():
             binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
                                   max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
                                   out_tokens=out, num_accepted=nacc, num_emitted=nemit,
-                                  err_word=err, workspace=cws, debug=dbg, top_p=top_p)
+                                  err_word=err, workspace=cws, debug=dbg, top_p=top_p, **pr)
             return
         if args.schedule == "serial":
             binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
                                    temperature=vin.T, top_k=vin.top_k, out_tokens=out,
                                    num_accepted=nacc, num_emitted=nemit, err_word=err,
-                                   workspace=ws, debug=dbg, top_p=top_p)
+                                   workspace=ws, debug=dbg, top_p=top_p, **pr)
         else:
             dbg.ev_stats_done = ev_stats[i].handle
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
                                    temperature=vin.T, top_k=vin.top_k, out_tokens=out,
                                    num_accepted=nacc, num_emitted=nemit, err_word=err,
-                                   workspace=ws, debug=dbg, top_p=top_p)
+                                   workspace=ws, debug=dbg, top_p=top_p, **pr)
             ev_stats[i].wait_on(side_s)
             with torch.cuda.stream(side_s):
                 binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
@@ -228,7 +241,7 @@ def main():
     # top_k above 1024 runs the multi-pass select inside the merge launch: no launch
     # streams the rows once
     generic = 0 < vin.top_k < V and vin.top_k > 1024
-    if filtered:      # the first launch holds the rows as keys and gathers candidates
+    if filtered or args.per_request:   # the chunk launch streams the rows
         stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
     else:
         stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
@@ -247,7 +260,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": (f"{wl.name}: B={B} k={'U{%d..%d}' % wl.k_range if wl.k_range else wl.k} "
                                 f"V={V} {vin.dtype} T={vin.T:g} top_k={vin.top_k}"
-                                + (f" top_p={top_p:g}" if 0.0 < top_p < 1.0 else "") + "; paged KV "
+                                + (f" top_p={top_p:g}" if 0.0 < top_p < 1.0 else "")
+                                + (" (per-request arrays)" if args.per_request else "") + "; paged KV "
                                 f"{kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
                    "global_batch": B, "positions_per_step": K, "parallelism": "single GPU",
                    "schedule": args.schedule},

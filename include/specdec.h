@@ -63,6 +63,9 @@ extern "C" {
 #define SPECDEC_ERR_ZFALLBACK 16   /* flag only: residual mass was 0 after a rejection;
                                       the replacement was drawn from p_i                   */
 #define SPECDEC_ERR_UNIFORM   32   /* a uniform outside [0, 1) (or NaN)                   */
+#define SPECDEC_ERR_PARAM     64   /* per-request parameters invalid: temperature <= 0 or
+                                      not finite, top_p NaN, or an active top_k above
+                                      specdec_params.top_k_max                            */
 
 /* ---- device-side bits of kv_paged_cache.state --------------------------------------- */
 #define KV_ERR_NOMEM       64        /* append needed more blocks than free: not applied   */
@@ -106,11 +109,26 @@ typedef struct specdec_debug {
                                    latency-bound sampling kernel runs                     */
 } specdec_debug;
 
+/* Per-request decoding transform ("Speculative decoding ...", sections 3 and 4: the same
+ * transform on p and q of a request; requests of one batch may differ). Each array holds
+ * B device values and replaces the scalar argument of the same name for every request;
+ * NULL keeps the scalar. A request whose values are invalid fails with SPECDEC_ERR_PARAM
+ * (num_accepted = -1) without affecting the others. Host struct, read during the call. */
+typedef struct specdec_params {
+    const float*   temperature;  /* [B] > 0 and finite                                   */
+    const int32_t* top_k;        /* [B] any value; <= 0 or >= V: off                     */
+    const float*   top_p;        /* [B] not NaN; <= 0 or >= 1: off                       */
+    int32_t        top_k_max;    /* with top_k: the largest active top_k[b] allowed; the
+                                    workspace is sized for it (>= 0; above 1024 those
+                                    rows take the multi-pass select)                    */
+} specdec_params;
+
 /* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned); 0
  * for sizes the call rejects (B < 1, K < 0, V outside [1, SPECDEC_MAX_V], bad dtype,
  * top_p NaN). */
 size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                     int32_t top_k, float top_p);
+                                     int32_t top_k, float top_p,
+                                     const specdec_params* per_request);
 
 /*
  * specdec_verify - one verification step for a batch of B requests.
@@ -148,12 +166,14 @@ size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dt
  * Host scalars: B >= 1, K = cu_draft[B] (the packed row count the caller allocated),
  * 0 <= max_k <= SPECDEC_MAX_K, 1 <= V <= SPECDEC_MAX_V, dtype SPECDEC_F32 or SPECDEC_BF16,
  * temperature > 0 and finite, top_k any value (<= 0 or >= V disables it), top_p any
- * value but NaN (<= 0 or >= 1 disables it). The nucleus mass decision is made with fp32
+ * value but NaN (<= 0 or >= 1 disables it); a scalar that per_request replaces is not
+ * checked. per_request: NULL, or per-request arrays (specdec_params; top_k_max >= 0 when
+ * top_k is given). The nucleus mass decision is made with fp32
  * exponentials summed in fixed point (2^-42 units): a row whose boundary mass lies within
  * about 1e-6 of top_p may keep one group of equal logits more or less than exact
  * arithmetic would.
  * workspace: device, 16-byte aligned, >= specdec_verify_workspace_size(B, K, V, dtype,
- * top_k, top_p) bytes, owned by the caller; its contents need no initialization and are
+ * top_k, top_p, per_request) bytes, owned by the caller; its contents need no initialization and are
  * scratch between calls. Calls that share a workspace must not overlap.
  * Returns SPECDEC_OK once enqueued, or SPECDEC_EINVAL / SPECDEC_EWORKSPACE /
  * SPECDEC_EHIP without enqueuing anything that writes outputs.
@@ -163,6 +183,7 @@ int specdec_verify(const void* target_logits, const void* draft_logits, int32_t 
                    const float* u_accept, const float* u_sample,
                    int32_t B, int32_t K, int32_t max_k, int32_t V,
                    float temperature, int32_t top_k, float top_p,
+                   const specdec_params* per_request,
                    int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                    int32_t* err_word, const specdec_debug* dbg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -261,7 +282,8 @@ int kv_rollback_draft(const kv_paged_cache* cache, int32_t B, const int32_t* num
 /* Bytes of device workspace specdec_cycle needs (16-byte aligned); 0 where
  * specdec_verify_workspace_size gives 0. */
 size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                    int32_t top_k, float top_p);
+                                    int32_t top_k, float top_p,
+                                    const specdec_params* per_request);
 
 /*
  * specdec_cycle - one speculative cycle with the same effect as the three calls
@@ -277,7 +299,8 @@ size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dty
  * calls. The launches are fused so that block allocation overlaps the logit stream and the
  * K/V scatter overlaps the per-request sampling. Arguments and their checks are those of
  * the three calls (B <= SPECDEC_MAX_KV_BATCH); workspace >=
- * specdec_cycle_workspace_size(B, K, V, dtype, top_k, top_p) bytes, 16-byte aligned.
+ * specdec_cycle_workspace_size(B, K, V, dtype, top_k, top_p, per_request) bytes, 16-byte
+ * aligned.
  */
 int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
                   const void* target_logits, const void* draft_logits, int32_t dtype,
@@ -285,6 +308,7 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
                   const float* u_accept, const float* u_sample,
                   int32_t B, int32_t K, int32_t max_k, int32_t V,
                   float temperature, int32_t top_k, float top_p,
+                  const specdec_params* per_request,
                   int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                   int32_t* err_word, const specdec_debug* dbg,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -37,6 +37,10 @@ Readings taken where the pages leave a step open (each is listed in the design n
   top-k); top_p <= 0 or >= 1 leaves the row unchanged.
 * the bonus token is emitted only when all proposals are accepted (section 2, section 6
   "Bad bonus-token logic").
+* temperature, top-k and top-p may differ between the requests of a batch; within a
+  request the same values shape every p_i and q_i. A request whose temperature is not
+  a positive finite number, whose top_p is NaN, or whose active top_k exceeds the
+  caller's declared bound fails (ERR_PARAM) and samples nothing.
 """
 
 from __future__ import annotations
@@ -55,8 +59,9 @@ ERR_NONFINITE = 4      # NaN or +inf logit in a row, or a row with no finite kep
 ERR_QZERO = 8          # flag: q_i(y_i) == 0 at an evaluated position
 ERR_ZFALLBACK = 16     # flag: residual mass 0 after a rejection; drew from p_i instead
 ERR_UNIFORM = 32       # a caller uniform outside [0, 1) or NaN
+ERR_PARAM = 64         # the request's temperature / top_p / top_k is invalid
 
-ERROR_BITS = ERR_TOKEN | ERR_K | ERR_NONFINITE | ERR_UNIFORM
+ERROR_BITS = ERR_TOKEN | ERR_K | ERR_NONFINITE | ERR_UNIFORM | ERR_PARAM
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -268,8 +273,16 @@ def _u_ok(u) -> bool:
     return 0.0 <= u < 1.0
 
 
+def params_ok(T: float, top_k: int, top_p: float, V: int, top_k_max=None) -> bool:
+    """Whether one request's transform parameters are valid."""
+    if not (T > 0.0 and math.isfinite(T)) or math.isnan(top_p):
+        return False
+    return top_k_max is None or not (0 < top_k < V) or top_k <= top_k_max
+
+
 def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: int,
-                   V: int, keep_probs: bool = True, top_p: float = 1.0) -> RequestResult:
+                   V: int, keep_probs: bool = True, top_p: float = 1.0,
+                   top_k_max=None) -> RequestResult:
     """Validate and verify one request from logits (float64 rows). With keep_probs=False
     the normalized rows are dropped from the result once used (large vocabularies)."""
     k = len(tokens)
@@ -278,6 +291,8 @@ def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: 
         err |= ERR_TOKEN
     if not all(_u_ok(u) for u in u_accept) or not _u_ok(u_sample):
         err |= ERR_UNIFORM
+    if not params_ok(T, top_k, top_p, V, top_k_max):
+        return RequestResult(-1, [], err | ERR_PARAM, None)
     rows_t = [transform(t_rows[i], T, top_k, top_p) for i in range(k + 1)]
     rows_d = [transform(d_rows[i], T, top_k, top_p) for i in range(k)]
     if not all(r.valid for r in rows_t) or not all(r.valid for r in rows_d):
@@ -313,21 +328,25 @@ def _decode_rows(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
-                 T: float, top_k: int, max_k: int, dtype: str,
+                 T, top_k, max_k: int, dtype: str,
                  requests: Optional[Sequence[int]] = None,
-                 keep_probs: bool = True, top_p: float = 1.0) -> BatchResult:
+                 keep_probs: bool = True, top_p=1.0, top_k_max=None) -> BatchResult:
     """Batched verification over packed ragged rows.
 
     target: [K+B, V] (fp32 values, or bf16 bit patterns as uint16); the rows of request b
     are cu[b] + b + i for i = 0..k_b. draft: [K, V]; rows cu[b] + i for i < k_b.
+    T, top_k, top_p: one value for every request, or one per request (T and top_p are
+    rounded to fp32). top_k_max: the bound on active per-request top_k values, if any.
     ``requests`` restricts the work to a subset (other entries stay -1 / 0).
     """
     cu = np.asarray(cu_draft, dtype=np.int64)
     B = cu.shape[0] - 1
     K = int(np.asarray(draft_tokens).shape[0])
     V = int(target.shape[1])
-    T = float(np.float32(T))
-    top_p = float(np.float32(top_p))
+    per = lambda x, f: [f(v) for v in np.broadcast_to(np.asarray(x), (B,))]
+    Ts = per(T, lambda v: float(np.float32(v)))
+    ks = per(top_k, int)
+    ps = per(top_p, lambda v: float(np.float32(v)))
     num_acc = np.full(B, -1, dtype=np.int32)
     num_emit = np.zeros(B, dtype=np.int32)
     out = np.full(K + B, -1, dtype=np.int32)
@@ -343,8 +362,8 @@ def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
         t_rows = _decode_rows(target[lo + b: lo + b + k + 1], dtype)
         d_rows = _decode_rows(draft[lo: hi], dtype)
         r = verify_request(t_rows, d_rows, np.asarray(draft_tokens[lo:hi]),
-                           np.asarray(u_accept[lo:hi]), u_sample[b], T, top_k, V, keep_probs,
-                           top_p)
+                           np.asarray(u_accept[lo:hi]), u_sample[b], Ts[b], ks[b], V, keep_probs,
+                           ps[b], top_k_max)
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

@@ -31,6 +31,7 @@ ERR_NONFINITE = 4
 ERR_QZERO = 8
 ERR_ZFALLBACK = 16
 ERR_UNIFORM = 32
+ERR_PARAM = 64
 KV_ERR_NOMEM = 64
 KV_ERR_APPEND = 128
 KV_ERR_ROLLBACK = 256
@@ -65,6 +66,32 @@ class SpecdecDebug(ctypes.Structure):
     ]
 
 
+class SpecdecParams(ctypes.Structure):
+    """Per-request transform arrays (device pointers, or None for the scalar)."""
+    _fields_ = [
+        ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
+        ("top_k_max", ctypes.c_int32),
+    ]
+
+
+def _params(B: int, dev, temperatures, top_ks, top_ps, top_k_max):
+    """SpecdecParams for optional per-request tensors, or None when none is given."""
+    if temperatures is None and top_ks is None and top_ps is None:
+        return None
+    if temperatures is not None:
+        _check(temperatures, "temperatures", torch.float32, B, dev)
+    if top_ks is not None:
+        _check(top_ks, "top_ks", torch.int32, B, dev)
+        if top_k_max is None:
+            raise ValueError("top_k_max is required with top_ks")
+    if top_ps is not None:
+        _check(top_ps, "top_ps", torch.float32, B, dev)
+    return SpecdecParams(_ptr(temperatures) if temperatures is not None else None,
+                         _ptr(top_ks) if top_ks is not None else None,
+                         _ptr(top_ps) if top_ps is not None else None,
+                         int(top_k_max) if top_k_max is not None else 0)
+
+
 class KvPagedCacheStruct(ctypes.Structure):
     _fields_ = [
         ("pool", ctypes.c_void_p),
@@ -93,10 +120,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specdec_status_string.argtypes = [ctypes.c_int]
     lib.specdec_status_string.restype = ctypes.c_char_p
     f32 = ctypes.c_float
-    lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
+    pp = ctypes.POINTER(SpecdecParams)
+    lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32, pp]
     lib.specdec_verify_workspace_size.restype = sz
     lib.specdec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
-                                   f32, i32, f32, vp, vp, vp, vp,
+                                   f32, i32, f32, pp, vp, vp, vp, vp,
                                    ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_verify.restype = ctypes.c_int
     lib.kv_paged_append_workspace_size.argtypes = [i32, i32]
@@ -107,10 +135,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for fn in (lib.kv_rollback, lib.kv_rollback_draft):
         fn.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp]
         fn.restype = ctypes.c_int
-    lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
+    lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32, pp]
     lib.specdec_cycle_workspace_size.restype = sz
     lib.specdec_cycle.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp,
-                                  vp, vp, i32, i32, i32, i32, f32, i32, f32, vp, vp, vp, vp,
+                                  vp, vp, i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_cycle.restype = ctypes.c_int
     _lib = lib
@@ -150,9 +178,14 @@ def _logits_dtype(t: torch.Tensor) -> int:
     raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
 
 
+def _pref(params):
+    return ctypes.byref(params) if params is not None else None
+
+
 def specdec_verify_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int,
-                                  top_p: float = 1.0) -> int:
-    return int(load_library().specdec_verify_workspace_size(B, K, V, dtype, top_k, float(top_p)))
+                                  top_p: float = 1.0, params: Optional[SpecdecParams] = None) -> int:
+    return int(load_library().specdec_verify_workspace_size(B, K, V, dtype, top_k, float(top_p),
+                                                            _pref(params)))
 
 
 def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
@@ -161,8 +194,13 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                    temperature: float, top_k: int, out_tokens: torch.Tensor,
                    num_accepted: torch.Tensor, num_emitted: torch.Tensor,
                    err_word: torch.Tensor, workspace: torch.Tensor,
-                   debug: Optional[SpecdecDebug] = None, top_p: float = 1.0) -> None:
-    """Enqueue one verification step on torch's current stream (shapes as in the header)."""
+                   debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
+                   temperatures: Optional[torch.Tensor] = None,
+                   top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
+                   top_k_max: Optional[int] = None) -> None:
+    """Enqueue one verification step on torch's current stream (shapes as in the header).
+    temperatures / top_ks / top_ps: optional per-request [B] device tensors replacing the
+    scalars (top_k_max bounds the active top_ks)."""
     lib = load_library()
     dev = target_logits.device
     if dev.type != "cuda":
@@ -184,10 +222,11 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     _check(num_emitted, "num_emitted", torch.int32, B, dev)
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
+    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max)
     st = lib.specdec_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(cu_draft),
         _ptr(u_accept), _ptr(u_sample), B, K, max_k, V, float(temperature), int(top_k),
-        float(top_p), _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
+        float(top_p), _pref(prm), _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
         ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
@@ -264,8 +303,9 @@ def kv_rollback(cache: PagedKVCache, num_accepted: torch.Tensor, cu_draft: torch
 
 
 def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int,
-                                 top_p: float = 1.0) -> int:
-    return int(load_library().specdec_cycle_workspace_size(B, K, V, dtype, top_k, float(top_p)))
+                                 top_p: float = 1.0, params: Optional[SpecdecParams] = None) -> int:
+    return int(load_library().specdec_cycle_workspace_size(B, K, V, dtype, top_k, float(top_p),
+                                                           _pref(params)))
 
 
 def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
@@ -275,7 +315,10 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
                   temperature: float, top_k: int, out_tokens: torch.Tensor,
                   num_accepted: torch.Tensor, num_emitted: torch.Tensor,
                   err_word: torch.Tensor, workspace: torch.Tensor,
-                  debug: Optional[SpecdecDebug] = None, top_p: float = 1.0) -> None:
+                  debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
+                  temperatures: Optional[torch.Tensor] = None,
+                  top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
+                  top_k_max: Optional[int] = None) -> None:
     """Enqueue append -> verify -> rollback of one cycle as fused launches."""
     lib = load_library()
     dev = target_logits.device
@@ -302,10 +345,12 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
     _check(num_emitted, "num_emitted", torch.int32, B, dev)
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
+    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max)
     st = lib.specdec_cycle(
         ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
         dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,
-        V, float(temperature), int(top_k), float(top_p), _ptr(out_tokens), _ptr(num_accepted),
+        V, float(temperature), int(top_k), float(top_p), _pref(prm), _ptr(out_tokens),
+        _ptr(num_accepted),
         _ptr(num_emitted), _ptr(err_word), ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:

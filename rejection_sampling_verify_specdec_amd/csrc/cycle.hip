@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
 
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
 
-template <bool BF16, bool VEC, bool P2>
+// P2: 0 top-k, 1 top-p alone, 2 per-request parameters
+template <bool BF16, bool VEC, int P2>
 __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
                                                       int B, int N, uint8_t* __restrict__ aws,
                                                       TopkArgs a) {
@@ -60,12 +61,20 @@ __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __re
         return;
     }
     const int w = blockIdx.x - 1;
-    topk_chunk_body<BF16, VEC, P2>(a, w / a.nchunks, w % a.nchunks);
+    if constexpr (P2 == 2) chunk_pr_body<BF16, VEC>(a, w / a.nchunks, w % a.nchunks);
+    else topk_chunk_body<BF16, VEC, P2>(a, w / a.nchunks, w % a.nchunks,
+                                        ChunkSel{a.top_k, a.c, P2 == 1});
 }
 
-template <bool BF16>
+template <bool BF16, bool PR>
 __global__ __launch_bounds__(kMergeNT) void k_cycle_topk_merge(TopkArgs a) {
-    topk_merge_body<BF16>(a, blockIdx.x);
+    if constexpr (PR) merge_pr_body<BF16>(a, blockIdx.x);
+    else topk_merge_body<BF16>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
+}
+
+__global__ __launch_bounds__(256) void k_cycle_row_params(ParamArgs a, int rows) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < rows) row_params_one(a, r);
 }
 
 static_assert(kDecideNT == kScNT, "decision and scatter workgroups share one launch");
@@ -118,23 +127,31 @@ template <bool BF16, bool VEC>
 static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
                          const uint8_t* tgt, const uint8_t* dft, const int* cu, int B, int K,
                          int V, float top_p, float c, const WsPlan& p, uint8_t* vws, uint8_t* aws,
-                         const SampleArgs& sa, const specdec_debug* dbg, hipStream_t st) {
+                         const SampleArgs& sa, const ParamArgs& pa, const specdec_debug* dbg,
+                         hipStream_t st) {
     const int rows = 2 * K + B;
     const int N = K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
     float* thr = reinterpret_cast<float*>(vws + p.thr);
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (p.filter) {
+    if (p.pr) {
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
+        hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
+                           pa, rows);
+        hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 2>), dim3((unsigned)rows * p.nchunks + 1),
+                              dim3(kTkNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
+        hipLaunchKernelGGL((k_cycle_topk_merge<BF16, true>), dim3(rows), dim3(kMergeNT), 0, st, ta);
+    } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         const unsigned nchunk_wg = ta.generic ? 0u : (unsigned)rows * p.nchunks;
         if (p.topp_mode == 2)
-            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, true>), dim3(nchunk_wg + 1), dim3(kTkNT),
+            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 1>), dim3(nchunk_wg + 1), dim3(kTkNT),
                                   0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
         else
-            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, false>), dim3(nchunk_wg + 1), dim3(kTkNT),
+            hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 0>), dim3(nchunk_wg + 1), dim3(kTkNT),
                                   0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
-        hipLaunchKernelGGL((k_cycle_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, ta);
+        hipLaunchKernelGGL((k_cycle_topk_merge<BF16, false>), dim3(rows), dim3(kMergeNT), 0, st, ta);
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,
@@ -155,11 +172,13 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
 }  // namespace sd
 
 extern "C" size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                               int32_t top_k, float top_p) {
+                                               int32_t top_k, float top_p,
+                                               const specdec_params* per_request) {
     if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) ||
-        top_p != top_p)
+        (top_p != top_p && !(per_request && per_request->top_p)) ||
+        (per_request && per_request->top_k && per_request->top_k_max < 0))
         return 0;
-    return sd::align256(sd::plan_ws(B, K, V, dtype, top_k, top_p).total) +
+    return sd::align256(sd::plan_ws(B, K, V, dtype, top_k, top_p, per_request).total) +
            sd::append_ws_bytes(B, K + B);
 }
 
@@ -168,7 +187,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
                              const int32_t* draft_tokens, const int32_t* cu_draft,
                              const float* u_accept, const float* u_sample, int32_t B, int32_t K,
                              int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                             float top_p, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                             float top_p, const specdec_params* per_request, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                              int32_t* err_word, const specdec_debug* dbg, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
     using namespace sd;
@@ -176,7 +195,11 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
-    if (!(temperature > 0.0f) || !isfinite(temperature) || top_p != top_p) return SPECDEC_EINVAL;
+    const bool pr_t = per_request && per_request->temperature;
+    const bool pr_p = per_request && per_request->top_p;
+    if (!pr_t && (!(temperature > 0.0f) || !isfinite(temperature))) return SPECDEC_EINVAL;
+    if (!pr_p && top_p != top_p) return SPECDEC_EINVAL;
+    if (per_request && per_request->top_k && per_request->top_k_max < 0) return SPECDEC_EINVAL;
     if (!target_logits || !cu_draft || !u_sample || !out_tokens || !num_accepted ||
         !num_emitted || !err_word)
         return SPECDEC_EINVAL;
@@ -185,7 +208,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     if (!geometry_ok(cache) || B > SPECDEC_MAX_KV_BATCH || !k_new || !v_new ||
         ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
         return SPECDEC_EINVAL;
-    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p);
+    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     const size_t vbytes = align256(p.total);
@@ -194,7 +217,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
         return SPECDEC_EWORKSPACE;
 
     const double c64 = 1.4426950408889634074 / (double)temperature;   // log2(e) / T
-    const float c = (float)c64;
+    const float c = pr_t ? 1.0f : (float)c64;
     if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
     const int es = dtype == SPECDEC_BF16 ? 2 : 4;
     const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)target_logits & 15) == 0 &&
@@ -221,6 +244,7 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.nch = p.nch;
     sa.topk = p.filter;
     sa.c = c;
+    sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(vws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
     sa.rec = reinterpret_cast<Decision*>(vws + p.rec);
@@ -235,13 +259,15 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.dbg = dbg ? *dbg : specdec_debug{};
 
     const KvArgs kv = args_of(cache);
+    ParamArgs pa{};
+    if (p.pr) pa = param_args(cu_draft, B, K, V, temperature, top_k, top_p, per_request, p, vws);
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
-        else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
+        if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
+        else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
     } else {
-        if (vec) launch_cycle<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
-        else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, dbg, stream);
+        if (vec) launch_cycle<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
+        else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

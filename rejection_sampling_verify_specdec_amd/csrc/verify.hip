@@ -51,12 +51,29 @@ __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ t
 
 template <bool BF16, bool VEC, bool P2>
 __global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
-    topk_chunk_body<BF16, VEC, P2>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+    topk_chunk_body<BF16, VEC, P2 ? 1 : 0>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks,
+                                          ChunkSel{a.top_k, a.c, P2});
 }
 
 template <bool BF16>
 __global__ __launch_bounds__(kMergeNT) void k_topk_merge(TopkArgs a) {
-    topk_merge_body<BF16>(a, blockIdx.x);
+    topk_merge_body<BF16>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
+}
+
+// per-request parameters: each row's transform, then the chunks and merges that read it
+__global__ __launch_bounds__(256) void k_row_params(ParamArgs a, int rows) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < rows) row_params_one(a, r);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTkNT) void k_chunks_pr(TopkArgs a) {
+    chunk_pr_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kMergeNT) void k_merge_pr(TopkArgs a) {
+    merge_pr_body<BF16>(a, blockIdx.x);
 }
 
 template <bool BF16>
@@ -77,14 +94,21 @@ __global__ __launch_bounds__(kPickNT) void k_pick(SampleArgs a) {
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
                        float top_p, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
-                       const specdec_debug* dbg, hipStream_t st) {
+                       const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st) {
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
     float* thr = reinterpret_cast<float*>(ws + p.thr);
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (p.filter) {
+    if (p.pr) {
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
+        hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,
+                           rows);
+        hipExtLaunchKernelGGL((k_chunks_pr<BF16, VEC>), dim3((unsigned)rows * p.nchunks),
+                              dim3(kTkNT), 0, st, e0, e1, 0, ta);
+        hipLaunchKernelGGL((k_merge_pr<BF16>), dim3(rows), dim3(kMergeNT), 0, st, ta);
+    } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         if (!ta.generic) {
             if (p.topp_mode == 2)
@@ -112,30 +136,36 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
 }  // namespace sd
 
 extern "C" size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V, int32_t dtype,
-                                                int32_t top_k, float top_p) {
+                                                int32_t top_k, float top_p,
+                                                const specdec_params* per_request) {
     if (B < 1 || K < 0 || V < 1 || V > SPECDEC_MAX_V || (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) ||
-        top_p != top_p)
+        (top_p != top_p && !(per_request && per_request->top_p)) ||
+        (per_request && per_request->top_k && per_request->top_k_max < 0))
         return 0;
-    return sd::plan_ws(B, K, V, dtype, top_k, top_p).total;
+    return sd::plan_ws(B, K, V, dtype, top_k, top_p, per_request).total;
 }
 
 extern "C" int specdec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
                               const int32_t* draft_tokens, const int32_t* cu_draft,
                               const float* u_accept, const float* u_sample, int32_t B, int32_t K,
                               int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                              float top_p, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                              float top_p, const specdec_params* per_request, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                               int32_t* err_word, const specdec_debug* dbg, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
     using namespace sd;
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
-    if (!(temperature > 0.0f) || !isfinite(temperature) || top_p != top_p) return SPECDEC_EINVAL;
+    const bool pr_t = per_request && per_request->temperature;
+    const bool pr_p = per_request && per_request->top_p;
+    if (!pr_t && (!(temperature > 0.0f) || !isfinite(temperature))) return SPECDEC_EINVAL;
+    if (!pr_p && top_p != top_p) return SPECDEC_EINVAL;
+    if (per_request && per_request->top_k && per_request->top_k_max < 0) return SPECDEC_EINVAL;
     if (!target_logits || !cu_draft || !u_sample || !out_tokens || !num_accepted ||
         !num_emitted || !err_word)
         return SPECDEC_EINVAL;
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
-    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p);
+    const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
         V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
@@ -143,7 +173,7 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
         return SPECDEC_EWORKSPACE;
 
     const double c64 = 1.4426950408889634074 / (double)temperature;   // log2(e) / T
-    const float c = (float)c64;
+    const float c = pr_t ? 1.0f : (float)c64;
     if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
     const int es = dtype == SPECDEC_BF16 ? 2 : 4;
     const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)target_logits & 15) == 0 &&
@@ -167,6 +197,7 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.nch = p.nch;
     sa.topk = p.filter;
     sa.c = c;
+    sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(ws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
     sa.rec = reinterpret_cast<Decision*>(ws + p.rec);
@@ -184,13 +215,16 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
         sa.dbg = specdec_debug{};
     }
 
+    ParamArgs pa{};
+    if (p.pr) pa = param_args(cu_draft, B, K, V, temperature, top_k, top_p, per_request, p, ws);
+
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
-        else launch_all<true, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
+        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
+        else launch_all<true, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
     } else {
-        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
-        else launch_all<false, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, dbg, stream);
+        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
+        else launch_all<false, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

@@ -344,6 +344,32 @@ struct TopkArgs {
     float top_p;
     RowPartial* cpart;       // mode 2: [rows][nchunks] each chunk's max and exp-sum
     uint32_t* ctc;           // mode 2: [rows][nchunks] each chunk's candidate bound t_c
+    const struct RowParams* rpar;   // per-request parameters: [rows] each row's, else null
+};
+
+// The transform of one row when temperature / top-k / top-p come per request.
+constexpr int kRpMode = 3;         // flags & kRpMode: 0 none, 1 top-k (and maybe top-p),
+                                   // 2 top-p alone
+constexpr int kRpBad = 4;          // the request's parameters are invalid
+constexpr int kRpGeneric = 8;      // the row takes the multi-pass select
+struct alignas(16) RowParams {
+    float c;        // log2(e) / T
+    int k;          // the chunk select's k: top_k (mode 1), k_c (mode 2), 0 (mode 0)
+    float top_p;
+    int flags;
+};
+
+// What one chunk workgroup selects, and what one merge workgroup applies.
+struct ChunkSel {
+    int top_k;      // the chunk's k
+    float c;
+    bool p2;        // also the chunk's max, exp-sum and bound (top-p alone)
+};
+struct RowSel {
+    int top_k;      // exact top-k select when topp_mode != 2
+    int topp_mode;  // 0: no top-p; 1: top-p inside the top-k set; 2: top-p alone
+    float top_p;
+    float c;
 };
 
 // Candidates per row gathered for a top-p row without top-k: the nucleus comes from them
@@ -434,10 +460,12 @@ SD_DEV void hist_select(const unsigned* hist, int* dig, int* krem) {
     }
 }
 
-// P2: top-p without top-k; the chunk also writes its max and exp-sum (cpart) and its bound
-// t_c (ctc), from which the merge knows the row's exp-sum and which candidates are complete.
-template <bool BF16, bool VEC, bool P2>
-SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
+// P2 (top-p without top-k; 0 never, 1 always, 2 as sel.p2 says): the chunk also writes its
+// max and exp-sum (cpart) and its bound t_c (ctc), from which the merge knows the row's
+// exp-sum and which candidates are complete.
+template <bool BF16, bool VEC, int P2>
+SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk, const ChunkSel& sel) {
+    const bool p2 = P2 == 2 ? sel.p2 : P2 == 1;
     constexpr int NT = kTkNT;
     constexpr int NR = kTkRegs;
     constexpr int EPR = BF16 ? 2 : 1;                 // elements per register
@@ -511,8 +539,8 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     // 2. t_c: every wave takes the ceil(top_k / 4)-th largest of its per-thread (or, when
     //    top_k > 256, per-group) max keys; t_c = the smallest of the four, so each wave, and
     //    the chunk, holds at least top_k elements >= t_c. Upper 16 key bits for fp32.
-    const bool groups = a.top_k > NT;
-    const int mth = (a.top_k + kTkWaves - 1) / kTkWaves;
+    const bool groups = sel.top_k > NT;
+    const int mth = (sel.top_k + kTkWaves - 1) / kTkWaves;
     uint32_t tv[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) tv[g] = BF16 ? gm[g] : gm[g] >> 16;
@@ -534,15 +562,15 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
         else krem -= n;
     }
     if (lane == 0) s_tw[wv] = tw;
-    if constexpr (P2) {
+    if (P2 != 0 && p2) {
         // top-p without top-k also needs the row's exp-sum: each wave sums exp2((z - m_w) c)
         // over its elements with its own max m_w; thread 0 combines the four in fp64
         const uint32_t wk = uint32_t(wave_max_i(int(kmax ^ 0x80000000u))) ^ 0x80000000u;
         const float mw = key_to_float<BF16>(BF16 ? (wk & 0xffffu) : wk);
         double sw = 0.0;
         if (mw > -INFINITY && !wbad) {
-            const float mc = mw * a.c;
-            const float emc = fmaf(mw, a.c, -mc);
+            const float mc = mw * sel.c;
+            const float emc = fmaf(mw, sel.c, -mc);
             // fp32 trees of 16 (8) terms per register group, then across the groups
             float gs[4];
 #pragma unroll
@@ -554,7 +582,7 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
                     for (int h = 0; h < EPR; ++h) {
                         const uint32_t k = (r[g * (NR / 4) + w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
                         e[w * EPR + h] =
-                            __builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), a.c, -mc));
+                            __builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), sel.c, -mc));
                     }
                 gs[g] = tree_sum(e);
             }
@@ -569,14 +597,14 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk) {
     uint32_t t0 = min(min(s_tw[0], s_tw[1]), min(s_tw[2], s_tw[3]));
     if constexpr (!BF16) t0 <<= 16;
     if (t0 == Kt::KEY_PZERO) t0 = Kt::KEY_NZERO;
-    if (P2 && tid == 0) {
+    if (P2 != 0 && p2 && tid == 0) {
         float mcx = s_mw[0];
         for (int i = 1; i < kTkWaves; ++i) mcx = fmaxf(mcx, s_mw[i]);
         double sc = 0.0;
         if (mcx > -INFINITY)
             for (int i = 0; i < kTkWaves; ++i)
                 if (s_mw[i] > -INFINITY)
-                    sc += s_sw[i] * exp2(((double)s_mw[i] - (double)mcx) * (double)a.c);
+                    sc += s_sw[i] * exp2(((double)s_mw[i] - (double)mcx) * (double)sel.c);
         RowPartial rp;
         rp.m = mcx;
         rp.nkept = 0;
@@ -709,16 +737,16 @@ SD_DEV bool nucleus_key(Each each, uint32_t lo, float c, float mc, double frac, 
 constexpr int kToppRowDigit = 10;
 constexpr int kToppRowBins = 1024;
 template <bool BF16, int NT>
-SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
-                           unsigned long long* h64) {
+SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo, float c,
+                           float top_p, unsigned long long* h64) {
     using Kt = TopkKeys<BF16>;
     constexpr int ES = BF16 ? 2 : 4;
     __shared__ double redd[NT / kWave];
     __shared__ int redi[NT / kWave];
     const int tid = threadIdx.x;
     const uint8_t* base = row_ptr(a.tgt, a.dft, a.rows_t, row, a.V, ES);
-    const float mc = m * a.c;
-    const float emc = fmaf(m, a.c, -mc);
+    const float mc = m * c;
+    const float emc = fmaf(m, c, -mc);
     auto keyz = [](float z) {                    // canonical key of a logit (-0 as +0)
         const uint32_t k = BF16 ? f2key(z) >> 16 : f2key(z);
         return k == Kt::KEY_NZERO ? Kt::KEY_PZERO : k;
@@ -731,13 +759,13 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
                 if (z > -INFINITY) f(keyz(z), z);
             });
         },
-        lo, a.c, mc, (double)a.top_p, 0.0, h64, &K);
+        lo, c, mc, (double)top_p, 0.0, h64, &K);
     const float thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
     float acc = 0.f;
     int kept = 0;
     walk_row<BF16, NT, 4>(base, a.V, [&](float z) {
         if (z >= thr && z > -INFINITY) {
-            acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
+            acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
             ++kept;
         }
     });
@@ -754,7 +782,7 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo,
 }
 
 template <bool BF16>
-SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
+SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
     constexpr int NT = kMergeNT;
     constexpr int LPT = kTkMaxChunks / NT;              // lists per thread at most
     constexpr int UNR = 8;                              // candidate loads in flight per thread
@@ -791,7 +819,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     }
     if (a.generic) mine = kMergeCap + 1;
     if (tid == 0) {
-        s_krem = a.top_k;
+        s_krem = sel.top_k;
         s_kmax = 0u;
         s_nk = 0;
     }
@@ -800,9 +828,9 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     if (total > kMergeCap) {
         if (listed && tid == 0) a.kn[row] = -1;
         // generic select (all of the row's finite tokens for top-p alone), then the nucleus
-        topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, a.topp_mode == 2 ? a.V : a.top_k,
-                                 a.c, a.part, a.row_thr, row);
-        if (a.topp_mode) {
+        topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, sel.topp_mode == 2 ? a.V : sel.top_k,
+                                 sel.c, a.part, a.row_thr, row);
+        if (sel.topp_mode) {
             // the row max and validity as the select left them (tid 0 wrote them)
             if (tid == 0) {
                 const RowPartial rp = a.part[row];
@@ -815,8 +843,8 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
             const float rm = (float)redd[0], tk = (float)redd[1];
             __syncthreads();
             if (run)
-                topp_rows_body<BF16, NT>(a, row, rm, a.topp_mode == 1 ? tk : -INFINITY,
-                                         reinterpret_cast<unsigned long long*>(keys));
+                topp_rows_body<BF16, NT>(a, row, rm, sel.topp_mode == 1 ? tk : -INFINITY, sel.c,
+                                         sel.top_p, reinterpret_cast<unsigned long long*>(keys));
         }
         return;
     }
@@ -868,7 +896,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
     // exact top_k-th largest candidate key, one 8-bit digit at a time (no top-k: none)
     uint32_t prefix = 0u;
 #pragma unroll
-    for (int shift = Kt::KBITS - 8; shift >= 0 && a.topp_mode != 2; shift -= 8) {
+    for (int shift = Kt::KBITS - 8; shift >= 0 && sel.topp_mode != 2; shift -= 8) {
         const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
         for (int i = tid; i < 256; i += NT) hist[i] = 0u;
         __syncthreads();
@@ -881,20 +909,20 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
         __syncthreads();
         prefix |= (uint32_t)s_dig << shift;
     }
-    float thr = a.topp_mode == 2 ? -INFINITY : key_to_float<BF16>(prefix);
+    float thr = sel.topp_mode == 2 ? -INFINITY : key_to_float<BF16>(prefix);
     const float m = key_to_float<BF16>(s_kmax);
-    const float mc = m * a.c;
-    const float emc = fmaf(m, a.c, -mc);
-    if (a.topp_mode && m > -INFINITY) {
+    const float mc = m * sel.c;
+    const float emc = fmaf(m, sel.c, -mc);
+    if (sel.topp_mode && m > -INFINITY) {
         // top-p: the nucleus boundary among the candidates (-0 ranks with +0, as the float
         // comparisons do)
         auto canon = [](uint32_t k) { return k == Kt::KEY_NZERO ? Kt::KEY_PZERO : k; };
         uint32_t lo;
         double frac = 0.0, need = 0.0;
-        if (a.topp_mode == 1) {
+        if (sel.topp_mode == 1) {
             // with top-k: the kept set is every candidate >= the top-k threshold
             lo = max(canon(prefix), Kt::KEY_NINF + 1u);
-            frac = (double)a.top_p;
+            frac = (double)sel.top_p;
         } else {
             // no top-k: the row's exp-sum from the chunk partials; the candidates hold the
             // complete upper set above every chunk's bound t_c
@@ -906,7 +934,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
                 if (l < nl) {
                     const RowPartial cp = a.cpart[(size_t)row * nl + l];
                     if (cp.m > -INFINITY)
-                        sp += cp.s * exp2(((double)cp.m - (double)m) * (double)a.c);
+                        sp += cp.s * exp2(((double)cp.m - (double)m) * (double)sel.c);
                     tg = max(tg, a.ctc[(size_t)row * nl + l]);
                 }
             }
@@ -914,7 +942,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
             tg = uint32_t(block_max_i<NT>(int(tg ^ 0x80000000u), redi)) ^ 0x80000000u;
             lo = (tg == Kt::KEY_PZERO || tg == Kt::KEY_NZERO) ? Kt::KEY_PZERO + 1u : canon(tg);
             lo = max(lo, Kt::KEY_NINF + 1u);
-            need = (double)a.top_p * S * exp2((double)emc) * kMassFix;
+            need = (double)sel.top_p * S * exp2((double)emc) * kMassFix;
         }
         unsigned long long* h64 = reinterpret_cast<unsigned long long*>(s_u32);
         uint32_t K = lo;
@@ -925,12 +953,12 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
                     f(k, key_to_float<BF16>(k));
                 }
             },
-            lo, a.c, mc, frac, need, h64, &K);
-        if (!ok && a.topp_mode == 2) {
+            lo, sel.c, mc, frac, need, h64, &K);
+        if (!ok && sel.topp_mode == 2) {
             // the nucleus reaches below the candidates: full passes over the row
             if (listed && tid == 0) a.kn[row] = -1;
             __syncthreads();
-            topp_rows_body<BF16, NT>(a, row, m, -INFINITY,
+            topp_rows_body<BF16, NT>(a, row, m, -INFINITY, sel.c, sel.top_p,
                                      reinterpret_cast<unsigned long long*>(keys));
             return;
         }
@@ -943,7 +971,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row) {
         const uint32_t k = key_of(keys[i]);
         const float z = key_to_float<BF16>(k);
         if (z >= thr && z > -INFINITY) {
-            acc += __builtin_amdgcn_exp2f(fmaf(z, a.c, -mc));
+            acc += __builtin_amdgcn_exp2f(fmaf(z, sel.c, -mc));
             ++kept;
             if (listed) {
                 const int pos = atomicAdd(&s_nk, 1);
@@ -1020,7 +1048,8 @@ struct Decision {
     float mc_t, mc_d, thr_t, thr_d;
     double al_t, al_d;
     float u;
-    int pad2, pad3, pad4;
+    float c;                 // log2(e) / T of the request
+    int pad3, pad4;
 };
 
 struct SampleArgs {
@@ -1035,6 +1064,7 @@ struct SampleArgs {
     int topk;                // 1 when rows carry a top-k threshold
     int nch;                 // sampling chunks per row
     float c;
+    const RowParams* rpar;   // per-request parameters: [rows] each row's, else null
     const RowPartial* part;
     const float* row_thr;
     Decision* rec;           // [B] each request's decision, for the draw
@@ -1120,7 +1150,6 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
     __shared__ int s_rowbad;
     const int tid = threadIdx.x, lane = tid % kWave;
     const int rows_t = a.K + a.B;
-    const double cd = (double)a.c;
 
     const int lo = a.cu[b], hi = a.cu[b + 1];
     const int k = hi - lo;
@@ -1140,6 +1169,15 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         __syncthreads();
         return;
     }
+    // the request's temperature (and whether its parameters are valid)
+    float cf = a.c;
+    int pbad = 0;
+    if (a.rpar) {
+        const RowParams rq = a.rpar[lo + b];
+        cf = rq.c;
+        pbad = rq.flags & kRpBad;
+    }
+    const double cd = (double)cf;
     if (tid == 0) s_rowbad = 0;
     __syncthreads();
     const int nrows = 2 * k + 1;   // <= kMaxRows <= NT
@@ -1210,13 +1248,16 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         }
         const double us = (double)a.u_smp[b];
         if (lane == 0 && !(us >= 0.0 && us < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-        if (lane == 0 && s_rowbad) flags |= SPECDEC_ERR_NONFINITE;
+        if (lane == 0 && s_rowbad && !pbad) flags |= SPECDEC_ERR_NONFINITE;
+        if (lane == 0 && pbad) flags |= SPECDEC_ERR_PARAM;
         const unsigned long long rej = __ballot(lane < k && !acc);
         const int j = rej ? (__ffsll((long long)rej) - 1) : k;
-        if (lane < k && lane <= j && Q == 0.0 && !(flags & SPECDEC_ERR_TOKEN)) flags |= SPECDEC_ERR_QZERO;
+        if (lane < k && lane <= j && Q == 0.0 && !(flags & SPECDEC_ERR_TOKEN) && !pbad)
+            flags |= SPECDEC_ERR_QZERO;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
-        const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE)) != 0;
+        const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE |
+                                   SPECDEC_ERR_PARAM)) != 0;
         if (publish) {
             if (lane < k) {
                 if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
@@ -1236,18 +1277,19 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
             d.err = err;
             d.a = j;
             d.k = k;
-            d.pad = d.pad2 = d.pad3 = d.pad4 = 0;
+            d.pad = d.pad3 = d.pad4 = 0;
+            d.c = cf;
             d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
             d.row_t = lo + b + j;
             d.row_d = j < k ? lo + j : 0;
             const float mt = s_m[j];
-            d.mc_t = mt * a.c;
-            d.al_t = exp2(-(double)fmaf(mt, a.c, -d.mc_t)) / s_S[j];
+            d.mc_t = mt * cf;
+            d.al_t = exp2(-(double)fmaf(mt, cf, -d.mc_t)) / s_S[j];
             d.thr_t = s_thr[j];
             if (j < k) {
                 const float md = s_m[k + 1 + j];
-                d.mc_d = md * a.c;
-                d.al_d = exp2(-(double)fmaf(md, a.c, -d.mc_d)) / s_S[k + 1 + j];
+                d.mc_d = md * cf;
+                d.al_d = exp2(-(double)fmaf(md, cf, -d.mc_d)) / s_S[k + 1 + j];
                 d.thr_d = s_thr[k + 1 + j];
             } else {
                 d.mc_d = 0.f;
@@ -1397,7 +1439,7 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
     double run = 0.0, W;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, a.c, resid) : 0.0;
+        w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, r.c, resid) : 0.0;
         run += w[e];
     }
     double C = block_excl_scan_d<NT>(run, redd, &W);
@@ -1408,7 +1450,7 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
         run = 0.0;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, a.c, false) : 0.0;
+            w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, r.c, false) : 0.0;
             run += w[e];
         }
         C = block_excl_scan_d<NT>(run, redd, &W);
@@ -1466,7 +1508,7 @@ SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
     const bool resid = r.mode == MODE_RESID;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
-    chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, chunk, r, a.c, resid, a.topk != 0, red,
+    chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, chunk, r, r.c, resid, a.topk != 0, red,
                                      a.wsum + ((size_t)b * a.nch + chunk) * kSSub);
 }
 
@@ -1507,7 +1549,7 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
         for (int q = 0; q < nch; ++q)
-            chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, q, r, a.c, false, a.topk != 0, red,
+            chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, q, r, r.c, false, a.topk != 0, red,
                                              s_cs + q * kSSub);
         if (tid == 0) {
             double W = 0.0;
@@ -1544,7 +1586,7 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     double run = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, a.c, resid);
+        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, r.c, resid);
         run += w[e];
     }
     double tot;
@@ -1580,14 +1622,141 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Per-request transform parameters. The row's request: for a target row r the b with
+// cu[b] + b <= r < cu[b+1] + b + 1, for a draft row r' the b with cu[b] <= r' < cu[b+1]
+// (a binary search over cu; a malformed cu is reported by the decision, the b found here
+// only picks parameters). A request with invalid parameters gets c = 1 and no filter, so
+// its rows are processed harmlessly, and the decision fails it with SPECDEC_ERR_PARAM.
+// ---------------------------------------------------------------------------------------
+struct ParamArgs {
+    const int* cu;
+    int B, K, V;
+    const float* temp;       // [B] or null: the scalar T for every request
+    const int* topk;         // [B] or null
+    const float* topp;       // [B] or null
+    float T;
+    int top_k;
+    float top_p;
+    int top_k_max;           // requests with an active top_k above it fail
+    int kc;                  // the chunk k of a top-p-alone row
+    RowParams* out;          // [2K+B]
+};
+
+SD_DEV void row_params_one(const ParamArgs& a, int r) {
+    const int rows_t = a.K + a.B;
+    const bool tgt = r < rows_t;
+    const int x = tgt ? r : r - rows_t;
+    int lo = 0, hi = a.B;                       // largest b with start(b) <= x
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.cu[mid] + (tgt ? mid : 0) <= x) lo = mid;
+        else hi = mid;
+    }
+    const int b = lo;
+    const float T = a.temp ? a.temp[b] : a.T;
+    const int k = a.topk ? a.topk[b] : a.top_k;
+    const float tp = a.topp ? a.topp[b] : a.top_p;
+    const bool kon = k > 0 && k < a.V;
+    const bool pon = tp > 0.0f && tp < 1.0f;
+    const float c = (float)(1.4426950408889634074 / (double)T);   // log2(e) / T
+    const bool bad = !(T > 0.0f) || !isfinite(T) || !(c > 0.0f) || !isfinite(c) || tp != tp ||
+                     (kon && k > a.top_k_max);
+    RowParams rp;
+    if (bad) {
+        rp.c = 1.0f;
+        rp.k = 0;
+        rp.top_p = 1.0f;
+        rp.flags = kRpBad;
+    } else {
+        const int mode = kon ? 1 : (pon ? 2 : 0);
+        rp.c = c;
+        rp.k = mode == 1 ? k : (mode == 2 ? a.kc : 0);
+        rp.top_p = pon ? tp : 1.0f;
+        const bool generic = (mode == 1 && k > kTkMaxK) || (mode == 2 && a.kc >= a.V);
+        rp.flags = mode | (generic ? kRpGeneric : 0);
+    }
+    a.out[r] = rp;
+}
+
+// One chunk of one row under per-request parameters: plain statistics into cpart for an
+// unfiltered row, the candidate select otherwise (nothing for a row that takes the
+// multi-pass select).
+template <bool BF16, bool VEC>
+SD_DEV void chunk_pr_body(const TopkArgs& a, int row, int chunk) {
+    const RowParams rp = a.rpar[row];
+    const int mode = rp.flags & kRpMode;
+    const size_t ci = (size_t)row * a.nchunks + chunk;
+    if (mode == 0) {
+        row_stats_body<BF16, VEC>(a.tgt, a.dft, a.rows_t, a.V, a.nchunks, rp.c, a.cpart, (int)ci);
+        if (threadIdx.x == 0) a.cnt[ci] = 0;
+        return;
+    }
+    if (rp.flags & kRpGeneric) {
+        if (threadIdx.x == 0) a.cnt[ci] = kTkWaves * a.wcap + 1;
+        return;
+    }
+    topk_chunk_body<BF16, VEC, 2>(a, row, chunk, ChunkSel{rp.k, rp.c, mode == 2});
+}
+
+// The merge of one row under per-request parameters; an unfiltered row combines its chunk
+// statistics (max, then the exp-sums rescaled to it in fp64, fixed order).
+template <bool BF16>
+SD_DEV void merge_pr_body(const TopkArgs& a, int row) {
+    constexpr int NT = kMergeNT;
+    constexpr int LPT = kTkMaxChunks / NT;
+    const RowParams rp = a.rpar[row];
+    const int mode = rp.flags & kRpMode;
+    if (mode != 0) {
+        topk_merge_body<BF16>(a, row, RowSel{rp.k, mode == 2 ? 2 : (rp.top_p < 1.0f ? 1 : 0),
+                                             rp.top_p, rp.c});
+        return;
+    }
+    __shared__ float redf[NT / kWave];
+    __shared__ double redd[NT / kWave];
+    const int tid = threadIdx.x;
+    const int nl = a.nchunks;
+    RowPartial cp[LPT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+        const int l = tid * LPT + q;
+        cp[q] = l < nl ? a.cpart[(size_t)row * nl + l] : RowPartial{-INFINITY, 0, 0.0};
+        mx = fmaxf(mx, cp[q].m);
+    }
+    const float m = block_max<NT>(mx, redf);
+    double sp = 0.0;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q)   // chunks with no finite entry carry 0 (or NaN)
+        sp += cp[q].m == -INFINITY ? cp[q].s
+                                   : cp[q].s * exp2(((double)cp[q].m - (double)m) * (double)rp.c);
+    const double S = block_sum<NT>(sp, redd);
+    if (tid == 0) {
+        RowPartial out;
+        out.m = m;
+        out.nkept = -1;
+        out.s = S;
+        a.part[row] = out;
+        a.row_thr[row] = -INFINITY;
+        if (BF16 && a.kn && row < a.rows_t) a.kn[row] = -1;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------------------
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc, total;
+    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc, rpar,
+        total;
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
+    int pr;                  // per-request parameters: every row through the chunk select
+    int kc;                  // the chunk k of a top-p-alone row
 };
+
+static inline bool per_request(const specdec_params* pr) {
+    return pr && (pr->temperature || pr->top_k || pr->top_p);
+}
 
 static inline bool topk_active(int top_k, int V) { return top_k > 0 && top_k < V; }
 static inline bool topp_active(float top_p) { return top_p > 0.0f && top_p < 1.0f; }
@@ -1614,15 +1783,30 @@ static inline bool select_generic(int top_k, float top_p, int V, int nchunks) {
     return topk_generic(k) || k >= V;
 }
 
-static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float top_p) {
+static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float top_p,
+                             const specdec_params* prm) {
     WsPlan p{};
     // the vector and scalar layouts use the same chunk length
     const int ch = dtype == SPECDEC_BF16 ? Layout<true, true>::CH : Layout<false, true>::CH;
     p.nchunks = (V + ch - 1) / ch;
-    p.filter = filter_active(top_k, top_p, V);
-    p.topp_mode = topp_mode(top_k, top_p, V);
-    p.sel_k = select_k(top_k, top_p, V, p.nchunks);
-    p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
+    p.kc = select_k(0, 0.5f, V, p.nchunks);
+    p.pr = per_request(prm);
+    if (p.pr) {
+        // lists sized for the largest chunk k any row may use
+        int kmax = 0;
+        if (prm->top_k) kmax = prm->top_k_max < kTkMaxK ? prm->top_k_max : kTkMaxK;
+        else if (topk_active(top_k, V) && !topk_generic(top_k)) kmax = top_k;
+        if (prm->top_p || topp_active(top_p)) kmax = kmax > p.kc ? kmax : p.kc;
+        p.filter = 1;
+        p.topp_mode = -1;               // per row
+        p.sel_k = kmax > 0 ? kmax : 1;
+        p.sel_generic = 0;
+    } else {
+        p.filter = filter_active(top_k, top_p, V);
+        p.topp_mode = topp_mode(top_k, top_p, V);
+        p.sel_k = select_k(top_k, top_p, V, p.nchunks);
+        p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
+    }
     p.nparts = p.filter ? 1 : p.nchunks;
     const size_t rows = (size_t)2 * K + B;
     size_t off = 0;
@@ -1642,7 +1826,7 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         off = align256(off + lists * sizeof(int));
         p.tk_cand = off;
         off = align256(off + lists * (size_t)topk_cstride(p.tk_wcap) * sizeof(uint32_t));
-        if (p.topp_mode == 2) {            // per-chunk max / exp-sum and bound
+        if (p.topp_mode == 2 || p.pr) {    // per-chunk max / exp-sum and bound
             p.tk_cpart = off;
             off = align256(off + lists * sizeof(RowPartial));
             p.tk_ctc = off;
@@ -1659,8 +1843,30 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
             off = align256(off + rows_t * kKeptCap * sizeof(uint16_t));
         }
     }
+    p.rpar = off;
+    if (p.pr) off = align256(off + rows * sizeof(RowParams));
     p.total = off;
     return p;
+}
+
+static inline ParamArgs param_args(const int* cu, int B, int K, int V, float T, int top_k,
+                                   float top_p, const specdec_params* prm, const WsPlan& p,
+                                   uint8_t* ws) {
+    ParamArgs a;
+    a.cu = cu;
+    a.B = B;
+    a.K = K;
+    a.V = V;
+    a.temp = prm->temperature;
+    a.topk = prm->top_k;
+    a.topp = prm->top_p;
+    a.T = T;
+    a.top_k = top_k;
+    a.top_p = top_p;
+    a.top_k_max = prm->top_k ? prm->top_k_max : top_k;
+    a.kc = p.kc;
+    a.out = reinterpret_cast<RowParams*>(ws + p.rpar);
+    return a;
 }
 
 static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int rows_t, int V,
@@ -1685,8 +1891,10 @@ static inline TopkArgs topk_args(const uint8_t* tgt, const uint8_t* dft, int row
     a.row_thr = reinterpret_cast<float*>(ws + p.thr);
     a.topp_mode = p.topp_mode;
     a.top_p = top_p;
-    a.cpart = p.topp_mode == 2 ? reinterpret_cast<RowPartial*>(ws + p.tk_cpart) : nullptr;
-    a.ctc = p.topp_mode == 2 ? reinterpret_cast<uint32_t*>(ws + p.tk_ctc) : nullptr;
+    const bool parts = p.topp_mode == 2 || p.pr;
+    a.cpart = parts ? reinterpret_cast<RowPartial*>(ws + p.tk_cpart) : nullptr;
+    a.ctc = parts ? reinterpret_cast<uint32_t*>(ws + p.tk_ctc) : nullptr;
+    a.rpar = p.pr ? reinterpret_cast<const RowParams*>(ws + p.rpar) : nullptr;
     return a;
 }
 

@@ -68,12 +68,19 @@ class VerifyOnDevice:
     """Inputs of one verification batch resident on the GPU, plus outputs and workspace."""
 
     def __init__(self, vin: VerifyInputs, device=None, max_k: Optional[int] = None,
-                 top_k: Optional[int] = None, T: Optional[float] = None, top_p: float = 1.0):
+                 top_k: Optional[int] = None, T: Optional[float] = None, top_p: float = 1.0,
+                 temps=None, top_ks=None, top_ps=None, top_k_max: Optional[int] = None):
         d = device or dev()
         self.vin = vin
         self.max_k = vin.max_k if max_k is None else max_k
         self.top_k = vin.top_k if top_k is None else top_k
         self.top_p = top_p
+        # optional per-request [B] arrays replacing the scalars
+        f32 = lambda x: None if x is None else torch.tensor(np.asarray(x, np.float32), device=d)
+        self.temps, self.top_ps = f32(temps), f32(top_ps)
+        self.top_ks = None if top_ks is None else torch.tensor(np.asarray(top_ks, np.int32), device=d)
+        self.top_k_max = top_k_max
+        self.params = binding._params(vin.B, d, self.temps, self.top_ks, self.top_ps, top_k_max)
         self.T = vin.T if T is None else T
         self.tgt = _logits_t(vin.target, vin.dtype, d)
         self.dft = _logits_t(vin.draft.reshape(vin.K, vin.V), vin.dtype, d)
@@ -88,7 +95,8 @@ class VerifyOnDevice:
         self.num_emit = torch.full((B,), -9, dtype=torch.int32, device=d)
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
         dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-        ws = binding.specdec_verify_workspace_size(B, K, vin.V, dt, self.top_k, self.top_p)
+        ws = binding.specdec_verify_workspace_size(B, K, vin.V, dt, self.top_k, self.top_p,
+                                                   self.params)
         self.ws = torch.empty(ws, dtype=torch.uint8, device=d)
         self.p_y = torch.full((max(K, 1),), -1.0, dtype=torch.float64, device=d)
         self.q_y = torch.full((max(K, 1),), -1.0, dtype=torch.float64, device=d)
@@ -111,7 +119,8 @@ class VerifyOnDevice:
             max_k=self.max_k, temperature=self.T, top_k=self.top_k,
             out_tokens=self.out_tokens, num_accepted=self.num_acc, num_emitted=self.num_emit,
             err_word=self.err, workspace=self.ws, debug=self.dbg if debug else None,
-            top_p=self.top_p)
+            top_p=self.top_p, temperatures=self.temps, top_ks=self.top_ks, top_ps=self.top_ps,
+            top_k_max=self.top_k_max)
 
     def result(self) -> GpuVerify:
         torch.cuda.synchronize()
@@ -128,12 +137,14 @@ def run_verify(vin: VerifyInputs, **kw) -> GpuVerify:
 
 
 def oracle_verify(vin: VerifyInputs, requests=None, keep_probs=False, max_k=None, top_k=None,
-                  T=None, top_p: float = 1.0):
+                  T=None, top_p=1.0, top_k_max=None):
+    """T, top_k, top_p: scalars or per-request arrays."""
     return oracle.verify_batch(vin.target, vin.draft, vin.draft_tokens, vin.cu_draft,
                                vin.u_accept, vin.u_sample, vin.T if T is None else T,
                                vin.top_k if top_k is None else top_k,
                                vin.max_k if max_k is None else max_k, vin.dtype,
-                               requests=requests, keep_probs=keep_probs, top_p=top_p)
+                               requests=requests, keep_probs=keep_probs, top_p=top_p,
+                               top_k_max=top_k_max)
 
 
 @dataclass
@@ -191,13 +202,17 @@ def _resample(vin: VerifyInputs, b: int, a: int, T: float, top_k: int, top_p: fl
 
 
 def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, top_k=None,
-                   check_debug: bool = True, top_p: float = 1.0) -> Report:
-    T = vin.T if T is None else T
-    top_k = vin.top_k if top_k is None else top_k
-    rep = Report()
+                   check_debug: bool = True, top_p=1.0) -> Report:
+    """T, top_k, top_p: scalars or per-request arrays."""
     B, K = vin.B, vin.K
+    per = lambda x: np.broadcast_to(np.asarray(x), (B,))
+    Ts = per(vin.T if T is None else T)
+    ks = per(vin.top_k if top_k is None else top_k)
+    ps = per(top_p)
+    rep = Report()
     reqs = range(B) if requests is None else requests
     for b in reqs:
+        T, top_k, top_p = float(np.float32(Ts[b])), int(ks[b]), float(ps[b])
         lo, hi = int(vin.cu_draft[b]), int(vin.cu_draft[b + 1])
         k = hi - lo
         r = o.requests[b]

@@ -56,6 +56,14 @@ def test_workspace_sizes(lib):
     assert binding.specdec_verify_workspace_size(1, 1, binding.MAX_V, binding.SPECDEC_BF16, 64) > 0
     assert binding.specdec_verify_workspace_size(1, 1, binding.MAX_V + 1, binding.SPECDEC_BF16, 0) == 0
     assert binding.specdec_cycle_workspace_size(1, 1, binding.MAX_V + 1, binding.SPECDEC_F32, 0) == 0
+    # per-request parameters: lists for the largest chunk k, row parameters, chunk partials
+    pr = binding.SpecdecParams(16, 16, None, 64)
+    assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 0, 1.0,
+                                                 pr) >= 2816 * 8 * 1040 * 4 + 2816 * 16
+    assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 0, 1.0,
+                                                 binding.SpecdecParams(None, 16, None, -1)) == 0
+    assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 0, 1.0,
+                                                 binding.SpecdecParams(None, None, None, 0)) == n
     # top-p alone gathers candidates like top-k; top-p NaN is rejected, <= 0 or >= 1 is off
     assert binding.specdec_verify_workspace_size(256, 1280, 128256, binding.SPECDEC_BF16, 0,
                                                  0.9) >= 2816 * 8 * 1040 * 4
@@ -69,26 +77,34 @@ def test_workspace_sizes(lib):
 def test_host_validation_returns_einval_without_gpu(lib):
     vp = None
     # B = 0
-    assert lib.specdec_verify(vp, vp, 1, vp, vp, vp, vp, 0, 0, 4, 10, 1.0, 0, 1.0, vp, vp, vp, vp,
+    assert lib.specdec_verify(vp, vp, 1, vp, vp, vp, vp, 0, 0, 4, 10, 1.0, 0, 1.0, None, vp, vp, vp, vp,
                               None, vp, 0, vp) == binding.SPECDEC_EINVAL
     # temperature <= 0, and NaN
     for T in (0.0, -1.0, float("nan"), float("inf")):
-        assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, T, 0, 1.0, 1, 1, 1, 1,
+        assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, T, 0, 1.0, None, 1, 1, 1, 1,
                                   None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
     # top_p NaN
-    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, 1.0, 0, float("nan"), 1, 1, 1, 1,
+    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, 1.0, 0, float("nan"), None, 1, 1, 1, 1,
                               None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
+    # per-request arrays: T and top_p scalars they replace are not checked; top_k_max < 0
+    pr_t = binding.SpecdecParams(16, None, None, 0)
+    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, float("nan"), 0, 1.0,
+                              ctypes.byref(pr_t), 1, 1, 1, 1, None, 16, 8,
+                              vp) == binding.SPECDEC_EWORKSPACE
+    pr_k = binding.SpecdecParams(None, 16, None, -1)
+    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 4, 10, 1.0, 0, 1.0, ctypes.byref(pr_k),
+                              1, 1, 1, 1, None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
     # max_k above the limit, K > B * max_k, bad dtype
-    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 65, 10, 1.0, 0, 1.0, 1, 1, 1, 1,
+    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 1, 1, 65, 10, 1.0, 0, 1.0, None, 1, 1, 1, 1,
                               None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
-    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 2, 9, 4, 10, 1.0, 0, 1.0, 1, 1, 1, 1,
+    assert lib.specdec_verify(1, 1, 1, 1, 1, 1, 1, 2, 9, 4, 10, 1.0, 0, 1.0, None, 1, 1, 1, 1,
                               None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
-    assert lib.specdec_verify(1, 1, 7, 1, 1, 1, 1, 1, 1, 4, 10, 1.0, 0, 1.0, 1, 1, 1, 1,
+    assert lib.specdec_verify(1, 1, 7, 1, 1, 1, 1, 1, 1, 4, 10, 1.0, 0, 1.0, None, 1, 1, 1, 1,
                               None, 16, 1 << 30, vp) == binding.SPECDEC_EINVAL
     # workspace too small / misaligned
-    assert lib.specdec_verify(16, 16, 1, 16, 16, 16, 16, 1, 1, 4, 10, 1.0, 0, 1.0, 16, 16, 16, 16,
+    assert lib.specdec_verify(16, 16, 1, 16, 16, 16, 16, 1, 1, 4, 10, 1.0, 0, 1.0, None, 16, 16, 16, 16,
                               None, 16, 8, vp) == binding.SPECDEC_EWORKSPACE
-    assert lib.specdec_verify(16, 16, 1, 16, 16, 16, 16, 1, 1, 4, 10, 1.0, 0, 1.0, 16, 16, 16, 16,
+    assert lib.specdec_verify(16, 16, 1, 16, 16, 16, 16, 1, 1, 4, 10, 1.0, 0, 1.0, None, 16, 16, 16, 16,
                               None, 17, 1 << 30, vp) == binding.SPECDEC_EWORKSPACE
 
 

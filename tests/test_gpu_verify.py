@@ -194,7 +194,7 @@ def test_vocabulary_past_the_limit_is_einval():
     lib = binding.load_library()
     st = lib.specdec_verify(v.tgt.data_ptr(), v.dft.data_ptr(), 1, v.tokens.data_ptr(),
                             v.cu.data_ptr(), v.u_acc.data_ptr(), v.u_smp.data_ptr(), 1, vin.K,
-                            vin.max_k, binding.MAX_V + 1, 1.0, 0, 1.0, v.out_tokens.data_ptr(),
+                            vin.max_k, binding.MAX_V + 1, 1.0, 0, 1.0, None, v.out_tokens.data_ptr(),
                             v.num_acc.data_ptr(), v.num_emit.data_ptr(), v.err.data_ptr(), None,
                             v.ws.data_ptr(), v.ws.numel(), None)
     assert st == binding.SPECDEC_EINVAL
