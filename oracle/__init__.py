@@ -30,6 +30,9 @@ from .verify import (  # noqa: F401
     inverse_cdf, inverse_cdf_np, verify_probs, verify_request, verify_batch,
     BatchResult,
 )
+from .analytics import (  # noqa: F401
+    acceptance_rate, expected_emitted, acceptance_batch,
+)
 from .kv import (  # noqa: F401
     KV_ERR_NOMEM, KV_ERR_APPEND, KV_ERR_ROLLBACK,
     PagedKV, ContiguousKV,
