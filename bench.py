@@ -105,6 +105,48 @@ def cpu_baseline(vin, kv, min_seconds: float, top_p: float):
                        f"input generation and copies excluded")}
 
 
+def acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp, out, nacc,
+                     nemit, err, ws, top_p, pr, cycle_ms):
+    """After the timed cycles, outside them: verification of the same batch with the
+    acceptance analytics on. Reports the mean acceptance probability of a proposal, E[A]
+    (expected tokens per cycle and request, the correction or bonus included), the tokens
+    this batch actually emitted, and E[A] summed over the batch per second of measured
+    cycle time: the section 4 throughput proxy with the draft cost left out (the draft
+    model is not part of this path), so an upper bound. Also the analytics pass's cost."""
+    B, K = vin.B, vin.K
+    beta = torch.empty(max(K, 1), dtype=torch.float64, device=d)
+    expd = torch.empty(B, dtype=torch.float64, device=d)
+    dbg = binding.SpecdecDebug()
+    dbg.accept_prob, dbg.expected_emitted = beta.data_ptr(), expd.data_ptr()
+
+    def call(debug):
+        binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
+                               temperature=vin.T, top_k=vin.top_k, out_tokens=out,
+                               num_accepted=nacc, num_emitted=nemit, err_word=err, workspace=ws,
+                               debug=debug, top_p=top_p, **pr)
+
+    times = {}
+    for name, debug in (("plain", None), ("analytics", dbg)):
+        for _ in range(3):
+            call(debug)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            call(debug)
+        e1.record()
+        torch.cuda.synchronize()
+        times[name] = e0.elapsed_time(e1) / 10
+    b = beta[:K].cpu().numpy()
+    e = expd.cpu().numpy()
+    emitted = nemit.cpu().numpy()
+    ok = ~np.isnan(e)
+    return {"mean_accept_prob": float(np.nanmean(b)) if K else None,
+            "mean_expected_emitted": float(e[ok].mean()) if ok.any() else None,
+            "realized_emitted_per_request": float(emitted.mean()),
+            "proxy_tokens_per_s_no_draft_cost": float(e[ok].sum() / (cycle_ms / 1e3)),
+            "verify_ms": times["plain"], "verify_with_analytics_ms": times["analytics"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -228,6 +270,8 @@ def main():
     stats_ms = [evs[i][0].elapsed_ms(evs[i][1]) for i in timed]
     stats_avg_s = float(np.mean(stats_ms)) / 1e3
     ms_per_step = elapsed / args.steps * 1e3
+    acceptance = acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
+                                  out, nacc, nemit, err, ws, top_p, pr, ms_per_step)
     es = 2 if vin.dtype == "bf16" else 4
     rows = 2 * K + B
     logit_bytes = rows * V * es
@@ -276,6 +320,7 @@ def main():
     }
     if generic:
         res["roofline"] = None
+    res["acceptance"] = acceptance
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
     print(json.dumps(res))

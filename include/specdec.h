@@ -107,6 +107,13 @@ typedef struct specdec_debug {
                                    streamed: independent bandwidth-bound work (the K/V
                                    scatter) can start on another stream while the
                                    latency-bound sampling kernel runs                     */
+    /* Acceptance analytics ("Speculative decoding ...", section 3: a proposal drawn from q_i
+     * is accepted with probability beta_i = sum_x min(p_i(x), q_i(x)) = 1 - (the residual
+     * mass); section 4: E[A], the expected output of a cycle). Either pointer non-NULL adds
+     * one pass over every proposal's row pair after the draw (the kept-token lists of bf16
+     * top-k / top-p rows instead, where they exist). NaN for a failed request. */
+    double*  accept_prob;       /* [K] beta_i of every proposal position                  */
+    double*  expected_emitted;  /* [B] E[A] = 1 + sum_j prod_{i<=j} beta_i                */
 } specdec_debug;
 
 /* Per-request decoding transform ("Speculative decoding ...", sections 3 and 4: the same

@@ -48,10 +48,12 @@ def expected_emitted(betas: Sequence):
 
 
 def acceptance_batch(target, draft, cu_draft, T, top_k, dtype: str, top_p=1.0,
-                     top_k_max=None, requests: Optional[Sequence[int]] = None):
+                     top_k_max=None, requests: Optional[Sequence[int]] = None,
+                     draft_tokens=None, u_accept=None, u_sample=None):
     """Per-position beta_i [K] and per-request E[A] [B] of a packed ragged batch (rows as
-    in verify_batch). Requests with malformed offsets, invalid parameters or a row that
-    cannot be normalized get NaN."""
+    in verify_batch). Requests that fail verification get NaN: malformed offsets, invalid
+    parameters, a row that cannot be normalized and, when the proposals and uniforms are
+    given, a token outside [0, V) or a uniform outside [0, 1)."""
     cu = np.asarray(cu_draft, dtype=np.int64)
     B = cu.shape[0] - 1
     K = int(draft.shape[0])
@@ -68,6 +70,11 @@ def acceptance_batch(target, draft, cu_draft, T, top_k, dtype: str, top_p=1.0,
             continue
         lo, hi = int(cu[b]), int(cu[b + 1])
         if not params_ok(Ts[b], ks[b], ps[b], V, top_k_max):
+            continue
+        if draft_tokens is not None and any(not 0 <= int(y) < V for y in draft_tokens[lo:hi]):
+            continue
+        if u_accept is not None and not all(0.0 <= float(u) < 1.0
+                                            for u in list(u_accept[lo:hi]) + [u_sample[b]]):
             continue
         t_rows = _decode_rows(target[lo + b: hi + b + 1], dtype)
         d_rows = _decode_rows(draft[lo:hi], dtype)

@@ -63,6 +63,7 @@ class SpecdecDebug(ctypes.Structure):
         ("req_flags", ctypes.c_void_p),
         ("ev_stats_begin", ctypes.c_void_p), ("ev_stats_end", ctypes.c_void_p),
         ("ev_stats_done", ctypes.c_void_p),
+        ("accept_prob", ctypes.c_void_p), ("expected_emitted", ctypes.c_void_p),
     ]
 
 

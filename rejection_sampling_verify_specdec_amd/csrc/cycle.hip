@@ -32,6 +32,16 @@
 
 namespace sd {
 
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kPartNT) void k_accept_part(SampleArgs a) {
+    accept_part_body<BF16, VEC, kPartNT>(a, blockIdx.x / a.nch, blockIdx.x % a.nch);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kWave) void k_accept_final(SampleArgs a) {
+    accept_final_body<BF16>(a, blockIdx.x);
+}
+
 constexpr int kCycAllocNT = kNT;   // allocation workgroup inside the statistics launch
 constexpr int kCycScatterPPT = kScPPT;   // token rows per scatter thread in flight
 
@@ -166,6 +176,14 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
                        st, sa, kv, rb);
     hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
+    if (sa.prec && K > 0) {
+        // acceptance analytics: residual mass of every proposal position, then beta and E[A]
+        hipLaunchKernelGGL((k_accept_part<BF16, VEC>), dim3((unsigned)K * p.nch), dim3(kPartNT), 0,
+                           st, sa);
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    } else if (sa.prec) {
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    }
     if (!rb) hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, sa, kv);
 }
 
@@ -209,7 +227,8 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
         ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15))
         return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
-    if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu || V > SPECDEC_MAX_V)
+    if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu ||
+        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     const size_t vbytes = align256(p.total);
     if (!workspace || workspace_bytes < vbytes + append_ws_bytes(B, K + B) ||
@@ -257,6 +276,9 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.num_emit = num_emitted;
     sa.err_word = err_word;
     sa.dbg = dbg ? *dbg : specdec_debug{};
+    const bool analytics = dbg && (dbg->accept_prob || dbg->expected_emitted);
+    sa.prec = analytics ? reinterpret_cast<Decision*>(vws + p.prec) : nullptr;
+    sa.wacc = analytics ? reinterpret_cast<double*>(vws + p.wacc) : nullptr;
 
     const KvArgs kv = args_of(cache);
     ParamArgs pa{};

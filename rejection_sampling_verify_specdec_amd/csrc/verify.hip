@@ -42,6 +42,16 @@
 namespace sd {
 
 template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kPartNT) void k_accept_part(SampleArgs a) {
+    accept_part_body<BF16, VEC, kPartNT>(a, blockIdx.x / a.nch, blockIdx.x % a.nch);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kWave) void k_accept_final(SampleArgs a) {
+    accept_final_body<BF16>(a, blockIdx.x);
+}
+
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ tgt,
                                                    const uint8_t* __restrict__ dft,
                                                    int rows_t, int V, int nchunks, float c,
@@ -131,6 +141,14 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     hipLaunchKernelGGL((k_decide<BF16>), dim3(B), dim3(kDecideNT), 0, st, sa);
     hipLaunchKernelGGL((k_part<BF16, VEC>), dim3((unsigned)B * p.nch), dim3(kPartNT), 0, st, sa);
     hipLaunchKernelGGL((k_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
+    if (sa.prec && K > 0) {
+        // acceptance analytics: residual mass of every proposal position, then beta and E[A]
+        hipLaunchKernelGGL((k_accept_part<BF16, VEC>), dim3((unsigned)K * p.nch), dim3(kPartNT), 0,
+                           st, sa);
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    } else if (sa.prec) {
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    }
 }
 
 }  // namespace sd
@@ -167,7 +185,7 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
-        V > SPECDEC_MAX_V)
+        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V)
         return SPECDEC_EINVAL;
     if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;
@@ -214,6 +232,9 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     } else {
         sa.dbg = specdec_debug{};
     }
+    const bool analytics = dbg && (dbg->accept_prob || dbg->expected_emitted);
+    sa.prec = analytics ? reinterpret_cast<Decision*>(ws + p.prec) : nullptr;
+    sa.wacc = analytics ? reinterpret_cast<double*>(ws + p.wacc) : nullptr;
 
     ParamArgs pa{};
     if (p.pr) pa = param_args(cu_draft, B, K, V, temperature, top_k, top_p, per_request, p, ws);

@@ -1077,6 +1077,8 @@ struct SampleArgs {
     int* num_emit;
     int* err_word;
     specdec_debug dbg;
+    Decision* prec;          // analytics: [K] the row pair of every proposal position, else null
+    double* wacc;            // analytics: [K][nch][kSSub] sub-chunk sums of max(0, p - q)
 };
 
 constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
@@ -1298,6 +1300,28 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
             }
             d.u = a.u_smp[b];
             D = d;
+        }
+        if (publish && a.prec && lane < k) {
+            // analytics: the row pair of this position, for the residual mass of every one
+            Decision q;
+            q.flags = 0;
+            q.err = err;
+            q.a = lane;
+            q.k = k;
+            q.mode = err ? MODE_NONE : MODE_RESID;
+            q.row_t = lo + b + lane;
+            q.row_d = lo + lane;
+            q.pad = q.pad3 = q.pad4 = 0;
+            q.c = cf;
+            q.u = 0.f;
+            const float mt = s_m[lane], md = s_m[k + 1 + lane];
+            q.mc_t = mt * cf;
+            q.al_t = exp2(-(double)fmaf(mt, cf, -q.mc_t)) / s_S[lane];
+            q.thr_t = s_thr[lane];
+            q.mc_d = md * cf;
+            q.al_d = exp2(-(double)fmaf(md, cf, -q.mc_d)) / s_S[k + 1 + lane];
+            q.thr_d = s_thr[k + 1 + lane];
+            a.prec[lo + lane] = q;
         }
     }
     __syncthreads();
@@ -1622,6 +1646,87 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Acceptance analytics: beta_i = 1 - W_i for every proposal position, W_i the residual mass
+// sum_x max(0, p_i(x) - q_i(x)) summed exactly as the draw sums it; E[A] per request.
+// ---------------------------------------------------------------------------------------
+// W over a bf16 target row's kept-token list (tokens outside it have p = 0).
+template <bool BF16, int NT>
+SD_DEV double listed_resid_sum(const SampleArgs& a, const Decision& q, int n) {
+    constexpr int EPT = kKeptCap / NT;
+    __shared__ double redd[NT / kWave];
+    const int tid = threadIdx.x;
+    const uint32_t* tok = a.ktok + (size_t)q.row_t * kKeptCap;
+    const uint16_t* key = a.kkey + (size_t)q.row_t * kKeptCap;
+    const uint8_t* drow = a.dft + (size_t)q.row_d * a.V * (BF16 ? 2 : 4);
+    double run = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        const int i = tid * EPT + e;
+        if (i < n) {
+            const int x = (int)tok[i];
+            run += weight(key_to_float<BF16>(key[i]), load_elem(drow, x, BF16), q, q.c, true);
+        }
+    }
+    return block_sum<NT>(run, redd);
+}
+
+// Workgroup (position r, chunk): the chunk's four sub-chunk sums of max(0, p - q).
+template <bool BF16, bool VEC, int NT>
+SD_DEV void accept_part_body(const SampleArgs& a, int r, int chunk) {
+    using Lt = Layout<BF16, VEC>;
+    __shared__ double red[kSSub * (NT / kWave)];
+    const Decision q = a.prec[r];
+    if (q.mode == MODE_NONE) return;
+    double* out = a.wacc + ((size_t)r * a.nch + chunk) * kSSub;
+    if constexpr (BF16) {
+        if (a.kn) {
+            const int n = a.kn[q.row_t];
+            if (n >= 0) {
+                if (chunk == 0) {
+                    const double W = listed_resid_sum<BF16, NT>(a, q, n);
+                    if (threadIdx.x < kSSub) out[threadIdx.x] = threadIdx.x == 0 ? W : 0.0;
+                }
+                return;
+            }
+        }
+    }
+    const uint8_t* trow = a.tgt + (size_t)q.row_t * a.V * Lt::ES;
+    const uint8_t* drow = a.dft + (size_t)q.row_d * a.V * Lt::ES;
+    chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, chunk, q, q.c, true, a.topk != 0, red, out);
+}
+
+// One wave per request: beta_i = 1 - W_i (sums in a fixed order, clamped to [0, 1]), then
+// E[A] = 1 + sum_j prod_{i<=j} beta_i. Failed requests get NaN (positions only when the
+// offsets are sound).
+template <bool BF16>
+SD_DEV void accept_final_body(const SampleArgs& a, int b) {
+    const int lane = threadIdx.x;
+    const Decision r = a.rec[b];
+    const bool cu_ok = !(r.mode == MODE_NONE && (r.flags & SPECDEC_ERR_K));
+    const int lo = cu_ok ? a.cu[b] : 0;
+    const int k = cu_ok ? a.cu[b + 1] - lo : 0;
+    double beta = NAN;
+    if (r.mode != MODE_NONE && lane < k) {
+        const int pos = lo + lane;
+        const double* w = a.wacc + (size_t)pos * a.nch * kSSub;
+        bool listed = false;
+        if constexpr (BF16) listed = a.kn && a.kn[a.prec[pos].row_t] >= 0;
+        double W = 0.0;
+        const int nsum = listed ? 1 : a.nch * kSSub;
+        for (int i = 0; i < nsum; ++i) W += w[i];
+        beta = fmin(1.0, fmax(0.0, 1.0 - W));
+    }
+    if (lane < k && a.dbg.accept_prob) a.dbg.accept_prob[lo + lane] = beta;
+    double e = 1.0, run = 1.0;
+    for (int i = 0; i < k; ++i) {
+        run *= __shfl(beta, i, kWave);
+        e += run;
+    }
+    if (lane == 0 && a.dbg.expected_emitted)
+        a.dbg.expected_emitted[b] = r.mode == MODE_NONE ? (double)NAN : e;
+}
+
+// ---------------------------------------------------------------------------------------
 // Per-request transform parameters. The row's request: for a target row r the b with
 // cu[b] + b <= r < cu[b+1] + b + 1, for a draft row r' the b with cu[b] <= r' < cu[b+1]
 // (a binary search over cu; a malformed cu is reported by the decision, the b found here
@@ -1748,7 +1853,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
     size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc, rpar,
-        total;
+        prec, wacc, total;
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
     int pr;                  // per-request parameters: every row through the chunk select
     int kc;                  // the chunk k of a top-p-alone row
@@ -1845,6 +1950,11 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
     }
     p.rpar = off;
     if (p.pr) off = align256(off + rows * sizeof(RowParams));
+    // acceptance analytics: a record and the sub-chunk residual sums of every position
+    p.prec = off;
+    off = align256(off + (size_t)K * sizeof(Decision));
+    p.wacc = off;
+    off = align256(off + (size_t)K * p.nch * kSSub * sizeof(double));
     p.total = off;
     return p;
 }

@@ -62,6 +62,8 @@ class GpuVerify:
     resid_mass: np.ndarray
     picked_prob: np.ndarray
     req_flags: np.ndarray
+    accept_prob: Optional[np.ndarray] = None
+    expected_emitted: Optional[np.ndarray] = None
 
 
 class VerifyOnDevice:
@@ -69,7 +71,8 @@ class VerifyOnDevice:
 
     def __init__(self, vin: VerifyInputs, device=None, max_k: Optional[int] = None,
                  top_k: Optional[int] = None, T: Optional[float] = None, top_p: float = 1.0,
-                 temps=None, top_ks=None, top_ps=None, top_k_max: Optional[int] = None):
+                 temps=None, top_ks=None, top_ps=None, top_k_max: Optional[int] = None,
+                 analytics: bool = False):
         d = device or dev()
         self.vin = vin
         self.max_k = vin.max_k if max_k is None else max_k
@@ -107,11 +110,17 @@ class VerifyOnDevice:
         self.resid_mass = torch.full((B,), -1.0, dtype=torch.float64, device=d)
         self.picked = torch.full((B,), -1.0, dtype=torch.float64, device=d)
         self.req_flags = torch.full((B,), -1, dtype=torch.int32, device=d)
+        self.accept_prob = self.expected = None
+        if analytics:
+            self.accept_prob = torch.full((max(K, 1),), -1.0, dtype=torch.float64, device=d)
+            self.expected = torch.full((B,), -1.0, dtype=torch.float64, device=d)
         self.dbg = binding.SpecdecDebug(
             self.p_y.data_ptr(), self.q_y.data_ptr(), self.row_max.data_ptr(),
             self.row_sum.data_ptr(), self.row_thr.data_ptr(), self.row_nkept.data_ptr(),
             self.resid_mass.data_ptr(), self.picked.data_ptr(), self.req_flags.data_ptr(),
-            None, None)
+            None, None, None,
+            self.accept_prob.data_ptr() if analytics else None,
+            self.expected.data_ptr() if analytics else None)
 
     def run(self, debug: bool = True) -> None:
         binding.specdec_verify(
@@ -127,7 +136,9 @@ class VerifyOnDevice:
         c = lambda t: t.cpu().numpy()
         return GpuVerify(c(self.num_acc), c(self.num_emit), c(self.out_tokens), int(self.err.item()),
                          c(self.p_y), c(self.q_y), c(self.row_max), c(self.row_sum), c(self.row_thr),
-                         c(self.row_nkept), c(self.resid_mass), c(self.picked), c(self.req_flags))
+                         c(self.row_nkept), c(self.resid_mass), c(self.picked), c(self.req_flags),
+                         None if self.accept_prob is None else c(self.accept_prob)[:self.vin.K],
+                         None if self.expected is None else c(self.expected))
 
 
 def run_verify(vin: VerifyInputs, **kw) -> GpuVerify:
