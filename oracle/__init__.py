@@ -33,6 +33,10 @@ from .verify import (  # noqa: F401
 from .analytics import (  # noqa: F401
     acceptance_rate, expected_emitted, acceptance_batch,
 )
+from .tree import (  # noqa: F401
+    ERR_TREE, children_of, tree_verify_probs, tree_verify_request, tree_verify_batch,
+    tree_commit,
+)
 from .kv import (  # noqa: F401
     KV_ERR_NOMEM, KV_ERR_APPEND, KV_ERR_ROLLBACK,
     PagedKV, ContiguousKV,
