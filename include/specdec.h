@@ -63,6 +63,7 @@ extern "C" {
 #define SPECDEC_ERR_ZFALLBACK 16   /* flag only: residual mass was 0 after a rejection;
                                       the replacement was drawn from p_i                   */
 #define SPECDEC_ERR_UNIFORM   32   /* a uniform outside [0, 1) (or NaN)                   */
+#define SPECDEC_ERR_TREE     128   /* a draft tree's parent index outside {-1, .., j-1}   */
 #define SPECDEC_ERR_PARAM     64   /* per-request parameters invalid: temperature <= 0 or
                                       not finite, top_p NaN, or an active top_k above
                                       specdec_params.top_k_max                            */
@@ -76,6 +77,7 @@ extern "C" {
 
 /* Largest proposal count per request, batch size for the KV calls, and vocabulary. */
 #define SPECDEC_MAX_K      64
+#define SPECDEC_MAX_TREE   64         /* nodes of one request's draft tree               */
 #define SPECDEC_MAX_KV_BATCH 4096
 #define SPECDEC_MAX_V      2097152
 
@@ -319,6 +321,63 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
                   int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                   int32_t* err_word, const specdec_debug* dbg,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* =====================================================================================
+ * Draft trees
+ * ===================================================================================== */
+
+/*
+ * specdec_tree_verify - verification of one draft tree per request.
+ *
+ * Request b owns nodes cu_nodes[b] .. cu_nodes[b+1]-1 (n_b <= max_nodes <= SPECDEC_MAX_TREE);
+ * node j (local index) has token tree_tokens[cu_nodes[b] + j] and parent
+ * tree_parent[cu_nodes[b] + j] in {-1, 0, .., j-1} (-1: a child of the root, the position
+ * after the committed prefix). Positions: 0 the root, 1 + j the position after node j;
+ * target_logits / draft_logits [N+B][V] hold the rows of request b's positions at
+ * cu_nodes[b] + b + v (draft rows of nodes without children are not read).
+ * The children of a position are alternatives for the next token, each drawn by the draft
+ * from that position's q; they are tried in node order, child j accepted iff
+ * u_accept[cu_nodes[b] + j] * q(y_j) < p'(y_j), where p' starts as the position's p and
+ * after each rejected child becomes normalize(max(0, p' - q)) ("Speculative decoding ...",
+ * sections 2-3: the linear rule, with the residual applied sibling after sibling). The first
+ * accepted child continues the walk from its position; when every child is rejected the
+ * replacement is drawn from the last residual, and a position reached by acceptance with
+ * no children yields the bonus token from its p; both by inverse CDF with u_sample[b]
+ * (ascending ids). Temperature only (no top-k / top-p on trees).
+ * Outputs (device): num_accepted [B] = the accepted path's length (-1 on error),
+ * num_emitted [B] = that + 1; out_tokens [N+B]: request b writes the path's tokens then
+ * the drawn token at cu_nodes[b] + b; accepted_nodes [N]: the path's local node indices,
+ * root first, at cu_nodes[b]; err_word [1] OR-ed SPECDEC_ERR_* bits (SPECDEC_ERR_TREE for a
+ * bad parent); req_flags [B] (or NULL) each request's bits.
+ * Host: B >= 1, N = cu_nodes[B], 0 <= max_nodes <= SPECDEC_MAX_TREE, 1 <= V <=
+ * SPECDEC_MAX_V, temperature > 0 and finite; EINVAL otherwise, before anything is
+ * enqueued. No workspace: the walk keeps its state in LDS, one 1024-thread workgroup per
+ * request.
+ */
+int specdec_tree_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                        const int32_t* tree_tokens, const int32_t* tree_parent,
+                        const int32_t* cu_nodes, const float* u_accept, const float* u_sample,
+                        int32_t B, int32_t N, int32_t max_nodes, int32_t V, float temperature,
+                        int32_t* out_tokens, int32_t* accepted_nodes, int32_t* num_accepted,
+                        int32_t* num_emitted, int32_t* err_word, int32_t* req_flags,
+                        hipStream_t stream);
+
+/*
+ * kv_tree_commit - keep the accepted path of every request's tree in the cache ("Keep cache
+ * validity aligned with the committed token history", paragraph 3: gather the accepted
+ * path into the cache layout, drop the siblings). The cycle appended n_b + 1 entries per
+ * request with kv_paged_append (the pending token, then node j at the pending slot + 1 + j;
+ * cu_new[b] = cu_nodes[b] + b). Path node i (i = 1..a_b, from accepted_nodes) moves to the
+ * pending slot + i, in increasing i; then the cache is truncated to the pending slot + 1 +
+ * a_b and blocks past the end are released as kv_rollback does (n_b - a_b dropped). A
+ * request with a_b < 0 or > n_b, a path not strictly increasing within [0, n_b), offsets
+ * outside [0, N] (N: the length of accepted_nodes, = cu_nodes[B]), or fewer than n_b + 1
+ * entries is left as it is and flagged (KV_ERR_ROLLBACK). Nothing is done after an append
+ * that was not applied. Two launches on `stream`; no workspace.
+ */
+int kv_tree_commit(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                   const int32_t* accepted_nodes, const int32_t* cu_nodes, int32_t N,
+                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,8 @@ ERR_QZERO = 8
 ERR_ZFALLBACK = 16
 ERR_UNIFORM = 32
 ERR_PARAM = 64
+ERR_TREE = 128
+MAX_TREE = 64
 KV_ERR_NOMEM = 64
 KV_ERR_APPEND = 128
 KV_ERR_ROLLBACK = 256
@@ -44,7 +46,7 @@ MAX_V = 2097152
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
-    "specdec_cycle_workspace_size", "specdec_cycle",
+    "specdec_cycle_workspace_size", "specdec_cycle", "specdec_tree_verify", "kv_tree_commit",
 ]
 
 
@@ -142,6 +144,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   vp, vp, i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_cycle.restype = ctypes.c_int
+    lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
+                                        vp, vp, vp, vp, vp, vp, vp]
+    lib.specdec_tree_verify.restype = ctypes.c_int
+    lib.kv_tree_commit.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32, vp]
+    lib.kv_tree_commit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -409,3 +416,59 @@ class HipEvent:
                 _hip_rt().hipEventDestroy(self.handle)
         except Exception:
             pass
+
+
+def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                        tree_tokens: torch.Tensor, tree_parent: torch.Tensor,
+                        cu_nodes: torch.Tensor, u_accept: torch.Tensor, u_sample: torch.Tensor,
+                        *, max_nodes: int, temperature: float, out_tokens: torch.Tensor,
+                        accepted_nodes: torch.Tensor, num_accepted: torch.Tensor,
+                        num_emitted: torch.Tensor, err_word: torch.Tensor,
+                        req_flags: Optional[torch.Tensor] = None) -> None:
+    """Enqueue the verification of one draft tree per request (shapes as in the header)."""
+    lib = load_library()
+    dev = target_logits.device
+    dtype = _logits_dtype(target_logits)
+    if target_logits.dim() != 2:
+        raise ValueError("target_logits must be [N+B, V]")
+    B = cu_nodes.numel() - 1
+    R, V = target_logits.shape
+    N = R - B
+    _check(target_logits, "target_logits", target_logits.dtype, device=dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, R * V, dev)
+    _check(tree_tokens, "tree_tokens", torch.int32, N, dev)
+    _check(tree_parent, "tree_parent", torch.int32, N, dev)
+    _check(cu_nodes, "cu_nodes", torch.int32, B + 1, dev)
+    _check(u_accept, "u_accept", torch.float32, N, dev)
+    _check(u_sample, "u_sample", torch.float32, B, dev)
+    _check(out_tokens, "out_tokens", torch.int32, N + B, dev)
+    _check(accepted_nodes, "accepted_nodes", torch.int32, N, dev)
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(num_emitted, "num_emitted", torch.int32, B, dev)
+    _check(err_word, "err_word", torch.int32, 1, dev)
+    if req_flags is not None:
+        _check(req_flags, "req_flags", torch.int32, B, dev)
+    st = lib.specdec_tree_verify(
+        _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(tree_tokens), _ptr(tree_parent),
+        _ptr(cu_nodes), _ptr(u_accept), _ptr(u_sample), B, N, max_nodes, V, float(temperature),
+        _ptr(out_tokens), _ptr(accepted_nodes) if N else None, _ptr(num_accepted),
+        _ptr(num_emitted),
+        _ptr(err_word), _ptr(req_flags) if req_flags is not None else None, _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_tree_verify", st)
+
+
+def kv_tree_commit(cache: PagedKVCache, num_accepted: torch.Tensor, accepted_nodes: torch.Tensor,
+                   cu_nodes: torch.Tensor) -> None:
+    """Enqueue the gather of every request's accepted path and the truncation after it."""
+    lib = load_library()
+    dev = cache.device
+    B = cu_nodes.numel() - 1
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(cu_nodes, "cu_nodes", torch.int32, B + 1, dev)
+    _check(accepted_nodes, "accepted_nodes", torch.int32, None, dev)
+    st = lib.kv_tree_commit(ctypes.byref(cache.struct), B, _ptr(num_accepted),
+                            _ptr(accepted_nodes) if accepted_nodes.numel() else None,
+                            _ptr(cu_nodes), int(accepted_nodes.numel()), _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("kv_tree_commit", st)

@@ -45,8 +45,17 @@ __global__ __launch_bounds__(kScNT) void k_kv_scatter(KvArgs a, const uint8_t* _
 
 __global__ __launch_bounds__(kKvNT) void k_kv_rollback(KvArgs a, const int* __restrict__ num_acc,
                                                        const int* __restrict__ cu, int B,
-                                                       int draft) {
-    rollback_body(a, num_acc, cu, B, draft);
+                                                       int draft, const int* __restrict__ tree,
+                                                       int tree_n) {
+    rollback_body(a, num_acc, cu, B, draft, tree, tree_n);
+}
+
+__global__ __launch_bounds__(kTreeGatherNT) void k_kv_tree_gather(KvArgs a,
+                                                                  const int* __restrict__ num_acc,
+                                                                  const int* __restrict__ nodes,
+                                                                  const int* __restrict__ cu,
+                                                                  int N) {
+    tree_gather_body(a, num_acc, nodes, cu, N, blockIdx.x / (a.L * 2), blockIdx.x % (a.L * 2));
 }
 
 }  // namespace sd
@@ -88,7 +97,7 @@ static int rollback_call(const kv_paged_cache* cache, int32_t B, const int32_t* 
     const KvArgs a = args_of(cache);
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_kv_rollback, dim3(1), dim3(kKvNT), 0, stream, a, num_accepted, cu_draft,
-                       B, draft);
+                       B, draft, static_cast<const int*>(nullptr), 0);
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }
 
@@ -101,4 +110,21 @@ extern "C" int kv_rollback_draft(const kv_paged_cache* cache, int32_t B,
                                  const int32_t* num_accepted, const int32_t* cu_draft,
                                  hipStream_t stream) {
     return rollback_call(cache, B, num_accepted, cu_draft, stream, 1);
+}
+
+extern "C" int kv_tree_commit(const kv_paged_cache* cache, int32_t B, const int32_t* num_accepted,
+                              const int32_t* accepted_nodes, const int32_t* cu_nodes, int32_t N,
+                              hipStream_t stream) {
+    using namespace sd;
+    if (!geometry_ok(cache) || B < 1 || B > SPECDEC_MAX_KV_BATCH || N < 0 || !num_accepted ||
+        !cu_nodes || (N > 0 && !accepted_nodes))
+        return SPECDEC_EINVAL;
+    if ((long long)B * cache->num_layers * 2 > 0x7fffffffLL) return SPECDEC_EINVAL;
+    const KvArgs a = args_of(cache);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_kv_tree_gather, dim3((unsigned)B * a.L * 2), dim3(kTreeGatherNT), 0,
+                       stream, a, num_accepted, accepted_nodes, cu_nodes, N);
+    hipLaunchKernelGGL(k_kv_rollback, dim3(1), dim3(kKvNT), 0, stream, a, num_accepted, cu_nodes,
+                       B, 0, accepted_nodes, N);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

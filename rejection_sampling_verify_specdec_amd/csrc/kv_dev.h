@@ -15,6 +15,7 @@ constexpr int kKvNT = 1024;      // rollback workgroup (and the standalone alloc
 constexpr int kScNT = 256;       // standalone scatter workgroup
 constexpr int kScPPT = 8;        // token rows per scatter thread in flight
 constexpr int kEvCap = 2048;     // rollback events per window
+constexpr int kTreeGatherNT = 128;   // tree commit gather workgroup
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -290,12 +291,66 @@ SD_DEV void scatter_body(const KvArgs& a, const uint8_t* __restrict__ knew,
     }
 }
 
+// A tree's accepted path: a nodes, strictly increasing local indices within [0, n).
+SD_DEV bool tree_path_ok(const int* __restrict__ path, int a, int n) {
+    int prev = -1;
+    for (int i = 0; i < a; ++i) {
+        const int j = path[i];
+        if (j <= prev || j >= n) return false;
+        prev = j;
+    }
+    return true;
+}
+
+// Whether request b's tree commit applies: a sound accepted count and path, and the n + 1
+// entries of the cycle in the cache.
+SD_DEV bool tree_commit_ok(const KvArgs& a, const int* __restrict__ num_acc,
+                           const int* __restrict__ nodes, const int* __restrict__ cu, int b,
+                           int N) {
+    const int lo = cu[b], hi = cu[b + 1], n = hi - lo, acc = num_acc[b], s = a.seq_lens[b];
+    return lo >= 0 && hi <= N && n >= 0 && acc >= 0 && acc <= n && s >= n + 1 &&
+           (long long)s <= (long long)a.MBR * a.bs && tree_path_ok(nodes + lo, acc, n);
+}
+
+// Tree commit, gather: workgroup (b, layer-plane) moves the accepted path's entries of
+// request b to the slots after its pending token, in path order (each destination lies
+// below every source still to be read; threads keep their 16-byte pieces across copies).
+SD_DEV void tree_gather_body(const KvArgs& a, const int* __restrict__ num_acc,
+                             const int* __restrict__ nodes, const int* __restrict__ cu, int N,
+                             int b, int ulk) {
+    if (*a.state & KV_APPEND_REJECTED) return;
+    if (!tree_commit_ok(a, num_acc, nodes, cu, b, N)) return;
+    const int n = cu[b + 1] - cu[b], acc = num_acc[b];
+    const int base = a.seq_lens[b] - (n + 1);
+    const size_t ub = (size_t)a.H * a.D * 2;
+    const int nvec = (int)(ub / 16);
+    for (int i = 1; i <= acc; ++i) {
+        const int src = base + 1 + nodes[cu[b] + i - 1], dst = base + i;
+        if (src != dst) {
+            const int Xs = a.tables[(size_t)b * a.MBR + src / a.bs];
+            const int Xd = a.tables[(size_t)b * a.MBR + dst / a.bs];
+            if (Xs >= 0 && Xs < a.NB && Xd >= 0 && Xd < a.NB) {
+                const u32x4* sp = reinterpret_cast<const u32x4*>(
+                    a.pool + (((size_t)ulk * a.NB + Xs) * a.bs + src % a.bs) * ub);
+                u32x4* dp = reinterpret_cast<u32x4*>(
+                    a.pool + (((size_t)ulk * a.NB + Xd) * a.bs + dst % a.bs) * ub);
+                for (int q = threadIdx.x; q < nvec; q += blockDim.x) dp[q] = sp[q];
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Rollback of every request by one workgroup of NT threads, for B <= MAXB requests;
 // events (freed logical blocks) are processed in windows of EVCAP.
 // draft = 1: the draft model's convention, drop max(0, k_b - 1 - a_b) instead of k_b - a_b.
+// tree_nodes (tree commit, tree_n nodes): requests whose accepted path or offsets are
+// unsound, or that hold fewer than k_b + 1 entries, are skipped and flagged like other
+// invalid requests.
 template <int NT = kKvNT, int MAXB = SPECDEC_MAX_KV_BATCH, int EVCAP = kEvCap>
 SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
-                          const int* __restrict__ cu, int B, int draft = 0) {
+                          const int* __restrict__ cu, int B, int draft = 0,
+                          const int* __restrict__ tree_nodes = nullptr, int tree_n = 0) {
     constexpr int RPT = MAXB / NT;    // requests per thread
     constexpr int EPT = EVCAP / NT;   // window events per thread
     static_assert(RPT * NT == MAXB && EPT * NT == EVCAP, "whole rounds per thread");
@@ -322,7 +377,8 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
             const int k = cu[b + 1] - cu[b], acc = num_acc[b], s = a.seq_lens[b];
             const int drop = draft ? max(0, k - 1 - acc) : k - acc;
             if (k < 0 || acc < 0 || acc > k || drop > s ||
-                (long long)s > (long long)a.MBR * a.bs) {
+                (long long)s > (long long)a.MBR * a.bs ||
+                (tree_nodes && !tree_commit_ok(a, num_acc, tree_nodes, cu, b, tree_n))) {
                 err = 1;
             } else {
                 valid[i] = 1;

@@ -304,3 +304,76 @@ def make_kv(wl, vin: VerifyInputs, seed: int = 0, a_hint: Optional[np.ndarray] =
     cu_new = (vin.cu_draft.astype(np.int64) + np.arange(B + 1)).astype(np.int32)
     return KVInputs(L, H, D, bs, NB, MBR, tables, pre.astype(np.int32), refcount, free_list,
                     int(free_count), k_new, v_new, cu_new, blocks)
+
+
+@dataclass
+class TreeInputs:
+    """A batch of draft trees: request b owns nodes cu_nodes[b] .. cu_nodes[b+1]-1 and the
+    target / draft rows cu_nodes[b] + b + v of its positions v = 0 (root) .. n_b."""
+    B: int
+    V: int
+    N: int
+    max_nodes: int
+    dtype: str
+    T: float
+    target: np.ndarray            # [N+B, V] float32, or uint16 bf16 bits
+    draft: np.ndarray             # [N+B, V]
+    tokens: np.ndarray            # int32 [N]
+    parent: np.ndarray            # int32 [N], -1 or an earlier node of the request
+    cu_nodes: np.ndarray          # int32 [B+1]
+    u_accept: np.ndarray          # float32 [N]
+    u_sample: np.ndarray          # float32 [B]
+
+    # the names the cache generator reads: one cache entry per node plus the pending token
+    @property
+    def K(self) -> int:
+        return self.N
+
+    @property
+    def cu_draft(self) -> np.ndarray:
+        return self.cu_nodes
+
+    @property
+    def k_b(self) -> np.ndarray:
+        return np.diff(self.cu_nodes)
+
+
+def make_tree(seed: int = 0, B: int = 16, V: int = 32000, dtype: str = "bf16", T: float = 0.7,
+              n_range=(1, 16), target_std: float = 3.0, noise_std: float = 1.5,
+              branch: float = 0.5, max_nodes: int = 64) -> TreeInputs:
+    """Seeded trees: node j's parent is j - 1 (the chain goes on) or, with probability
+    ``branch``, a uniform pick among the root and the earlier nodes. Target rows N(0,
+    target_std) per position, draft rows the target row plus N(0, noise_std); each node's
+    token is a Gumbel-max draw from the draft row of its parent's position (siblings are
+    independent draws), standing in for the draft model."""
+    rng = np.random.default_rng(seed)
+    n_b = rng.integers(n_range[0], n_range[1] + 1, size=B)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(n_b)
+    N = int(cu[-1])
+    parent = np.zeros(N, dtype=np.int32)
+    for b in range(B):
+        for j in range(int(n_b[b])):
+            if j == 0:
+                parent[cu[b]] = -1
+            elif rng.random() < branch:
+                parent[cu[b] + j] = int(rng.integers(-1, j))
+            else:
+                parent[cu[b] + j] = j - 1
+    target32 = rng.standard_normal((N + B, V), dtype=np.float32) * np.float32(target_std)
+    draft32 = target32 + rng.standard_normal((N + B, V), dtype=np.float32) * np.float32(noise_std)
+    if dtype == "bf16":
+        target, draft = f32_to_bf16_bits(target32), f32_to_bf16_bits(draft32)
+        dvals = bf16_bits_to_f32(draft)
+    else:
+        target, draft, dvals = target32, draft32, draft32
+    # the draft row each node was drawn from: its parent's position
+    req = np.repeat(np.arange(B), n_b)
+    rows = cu[req] + req + parent + 1
+    tokens = _gumbel_sample(dvals[rows], float(np.float32(T)), 0, rng) if N else \
+        np.zeros(0, dtype=np.int32)
+    u_accept = rng.random(N, dtype=np.float32)
+    u_sample = rng.random(B, dtype=np.float32)
+    return TreeInputs(B, V, N, max_nodes, dtype, float(np.float32(T)), np.ascontiguousarray(target),
+                      np.ascontiguousarray(draft), tokens.astype(np.int32), parent, cu, u_accept,
+                      u_sample)
