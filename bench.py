@@ -147,8 +147,133 @@ def acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
             "verify_ms": times["plain"], "verify_with_analytics_ms": times["analytics"]}
 
 
+def tree_main(args):
+    """Draft trees: per step, append the pending token and every node (kv_paged_append),
+    verify the trees (specdec_tree_verify), keep the accepted paths (kv_tree_commit). The
+    line reports verified nodes per second, each call's time from events around it on
+    every timed step, and the bytes the walk read, replayed on the host from the outputs
+    (per visited position: its max / exp-sum pass, one pass over the row pair per rejected
+    child, the bonus pass at a leaf; the draw's rescans of 2048 tokens)."""
+    import torch
+    from rejection_sampling_verify_specdec_amd import binding, synth
+
+    if not os.path.exists(binding.LIB_PATH):
+        from rejection_sampling_verify_specdec_amd import build as _b
+        _b.build()
+    binding.load_library()
+    d = torch.device("cuda:0")
+    cfg = synth.TREE_WORKLOADS[args.workload]
+    tin = synth.make_tree(seed=args.seed, **cfg)
+    kv = synth.make_kv("c2", tin, seed=args.seed, cycles=args.warmup + args.steps + 2)
+    B, N, V = tin.B, tin.N, tin.V
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(d)
+
+    def t(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(d)
+
+    tgt, dft = bf(tin.target), bf(tin.draft)
+    tokens, parent, cu = t(tin.tokens), t(tin.parent), t(tin.cu_nodes)
+    u_acc, u_smp = t(tin.u_accept), t(tin.u_sample)
+    pool = torch.empty((kv.L, 2, kv.num_blocks, kv.block_size, kv.H, kv.D), dtype=torch.bfloat16,
+                       device=d)
+    if kv.blocks:
+        ids = sorted(kv.blocks)
+        pool[:, :, torch.tensor(ids, device=d)] = bf(np.stack([kv.blocks[X][0] for X in ids], axis=2))
+    cache = binding.PagedKVCache(pool, t(kv.block_tables), t(kv.seq_lens), t(kv.refcount),
+                                 t(kv.free_list), torch.tensor([kv.free_count], dtype=torch.int32, device=d),
+                                 torch.zeros(1, dtype=torch.int32, device=d))
+    k_new, v_new, cu_new = bf(kv.k_new), bf(kv.v_new), t(kv.cu_new)
+    out = torch.empty(N + B, dtype=torch.int32, device=d)
+    nodes = torch.empty(N, dtype=torch.int32, device=d)
+    nacc = torch.empty(B, dtype=torch.int32, device=d)
+    nemit = torch.empty(B, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    kws = torch.empty(binding.kv_paged_append_workspace_size(B, N + B), dtype=torch.uint8, device=d)
+    n = args.warmup + args.steps
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in range(args.warmup, n)}
+
+    def step(i):
+        e = ev.get(i)
+        if e:
+            e[0].record()
+        binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
+        if e:
+            e[1].record()
+        binding.specdec_tree_verify(tgt, dft, tokens, parent, cu, u_acc, u_smp,
+                                    max_nodes=tin.max_nodes, temperature=tin.T, out_tokens=out,
+                                    accepted_nodes=nodes, num_accepted=nacc, num_emitted=nemit,
+                                    err_word=err)
+        if e:
+            e[2].record()
+        binding.kv_tree_commit(cache, nacc, nodes, cu)
+        if e:
+            e[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = lambda a, b: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in ev]))
+    append_ms, verify_ms, commit_ms = ms(0, 1), ms(1, 2), ms(2, 3)
+    # bytes the walk read, replayed from the outputs
+    a = nacc.cpu().numpy()
+    path = nodes.cpu().numpy()
+    row = V * 2
+    walk = 0
+    for b in range(B):
+        lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
+        par = tin.parent[lo:hi]
+        kids = [[] for _ in range(hi - lo + 1)]
+        for j, pa in enumerate(par):
+            kids[int(pa) + 1].append(j)
+        v = 0
+        steps = list(path[lo: lo + max(int(a[b]), 0)]) + [None]
+        for nxt in steps:
+            if not kids[v]:
+                walk += 2 * row                                   # stats + bonus pass
+                break
+            walk += 2 * row                                       # target + draft stats
+            rej = kids[v].index(nxt) if nxt is not None else len(kids[v])
+            walk += rej * 2 * row                                 # residual passes
+            if nxt is None:
+                break
+            v = int(nxt) + 1
+    res = {
+        "metric": "verified draft-tree nodes/sec (tree workload; the headline line is the "
+                  "linear cycle)",
+        "value": N * args.steps / elapsed,
+        "unit": "nodes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"{args.workload}: B={B} trees of U{{{cfg['n_range'][0]}.."
+                                f"{cfg['n_range'][1]}}} nodes (N={N}), V={V} bf16 T={tin.T:g}; "
+                                f"paged KV {kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
+                   "global_batch": B, "parallelism": "single GPU"},
+        "tree": {"append_ms": append_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
+                 "mean_accepted": float(a[a >= 0].mean()), "walk_bytes": walk,
+                 "walk_gbps": walk / (verify_ms / 1e3) / 1e9,
+                 "walk_frac_of_peak": walk / (verify_ms / 1e3) / 1e9 / PEAK_GBPS},
+    }
+    if int(cache.state.item()):
+        print(f"# warning: cache state word {int(cache.state.item()):#x}", file=sys.stderr)
+    print(json.dumps(res))
+
+
 def main():
     args = parse()
+    if args.workload.startswith("t") and args.workload != "tiny":
+        if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+            print("bench.py measures one GPU.", file=sys.stderr)
+            sys.exit(2)
+        return tree_main(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the verification path shards by request with no "
               "cross-GPU exchange, and runs on more than one GPU are not part of this build.",

@@ -53,15 +53,59 @@ struct TreeArgs {
     int* req_flags;          // [B] or null
 };
 
+// Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
+// or past V read as -inf.
+template <bool BF16>
+struct Tok8 {
+    u32x4 v[BF16 ? 1 : 2];
+    SD_DEV float get(int e) const {
+        if constexpr (BF16) {
+            const uint32_t w = v[0][e >> 1];
+            return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+        } else {
+            return __uint_as_float(v[e >> 2][e & 3]);
+        }
+    }
+};
+
+template <bool BF16, bool VEC>
+SD_DEV Tok8<BF16> load8r(const uint8_t* __restrict__ row, int V, int i0) {
+    Tok8<BF16> t;
+    constexpr uint32_t NINF = BF16 ? 0xff80ff80u : 0xff800000u;
+    if constexpr (VEC) {
+        // whole 16-byte vectors: V * size is a multiple of 16, so i0 < V covers all 8
+        const u32x4* p = reinterpret_cast<const u32x4*>(row) + (BF16 ? i0 / 8 : i0 / 4);
+#pragma unroll
+        for (int h = 0; h < (BF16 ? 1 : 2); ++h)
+            t.v[h] = i0 < V ? __builtin_nontemporal_load(p + h) : (u32x4){NINF, NINF, NINF, NINF};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t bits;
+            if constexpr (BF16)
+                bits = i0 + e < V ? (uint32_t)reinterpret_cast<const uint16_t*>(row)[i0 + e] : 0xff80u;
+            else
+                bits = i0 + e < V ? reinterpret_cast<const uint32_t*>(row)[i0 + e] : NINF;
+            if constexpr (BF16) {
+                if (e & 1) t.v[0][e >> 1] |= bits << 16;
+                else t.v[0][e >> 1] = bits;
+            } else {
+                t.v[e >> 2][e & 3] = bits;
+            }
+        }
+    }
+    return t;
+}
+
 // The exponential form of the linear path: p(x) = exp2(z c - mc) * al, 0 for z = -inf.
 SD_DEV double tree_prob(float z, float c, float mc, double al) {
     return z > -INFINITY ? (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al : 0.0;
 }
 
-// Residual chain: f_0 = p, f_{s+1} = max(0, f_s - q) / W[s].
-SD_DEV double tree_chain(double p, double q, const double* W, int t) {
+// Residual chain: f_0 = p, f_{s+1} = max(0, f_s - q) / W_s, with Winv[s] = 1 / W_s.
+SD_DEV double tree_chain(double p, double q, const double* Winv, int t) {
     double f = p;
-    for (int s = 0; s < t; ++s) f = fmax(f - q, 0.0) / W[s];
+    for (int s = 0; s < t; ++s) f = fmax(f - q, 0.0) * Winv[s];
     return f;
 }
 
@@ -78,81 +122,126 @@ SD_DEV double tree_weight(float zt, float zd, int kind, int t, float c, float mc
     return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
 }
 
-// Max and exp-sum of one row, or NaN when it holds NaN / +inf. Per thread a running max
-// with its sum in units of exp2(z c - fl(m c)), rescaled when the max grows; combined
-// over the workgroup in a fixed order. Returns S = sum exp2((z - m) c) and sets *m.
-template <bool BF16, bool VEC>
-SD_DEV double tree_row_stats(const uint8_t* row, int V, float c, float* m_out, double* red,
-                             float* redf, int* redi) {
-    const int tid = threadIdx.x;
-    float ml = -INFINITY;
-    double sl = 0.0;
+// Running max / exp-sum of one thread's share of a row: the sum is kept in units of
+// exp2(z c - fl(m c)) and rescaled when the max grows.
+struct RowAcc {
+    float m = -INFINITY;
+    double s = 0.0;
     int bad = 0;
-    for (int i0 = tid * 8; i0 < V; i0 += kTreeTile) {
+    template <class T8>
+    SD_DEV void add(const T8& z8, float c) {
         float z[8];
-        load8<BF16, VEC>(row, V, i0, z);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = z8.get(e);
         float mt = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             bad |= (z[e] != z[e]) | (z[e] == INFINITY);
             mt = fmaxf(mt, z[e]);
         }
-        if (mt > ml) {
-            if (ml > -INFINITY) sl *= exp2((double)(ml * c) - (double)(mt * c));
-            ml = mt;
+        if (mt > m) {
+            if (m > -INFINITY) s *= exp2((double)(m * c) - (double)(mt * c));
+            m = mt;
         }
-        if (ml > -INFINITY) {
-            const float mc = ml * c;
+        if (m > -INFINITY) {
+            const float mc = m * c;
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc += __builtin_amdgcn_exp2f(fmaf(z[e], c, -mc));
-            sl += (double)acc;
+            s += (double)acc;
         }
     }
-    bad = block_max_i<kTreeNT>(bad, redi);
-    const float m = block_max<kTreeNT>(ml, redf);
+};
+
+// Workgroup max and S = sum exp2((z - m) c) from the threads' accumulators (fixed order);
+// NaN when the row holds NaN / +inf.
+SD_DEV double row_acc_finish(const RowAcc& r, float c, float* m_out, double* red, float* redf,
+                             int* redi) {
+    const int bad = block_max_i<kTreeNT>(r.bad, redi);
+    const float m = block_max<kTreeNT>(r.m, redf);
     const float mc = m * c;
-    const double mine = ml > -INFINITY ? sl * exp2((double)(ml * c) - (double)mc) : 0.0;
-    double S = block_sum<kTreeNT>(mine, red);
+    const double mine = r.m > -INFINITY ? r.s * exp2((double)(r.m * c) - (double)mc) : 0.0;
+    const double S = block_sum<kTreeNT>(mine, red);
     *m_out = m;
     if (bad) return (double)NAN;
     // from units of exp2(z c - mc) to exp2((z - m) c): m c = mc + emc exactly
     return m > -INFINITY ? S * exp2(-(double)fmaf(m, c, -mc)) : 0.0;
 }
 
-// One pass over the row pair: sub-chunk sums of the weights into sub[] (LDS); returns the
-// total (fixed order).
+// Max and exp-sum of a position's target row and, with both, of its draft row, in one
+// pass with two tiles of loads in flight per thread.
+template <bool BF16, bool VEC>
+SD_DEV void tree_row_stats(const uint8_t* trow, const uint8_t* drow, bool both, int V, float c,
+                           float* mt, double* St, float* md, double* Sd, double* red,
+                           float* redf, int* redi) {
+    const int tid = threadIdx.x;
+    RowAcc at, ad;
+    for (int i0 = tid * 8; i0 < V; i0 += 2 * kTreeTile) {
+        const int i1 = i0 + kTreeTile;
+        const Tok8<BF16> z0 = load8r<BF16, VEC>(trow, V, i0), z1 = load8r<BF16, VEC>(trow, V, i1);
+        Tok8<BF16> y0, y1;
+        if (both) {
+            y0 = load8r<BF16, VEC>(drow, V, i0);
+            y1 = load8r<BF16, VEC>(drow, V, i1);
+        }
+        at.add(z0, c);
+        at.add(z1, c);
+        if (both) {
+            ad.add(y0, c);
+            ad.add(y1, c);
+        }
+    }
+    *St = row_acc_finish(at, c, mt, red, redf, redi);
+    if (both) *Sd = row_acc_finish(ad, c, md, red, redf, redi);
+}
+
+// One pass over the row pair with two tiles of loads in flight per thread: sub-chunk sums
+// of the weights into sub[] (LDS; every wave's sum of a tile goes to wsub, then four wave
+// sums per sub-chunk, fixed order); returns the total (fixed order).
+constexpr int kTreeMaxTile = SPECDEC_MAX_V / kTreeTile;
 template <bool BF16, bool VEC>
 SD_DEV double tree_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int kind,
                         int t, float mct, double alt, float mcd, double ald, const double* W,
-                        double* sub, double* wred) {
+                        double* sub, double* wsub, double* red) {
+    constexpr int NW = kTreeNT / kWave;
     const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
     const int ntile = (a.V + kTreeTile - 1) / kTreeTile;
-    for (int tile = 0; tile < ntile; ++tile) {
-        const int i0 = tile * kTreeTile + tid * 8;
-        float zt[8], zd[8];
-        load8<BF16, VEC>(trow, a.V, i0, zt);
-        if (kind != TW_P) load8<BF16, VEC>(drow, a.V, i0, zd);
-        double s = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            s += tree_weight(zt[e], kind != TW_P ? zd[e] : -INFINITY, kind, t, a.c, mct, alt, mcd,
-                             ald, W);
-        s = wave_sum(s);
-        if (l == 0) wred[w] = s;
-        __syncthreads();
-        if (tid < kTreeSubPerTile) {
-            constexpr int WPS = kTreeSub / 8 / kWave;   // waves per sub-chunk
-            double x = 0.0;
-#pragma unroll
-            for (int i = 0; i < WPS; ++i) x += wred[tid * WPS + i];
-            sub[tile * kTreeSubPerTile + tid] = x;
+    for (int tile = 0; tile < ntile; tile += 2) {
+        const int i0 = tile * kTreeTile + tid * 8, i1 = i0 + kTreeTile;
+        const Tok8<BF16> zt0 = load8r<BF16, VEC>(trow, a.V, i0);
+        const Tok8<BF16> zt1 = load8r<BF16, VEC>(trow, a.V, i1);
+        Tok8<BF16> zd0, zd1;
+        if (kind != TW_P) {
+            zd0 = load8r<BF16, VEC>(drow, a.V, i0);
+            zd1 = load8r<BF16, VEC>(drow, a.V, i1);
         }
-        __syncthreads();
+        double s0 = 0.0, s1 = 0.0;
+#pragma unroll 2
+        for (int e = 0; e < 8; ++e) {
+            s0 += tree_weight(zt0.get(e), kind != TW_P ? zd0.get(e) : -INFINITY, kind, t, a.c,
+                              mct, alt, mcd, ald, W);
+            s1 += tree_weight(zt1.get(e), kind != TW_P ? zd1.get(e) : -INFINITY, kind, t, a.c,
+                              mct, alt, mcd, ald, W);
+        }
+        s0 = wave_sum(s0);
+        s1 = wave_sum(s1);
+        if (l == 0) {
+            wsub[tile * NW + w] = s0;
+            if (tile + 1 < ntile) wsub[(tile + 1) * NW + w] = s1;
+        }
     }
+    __syncthreads();
+    constexpr int WPS = kTreeSub / 8 / kWave;          // waves per sub-chunk
+    for (int q = tid; q < ntile * kTreeSubPerTile; q += kTreeNT) {
+        double x = 0.0;
+#pragma unroll
+        for (int i = 0; i < WPS; ++i) x += wsub[q * WPS + i];
+        sub[q] = x;
+    }
+    __syncthreads();
     // the total, in a fixed order (sub-chunks past the vocabulary hold 0)
     const int nsub = (a.V + kTreeSub - 1) / kTreeSub;
-    return block_sum<kTreeNT>(tid < nsub ? sub[tid] : 0.0, wred);
+    return block_sum<kTreeNT>(tid < nsub ? sub[tid] : 0.0, red);
 }
 
 // Inverse CDF over the weights whose sub-chunk sums are in sub[]: the smallest x with
@@ -220,11 +309,11 @@ template <bool BF16, bool VEC>
 SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
     using Lt = Layout<BF16, VEC>;
     __shared__ double red[kTreeNT / kWave + 1];
-    __shared__ double wred[kTreeNT / kWave];
+    __shared__ double wsub[kTreeMaxTile * (kTreeNT / kWave)];
     __shared__ float redf[kTreeNT / kWave];
     __shared__ int redi[kTreeNT / kWave];
     __shared__ double sub[kTreeMaxSub];
-    __shared__ double sW[SPECDEC_MAX_TREE];
+    __shared__ double sW[SPECDEC_MAX_TREE];        // 1 / W_s of the residuals so far
     __shared__ int s_path[SPECDEC_MAX_TREE];
     __shared__ int s_flags, s_x;
     __shared__ unsigned long long s_kids;
@@ -276,9 +365,9 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
             __syncthreads();
             unsigned long long kids = s_kids;
             float mt, md = 0.f;
-            const double St = tree_row_stats<BF16, VEC>(trow, a.V, a.c, &mt, red, redf, redi);
-            double Sd = 1.0;
-            if (kids) Sd = tree_row_stats<BF16, VEC>(drow, a.V, a.c, &md, red, redf, redi);
+            double St, Sd = 1.0;
+            tree_row_stats<BF16, VEC>(trow, drow, kids != 0, a.V, a.c, &mt, &St, &md, &Sd, red,
+                                      redf, redi);
             if (!(St > 0.0 && St < INFINITY && mt > -INFINITY) ||
                 (kids && !(Sd > 0.0 && Sd < INFINITY && md > -INFINITY))) {
                 flags |= SPECDEC_ERR_NONFINITE;
@@ -289,7 +378,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
             const double ald = kids ? exp2(-(double)fmaf(md, a.c, -mcd)) / Sd : 0.0;
             if (!kids) {                             // bonus from p at a leaf
                 const double Wt = tree_pass<BF16, VEC>(a, trow, drow, TW_P, 0, mct, alt, mcd,
-                                                       ald, sW, sub, wred);
+                                                       ald, sW, sub, wsub, red);
                 (void)Wt;
                 x = tree_draw<BF16, VEC>(a, trow, drow, TW_P, 0, mct, alt, mcd, ald, sW, sub,
                                          a.u_smp[b], red, redi);
@@ -314,17 +403,17 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
                 if (next >= 0) break;
                 // rejected: the residual mass after t + 1 rejections
                 const double Wn = tree_pass<BF16, VEC>(a, trow, drow, TW_RESID, t + 1, mct, alt,
-                                                       mcd, ald, sW, sub, wred);
+                                                       mcd, ald, sW, sub, wsub, red);
                 if (!(Wn > 0.0)) {
                     // no residual mass (not possible in exact arithmetic): draw from the
                     // distribution the child was tested against
                     flags |= SPECDEC_ERR_ZFALLBACK;
                     kind = TW_TESTED;
                     (void)tree_pass<BF16, VEC>(a, trow, drow, TW_TESTED, t, mct, alt, mcd, ald, sW,
-                                               sub, wred);
+                                               sub, wsub, red);
                     break;
                 }
-                if (tid == 0) sW[t] = Wn;
+                if (tid == 0) sW[t] = 1.0 / Wn;
                 __syncthreads();
                 ++t;
             }

@@ -377,3 +377,12 @@ def make_tree(seed: int = 0, B: int = 16, V: int = 32000, dtype: str = "bf16", T
     return TreeInputs(B, V, N, max_nodes, dtype, float(np.float32(T)), np.ascontiguousarray(target),
                       np.ascontiguousarray(draft), tokens.astype(np.int32), parent, cu, u_accept,
                       u_sample)
+
+
+# Tree workloads: B requests with U{n_lo..n_hi}-node trees (children of a node are
+# independent draws from its draft row), target N(0, target_std), draft = target +
+# N(0, noise_std), bf16 rows; paged KV as the headline workload.
+TREE_WORKLOADS = {
+    "t1": dict(B=128, V=128256, dtype="bf16", T=0.7, n_range=(8, 24), target_std=3.0,
+               noise_std=0.5, branch=0.5),
+}
