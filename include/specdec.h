@@ -130,6 +130,17 @@ typedef struct specdec_params {
     int32_t        top_k_max;    /* with top_k: the largest active top_k[b] allowed; the
                                     workspace is sized for it (>= 0; above 1024 those
                                     rows take the multi-pass select)                    */
+    /* Stopping ("Keep cache validity aligned with the committed token history",
+     * paragraph 6 lists EOS and output caps among the cases to test): when the accepted
+     * proposals contain the request's end-of-sequence token, or the request may emit
+     * fewer tokens than the cycle would, the output ends there: y_1 .. y_L with
+     * L = the first EOS position (inclusive), or the cap, whichever is smaller, if that
+     * falls within the accepted proposals; then nothing is drawn, num_emitted = L and
+     * num_accepted = L (the cache keeps the pending token and y_1 .. y_L). A drawn
+     * replacement or bonus token equal to EOS just ends the output naturally. Neither
+     * array changes the transform or the path the rows take. */
+    const int32_t* eos_token;    /* [B] device or NULL; < 0: none                        */
+    const int32_t* max_emit;     /* [B] device or NULL; <= 0: no cap                     */
 } specdec_params;
 
 /* Bytes of device workspace specdec_verify needs for these sizes (16-byte aligned); 0

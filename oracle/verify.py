@@ -37,6 +37,12 @@ Readings taken where the pages leave a step open (each is listed in the design n
   top-k); top_p <= 0 or >= 1 leaves the row unchanged.
 * the bonus token is emitted only when all proposals are accepted (section 2, section 6
   "Bad bonus-token logic").
+* stopping ("Keep cache validity aligned with the committed token history", paragraph 6
+  names EOS and output caps among the cases to test): a request's output ends at the first
+  accepted proposal equal to its end-of-sequence token (inclusive), or after its cap of
+  tokens, when that falls within the accepted proposals; then nothing is drawn and the
+  accepted count is the number of tokens kept (the cache keeps their states). A drawn
+  replacement or bonus equal to EOS ends the output naturally.
 * temperature, top-k and top-p may differ between the requests of a batch; within a
   request the same values shape every p_i and q_i. A request whose temperature is not
   a positive finite number, whose top_p is NaN, or whose active top_k exceeds the
@@ -311,6 +317,21 @@ def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: 
     return RequestResult(res.a, res.emitted, err | res.flags, res, rows_t, rows_d)
 
 
+def _stop(r: RequestResult, eos, cap) -> RequestResult:
+    """Truncate one request's output at its first accepted EOS or at its cap."""
+    L = r.a + 1
+    if eos is not None and eos >= 0:
+        for i, y in enumerate(r.emitted[:r.a]):
+            if y == eos:
+                L = i + 1
+                break
+    if cap is not None and 0 < cap < L:
+        L = cap
+    if L > r.a:
+        return r
+    return RequestResult(L, r.emitted[:L], r.err, r.probs, r.rows_t, r.rows_d)
+
+
 @dataclass
 class BatchResult:
     num_accepted: np.ndarray     # int32 [B]
@@ -330,7 +351,8 @@ def _decode_rows(x: np.ndarray, dtype: str) -> np.ndarray:
 def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
                  T, top_k, max_k: int, dtype: str,
                  requests: Optional[Sequence[int]] = None,
-                 keep_probs: bool = True, top_p=1.0, top_k_max=None) -> BatchResult:
+                 keep_probs: bool = True, top_p=1.0, top_k_max=None, eos=None,
+                 max_emit=None) -> BatchResult:
     """Batched verification over packed ragged rows.
 
     target: [K+B, V] (fp32 values, or bf16 bit patterns as uint16); the rows of request b
@@ -364,6 +386,9 @@ def verify_batch(target, draft, draft_tokens, cu_draft, u_accept, u_sample,
         r = verify_request(t_rows, d_rows, np.asarray(draft_tokens[lo:hi]),
                            np.asarray(u_accept[lo:hi]), u_sample[b], Ts[b], ks[b], V, keep_probs,
                            ps[b], top_k_max)
+        if r.a >= 0:
+            r = _stop(r, None if eos is None else int(eos[b]),
+                      None if max_emit is None else int(max_emit[b]))
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

@@ -74,13 +74,19 @@ class SpecdecParams(ctypes.Structure):
     _fields_ = [
         ("temperature", ctypes.c_void_p), ("top_k", ctypes.c_void_p), ("top_p", ctypes.c_void_p),
         ("top_k_max", ctypes.c_int32),
+        ("eos_token", ctypes.c_void_p), ("max_emit", ctypes.c_void_p),
     ]
 
 
-def _params(B: int, dev, temperatures, top_ks, top_ps, top_k_max):
+def _params(B: int, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens=None,
+            max_emit=None):
     """SpecdecParams for optional per-request tensors, or None when none is given."""
-    if temperatures is None and top_ks is None and top_ps is None:
+    if all(x is None for x in (temperatures, top_ks, top_ps, eos_tokens, max_emit)):
         return None
+    if eos_tokens is not None:
+        _check(eos_tokens, "eos_tokens", torch.int32, B, dev)
+    if max_emit is not None:
+        _check(max_emit, "max_emit", torch.int32, B, dev)
     if temperatures is not None:
         _check(temperatures, "temperatures", torch.float32, B, dev)
     if top_ks is not None:
@@ -89,10 +95,10 @@ def _params(B: int, dev, temperatures, top_ks, top_ps, top_k_max):
             raise ValueError("top_k_max is required with top_ks")
     if top_ps is not None:
         _check(top_ps, "top_ps", torch.float32, B, dev)
-    return SpecdecParams(_ptr(temperatures) if temperatures is not None else None,
-                         _ptr(top_ks) if top_ks is not None else None,
-                         _ptr(top_ps) if top_ps is not None else None,
-                         int(top_k_max) if top_k_max is not None else 0)
+    opt = lambda t: _ptr(t) if t is not None else None
+    return SpecdecParams(opt(temperatures), opt(top_ks), opt(top_ps),
+                         int(top_k_max) if top_k_max is not None else 0, opt(eos_tokens),
+                         opt(max_emit))
 
 
 class KvPagedCacheStruct(ctypes.Structure):
@@ -205,7 +211,8 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                    debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
                    temperatures: Optional[torch.Tensor] = None,
                    top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
-                   top_k_max: Optional[int] = None) -> None:
+                   top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
+                   max_emit: Optional[torch.Tensor] = None) -> None:
     """Enqueue one verification step on torch's current stream (shapes as in the header).
     temperatures / top_ks / top_ps: optional per-request [B] device tensors replacing the
     scalars (top_k_max bounds the active top_ks)."""
@@ -230,7 +237,7 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     _check(num_emitted, "num_emitted", torch.int32, B, dev)
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
-    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max)
+    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
     st = lib.specdec_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(cu_draft),
         _ptr(u_accept), _ptr(u_sample), B, K, max_k, V, float(temperature), int(top_k),
@@ -326,7 +333,8 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
                   debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
                   temperatures: Optional[torch.Tensor] = None,
                   top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
-                  top_k_max: Optional[int] = None) -> None:
+                  top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
+                  max_emit: Optional[torch.Tensor] = None) -> None:
     """Enqueue append -> verify -> rollback of one cycle as fused launches."""
     lib = load_library()
     dev = target_logits.device
@@ -353,7 +361,7 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
     _check(num_emitted, "num_emitted", torch.int32, B, dev)
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
-    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max)
+    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
     st = lib.specdec_cycle(
         ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
         dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,

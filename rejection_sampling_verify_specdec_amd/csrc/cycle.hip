@@ -263,6 +263,8 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.nch = p.nch;
     sa.topk = p.filter;
     sa.c = c;
+    sa.eos = per_request ? per_request->eos_token : nullptr;
+    sa.cap = per_request ? per_request->max_emit : nullptr;
     sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(vws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);

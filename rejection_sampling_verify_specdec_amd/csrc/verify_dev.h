@@ -1079,6 +1079,8 @@ struct SampleArgs {
     specdec_debug dbg;
     Decision* prec;          // analytics: [K] the row pair of every proposal position, else null
     double* wacc;            // analytics: [K][nch][kSSub] sub-chunk sums of max(0, p - q)
+    const int* eos;          // [B] end-of-sequence token per request (< 0 none), or null
+    const int* cap;          // [B] most tokens a request may emit (<= 0 none), or null
 };
 
 constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
@@ -1260,15 +1262,29 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         for (int o = 32; o > 0; o >>= 1) flags |= __shfl_xor(flags, o, kWave);
         const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE |
                                    SPECDEC_ERR_PARAM)) != 0;
+        // stopping: the output ends at the first accepted EOS (inclusive) or at the cap,
+        // when that falls within the accepted proposals; then nothing is drawn
+        int L = j + 1;
+        if (a.eos) {
+            const int eos = a.eos[b];
+            const unsigned long long hit = __ballot(lane < j && eos >= 0 && y == eos);
+            if (hit) L = __ffsll((long long)hit);
+        }
+        if (a.cap) {
+            const int cap = a.cap[b];
+            if (cap > 0 && cap < L) L = cap;
+        }
+        const bool stop = L <= j;
+        const int acc_n = stop ? L : j;            // proposals kept
         if (publish) {
             if (lane < k) {
                 if (a.dbg.p_y) a.dbg.p_y[lo + lane] = P;
                 if (a.dbg.q_y) a.dbg.q_y[lo + lane] = Q;
             }
-            if (!err && lane < j) a.out_tokens[lo + b + lane] = y;
+            if (!err && lane < acc_n) a.out_tokens[lo + b + lane] = y;
             if (lane == 0) {
-                a.num_acc[b] = err ? -1 : j;
-                a.num_emit[b] = err ? 0 : j + 1;
+                a.num_acc[b] = err ? -1 : acc_n;
+                a.num_emit[b] = err ? 0 : (stop ? L : j + 1);
                 if (flags) atomicOr(a.err_word, flags);
                 if (a.dbg.req_flags) a.dbg.req_flags[b] = flags;
             }
@@ -1281,7 +1297,7 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
             d.k = k;
             d.pad = d.pad3 = d.pad4 = 0;
             d.c = cf;
-            d.mode = err ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
+            d.mode = (err || stop) ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
             d.row_t = lo + b + j;
             d.row_d = j < k ? lo + j : 0;
             const float mt = s_m[j];
@@ -1859,6 +1875,7 @@ struct WsPlan {
     int kc;                  // the chunk k of a top-p-alone row
 };
 
+// the transform arrays (stopping arrays alone keep the scalar path)
 static inline bool per_request(const specdec_params* pr) {
     return pr && (pr->temperature || pr->top_k || pr->top_p);
 }

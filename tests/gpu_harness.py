@@ -72,7 +72,7 @@ class VerifyOnDevice:
     def __init__(self, vin: VerifyInputs, device=None, max_k: Optional[int] = None,
                  top_k: Optional[int] = None, T: Optional[float] = None, top_p: float = 1.0,
                  temps=None, top_ks=None, top_ps=None, top_k_max: Optional[int] = None,
-                 analytics: bool = False):
+                 analytics: bool = False, eos=None, max_emit=None):
         d = device or dev()
         self.vin = vin
         self.max_k = vin.max_k if max_k is None else max_k
@@ -83,7 +83,10 @@ class VerifyOnDevice:
         self.temps, self.top_ps = f32(temps), f32(top_ps)
         self.top_ks = None if top_ks is None else torch.tensor(np.asarray(top_ks, np.int32), device=d)
         self.top_k_max = top_k_max
-        self.params = binding._params(vin.B, d, self.temps, self.top_ks, self.top_ps, top_k_max)
+        i32 = lambda x: None if x is None else torch.tensor(np.asarray(x, np.int32), device=d)
+        self.eos, self.max_emit = i32(eos), i32(max_emit)
+        self.params = binding._params(vin.B, d, self.temps, self.top_ks, self.top_ps, top_k_max,
+                                      self.eos, self.max_emit)
         self.T = vin.T if T is None else T
         self.tgt = _logits_t(vin.target, vin.dtype, d)
         self.dft = _logits_t(vin.draft.reshape(vin.K, vin.V), vin.dtype, d)
@@ -129,7 +132,7 @@ class VerifyOnDevice:
             out_tokens=self.out_tokens, num_accepted=self.num_acc, num_emitted=self.num_emit,
             err_word=self.err, workspace=self.ws, debug=self.dbg if debug else None,
             top_p=self.top_p, temperatures=self.temps, top_ks=self.top_ks, top_ps=self.top_ps,
-            top_k_max=self.top_k_max)
+            top_k_max=self.top_k_max, eos_tokens=self.eos, max_emit=self.max_emit)
 
     def result(self) -> GpuVerify:
         torch.cuda.synchronize()
@@ -148,14 +151,14 @@ def run_verify(vin: VerifyInputs, **kw) -> GpuVerify:
 
 
 def oracle_verify(vin: VerifyInputs, requests=None, keep_probs=False, max_k=None, top_k=None,
-                  T=None, top_p=1.0, top_k_max=None):
+                  T=None, top_p=1.0, top_k_max=None, eos=None, max_emit=None):
     """T, top_k, top_p: scalars or per-request arrays."""
     return oracle.verify_batch(vin.target, vin.draft, vin.draft_tokens, vin.cu_draft,
                                vin.u_accept, vin.u_sample, vin.T if T is None else T,
                                vin.top_k if top_k is None else top_k,
                                vin.max_k if max_k is None else max_k, vin.dtype,
                                requests=requests, keep_probs=keep_probs, top_p=top_p,
-                               top_k_max=top_k_max)
+                               top_k_max=top_k_max, eos=eos, max_emit=max_emit)
 
 
 @dataclass
@@ -165,6 +168,7 @@ class Report:
     flagged: int = 0
     flagged_mismatch: int = 0
     flagged_nucleus: int = 0
+    stopped: int = 0
     max_rel_p: float = 0.0
     max_rel_S: float = 0.0
     max_rel_W: float = 0.0
@@ -273,6 +277,13 @@ def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, to
                     rep.fail(f"req {b}: after flagged accept mismatch token {gx} vs {x}")
             else:
                 rep.fail(f"req {b}: accepted {ga} vs oracle {oa} (margin {float(margins[first]):.3e})")
+            continue
+        if len(r.emitted) == oa:
+            # stopped at an accepted EOS or the cap: no draw
+            got = [int(x) for x in g.out_tokens[lo + b: lo + b + oa]]
+            rep.stopped += 1
+            if int(g.num_emitted[b]) != oa or got != r.emitted:
+                rep.fail(f"req {b}: stopped output {got} (n={g.num_emitted[b]}) vs {r.emitted}")
             continue
         if int(g.num_emitted[b]) != oa + 1:
             rep.fail(f"req {b}: num_emitted {g.num_emitted[b]} vs {oa + 1}")
