@@ -334,6 +334,47 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* =====================================================================================
+ * Contiguous KV cache
+ * ===================================================================================== */
+
+/* One contiguous buffer per request with a write pointer ("Walk through KV-cache updates
+ * when speculative decoding rejects some draft tokens": on a contiguous buffer rollback
+ * rewinds the write pointer). All device memory owned by the caller. Entry t of request b
+ * (layer l, K or V) lives at pool[l][kv][b][t]. */
+typedef struct kv_contig_cache {
+    void*    pool;            /* bf16 [L][2][batch][max_len][H][D]                     */
+    int32_t  num_layers;      /* L >= 1                                                */
+    int32_t  num_kv_heads;    /* H >= 1                                                */
+    int32_t  head_dim;        /* D >= 1; H*D*2 bytes must be a multiple of 16          */
+    int32_t  max_len;         /* entries per request, >= 1                             */
+    int32_t  batch;           /* requests the pool holds, >= B of every call           */
+    int32_t* seq_lens;        /* [batch] valid entries (the write pointer)             */
+    int32_t* state;           /* [1] KV_ERR_* sticky bits and KV_APPEND_REJECTED       */
+} kv_contig_cache;
+
+/*
+ * kv_contig_append - provisional append of n_b = cu_new[b+1] - cu_new[b] entries per
+ * request at seq_lens[b] .. seq_lens[b] + n_b - 1 (same k_new / v_new / cu_new layout as
+ * kv_paged_append). All-or-nothing: an entry past max_len (KV_ERR_NOMEM) or an invalid
+ * argument on device (KV_ERR_APPEND: n_b < 0, cu_new[0] != 0, cu_new[B] != N, seq_len
+ * outside [0, max_len]) leaves every request unchanged and sets KV_APPEND_REJECTED, which
+ * a successful append clears. Host checks as kv_paged_append (B <= batch). Three launches
+ * on `stream` (check, copy, commit); no workspace.
+ */
+int kv_contig_append(const kv_contig_cache* cache, int32_t B, const void* k_new,
+                     const void* v_new, const int32_t* cu_new, int32_t N, hipStream_t stream);
+
+/*
+ * kv_contig_rollback - rewind every request's write pointer to its committed prefix:
+ * drop k_b - a_b entries (draft = 0, the target's cache after a cycle that appended
+ * k_b + 1), or max(0, k_b - 1 - a_b) (draft = 1, the draft's convention as in
+ * kv_rollback_draft). Invalid requests (a_b < 0, a_b > k_b, more dropped than held) are
+ * skipped and set KV_ERR_ROLLBACK; no-op after an append that was not applied. One launch.
+ */
+int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* num_accepted,
+                       const int32_t* cu_draft, int32_t draft, hipStream_t stream);
+
+/* =====================================================================================
  * Draft trees
  * ===================================================================================== */
 

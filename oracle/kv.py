@@ -250,25 +250,50 @@ class PagedKV:
 
 class ContiguousKV:
     """Second model: one contiguous buffer per request with a write pointer that rollback
-    rewinds ("Walk through KV-cache updates ...": the contiguous alternative)."""
+    rewinds ("Walk through KV-cache updates ...": the contiguous alternative). With
+    ``max_len`` an append that would pass it is not applied (KV_ERR_NOMEM and
+    KV_APPEND_REJECTED, like the paged append), and invalid rollback requests are skipped
+    and flagged."""
 
-    def __init__(self, prefixes: List[np.ndarray]):
+    def __init__(self, prefixes: List[np.ndarray], max_len: Optional[int] = None):
         # prefixes[b]: uint16 [L][2][len_b][H][D]
         self.buf = [np.array(p, dtype=np.uint16, copy=True) for p in prefixes]
         self.len = [p.shape[2] for p in prefixes]
+        self.max_len = max_len
+        self.state = 0
 
-    def append(self, k_new: np.ndarray, v_new: np.ndarray, cu_new: Sequence[int]) -> None:
-        for b in range(len(self.buf)):
-            lo, hi = int(cu_new[b]), int(cu_new[b + 1])
+    def append(self, k_new: np.ndarray, v_new: np.ndarray, cu_new: Sequence[int]) -> int:
+        B = len(self.buf)
+        cu = [int(c) for c in cu_new]
+        n = [cu[b + 1] - cu[b] for b in range(B)]
+        self.state &= ~KV_APPEND_REJECTED
+        if cu[0] != 0 or cu[B] != int(k_new.shape[1]) or any(x < 0 for x in n):
+            self.state |= KV_ERR_APPEND | KV_APPEND_REJECTED
+            return KV_ERR_APPEND
+        if self.max_len is not None and any(self.len[b] + n[b] > self.max_len for b in range(B)):
+            self.state |= KV_ERR_NOMEM | KV_APPEND_REJECTED
+            return KV_ERR_NOMEM
+        for b in range(B):
+            lo, hi = cu[b], cu[b + 1]
             ent = np.stack([k_new[:, lo:hi], v_new[:, lo:hi]], axis=1)   # [L][2][n][H][D]
             self.buf[b] = np.concatenate([self.buf[b][:, :, :self.len[b]], ent], axis=2)
             self.len[b] += hi - lo
+        return 0
 
     def rollback(self, num_accepted: Sequence[int], cu_draft: Sequence[int],
-                 draft: bool = False) -> None:
+                 draft: bool = False) -> int:
+        if self.state & KV_APPEND_REJECTED:
+            return 0
+        err = 0
         for b in range(len(self.buf)):
             k, a = int(cu_draft[b + 1]) - int(cu_draft[b]), int(num_accepted[b])
-            self.len[b] -= max(0, k - 1 - a) if draft else k - a
+            drop = max(0, k - 1 - a) if draft else k - a
+            if k < 0 or a < 0 or a > k or drop > self.len[b]:
+                err |= KV_ERR_ROLLBACK
+                continue
+            self.len[b] -= drop
+        self.state |= err
+        return err
 
     def view(self, b: int, start: int = 0) -> np.ndarray:
         return self.buf[b][:, :, start:self.len[b]]

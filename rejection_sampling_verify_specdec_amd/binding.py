@@ -47,6 +47,7 @@ EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
     "specdec_cycle_workspace_size", "specdec_cycle", "specdec_tree_verify", "kv_tree_commit",
+    "kv_contig_append", "kv_contig_rollback",
 ]
 
 
@@ -113,6 +114,15 @@ class KvPagedCacheStruct(ctypes.Structure):
     ]
 
 
+class KvContigCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("pool", ctypes.c_void_p),
+        ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("max_len", ctypes.c_int32), ("batch", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p), ("state", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -155,6 +165,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specdec_tree_verify.restype = ctypes.c_int
     lib.kv_tree_commit.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32, vp]
     lib.kv_tree_commit.restype = ctypes.c_int
+    lib.kv_contig_append.argtypes = [ctypes.POINTER(KvContigCacheStruct), i32, vp, vp, vp, i32, vp]
+    lib.kv_contig_append.restype = ctypes.c_int
+    lib.kv_contig_rollback.argtypes = [ctypes.POINTER(KvContigCacheStruct), i32, vp, vp, i32, vp]
+    lib.kv_contig_rollback.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -480,3 +494,47 @@ def kv_tree_commit(cache: PagedKVCache, num_accepted: torch.Tensor, accepted_nod
                             _ptr(cu_nodes), int(accepted_nodes.numel()), _stream(dev))
     if st != SPECDEC_OK:
         raise SpecdecError("kv_tree_commit", st)
+
+
+class ContigKVCache:
+    """Device tensors of one contiguous cache plus the C struct that points at them."""
+
+    def __init__(self, pool: torch.Tensor, seq_lens: torch.Tensor, state: torch.Tensor):
+        if pool.dim() != 6 or pool.dtype != torch.bfloat16 or pool.shape[1] != 2:
+            raise ValueError("pool must be bf16 [L][2][batch][max_len][H][D]")
+        L, _, Bc, M, H, D = pool.shape
+        _check(pool, "pool", torch.bfloat16, device=pool.device)
+        _check(seq_lens, "seq_lens", torch.int32, Bc, pool.device)
+        _check(state, "state", torch.int32, 1, pool.device)
+        self.pool, self.seq_lens, self.state = pool, seq_lens, state
+        self.device = pool.device
+        self.struct = KvContigCacheStruct(pool.data_ptr(), L, H, D, M, Bc, seq_lens.data_ptr(),
+                                          state.data_ptr())
+
+
+def kv_contig_append(cache: ContigKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                     cu_new: torch.Tensor) -> None:
+    lib = load_library()
+    dev = cache.device
+    B = cu_new.numel() - 1
+    _check(cu_new, "cu_new", torch.int32, B + 1, dev)
+    N = k_new.shape[1] if k_new.dim() == 4 else 0
+    _check(k_new, "k_new", torch.bfloat16, device=dev)
+    _check(v_new, "v_new", torch.bfloat16, device=dev)
+    st = lib.kv_contig_append(ctypes.byref(cache.struct), B, _ptr(k_new) if N else None,
+                              _ptr(v_new) if N else None, _ptr(cu_new), N, _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("kv_contig_append", st)
+
+
+def kv_contig_rollback(cache: ContigKVCache, num_accepted: torch.Tensor, cu_draft: torch.Tensor,
+                       draft: bool = False) -> None:
+    lib = load_library()
+    dev = cache.device
+    B = cu_draft.numel() - 1
+    _check(num_accepted, "num_accepted", torch.int32, B, dev)
+    _check(cu_draft, "cu_draft", torch.int32, B + 1, dev)
+    st = lib.kv_contig_rollback(ctypes.byref(cache.struct), B, _ptr(num_accepted), _ptr(cu_draft),
+                                1 if draft else 0, _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("kv_contig_rollback", st)

@@ -58,7 +58,64 @@ __global__ __launch_bounds__(kTreeGatherNT) void k_kv_tree_gather(KvArgs a,
     tree_gather_body(a, num_acc, nodes, cu, N, blockIdx.x / (a.L * 2), blockIdx.x % (a.L * 2));
 }
 
+__global__ __launch_bounds__(kContigNT) void k_contig_check(ContigArgs a, const int* __restrict__ cu,
+                                                            int B, int N) {
+    contig_check_body(a, cu, B, N);
+}
+
+__global__ __launch_bounds__(256) void k_contig_copy(ContigArgs a, const uint8_t* __restrict__ knew,
+                                                     const uint8_t* __restrict__ vnew,
+                                                     const int* __restrict__ cu, int B, int N) {
+    contig_copy_body(a, knew, vnew, cu, B, N, blockIdx.x, blockIdx.y);
+}
+
+__global__ __launch_bounds__(kContigNT) void k_contig_commit(ContigArgs a, const int* __restrict__ cu,
+                                                             int B) {
+    contig_commit_body(a, cu, B);
+}
+
+__global__ __launch_bounds__(kContigNT) void k_contig_rollback(ContigArgs a,
+                                                               const int* __restrict__ num_acc,
+                                                               const int* __restrict__ cu, int B,
+                                                               int draft) {
+    contig_rollback_body(a, num_acc, cu, B, draft);
+}
+
 }  // namespace sd
+
+extern "C" int kv_contig_append(const kv_contig_cache* cache, int32_t B, const void* k_new,
+                                const void* v_new, const int32_t* cu_new, int32_t N,
+                                hipStream_t stream) {
+    using namespace sd;
+    if (!contig_ok(cache) || B < 1 || B > cache->batch || N < 0 || !cu_new) return SPECDEC_EINVAL;
+    if (N > 0 && (!k_new || !v_new || ((uintptr_t)k_new & 15) || ((uintptr_t)v_new & 15)))
+        return SPECDEC_EINVAL;
+    if ((long long)cache->num_layers * 2 > 65535) return SPECDEC_EINVAL;
+    const ContigArgs a = contig_args(cache);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_contig_check, dim3(1), dim3(kContigNT), 0, stream, a, cu_new, B, N);
+    const unsigned tiles = (unsigned)((N + kContigTPW - 1) / kContigTPW);
+    if (tiles > 0)
+        hipLaunchKernelGGL(k_contig_copy, dim3(tiles, (unsigned)a.L * 2), dim3(256), 0, stream, a,
+                           reinterpret_cast<const uint8_t*>(k_new),
+                           reinterpret_cast<const uint8_t*>(v_new), cu_new, B, N);
+    hipLaunchKernelGGL(k_contig_commit, dim3(1), dim3(kContigNT), 0, stream, a, cu_new, B);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}
+
+extern "C" int kv_contig_rollback(const kv_contig_cache* cache, int32_t B,
+                                  const int32_t* num_accepted, const int32_t* cu_draft,
+                                  int32_t draft, hipStream_t stream) {
+    using namespace sd;
+    if (!contig_ok(cache) || B < 1 || B > cache->batch || !num_accepted || !cu_draft ||
+        (draft != 0 && draft != 1))
+        return SPECDEC_EINVAL;
+    const ContigArgs a = contig_args(cache);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_contig_rollback, dim3(1), dim3(kContigNT), 0, stream, a, num_accepted,
+                       cu_draft, B, draft);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}
 
 extern "C" size_t kv_paged_append_workspace_size(int32_t B, int32_t N) {
     if (B < 1 || N < 0) return 0;

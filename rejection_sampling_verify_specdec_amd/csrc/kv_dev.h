@@ -483,6 +483,113 @@ SD_DEV void rollback_body(const KvArgs& a, const int* __restrict__ num_acc,
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Contiguous cache: a buffer per request and a write pointer.
+// ---------------------------------------------------------------------------------------
+struct ContigArgs {
+    uint8_t* pool;
+    int L, H, D, max_len, batch;
+    int* seq_lens;
+    int* state;
+};
+
+constexpr int kContigNT = 1024;      // check / commit / rollback workgroup
+constexpr int kContigTPW = 16;       // tokens per copy workgroup
+
+// Check of one append (one workgroup): every request's entries fit and the offsets are
+// sound; sets or clears KV_APPEND_REJECTED (with KV_ERR_NOMEM / KV_ERR_APPEND).
+SD_DEV void contig_check_body(const ContigArgs& a, const int* __restrict__ cu, int B, int N) {
+    __shared__ int redi[kContigNT / kWave];
+    int nomem = 0, bad = 0;
+    for (int b = threadIdx.x; b < B; b += kContigNT) {
+        const int n = cu[b + 1] - cu[b], s = a.seq_lens[b];
+        if (n < 0 || s < 0 || s > a.max_len) bad = 1;
+        else if ((long long)s + n > a.max_len) nomem = 1;
+    }
+    if (threadIdx.x == 0 && (cu[0] != 0 || cu[B] != N)) bad = 1;
+    nomem = block_max_i<kContigNT>(nomem, redi);
+    bad = block_max_i<kContigNT>(bad, redi);
+    if (threadIdx.x == 0) {
+        int st = *a.state & ~KV_APPEND_REJECTED;
+        if (bad) st |= KV_ERR_APPEND | KV_APPEND_REJECTED;
+        else if (nomem) st |= KV_ERR_NOMEM | KV_APPEND_REJECTED;
+        *a.state = st;
+    }
+}
+
+// Copy of kContigTPW entries of one layer-plane: entry e of request b (cu[b] <= e <
+// cu[b+1]) goes to slot seq_lens[b] + (e - cu[b]).
+SD_DEV void contig_copy_body(const ContigArgs& a, const uint8_t* __restrict__ knew,
+                             const uint8_t* __restrict__ vnew, const int* __restrict__ cu, int B,
+                             int N, int tile, int ulk) {
+    if (*a.state & KV_APPEND_REJECTED) return;
+    const size_t ub = (size_t)a.H * a.D * 2;
+    const int nvec = (int)(ub / 16);
+    const int l = ulk >> 1, kv = ulk & 1;
+    const uint8_t* src = kv ? vnew : knew;
+    for (int r = 0; r < kContigTPW; ++r) {
+        const int e = tile * kContigTPW + r;
+        if (e >= N) break;
+        int lo = 0, hi = B;                    // largest b with cu[b] <= e
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (cu[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        const int slot = a.seq_lens[lo] + (e - cu[lo]);
+        const u32x4* sp = reinterpret_cast<const u32x4*>(src + ((size_t)l * N + e) * ub);
+        u32x4* dp = reinterpret_cast<u32x4*>(
+            a.pool + ((((size_t)l * 2 + kv) * a.batch + lo) * a.max_len + slot) * ub);
+        for (int q = threadIdx.x; q < nvec; q += blockDim.x)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(sp + q), dp + q);
+    }
+}
+
+// Commit of an applied append: the write pointers move past the new entries.
+SD_DEV void contig_commit_body(const ContigArgs& a, const int* __restrict__ cu, int B) {
+    if (*a.state & KV_APPEND_REJECTED) return;
+    for (int b = threadIdx.x; b < B; b += blockDim.x) a.seq_lens[b] += cu[b + 1] - cu[b];
+}
+
+// Rewind of every request's write pointer to its committed prefix.
+SD_DEV void contig_rollback_body(const ContigArgs& a, const int* __restrict__ num_acc,
+                                 const int* __restrict__ cu, int B, int draft) {
+    __shared__ int redi[kContigNT / kWave];
+    if (*a.state & KV_APPEND_REJECTED) return;
+    int err = 0;
+    for (int b = threadIdx.x; b < B; b += kContigNT) {
+        const int k = cu[b + 1] - cu[b], acc = num_acc[b], s = a.seq_lens[b];
+        const int drop = draft ? max(0, k - 1 - acc) : k - acc;
+        if (k < 0 || acc < 0 || acc > k || drop > s || s > a.max_len) err = 1;
+        else a.seq_lens[b] = s - drop;
+    }
+    err = block_max_i<kContigNT>(err, redi);
+    if (threadIdx.x == 0 && err) atomicOr(a.state, KV_ERR_ROLLBACK);
+}
+
+static inline bool contig_ok(const kv_contig_cache* c) {
+    if (!c || !c->pool || !c->seq_lens || !c->state) return false;
+    if (c->num_layers < 1 || c->num_kv_heads < 1 || c->head_dim < 1 || c->max_len < 1 ||
+        c->batch < 1)
+        return false;
+    if (((size_t)c->num_kv_heads * c->head_dim * 2) % 16 != 0) return false;
+    if (((uintptr_t)c->pool & 15) != 0) return false;
+    return true;
+}
+
+static inline ContigArgs contig_args(const kv_contig_cache* c) {
+    ContigArgs a;
+    a.pool = reinterpret_cast<uint8_t*>(c->pool);
+    a.L = c->num_layers;
+    a.H = c->num_kv_heads;
+    a.D = c->head_dim;
+    a.max_len = c->max_len;
+    a.batch = c->batch;
+    a.seq_lens = c->seq_lens;
+    a.state = c->state;
+    return a;
+}
+
 static inline bool geometry_ok(const kv_paged_cache* c) {
     if (!c || !c->pool || !c->block_tables || !c->seq_lens || !c->refcount || !c->free_list ||
         !c->free_count || !c->state)

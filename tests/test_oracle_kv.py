@@ -310,3 +310,17 @@ def test_target_and_draft_caches_track_the_committed_history(seed):
             assert np.array_equal(dft.logical_view(b), _entries(1, b, 0, hist[b][:keep]))
         tgt.check_invariants()
         dft.check_invariants()
+
+
+def test_contiguous_capacity_all_or_nothing_and_invalid_rollbacks():
+    from oracle.kv import KV_APPEND_REJECTED
+    pre = [np.zeros((1, 2, n, 1, 2), np.uint16) for n in (3, 9)]
+    c = ContiguousKV(pre, max_len=10)
+    k = np.ones((1, 3, 1, 2), np.uint16)
+    # request 1 would hold 11 entries: nothing applied
+    assert c.append(k, k, [0, 1, 3]) == KV_ERR_NOMEM and c.len == [3, 9]
+    assert c.state & KV_APPEND_REJECTED
+    assert c.rollback([0, 0], [0, 1, 2]) == 0 and c.len == [3, 9]      # no-op after it
+    assert c.append(k[:, :2], k[:, :2], [0, 1, 2]) == 0 and c.len == [4, 10]
+    # a > k is skipped and flagged; the valid request rewinds
+    assert c.rollback([2, 0], [0, 1, 2]) == KV_ERR_ROLLBACK and c.len == [4, 9]
