@@ -58,6 +58,8 @@ def parse():
                         "(a known-size reference for HBM traffic counters)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum CPU time the oracle baseline runs for")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="processes for the n-core oracle baseline (0: min(16, available))")
     return p.parse_args()
 
 
@@ -103,6 +105,54 @@ def cpu_baseline(vin, kv, min_seconds: float, top_p: float):
             "sample": (f"{reps} whole cycles of the workload ({vin.K} positions each): fp64 "
                        f"verify {t_verify:.2f} s + paged append/rollback {t_kv:.2f} s, "
                        f"input generation and copies excluded")}
+
+
+def _oracle_shard(path, reqs, T, top_k, max_k, dtype, top_p):
+    """One worker of the n-core baseline: verify its requests from memory-mapped inputs."""
+    import oracle
+    a = {k: np.load(os.path.join(path, k + ".npy"), mmap_mode="r")
+         for k in ("target", "draft", "tokens", "cu", "u_acc", "u_smp")}
+    t0 = time.perf_counter()
+    oracle.verify_batch(a["target"], a["draft"], a["tokens"], a["cu"], a["u_acc"], a["u_smp"], T,
+                        top_k, max_k, dtype, requests=reqs, keep_probs=False, top_p=top_p)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_ncores(vin, top_p: float, workers: int, min_seconds: float = 2.0):
+    """The oracle's verification sharded by request over a pool of fresh processes (one
+    thread each), inputs memory-mapped from a temporary directory; whole batches repeated
+    for at least min_seconds of wall time. The paged append / rollback (sequential by
+    definition, and ~2% of the one-core time) are left out of this figure."""
+    import multiprocessing as mp
+    import tempfile
+    with tempfile.TemporaryDirectory(dir="/tmp") as path:
+        for k, x in (("target", vin.target), ("draft", vin.draft), ("tokens", vin.draft_tokens),
+                     ("cu", vin.cu_draft), ("u_acc", vin.u_accept), ("u_smp", vin.u_sample)):
+            np.save(os.path.join(path, k + ".npy"), np.ascontiguousarray(x))
+        shards = [list(range(w, vin.B, workers)) for w in range(workers)]
+        env = {"OMP_NUM_THREADS": "1", "OPENBLAS_NUM_THREADS": "1", "MKL_NUM_THREADS": "1"}
+        old = {k: os.environ.get(k) for k in env}
+        os.environ.update(env)
+        try:
+            with mp.get_context("spawn").Pool(workers) as pool:
+                pool.starmap(_oracle_shard, [(path, [0], vin.T, vin.top_k, vin.max_k, vin.dtype,
+                                              top_p)] * workers)        # warm the workers
+                reps, t = 0, 0.0
+                while reps == 0 or t < min_seconds:
+                    t0 = time.perf_counter()
+                    pool.starmap(_oracle_shard, [(path, sh, vin.T, vin.top_k, vin.max_k,
+                                                  vin.dtype, top_p) for sh in shards])
+                    t += time.perf_counter() - t0
+                    reps += 1
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    return {"value": vin.K * reps / t, "unit": "positions/s", "cores": workers, "kind": "oracle",
+            "sample": (f"{reps} verifications of the whole batch ({vin.K} positions), requests "
+                       f"spread over {workers} processes; paged append / rollback excluded")}
 
 
 def acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp, out, nacc,
@@ -292,7 +342,8 @@ def main():
     vin = synth.make_verify(wl, seed=args.seed,
                             **({} if args.top_k is None else {"top_k": args.top_k}))
     top_p = args.top_p
-    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + args.steps + 2)
+    # the pool holds the warm-up, the timed cycles and as many again for the percentiles
+    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + 2 * args.steps + 2)
     print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
           f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
 
@@ -340,8 +391,8 @@ def main():
     evs = {i: (binding.HipEvent(), binding.HipEvent()) for i in timed}
     main_s = torch.cuda.current_stream(d)
     side_s = torch.cuda.Stream(d)                      # default priority
-    ev_stats = [binding.HipEvent(timing=False) for _ in range(n)]
-    ev_kv = [binding.HipEvent(timing=False) for _ in range(n)]
+    ev_stats = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
+    ev_kv = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
 
     def step(i):
         dbg = binding.SpecdecDebug()
@@ -395,6 +446,17 @@ def main():
     stats_ms = [evs[i][0].elapsed_ms(evs[i][1]) for i in timed]
     stats_avg_s = float(np.mean(stats_ms)) / 1e3
     ms_per_step = elapsed / args.steps * 1e3
+    # per-cycle times (median, p10, p90) from events around each of as many further cycles,
+    # outside the timed region
+    cyc = []
+    for i in range(n, n + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(i)
+        e1.record()
+        cyc.append((e0, e1))
+    torch.cuda.synchronize()
+    cyc_ms = np.array([a.elapsed_time(b) for a, b in cyc])
     acceptance = acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
                                   out, nacc, nemit, err, ws, top_p, pr, ms_per_step)
     es = 2 if vin.dtype == "bf16" else 4
@@ -434,6 +496,7 @@ def main():
                                 f"{kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
                    "global_batch": B, "positions_per_step": K, "parallelism": "single GPU",
                    "schedule": args.schedule},
+        "cycle_ms_p10_p50_p90": [float(np.percentile(cyc_ms, q)) for q in (10, 50, 90)],
         "achieved_hbm_gbps": cycle_gbps,
         "pct_peak_hbm": 100.0 * cycle_gbps / PEAK_GBPS,
         "cycle_bytes": cycle_bytes,
@@ -448,6 +511,9 @@ def main():
     res["acceptance"] = acceptance
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        if workers > 1 and not args.per_request:
+            res["cpu_baseline_ncores"] = cpu_baseline_ncores(vin, top_p, workers)
     print(json.dumps(res))
 
 
