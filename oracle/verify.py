@@ -318,7 +318,9 @@ def verify_request(t_rows, d_rows, tokens, u_accept, u_sample, T: float, top_k: 
 
 
 def _stop(r: RequestResult, eos, cap) -> RequestResult:
-    """Truncate one request's output at its first accepted EOS or at its cap."""
+    """Truncate one request's output at its first accepted EOS or at its cap. A cut
+    request draws nothing, so the flag that describes the draw (ERR_ZFALLBACK) is dropped;
+    ERR_QZERO still reports every evaluated position."""
     L = r.a + 1
     if eos is not None and eos >= 0:
         for i, y in enumerate(r.emitted[:r.a]):
@@ -329,7 +331,7 @@ def _stop(r: RequestResult, eos, cap) -> RequestResult:
         L = cap
     if L > r.a:
         return r
-    return RequestResult(L, r.emitted[:L], r.err, r.probs, r.rows_t, r.rows_d)
+    return RequestResult(L, r.emitted[:L], r.err & ~ERR_ZFALLBACK, r.probs, r.rows_t, r.rows_d)
 
 
 @dataclass

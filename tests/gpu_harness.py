@@ -217,8 +217,9 @@ def _resample(vin: VerifyInputs, b: int, a: int, T: float, top_k: int, top_p: fl
 
 
 def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, top_k=None,
-                   check_debug: bool = True, top_p=1.0) -> Report:
-    """T, top_k, top_p: scalars or per-request arrays."""
+                   check_debug: bool = True, top_p=1.0, eos=None, max_emit=None) -> Report:
+    """T, top_k, top_p: scalars or per-request arrays; eos, max_emit: the stopping arrays
+    the call was given (needed only to judge requests whose nucleus is too close to call)."""
     B, K = vin.B, vin.K
     per = lambda x: np.broadcast_to(np.asarray(x), (B,))
     Ts = per(vin.T if T is None else T)
@@ -237,7 +238,8 @@ def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, to
                            for row in list(r.rows_t) + list(r.rows_d)):
             # a nucleus boundary too close to call: the outputs only have to be valid
             rep.flagged_nucleus += 1
-            if not (0 <= ga <= k and int(g.num_emitted[b]) == ga + 1):
+            if not (0 <= ga <= k and (int(g.num_emitted[b]) == ga + 1
+                                      or _gpu_stopped(g, b, lo, ga, eos, max_emit))):
                 rep.fail(f"req {b}: nucleus-flagged request not valid: a={ga} "
                          f"n={g.num_emitted[b]}")
             continue
@@ -271,6 +273,8 @@ def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, to
         if oa != ga:
             if float(margins[first]) < MARGIN:
                 rep.flagged_mismatch += 1
+                if _gpu_stopped(g, b, lo, ga, eos, max_emit):
+                    continue
                 x, W, m = _resample(vin, b, ga, T, top_k, top_p)
                 gx = int(g.out_tokens[lo + b + ga])
                 if gx != x and not (m is not None and m < MARGIN):
@@ -308,6 +312,15 @@ def compare_verify(vin: VerifyInputs, g: GpuVerify, o, requests=None, T=None, to
             if got[oa] == exp[oa] and not _close(float(g.picked_prob[b]), float(r.probs.picked), 1e-4):
                 rep.fail(f"req {b}: picked prob {g.picked_prob[b]} vs {r.probs.picked}")
     return rep
+
+
+def _gpu_stopped(g: GpuVerify, b: int, lo: int, ga: int, eos, max_emit) -> bool:
+    """The device stopped request b after its ga accepted tokens without a draw: the last
+    of them is the request's EOS token, or ga is its cap."""
+    if not (int(g.num_emitted[b]) == ga >= 1):
+        return False
+    return ((eos is not None and 0 <= int(eos[b]) == int(g.out_tokens[lo + b + ga - 1]))
+            or (max_emit is not None and int(max_emit[b]) == ga))
 
 
 def _cmp_row(rep: Report, what: str, row, g: GpuVerify, R: int, top_k: int,

@@ -21,6 +21,11 @@ pytestmark = pytest.mark.gpu
 ATOL = 1e-6
 
 
+def _mean(x):
+    x = x[~np.isnan(x)]
+    return float(x.mean()) if x.size else float("nan")
+
+
 def _run(vin, **kw):
     v = VerifyOnDevice(vin, analytics=True, **kw)
     v.run()
@@ -43,7 +48,7 @@ def _compare(vin, g, T=None, top_k=None, top_p=1.0, top_k_max=None):
     de = np.abs(g.expected_emitted[~ne] - E[~ne])
     log(f"[analytics] B={vin.B} K={vin.K} V={vin.V} {vin.dtype}: max |dbeta| = "
         f"{d.max() if d.size else 0:.2e}, max |dE| = {de.max() if de.size else 0:.2e}, "
-        f"mean beta {np.nanmean(beta):.4f}, mean E[A] {np.nanmean(E):.3f}")
+        f"mean beta {_mean(beta):.4f}, mean E[A] {_mean(E):.3f}")
     assert (d <= ATOL).all() and (de <= tol).all()
     return beta, E
 

@@ -43,7 +43,7 @@ def test_stopping_matches_oracle(wl, over):
     v.run()
     g = v.result()
     o = oracle_verify(vin, eos=eos, max_emit=cap)
-    rep = compare_verify(vin, g, o)
+    rep = compare_verify(vin, g, o, eos=eos, max_emit=cap)
     log(f"[stop] {wl}: {rep} stopped={rep.stopped}")
     assert not rep.errors, "\n".join(rep.errors)
     assert rep.stopped >= 3
@@ -80,7 +80,7 @@ def test_stopping_in_the_fused_cycle():
     for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
         assert np.array_equal(np.asarray(ma[f]), np.asarray(mb[f])), f
     o = oracle_verify(vin, eos=eos, max_emit=cap)
-    rep = compare_verify(vin, gb, o)
+    rep = compare_verify(vin, gb, o, eos=eos, max_emit=cap)
     assert not rep.errors, "\n".join(rep.errors)
     o_kv = oracle_kv(kv)
     o_kv.append(kv.k_new, kv.v_new, kv.cu_new)

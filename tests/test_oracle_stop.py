@@ -64,3 +64,22 @@ def test_stopped_cache_keeps_the_emitted_proposals():
     assert c.append(k, k, cu_new) == 0
     assert c.rollback(r.num_accepted, vin.cu_draft) == 0
     assert c.seq_lens == [1 + int(a) for a in r.num_accepted]
+
+
+def test_a_cut_request_draws_nothing_and_raises_no_fallback_flag():
+    # top-1 rows: p = q = one-hot on token 0. Proposal 0 is accepted (P = Q = 1); proposal 1
+    # has P = Q = 0 and is rejected with a zero residual, so the uncut request draws from p
+    # and carries QZERO | ZFALLBACK. Cut after the accepted token (cap 1, or EOS = 0), it
+    # draws nothing: QZERO stays (position 1 was evaluated), ZFALLBACK goes.
+    rows = np.array([[3.0, 1.0, 0.0, 0.0]] * 3, dtype=np.float32)
+    args = (rows, rows[:2].copy(), np.array([0, 1]), np.array([0, 2]),
+            np.array([0.5, 0.5], dtype=np.float32), np.array([0.3], dtype=np.float32),
+            1.0, 1, 2, "f32")
+    r = oracle.verify_batch(*args)
+    assert r.num_accepted[0] == 1 and r.requests[0].emitted == [0, 0]
+    assert r.err[0] == oracle.ERR_QZERO | oracle.ERR_ZFALLBACK
+    for kw in (dict(max_emit=[1]), dict(eos=[0])):
+        c = oracle.verify_batch(*args, **kw)
+        assert c.num_accepted[0] == 1 and c.num_emitted[0] == 1
+        assert c.requests[0].emitted == [0]
+        assert c.err[0] == oracle.ERR_QZERO
