@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--timing-every", type=int, default=4,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
+    p.add_argument("--team", type=int, default=0,
+                   help="tree workloads: workgroups per request walk (0: automatic)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before timing "
@@ -213,8 +215,10 @@ def tree_main(args):
     binding.load_library()
     d = torch.device("cuda:0")
     cfg = synth.TREE_WORKLOADS[args.workload]
+    print(f"# {args.workload}: drawing the synthetic trees", file=sys.stderr, flush=True)
     tin = synth.make_tree(seed=args.seed, **cfg)
     kv = synth.make_kv("c2", tin, seed=args.seed, cycles=args.warmup + args.steps + 2)
+    print(f"# {args.workload}: inputs ready, timing", file=sys.stderr, flush=True)
     B, N, V = tin.B, tin.N, tin.V
 
     def bf(x):
@@ -241,6 +245,8 @@ def tree_main(args):
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     kws = torch.empty(binding.kv_paged_append_workspace_size(B, N + B), dtype=torch.uint8, device=d)
+    tws = torch.empty(binding.specdec_tree_verify_workspace_size(B, N, tin.V), dtype=torch.uint8,
+                      device=d)
     n = args.warmup + args.steps
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in range(args.warmup, n)}
 
@@ -254,7 +260,7 @@ def tree_main(args):
         binding.specdec_tree_verify(tgt, dft, tokens, parent, cu, u_acc, u_smp,
                                     max_nodes=tin.max_nodes, temperature=tin.T, out_tokens=out,
                                     accepted_nodes=nodes, num_accepted=nacc, num_emitted=nemit,
-                                    err_word=err)
+                                    err_word=err, workspace=tws, team=args.team)
         if e:
             e[2].record()
         binding.kv_tree_commit(cache, nacc, nodes, cu)
@@ -307,7 +313,8 @@ def tree_main(args):
                                 f"{cfg['n_range'][1]}}} nodes (N={N}), V={V} bf16 T={tin.T:g}; "
                                 f"paged KV {kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
                    "global_batch": B, "parallelism": "single GPU"},
-        "tree": {"append_ms": append_ms, "verify_ms": verify_ms, "commit_ms": commit_ms,
+        "tree": {"team": args.team or "auto", "append_ms": append_ms, "verify_ms": verify_ms,
+                 "commit_ms": commit_ms,
                  "mean_accepted": float(a[a >= 0].mean()), "walk_bytes": walk,
                  "walk_gbps": walk / (verify_ms / 1e3) / 1e9,
                  "walk_frac_of_peak": walk / (verify_ms / 1e3) / 1e9 / PEAK_GBPS},

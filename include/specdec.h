@@ -64,6 +64,8 @@ extern "C" {
                                       the replacement was drawn from p_i                   */
 #define SPECDEC_ERR_UNIFORM   32   /* a uniform outside [0, 1) (or NaN)                   */
 #define SPECDEC_ERR_TREE     128   /* a draft tree's parent index outside {-1, .., j-1}   */
+#define SPECDEC_ERR_TEAM     256   /* a tree walk's workgroup waited past its bound for the
+                                      others of its request (not expected); request failed */
 #define SPECDEC_ERR_PARAM     64   /* per-request parameters invalid: temperature <= 0 or
                                       not finite, top_p NaN, or an active top_k above
                                       specdec_params.top_k_max                            */
@@ -401,17 +403,25 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * the drawn token at cu_nodes[b] + b; accepted_nodes [N]: the path's local node indices,
  * root first, at cu_nodes[b]; err_word [1] OR-ed SPECDEC_ERR_* bits (SPECDEC_ERR_TREE for a
  * bad parent); req_flags [B] (or NULL) each request's bits.
+ * team: workgroups that share one request's walk (each pass over a row is split among
+ * them); 0 picks min(16, max(1, CUs / B)), otherwise 1..16. The outputs do not depend on
+ * it: partial sums are combined in a fixed order.
+ * workspace: device, 16-byte aligned, >= specdec_tree_verify_workspace_size(B, N, V)
+ * bytes, owned by the caller, contents need not be initialized (the call resets its
+ * counters first); not used by other calls while this one runs.
  * Host: B >= 1, N = cu_nodes[B], 0 <= max_nodes <= SPECDEC_MAX_TREE, 1 <= V <=
- * SPECDEC_MAX_V, temperature > 0 and finite; EINVAL otherwise, before anything is
- * enqueued. No workspace: the walk keeps its state in LDS, one 1024-thread workgroup per
- * request.
+ * SPECDEC_MAX_V, temperature > 0 and finite, 0 <= team <= 16; EINVAL otherwise,
+ * EWORKSPACE for a missing / small / misaligned workspace, before anything is enqueued.
+ * Two launches on `stream` (counter reset, walk).
  */
+size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V);
 int specdec_tree_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
                         const int32_t* tree_tokens, const int32_t* tree_parent,
                         const int32_t* cu_nodes, const float* u_accept, const float* u_sample,
                         int32_t B, int32_t N, int32_t max_nodes, int32_t V, float temperature,
                         int32_t* out_tokens, int32_t* accepted_nodes, int32_t* num_accepted,
                         int32_t* num_emitted, int32_t* err_word, int32_t* req_flags,
+                        int32_t team, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
 /*

@@ -33,7 +33,9 @@ ERR_ZFALLBACK = 16
 ERR_UNIFORM = 32
 ERR_PARAM = 64
 ERR_TREE = 128
+ERR_TEAM = 256
 MAX_TREE = 64
+MAX_TREE_TEAM = 16
 KV_ERR_NOMEM = 64
 KV_ERR_APPEND = 128
 KV_ERR_ROLLBACK = 256
@@ -46,7 +48,8 @@ MAX_V = 2097152
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
-    "specdec_cycle_workspace_size", "specdec_cycle", "specdec_tree_verify", "kv_tree_commit",
+    "specdec_cycle_workspace_size", "specdec_cycle", "specdec_tree_verify_workspace_size",
+    "specdec_tree_verify", "kv_tree_commit",
     "kv_contig_append", "kv_contig_rollback",
 ]
 
@@ -160,8 +163,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   vp, vp, i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
     lib.specdec_cycle.restype = ctypes.c_int
+    lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32]
+    lib.specdec_tree_verify_workspace_size.restype = sz
     lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                        vp, vp, vp, vp, vp, vp, vp]
+                                        vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.specdec_tree_verify.restype = ctypes.c_int
     lib.kv_tree_commit.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32, vp]
     lib.kv_tree_commit.restype = ctypes.c_int
@@ -440,14 +445,20 @@ class HipEvent:
             pass
 
 
+def specdec_tree_verify_workspace_size(B: int, N: int, V: int) -> int:
+    return int(load_library().specdec_tree_verify_workspace_size(B, N, V))
+
+
 def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                         tree_tokens: torch.Tensor, tree_parent: torch.Tensor,
                         cu_nodes: torch.Tensor, u_accept: torch.Tensor, u_sample: torch.Tensor,
                         *, max_nodes: int, temperature: float, out_tokens: torch.Tensor,
                         accepted_nodes: torch.Tensor, num_accepted: torch.Tensor,
                         num_emitted: torch.Tensor, err_word: torch.Tensor,
-                        req_flags: Optional[torch.Tensor] = None) -> None:
-    """Enqueue the verification of one draft tree per request (shapes as in the header)."""
+                        workspace: torch.Tensor, req_flags: Optional[torch.Tensor] = None,
+                        team: int = 0) -> None:
+    """Enqueue the verification of one draft tree per request (shapes as in the header);
+    ``team`` workgroups share each request's walk (0: automatic)."""
     lib = load_library()
     dev = target_logits.device
     dtype = _logits_dtype(target_logits)
@@ -470,12 +481,14 @@ def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     _check(err_word, "err_word", torch.int32, 1, dev)
     if req_flags is not None:
         _check(req_flags, "req_flags", torch.int32, B, dev)
+    _check(workspace, "workspace", torch.uint8, device=dev)
     st = lib.specdec_tree_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(tree_tokens), _ptr(tree_parent),
         _ptr(cu_nodes), _ptr(u_accept), _ptr(u_sample), B, N, max_nodes, V, float(temperature),
         _ptr(out_tokens), _ptr(accepted_nodes) if N else None, _ptr(num_accepted),
         _ptr(num_emitted),
-        _ptr(err_word), _ptr(req_flags) if req_flags is not None else None, _stream(dev))
+        _ptr(err_word), _ptr(req_flags) if req_flags is not None else None, int(team),
+        _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
         raise SpecdecError("specdec_tree_verify", st)
 

@@ -1,6 +1,6 @@
-// Verification of draft trees for gfx950: one 1024-thread workgroup per request walks its
-// tree (tree_dev.h). The cache step that keeps the accepted path is kv_tree_commit
-// (kv.hip).
+// Verification of draft trees for gfx950: a team of 1024-thread workgroups walks each
+// request's tree, sharing every pass over a row (tree_dev.h). The cache step that keeps
+// the accepted path is kv_tree_commit (kv.hip).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -11,12 +11,45 @@
 
 namespace sd {
 
+// Block x serves request x % Bp as member x / Bp (Bp: B rounded up to a multiple of 8):
+// every request's first member is dispatched before any second one, and blocks are dealt
+// to the 8 XCDs in turn, so the members of a team share an XCD (and its L2) when the
+// dispatcher keeps that order; nothing depends on it.
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kTreeNT) void k_tree_verify(TreeArgs a) {
-    tree_walk_body<BF16, VEC>(a, blockIdx.x);
+    const int Bp = (a.B + 7) / 8 * 8;
+    const int b = blockIdx.x % Bp, mem = blockIdx.x / Bp;
+    if (b >= a.B) return;
+    tree_walk_body<BF16, VEC>(a, b, mem);
+}
+
+__global__ void k_tree_reset(int* ctr, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) ctr[i] = 0;
+}
+
+struct TreeWs {
+    size_t ctr_bytes, ring_bytes, total;
+    int nchunk, nsub, slot;
+};
+
+static bool tree_ws(int32_t B, int32_t N, int32_t V, TreeWs* w) {
+    if (B < 1 || N < 0 || V < 1 || V > SPECDEC_MAX_V) return false;
+    w->nchunk = (V + kTreeChunk - 1) / kTreeChunk;
+    w->nsub = (V + kTreeSub - 1) / kTreeSub;
+    w->slot = 64 * w->nchunk;           // >= 4 * nsub (weights); 4 per wave-chunk (stats)
+    w->ctr_bytes = ((size_t)B * kTreeCtrStride * sizeof(int) + 255) & ~(size_t)255;
+    w->ring_bytes = ((size_t)N + 2 * (size_t)B) * w->slot * sizeof(double);
+    w->total = w->ctr_bytes + w->ring_bytes;
+    return true;
 }
 
 }  // namespace sd
+
+extern "C" size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V) {
+    sd::TreeWs w;
+    return sd::tree_ws(B, N, V, &w) ? w.total : 0;
+}
 
 extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_logits,
                                    int32_t dtype, const int32_t* tree_tokens,
@@ -25,7 +58,8 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
                                    int32_t N, int32_t max_nodes, int32_t V, float temperature,
                                    int32_t* out_tokens, int32_t* accepted_nodes,
                                    int32_t* num_accepted, int32_t* num_emitted,
-                                   int32_t* err_word, int32_t* req_flags, hipStream_t stream) {
+                                   int32_t* err_word, int32_t* req_flags, int32_t team,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
     using namespace sd;
     if (B < 1 || N < 0 || V < 1 || V > SPECDEC_MAX_V || max_nodes < 0 ||
         max_nodes > SPECDEC_MAX_TREE)
@@ -40,6 +74,21 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
         return SPECDEC_EINVAL;
     const float c = (float)(1.4426950408889634074 / (double)temperature);   // log2(e) / T
     if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
+    if (team < 0 || team > kTreeMaxTeam) return SPECDEC_EINVAL;
+    TreeWs w;
+    if (!tree_ws(B, N, V, &w)) return SPECDEC_EINVAL;
+    if (!workspace || ((uintptr_t)workspace & 15) != 0 || workspace_bytes < w.total)
+        return SPECDEC_EWORKSPACE;
+    int G = team;
+    if (G == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return SPECDEC_EHIP;
+        G = cus / B;
+        G = G < 1 ? 1 : (G > kTreeMaxTeam ? kTreeMaxTeam : G);
+        if (G > w.nchunk) G = w.nchunk;
+    }
     const int es = dtype == SPECDEC_BF16 ? 2 : 4;
     const bool vec = ((size_t)V * es) % 16 == 0 && ((uintptr_t)target_logits & 15) == 0 &&
                      ((uintptr_t)draft_logits & 15) == 0;
@@ -62,13 +111,23 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     a.num_emit = num_emitted;
     a.err_word = err_word;
     a.req_flags = req_flags;
+    uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+    a.ctr = reinterpret_cast<int*>(ws);
+    a.ring = reinterpret_cast<double*>(ws + w.ctr_bytes);
+    a.nchunk = w.nchunk;
+    a.nsub = w.nsub;
+    a.slot = w.slot;
+    a.team = G;
+    const int nctr = B * kTreeCtrStride;
+    const int grid = (B + 7) / 8 * 8 * G;
     (void)hipGetLastError();
+    hipLaunchKernelGGL(k_tree_reset, dim3((nctr + 255) / 256), dim3(256), 0, stream, a.ctr, nctr);
     if (dtype == SPECDEC_BF16) {
-        if (vec) hipLaunchKernelGGL((k_tree_verify<true, true>), dim3(B), dim3(kTreeNT), 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_verify<true, false>), dim3(B), dim3(kTreeNT), 0, stream, a);
+        if (vec) hipLaunchKernelGGL((k_tree_verify<true, true>), dim3(grid), dim3(kTreeNT), 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_verify<true, false>), dim3(grid), dim3(kTreeNT), 0, stream, a);
     } else {
-        if (vec) hipLaunchKernelGGL((k_tree_verify<false, true>), dim3(B), dim3(kTreeNT), 0, stream, a);
-        else hipLaunchKernelGGL((k_tree_verify<false, false>), dim3(B), dim3(kTreeNT), 0, stream, a);
+        if (vec) hipLaunchKernelGGL((k_tree_verify<false, true>), dim3(grid), dim3(kTreeNT), 0, stream, a);
+        else hipLaunchKernelGGL((k_tree_verify<false, false>), dim3(grid), dim3(kTreeNT), 0, stream, a);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
 }

@@ -51,6 +51,12 @@ struct TreeArgs {
     int* num_emit;           // [B]
     int* err_word;           // [1]
     int* req_flags;          // [B] or null
+    double* ring;            // [(N + 2B) * slot]: request b's passes from (cu[b] + 2b) * slot
+    int* ctr;                // [B * kTreeCtrStride]: ticket and done counters, zeroed first
+    int nchunk;              // chunks (two tiles) per pass
+    int nsub;                // sub-chunks of a row
+    int slot;                // doubles per pass: 64 * nchunk (4 per wave and chunk)
+    int team;                // workgroups per request
 };
 
 // Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
@@ -122,126 +128,378 @@ SD_DEV double tree_weight(float zt, float zd, int kind, int t, float c, float mc
     return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
 }
 
-// Running max / exp-sum of one thread's share of a row: the sum is kept in units of
-// exp2(z c - fl(m c)) and rescaled when the max grows.
-struct RowAcc {
-    float m = -INFINITY;
-    double s = 0.0;
-    int bad = 0;
-    template <class T8>
-    SD_DEV void add(const T8& z8, float c) {
-        float z[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z[e] = z8.get(e);
-        float mt = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bad |= (z[e] != z[e]) | (z[e] == INFINITY);
-            mt = fmaxf(mt, z[e]);
-        }
-        if (mt > m) {
-            if (m > -INFINITY) s *= exp2((double)(m * c) - (double)(mt * c));
-            m = mt;
-        }
-        if (m > -INFINITY) {
-            const float mc = m * c;
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc += __builtin_amdgcn_exp2f(fmaf(z[e], c, -mc));
-            s += (double)acc;
-        }
-    }
+// ---------------------------------------------------------------------------------------
+// Teams: G workgroups share one request's walk. Every pass over a position's rows is cut
+// into chunks of two tiles (16384 tokens, 8 sub-chunks); a workgroup takes the next chunk
+// with an atomic ticket, writes the chunk's per-sub-chunk partials to the request's slot
+// of the workspace ring and counts the chunk done. Every member then waits for the whole
+// pass, combines the partials in a fixed order and takes the same decisions, so the
+// results do not depend on G or on which member computed which chunk. Tickets are only
+// waited for once a running workgroup holds them, so the wait always ends; it is bounded
+// all the same (SPECDEC_ERR_TEAM). A request makes at most n + 2 passes (one stats pass
+// per visited position, one per rejected child, one for the final draw), each with its
+// own slot, so a member that starts late replays the walk from the ring.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kTreeChunk = 2 * kTreeTile;                 // tokens per ticket
+constexpr int kTreeSubPerChunk = kTreeChunk / kTreeSub;   // 8
+constexpr int kTreeMaxTeam = 16;
+constexpr int kTreeCtrStride = 64;                        // ints per request: claim, done
+constexpr int kTreeDoneOff = 32;                          // done on its own 128-byte line
+constexpr int kTreeSpinLimit = 1 << 20;
+enum : int { TK_STATS = 3 };                              // pass kinds besides TW_*
+
+struct TeamLds {
+    int tk[2];                          // this workgroup's ticket, double-buffered
+    int timeout;
 };
 
-// Workgroup max and S = sum exp2((z - m) c) from the threads' accumulators (fixed order);
-// NaN when the row holds NaN / +inf.
-SD_DEV double row_acc_finish(const RowAcc& r, float c, float* m_out, double* red, float* redf,
-                             int* redi) {
-    const int bad = block_max_i<kTreeNT>(r.bad, redi);
-    const float m = block_max<kTreeNT>(r.m, redf);
-    const float mc = m * c;
-    const double mine = r.m > -INFINITY ? r.s * exp2((double)(r.m * c) - (double)mc) : 0.0;
-    const double S = block_sum<kTreeNT>(mine, red);
-    *m_out = m;
-    if (bad) return (double)NAN;
-    // from units of exp2(z c - mc) to exp2((z - m) c): m c = mc + emc exactly
-    return m > -INFINITY ? S * exp2(-(double)fmaf(m, c, -mc)) : 0.0;
+// The ring and the counters are shared by workgroups on different XCDs, whose L2 caches
+// are not coherent with each other: every access to them is an agent-scope atomic (the
+// hardware keeps those coherent without writing back or invalidating whole caches). A
+// writer waits for its ring stores to complete before the workgroup barrier that precedes
+// the done count; a reader loads the ring only after it has seen the count.
+// A team of one (solo) shares nothing: plain stores and loads, ordered by the workgroup
+// barrier.
+SD_DEV void ring_put(double* p, double x, bool solo) {
+    if (solo) *p = x;
+    else __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SD_DEV double ring_get(const double* p, bool solo) {
+    if (solo) return *p;
+    return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Max and exp-sum of a position's target row and, with both, of its draft row, in one
-// pass with two tiles of loads in flight per thread.
-template <bool BF16, bool VEC>
-SD_DEV void tree_row_stats(const uint8_t* trow, const uint8_t* drow, bool both, int V, float c,
-                           float* mt, double* St, float* md, double* Sd, double* red,
-                           float* redf, int* redi) {
-    const int tid = threadIdx.x;
-    RowAcc at, ad;
-    for (int i0 = tid * 8; i0 < V; i0 += 2 * kTreeTile) {
-        const int i1 = i0 + kTreeTile;
-        const Tok8<BF16> z0 = load8r<BF16, VEC>(trow, V, i0), z1 = load8r<BF16, VEC>(trow, V, i1);
-        Tok8<BF16> y0, y1;
-        if (both) {
-            y0 = load8r<BF16, VEC>(drow, V, i0);
-            y1 = load8r<BF16, VEC>(drow, V, i1);
+// Max m and S = sum exp2(z c - fl(m c)) of two tiles of one row over this wave (1024
+// tokens), m NaN when they hold NaN / +inf (every lane gets the wave's values).
+template <class T8>
+SD_DEV void wave_stats2(const T8& za, const T8& zb, float c, double* m_out, double* s_out) {
+    float z[16];
+    float tm = -INFINITY;
+    int bad = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        z[e] = za.get(e);
+        z[8 + e] = zb.get(e);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        bad |= (z[e] != z[e]) | (z[e] == INFINITY);
+        tm = fmaxf(tm, z[e]);
+    }
+    const float m = wave_max(tm);
+    float acc = 0.f;
+    if (m > -INFINITY) {
+        const float mc = m * c;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc += __builtin_amdgcn_exp2f(fmaf(z[e], c, -mc));
+    }
+    *m_out = wave_max_i(bad) ? (double)NAN : (double)m;
+    *s_out = wave_sum((double)acc);
+}
+
+// Weight of a token in a pass (tree_weight without the -inf tests: exp2 of -inf is 0).
+SD_DEV double team_prob(float z, float c, float mc, double al) {
+    return (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al;
+}
+SD_DEV double team_weight(float zt, float zd, int kind, int t, float c, float mct, double alt,
+                          float mcd, double ald, const double* W) {
+    const double p = team_prob(zt, c, mct, alt);
+    if (kind == TW_P) return p;
+    const double q = team_prob(zd, c, mcd, ald);
+    if (kind == TW_TESTED) return tree_chain(p, q, W, t);
+    return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
+}
+
+// Two tiles of the target row and, with DR, of the draft row: one chunk's loads.
+template <bool BF16>
+struct Quad {
+    Tok8<BF16> t0, t1, d0, d1;
+};
+
+// Eight tokens at i0 < V from whole 16-byte vectors (no bounds test).
+template <bool BF16>
+SD_DEV Tok8<BF16> load8f(const uint8_t* __restrict__ row, int i0) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(row) + (BF16 ? i0 / 8 : i0 / 4);
+    Tok8<BF16> t;
+#pragma unroll
+    for (int h = 0; h < (BF16 ? 1 : 2); ++h) t.v[h] = __builtin_nontemporal_load(p + h);
+    return t;
+}
+
+// FULL: the chunk lies inside the row and rows are whole vectors, so every load is issued
+// unconditionally (the compiler can then keep the next chunk's loads in flight).
+template <bool BF16, bool VEC, bool DR, bool FULL>
+SD_DEV Quad<BF16> team_load(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int ch) {
+    const int i0 = ch * kTreeChunk + threadIdx.x * 8, i1 = i0 + kTreeTile;
+    Quad<BF16> q;
+    if constexpr (FULL && VEC) {
+        q.t0 = load8f<BF16>(trow, i0);
+        q.t1 = load8f<BF16>(trow, i1);
+        if constexpr (DR) {
+            q.d0 = load8f<BF16>(drow, i0);
+            q.d1 = load8f<BF16>(drow, i1);
         }
-        at.add(z0, c);
-        at.add(z1, c);
-        if (both) {
-            ad.add(y0, c);
-            ad.add(y1, c);
+    } else {
+        q.t0 = load8r<BF16, VEC>(trow, a.V, i0);
+        q.t1 = load8r<BF16, VEC>(trow, a.V, i1);
+        if constexpr (DR) {
+            q.d0 = load8r<BF16, VEC>(drow, a.V, i0);
+            q.d1 = load8r<BF16, VEC>(drow, a.V, i1);
         }
     }
-    *St = row_acc_finish(at, c, mt, red, redf, redi);
-    if (both) *Sd = row_acc_finish(ad, c, md, red, redf, redi);
+    return q;
 }
 
-// One pass over the row pair with two tiles of loads in flight per thread: sub-chunk sums
-// of the weights into sub[] (LDS; every wave's sum of a tile goes to wsub, then four wave
-// sums per sub-chunk, fixed order); returns the total (fixed order).
-constexpr int kTreeMaxTile = SPECDEC_MAX_V / kTreeTile;
-template <bool BF16, bool VEC>
-SD_DEV double tree_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int kind,
-                        int t, float mct, double alt, float mcd, double ald, const double* W,
-                        double* sub, double* wsub, double* red) {
-    constexpr int NW = kTreeNT / kWave;
+// Pass kinds as compile-time cases of the chunk loop.
+enum : int { KC_STATS = 0, KC_P = 1, KC_RESID1 = 2, KC_CHAIN = 3 };
+
+// One chunk (two tiles) of a pass: every wave writes its partials to the slot. Stats:
+// slot[4 wc ..] = (m_t, s_t, m_d, s_d) of the wave's 1024 tokens (wc = chunk * 16 + wave);
+// weights: slot[wt] = the wave's sum over each of its two 512-token pieces (wave-tile
+// wt = tile * 16 + wave, for wt < 4 * nsub), from which the draw finds its sub-chunk.
+template <bool BF16, int KC>
+SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kind, bool both,
+                         int t, float mct, double alt, float mcd, double ald, const double* W,
+                         double* slot) {
     const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-    const int ntile = (a.V + kTreeTile - 1) / kTreeTile;
-    for (int tile = 0; tile < ntile; tile += 2) {
-        const int i0 = tile * kTreeTile + tid * 8, i1 = i0 + kTreeTile;
-        const Tok8<BF16> zt0 = load8r<BF16, VEC>(trow, a.V, i0);
-        const Tok8<BF16> zt1 = load8r<BF16, VEC>(trow, a.V, i1);
-        Tok8<BF16> zd0, zd1;
-        if (kind != TW_P) {
-            zd0 = load8r<BF16, VEC>(drow, a.V, i0);
-            zd1 = load8r<BF16, VEC>(drow, a.V, i1);
+    const int wt0 = 2 * ch * (kTreeNT / kWave) + w, wt1 = wt0 + kTreeNT / kWave;
+    const int nwt = 4 * a.nsub;
+    const bool solo = a.team == 1;
+    if constexpr (KC == KC_STATS) {
+        // one (m, s) per row for the wave's 1024 tokens of this chunk: entry ch * 16 + w
+        const int wc = ch * (kTreeNT / kWave) + w;
+        double m, sm;
+        wave_stats2(q.t0, q.t1, a.c, &m, &sm);
+        if (l == 0) {
+            ring_put(slot + 4 * wc, m, solo);
+            ring_put(slot + 4 * wc + 1, sm, solo);
         }
+        if (both) {
+            wave_stats2(q.d0, q.d1, a.c, &m, &sm);
+            if (l == 0) {
+                ring_put(slot + 4 * wc + 2, m, solo);
+                ring_put(slot + 4 * wc + 3, sm, solo);
+            }
+        }
+    } else {
         double s0 = 0.0, s1 = 0.0;
+        if constexpr (KC == KC_P) {              // the bonus: p alone
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s0 += team_prob(q.t0.get(e), a.c, mct, alt);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s1 += team_prob(q.t1.get(e), a.c, mct, alt);
+        } else if constexpr (KC == KC_RESID1) {  // the first residual, max(0, p - q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s0 += fmax(team_prob(q.t0.get(e), a.c, mct, alt) -
+                           team_prob(q.d0.get(e), a.c, mcd, ald), 0.0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                s1 += fmax(team_prob(q.t1.get(e), a.c, mct, alt) -
+                           team_prob(q.d1.get(e), a.c, mcd, ald), 0.0);
+        } else {                                 // longer residual chains, tested weights
 #pragma unroll 2
-        for (int e = 0; e < 8; ++e) {
-            s0 += tree_weight(zt0.get(e), kind != TW_P ? zd0.get(e) : -INFINITY, kind, t, a.c,
-                              mct, alt, mcd, ald, W);
-            s1 += tree_weight(zt1.get(e), kind != TW_P ? zd1.get(e) : -INFINITY, kind, t, a.c,
-                              mct, alt, mcd, ald, W);
+            for (int e = 0; e < 8; ++e) {
+                s0 += team_weight(q.t0.get(e), q.d0.get(e), kind, t, a.c, mct, alt, mcd, ald, W);
+                s1 += team_weight(q.t1.get(e), q.d1.get(e), kind, t, a.c, mct, alt, mcd, ald, W);
+            }
         }
         s0 = wave_sum(s0);
         s1 = wave_sum(s1);
         if (l == 0) {
-            wsub[tile * NW + w] = s0;
-            if (tile + 1 < ntile) wsub[(tile + 1) * NW + w] = s1;
+            if (wt0 < nwt) ring_put(slot + wt0, s0, solo);
+            if (wt1 < nwt) ring_put(slot + wt1, s1, solo);
         }
     }
+}
+
+// Chunks [c0, c1) of a pass: whole chunks with the next one's loads in flight (except for
+// the register-hungry chains), then a chunk that reaches past the row end with
+// bounds-tested loads.
+template <bool BF16, bool VEC, bool DR, int KC>
+SD_DEV void team_slice(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int c0,
+                       int c1, int kind, bool both, int t, float mct, double alt, float mcd,
+                       double ald, const double* W, double* slot) {
+    constexpr bool PIPE = KC != KC_CHAIN;
+    const int cfull = VEC ? min(c1, a.V / kTreeChunk) : c0;
+    if (c0 < cfull) {
+        if constexpr (PIPE) {
+            Quad<BF16> cur = team_load<BF16, VEC, DR, true>(a, trow, drow, c0);
+            for (int ch = c0; ch + 1 < cfull; ++ch) {
+                const Quad<BF16> nxt = team_load<BF16, VEC, DR, true>(a, trow, drow, ch + 1);
+                team_compute<BF16, KC>(a, cur, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+                cur = nxt;
+            }
+            team_compute<BF16, KC>(a, cur, cfull - 1, kind, both, t, mct, alt, mcd, ald, W, slot);
+        } else {
+            for (int ch = c0; ch < cfull; ++ch) {
+                const Quad<BF16> q = team_load<BF16, VEC, DR, true>(a, trow, drow, ch);
+                team_compute<BF16, KC>(a, q, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+            }
+        }
+    }
+    for (int ch = max(c0, cfull); ch < c1; ++ch) {
+        const Quad<BF16> q = team_load<BF16, VEC, DR, false>(a, trow, drow, ch);
+        team_compute<BF16, KC>(a, q, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+    }
+}
+
+// Pass k of request b by this member. A ticket is a slice of ceil(C / G) chunks (pass k:
+// tickets [k NS, (k + 1) NS), NS slices); the member takes slices while its ticket lies in
+// pass k (a ticket past it is kept for a later pass), counts its chunks done once its
+// stores have completed, then waits until all C chunks of the pass are done. `par` picks
+// the half of tk[] holding the current ticket. Returns false when the wait ran past its
+// bound.
+template <bool BF16, bool VEC>
+SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int k,
+                      int kind, bool both, int t, float mct, double alt, float mcd, double ald,
+                      const double* W, double* slot, int* claim, int* done, TeamLds& s,
+                      int& par) {
+    const int tid = threadIdx.x, l = tid % kWave;
+    const int C = a.nchunk, S = (C + a.team - 1) / a.team, NS = (C + S - 1) / S;
+    const bool solo = a.team == 1;
+    int mine = 0;                                     // chunks this member finished
+    for (;;) {
+        const int tk = solo ? k : s.tk[par];          // solo: the whole pass, no tickets
+        if (tk >= (k + 1) * NS) break;
+        int nx = 0;
+        if (tid == 0 && !solo)
+            nx = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int c0 = (tk - k * NS) * S, c1 = min(C, c0 + S);
+        if (kind == TK_STATS) {
+            if (both)
+                team_slice<BF16, VEC, true, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, mct,
+                                                      alt, mcd, ald, W, slot);
+            else
+                team_slice<BF16, VEC, false, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, mct,
+                                                       alt, mcd, ald, W, slot);
+        } else if (kind == TW_P) {
+            team_slice<BF16, VEC, false, KC_P>(a, trow, drow, c0, c1, kind, both, t, mct, alt,
+                                               mcd, ald, W, slot);
+        } else if (kind == TW_RESID && t == 1) {
+            team_slice<BF16, VEC, true, KC_RESID1>(a, trow, drow, c0, c1, kind, both, t, mct,
+                                                   alt, mcd, ald, W, slot);
+        } else {
+            team_slice<BF16, VEC, true, KC_CHAIN>(a, trow, drow, c0, c1, kind, both, t, mct, alt,
+                                                  mcd, ald, W, slot);
+        }
+        mine += c1 - c0;
+        if (solo) break;
+        // the other half: its last readers passed the barrier below one slice ago
+        if (tid == 0) s.tk[par ^ 1] = nx;
+        par ^= 1;
+        __syncthreads();
+    }
+    if (solo) {
+        __syncthreads();                              // the partials are visible to the WG
+        return true;
+    }
+    if (l == 0) __builtin_amdgcn_s_waitcnt(0);        // this wave's ring stores completed
     __syncthreads();
-    constexpr int WPS = kTreeSub / 8 / kWave;          // waves per sub-chunk
-    for (int q = tid; q < ntile * kTreeSubPerTile; q += kTreeNT) {
-        double x = 0.0;
-#pragma unroll
-        for (int i = 0; i < WPS; ++i) x += wsub[q * WPS + i];
-        sub[q] = x;
+    if (tid == 0) {
+        if (mine) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int it = 0, to = 0;
+        while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (k + 1) * C) {
+            if (++it > kTreeSpinLimit) {
+                to = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        s.timeout = to;
     }
     __syncthreads();
-    // the total, in a fixed order (sub-chunks past the vocabulary hold 0)
-    const int nsub = (a.V + kTreeSub - 1) / kTreeSub;
-    return block_sum<kTreeNT>(tid < nsub ? sub[tid] : 0.0, red);
+    return s.timeout == 0;
+}
+
+// Workgroup max / sum of two values at once, each in the order block_max / block_sum use
+// (lane butterfly, then waves in index order). red2 holds 2 * NT / 64 entries.
+SD_DEV void block_max2(float& x, float& y, float* red2) {
+    x = wave_max(x);
+    y = wave_max(y);
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    constexpr int NW = kTreeNT / kWave;
+    if (l == 0) { red2[w] = x; red2[NW + w] = y; }
+    __syncthreads();
+    x = red2[0];
+    y = red2[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) { x = fmaxf(x, red2[i]); y = fmaxf(y, red2[NW + i]); }
+    __syncthreads();
+}
+SD_DEV void block_sum2(double& x, double& y, double* red2) {
+    x = wave_sum(x);
+    y = wave_sum(y);
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    constexpr int NW = kTreeNT / kWave;
+    if (l == 0) { red2[w] = x; red2[NW + w] = y; }
+    __syncthreads();
+    x = red2[0];
+    y = red2[NW];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) { x += red2[i]; y += red2[NW + i]; }
+    __syncthreads();
+}
+
+// Max and S = sum exp2((z - m) c) of the target row and (with both) the draft row from a
+// stats slot: entries wc = 0 .. 16 C - 1 combined in index order (thread i takes i and
+// i + 1024); S is NaN when the row holds NaN / +inf.
+SD_DEV void team_stats_final(const TreeArgs& a, const double* slot, bool both, float* mt,
+                             double* St, float* md, double* Sd, double* red2, float* redf2,
+                             int* redi) {
+    const int tid = threadIdx.x;
+    const bool solo = a.team == 1;
+    const int nwc = a.nchunk * (kTreeNT / kWave);
+    // this thread's entries (at most two), each row's (m, s)
+    double m_[2][2], s_[2][2];
+    int bad = 0;
+    float mx_t = -INFINITY, mx_d = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int i = tid + h * kTreeNT;
+        m_[h][0] = m_[h][1] = -INFINITY;
+        s_[h][0] = s_[h][1] = 0.0;
+        if (i < nwc) {
+            m_[h][0] = ring_get(slot + 4 * i, solo);
+            s_[h][0] = ring_get(slot + 4 * i + 1, solo);
+            if (both) {
+                m_[h][1] = ring_get(slot + 4 * i + 2, solo);
+                s_[h][1] = ring_get(slot + 4 * i + 3, solo);
+            }
+        }
+        bad |= (m_[h][0] != m_[h][0]) | ((m_[h][1] != m_[h][1]) << 1);
+        mx_t = fmaxf(mx_t, (float)m_[h][0]);
+        mx_d = fmaxf(mx_d, (float)m_[h][1]);
+    }
+    bad = block_max_i<kTreeNT>(bad, redi);
+    block_max2(mx_t, mx_d, redf2);
+    const float mct = mx_t * a.c, mcd = mx_d * a.c;
+    double xt = 0.0, xd = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (m_[h][0] > -INFINITY) xt += s_[h][0] * exp2((double)((float)m_[h][0] * a.c) - (double)mct);
+        if (m_[h][1] > -INFINITY) xd += s_[h][1] * exp2((double)((float)m_[h][1] * a.c) - (double)mcd);
+    }
+    block_sum2(xt, xd, red2);
+    *mt = mx_t;
+    *md = mx_d;
+    *St = (bad & 1) ? (double)NAN : (mx_t > -INFINITY ? xt * exp2(-(double)fmaf(mx_t, a.c, -mct)) : 0.0);
+    *Sd = (bad & 2) ? (double)NAN : (mx_d > -INFINITY ? xd * exp2(-(double)fmaf(mx_d, a.c, -mcd)) : 0.0);
+}
+
+// Sub-chunk q's weight sum from its four waves (index order).
+SD_DEV double team_weight_sub(const double* slot, int q, bool solo) {
+    double x = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x += ring_get(slot + 4 * q + i, solo);
+    return x;
+}
+
+// The total of a weight slot, sub-chunks in index order.
+SD_DEV double team_weight_total(const TreeArgs& a, const double* slot, double* red) {
+    const int tid = threadIdx.x;
+    return block_sum<kTreeNT>(tid < a.nsub ? team_weight_sub(slot, tid, a.team == 1) : 0.0, red);
 }
 
 // Inverse CDF over the weights whose sub-chunk sums are in sub[]: the smallest x with
@@ -304,26 +562,28 @@ SD_DEV int tree_draw(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow
     return x;
 }
 
-// The walk of request b.
+// The walk of request b by member `mem` of its team; member 0 draws and writes the outputs.
 template <bool BF16, bool VEC>
-SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
+SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
     using Lt = Layout<BF16, VEC>;
     __shared__ double red[kTreeNT / kWave + 1];
-    __shared__ double wsub[kTreeMaxTile * (kTreeNT / kWave)];
     __shared__ float redf[kTreeNT / kWave];
     __shared__ int redi[kTreeNT / kWave];
     __shared__ double sub[kTreeMaxSub];
     __shared__ double sW[SPECDEC_MAX_TREE];        // 1 / W_s of the residuals so far
     __shared__ int s_path[SPECDEC_MAX_TREE];
-    __shared__ int s_flags, s_x;
+    __shared__ int s_flags;
     __shared__ unsigned long long s_kids;
     __shared__ int s_next;
+    __shared__ TeamLds tl;
+    __shared__ double red2[2 * (kTreeNT / kWave)];
+    __shared__ float redf2[2 * (kTreeNT / kWave)];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int lo = a.cu[b], hi = a.cu[b + 1], n = hi - lo;
     const bool bad_k = a.cu[0] != 0 || a.cu[a.B] != a.N || n < 0 || n > a.max_nodes || lo < 0 ||
                        hi > a.N;
     if (bad_k) {
-        if (tid == 0) {
+        if (tid == 0 && mem == 0) {
             a.num_acc[b] = -1;
             a.num_emit[b] = 0;
             atomicOr(a.err_word, SPECDEC_ERR_K);
@@ -353,10 +613,23 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
     int flags = s_flags;
     int na = 0, x = -1;
     if (!flags) {
+        int* claim = a.ctr + (size_t)b * kTreeCtrStride;
+        int* done = claim + kTreeDoneOff;
+        double* ring = a.ring + (size_t)(lo + 2 * b) * a.slot;
+        if (tid == 0 && a.team > 1)
+            tl.tk[0] = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        int par = 0;                                 // tl.tk[par]: the current ticket
+        int k = 0;      // passes so far: at most n + 2 (ring slots), checked before each
+        int wslot = -1, kind = TW_RESID, t = 0;      // the final draw's slot, kind, residual
+        float mct = 0.f, mcd = 0.f;
+        double alt = 0.0, ald = 0.0;
+        const uint8_t* trow = nullptr;
+        const uint8_t* drow = nullptr;
         int v = 0;                                   // position: 0 root, 1 + j node j
         while (true) {
-            const uint8_t* trow = a.tgt + (size_t)(lo + b + v) * a.V * Lt::ES;
-            const uint8_t* drow = a.dft + (size_t)(lo + b + v) * a.V * Lt::ES;
+            trow = a.tgt + (size_t)(lo + b + v) * a.V * Lt::ES;
+            drow = a.dft + (size_t)(lo + b + v) * a.V * Lt::ES;
             if (tid < kWave) {
                 const bool kid = lane < n && a.parent[lo + lane] == v - 1;
                 const unsigned long long m = __ballot(kid);
@@ -364,27 +637,44 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
             }
             __syncthreads();
             unsigned long long kids = s_kids;
-            float mt, md = 0.f;
-            double St, Sd = 1.0;
-            tree_row_stats<BF16, VEC>(trow, drow, kids != 0, a.V, a.c, &mt, &St, &md, &Sd, red,
-                                      redf, redi);
+            if (k > n + 1 ||
+                !team_pass<BF16, VEC>(a, trow, drow, k, TK_STATS, kids != 0, 0, 0.f, 0.0, 0.f,
+                                      0.0, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                flags |= SPECDEC_ERR_TEAM;
+                break;
+            }
+            float mt, md;
+            double St, Sd;
+            team_stats_final(a, ring + (size_t)k * a.slot, kids != 0, &mt, &St, &md, &Sd, red2,
+                             redf2, redi);
+            if (!kids) {
+                md = 0.f;
+                Sd = 1.0;
+            }
+            ++k;
             if (!(St > 0.0 && St < INFINITY && mt > -INFINITY) ||
                 (kids && !(Sd > 0.0 && Sd < INFINITY && md > -INFINITY))) {
                 flags |= SPECDEC_ERR_NONFINITE;
                 break;
             }
-            const float mct = mt * a.c, mcd = md * a.c;
-            const double alt = exp2(-(double)fmaf(mt, a.c, -mct)) / St;
-            const double ald = kids ? exp2(-(double)fmaf(md, a.c, -mcd)) / Sd : 0.0;
+            mct = mt * a.c;
+            mcd = md * a.c;
+            alt = exp2(-(double)fmaf(mt, a.c, -mct)) / St;
+            ald = kids ? exp2(-(double)fmaf(md, a.c, -mcd)) / Sd : 0.0;
             if (!kids) {                             // bonus from p at a leaf
-                const double Wt = tree_pass<BF16, VEC>(a, trow, drow, TW_P, 0, mct, alt, mcd,
-                                                       ald, sW, sub, wsub, red);
-                (void)Wt;
-                x = tree_draw<BF16, VEC>(a, trow, drow, TW_P, 0, mct, alt, mcd, ald, sW, sub,
-                                         a.u_smp[b], red, redi);
+                if (k > n + 1 ||
+                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_P, false, 0, mct, alt, mcd, ald,
+                                          sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                    flags |= SPECDEC_ERR_TEAM;
+                    break;
+                }
+                wslot = k++;
+                kind = TW_P;
+                t = 0;
                 break;
             }
-            int t = 0, kind = TW_RESID;
+            t = 0;
+            kind = TW_RESID;
             int next = -1;
             while (kids) {
                 const int j = __ffsll((long long)kids) - 1;
@@ -402,40 +692,59 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b) {
                 __syncthreads();
                 if (next >= 0) break;
                 // rejected: the residual mass after t + 1 rejections
-                const double Wn = tree_pass<BF16, VEC>(a, trow, drow, TW_RESID, t + 1, mct, alt,
-                                                       mcd, ald, sW, sub, wsub, red);
+                if (k > n + 1 ||
+                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_RESID, true, t + 1, mct, alt, mcd,
+                                          ald, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                    flags |= SPECDEC_ERR_TEAM;
+                    break;
+                }
+                const double Wn = team_weight_total(a, ring + (size_t)k * a.slot, red);
+                wslot = k++;
                 if (!(Wn > 0.0)) {
                     // no residual mass (not possible in exact arithmetic): draw from the
                     // distribution the child was tested against
                     flags |= SPECDEC_ERR_ZFALLBACK;
                     kind = TW_TESTED;
-                    (void)tree_pass<BF16, VEC>(a, trow, drow, TW_TESTED, t, mct, alt, mcd, ald, sW,
-                                               sub, wsub, red);
+                    if (k > n + 1 ||
+                        !team_pass<BF16, VEC>(a, trow, drow, k, TW_TESTED, true, t, mct, alt, mcd,
+                                              ald, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                        flags |= SPECDEC_ERR_TEAM;
+                        break;
+                    }
+                    wslot = k++;
                     break;
                 }
                 if (tid == 0) sW[t] = 1.0 / Wn;
                 __syncthreads();
                 ++t;
             }
+            if (flags & SPECDEC_ERR_TEAM) break;
             if (next >= 0) {
                 if (tid == 0) s_path[na] = next;
                 ++na;
                 v = next + 1;
                 continue;
             }
-            // every child rejected: the replacement from the last residual (or the tested
-            // distribution after a zero residual)
+            break;                                   // every child rejected
+        }
+        // the replacement (from the last residual, or the tested distribution after a zero
+        // residual) or the bonus: member 0 rescans one sub-chunk
+        if (mem == 0 && wslot >= 0 && !(flags & (SPECDEC_ERR_NONFINITE | SPECDEC_ERR_TEAM))) {
+            const double* sl = ring + (size_t)wslot * a.slot;
+            for (int q = tid; q < a.nsub; q += kTreeNT) sub[q] = team_weight_sub(sl, q, a.team == 1);
+            __syncthreads();
             x = tree_draw<BF16, VEC>(a, trow, drow, kind, t, mct, alt, mcd, ald, sW, sub,
                                      a.u_smp[b], red, redi);
-            break;
         }
         __syncthreads();
         flags |= s_flags;
     }
-    if (x < 0 && !(flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_TREE)))
+    if (mem != 0) return;
+    if (x < 0 && !(flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_TREE |
+                            SPECDEC_ERR_TEAM)))
         flags |= SPECDEC_ERR_NONFINITE;          // nothing to draw from
     const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE |
-                               SPECDEC_ERR_TREE)) != 0;
+                               SPECDEC_ERR_TREE | SPECDEC_ERR_TEAM)) != 0;
     if (tid < na && !err) {
         a.nodes_out[lo + tid] = s_path[tid];
         a.out_tokens[lo + b + tid] = a.tokens[lo + s_path[tid]];

@@ -95,8 +95,19 @@ WORKLOADS: Dict[str, Workload] = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (round to nearest, ties to even); bit patterns as uint16."""
     x = np.asarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x).reshape(-1).view(np.uint32)
+    r = np.empty(u.shape, dtype=np.uint16)
+    # in 32 bits: every non-NaN pattern is <= 0xFF800000, so adding <= 0x8000 cannot wrap
+    # (NaN lanes are replaced below); chunked to bound the temporaries
+    step = 1 << 22
+    for s in range(0, u.size, step):
+        t = u[s:s + step] >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u[s:s + step]
+        t >>= np.uint32(16)
+        r[s:s + step] = t
+    r = r.reshape(x.shape)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
@@ -384,5 +395,8 @@ def make_tree(seed: int = 0, B: int = 16, V: int = 32000, dtype: str = "bf16", T
 # N(0, noise_std), bf16 rows; paged KV as the headline workload.
 TREE_WORKLOADS = {
     "t1": dict(B=128, V=128256, dtype="bf16", T=0.7, n_range=(8, 24), target_std=3.0,
+               noise_std=0.5, branch=0.5),
+    # a small serving batch: latency of one step rather than throughput
+    "t2": dict(B=8, V=128256, dtype="bf16", T=0.7, n_range=(8, 24), target_std=3.0,
                noise_std=0.5, branch=0.5),
 }

@@ -131,3 +131,26 @@ def test_product_path_fails_loudly_without_library(tmp_path):
             binding.load_library(str(tmp_path / "nope.so"))
     finally:
         binding._lib = saved
+
+
+def test_tree_workspace_and_host_validation_without_gpu(lib):
+    # the pass ring: (N + 2B) slots of 4 doubles per 2048-token sub-chunk, after the counters
+    n = binding.specdec_tree_verify_workspace_size(128, 2071, 128256)
+    assert n >= (2071 + 256) * 4 * 63 * 8 + 128 * 64 * 4
+    assert binding.specdec_tree_verify_workspace_size(0, 0, 100) == 0
+    assert binding.specdec_tree_verify_workspace_size(1, 0, binding.MAX_V + 1) == 0
+    vp = None
+
+    def call(team=0, ws=16, nbytes=1 << 30, T=1.0, B=1, N=1, max_nodes=4, V=1000):
+        return lib.specdec_tree_verify(16, 16, binding.SPECDEC_BF16, 16, 16, 16, 16, 16, B, N,
+                                       max_nodes, V, T, 16, 16, 16, 16, 16, vp, team, ws, nbytes,
+                                       vp)
+    assert call(team=-1) == binding.SPECDEC_EINVAL
+    assert call(team=binding.MAX_TREE_TEAM + 1) == binding.SPECDEC_EINVAL
+    assert call(T=0.0) == binding.SPECDEC_EINVAL
+    assert call(max_nodes=binding.MAX_TREE + 1) == binding.SPECDEC_EINVAL
+    assert call(N=5, max_nodes=4) == binding.SPECDEC_EINVAL
+    assert call(ws=None) == binding.SPECDEC_EWORKSPACE
+    assert call(ws=17) == binding.SPECDEC_EWORKSPACE
+    assert call(nbytes=binding.specdec_tree_verify_workspace_size(1, 1, 1000) - 1,
+                team=1) == binding.SPECDEC_EWORKSPACE

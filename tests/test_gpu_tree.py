@@ -34,8 +34,9 @@ def _logits(x, dtype, d):
 
 
 class TreeOnDevice:
-    def __init__(self, tin):
+    def __init__(self, tin, team: int = 0, ws_fill: int = 0):
         d = dev()
+        self.team = team
         self.tin = tin
         self.tgt = _logits(tin.target, tin.dtype, d)
         self.dft = _logits(tin.draft, tin.dtype, d)
@@ -49,6 +50,9 @@ class TreeOnDevice:
         self.num_emit = torch.full((B,), -9, dtype=torch.int32, device=d)
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
         self.flags = torch.full((B,), -1, dtype=torch.int32, device=d)
+        # the call resets what it needs: start from arbitrary contents
+        self.ws = torch.full((binding.specdec_tree_verify_workspace_size(B, N, tin.V),), ws_fill,
+                             dtype=torch.uint8, device=d)
 
     def run(self):
         binding.specdec_tree_verify(self.tgt, self.dft, self.tokens, self.parent, self.cu,
@@ -56,7 +60,7 @@ class TreeOnDevice:
                                     temperature=self.tin.T, out_tokens=self.out,
                                     accepted_nodes=self.nodes, num_accepted=self.num_acc,
                                     num_emitted=self.num_emit, err_word=self.err,
-                                    req_flags=self.flags)
+                                    workspace=self.ws, req_flags=self.flags, team=self.team)
         torch.cuda.synchronize()
         c = lambda x: x.cpu().numpy()
         return dict(a=c(self.num_acc), n=c(self.num_emit), out=c(self.out), nodes=c(self.nodes),
@@ -249,3 +253,23 @@ def test_tree_commit_rejects_unsound_paths():
     torch.cuda.synchronize()
     assert np.array_equal(cache.seq_lens.cpu().numpy(), meta["seq_lens"])
     assert int(cache.state.item()) & binding.KV_ERR_ROLLBACK
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 128256), ("f32", 32000), ("bf16", 4001)])
+def test_team_sizes_give_identical_results(dtype, V):
+    # every member combines the chunk partials in one fixed order, so the walk, the draw
+    # and the flags do not depend on how many workgroups share a request (more members
+    # than chunks included) or on what the workspace held before the call
+    tin = synth.make_tree(seed=113, B=6, V=V, dtype=dtype, n_range=(5, 30))
+    log(f"[tree-team] B={tin.B} N={tin.N} V={V} {dtype}: team 1")
+    ref = TreeOnDevice(tin, team=1).run()
+    o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
+                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype)
+    errs, _, _ = compare_tree(tin, ref, o)
+    assert not errs, "\n".join(errs[:20])
+    for team in (2, 3, 5, 8, 16, 0):
+        log(f"[tree-team]   team {team}")
+        g = TreeOnDevice(tin, team=team, ws_fill=0xAB).run()
+        for key in ("a", "n", "out", "nodes", "flags"):
+            assert np.array_equal(g[key], ref[key]), (team, key)
+        assert g["err"] == ref["err"], team
