@@ -211,7 +211,10 @@ SD_DEV double team_weight(float zt, float zd, int kind, int t, float c, float mc
     return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
 }
 
-// Two tiles of the target row and, with DR, of the draft row: one chunk's loads.
+constexpr int kTreeWaveSpan = kTreeChunk / (kTreeNT / kWave);   // 1024 tokens per wave
+static_assert(kTreeSub == 2 * kTreeWaveSpan, "a sub-chunk is two waves' spans");
+
+// A chunk of the target row and, with DR, of the draft row: its loads.
 template <bool BF16>
 struct Quad {
     Tok8<BF16> t0, t1, d0, d1;
@@ -229,9 +232,12 @@ SD_DEV Tok8<BF16> load8f(const uint8_t* __restrict__ row, int i0) {
 
 // FULL: the chunk lies inside the row and rows are whole vectors, so every load is issued
 // unconditionally (the compiler can then keep the next chunk's loads in flight).
+// Wave w of the workgroup covers the chunk's tokens [w * 1024, w * 1024 + 1024): lane l
+// takes 8 at l * 8 and 8 at 512 + l * 8 (each load instruction reads 1 KB contiguous).
 template <bool BF16, bool VEC, bool DR, bool FULL>
 SD_DEV Quad<BF16> team_load(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int ch) {
-    const int i0 = ch * kTreeChunk + threadIdx.x * 8, i1 = i0 + kTreeTile;
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    const int i0 = ch * kTreeChunk + w * kTreeWaveSpan + l * 8, i1 = i0 + kTreeWaveSpan / 2;
     Quad<BF16> q;
     if constexpr (FULL && VEC) {
         q.t0 = load8f<BF16>(trow, i0);
@@ -254,21 +260,17 @@ SD_DEV Quad<BF16> team_load(const TreeArgs& a, const uint8_t* trow, const uint8_
 // Pass kinds as compile-time cases of the chunk loop.
 enum : int { KC_STATS = 0, KC_P = 1, KC_RESID1 = 2, KC_CHAIN = 3 };
 
-// One chunk (two tiles) of a pass: every wave writes its partials to the slot. Stats:
-// slot[4 wc ..] = (m_t, s_t, m_d, s_d) of the wave's 1024 tokens (wc = chunk * 16 + wave);
-// weights: slot[wt] = the wave's sum over each of its two 512-token pieces (wave-tile
-// wt = tile * 16 + wave, for wt < 4 * nsub), from which the draw finds its sub-chunk.
+// One chunk of a pass: every wave writes the partials of its 1024 tokens (entry wc =
+// chunk * 16 + wave) to the slot. Stats: slot[4 wc ..] = (m_t, s_t, m_d, s_d); weights:
+// slot[wc] = the wave's sum (sub-chunk q, 2048 tokens, is entries 2q and 2q + 1).
 template <bool BF16, int KC>
 SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kind, bool both,
                          int t, float mct, double alt, float mcd, double ald, const double* W,
                          double* slot) {
     const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
-    const int wt0 = 2 * ch * (kTreeNT / kWave) + w, wt1 = wt0 + kTreeNT / kWave;
-    const int nwt = 4 * a.nsub;
+    const int wc = ch * (kTreeNT / kWave) + w;
     const bool solo = a.team == 1;
     if constexpr (KC == KC_STATS) {
-        // one (m, s) per row for the wave's 1024 tokens of this chunk: entry ch * 16 + w
-        const int wc = ch * (kTreeNT / kWave) + w;
         double m, sm;
         wave_stats2(q.t0, q.t1, a.c, &m, &sm);
         if (l == 0) {
@@ -305,12 +307,8 @@ SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kin
                 s1 += team_weight(q.t1.get(e), q.d1.get(e), kind, t, a.c, mct, alt, mcd, ald, W);
             }
         }
-        s0 = wave_sum(s0);
-        s1 = wave_sum(s1);
-        if (l == 0) {
-            if (wt0 < nwt) ring_put(slot + wt0, s0, solo);
-            if (wt1 < nwt) ring_put(slot + wt1, s1, solo);
-        }
+        const double sw = wave_sum(s0 + s1);
+        if (l == 0) ring_put(slot + wc, sw, solo);
     }
 }
 
@@ -488,12 +486,9 @@ SD_DEV void team_stats_final(const TreeArgs& a, const double* slot, bool both, f
     *Sd = (bad & 2) ? (double)NAN : (mx_d > -INFINITY ? xd * exp2(-(double)fmaf(mx_d, a.c, -mcd)) : 0.0);
 }
 
-// Sub-chunk q's weight sum from its four waves (index order).
+// Sub-chunk q's weight sum: its two waves' entries in order.
 SD_DEV double team_weight_sub(const double* slot, int q, bool solo) {
-    double x = 0.0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x += ring_get(slot + 4 * q + i, solo);
-    return x;
+    return ring_get(slot + 2 * q, solo) + ring_get(slot + 2 * q + 1, solo);
 }
 
 // The total of a weight slot, sub-chunks in index order.
@@ -572,6 +567,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
     __shared__ double sub[kTreeMaxSub];
     __shared__ double sW[SPECDEC_MAX_TREE];        // 1 / W_s of the residuals so far
     __shared__ int s_path[SPECDEC_MAX_TREE];
+    __shared__ float s_zt[SPECDEC_MAX_TREE], s_zd[SPECDEC_MAX_TREE];
     __shared__ int s_flags;
     __shared__ unsigned long long s_kids;
     __shared__ int s_next;
@@ -634,6 +630,13 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 const bool kid = lane < n && a.parent[lo + lane] == v - 1;
                 const unsigned long long m = __ballot(kid);
                 if (lane == 0) s_kids = m;
+                // the children's logits at this position, for their accept tests (the
+                // loads complete during the stats pass)
+                if (kid) {
+                    const int y = a.tokens[lo + lane];
+                    s_zt[lane] = load_elem(trow, y, BF16);
+                    s_zd[lane] = load_elem(drow, y, BF16);
+                }
             }
             __syncthreads();
             unsigned long long kids = s_kids;
@@ -680,8 +683,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 const int j = __ffsll((long long)kids) - 1;
                 kids &= kids - 1;
                 if (tid == 0) {
-                    const int y = a.tokens[lo + j];
-                    const float zt = load_elem(trow, y, BF16), zd = load_elem(drow, y, BF16);
+                    const float zt = s_zt[j], zd = s_zd[j];
                     const double q = tree_prob(zd, a.c, mcd, ald);
                     const double P = tree_chain(tree_prob(zt, a.c, mct, alt), q, sW, t);
                     if (q == 0.0) s_flags |= SPECDEC_ERR_QZERO;
