@@ -1,4 +1,4 @@
-// Verification of a draft tree, one workgroup per request (gfx950).
+// Verification of a draft tree by a team of workgroups per request (gfx950).
 //
 // The rule generalizes "Speculative decoding: accelerate LLM generation without changing
 // its answers", section 2, to several proposals for the same position: the children of a
@@ -14,7 +14,8 @@
 // The walk is sequential per request and reads only the rows it visits: one pass over a
 // position's target (and draft) row for its max and exp-sum, one pass over the row pair
 // per rejected child (its residual mass, summed per 2048-token sub-chunk), and a rescan of
-// one sub-chunk for the draw. A workgroup of 1024 threads keeps 64 KB of loads in flight.
+// one sub-chunk for the draw. The passes themselves are split among the team (see
+// "Teams" below); every member takes the same decisions from the same combined sums.
 
 #pragma once
 
@@ -30,7 +31,6 @@ namespace sd {
 constexpr int kTreeNT = 1024;                    // threads of a walk workgroup
 constexpr int kTreeTile = kTreeNT * 8;           // tokens per tile, 8 consecutive per thread
 constexpr int kTreeSub = 2048;                   // tokens per sub-chunk (256 threads)
-constexpr int kTreeSubPerTile = kTreeTile / kTreeSub;
 constexpr int kTreeMaxSub = SPECDEC_MAX_V / kTreeSub;
 static_assert(kTreeMaxSub <= kTreeNT, "one sub-chunk sum per thread in the draw");
 static_assert(SPECDEC_MAX_TREE <= kWave, "a wave ballot covers the nodes of a request");

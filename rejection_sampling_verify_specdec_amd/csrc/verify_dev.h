@@ -230,7 +230,7 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
     // pass 0: max, invalid entries (NaN, +inf)
     float mx = -INFINITY;
     int bad = 0;
-    walk_row<BF16, NT, 4>(base, V, [&](float z) {
+    walk_row<BF16, NT, 8>(base, V, [&](float z) {
         mx = fmaxf(mx, z);
         bad |= (z != z) | (z == INFINITY);
     });
@@ -250,7 +250,7 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
         __syncthreads();
         const uint32_t prefix = s_prefix;
         const uint32_t hmask = pass == 0 ? 0u : (0xffffffffu << (shift + 8));
-        walk_row<BF16, NT, 4>(base, V, [&](float z) {
+        walk_row<BF16, NT, 8>(base, V, [&](float z) {
             const uint32_t k = f2key(z);
             if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xff], 1u);
         });
@@ -276,7 +276,7 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
     const float emc = fmaf(m, c, -mc);
     float acc = 0.f;
     int kept = 0;
-    walk_row<BF16, NT, 4>(base, V, [&](float z) {
+    walk_row<BF16, NT, 8>(base, V, [&](float z) {
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
             ++kept;
@@ -316,7 +316,7 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // ---------------------------------------------------------------------------------------
 constexpr int kTkNT = kNT;         // threads of a chunk workgroup
 constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-byte vectors)
-constexpr int kMergeNT = 128;      // threads of a merge workgroup
+constexpr int kMergeNT = 256;      // threads of a merge workgroup
 constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
 constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
@@ -755,7 +755,7 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo, fl
     uint32_t K = lo;
     const bool ok = nucleus_key<NT, Kt::KBITS, kToppRowDigit, kToppRowBins>(
         [&](auto f) {
-            walk_row<BF16, NT, 4>(base, a.V, [&](float z) {
+            walk_row<BF16, NT, 8>(base, a.V, [&](float z) {
                 if (z > -INFINITY) f(keyz(z), z);
             });
         },
@@ -763,7 +763,7 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo, fl
     const float thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
     float acc = 0.f;
     int kept = 0;
-    walk_row<BF16, NT, 4>(base, a.V, [&](float z) {
+    walk_row<BF16, NT, 8>(base, a.V, [&](float z) {
         if (z >= thr && z > -INFINITY) {
             acc += __builtin_amdgcn_exp2f(fmaf(z, c, -mc));
             ++kept;
@@ -781,10 +781,125 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo, fl
     }
 }
 
+// Top-p alone, bf16, when the candidates' complete upper set (keys >= lo) is short of the
+// nucleus: every bf16 key is one logit value, so one pass that counts the row's tokens on
+// each of the 1024 keys below lo finds the boundary exactly, each key's mass being its
+// count times one exponential (the same fixed-point mass the per-token sums use), and the
+// kept sum follows from the counts without another pass. keys[0 .. total) are the row's
+// candidate entries (key << 16 | offset); need is the nucleus mass in fixed point, in
+// units of exp2(z c - mc). Returns false, having written nothing, when the boundary lies
+// further below (the caller then runs the full-row passes).
+constexpr int kToppBelow = 1024;
+template <int NT>
+SD_DEV bool topp_below_bf16(const TopkArgs& a, int row, float m, float mc, float emc, float c,
+                            uint32_t lo, double need, const uint32_t* keys, int total) {
+    using Kt = TopkKeys<true>;
+    constexpr int BPT = kToppBelow / NT;
+    static_assert(BPT * NT == kToppBelow, "whole bins per thread");
+    __shared__ unsigned s_cnt[kToppBelow];              // bin i: key lo - 1 - i
+    __shared__ unsigned long long s_red[NT / kWave];
+    __shared__ double redd[NT / kWave];
+    __shared__ int redi[NT / kWave];
+    __shared__ int s_bin;
+    const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+    auto canon = [](uint32_t k) { return k == Kt::KEY_NZERO ? Kt::KEY_PZERO : k; };
+    auto zof = [](uint32_t k) { return key_to_float<true>(k); };
+    // 1. the upper set's mass, in the nucleus' fixed point
+    unsigned long long up = 0ull;
+    for (int i = tid; i < total; i += NT) {
+        const uint32_t k = canon(keys[i] >> 16);
+        if (k >= lo) up += mass_fix(__builtin_amdgcn_exp2f(fmaf(zof(k), c, -mc)));
+    }
+    up = wave_sum_u64(up);
+    if (l == 0) s_red[w] = up;
+    for (int i = tid; i < kToppBelow; i += NT) s_cnt[i] = 0u;
+    __syncthreads();
+    up = 0ull;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) up += s_red[i];
+    const double need2 = need - (double)up;
+    // 2. one pass: tokens per key in [lo - 1024, lo)
+    const uint32_t kfloor = lo > Kt::KEY_NINF + 1u + kToppBelow ? lo - kToppBelow : Kt::KEY_NINF + 1u;
+    const uint8_t* base = row_ptr(a.tgt, a.dft, a.rows_t, row, a.V, 2);
+    walk_row<true, NT, 8>(base, a.V, [&](float z) {
+        const uint32_t k = canon(f2key(z) >> 16);
+        if (k < lo && k >= kfloor) atomicAdd(&s_cnt[lo - 1u - k], 1u);
+    });
+    __syncthreads();
+    // 3. the first bin (descending keys) whose cumulative mass reaches need2
+    unsigned long long own = 0ull, bm[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int i = tid * BPT + j;
+        const uint32_t k = lo - 1u - (uint32_t)i;
+        bm[j] = (k >= kfloor && s_cnt[i]) ?
+                    (unsigned long long)s_cnt[i] * mass_fix(__builtin_amdgcn_exp2f(fmaf(zof(k), c, -mc))) : 0ull;
+        own += bm[j];
+    }
+    unsigned long long x = own;                          // inclusive scan over threads
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o, kWave);
+        if (l >= o) x += y;
+    }
+    if (l == kWave - 1) s_red[w] = x;
+    if (tid == 0) s_bin = kToppBelow;
+    __syncthreads();
+    unsigned long long before = x - own;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) before += i < w ? s_red[i] : 0ull;
+    if ((double)(before + own) >= need2 && (double)before < need2) {
+        unsigned long long acc = before;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            acc += bm[j];
+            if ((double)acc >= need2) {
+                s_bin = tid * BPT + j;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const int bin = s_bin;
+    if (bin >= kToppBelow || lo - 1u - (uint32_t)bin < kfloor) return false;
+    const uint32_t K = lo - 1u - (uint32_t)bin;
+    // 4. kept count and exp-sum: the upper set's candidates, then the bins down to K
+    float accf = 0.f;
+    int kept = 0;
+    for (int i = tid; i < total; i += NT) {
+        const uint32_t k = canon(keys[i] >> 16);
+        if (k >= lo) {
+            accf += __builtin_amdgcn_exp2f(fmaf(zof(k), c, -mc));
+            ++kept;
+        }
+    }
+    double accd = (double)accf;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int i = tid * BPT + j;
+        if (i <= bin && s_cnt[i]) {
+            const uint32_t k = lo - 1u - (uint32_t)i;
+            accd += (double)s_cnt[i] * (double)__builtin_amdgcn_exp2f(fmaf(zof(k), c, -mc));
+            kept += (int)s_cnt[i];
+        }
+    }
+    const double tot = block_sum<NT>(accd, redd);
+    kept = block_sum_i<NT>(kept, redi);
+    if (tid == 0) {
+        RowPartial rp;
+        rp.m = m;
+        rp.nkept = kept;
+        rp.s = tot * exp2(-(double)emc);
+        a.part[row] = rp;
+        a.row_thr[row] = zof(K);
+    }
+    return true;
+}
+
 template <bool BF16>
 SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
     constexpr int NT = kMergeNT;
-    constexpr int LPT = kTkMaxChunks / NT;              // lists per thread at most
+    constexpr int LPT = kTkMaxChunks > NT ? kTkMaxChunks / NT : 1;   // lists per thread
     constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
     static_assert(kKeptCap >= 256, "the histogram and the kept-token list share LDS");
@@ -955,9 +1070,13 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
             },
             lo, sel.c, mc, frac, need, h64, &K);
         if (!ok && sel.topp_mode == 2) {
-            // the nucleus reaches below the candidates: full passes over the row
+            // the nucleus reaches below the candidates: for bf16 first one counting pass
+            // over the keys just below them, else (or when it reaches further) full passes
             if (listed && tid == 0) a.kn[row] = -1;
             __syncthreads();
+            if constexpr (BF16) {
+                if (topp_below_bf16<NT>(a, row, m, mc, emc, sel.c, lo, need, keys, total)) return;
+            }
             topp_rows_body<BF16, NT>(a, row, m, -INFINITY, sel.c, sel.top_p,
                                      reinterpret_cast<unsigned long long*>(keys));
             return;
@@ -1824,7 +1943,7 @@ SD_DEV void chunk_pr_body(const TopkArgs& a, int row, int chunk) {
 template <bool BF16>
 SD_DEV void merge_pr_body(const TopkArgs& a, int row) {
     constexpr int NT = kMergeNT;
-    constexpr int LPT = kTkMaxChunks / NT;
+    constexpr int LPT = kTkMaxChunks > NT ? kTkMaxChunks / NT : 1;
     const RowParams rp = a.rpar[row];
     const int mode = rp.flags & kRpMode;
     if (mode != 0) {

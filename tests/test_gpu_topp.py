@@ -52,11 +52,20 @@ def _check(vin, top_p, requests=None, min_checked=1):
     return g, o
 
 
-@pytest.mark.parametrize("top_p", [0.3, 0.9, 0.99])
+@pytest.mark.parametrize("top_p", [0.3, 0.9, 0.95, 0.99, 0.999])
 def test_topp_alone_bf16(top_p):
-    # 0.3 and 0.9 keep tens to hundreds of tokens (candidates), 0.99 thousands (full passes)
+    # 0.3 and 0.9 keep tens to hundreds of tokens (the candidates hold the nucleus); 0.95
+    # up to ~1700 and 0.99 thousands (one counting pass over the keys below the candidates);
+    # 0.999 tens of thousands on some rows
     vin = synth.make_verify("c2", seed=60, B=6)
     _check(_redraw(vin, top_p, 61), top_p)
+
+
+def test_topp_flat_rows_reach_far_below_the_candidates():
+    # nearly uniform rows at top_p 0.999: the boundary lies more than 1024 keys below the
+    # candidates' upper set, so the counting pass gives way to the full-row passes
+    vin = synth.make_verify("c2", seed=62, B=6, target_std=0.5, classes=((1.0, "noise", 0.1),))
+    _check(_redraw(vin, 0.999, 63), 0.999)
 
 
 @pytest.mark.parametrize("top_p,std,V", [(0.8, 8.0, 32000), (0.9, 1.0, 4000)])
@@ -136,10 +145,11 @@ def test_topp_planted_rows(top_k):
     _check(_redraw(_plant(vin, pats, seed=69), 0.7, 70), 0.7)
 
 
-def test_topp_full_size_sampled():
+@pytest.mark.parametrize("top_p", [0.9, 0.95, 0.99])
+def test_topp_full_size_sampled(top_p):
     vin = synth.make_verify("c2", seed=71)
     reqs = sorted(np.random.default_rng(72).choice(vin.B, size=16, replace=False).tolist())
-    _check(_redraw(vin, 0.9, 73, reqs), 0.9, requests=reqs)
+    _check(_redraw(vin, top_p, 73, reqs), top_p, requests=reqs)
 
 
 @pytest.mark.parametrize("off", [0.0, -0.5, 1.0, 3.0])
