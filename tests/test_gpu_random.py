@@ -102,3 +102,30 @@ def test_random_fused_cycles_equal_three_calls(seed):
     for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
         assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
     assert np.array_equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_trees_match_the_oracle_for_any_team(seed):
+    # random tree batches (sizes, vocabulary, dtype, temperature, branching, draft noise,
+    # empty trees) with a random team size: checked against the oracle, and bit for bit
+    # against a team of one
+    from test_gpu_tree import TreeOnDevice, compare_tree
+    import oracle
+    r = np.random.default_rng(2000 + seed)
+    nlo = int(r.integers(0, 6))
+    kw = dict(B=int(r.integers(1, 13)), V=int(r.choice([97, 1000, 4001, 16384, 40000])),
+              dtype="bf16" if r.random() < 0.6 else "f32", T=float(r.choice([0.5, 1.0, 1.5])),
+              n_range=(nlo, nlo + int(r.integers(0, 30))), branch=float(r.choice([0.0, 0.5, 1.0])),
+              noise_std=float(r.choice([0.1, 0.5, 2.0])), target_std=float(r.choice([1.0, 3.0])))
+    team = int(r.choice([0, 2, 3, 7, 16]))
+    tin = synth.make_tree(seed=3000 + seed, **kw)
+    log(f"[random-tree] seed {seed}: {kw} N={tin.N} team {team}")
+    g = TreeOnDevice(tin, team=team, ws_fill=0x5A).run()
+    o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
+                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype)
+    errs, fl, mism = compare_tree(tin, g, o)
+    log(f"[random-tree]   flagged {fl}, flagged mismatches {mism}")
+    assert not errs, f"seed {seed} {kw} team {team}\n" + "\n".join(errs[:20])
+    solo = TreeOnDevice(tin, team=1).run()
+    for key in ("a", "n", "out", "nodes", "flags"):
+        assert np.array_equal(g[key], solo[key]), key
