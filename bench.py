@@ -401,10 +401,14 @@ def main():
     ev_stats = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
     ev_kv = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
 
+    # serial schedule: events around each call on the timing steps
+    call_ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in timed}
+
     def step(i):
         dbg = binding.SpecdecDebug()
         if i in evs:
             dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
+        ce = call_ev.get(i) if args.schedule == "serial" else None
         if args.schedule == "fused":
             binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
                                   max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
@@ -412,11 +416,17 @@ def main():
                                   err_word=err, workspace=cws, debug=dbg, top_p=top_p, **pr)
             return
         if args.schedule == "serial":
+            if ce:
+                ce[0].record()
             binding.kv_paged_append(cache, k_new, v_new, cu_new, kws)
+            if ce:
+                ce[1].record()
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
                                    temperature=vin.T, top_k=vin.top_k, out_tokens=out,
                                    num_accepted=nacc, num_emitted=nemit, err_word=err,
                                    workspace=ws, debug=dbg, top_p=top_p, **pr)
+            if ce:
+                ce[2].record()
         else:
             dbg.ev_stats_done = ev_stats[i].handle
             binding.specdec_verify(tgt, dft, tokens, cu, u_acc, u_smp, max_k=vin.max_k,
@@ -429,6 +439,8 @@ def main():
             ev_kv[i].record(side_s)
             ev_kv[i].wait_on(main_s)
         binding.kv_rollback(cache, nacc, cu)
+        if ce:
+            ce[3].record()
 
     if args.calibrate_copy_mib:
         nb = args.calibrate_copy_mib << 20
@@ -513,8 +525,21 @@ def main():
                      "algorithmic_bytes": logit_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
     }
+    if args.schedule == "serial":
+        # each call's time from events around it on the timing steps, and the bytes it must
+        # move: the append reads and writes the new K/V, the verify reads every logit row
+        # once, the rollback touches metadata only
+        cms = lambda a_, b_: float(np.mean([call_ev[i][a_].elapsed_time(call_ev[i][b_]) for i in timed]))
+        ap, ve, rb = cms(0, 1), cms(1, 2), cms(2, 3)
+        res["per_call"] = {"append_ms": ap, "append_gbps": kv_bytes / (ap / 1e3) / 1e9,
+                           "verify_ms": ve, "verify_gbps": logit_bytes / (ve / 1e3) / 1e9,
+                           "rollback_ms": rb}
     if generic:
         res["roofline"] = None
+    try:
+        res["device_memory"] = binding.device_memory(d.index or 0)
+    except Exception as e:   # reported, not needed for the line
+        res["device_memory"] = {"error": str(e)}
     res["acceptance"] = acceptance
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)

@@ -404,11 +404,33 @@ def _hip_rt() -> ctypes.CDLL:
         _hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         _hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        _hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                               ctypes.c_int]
         _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         _hip.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                              ctypes.c_void_p]
     return _hip
+
+
+_HIP_ATTR_MEMORY_BUS_WIDTH = 59      # hipDeviceAttributeMemoryBusWidth (bits)
+_HIP_ATTR_MEMORY_CLOCK_RATE = 60     # hipDeviceAttributeMemoryClockRate (kHz)
+
+
+def device_memory(device: int = 0) -> dict:
+    """The device's memory bus width (bits) and peak memory clock (kHz) as HIP reports
+    them, and their product in GB/s (bytes per clock x clock; the transfers per clock
+    depend on the memory type)."""
+    rt = _hip_rt()
+    v = ctypes.c_int()
+    out = {}
+    for name, attr in (("bus_width_bits", _HIP_ATTR_MEMORY_BUS_WIDTH),
+                       ("clock_khz", _HIP_ATTR_MEMORY_CLOCK_RATE)):
+        if rt.hipDeviceGetAttribute(ctypes.byref(v), attr, device) != 0:
+            raise RuntimeError("hipDeviceGetAttribute failed")
+        out[name] = int(v.value)
+    out["clock_x_bus_gbps"] = out["clock_khz"] * 1e3 * out["bus_width_bits"] / 8 / 1e9
+    return out
 
 
 class HipEvent:
