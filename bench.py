@@ -54,6 +54,9 @@ def parse():
                         "n-th step (they add a few microseconds to those steps)")
     p.add_argument("--team", type=int, default=0,
                    help="tree workloads: workgroups per request walk (0: automatic)")
+    p.add_argument("--flush-mib", type=int, default=512,
+                   help="for the flushed percentiles: MiB written before each of those cycles, "
+                        "outside its events, so no input is left in the 256 MB MALL (0: skip)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before timing "
@@ -349,8 +352,9 @@ def main():
     vin = synth.make_verify(wl, seed=args.seed,
                             **({} if args.top_k is None else {"top_k": args.top_k}))
     top_p = args.top_p
-    # the pool holds the warm-up, the timed cycles and as many again for the percentiles
-    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + 2 * args.steps + 2)
+    # the pool holds the warm-up, the timed cycles and twice as many again for the
+    # percentiles (without and with a cache flush before each cycle)
+    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + 3 * args.steps + 2)
     print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
           f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
 
@@ -398,8 +402,8 @@ def main():
     evs = {i: (binding.HipEvent(), binding.HipEvent()) for i in timed}
     main_s = torch.cuda.current_stream(d)
     side_s = torch.cuda.Stream(d)                      # default priority
-    ev_stats = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
-    ev_kv = [binding.HipEvent(timing=False) for _ in range(n + args.steps)]
+    ev_stats = [binding.HipEvent(timing=False) for _ in range(n + 2 * args.steps)]
+    ev_kv = [binding.HipEvent(timing=False) for _ in range(n + 2 * args.steps)]
 
     # serial schedule: events around each call on the timing steps
     call_ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in timed}
@@ -476,6 +480,21 @@ def main():
         cyc.append((e0, e1))
     torch.cuda.synchronize()
     cyc_ms = np.array([a.elapsed_time(b) for a, b in cyc])
+    # and as many again, each after a write of --flush-mib MiB outside its events
+    cyc_fl_ms = None
+    if args.flush_mib:
+        junk = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=d)
+        cyc = []
+        for i in range(n + args.steps, n + 2 * args.steps):
+            junk.fill_(i & 0xff)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(i)
+            e1.record()
+            cyc.append((e0, e1))
+        torch.cuda.synchronize()
+        cyc_fl_ms = np.array([a.elapsed_time(b) for a, b in cyc])
+        del junk
     acceptance = acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
                                   out, nacc, nemit, err, ws, top_p, pr, ms_per_step)
     es = 2 if vin.dtype == "bf16" else 4
@@ -516,6 +535,8 @@ def main():
                    "global_batch": B, "positions_per_step": K, "parallelism": "single GPU",
                    "schedule": args.schedule},
         "cycle_ms_p10_p50_p90": [float(np.percentile(cyc_ms, q)) for q in (10, 50, 90)],
+        "cycle_ms_p10_p50_p90_flushed": (None if cyc_fl_ms is None else
+                                         [float(np.percentile(cyc_fl_ms, q)) for q in (10, 50, 90)]),
         "achieved_hbm_gbps": cycle_gbps,
         "pct_peak_hbm": 100.0 * cycle_gbps / PEAK_GBPS,
         "cycle_bytes": cycle_bytes,
