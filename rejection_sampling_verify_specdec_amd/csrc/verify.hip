@@ -65,9 +65,9 @@ __global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
                                           ChunkSel{a.top_k, a.c, P2});
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kMergeNT) void k_topk_merge(TopkArgs a) {
-    topk_merge_body<BF16>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) void k_topk_merge(TopkArgs a) {
+    topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
 }
 
 // per-request parameters: each row's transform, then the chunks and merges that read it
@@ -81,9 +81,9 @@ __global__ __launch_bounds__(kTkNT) void k_chunks_pr(TopkArgs a) {
     chunk_pr_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kMergeNT) void k_merge_pr(TopkArgs a) {
-    merge_pr_body<BF16>(a, blockIdx.x);
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) void k_merge_pr(TopkArgs a) {
+    merge_pr_body<BF16, NT>(a, blockIdx.x);
 }
 
 template <bool BF16>
@@ -117,7 +117,10 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                            rows);
         hipExtLaunchKernelGGL((k_chunks_pr<BF16, VEC>), dim3((unsigned)rows * p.nchunks),
                               dim3(kTkNT), 0, st, e0, e1, 0, ta);
-        hipLaunchKernelGGL((k_merge_pr<BF16>), dim3(rows), dim3(kMergeNT), 0, st, ta);
+        if (p.wide_merge)
+            hipLaunchKernelGGL((k_merge_pr<BF16, kMergeNTp>), dim3(rows), dim3(kMergeNTp), 0, st, ta);
+        else
+            hipLaunchKernelGGL((k_merge_pr<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st, ta);
     } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         if (!ta.generic) {
@@ -131,8 +134,12 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                                       0, ta);
             e0 = e1 = nullptr;
         }
-        hipExtLaunchKernelGGL((k_topk_merge<BF16>), dim3(rows), dim3(kMergeNT), 0, st, e0, e1, 0,
-                              ta);
+        if (p.wide_merge)
+            hipExtLaunchKernelGGL((k_topk_merge<BF16, kMergeNTp>), dim3(rows), dim3(kMergeNTp), 0,
+                                  st, e0, e1, 0, ta);
+        else
+            hipExtLaunchKernelGGL((k_topk_merge<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st,
+                                  e0, e1, 0, ta);
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
                               0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);

@@ -316,7 +316,8 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // ---------------------------------------------------------------------------------------
 constexpr int kTkNT = kNT;         // threads of a chunk workgroup
 constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-byte vectors)
-constexpr int kMergeNT = 256;      // threads of a merge workgroup
+constexpr int kMergeNT = 128;      // threads of a merge workgroup (candidates only)
+constexpr int kMergeNTp = 256;     // with top-p alone: rows may need passes over the row
 constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
 constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
@@ -896,9 +897,8 @@ SD_DEV bool topp_below_bf16(const TopkArgs& a, int row, float m, float mc, float
     return true;
 }
 
-template <bool BF16>
+template <bool BF16, int NT>
 SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
-    constexpr int NT = kMergeNT;
     constexpr int LPT = kTkMaxChunks > NT ? kTkMaxChunks / NT : 1;   // lists per thread
     constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
@@ -1940,14 +1940,13 @@ SD_DEV void chunk_pr_body(const TopkArgs& a, int row, int chunk) {
 
 // The merge of one row under per-request parameters; an unfiltered row combines its chunk
 // statistics (max, then the exp-sums rescaled to it in fp64, fixed order).
-template <bool BF16>
+template <bool BF16, int NT>
 SD_DEV void merge_pr_body(const TopkArgs& a, int row) {
-    constexpr int NT = kMergeNT;
     constexpr int LPT = kTkMaxChunks > NT ? kTkMaxChunks / NT : 1;
     const RowParams rp = a.rpar[row];
     const int mode = rp.flags & kRpMode;
     if (mode != 0) {
-        topk_merge_body<BF16>(a, row, RowSel{rp.k, mode == 2 ? 2 : (rp.top_p < 1.0f ? 1 : 0),
+        topk_merge_body<BF16, NT>(a, row, RowSel{rp.k, mode == 2 ? 2 : (rp.top_p < 1.0f ? 1 : 0),
                                              rp.top_p, rp.c});
         return;
     }
@@ -1991,6 +1990,7 @@ struct WsPlan {
         prec, wacc, total;
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
     int pr;                  // per-request parameters: every row through the chunk select
+    int wide_merge;          // top-p on: the wider merge workgroups (rows may need passes)
     int kc;                  // the chunk k of a top-p-alone row
 };
 
@@ -2038,6 +2038,7 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         if (prm->top_k) kmax = prm->top_k_max < kTkMaxK ? prm->top_k_max : kTkMaxK;
         else if (topk_active(top_k, V) && !topk_generic(top_k)) kmax = top_k;
         if (prm->top_p || topp_active(top_p)) kmax = kmax > p.kc ? kmax : p.kc;
+        p.wide_merge = (prm->top_p || topp_active(top_p)) ? 1 : 0;
         p.filter = 1;
         p.topp_mode = -1;               // per row
         p.sel_k = kmax > 0 ? kmax : 1;
@@ -2047,6 +2048,9 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         p.topp_mode = topp_mode(top_k, top_p, V);
         p.sel_k = select_k(top_k, top_p, V, p.nchunks);
         p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
+        // whenever top-p is on (with or without top-k), as for per-request arrays, so the
+        // two paths keep identical sums
+        p.wide_merge = p.topp_mode != 0 ? 1 : 0;
     }
     p.nparts = p.filter ? 1 : p.nchunks;
     const size_t rows = (size_t)2 * K + B;
