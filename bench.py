@@ -510,7 +510,8 @@ def main():
     # top_k above 1024 runs the multi-pass select inside the merge launch: no launch
     # streams the rows once
     generic = 0 < vin.top_k < V and vin.top_k > 1024
-    if filtered or args.per_request:   # the chunk launch streams the rows
+    # per-request arrays hold temperatures only when no top-k / top-p is on: plain statistics
+    if filtered:                       # the chunk launch streams the rows
         stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
     else:
         stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"

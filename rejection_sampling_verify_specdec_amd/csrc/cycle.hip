@@ -51,12 +51,13 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
                                                      const uint8_t* __restrict__ tgt,
                                                      const uint8_t* __restrict__ dft,
                                                      int rows_t, int V, int nchunks, float c,
-                                                     RowPartial* __restrict__ part) {
+                                                     RowPartial* __restrict__ part,
+                                                     const RowParams* __restrict__ rpar) {
     if (blockIdx.x == 0) {
         alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
         return;
     }
-    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1);
+    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1, rpar);
 }
 
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
@@ -145,7 +146,13 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     float* thr = reinterpret_cast<float*>(vws + p.thr);
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (p.pr) {
+    if (p.pr_plain) {
+        hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
+                           pa, rows);
+        hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
+                              dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,
+                              p.nchunks, c, part, reinterpret_cast<const RowParams*>(vws + p.rpar));
+    } else if (p.pr) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
                            pa, rows);
@@ -175,7 +182,7 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,
-                              p.nchunks, c, part);
+                              p.nchunks, c, part, (const RowParams*)nullptr);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
     const int tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);

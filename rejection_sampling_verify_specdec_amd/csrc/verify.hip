@@ -55,8 +55,9 @@ template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_row_stats(const uint8_t* __restrict__ tgt,
                                                    const uint8_t* __restrict__ dft,
                                                    int rows_t, int V, int nchunks, float c,
-                                                   RowPartial* __restrict__ part) {
-    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x);
+                                                   RowPartial* __restrict__ part,
+                                                   const RowParams* __restrict__ rpar) {
+    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x, rpar);
 }
 
 template <bool BF16, bool VEC, bool P2>
@@ -111,7 +112,13 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (p.pr) {
+    if (p.pr_plain) {
+        hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,
+                           rows);
+        hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
+                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part,
+                              reinterpret_cast<const RowParams*>(ws + p.rpar));
+    } else if (p.pr) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,
                            rows);
@@ -142,7 +149,8 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                                   e0, e1, 0, ta);
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
-                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part);
+                              0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part,
+                              (const RowParams*)nullptr);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
     hipLaunchKernelGGL((k_decide<BF16>), dim3(B), dim3(kDecideNT), 0, st, sa);

@@ -147,16 +147,30 @@ SD_DEV const uint8_t* row_ptr(const uint8_t* tgt, const uint8_t* dft, int rows_t
 // ---------------------------------------------------------------------------------------
 // Row statistics, chunked: max and sum of exp2((z - m_c) * c) per chunk.
 // ---------------------------------------------------------------------------------------
+// The transform of one row when temperature / top-k / top-p come per request.
+constexpr int kRpMode = 3;         // flags & kRpMode: 0 none, 1 top-k (and maybe top-p),
+                                   // 2 top-p alone
+constexpr int kRpBad = 4;          // the request's parameters are invalid
+constexpr int kRpGeneric = 8;      // the row takes the multi-pass select
+struct alignas(16) RowParams {
+    float c;        // log2(e) / T
+    int k;          // the chunk select's k: top_k (mode 1), k_c (mode 2), 0 (mode 0)
+    float top_p;
+    int flags;
+};
+
 template <bool BF16, bool VEC>
 SD_DEV void row_stats_body(const uint8_t* __restrict__ tgt, const uint8_t* __restrict__ dft,
                            int rows_t, int V, int nchunks, float c,
-                           RowPartial* __restrict__ part, int bid) {
+                           RowPartial* __restrict__ part, int bid,
+                           const RowParams* __restrict__ rpar = nullptr) {
     using Lt = Layout<BF16, VEC>;
     __shared__ float redf[kNT / kWave];
     __shared__ double redd[kNT / kWave];
     __shared__ int redi[kNT / kWave];
     const int row = bid / nchunks;
     const int chunk = bid - row * nchunks;
+    if (rpar) c = rpar[row].c;       // per-request temperatures: the row's log2(e) / T
     const uint8_t* base = row_ptr(tgt, dft, rows_t, row, V, Lt::ES);
     float z[Lt::EPT];
     load_chunk<BF16, VEC>(base, V, chunk * Lt::CH, z);
@@ -348,17 +362,7 @@ struct TopkArgs {
     const struct RowParams* rpar;   // per-request parameters: [rows] each row's, else null
 };
 
-// The transform of one row when temperature / top-k / top-p come per request.
-constexpr int kRpMode = 3;         // flags & kRpMode: 0 none, 1 top-k (and maybe top-p),
-                                   // 2 top-p alone
-constexpr int kRpBad = 4;          // the request's parameters are invalid
-constexpr int kRpGeneric = 8;      // the row takes the multi-pass select
-struct alignas(16) RowParams {
-    float c;        // log2(e) / T
-    int k;          // the chunk select's k: top_k (mode 1), k_c (mode 2), 0 (mode 0)
-    float top_p;
-    int flags;
-};
+
 
 // What one chunk workgroup selects, and what one merge workgroup applies.
 struct ChunkSel {
@@ -1991,6 +1995,7 @@ struct WsPlan {
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
     int pr;                  // per-request parameters: every row through the chunk select
     int wide_merge;          // top-p on: the wider merge workgroups (rows may need passes)
+    int pr_plain;            // per-request temperatures only: plain statistics, per-row c
     int kc;                  // the chunk k of a top-p-alone row
 };
 
@@ -2032,7 +2037,17 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
     p.nchunks = (V + ch - 1) / ch;
     p.kc = select_k(0, 0.5f, V, p.nchunks);
     p.pr = per_request(prm);
-    if (p.pr) {
+    p.pr_plain = p.pr && !prm->top_k && !prm->top_p && !topk_active(top_k, V) &&
+                 !topp_active(top_p);
+    if (p.pr_plain) {
+        // temperatures alone transform nothing but the exp-sums: the plain statistics, each
+        // row with its request's log2(e) / T
+        p.filter = 0;
+        p.topp_mode = 0;
+        p.sel_k = 0;
+        p.sel_generic = 0;
+        p.wide_merge = 0;
+    } else if (p.pr) {
         // lists sized for the largest chunk k any row may use
         int kmax = 0;
         if (prm->top_k) kmax = prm->top_k_max < kTkMaxK ? prm->top_k_max : kTkMaxK;

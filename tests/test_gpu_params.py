@@ -110,6 +110,22 @@ def test_uniform_arrays_match_the_scalars():
         assert np.array_equal(getattr(ga, f), getattr(gb, f)), f
 
 
+@pytest.mark.parametrize("wl", ["c2", "c1"])
+def test_uniform_temperature_arrays_match_the_scalar(wl):
+    # temperatures alone take the plain statistics with each row's log2(e) / T: equal
+    # temperatures give the scalar call's results bit for bit, debug values included
+    vin = synth.make_verify(wl, seed=97, B=12, V=30000 if wl == "c2" else None)
+    a = VerifyOnDevice(vin)
+    a.run()
+    ga = a.result()
+    b = VerifyOnDevice(vin, temps=[vin.T] * vin.B)
+    b.run()
+    gb = b.result()
+    for f in ("num_accepted", "num_emitted", "out_tokens", "row_max", "row_sum", "p_y", "q_y",
+              "resid_mass", "picked_prob", "req_flags"):
+        assert np.array_equal(getattr(ga, f), getattr(gb, f)), f
+
+
 def test_full_size_sampled_per_request_temperature():
     vin = synth.make_verify("c2", seed=92)
     rng = np.random.default_rng(93)
@@ -119,9 +135,10 @@ def test_full_size_sampled_per_request_temperature():
     _check(vin, Ts, 0, ps, requests=reqs, seed=94)
 
 
-@pytest.mark.parametrize("wl", ["c4", "c1"])
-def test_fused_cycle_equals_three_calls_per_request(wl):
-    vin = synth.make_verify(wl, seed=95, B=12, V=30000 if wl == "c4" else None, k=3)
+@pytest.mark.parametrize("wl,temps_only", [("c4", False), ("c1", False), ("c4", True)])
+def test_fused_cycle_equals_three_calls_per_request(wl, temps_only):
+    vin = synth.make_verify(wl, seed=95, B=12, V=30000 if wl == "c4" else None, k=3,
+                            **({"top_k": 0} if temps_only else {}))
     rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=100, prefix_hi=300, share_group=3,
                          share_blocks=2)
     kv = synth.make_kv(wl, vin, seed=95, recipe=rec)
@@ -129,6 +146,9 @@ def test_fused_cycle_equals_three_calls_per_request(wl):
     Ts = rng.uniform(0.4, 1.4, vin.B).astype(np.float32)
     ks = rng.choice([0, 8, 64, 2000], vin.B).astype(np.int32)
     ps = rng.choice([1.0, 0.9, 0.5], vin.B).astype(np.float32)
+    if temps_only:
+        Ts[3] = -1.0                          # an invalid temperature fails its request alone
+        ks, ps = None, None
     outs = []
     for mode in ("calls", "fused"):
         log(f"[params-fused] {wl} {mode}")
@@ -160,8 +180,9 @@ def test_fused_cycle_equals_three_calls_per_request(wl):
         assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
     assert np.array_equal(a[2], b[2])
     # and the decisions are the oracle's
-    o = oracle_verify(vin, T=Ts, top_k=ks, top_p=ps, top_k_max=2000)
-    rep = compare_verify(vin, a[0], o, T=Ts, top_k=ks, top_p=ps)
+    ok_, op_ = (0, 1.0) if temps_only else (ks, ps)
+    o = oracle_verify(vin, T=Ts, top_k=ok_, top_p=op_, top_k_max=2000)
+    rep = compare_verify(vin, a[0], o, T=Ts, top_k=ok_, top_p=op_)
     log(f"[params-fused]   {rep}")
     assert not rep.errors, "\n".join(rep.errors)
     o_kv = oracle_kv(kv)
