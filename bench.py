@@ -37,6 +37,8 @@ def parse():
                    help="untimed cycles first: the GPU clock settles over the first ~10 ms")
     p.add_argument("--workload", default="c2")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--batch", type=int, default=None,
+                   help="override the workload's batch size B (latency at small batches)")
     p.add_argument("--top-k", type=int, default=None,
                    help="override the workload's top_k (0 = off)")
     p.add_argument("--top-p", type=float, default=1.0,
@@ -57,6 +59,9 @@ def parse():
     p.add_argument("--flush-mib", type=int, default=512,
                    help="for the flushed percentiles: MiB written before each of those cycles, "
                         "outside its events, so no input is left in the 256 MB MALL (0: skip)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the fused cycle captured once in a HIP graph and replayed "
+                        "(no host launch cost per cycle: what small batches need)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before timing "
@@ -349,12 +354,13 @@ def main():
     d = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     t0 = time.time()
-    vin = synth.make_verify(wl, seed=args.seed,
+    vin = synth.make_verify(wl, seed=args.seed, B=args.batch,
                             **({} if args.top_k is None else {"top_k": args.top_k}))
     top_p = args.top_p
     # the pool holds the warm-up, the timed cycles and twice as many again for the
     # percentiles (without and with a cache flush before each cycle)
-    kv = synth.make_kv(wl, vin, seed=args.seed, cycles=args.warmup + 3 * args.steps + 2)
+    kv = synth.make_kv(wl, vin, seed=args.seed,
+                       cycles=args.warmup + (5 if args.graph else 3) * args.steps + 4)
     print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
           f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
 
@@ -495,6 +501,40 @@ def main():
         torch.cuda.synchronize()
         cyc_fl_ms = np.array([a.elapsed_time(b) for a, b in cyc])
         del junk
+    graph = None
+    if args.graph and args.schedule == "fused":
+        # one cycle captured (its launches read every size and pointer from device memory or
+        # their arguments, so each replay is the next cycle), then replays timed like the
+        # eager cycles
+        gs = torch.cuda.Stream(d)
+        gs.wait_stream(main_s)
+        with torch.cuda.stream(gs):
+            step(n + 2 * args.steps)                      # an eager cycle on the capture stream
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            step(n + 2 * args.steps + 1)
+        torch.cuda.synchronize()
+        for _ in range(min(args.warmup, args.steps)):
+            g.replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        g_ms = (time.perf_counter() - tg0) / args.steps * 1e3
+        ev = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        g_cyc = np.array([a.elapsed_time(b) for a, b in ev])
+        graph = {"ms_per_step": g_ms, "value": K / (g_ms / 1e3),
+                 "cycle_ms_p10_p50_p90": [float(np.percentile(g_cyc, q)) for q in (10, 50, 90)]}
+        del g
     acceptance = acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
                                   out, nacc, nemit, err, ws, top_p, pr, ms_per_step)
     es = 2 if vin.dtype == "bf16" else 4
@@ -562,6 +602,8 @@ def main():
         res["device_memory"] = binding.device_memory(d.index or 0)
     except Exception as e:   # reported, not needed for the line
         res["device_memory"] = {"error": str(e)}
+    if graph is not None:
+        res["graph"] = graph
     res["acceptance"] = acceptance
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
