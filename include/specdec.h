@@ -412,7 +412,11 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * Host: B >= 1, N = cu_nodes[B], 0 <= max_nodes <= SPECDEC_MAX_TREE, 1 <= V <=
  * SPECDEC_MAX_V, temperature > 0 and finite, 0 <= team <= 16; EINVAL otherwise,
  * EWORKSPACE for a missing / small / misaligned workspace, before anything is enqueued.
- * Two launches on `stream` (counter reset, walk).
+ * Two launches on `stream` (counter reset, walk). Testing only: the environment variable
+ * SPECDEC_TREE_SPIN_LIMIT (a decimal integer in [0, 2^20], read at each call; anything
+ * else is ignored) lowers the bound on the polls a member makes while it waits for the
+ * rest of its team (default 2^20); a member that reaches the bound gives up, and its
+ * request fails with SPECDEC_ERR_TEAM (the other requests are unaffected).
  */
 size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V);
 int specdec_tree_verify(const void* target_logits, const void* draft_logits, int32_t dtype,

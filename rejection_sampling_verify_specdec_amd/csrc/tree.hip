@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "tree_dev.h"
 
@@ -118,6 +119,13 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     a.nsub = w.nsub;
     a.slot = w.slot;
     a.team = G;
+    // testing only: a smaller bound on the team's wait forces SPECDEC_ERR_TEAM from the host
+    a.spin_limit = kTreeSpinLimit;
+    if (const char* lim = getenv("SPECDEC_TREE_SPIN_LIMIT")) {
+        char* end = nullptr;
+        const long v = strtol(lim, &end, 10);
+        if (end != lim && *end == '\0' && v >= 0 && v <= kTreeSpinLimit) a.spin_limit = (int)v;
+    }
     const int nctr = B * kTreeCtrStride;
     const int grid = (B + 7) / 8 * 8 * G;
     (void)hipGetLastError();

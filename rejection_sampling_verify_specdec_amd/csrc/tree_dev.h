@@ -57,6 +57,7 @@ struct TreeArgs {
     int nsub;                // sub-chunks of a row
     int slot;                // doubles per pass: 64 * nchunk (4 per wave and chunk)
     int team;                // workgroups per request
+    int spin_limit;          // polls a member waits for the others before it gives up
 };
 
 // Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
@@ -399,7 +400,7 @@ SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* dro
         if (mine) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int it = 0, to = 0;
         while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (k + 1) * C) {
-            if (++it > kTreeSpinLimit) {
+            if (++it > a.spin_limit) {
                 to = 1;
                 break;
             }

@@ -273,3 +273,33 @@ def test_team_sizes_give_identical_results(dtype, V):
         for key in ("a", "n", "out", "nodes", "flags"):
             assert np.array_equal(g[key], ref[key]), (team, key)
         assert g["err"] == ref["err"], team
+
+
+def test_team_wait_bound_fails_requests_cleanly(monkeypatch):
+    # the team's wait is bounded: with a bound of zero polls, members that would wait for
+    # the others give up, and their requests fail with SPECDEC_ERR_TEAM (num_accepted -1,
+    # nothing emitted) while every other request keeps the normal result; the launch ends
+    tin = synth.make_tree(seed=114, B=8, V=128256, dtype="bf16", n_range=(10, 30))
+    ref = TreeOnDevice(tin, team=4).run()
+    monkeypatch.setenv("SPECDEC_TREE_SPIN_LIMIT", "0")
+    log("[tree-team] wait bound 0 polls, team 4")
+    g = TreeOnDevice(tin, team=4).run()
+    monkeypatch.delenv("SPECDEC_TREE_SPIN_LIMIT")
+    failed = [b for b in range(tin.B) if g["flags"][b] & binding.ERR_TEAM]
+    log(f"[tree-team]   {len(failed)} of {tin.B} requests gave up")
+    assert failed, "a zero-poll bound should make some member give up"
+    for b in range(tin.B):
+        if b in failed:
+            assert g["a"][b] == -1 and g["n"][b] == 0
+        else:
+            assert g["a"][b] == ref["a"][b] and g["n"][b] == ref["n"][b]
+            lo = int(tin.cu_nodes[b])
+            n = int(ref["n"][b])
+            assert np.array_equal(g["out"][lo + b: lo + b + n], ref["out"][lo + b: lo + b + n])
+            assert np.array_equal(g["nodes"][lo: lo + n - 1], ref["nodes"][lo: lo + n - 1])
+            assert g["flags"][b] == ref["flags"][b]
+    assert g["err"] & binding.ERR_TEAM
+    # and a normal call afterwards is unaffected
+    again = TreeOnDevice(tin, team=4).run()
+    for key in ("a", "n", "out", "nodes", "flags"):
+        assert np.array_equal(again[key], ref[key]), key
