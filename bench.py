@@ -46,11 +46,14 @@ def parse():
     p.add_argument("--per-request", action="store_true",
                    help="pass the transform as per-request arrays (same values for every "
                         "request): measures the per-request path")
-    p.add_argument("--schedule", choices=["fused", "serial", "overlap"], default="fused",
+    p.add_argument("--schedule", choices=["fused", "early-exit", "serial", "overlap"], default="fused",
                    help="fused: specdec_cycle (allocation inside the logit-streaming launch, "
                         "K/V scatter beside the sampling workgroups); serial: append, verify, "
                         "rollback as three calls on one stream; overlap: the three calls with "
-                        "the append on a second stream after the logit rows are streamed")
+                        "the append on a second stream after the logit rows are streamed; "
+                        "early-exit: specdec_cycle_early_exit (row statistics position by "
+                        "position, no row read past a request's first rejection; plain "
+                        "temperature only)")
     p.add_argument("--timing-every", type=int, default=4,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
@@ -388,6 +391,10 @@ def main():
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+    if args.schedule == "early-exit" and (0 < vin.top_k < V or 0.0 < top_p < 1.0 or
+                                          args.per_request):
+        raise SystemExit("--schedule early-exit takes plain temperature only (no top-k, "
+                         "top-p or per-request arrays)")
     pr = {}
     if args.per_request:
         pr["temperatures"] = torch.full((B,), vin.T, dtype=torch.float32, device=d)
@@ -419,11 +426,12 @@ def main():
         if i in evs:
             dbg.ev_stats_begin, dbg.ev_stats_end = evs[i][0].handle, evs[i][1].handle
         ce = call_ev.get(i) if args.schedule == "serial" else None
-        if args.schedule == "fused":
+        if args.schedule in ("fused", "early-exit"):
             binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
                                   max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
                                   out_tokens=out, num_accepted=nacc, num_emitted=nemit,
-                                  err_word=err, workspace=cws, debug=dbg, top_p=top_p, **pr)
+                                  err_word=err, workspace=cws, debug=dbg, top_p=top_p,
+                                  early_exit=args.schedule == "early-exit", **pr)
             return
         if args.schedule == "serial":
             if ce:
@@ -502,7 +510,7 @@ def main():
         cyc_fl_ms = np.array([a.elapsed_time(b) for a, b in cyc])
         del junk
     graph = None
-    if args.graph and args.schedule == "fused":
+    if args.graph and args.schedule in ("fused", "early-exit"):
         # one cycle captured (its launches read every size and pointer from device memory or
         # their arguments, so each replay is the next cycle), then replays timed like the
         # eager cycles
@@ -542,16 +550,28 @@ def main():
     logit_bytes = rows * V * es
     kv_bytes = 2 * (K + B) * kv.L * 2 * kv.H * kv.D * 2      # read + write, K and V
     small = 4 * (3 * K + 6 * B + 2)                         # tokens, uniforms, offsets, outputs
-    cycle_bytes = logit_bytes + kv_bytes + small
+    # the rows this batch's outputs depend on: each request's target and draft rows up to
+    # its first rejection (its correction row included), or every row when all proposals
+    # were accepted (the bonus row included); the full cycle reads the rest as well (every
+    # proposal gets its statistics) but they decide nothing, and the early-exit cycle reads
+    # exactly these
+    kb = np.diff(np.asarray(vin.cu_draft, dtype=np.int64))
+    ab = np.maximum(nacc.cpu().numpy().astype(np.int64), 0)
+    seq_rows = int(np.where(ab < kb, 2 * (ab + 1), 2 * kb + 1).sum())
+    early = args.schedule == "early-exit"
+    read_bytes = (seq_rows if early else rows) * V * es
+    cycle_bytes = read_bytes + kv_bytes + small
     positions_per_s = K * args.steps / elapsed
     cycle_gbps = cycle_bytes / (ms_per_step / 1e3) / 1e9
-    achieved = logit_bytes / stats_avg_s / 1e9
+    achieved = read_bytes / stats_avg_s / 1e9
     filtered = 0 < vin.top_k < V or 0.0 < top_p < 1.0
     # top_k above 1024 runs the multi-pass select inside the merge launch: no launch
     # streams the rows once
     generic = 0 < vin.top_k < V and vin.top_k > 1024
     # per-request arrays hold temperatures only when no top-k / top-p is on: plain statistics
-    if filtered:                       # the chunk launch streams the rows
+    if early:                          # max_k + 1 launches, timed as one span
+        stats_kernel = "k_cycle_pass"
+    elif filtered:                     # the chunk launch streams the rows
         stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
     else:
         stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
@@ -583,8 +603,8 @@ def main():
         "cycle_bytes": cycle_bytes,
         "roofline": {"bound": "hbm", "kernel": stats_kernel, "achieved": achieved,
                      "peak": PEAK_GBPS, "unit": "GB/s", "frac": achieved / PEAK_GBPS,
-                     "traffic": traffic_from_profile(stats_kernel, wl.name),
-                     "algorithmic_bytes": logit_bytes,
+                     "traffic": None if early else traffic_from_profile(stats_kernel, wl.name),
+                     "algorithmic_bytes": read_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
     }
     if args.schedule == "serial":
@@ -598,6 +618,10 @@ def main():
                            "rollback_ms": rb}
     if generic:
         res["roofline"] = None
+    seq_bytes = seq_rows * V * es + kv_bytes + small
+    res["sequential_minimum"] = {"logit_rows": seq_rows, "logit_rows_streamed": rows,
+                                 "cycle_bytes": seq_bytes,
+                                 "gbps_at_measured_cycle": seq_bytes / (ms_per_step / 1e3) / 1e9}
     try:
         res["device_memory"] = binding.device_memory(d.index or 0)
     except Exception as e:   # reported, not needed for the line

@@ -335,6 +335,38 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
                   int32_t* err_word, const specdec_debug* dbg,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* specdec_cycle_early_exit: the same cycle, reading no logit row past a request's first
+ * rejection. "Speculative decoding: accelerate LLM generation without changing its
+ * answers" §2-3: once proposal i is rejected, nothing after it is looked at; the accepted
+ * count, the emitted tokens, the draw and the cache step depend only on the rows of
+ * positions 0..j (j the first rejection, or k_b with the bonus row).
+ *
+ * Arguments, layouts, ownership, workspace (specdec_cycle_workspace_size with the same
+ * arguments) and results: as specdec_cycle, bit for bit, for every request whose rows are
+ * finite. Differences, all from the rows that are not read:
+ *   - the row statistics run as max_k + 1 launches, one per position p, each reading the
+ *     rows of position p of the requests whose proposals before p were all accepted;
+ *   - SPECDEC_ERR_NONFINITE covers the rows read (a non-finite row after the first
+ *     rejection is not seen);
+ *   - debug p_y / q_y after the first rejection, and row_max / row_sum / row_thr of rows
+ *     not read, are NaN (row_nkept -1);
+ *   - events: ev_stats_begin / ev_stats_end bracket all the statistics launches.
+ * Host: every specdec_cycle check, and also EINVAL, before anything is enqueued, when top-k
+ * (0 < top_k < V) or top-p (0 < top_p < 1) is on, when per_request carries temperature,
+ * top_k or top_p arrays (eos_token and max_emit are allowed), or when dbg asks for the
+ * acceptance analytics (accept_prob, expected_emitted: they need every row).
+ */
+int specdec_cycle_early_exit(const kv_paged_cache* cache, const void* k_new, const void* v_new,
+                             const void* target_logits, const void* draft_logits, int32_t dtype,
+                             const int32_t* draft_tokens, const int32_t* cu_draft,
+                             const float* u_accept, const float* u_sample,
+                             int32_t B, int32_t K, int32_t max_k, int32_t V,
+                             float temperature, int32_t top_k, float top_p,
+                             const specdec_params* per_request,
+                             int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                             int32_t* err_word, const specdec_debug* dbg,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* =====================================================================================
  * Contiguous KV cache
  * ===================================================================================== */

@@ -48,7 +48,8 @@ MAX_V = 2097152
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
-    "specdec_cycle_workspace_size", "specdec_cycle", "specdec_tree_verify_workspace_size",
+    "specdec_cycle_workspace_size", "specdec_cycle", "specdec_cycle_early_exit",
+    "specdec_tree_verify_workspace_size",
     "specdec_tree_verify", "kv_tree_commit",
     "kv_contig_append", "kv_contig_rollback",
 ]
@@ -159,10 +160,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.specdec_cycle_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32, pp]
     lib.specdec_cycle_workspace_size.restype = sz
-    lib.specdec_cycle.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp,
-                                  vp, vp, i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
-                                  ctypes.POINTER(SpecdecDebug), vp, sz, vp]
-    lib.specdec_cycle.restype = ctypes.c_int
+    for fn in (lib.specdec_cycle, lib.specdec_cycle_early_exit):
+        fn.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32, vp, vp, vp, vp,
+                       i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
+                       ctypes.POINTER(SpecdecDebug), vp, sz, vp]
+        fn.restype = ctypes.c_int
     lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.specdec_tree_verify_workspace_size.restype = sz
     lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
@@ -353,8 +355,10 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
                   temperatures: Optional[torch.Tensor] = None,
                   top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
                   top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
-                  max_emit: Optional[torch.Tensor] = None) -> None:
-    """Enqueue append -> verify -> rollback of one cycle as fused launches."""
+                  max_emit: Optional[torch.Tensor] = None, early_exit: bool = False) -> None:
+    """Enqueue append -> verify -> rollback of one cycle as fused launches. With
+    ``early_exit`` (specdec_cycle_early_exit) the row statistics run position by position and
+    no row past a request's first rejection is read."""
     lib = load_library()
     dev = target_logits.device
     dtype = _logits_dtype(target_logits)
@@ -381,7 +385,8 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
     prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
-    st = lib.specdec_cycle(
+    name = "specdec_cycle_early_exit" if early_exit else "specdec_cycle"
+    st = getattr(lib, name)(
         ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
         dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,
         V, float(temperature), int(top_k), float(top_p), _pref(prm), _ptr(out_tokens),
@@ -389,7 +394,7 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
         _ptr(num_emitted), _ptr(err_word), ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
-        raise SpecdecError("specdec_cycle", st)
+        raise SpecdecError(name, st)
 
 
 # --- HIP events and stream waits through the runtime (timing, cross-stream ordering) -----

@@ -60,6 +60,24 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1, rpar);
 }
 
+// Early-exit statistics: launch p holds the statistics of position p's rows (workgroup 0
+// of launch 0 allocates the cycle's blocks first, as k_cycle_stats does).
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_cycle_pass(KvArgs kv, const int* __restrict__ cu,
+                                                    int B, int N, uint8_t* __restrict__ aws,
+                                                    SampleArgs sa, RowPartial* __restrict__ part,
+                                                    int p) {
+    if (p == 0) {
+        if (blockIdx.x == 0) {
+            alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
+            return;
+        }
+        pass_body<BF16, VEC>(sa, part, 0, blockIdx.x - 1);
+    } else {
+        pass_body<BF16, VEC>(sa, part, p, blockIdx.x);
+    }
+}
+
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
 
 // P2: 0 top-k, 1 top-p alone, 2 per-request parameters
@@ -134,6 +152,31 @@ __global__ __launch_bounds__(kKvNT) void k_cycle_rollback(SampleArgs sa, KvArgs 
     rollback_body(kv, sa.num_acc, sa.cu, sa.B);
 }
 
+// decision (with the K/V scatter), draw, rollback; analytics when asked
+template <bool BF16, bool VEC>
+static void launch_cycle_tail(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew, int B,
+                              int K, const WsPlan& p, uint8_t* aws, const SampleArgs& sa,
+                              hipStream_t st) {
+    const int N = K + B;
+    const int tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);
+    const int ntiles = (N + tpw - 1) / tpw;
+    hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
+                       dim3(kDecideNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
+    const int rb = B <= kCycRbMaxB;
+    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
+                       st, sa, kv, rb);
+    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
+    if (sa.prec && K > 0) {
+        // acceptance analytics: residual mass of every proposal position, then beta and E[A]
+        hipLaunchKernelGGL((k_accept_part<BF16, VEC>), dim3((unsigned)K * p.nch), dim3(kPartNT), 0,
+                           st, sa);
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    } else if (sa.prec) {
+        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
+    }
+    if (!rb) hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, sa, kv);
+}
+
 template <bool BF16, bool VEC>
 static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
                          const uint8_t* tgt, const uint8_t* dft, const int* cu, int B, int K,
@@ -185,23 +228,25 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
                               p.nchunks, c, part, (const RowParams*)nullptr);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
-    const int tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);
-    const int ntiles = (N + tpw - 1) / tpw;
-    hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
-                       dim3(kDecideNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
-    const int rb = B <= kCycRbMaxB;
-    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
-                       st, sa, kv, rb);
-    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
-    if (sa.prec && K > 0) {
-        // acceptance analytics: residual mass of every proposal position, then beta and E[A]
-        hipLaunchKernelGGL((k_accept_part<BF16, VEC>), dim3((unsigned)K * p.nch), dim3(kPartNT), 0,
-                           st, sa);
-        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
-    } else if (sa.prec) {
-        hipLaunchKernelGGL((k_accept_final<BF16>), dim3(B), dim3(kWave), 0, st, sa);
-    }
-    if (!rb) hipLaunchKernelGGL(k_cycle_rollback, dim3(1), dim3(kKvNT), 0, st, sa, kv);
+    launch_cycle_tail<BF16, VEC>(kv, knew, vnew, B, K, p, aws, sa, st);
+}
+
+// The early-exit cycle: one statistics launch per position (plain temperature only), then
+// the same decision, draw and cache launches.
+template <bool BF16, bool VEC>
+static void launch_cycle_early(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
+                               const int* cu, int B, int K, int max_k, const WsPlan& p,
+                               uint8_t* vws, uint8_t* aws, const SampleArgs& sa,
+                               const specdec_debug* dbg, hipStream_t st) {
+    RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
+    const unsigned nwg = (unsigned)B * 2u * (unsigned)p.nchunks;
+    if (dbg && dbg->ev_stats_begin) (void)hipEventRecord(dbg->ev_stats_begin, st);
+    for (int q = 0; q <= max_k; ++q)
+        hipLaunchKernelGGL((k_cycle_pass<BF16, VEC>), dim3(nwg + (q == 0 ? 1u : 0u)), dim3(kNT), 0,
+                           st, kv, cu, B, K + B, aws, sa, part, q);
+    if (dbg && dbg->ev_stats_end) (void)hipEventRecord(dbg->ev_stats_end, st);
+    if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
+    launch_cycle_tail<BF16, VEC>(kv, knew, vnew, B, K, p, aws, sa, st);
 }
 
 }  // namespace sd
@@ -217,15 +262,22 @@ extern "C" size_t specdec_cycle_workspace_size(int32_t B, int32_t K, int32_t V, 
            sd::append_ws_bytes(B, K + B);
 }
 
-extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
-                             const void* target_logits, const void* draft_logits, int32_t dtype,
-                             const int32_t* draft_tokens, const int32_t* cu_draft,
-                             const float* u_accept, const float* u_sample, int32_t B, int32_t K,
-                             int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                             float top_p, const specdec_params* per_request, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
-                             int32_t* err_word, const specdec_debug* dbg, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_new,
+                       const void* v_new, const void* target_logits, const void* draft_logits,
+                       int32_t dtype, const int32_t* draft_tokens, const int32_t* cu_draft,
+                       const float* u_accept, const float* u_sample, int32_t B, int32_t K,
+                       int32_t max_k, int32_t V, float temperature, int32_t top_k, float top_p,
+                       const specdec_params* per_request, int32_t* out_tokens,
+                       int32_t* num_accepted, int32_t* num_emitted, int32_t* err_word,
+                       const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
     using namespace sd;
+    // early exit: plain temperature only, no analytics (they need every row)
+    if (early && (topk_active(top_k, V) || topp_active(top_p) ||
+                  (per_request && (per_request->temperature || per_request->top_k ||
+                                   per_request->top_p)) ||
+                  (dbg && (dbg->accept_prob || dbg->expected_emitted))))
+        return SPECDEC_EINVAL;
     // verification arguments: the same checks as specdec_verify
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
@@ -282,6 +334,8 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     sa.c = c;
     sa.eos = per_request ? per_request->eos_token : nullptr;
     sa.cap = per_request ? per_request->max_emit : nullptr;
+    sa.early = early ? 1 : 0;
+    sa.live = reinterpret_cast<int*>(vws + p.live);
     sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(vws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(vws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(vws + p.thr);
@@ -303,7 +357,15 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
     ParamArgs pa{};
     if (p.pr) pa = param_args(cu_draft, B, K, V, temperature, top_k, top_p, per_request, p, vws);
     (void)hipGetLastError();
-    if (dtype == SPECDEC_BF16) {
+    if (early) {
+        if (dtype == SPECDEC_BF16) {
+            if (vec) launch_cycle_early<true, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+            else launch_cycle_early<true, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+        } else {
+            if (vec) launch_cycle_early<false, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+            else launch_cycle_early<false, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+        }
+    } else if (dtype == SPECDEC_BF16) {
         if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
         else launch_cycle<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
     } else {
@@ -311,4 +373,37 @@ extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, con
         else launch_cycle<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}
+
+extern "C" int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_new,
+                             const void* target_logits, const void* draft_logits, int32_t dtype,
+                             const int32_t* draft_tokens, const int32_t* cu_draft,
+                             const float* u_accept, const float* u_sample, int32_t B, int32_t K,
+                             int32_t max_k, int32_t V, float temperature, int32_t top_k,
+                             float top_p, const specdec_params* per_request, int32_t* out_tokens,
+                             int32_t* num_accepted, int32_t* num_emitted, int32_t* err_word,
+                             const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    return cycle_entry(false, cache, k_new, v_new, target_logits, draft_logits, dtype,
+                       draft_tokens, cu_draft, u_accept, u_sample, B, K, max_k, V, temperature,
+                       top_k, top_p, per_request, out_tokens, num_accepted, num_emitted, err_word,
+                       dbg, workspace, workspace_bytes, stream);
+}
+
+extern "C" int specdec_cycle_early_exit(const kv_paged_cache* cache, const void* k_new,
+                                        const void* v_new, const void* target_logits,
+                                        const void* draft_logits, int32_t dtype,
+                                        const int32_t* draft_tokens, const int32_t* cu_draft,
+                                        const float* u_accept, const float* u_sample, int32_t B,
+                                        int32_t K, int32_t max_k, int32_t V, float temperature,
+                                        int32_t top_k, float top_p,
+                                        const specdec_params* per_request, int32_t* out_tokens,
+                                        int32_t* num_accepted, int32_t* num_emitted,
+                                        int32_t* err_word, const specdec_debug* dbg,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+    return cycle_entry(true, cache, k_new, v_new, target_logits, draft_logits, dtype,
+                       draft_tokens, cu_draft, u_accept, u_sample, B, K, max_k, V, temperature,
+                       top_k, top_p, per_request, out_tokens, num_accepted, num_emitted, err_word,
+                       dbg, workspace, workspace_bytes, stream);
 }

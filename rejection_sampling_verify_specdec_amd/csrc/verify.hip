@@ -232,6 +232,8 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.c = c;
     sa.eos = per_request ? per_request->eos_token : nullptr;
     sa.cap = per_request ? per_request->max_emit : nullptr;
+    sa.early = 0;
+    sa.live = nullptr;
     sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(ws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);

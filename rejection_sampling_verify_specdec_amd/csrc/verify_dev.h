@@ -1204,9 +1204,49 @@ struct SampleArgs {
     double* wacc;            // analytics: [K][nch][kSSub] sub-chunk sums of max(0, p - q)
     const int* eos;          // [B] end-of-sequence token per request (< 0 none), or null
     const int* cap;          // [B] most tokens a request may emit (<= 0 none), or null
+    int early;               // 1: rows past each request's first rejection were not read
+    int* live;               // early exit: [2][B] each request's liveness, one buffer per
+                             // launch parity
 };
 
 constexpr int kMaxRows = 2 * SPECDEC_MAX_K + 1;
+
+// A row's max m and exp-sum S (and kept count) from its chunk partials, combined in fp64 in
+// a fixed order: batches of eight, what was summed so far rescaled to the running max.
+SD_DEV void combine_partials(const RowPartial* pp, int nparts, double cd, float* m_out,
+                             double* S_out, int* nk_out) {
+    float m = -INFINITY;
+    double S = 0.0;
+    int nk = 0;
+    for (int q0 = 0; q0 < nparts; q0 += 8) {
+        RowPartial x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {                // the batch's loads issue together
+            if (q0 + q < nparts) x[q] = pp[q0 + q];
+            else x[q] = RowPartial{-INFINITY, 0, 0.0};
+        }
+        float mb = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) mb = fmaxf(mb, x[q].m);
+        const float mn = fmaxf(m, mb);
+        if (m != -INFINITY && mn != m) S *= exp2((double)(m - mn) * cd);
+        m = mn;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            // chunks with no finite entry carry 0 (or NaN, which must propagate)
+            S += x[q].m == -INFINITY ? x[q].s : x[q].s * exp2((double)(x[q].m - m) * cd);
+            nk += x[q].nkept;
+        }
+    }
+    *m_out = m;
+    *S_out = S;
+    *nk_out = nk;
+}
+
+// p(x) of a logit z in a row with max m, exp-sum S and threshold thr, in fp64
+SD_DEV double kept_prob(float z, float m, double S, float thr, double cd) {
+    return (z >= thr && z > -INFINITY) ? exp2(((double)z - (double)m) * cd) / S : 0.0;
+}
 
 // Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection (RESID), p(x)
 // for the bonus; p and q in fp64 from fp32 exponentials of the same form the statistics
@@ -1275,6 +1315,8 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
     __shared__ double s_S[kMaxRows];
     __shared__ float s_thr[kMaxRows];
     __shared__ int s_rowbad;
+    __shared__ int s_bad[kMaxRows];     // early exit: each row's validity
+    __shared__ int s_vis;               // early exit: the last visited position
     const int tid = threadIdx.x, lane = tid % kWave;
     const int rows_t = a.K + a.B;
 
@@ -1311,38 +1353,18 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
     if (tid < nrows) {
         const int r = tid;
         const int prow = r <= k ? lo + b + r : rows_t + lo + (r - k - 1);
-        const RowPartial* pp = a.part + (size_t)prow * a.nparts;
-        float m = -INFINITY;
-        double S = 0.0;
-        int nk = 0;
-        // batches of 8 partials: their loads are issued together
-        for (int q0 = 0; q0 < a.nparts; q0 += 8) {
-            RowPartial x[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (q0 + q < a.nparts) x[q] = pp[q0 + q];
-                else x[q] = RowPartial{-INFINITY, 0, 0.0};
-            }
-            float mb = -INFINITY;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) mb = fmaxf(mb, x[q].m);
-            const float mn = fmaxf(m, mb);
-            // rescale what was summed so far to the new max, then add this batch
-            if (m != -INFINITY && mn != m) S *= exp2((double)(m - mn) * cd);
-            m = mn;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                // chunks with no finite entry carry 0 (or NaN, which must propagate)
-                S += x[q].m == -INFINITY ? x[q].s : x[q].s * exp2((double)(x[q].m - m) * cd);
-                nk += x[q].nkept;
-            }
-        }
+        float m;
+        double S;
+        int nk;
+        combine_partials(a.part + (size_t)prow * a.nparts, a.nparts, cd, &m, &S, &nk);
         const float thr = a.topk ? a.row_thr[prow] : -INFINITY;
         s_m[r] = m;
         s_S[r] = S;
         s_thr[r] = thr;
-        if (!(S > 0.0 && S < INFINITY && m > -INFINITY)) atomicOr(&s_rowbad, 1);
-        if (publish) {
+        const bool rbad = !(S > 0.0 && S < INFINITY && m > -INFINITY);
+        if (a.early) s_bad[r] = rbad;
+        else if (rbad) atomicOr(&s_rowbad, 1);
+        if (publish && !a.early) {
             if (a.dbg.row_max) a.dbg.row_max[prow] = m;
             if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
             if (a.dbg.row_thr) a.dbg.row_thr[prow] = thr;
@@ -1366,16 +1388,29 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
                 const float zt = load_elem(a.tgt + (size_t)(lo + b + lane) * a.V * Lt::ES, y, BF16);
                 const float zd = load_elem(a.dft + (size_t)(lo + lane) * a.V * Lt::ES, y, BF16);
                 const int rt = lane, rd = k + 1 + lane;
-                if (zt >= s_thr[rt] && zt > -INFINITY)
-                    P = exp2(((double)zt - (double)s_m[rt]) * cd) / s_S[rt];
-                if (zd >= s_thr[rd] && zd > -INFINITY)
-                    Q = exp2(((double)zd - (double)s_m[rd]) * cd) / s_S[rd];
+                P = kept_prob(zt, s_m[rt], s_S[rt], s_thr[rt], cd);
+                Q = kept_prob(zd, s_m[rd], s_S[rd], s_thr[rd], cd);
                 acc = u * Q < P;
             }
         }
+        // early exit: the rows of position i were read only if proposals 0..i-1 passed the
+        // test the statistics launches apply (valid uniform and token, accepted); the
+        // request's visited positions are 0..vis
+        bool rowbad = s_rowbad != 0;
+        if (a.early) {
+            const bool ok = (flags & (SPECDEC_ERR_UNIFORM | SPECDEC_ERR_TOKEN)) == 0 && acc;
+            const unsigned long long stop = __ballot(lane < k && !ok);
+            const int vis = stop ? (__ffsll((long long)stop) - 1) : k;
+            int rb = 0;
+            for (int r = lane; r < nrows; r += kWave)     // target rows 0..k, then draft rows
+                if ((r <= k ? r : r - k - 1) <= vis) rb |= s_bad[r];
+            rowbad = __ballot(rb) != 0ull;
+            if (lane == 0) s_vis = vis;
+            if (lane > vis && lane < k) P = Q = NAN;    // rows never read
+        }
         const double us = (double)a.u_smp[b];
         if (lane == 0 && !(us >= 0.0 && us < 1.0)) flags |= SPECDEC_ERR_UNIFORM;
-        if (lane == 0 && s_rowbad && !pbad) flags |= SPECDEC_ERR_NONFINITE;
+        if (lane == 0 && rowbad && !pbad) flags |= SPECDEC_ERR_NONFINITE;
         if (lane == 0 && pbad) flags |= SPECDEC_ERR_PARAM;
         const unsigned long long rej = __ballot(lane < k && !acc);
         const int j = rej ? (__ffsll((long long)rej) - 1) : k;
@@ -1464,6 +1499,15 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         }
     }
     __syncthreads();
+    if (a.early && publish && tid < nrows) {
+        // early exit: statistics of the visited rows; rows never read report NaN
+        const int prow = tid <= k ? lo + b + tid : rows_t + lo + (tid - k - 1);
+        const bool seen = (tid <= k ? tid : tid - k - 1) <= s_vis;
+        if (a.dbg.row_max) a.dbg.row_max[prow] = seen ? s_m[tid] : NAN;
+        if (a.dbg.row_sum) a.dbg.row_sum[prow] = seen ? s_S[tid] : NAN;
+        if (a.dbg.row_thr) a.dbg.row_thr[prow] = seen ? s_thr[tid] : NAN;
+        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = -1;
+    }
 }
 
 // Sums of the sampling weights over the kSSub sub-chunks (kSSubLen consecutive tokens
@@ -1566,6 +1610,73 @@ SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
     __shared__ Decision D;
     decide_body<BF16, NT>(a, b, true, D);
     if (threadIdx.x == 0) a.rec[b] = D;
+}
+
+// ---------------------------------------------------------------------------------------
+// Early exit (an opt-in cycle): the statistics run position by position, one launch per
+// position p = 0..max_k. Workgroup (b, side, chunk) of launch p reads its chunk of request
+// b's target row p (side 0) or draft row p (side 1, only while p < k_b) if every proposal
+// before p passed the accept test with a valid uniform and token. That test is evaluated
+// again here from the partials the earlier launches wrote, with the decision's own
+// arithmetic (combine_partials, kept_prob, u * Q < P), so both agree on the rows that
+// were read. Rows past a request's first rejection are never read; the decision, the
+// draw and the cache steps then run as in the full cycle. Plain temperature only (no
+// top-k / top-p): partials are per chunk.
+// ---------------------------------------------------------------------------------------
+template <bool BF16, bool VEC>
+SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+    using Lt = Layout<BF16, true>;
+    __shared__ int s_live;
+    const int nchunks = a.nparts;
+    const int b = w / (2 * nchunks);
+    const int side = (w / nchunks) & 1;
+    const int chunk = w - (w / nchunks) * nchunks;
+    const int rows_t = a.K + a.B;
+    const int lo = a.cu[b], hi = a.cu[b + 1];
+    const int k = hi - lo;
+    if (threadIdx.x < 2) {
+        // lane 0 takes the target row of proposal p-1, lane 1 its draft row
+        const int lane = threadIdx.x;
+        // live at p: proposals 0..p-1 all passed. The previous launch left the flag for
+        // 0..p-2 (live[(p-1) & 1], 0 also for malformed offsets); proposal p-1 is tested
+        // here from its rows' partials.
+        bool live;
+        if (p == 0) {
+            live = !(a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
+                     hi > a.K);
+        } else {
+            live = a.live[((p - 1) & 1) * a.B + b] != 0 && p <= k;
+            if (live) {
+                const int i = lo + p - 1;
+                const int y = a.tokens[i];
+                const double u = (double)a.u_acc[i];
+                live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
+                if (live) {
+                    const double cd = (double)a.c;
+                    const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
+                    const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
+                                                    : a.dft + (size_t)i * a.V * Lt::ES;
+                    float m;
+                    double S;
+                    int nk;
+                    combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
+                    const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
+                    const double Q = __shfl(pr, 1, kWave);
+                    live = u * Q < pr;               // lane 0's: P = its own
+                }
+            }
+        }
+        if (lane == 0) {
+            // one workgroup per request leaves the flag for the next launch (every launch
+            // writes every request's flag, so none is stale)
+            if (side == 0 && chunk == 0) a.live[(p & 1) * a.B + b] = live ? 1 : 0;
+            s_live = live && (side == 0 || p < k);
+        }
+    }
+    __syncthreads();
+    if (!s_live) return;
+    const int row = side == 0 ? lo + b + p : rows_t + lo + p;
+    row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part, row * nchunks + chunk);
 }
 
 // Draw from the target row's kept-token list (bf16 top-k rows). Tokens outside the list
@@ -1990,8 +2101,8 @@ SD_DEV void merge_pr_body(const TopkArgs& a, int row) {
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsPlan {
-    size_t part, thr, rec, wsum, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc, rpar,
-        prec, wacc, total;
+    size_t part, thr, rec, wsum, live, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc,
+        rpar, prec, wacc, total;
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
     int pr;                  // per-request parameters: every row through the chunk select
     int wide_merge;          // top-p on: the wider merge workgroups (rows may need passes)
@@ -2079,6 +2190,8 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
     off = align256(off + (size_t)B * sizeof(Decision));
     p.wsum = off;
     off = align256(off + (size_t)B * p.nch * kSSub * sizeof(double));
+    p.live = off;                          // early-exit liveness flags
+    off = align256(off + (size_t)2 * B * sizeof(int));
     p.tk_cnt = p.tk_cand = p.tk_cpart = p.tk_ctc = off;
     if (p.filter && !p.sel_generic) {
         p.tk_wcap = topk_wcap(p.sel_k);

@@ -154,3 +154,33 @@ def test_tree_workspace_and_host_validation_without_gpu(lib):
     assert call(ws=17) == binding.SPECDEC_EWORKSPACE
     assert call(nbytes=binding.specdec_tree_verify_workspace_size(1, 1, 1000) - 1,
                 team=1) == binding.SPECDEC_EWORKSPACE
+
+
+def test_early_exit_host_validation_without_gpu(lib):
+    # the early-exit cycle takes plain temperature only: top-k, top-p, per-request transform
+    # arrays and the acceptance analytics are EINVAL before anything is enqueued; allowed
+    # arguments go on to the workspace check (8 bytes: EWORKSPACE), as specdec_cycle does
+    c = binding.KvPagedCacheStruct(16, 2, 2, 8, 16, 64, 8, 16, 16, 16, 16, 16, 16)
+
+    def call(fn, top_k=0, top_p=1.0, pr=None, dbg=None):
+        return fn(ctypes.byref(c), 16, 16, 16, 16, 1, 16, 16, 16, 16, 4, 8, 2, 1000, 1.0, top_k,
+                  top_p, ctypes.byref(pr) if pr is not None else None, 16, 16, 16, 16,
+                  ctypes.byref(dbg) if dbg is not None else None, 16, 8, None)
+
+    ee, full = lib.specdec_cycle_early_exit, lib.specdec_cycle
+    analytics = binding.SpecdecDebug()
+    analytics.accept_prob = 16
+    eos_only = binding.SpecdecParams(None, None, None, 0, 16, 16)
+    for kw in (dict(top_k=10), dict(top_p=0.9), dict(top_p=0.5, top_k=999),
+               dict(pr=binding.SpecdecParams(16, None, None, 0)),
+               dict(pr=binding.SpecdecParams(None, 16, None, 4)),
+               dict(pr=binding.SpecdecParams(None, None, 16, 0)), dict(dbg=analytics)):
+        assert call(ee, **kw) == binding.SPECDEC_EINVAL, kw
+        assert call(full, **kw) == binding.SPECDEC_EWORKSPACE, kw
+    for kw in (dict(), dict(top_k=1000), dict(top_k=0, top_p=1.0, pr=eos_only),
+               dict(dbg=binding.SpecdecDebug())):
+        assert call(ee, **kw) == binding.SPECDEC_EWORKSPACE, kw
+    # the checks both entry points share
+    assert call(ee, top_p=float("nan")) == binding.SPECDEC_EINVAL
+    assert ee(ctypes.byref(c), 16, 16, 16, 16, 1, 16, 16, 16, 16, 0, 8, 2, 1000, 1.0, 0, 1.0,
+              None, 16, 16, 16, 16, None, 16, 1 << 30, None) == binding.SPECDEC_EINVAL

@@ -1,0 +1,212 @@
+"""The early-exit cycle (specdec_cycle_early_exit: row statistics position by position,
+no row read past a request's first rejection) against the full cycle, on twin inputs and
+caches: accepted counts, emitted tokens, error word, request flags, the draw's W and
+picked probability, cache metadata and pool bits are equal bit for bit; p(y), q(y) and
+the row statistics of the positions it read are equal too, and those of the positions it
+did not read are NaN. The full cycle is itself checked against the oracle elsewhere, so
+this carries the oracle parity over ("Speculative decoding: accelerate LLM generation
+without changing its answers" §2-3: nothing after the first rejection is looked at).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import KVOnDevice, VerifyOnDevice, log
+from rejection_sampling_verify_specdec_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(vin, kv, early, top_k=None, eos=None, max_emit=None, cu=None, free_count=None,
+         plant=None):
+    g_kv = KVOnDevice(kv, vin.B)
+    if free_count is not None:
+        g_kv.cache.free_count.fill_(free_count)
+    g_v = VerifyOnDevice(vin, top_k=top_k, eos=eos, max_emit=max_emit)
+    if cu is not None:
+        g_v.cu.copy_(torch.tensor(cu, dtype=torch.int32))
+    if plant is not None:
+        plant(g_v)
+    dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
+    ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, g_v.top_k,
+                                                          1.0, g_v.params),
+                     dtype=torch.uint8, device=g_v.tgt.device)
+    ws.fill_(0x5A if early else 0xA5)      # stale partials must not matter
+    binding.specdec_cycle(g_kv.cache, g_kv.k_new, g_kv.v_new, g_v.tgt, g_v.dft, g_v.tokens,
+                          g_v.cu, g_v.u_acc, g_v.u_smp, max_k=vin.max_k, temperature=vin.T,
+                          top_k=g_v.top_k, out_tokens=g_v.out_tokens, num_accepted=g_v.num_acc,
+                          num_emitted=g_v.num_emit, err_word=g_v.err, workspace=ws,
+                          debug=g_v.dbg, eos_tokens=g_v.eos, max_emit=g_v.max_emit,
+                          early_exit=early)
+    r = g_v.result()
+    u = g_v.u_acc.cpu().numpy()
+    y = g_v.tokens.cpu().numpy()
+    return r, g_kv.meta(), g_kv.pool.view(torch.int16).cpu().numpy(), u, y
+
+
+def _visited(vin, full, u, y):
+    """Last position whose rows the early-exit cycle reads, per request, from the full
+    cycle's p(y), q(y): the first proposal with an invalid uniform or token or that fails
+    u * Q < P (the same fp64 comparison), else k_b."""
+    vis = []
+    cu = vin.cu_draft
+    for b in range(vin.B):
+        lo, k = int(cu[b]), int(cu[b + 1] - cu[b])
+        v = k
+        for i in range(k):
+            ui, yi = float(u[lo + i]), int(y[lo + i])
+            ok = 0.0 <= ui < 1.0 and 0 <= yi < vin.V and ui * full.q_y[lo + i] < full.p_y[lo + i]
+            if not ok:
+                v = i
+                break
+        vis.append(v)
+    return vis
+
+
+def _same(a, b):
+    return a == b or (np.isnan(a) and np.isnan(b))
+
+
+def _compare(vin, full, early, u, y):
+    (f, fm, fp), (e, em, ep) = full, early
+    for name in ("num_accepted", "num_emitted", "out_tokens", "err_word", "resid_mass",
+                 "picked_prob", "req_flags"):
+        assert np.array_equal(np.asarray(getattr(f, name)), np.asarray(getattr(e, name)),
+                              equal_nan=True), name
+    for name in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
+        assert np.array_equal(np.asarray(fm[name]), np.asarray(em[name])), name
+    assert np.array_equal(fp, ep), "pool bits"
+    vis = _visited(vin, f, u, y)
+    cu, rows_t = vin.cu_draft, vin.K + vin.B
+    read = 0
+    for b in range(vin.B):
+        if f.req_flags[b] & binding.ERR_K:        # nothing was evaluated
+            continue
+        lo, k = int(cu[b]), int(cu[b + 1] - cu[b])
+        for i in range(k):
+            if i <= vis[b]:
+                assert _same(e.p_y[lo + i], f.p_y[lo + i]) and _same(e.q_y[lo + i], f.q_y[lo + i]), (b, i)
+            else:
+                assert np.isnan(e.p_y[lo + i]) and np.isnan(e.q_y[lo + i]), (b, i)
+        for i in range(k + 1):
+            rows = [lo + b + i] + ([rows_t + lo + i] if i < k else [])
+            for r in rows:
+                if i <= vis[b]:
+                    read += 1
+                    assert _same(e.row_max[r], f.row_max[r]) and _same(e.row_sum[r], f.row_sum[r]), (b, i)
+                else:
+                    assert np.isnan(e.row_max[r]) and np.isnan(e.row_sum[r]), (b, i)
+    return read, 2 * vin.K + vin.B
+
+
+def _both(vin, kv, **kw):
+    full = _run(vin, kv, False, **kw)
+    early = _run(vin, kv, True, **kw)
+    read, rows = _compare(vin, full[:3], early[:3], *full[3:])
+    acc = full[0].num_accepted
+    log(f"[early-exit]   rows read {read} of {rows}; accepted {int(acc[acc >= 0].sum())}, "
+        f"err {full[0].err_word:#x}")
+    return full[0]
+
+
+def _small_kv(wl, vin, seed, **over):
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=40, prefix_hi=300, **over)
+    return synth.make_kv(wl, vin, seed=seed, recipe=rec)
+
+
+@pytest.mark.parametrize("wl,dtype,V,k_range", [
+    ("c2", "bf16", 20000, None),          # 128-bit loads
+    ("c2", "bf16", 5003, (0, 6)),         # odd V (element loads), empty and ragged k_b
+    ("c1", "f32", 4000, None),
+    ("c1", "f32", 32000, (0, 8)),
+    ("c3", "bf16", 6000, None),           # copy / early-reject / normal classes, k_b 1..8
+])
+def test_early_exit_equals_the_full_cycle(wl, dtype, V, k_range):
+    over = dict(dtype=dtype)
+    if k_range is not None:
+        over.update(k_range=k_range, k=k_range[1])
+    vin = synth.make_verify(wl, seed=150, B=24, V=V, **over)
+    kv = _small_kv(wl, vin, 150, share_group=3, share_blocks=2)
+    log(f"[early-exit] {wl} {dtype} V={V} B={vin.B} K={vin.K} max_k={vin.max_k}")
+    _both(vin, kv)
+
+
+def test_early_exit_top_k_switched_off():
+    # top_k = V keeps every token: the plain path, so early exit takes it
+    vin = synth.make_verify("c2", seed=151, B=10, V=3000)
+    kv = _small_kv("c2", vin, 151)
+    log("[early-exit] top_k = V")
+    _both(vin, kv, top_k=vin.V)
+
+
+def test_early_exit_with_stops_and_errors():
+    vin = synth.make_verify("c3", seed=152, B=20, V=4096)
+    kv = _small_kv("c3", vin, 152)
+    cu = vin.cu_draft
+    kb = np.diff(cu)
+    eos = np.full(vin.B, -1, np.int32)
+    cap = np.zeros(vin.B, np.int32)
+    for b in range(0, vin.B, 3):             # EOS at the request's first or second proposal
+        eos[b] = int(vin.draft_tokens[cu[b] + min((b // 3) % 2, int(kb[b]) - 1)])
+    cap[1::4] = 1
+    cap[2::5] = 3
+    # three requests with two proposals or more: a uniform out of range at the second
+    # proposal, a token out of range at the first, NaN in the first target row (always read)
+    bu, bt, bn = [b for b in range(4, vin.B) if kb[b] >= 2][:3]
+
+    def plant(g):
+        g.u_acc[int(cu[bu]) + 1] = 1.5
+        g.tokens[int(cu[bt])] = vin.V + 3
+        g.tgt[int(cu[bn]) + bn, 17] = float("nan")
+
+    log("[early-exit] EOS, caps, bad uniform, bad token, NaN in a read row")
+    f = _both(vin, kv, eos=eos, max_emit=cap, plant=plant)
+    assert f.req_flags[bu] & binding.ERR_UNIFORM and f.req_flags[bt] & binding.ERR_TOKEN
+    assert f.req_flags[bn] & binding.ERR_NONFINITE
+
+
+def test_early_exit_out_of_blocks_and_bad_offsets():
+    vin = synth.make_verify("c4", seed=153, B=12, V=2048, top_k=0)
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=520, prefix_hi=700, share_group=4,
+                         share_blocks=32)
+    kv = synth.make_kv("c4", vin, seed=153, recipe=rec)
+    log("[early-exit] free_count 3 (ENOMEM)")
+    _both(vin, kv, free_count=3)
+    cu = vin.cu_draft.copy()
+    cu[-1] += 1
+    log("[early-exit] bad offsets")
+    _both(vin, kv, cu=cu)
+
+
+def test_early_exit_skips_rows_after_the_first_rejection():
+    # a non-finite row after a request's first rejection is not read: the full cycle
+    # reports it, the early-exit cycle returns the request's normal result
+    vin = synth.make_verify("c2", seed=154, B=8, V=4096)
+    kv = _small_kv("c2", vin, 154)
+    full, _, _, u, y = _run(vin, kv, False)
+    vis = _visited(vin, full, u, y)
+    b = next(i for i in range(vin.B) if vis[i] + 2 <= int(vin.cu_draft[i + 1] - vin.cu_draft[i]))
+    row = int(vin.cu_draft[b]) + b + vis[b] + 2     # a target row two positions past it
+
+    def plant(g):
+        g.tgt[row, 5] = float("nan")
+
+    log(f"[early-exit] NaN in request {b}'s target row {row} (first rejection at {vis[b]})")
+    f = _run(vin, kv, False, plant=plant)[0]
+    e = _run(vin, kv, True, plant=plant)[0]
+    assert f.req_flags[b] & binding.ERR_NONFINITE and f.num_accepted[b] == -1
+    assert not e.req_flags[b] & binding.ERR_NONFINITE
+    assert e.num_accepted[b] == full.num_accepted[b] and e.num_emitted[b] == full.num_emitted[b]
+    lo = int(vin.cu_draft[b]) + b
+    n = int(full.num_emitted[b])
+    assert np.array_equal(e.out_tokens[lo:lo + n], full.out_tokens[lo:lo + n])
+
+
+def test_early_exit_full_batch_and_vocabulary():
+    # the benchmark's batch and vocabulary (B = 256, k = 5, V = 128256 bf16, T = 0.7) with a
+    # small cache geometry
+    vin = synth.make_verify("c2", seed=155)
+    kv = _small_kv("c2", vin, 155)
+    log(f"[early-exit] c2 full size: B={vin.B} V={vin.V}")
+    _both(vin, kv)
