@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 output databases (kernel trace, PMC counters) as short text.
 
     python -m rejection_sampling_verify_specdec_amd.profsum trace DB [--cmd "..."]
+    python -m rejection_sampling_verify_specdec_amd.profsum sequence DB --match k_cycle_ --count 9
     python -m rejection_sampling_verify_specdec_amd.profsum traffic FETCH_DB WRITE_DB \
         --kernel k_cycle_stats --calib-kernel copyBuffer --calib-bytes N --alg-bytes A \
         [--json profiles/KERNEL_WORKLOAD_traffic.json --workload c2 --cmd "..."]
 
-``trace`` prints count / average / min / max duration per kernel. ``traffic`` turns the
+``trace`` prints count / average / min / max duration per kernel; ``sequence`` the last
+dispatches matching a name, in launch order, with durations and gaps. ``traffic`` turns the
 FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of a kernel into HBM bytes per
 launch, scaled by what the same counters read for a plain copy kernel of known size (the
 largest dispatch of the calibration kernel: the copy of N bytes), and optionally writes
@@ -44,6 +46,24 @@ def trace(db, cmd=None, top=12):
     out.append(f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}")
     for name, n, avg, mn, mx in _kernels(db)[:top]:
         out.append(f"{name[:64]:64s} {n:6d} {avg / 1e3:9.2f} {mn / 1e3:9.2f} {mx / 1e3:9.2f}")
+    return "\n".join(out)
+
+
+def sequence(db, match, count, cmd=None):
+    """The last `count` dispatches whose kernel name contains `match`, in launch order, with
+    each one's duration and the idle gap before it (one cycle's launches, say)."""
+    con = sqlite3.connect(db)
+    rows = [r for r in con.execute("select name, start, end from kernels order by start")
+            if match in r[0]][-count:]
+    out = [f"command: {cmd}"] if cmd else []
+    out.append(f"{'kernel':48s} {'dur_us':>9s} {'gap_us':>9s}")
+    prev = None
+    for name, s, e in rows:
+        gap = (s - prev) / 1e3 if prev is not None else 0.0
+        out.append(f"{name.split('(')[0][:48]:48s} {(e - s) / 1e3:9.2f} {gap:9.2f}")
+        prev = e
+    if rows:
+        out.append(f"{'span':48s} {(rows[-1][2] - rows[0][1]) / 1e3:9.2f}")
     return "\n".join(out)
 
 
@@ -94,6 +114,11 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("db")
     t.add_argument("--cmd")
+    q = sub.add_parser("sequence")
+    q.add_argument("db")
+    q.add_argument("--match", default="sd::")
+    q.add_argument("--count", type=int, default=20)
+    q.add_argument("--cmd")
     p = sub.add_parser("traffic")
     p.add_argument("fetch_db")
     p.add_argument("write_db")
@@ -107,6 +132,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.what == "trace":
         print(trace(a.db, a.cmd))
+    elif a.what == "sequence":
+        print(sequence(a.db, a.match, a.count, a.cmd))
     else:
         text, info = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes,
                              a.alg_bytes)

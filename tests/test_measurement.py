@@ -69,3 +69,23 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_sequence_lists_the_last_matching_dispatches_in_order(tmp_path):
+    db = str(tmp_path / "k.db")
+    con = sqlite3.connect(db)
+    con.execute("create table kernels (name text, start int, end int)")
+    con.executemany("insert into kernels values (?, ?, ?)", [
+        ("void sd::k_cycle_pass<true, true>(sd::KvArgs)", 1000, 26000),
+        ("at::native::fill", 26000, 30000),
+        ("void sd::k_cycle_pass<true, true>(sd::KvArgs)", 30500, 40000),
+        ("void sd::k_cycle_decide<true>(sd::SampleArgs)", 40000, 120000),
+    ])
+    con.commit()
+    con.close()
+    lines = profsum.sequence(db, "k_cycle_", 2).splitlines()
+    assert lines[1].split()[-2:] == ["9.50", "0.00"]          # the second pass, no gap shown
+    assert "k_cycle_decide" in lines[2] and lines[2].split()[-2:] == ["80.00", "0.00"]
+    assert lines[-1].split()[-1] == "89.50"                   # span of the two
+    lines = profsum.sequence(db, "k_cycle_", 3).splitlines()
+    assert lines[2].split()[-1] == "4.50"                     # gap past the fill
