@@ -52,8 +52,8 @@ def parse():
                         "rollback as three calls on one stream; overlap: the three calls with "
                         "the append on a second stream after the logit rows are streamed; "
                         "early-exit: specdec_cycle_early_exit (row statistics position by "
-                        "position, no row read past a request's first rejection; plain "
-                        "temperature only)")
+                        "position, no row read past a request's first rejection; temperature "
+                        "only)")
     p.add_argument("--timing-every", type=int, default=4,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
@@ -391,10 +391,9 @@ def main():
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-    if args.schedule == "early-exit" and (0 < vin.top_k < V or 0.0 < top_p < 1.0 or
-                                          args.per_request):
-        raise SystemExit("--schedule early-exit takes plain temperature only (no top-k, "
-                         "top-p or per-request arrays)")
+    if args.schedule == "early-exit" and (0 < vin.top_k < V or 0.0 < top_p < 1.0):
+        raise SystemExit("--schedule early-exit takes temperature only (scalar or per "
+                         "request; no top-k or top-p)")
     pr = {}
     if args.per_request:
         pr["temperatures"] = torch.full((B,), vin.T, dtype=torch.float32, device=d)

@@ -351,9 +351,11 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
  *   - debug p_y / q_y after the first rejection, and row_max / row_sum / row_thr of rows
  *     not read, are NaN (row_nkept -1);
  *   - events: ev_stats_begin / ev_stats_end bracket all the statistics launches.
+ * Temperature only: scalar, or per request (per_request->temperature; a request with an
+ * invalid temperature reads no row and fails with SPECDEC_ERR_PARAM as in specdec_cycle).
  * Host: every specdec_cycle check, and also EINVAL, before anything is enqueued, when top-k
- * (0 < top_k < V) or top-p (0 < top_p < 1) is on, when per_request carries temperature,
- * top_k or top_p arrays (eos_token and max_emit are allowed), or when dbg asks for the
+ * (0 < top_k < V) or top-p (0 < top_p < 1) is on, when per_request carries top_k or top_p
+ * arrays (temperature, eos_token and max_emit are allowed), or when dbg asks for the
  * acceptance analytics (accept_prob, expected_emitted: they need every row).
  */
 int specdec_cycle_early_exit(const kv_paged_cache* cache, const void* k_new, const void* v_new,

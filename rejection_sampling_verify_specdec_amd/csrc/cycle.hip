@@ -231,14 +231,19 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     launch_cycle_tail<BF16, VEC>(kv, knew, vnew, B, K, p, aws, sa, st);
 }
 
-// The early-exit cycle: one statistics launch per position (plain temperature only), then
-// the same decision, draw and cache launches.
+// The early-exit cycle: one statistics launch per position (temperature only, scalar or
+// per request), then the same decision, draw and cache launches.
 template <bool BF16, bool VEC>
 static void launch_cycle_early(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
                                const int* cu, int B, int K, int max_k, const WsPlan& p,
                                uint8_t* vws, uint8_t* aws, const SampleArgs& sa,
-                               const specdec_debug* dbg, hipStream_t st) {
+                               const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st) {
     RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
+    if (p.pr_plain) {          // per-request temperatures: each row's log2(e) / T first
+        const int rows = 2 * K + B;
+        hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
+                           pa, rows);
+    }
     const unsigned nwg = (unsigned)B * 2u * (unsigned)p.nchunks;
     if (dbg && dbg->ev_stats_begin) (void)hipEventRecord(dbg->ev_stats_begin, st);
     for (int q = 0; q <= max_k; ++q)
@@ -272,10 +277,10 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
                        const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
     using namespace sd;
-    // early exit: plain temperature only, no analytics (they need every row)
+    // early exit: temperature only (scalar or per request), no analytics (they need every
+    // row)
     if (early && (topk_active(top_k, V) || topp_active(top_p) ||
-                  (per_request && (per_request->temperature || per_request->top_k ||
-                                   per_request->top_p)) ||
+                  (per_request && (per_request->top_k || per_request->top_p)) ||
                   (dbg && (dbg->accept_prob || dbg->expected_emitted))))
         return SPECDEC_EINVAL;
     // verification arguments: the same checks as specdec_verify
@@ -359,11 +364,11 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
     (void)hipGetLastError();
     if (early) {
         if (dtype == SPECDEC_BF16) {
-            if (vec) launch_cycle_early<true, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
-            else launch_cycle_early<true, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+            if (vec) launch_cycle_early<true, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
+            else launch_cycle_early<true, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
         } else {
-            if (vec) launch_cycle_early<false, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
-            else launch_cycle_early<false, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, dbg, stream);
+            if (vec) launch_cycle_early<false, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
+            else launch_cycle_early<false, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
         }
     } else if (dtype == SPECDEC_BF16) {
         if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);

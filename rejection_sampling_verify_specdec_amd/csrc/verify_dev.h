@@ -1400,7 +1400,8 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         if (a.early) {
             const bool ok = (flags & (SPECDEC_ERR_UNIFORM | SPECDEC_ERR_TOKEN)) == 0 && acc;
             const unsigned long long stop = __ballot(lane < k && !ok);
-            const int vis = stop ? (__ffsll((long long)stop) - 1) : k;
+            // invalid parameters: the statistics launches read none of the rows
+            const int vis = pbad ? -1 : (stop ? (__ffsll((long long)stop) - 1) : k);
             int rb = 0;
             for (int r = lane; r < nrows; r += kWave)     // target rows 0..k, then draft rows
                 if ((r <= k ? r : r - k - 1) <= vis) rb |= s_bad[r];
@@ -1620,8 +1621,8 @@ SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
 // again here from the partials the earlier launches wrote, with the decision's own
 // arithmetic (combine_partials, kept_prob, u * Q < P), so both agree on the rows that
 // were read. Rows past a request's first rejection are never read; the decision, the
-// draw and the cache steps then run as in the full cycle. Plain temperature only (no
-// top-k / top-p): partials are per chunk.
+// draw and the cache steps then run as in the full cycle. Temperature only, scalar or per
+// request (no top-k / top-p): partials are per chunk.
 // ---------------------------------------------------------------------------------------
 template <bool BF16, bool VEC>
 SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
@@ -1644,6 +1645,8 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
         if (p == 0) {
             live = !(a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
                      hi > a.K);
+            // a request with invalid parameters fails in the decision without its rows
+            if (live && a.rpar) live = !(a.rpar[lo + b].flags & kRpBad);
         } else {
             live = a.live[((p - 1) & 1) * a.B + b] != 0 && p <= k;
             if (live) {
@@ -1652,7 +1655,8 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
                 const double u = (double)a.u_acc[i];
                 live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
                 if (live) {
-                    const double cd = (double)a.c;
+                    // the request's log2(e) / T, as the decision takes it
+                    const double cd = (double)(a.rpar ? a.rpar[lo + b].c : a.c);
                     const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
                     const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
                                                     : a.dft + (size_t)i * a.V * Lt::ES;
@@ -1676,7 +1680,8 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
     __syncthreads();
     if (!s_live) return;
     const int row = side == 0 ? lo + b + p : rows_t + lo + p;
-    row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part, row * nchunks + chunk);
+    row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part, row * nchunks + chunk,
+                              a.rpar);
 }
 
 // Draw from the target row's kept-token list (bf16 top-k rows). Tokens outside the list

@@ -19,11 +19,11 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(vin, kv, early, top_k=None, eos=None, max_emit=None, cu=None, free_count=None,
-         plant=None):
+         plant=None, temps=None):
     g_kv = KVOnDevice(kv, vin.B)
     if free_count is not None:
         g_kv.cache.free_count.fill_(free_count)
-    g_v = VerifyOnDevice(vin, top_k=top_k, eos=eos, max_emit=max_emit)
+    g_v = VerifyOnDevice(vin, top_k=top_k, eos=eos, max_emit=max_emit, temps=temps)
     if cu is not None:
         g_v.cu.copy_(torch.tensor(cu, dtype=torch.int32))
     if plant is not None:
@@ -38,7 +38,7 @@ def _run(vin, kv, early, top_k=None, eos=None, max_emit=None, cu=None, free_coun
                           top_k=g_v.top_k, out_tokens=g_v.out_tokens, num_accepted=g_v.num_acc,
                           num_emitted=g_v.num_emit, err_word=g_v.err, workspace=ws,
                           debug=g_v.dbg, eos_tokens=g_v.eos, max_emit=g_v.max_emit,
-                          early_exit=early)
+                          temperatures=g_v.temps, early_exit=early)
     r = g_v.result()
     u = g_v.u_acc.cpu().numpy()
     y = g_v.tokens.cpu().numpy()
@@ -53,6 +53,9 @@ def _visited(vin, full, u, y):
     cu = vin.cu_draft
     for b in range(vin.B):
         lo, k = int(cu[b]), int(cu[b + 1] - cu[b])
+        if full.req_flags[b] & binding.ERR_PARAM:      # invalid parameters: nothing read
+            vis.append(-1)
+            continue
         v = k
         for i in range(k):
             ui, yi = float(u[lo + i]), int(y[lo + i])
@@ -130,6 +133,22 @@ def test_early_exit_equals_the_full_cycle(wl, dtype, V, k_range):
     kv = _small_kv(wl, vin, 150, share_group=3, share_blocks=2)
     log(f"[early-exit] {wl} {dtype} V={V} B={vin.B} K={vin.K} max_k={vin.max_k}")
     _both(vin, kv)
+
+
+@pytest.mark.parametrize("wl,dtype,V,k_range", [("c2", "bf16", 20000, None),
+                                                ("c1", "f32", 5003, (0, 7))])
+def test_early_exit_per_request_temperatures(wl, dtype, V, k_range):
+    over = dict(dtype=dtype)
+    if k_range is not None:
+        over.update(k_range=k_range, k=k_range[1])
+    vin = synth.make_verify(wl, seed=156, B=20, V=V, **over)
+    kv = _small_kv(wl, vin, 156)
+    temps = np.random.default_rng(156).choice([0.4, 0.8, 1.2, 1.6], vin.B).astype(np.float32)
+    temps[3] = 0.0                     # invalid: that request fails, reading no row
+    temps[7] = float("nan")
+    log(f"[early-exit] per-request temperatures {wl} {dtype} V={V}")
+    f = _both(vin, kv, temps=temps)
+    assert f.req_flags[3] & binding.ERR_PARAM and f.req_flags[7] & binding.ERR_PARAM
 
 
 def test_early_exit_top_k_switched_off():
