@@ -186,7 +186,6 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     const int rows = 2 * K + B;
     const int N = K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
-    float* thr = reinterpret_cast<float*>(vws + p.thr);
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (p.pr_plain) {

@@ -563,7 +563,6 @@ template <bool BF16, bool VEC>
 SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
     using Lt = Layout<BF16, VEC>;
     __shared__ double red[kTreeNT / kWave + 1];
-    __shared__ float redf[kTreeNT / kWave];
     __shared__ int redi[kTreeNT / kWave];
     __shared__ double sub[kTreeMaxSub];
     __shared__ double sW[SPECDEC_MAX_TREE];        // 1 / W_s of the residuals so far

@@ -108,7 +108,6 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                        const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st) {
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
-    float* thr = reinterpret_cast<float*>(ws + p.thr);
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;

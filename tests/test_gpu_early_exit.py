@@ -151,6 +151,18 @@ def test_early_exit_per_request_temperatures(wl, dtype, V, k_range):
     assert f.req_flags[3] & binding.ERR_PARAM and f.req_flags[7] & binding.ERR_PARAM
 
 
+def test_early_exit_at_the_largest_proposal_count():
+    # k_b up to 64 (65 statistics launches): copied drafts accept every proposal and draw
+    # the bonus from target row 64; low-noise drafts reject deep in the row
+    vin = synth.make_verify("c3", seed=157, B=6, V=1000, k_range=(60, 64), k=64,
+                            classes=((0.5, "copy", 0.0), (0.5, "noise", 0.3)))
+    kv = _small_kv("c3", vin, 157)
+    log(f"[early-exit] max_k {vin.max_k}, k_b {np.diff(vin.cu_draft).tolist()}")
+    f = _both(vin, kv)
+    kb = np.diff(vin.cu_draft)
+    assert (f.num_accepted == kb).sum() >= 3 and (kb == 64).any()
+
+
 def test_early_exit_top_k_switched_off():
     # top_k = V keeps every token: the plain path, so early exit takes it
     vin = synth.make_verify("c2", seed=151, B=10, V=3000)
