@@ -163,6 +163,15 @@ def test_early_exit_at_the_largest_proposal_count():
     assert (f.num_accepted == kb).sum() >= 3 and (kb == 64).any()
 
 
+def test_early_exit_without_proposals():
+    # K = 0, max_k = 0: one statistics launch over the bonus rows
+    vin = synth.make_verify("c2", seed=158, B=5, V=3000, k_range=(0, 0), k=0)
+    kv = _small_kv("c2", vin, 158)
+    log("[early-exit] K = 0")
+    f = _both(vin, kv)
+    assert (f.num_emitted == 1).all()
+
+
 def test_early_exit_top_k_switched_off():
     # top_k = V keeps every token: the plain path, so early exit takes it
     vin = synth.make_verify("c2", seed=151, B=10, V=3000)
