@@ -1635,12 +1635,18 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
     const int rows_t = a.K + a.B;
     const int lo = a.cu[b], hi = a.cu[b + 1];
     const int k = hi - lo;
+    if (p > 0 && (a.live[((p - 1) & 1) * a.B + b] == 0 || p > k)) {
+        // not live: every thread leaves at once (the flag is the same for the whole
+        // workgroup); one workgroup per request passes the 0 on
+        if (side == 0 && chunk == 0 && threadIdx.x == 0) a.live[(p & 1) * a.B + b] = 0;
+        return;
+    }
     if (threadIdx.x < 2) {
         // lane 0 takes the target row of proposal p-1, lane 1 its draft row
         const int lane = threadIdx.x;
         // live at p: proposals 0..p-1 all passed. The previous launch left the flag for
-        // 0..p-2 (live[(p-1) & 1], 0 also for malformed offsets); proposal p-1 is tested
-        // here from its rows' partials.
+        // 0..p-2 (live[(p-1) & 1], 0 also for malformed offsets or invalid parameters);
+        // proposal p-1 is tested here from its rows' partials.
         bool live;
         if (p == 0) {
             live = !(a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
@@ -1648,26 +1654,24 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
             // a request with invalid parameters fails in the decision without its rows
             if (live && a.rpar) live = !(a.rpar[lo + b].flags & kRpBad);
         } else {
-            live = a.live[((p - 1) & 1) * a.B + b] != 0 && p <= k;
+            // live through proposal p-2 and p <= k (checked above): test proposal p-1
+            const int i = lo + p - 1;
+            const int y = a.tokens[i];
+            const double u = (double)a.u_acc[i];
+            live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
             if (live) {
-                const int i = lo + p - 1;
-                const int y = a.tokens[i];
-                const double u = (double)a.u_acc[i];
-                live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
-                if (live) {
-                    // the request's log2(e) / T, as the decision takes it
-                    const double cd = (double)(a.rpar ? a.rpar[lo + b].c : a.c);
-                    const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
-                    const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
-                                                    : a.dft + (size_t)i * a.V * Lt::ES;
-                    float m;
-                    double S;
-                    int nk;
-                    combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
-                    const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
-                    const double Q = __shfl(pr, 1, kWave);
-                    live = u * Q < pr;               // lane 0's: P = its own
-                }
+                // the request's log2(e) / T, as the decision takes it
+                const double cd = (double)(a.rpar ? a.rpar[lo + b].c : a.c);
+                const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
+                const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
+                                                : a.dft + (size_t)i * a.V * Lt::ES;
+                float m;
+                double S;
+                int nk;
+                combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
+                const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
+                const double Q = __shfl(pr, 1, kWave);
+                live = u * Q < pr;                   // lane 0's: P = its own
             }
         }
         if (lane == 0) {
