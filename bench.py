@@ -66,6 +66,8 @@ def parse():
                    help="also time the fused cycle captured once in a HIP graph and replayed "
                         "(no host launch cost per cycle: what small batches need)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-early-exit-compare", action="store_true",
+                   help="skip timing specdec_cycle_early_exit beside the fused cycle")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before timing "
                         "(a known-size reference for HBM traffic counters)")
@@ -360,10 +362,16 @@ def main():
     vin = synth.make_verify(wl, seed=args.seed, B=args.batch,
                             **({} if args.top_k is None else {"top_k": args.top_k}))
     top_p = args.top_p
+    # the fused cycle with temperature only is also timed in its early-exit form, on the
+    # same batch and cache, after the timed region
+    compare_early = (args.schedule == "fused" and not args.no_early_exit_compare and
+                     not 0 < vin.top_k < vin.V and not 0.0 < top_p < 1.0)
     # the pool holds the warm-up, the timed cycles and twice as many again for the
-    # percentiles (without and with a cache flush before each cycle)
+    # percentiles (without and with a cache flush before each cycle), and the early-exit
+    # comparison's cycles
     kv = synth.make_kv(wl, vin, seed=args.seed,
-                       cycles=args.warmup + (5 if args.graph else 3) * args.steps + 4)
+                       cycles=args.warmup + (5 if args.graph else 3) * args.steps + 4 +
+                       (args.steps + 10 if compare_early else 0))
     print(f"# inputs drawn in {time.time() - t0:.1f} s: B={vin.B} K={vin.K} V={vin.V} "
           f"NB={kv.num_blocks}", file=sys.stderr, flush=True)
 
@@ -508,6 +516,25 @@ def main():
         torch.cuda.synchronize()
         cyc_fl_ms = np.array([a.elapsed_time(b) for a, b in cyc])
         del junk
+    early_cmp = None
+    if compare_early:
+        # specdec_cycle_early_exit on the same batch: 10 untimed cycles, then as many as
+        # the timed region, by wall clock
+        def ee_step():
+            binding.specdec_cycle(cache, k_new, v_new, tgt, dft, tokens, cu, u_acc, u_smp,
+                                  max_k=vin.max_k, temperature=vin.T, top_k=vin.top_k,
+                                  out_tokens=out, num_accepted=nacc, num_emitted=nemit,
+                                  err_word=err, workspace=cws, top_p=top_p, early_exit=True,
+                                  **pr)
+        for _ in range(10):
+            ee_step()
+        torch.cuda.synchronize()
+        te0 = time.perf_counter()
+        for _ in range(args.steps):
+            ee_step()
+        torch.cuda.synchronize()
+        ee_ms = (time.perf_counter() - te0) / args.steps * 1e3
+        early_cmp = {"ms_per_step": ee_ms, "value": vin.K / (ee_ms / 1e3), "unit": "positions/s"}
     graph = None
     if args.graph and args.schedule in ("fused", "early-exit"):
         # one cycle captured (its launches read every size and pointer from device memory or
@@ -628,6 +655,11 @@ def main():
     if graph is not None:
         res["graph"] = graph
     res["acceptance"] = acceptance
+    if early_cmp is not None:
+        # not the headline: the metric counts every logit row, which this cycle skips
+        early_cmp["logit_rows_read"] = seq_rows
+        early_cmp["logit_rows"] = rows
+        res["early_exit"] = early_cmp
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(vin, kv, args.cpu_seconds, top_p)
         workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
