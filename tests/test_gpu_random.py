@@ -129,3 +129,32 @@ def test_random_trees_match_the_oracle_for_any_team(seed):
     solo = TreeOnDevice(tin, team=1).run()
     for key in ("a", "n", "out", "nodes", "flags"):
         assert np.array_equal(g[key], solo[key]), key
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_early_exit_cycles_equal_the_full_cycle(seed):
+    # the early-exit cycle on random temperature-only batches (dtype, V, B, ragged and empty
+    # k_b, scalar or per-request temperatures with an invalid one now and then, EOS / caps,
+    # draft noise): bit for bit against the full cycle on twin caches
+    from test_gpu_early_exit import _both
+    opts, r = _case(200 + seed)
+    opts.update(top_k=0, top_p=1.0)
+    vin = _inputs(opts, 200 + seed)
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=10, prefix_hi=200, share_group=2,
+                         share_blocks=1)
+    kv = synth.make_kv("c1", vin, seed=seed, recipe=rec)
+    kw = {}
+    if opts["per_request"]:
+        temps = r.choice([0.4, 0.8, 1.2], vin.B).astype(np.float32)
+        if r.random() < 0.5:
+            temps[int(r.integers(0, vin.B))] = 0.0
+        kw["temps"] = temps
+    if opts["stop"]:
+        eos = r.integers(0, vin.V, vin.B).astype(np.int32)
+        for b in range(vin.B):
+            lo, hi = int(vin.cu_draft[b]), int(vin.cu_draft[b + 1])
+            if hi > lo and r.random() < 0.5:
+                eos[b] = vin.draft_tokens[lo]
+        kw.update(eos=eos, max_emit=r.integers(0, 5, vin.B).astype(np.int32))
+    log(f"[random-early] seed {seed}: {opts} K={vin.K}")
+    _both(vin, kv, **kw)
