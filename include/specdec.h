@@ -210,6 +210,30 @@ int specdec_verify(const void* target_logits, const void* draft_logits, int32_t 
                    int32_t* err_word, const specdec_debug* dbg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* specdec_verify_early_exit: specdec_verify reading no logit row past a request's first
+ * rejection ("Speculative decoding: accelerate LLM generation without changing its
+ * answers" §2-3: nothing after the first rejected proposal decides anything). The row
+ * statistics run as max_k + 1 launches, one per position, each reading the rows of the
+ * requests whose earlier proposals were all accepted; the decision and the draw follow.
+ * Arguments, layouts, ownership and workspace (specdec_verify_workspace_size with the same
+ * arguments): as specdec_verify, and the same results bit for bit for every request whose
+ * read rows are finite. A non-finite row past the first rejection is not reported; debug
+ * p_y / q_y past the first rejection and row_max / row_sum / row_thr of rows not read are
+ * NaN (row_nkept -1); ev_stats_begin / ev_stats_end bracket all the statistics launches.
+ * Temperature only, scalar or per request. Host: every specdec_verify check, and also
+ * EINVAL, before anything is enqueued, for top-k (0 < top_k < V), top-p (0 < top_p < 1),
+ * per_request top_k or top_p arrays, or the acceptance analytics in dbg.
+ */
+int specdec_verify_early_exit(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              const int32_t* draft_tokens, const int32_t* cu_draft,
+                              const float* u_accept, const float* u_sample,
+                              int32_t B, int32_t K, int32_t max_k, int32_t V,
+                              float temperature, int32_t top_k, float top_p,
+                              const specdec_params* per_request,
+                              int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                              int32_t* err_word, const specdec_debug* dbg,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* =====================================================================================
  * Paged KV cache
  * ===================================================================================== */

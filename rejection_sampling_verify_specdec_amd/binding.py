@@ -47,6 +47,7 @@ MAX_V = 2097152
 
 EXPORTED = [
     "specdec_status_string", "specdec_verify_workspace_size", "specdec_verify",
+    "specdec_verify_early_exit",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
     "specdec_cycle_workspace_size", "specdec_cycle", "specdec_cycle_early_exit",
     "specdec_tree_verify_workspace_size",
@@ -146,10 +147,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     pp = ctypes.POINTER(SpecdecParams)
     lib.specdec_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32, pp]
     lib.specdec_verify_workspace_size.restype = sz
-    lib.specdec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32,
-                                   f32, i32, f32, pp, vp, vp, vp, vp,
-                                   ctypes.POINTER(SpecdecDebug), vp, sz, vp]
-    lib.specdec_verify.restype = ctypes.c_int
+    for fn in (lib.specdec_verify, lib.specdec_verify_early_exit):
+        fn.argtypes = [vp, vp, i32, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, f32, pp, vp,
+                       vp, vp, vp, ctypes.POINTER(SpecdecDebug), vp, sz, vp]
+        fn.restype = ctypes.c_int
     lib.kv_paged_append_workspace_size.argtypes = [i32, i32]
     lib.kv_paged_append_workspace_size.restype = sz
     lib.kv_paged_append.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32,
@@ -233,10 +234,11 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                    temperatures: Optional[torch.Tensor] = None,
                    top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
                    top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
-                   max_emit: Optional[torch.Tensor] = None) -> None:
+                   max_emit: Optional[torch.Tensor] = None, early_exit: bool = False) -> None:
     """Enqueue one verification step on torch's current stream (shapes as in the header).
     temperatures / top_ks / top_ps: optional per-request [B] device tensors replacing the
-    scalars (top_k_max bounds the active top_ks)."""
+    scalars (top_k_max bounds the active top_ks). ``early_exit``
+    (specdec_verify_early_exit): no row is read past a request's first rejection."""
     lib = load_library()
     dev = target_logits.device
     if dev.type != "cuda":
@@ -259,14 +261,15 @@ def specdec_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     _check(err_word, "err_word", torch.int32, 1, dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
     prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
-    st = lib.specdec_verify(
+    name = "specdec_verify_early_exit" if early_exit else "specdec_verify"
+    st = getattr(lib, name)(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(cu_draft),
         _ptr(u_accept), _ptr(u_sample), B, K, max_k, V, float(temperature), int(top_k),
         float(top_p), _pref(prm), _ptr(out_tokens), _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
         ctypes.byref(debug) if debug is not None else None,
         _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
-        raise SpecdecError("specdec_verify", st)
+        raise SpecdecError(name, st)
 
 
 class PagedKVCache:

@@ -102,16 +102,33 @@ __global__ __launch_bounds__(kPickNT) void k_pick(SampleArgs a) {
     pick_body<BF16, VEC, kPickNT>(a, blockIdx.x);
 }
 
+// Early exit: the statistics of position p's rows of the requests still live at p
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_pass(SampleArgs a, RowPartial* __restrict__ part, int p) {
+    pass_body<BF16, VEC>(a, part, p, blockIdx.x);
+}
+
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
                        float top_p, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
-                       const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st) {
+                       const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st,
+                       bool early, int max_k) {
     const int rows = 2 * K + B;
     RowPartial* part = reinterpret_cast<RowPartial*>(ws + p.part);
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (p.pr_plain) {
+    if (early) {
+        // one launch per position; the events bracket them all
+        if (p.pr_plain)
+            hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
+                               pa, rows);
+        if (e0) (void)hipEventRecord(e0, st);
+        for (int q = 0; q <= max_k; ++q)
+            hipLaunchKernelGGL((k_pass<BF16, VEC>), dim3((unsigned)B * 2u * (unsigned)p.nchunks),
+                               dim3(kNT), 0, st, sa, part, q);
+        if (e1) (void)hipEventRecord(e1, st);
+    } else if (p.pr_plain) {
         hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,
                            rows);
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
@@ -177,14 +194,21 @@ extern "C" size_t specdec_verify_workspace_size(int32_t B, int32_t K, int32_t V,
     return sd::plan_ws(B, K, V, dtype, top_k, top_p, per_request).total;
 }
 
-extern "C" int specdec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
-                              const int32_t* draft_tokens, const int32_t* cu_draft,
-                              const float* u_accept, const float* u_sample, int32_t B, int32_t K,
-                              int32_t max_k, int32_t V, float temperature, int32_t top_k,
-                              float top_p, const specdec_params* per_request, int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
-                              int32_t* err_word, const specdec_debug* dbg, void* workspace,
-                              size_t workspace_bytes, hipStream_t stream) {
+static int verify_entry(bool early, const void* target_logits, const void* draft_logits,
+                        int32_t dtype, const int32_t* draft_tokens, const int32_t* cu_draft,
+                        const float* u_accept, const float* u_sample, int32_t B, int32_t K,
+                        int32_t max_k, int32_t V, float temperature, int32_t top_k, float top_p,
+                        const specdec_params* per_request, int32_t* out_tokens,
+                        int32_t* num_accepted, int32_t* num_emitted, int32_t* err_word,
+                        const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
     using namespace sd;
+    // early exit: temperature only (scalar or per request), no analytics (they need every
+    // row)
+    if (early && (topk_active(top_k, V) || topp_active(top_p) ||
+                  (per_request && (per_request->top_k || per_request->top_p)) ||
+                  (dbg && (dbg->accept_prob || dbg->expected_emitted))))
+        return SPECDEC_EINVAL;
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
@@ -199,7 +223,8 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     if (K > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
-        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V)
+        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V ||
+        (early && (size_t)2 * B * p.nchunks > 0x7fffffffu))
         return SPECDEC_EINVAL;
     if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;
@@ -231,8 +256,8 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
     sa.c = c;
     sa.eos = per_request ? per_request->eos_token : nullptr;
     sa.cap = per_request ? per_request->max_emit : nullptr;
-    sa.early = 0;
-    sa.live = nullptr;
+    sa.early = early ? 1 : 0;
+    sa.live = reinterpret_cast<int*>(ws + p.live);
     sa.rpar = p.pr ? reinterpret_cast<const RowParams*>(ws + p.rpar) : nullptr;
     sa.part = reinterpret_cast<const RowPartial*>(ws + p.part);
     sa.row_thr = reinterpret_cast<const float*>(ws + p.thr);
@@ -259,13 +284,44 @@ extern "C" int specdec_verify(const void* target_logits, const void* draft_logit
 
     (void)hipGetLastError();
     if (dtype == SPECDEC_BF16) {
-        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
-        else launch_all<true, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
+        if (vec) launch_all<true, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream, early, max_k);
+        else launch_all<true, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream, early, max_k);
     } else {
-        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
-        else launch_all<false, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream);
+        if (vec) launch_all<false, true>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream, early, max_k);
+        else launch_all<false, false>(tgt, dft, B, K, V, top_p, c, p, ws, sa, pa, dbg, stream, early, max_k);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_EHIP;
+}
+
+extern "C" int specdec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              const int32_t* draft_tokens, const int32_t* cu_draft,
+                              const float* u_accept, const float* u_sample, int32_t B, int32_t K,
+                              int32_t max_k, int32_t V, float temperature, int32_t top_k,
+                              float top_p, const specdec_params* per_request,
+                              int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                              int32_t* err_word, const specdec_debug* dbg, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    return verify_entry(false, target_logits, draft_logits, dtype, draft_tokens, cu_draft,
+                        u_accept, u_sample, B, K, max_k, V, temperature, top_k, top_p,
+                        per_request, out_tokens, num_accepted, num_emitted, err_word, dbg,
+                        workspace, workspace_bytes, stream);
+}
+
+extern "C" int specdec_verify_early_exit(const void* target_logits, const void* draft_logits,
+                                         int32_t dtype, const int32_t* draft_tokens,
+                                         const int32_t* cu_draft, const float* u_accept,
+                                         const float* u_sample, int32_t B, int32_t K,
+                                         int32_t max_k, int32_t V, float temperature,
+                                         int32_t top_k, float top_p,
+                                         const specdec_params* per_request, int32_t* out_tokens,
+                                         int32_t* num_accepted, int32_t* num_emitted,
+                                         int32_t* err_word, const specdec_debug* dbg,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+    return verify_entry(true, target_logits, draft_logits, dtype, draft_tokens, cu_draft,
+                        u_accept, u_sample, B, K, max_k, V, temperature, top_k, top_p,
+                        per_request, out_tokens, num_accepted, num_emitted, err_word, dbg,
+                        workspace, workspace_bytes, stream);
 }
 
 extern "C" const char* specdec_status_string(int status) {

@@ -125,14 +125,15 @@ class VerifyOnDevice:
             self.accept_prob.data_ptr() if analytics else None,
             self.expected.data_ptr() if analytics else None)
 
-    def run(self, debug: bool = True) -> None:
+    def run(self, debug: bool = True, early_exit: bool = False) -> None:
         binding.specdec_verify(
             self.tgt, self.dft, self.tokens, self.cu, self.u_acc, self.u_smp,
             max_k=self.max_k, temperature=self.T, top_k=self.top_k,
             out_tokens=self.out_tokens, num_accepted=self.num_acc, num_emitted=self.num_emit,
             err_word=self.err, workspace=self.ws, debug=self.dbg if debug else None,
             top_p=self.top_p, temperatures=self.temps, top_ks=self.top_ks, top_ps=self.top_ps,
-            top_k_max=self.top_k_max, eos_tokens=self.eos, max_emit=self.max_emit)
+            top_k_max=self.top_k_max, eos_tokens=self.eos, max_emit=self.max_emit,
+            early_exit=early_exit)
 
     def result(self) -> GpuVerify:
         torch.cuda.synchronize()

@@ -185,3 +185,22 @@ def test_early_exit_host_validation_without_gpu(lib):
     assert call(ee, top_p=float("nan")) == binding.SPECDEC_EINVAL
     assert ee(ctypes.byref(c), 16, 16, 16, 16, 1, 16, 16, 16, 16, 0, 8, 2, 1000, 1.0, 0, 1.0,
               None, 16, 16, 16, 16, None, 16, 1 << 30, None) == binding.SPECDEC_EINVAL
+
+
+def test_verify_early_exit_host_validation_without_gpu(lib):
+    # as the cycle's: temperature only, no analytics; allowed arguments reach the workspace
+    # check
+    def call(fn, top_k=0, top_p=1.0, pr=None, dbg=None):
+        return fn(16, 16, 1, 16, 16, 16, 16, 4, 8, 2, 1000, 1.0, top_k, top_p,
+                  ctypes.byref(pr) if pr is not None else None, 16, 16, 16, 16,
+                  ctypes.byref(dbg) if dbg is not None else None, 16, 8, None)
+
+    ee, full = lib.specdec_verify_early_exit, lib.specdec_verify
+    analytics = binding.SpecdecDebug()
+    analytics.expected_emitted = 16
+    for kw in (dict(top_k=10), dict(top_p=0.9), dict(pr=binding.SpecdecParams(None, None, 16, 0)),
+               dict(pr=binding.SpecdecParams(None, 16, None, 4)), dict(dbg=analytics)):
+        assert call(ee, **kw) == binding.SPECDEC_EINVAL, kw
+        assert call(full, **kw) == binding.SPECDEC_EWORKSPACE, kw
+    for kw in (dict(), dict(top_k=1000), dict(pr=binding.SpecdecParams(16, None, None, 0))):
+        assert call(ee, **kw) == binding.SPECDEC_EWORKSPACE, kw

@@ -77,9 +77,10 @@ def _compare(vin, full, early, u, y):
                  "picked_prob", "req_flags"):
         assert np.array_equal(np.asarray(getattr(f, name)), np.asarray(getattr(e, name)),
                               equal_nan=True), name
-    for name in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
-        assert np.array_equal(np.asarray(fm[name]), np.asarray(em[name])), name
-    assert np.array_equal(fp, ep), "pool bits"
+    if fm is not None:
+        for name in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
+            assert np.array_equal(np.asarray(fm[name]), np.asarray(em[name])), name
+        assert np.array_equal(fp, ep), "pool bits"
     vis = _visited(vin, f, u, y)
     cu, rows_t = vin.cu_draft, vin.K + vin.B
     read = 0
@@ -250,3 +251,30 @@ def test_early_exit_full_batch_and_vocabulary():
     kv = _small_kv("c2", vin, 155)
     log(f"[early-exit] c2 full size: B={vin.B} V={vin.V}")
     _both(vin, kv)
+
+
+@pytest.mark.parametrize("wl,dtype,V,k_range,per_request", [
+    ("c2", "bf16", 20000, None, False), ("c2", "bf16", 5003, (0, 6), True),
+    ("c1", "f32", 32000, (0, 8), False), ("c3", "bf16", 6000, None, True)])
+def test_verify_early_exit_equals_specdec_verify(wl, dtype, V, k_range, per_request):
+    # the verify call alone (no cache): specdec_verify_early_exit against specdec_verify
+    over = dict(dtype=dtype)
+    if k_range is not None:
+        over.update(k_range=k_range, k=k_range[1])
+    vin = synth.make_verify(wl, seed=159, B=24, V=V, **over)
+    kw = {}
+    if per_request:
+        temps = np.random.default_rng(159).choice([0.5, 1.0, 1.5], vin.B).astype(np.float32)
+        temps[2] = -1.0
+        kw["temps"] = temps
+    full = VerifyOnDevice(vin, **kw)
+    full.run()
+    early = VerifyOnDevice(vin, **kw)
+    early.ws.fill_(0x5A)
+    early.run(early_exit=True)
+    f, e = full.result(), early.result()
+    read, rows = _compare(vin, (f, None, None), (e, None, None), full.u_acc.cpu().numpy(),
+                          full.tokens.cpu().numpy())
+    log(f"[verify-early-exit] {wl} {dtype} V={V}: rows read {read} of {rows}")
+    if per_request:
+        assert f.req_flags[2] & binding.ERR_PARAM
