@@ -173,6 +173,16 @@ def test_early_exit_without_proposals():
     assert (f.num_emitted == 1).all()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_early_exit_at_the_vocabulary_limit(dtype):
+    # V = 2,097,152: 128 (bf16) or 256 (fp32) statistics chunks per row, so the liveness
+    # test combines 16 or 32 batches of partials
+    vin = synth.make_verify("c1", seed=160, B=3, V=binding.MAX_V, k=3, dtype=dtype)
+    kv = _small_kv("c1", vin, 160)
+    log(f"[early-exit] V = {vin.V} {dtype}")
+    _both(vin, kv)
+
+
 def test_early_exit_top_k_switched_off():
     # top_k = V keeps every token: the plain path, so early exit takes it
     vin = synth.make_verify("c2", seed=151, B=10, V=3000)
