@@ -7,7 +7,8 @@
         [--json profiles/KERNEL_WORKLOAD_traffic.json --workload c2 --cmd "..."]
 
 ``trace`` prints count / average / min / max duration per kernel; ``sequence`` the last
-dispatches matching a name, in launch order, with durations and gaps. ``traffic`` turns the
+dispatches matching a name, in launch order, with durations and gaps; ``counters`` the
+average per dispatch of every counter of a --pmc run for the named kernels. ``traffic`` turns the
 FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch) of a kernel into HBM bytes per
 launch, scaled by what the same counters read for a plain copy kernel of known size (the
 largest dispatch of the calibration kernel: the copy of N bytes), and optionally writes
@@ -82,6 +83,32 @@ def _pmc(db, counter):
     raise RuntimeError("no counters_collection view in " + db)
 
 
+def counters(db, kernels, cmd=None):
+    """Average per dispatch of every counter in a --pmc database, for each kernel whose
+    name contains one of `kernels`."""
+    con = sqlite3.connect(db)
+    cols = [c[1] for c in con.execute("pragma table_info(counters_collection)")]
+    name_col = "kernel_name" if "kernel_name" in cols else "name"
+    val_col = "value" if "value" in cols else "counter_value"
+    cnt_col = "counter_name" if "counter_name" in cols else "counter"
+    rows = con.execute(f"select {name_col}, dispatch_id, {cnt_col}, sum({val_col}) from "
+                       f"counters_collection group by dispatch_id, {cnt_col}").fetchall()
+    out = [f"command: {cmd}"] if cmd else []
+    for key in kernels:
+        per = {}
+        for name, disp, cnt, val in rows:
+            if key in name:
+                per.setdefault(cnt, {})[disp] = val
+        if not per:
+            continue
+        n = max(len(v) for v in per.values())
+        out.append(f"{key}: {n} dispatches, average per dispatch")
+        for cnt in sorted(per):
+            v = per[cnt]
+            out.append(f"  {cnt:24s} {sum(v.values()) / len(v):16.1f}")
+    return "\n".join(out)
+
+
 def traffic(fetch_db, write_db, kernel, calib_kernel, calib_bytes, alg_bytes=None):
     f = _pmc(fetch_db, "FETCH_SIZE")
     w = _pmc(write_db, "WRITE_SIZE")
@@ -119,6 +146,10 @@ def main(argv=None):
     q.add_argument("--match", default="sd::")
     q.add_argument("--count", type=int, default=20)
     q.add_argument("--cmd")
+    c = sub.add_parser("counters")
+    c.add_argument("db")
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--cmd")
     p = sub.add_parser("traffic")
     p.add_argument("fetch_db")
     p.add_argument("write_db")
@@ -134,6 +165,8 @@ def main(argv=None):
         print(trace(a.db, a.cmd))
     elif a.what == "sequence":
         print(sequence(a.db, a.match, a.count, a.cmd))
+    elif a.what == "counters":
+        print(counters(a.db, a.kernel, a.cmd))
     else:
         text, info = traffic(a.fetch_db, a.write_db, a.kernel, a.calib_kernel, a.calib_bytes,
                              a.alg_bytes)

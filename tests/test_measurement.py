@@ -89,3 +89,17 @@ def test_sequence_lists_the_last_matching_dispatches_in_order(tmp_path):
     assert lines[-1].split()[-1] == "89.50"                   # span of the two
     lines = profsum.sequence(db, "k_cycle_", 3).splitlines()
     assert lines[2].split()[-1] == "4.50"                     # gap past the fill
+
+
+def test_counters_average_per_dispatch(tmp_path):
+    db = str(tmp_path / "c.db")
+    _counter_db(db, [("k_cycle_topk_merge<true>", 1, "SQ_WAVES", 10.0),
+                     ("k_cycle_topk_merge<true>", 1, "SQ_WAVES", 6.0),      # summed per dispatch
+                     ("k_cycle_topk_merge<true>", 2, "SQ_WAVES", 20.0),
+                     ("k_cycle_topk_merge<true>", 1, "SQ_BUSY_CYCLES", 100.0),
+                     ("k_cycle_topk_merge<true>", 2, "SQ_BUSY_CYCLES", 300.0),
+                     ("other", 3, "SQ_WAVES", 999.0)])
+    lines = profsum.counters(db, ["k_cycle_topk_merge"]).splitlines()
+    assert lines[0].startswith("k_cycle_topk_merge: 2 dispatches")
+    vals = {ln.split()[0]: float(ln.split()[1]) for ln in lines[1:]}
+    assert vals == {"SQ_BUSY_CYCLES": 200.0, "SQ_WAVES": 18.0}
