@@ -34,6 +34,7 @@ import numpy as np
 
 from .kv import KV_APPEND_REJECTED, KV_ERR_ROLLBACK, PagedKV
 from .verify import (ERR_K, ERR_NONFINITE, ERR_QZERO, ERR_TOKEN, ERR_UNIFORM, ERR_ZFALLBACK,
+                     RESID_FLOOR,
                      _decode_rows, _icdf, _u_ok, accept, residual_weights, transform)
 
 ERR_TREE = 128          # a parent index outside {-1, .., j-1}
@@ -91,7 +92,7 @@ def tree_verify_probs(P_rows, Q_rows, parent, tokens, u_accept, u_sample,
                     break
                 r = residual_weights(p, q)
                 W = sum(r)
-                if not W > 0:
+                if not W > RESID_FLOOR:
                     # residual mass 0 (not possible in exact arithmetic): the replacement is
                     # drawn from the distribution the child was tested against
                     flags |= ERR_ZFALLBACK

@@ -64,6 +64,13 @@ ERR_K = 2              # ragged offsets inconsistent: k_b < 0, k_b > max_k, cu[0
 ERR_NONFINITE = 4      # NaN or +inf logit in a row, or a row with no finite kept logit
 ERR_QZERO = 8          # flag: q_i(y_i) == 0 at an evaluated position
 ERR_ZFALLBACK = 16     # flag: residual mass 0 after a rejection; drew from p_i instead
+
+# A residual mass at or below this counts as zero. The draw after a rejection is undefined
+# when max(0, p - q) has no mass ("Speculative decoding ...", section 2: never divide by
+# zero); p and q that agree in exact arithmetic (one-token kept sets, say) leave only
+# rounding noise in p - q, far below this, and a genuine residual this small would be drawn
+# with probability below 1e-12.
+RESID_FLOOR = 2.0 ** -40
 ERR_UNIFORM = 32       # a caller uniform outside [0, 1) or NaN
 ERR_PARAM = 64         # the request's temperature / top_p / top_k is invalid
 
@@ -247,7 +254,7 @@ def verify_probs(P_rows, Q_rows, tokens, u_accept, u_sample) -> ProbsResult:
         mode = "resid"
         w = residual_weights(P_rows[a], Q_rows[a])
         x, W, margin = _icdf(w, u_sample)
-        if x is None:
+        if x is None or not W > RESID_FLOOR:
             flags |= ERR_ZFALLBACK
             w = P_rows[a]
             x, W, margin = _icdf(w, u_sample)

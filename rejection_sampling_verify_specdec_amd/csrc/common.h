@@ -9,6 +9,11 @@
 
 namespace sd {
 
+// A residual mass at or below 2^-40 counts as zero: the draw after a rejection then takes
+// p instead (the residual is undefined without mass). Target and draft rows that agree in
+// exact arithmetic leave only rounding noise in p - q, far below this.
+constexpr double kResidFloor = 0x1p-40;
+
 constexpr int kWave = 64;
 
 SD_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -702,7 +702,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 }
                 const double Wn = team_weight_total(a, ring + (size_t)k * a.slot, red);
                 wslot = k++;
-                if (!(Wn > 0.0)) {
+                if (!(Wn > kResidFloor)) {
                     // no residual mass (not possible in exact arithmetic): draw from the
                     // distribution the child was tested against
                     flags |= SPECDEC_ERR_ZFALLBACK;

@@ -1726,7 +1726,7 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
         run += w[e];
     }
     double C = block_excl_scan_d<NT>(run, redd, &W);
-    if (resid && !(W > 0.0)) {
+    if (resid && !(W > kResidFloor)) {
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;
@@ -1827,7 +1827,7 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
         s_W = W;
     }
     __syncthreads();
-    if (resid && !(s_W > 0.0)) {
+    if (resid && !(s_W > kResidFloor)) {
         // residual mass 0 after a rejection: draw the replacement from p_j instead
         resid = false;
         r.flags |= SPECDEC_ERR_ZFALLBACK;

@@ -158,3 +158,11 @@ def test_random_early_exit_cycles_equal_the_full_cycle(seed):
         kw.update(eos=eos, max_emit=r.integers(0, 5, vin.B).astype(np.int32))
     log(f"[random-early] seed {seed}: {opts} K={vin.K}")
     _both(vin, kv, **kw)
+
+
+def test_zero_residual_draw_falls_back_like_the_oracle():
+    # per-request top-p 0.8 at T = 0.4 keeps one and the same token in a request's target
+    # and draft rows and the proposal lies outside both: the residual is zero in exact
+    # arithmetic, so both sides draw from p and flag it (rounding noise stays below the
+    # 2^-40 floor)
+    test_random_batches_match_the_oracle(209)

@@ -429,3 +429,25 @@ def test_batch_errors_and_layout():
     ua2[0] = 1.0
     r2 = oracle.verify_batch(tgt, dft, toks, cu, ua2, us, 1.0, 0, 4, "f32")
     assert r2.err[0] & oracle.ERR_UNIFORM
+
+
+def test_residual_mass_below_the_floor_counts_as_zero():
+    # the proposal (token 2) has P = Q = 0 and is rejected; the residual max(0, p - q) has
+    # mass d. At or below 2^-40 the draw falls back to p (flagged); above it the residual
+    # is drawn (its one positive token)
+    from oracle.verify import ERR_QZERO, ERR_ZFALLBACK, RESID_FLOOR, verify_probs
+    assert RESID_FLOOR == 2.0 ** -40
+    q = [0.5, 0.5, 0.0]
+    for d, fallback in ((0.0, True), (2.0 ** -41, True), (2.0 ** -40, True), (2.0 ** -39, False)):
+        p = [0.5 + d, 0.5 - d, 0.0, ]
+        r = verify_probs([p, p], [q], [2], [0.5], 0.75)
+        assert r.a == 0 and r.flags & ERR_QZERO
+        assert bool(r.flags & ERR_ZFALLBACK) == fallback, d
+        if fallback:
+            assert r.emitted == [1] and r.W == 1.0          # 0.75 of p: token 1
+        else:
+            assert r.emitted == [0] and r.W == d            # the residual's only token
+    # exact arithmetic: identical one-token rows leave no residual at all
+    one = [F(0), F(1), F(0)]
+    r = verify_probs([one, one], [one], [2], [F(1, 2)], F(1, 3))
+    assert r.flags & ERR_ZFALLBACK and r.emitted == [1]
