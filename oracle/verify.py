@@ -67,10 +67,13 @@ ERR_ZFALLBACK = 16     # flag: residual mass 0 after a rejection; drew from p_i 
 
 # A residual mass at or below this counts as zero. The draw after a rejection is undefined
 # when max(0, p - q) has no mass ("Speculative decoding ...", section 2: never divide by
-# zero); p and q that agree in exact arithmetic (one-token kept sets, say) leave only
-# rounding noise in p - q, far below this, and a genuine residual this small would be drawn
-# with probability below 1e-12.
-RESID_FLOOR = 2.0 ** -40
+# zero). p and q that agree in exact arithmetic (kept sets with the same logit
+# differences) leave only rounding noise in p - q, and the GPU path's fp32 exponentials
+# carry up to ~2^-22 relative error per token, so a residual mass below 2^-20 cannot be
+# told from zero there; both sides take the decision at that resolution. A proposal drawn
+# from q is rejected with probability equal to the residual mass, so the fallback replaces
+# a residual draw only in events of probability at most 2^-20.
+RESID_FLOOR = 2.0 ** -20
 ERR_UNIFORM = 32       # a caller uniform outside [0, 1) or NaN
 ERR_PARAM = 64         # the request's temperature / top_p / top_k is invalid
 
@@ -226,6 +229,7 @@ class ProbsResult:
     picked: object              # w(x*) / W
     sample_margin: object
     flags: int                  # ERR_QZERO / ERR_ZFALLBACK
+    W_resid: object = None      # residual mass before any fallback (None for the bonus)
 
 
 def verify_probs(P_rows, Q_rows, tokens, u_accept, u_sample) -> ProbsResult:
@@ -254,17 +258,19 @@ def verify_probs(P_rows, Q_rows, tokens, u_accept, u_sample) -> ProbsResult:
         mode = "resid"
         w = residual_weights(P_rows[a], Q_rows[a])
         x, W, margin = _icdf(w, u_sample)
+        W_resid = W
         if x is None or not W > RESID_FLOOR:
             flags |= ERR_ZFALLBACK
             w = P_rows[a]
             x, W, margin = _icdf(w, u_sample)
     else:
         mode = "bonus"
+        W_resid = None
         w = P_rows[k]
         x, W, margin = _icdf(w, u_sample)
     picked = w[x] / W
     emitted = [int(t) for t in tokens[:a]] + [int(x)]
-    return ProbsResult(a, emitted, P, Q, margins, mode, W, picked, margin, flags)
+    return ProbsResult(a, emitted, P, Q, margins, mode, W, picked, margin, flags, W_resid)
 
 
 # --------------------------------------------------------------------------------------

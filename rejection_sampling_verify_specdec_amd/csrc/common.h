@@ -9,10 +9,11 @@
 
 namespace sd {
 
-// A residual mass at or below 2^-40 counts as zero: the draw after a rejection then takes
+// A residual mass at or below 2^-20 counts as zero: the draw after a rejection then takes
 // p instead (the residual is undefined without mass). Target and draft rows that agree in
-// exact arithmetic leave only rounding noise in p - q, far below this.
-constexpr double kResidFloor = 0x1p-40;
+// exact arithmetic leave only rounding noise in p - q, and the fp32 exponentials carry up
+// to ~2^-22 relative error per token, so a smaller mass cannot be told from zero.
+constexpr double kResidFloor = 0x1p-20;
 
 constexpr int kWave = 64;
 

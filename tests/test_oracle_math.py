@@ -433,12 +433,12 @@ def test_batch_errors_and_layout():
 
 def test_residual_mass_below_the_floor_counts_as_zero():
     # the proposal (token 2) has P = Q = 0 and is rejected; the residual max(0, p - q) has
-    # mass d. At or below 2^-40 the draw falls back to p (flagged); above it the residual
+    # mass d. At or below 2^-20 the draw falls back to p (flagged); above it the residual
     # is drawn (its one positive token)
     from oracle.verify import ERR_QZERO, ERR_ZFALLBACK, RESID_FLOOR, verify_probs
-    assert RESID_FLOOR == 2.0 ** -40
+    assert RESID_FLOOR == 2.0 ** -20
     q = [0.5, 0.5, 0.0]
-    for d, fallback in ((0.0, True), (2.0 ** -41, True), (2.0 ** -40, True), (2.0 ** -39, False)):
+    for d, fallback in ((0.0, True), (2.0 ** -41, True), (2.0 ** -20, True), (2.0 ** -19, False)):
         p = [0.5 + d, 0.5 - d, 0.0, ]
         r = verify_probs([p, p], [q], [2], [0.5], 0.75)
         assert r.a == 0 and r.flags & ERR_QZERO
