@@ -25,7 +25,7 @@ Where the pages leave a step open the reading taken is stated at the function.
 """
 
 from .verify import (  # noqa: F401
-    ERR_TOKEN, ERR_K, ERR_NONFINITE, ERR_QZERO, ERR_ZFALLBACK, ERR_UNIFORM, ERR_PARAM, RESID_FLOOR,
+    ERR_TOKEN, ERR_K, ERR_NONFINITE, ERR_QZERO, ERR_ZFALLBACK, ERR_UNIFORM, ERR_PARAM,
     params_ok, bf16_bits_to_f64, Transformed, transform, accept, residual_weights,
     inverse_cdf, inverse_cdf_np, verify_probs, verify_request, verify_batch,
     BatchResult,

@@ -34,7 +34,6 @@ import numpy as np
 
 from .kv import KV_APPEND_REJECTED, KV_ERR_ROLLBACK, PagedKV
 from .verify import (ERR_K, ERR_NONFINITE, ERR_QZERO, ERR_TOKEN, ERR_UNIFORM, ERR_ZFALLBACK,
-                     RESID_FLOOR,
                      _decode_rows, _icdf, _u_ok, accept, residual_weights, transform)
 
 ERR_TREE = 128          # a parent index outside {-1, .., j-1}
@@ -59,6 +58,7 @@ class TreeResult:
     sample_margin: float = math.inf
     W: object = None            # total weight of the final draw
     tried: List[int] = field(default_factory=list)             # nodes tested, in order
+    resid_W: list = field(default_factory=list)  # residual mass after each rejected child
 
 
 def tree_verify_probs(P_rows, Q_rows, parent, tokens, u_accept, u_sample,
@@ -72,6 +72,7 @@ def tree_verify_probs(P_rows, Q_rows, parent, tokens, u_accept, u_sample,
     v, path, flags = 0, [], 0
     margins: List[float] = []
     tried: List[int] = []
+    resid_W: list = []
     while True:
         p = get_p(v)
         if not kids[v]:
@@ -92,9 +93,11 @@ def tree_verify_probs(P_rows, Q_rows, parent, tokens, u_accept, u_sample,
                     break
                 r = residual_weights(p, q)
                 W = sum(r)
-                if not W > RESID_FLOOR:
-                    # residual mass 0 (not possible in exact arithmetic): the replacement is
-                    # drawn from the distribution the child was tested against
+                resid_W.append(W)
+                if not W > 0:
+                    # residual mass 0 (the tested distribution and q agree exactly): the
+                    # replacement is drawn from the distribution the child was tested
+                    # against
                     flags |= ERR_ZFALLBACK
                     w = p
                     break
@@ -106,7 +109,7 @@ def tree_verify_probs(P_rows, Q_rows, parent, tokens, u_accept, u_sample,
                 continue
         x, W, margin = _icdf(w, u_sample)
         emitted = [int(tokens[j]) for j in path] + [int(x)]
-        return TreeResult(path, emitted, flags, margins, margin, W, tried)
+        return TreeResult(path, emitted, flags, margins, margin, W, tried, resid_W)
 
 
 @dataclass

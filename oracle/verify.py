@@ -24,8 +24,14 @@ Readings taken where the pages leave a step open (each is listed in the design n
 * inverse CDF walks token ids in ascending order and returns the smallest x whose running
   sum C(x) exceeds t = u * W, with W the final running sum. If rounding leaves no such x,
   the last x with positive weight is taken.
-* a residual mass of exactly 0 after a rejection cannot happen in exact arithmetic
-  (section 3); if it does, the replacement is drawn from p_i and the request is flagged.
+* a residual mass of 0 after a rejection cannot happen in exact arithmetic when the
+  proposal was drawn from q_i (section 3: the rejection probability equals the residual
+  mass), but it can when the two distributions agree and the proposal lies outside both
+  (a transform dropped it). Then the replacement is drawn from p_i and the request is
+  flagged (section 6: never divide by zero). Zero is decided on the fp64 sum: p and q
+  that agree exactly (equal kept sets, logits equal up to one common shift) are computed
+  by the same fp64 operations on the same values z - m and are bitwise equal, so their
+  residual sums to exactly 0; any other pair leaves a positive fp64 residual.
 * top-k keeps every token whose logit is >= the k-th largest logit of the row, counting
   multiplicity (ties inclusive), and selects on the raw logits, which is the same set for
   any temperature T > 0.
@@ -64,16 +70,6 @@ ERR_K = 2              # ragged offsets inconsistent: k_b < 0, k_b > max_k, cu[0
 ERR_NONFINITE = 4      # NaN or +inf logit in a row, or a row with no finite kept logit
 ERR_QZERO = 8          # flag: q_i(y_i) == 0 at an evaluated position
 ERR_ZFALLBACK = 16     # flag: residual mass 0 after a rejection; drew from p_i instead
-
-# A residual mass at or below this counts as zero. The draw after a rejection is undefined
-# when max(0, p - q) has no mass ("Speculative decoding ...", section 2: never divide by
-# zero). p and q that agree in exact arithmetic (kept sets with the same logit
-# differences) leave only rounding noise in p - q, and the GPU path's fp32 exponentials
-# carry up to ~2^-22 relative error per token, so a residual mass below 2^-20 cannot be
-# told from zero there; both sides take the decision at that resolution. A proposal drawn
-# from q is rejected with probability equal to the residual mass, so the fallback replaces
-# a residual draw only in events of probability at most 2^-20.
-RESID_FLOOR = 2.0 ** -20
 ERR_UNIFORM = 32       # a caller uniform outside [0, 1) or NaN
 ERR_PARAM = 64         # the request's temperature / top_p / top_k is invalid
 
@@ -259,7 +255,8 @@ def verify_probs(P_rows, Q_rows, tokens, u_accept, u_sample) -> ProbsResult:
         w = residual_weights(P_rows[a], Q_rows[a])
         x, W, margin = _icdf(w, u_sample)
         W_resid = W
-        if x is None or not W > RESID_FLOOR:
+        if x is None:
+            # the residual has no mass (W == 0): draw from p_i instead
             flags |= ERR_ZFALLBACK
             w = P_rows[a]
             x, W, margin = _icdf(w, u_sample)

@@ -431,23 +431,109 @@ def test_batch_errors_and_layout():
     assert r2.err[0] & oracle.ERR_UNIFORM
 
 
-def test_residual_mass_below_the_floor_counts_as_zero():
-    # the proposal (token 2) has P = Q = 0 and is rejected; the residual max(0, p - q) has
-    # mass d. At or below 2^-20 the draw falls back to p (flagged); above it the residual
-    # is drawn (its one positive token)
-    from oracle.verify import ERR_QZERO, ERR_ZFALLBACK, RESID_FLOOR, verify_probs
-    assert RESID_FLOOR == 2.0 ** -20
-    q = [0.5, 0.5, 0.0]
-    for d, fallback in ((0.0, True), (2.0 ** -41, True), (2.0 ** -20, True), (2.0 ** -19, False)):
-        p = [0.5 + d, 0.5 - d, 0.0, ]
-        r = verify_probs([p, p], [q], [2], [0.5], 0.75)
-        assert r.a == 0 and r.flags & ERR_QZERO
-        assert bool(r.flags & ERR_ZFALLBACK) == fallback, d
-        if fallback:
-            assert r.emitted == [1] and r.W == 1.0          # 0.75 of p: token 1
+def test_tiny_residual_is_drawn_from():
+    # section 2: at a rejection the replacement comes from normalize(max(0, p - q)) whenever
+    # that residual has any mass. The proposal (token 2) has P = Q = 0 and is rejected; the
+    # residual is d at token 0 and 0 elsewhere, so the replacement is token 0 for every
+    # u_sample, however small d is; only d = 0 exactly falls back to p (flagged)
+    from oracle.verify import ERR_QZERO, ERR_ZFALLBACK
+    q = [F(1, 2), F(1, 2), F(0)]
+    for d in (F(0), F(1, 2 ** 60), F(1, 2 ** 30), F(1, 2 ** 20), F(1, 8)):
+        p = [F(1, 2) + d, F(1, 2) - d, F(0)]
+        for us in (F(0), F(1, 3), F(3, 4), F(2 ** 30 - 1, 2 ** 30)):
+            r = verify_probs([p, p], [q], [2], [F(1, 2)], us)
+            assert r.a == 0 and r.flags & ERR_QZERO
+            assert bool(r.flags & ERR_ZFALLBACK) == (d == 0), d
+            if d == 0:
+                # from p = (1/2, 1/2, 0): token 0 below u = 1/2, token 1 from there on
+                assert r.emitted == [0 if us < F(1, 2) else 1] and r.W == 1
+            else:
+                assert r.emitted == [0] and r.W == d and r.W_resid == d and r.picked == 1
+    # the same in fp64: p = (1/2 + 2^-30, 1/2 - 2^-30, 0) is exact, so is its residual
+    d = 2.0 ** -30
+    r = verify_probs([np.array([0.5 + d, 0.5 - d, 0.0])] * 2, [np.array([0.5, 0.5, 0.0])], [2],
+                     [0.5], 0.75)
+    assert r.emitted == [0] and r.W == d and not r.flags & ERR_ZFALLBACK
+
+
+def _shifted_pair(rng, V, shift):
+    """bf16 bit patterns of a target row on the grid k / 16 (|k| <= 100) and a draft row
+    equal to it plus `shift` (a multiple of 1/16 that keeps every value exact in bf16)."""
+    from rejection_sampling_verify_specdec_amd.synth import f32_to_bf16_bits
+    z = rng.integers(-100, 101, size=V).astype(np.float32) / np.float32(16)
+    t, d = f32_to_bf16_bits(z), f32_to_bf16_bits(z + np.float32(shift))
+    assert np.array_equal(bf16_bits_to_f64(d) - bf16_bits_to_f64(t), np.full(V, shift))
+    return t, d
+
+
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (5, 1.0), (0, 0.6), (40, 0.3)])
+def test_shifted_logits_leave_exactly_zero_residual(top_k, top_p):
+    # section 3 and variation 1 of section 5: a draft distribution equal to the target's
+    # leaves no residual. Softmax is invariant under a common shift of the logits, so a
+    # draft row equal to the target row plus a constant gives q = p after any transform
+    # that selects on logit order (top-k, top-p). The fp64 oracle must see that zero
+    # exactly (it decides the fallback on it): the proposal is the one token outside both
+    # kept sets, rejected with P = Q = 0, and the replacement is drawn from p
+    from oracle.verify import ERR_QZERO, ERR_ZFALLBACK
+    rng = np.random.default_rng(11)
+    V = 200
+    for shift in (0.5, -3.25, 7.0):
+        t, d = _shifted_pair(rng, V, shift)
+        zt = bf16_bits_to_f64(t)
+        if top_k or top_p < 1:
+            tr = transform(zt, 0.7, top_k, top_p)
+            y = int(np.argmin(np.where(tr.p > 0, np.inf, zt)))   # a dropped token
+            assert tr.p[y] == 0
         else:
-            assert r.emitted == [0] and r.W == d            # the residual's only token
-    # exact arithmetic: identical one-token rows leave no residual at all
-    one = [F(0), F(1), F(0)]
-    r = verify_probs([one, one], [one], [2], [F(1, 2)], F(1, 3))
-    assert r.flags & ERR_ZFALLBACK and r.emitted == [1]
+            t[17] = 0xff80                      # -inf on both sides: P = Q = 0
+            d[17] = 0xff80
+            y = 17
+        for us in (0.1, 0.5, 0.93):
+            r = oracle.verify_batch(np.stack([t, t]), d[None], np.array([y]), np.array([0, 1]),
+                                    np.array([0.25], np.float32), np.array([us], np.float32),
+                                    0.7, top_k, 1, "bf16", top_p=top_p)
+            res = r.requests[0]
+            assert r.num_accepted[0] == 0 and res.err & ERR_QZERO and res.err & ERR_ZFALLBACK
+            assert res.probs.W_resid == 0.0
+            p = res.rows_t[0].p
+            assert np.array_equal(p, res.rows_d[0].p)
+            x, _, _ = inverse_cdf(list(p), float(np.float32(us)))
+            assert res.emitted == [x] and p[x] > 0
+        # a single token off the shift makes the residual positive: it is drawn from
+        t2 = t.copy()
+        kept = np.nonzero(oracle.transform(bf16_bits_to_f64(t), 0.7, top_k, top_p).p > 0)[0]
+        j = int(kept[len(kept) // 2])
+        if len(kept) > 1:
+            zj = bf16_bits_to_f64(t2[j:j + 1])[0] - 1.0 / 16
+            from rejection_sampling_verify_specdec_amd.synth import f32_to_bf16_bits
+            t2[j] = f32_to_bf16_bits(np.array([zj], np.float32))[0]
+            r = oracle.verify_batch(np.stack([t2, t2]), d[None], np.array([y]), np.array([0, 1]),
+                                    np.array([0.25], np.float32), np.array([0.5], np.float32),
+                                    0.7, top_k, 1, "bf16", top_p=top_p)
+            res = r.requests[0]
+            if res.rows_t[0].nkept == res.rows_d[0].nkept:
+                assert res.probs.W_resid > 0 and not res.err & ERR_ZFALLBACK
+
+
+@pytest.mark.parametrize("gap", [1e-6, 1e-4, 0.3, 4.0])
+def test_two_token_residual_matches_closed_form(gap):
+    # two live tokens with logits (0, a) under p and (0, b) under q: p(1) = sigmoid(a), and
+    # the residual mass is |sigmoid(a) - sigmoid(b)| = sinh((a - b)/2) / (2 cosh(a/2)
+    # cosh(b/2)), a form without cancellation. The proposal is a third token at -inf on both
+    # sides (P = Q = 0: rejected), so the draw always comes from the residual. The fp64
+    # oracle resolves the mass to 1e-8 relative even when the rows are 1e-6 apart
+    from oracle.verify import ERR_ZFALLBACK
+    for a in (-1.5, 0.0, 2.0):
+        b = a - gap
+        tgt = np.array([[0.0, a, -np.inf], [0.0, 0.0, 0.0]], np.float32)
+        dft = np.array([[0.0, b, -np.inf]], np.float32)
+        a32, b32 = float(np.float32(a)), float(np.float32(b))
+        exact = abs(math.sinh((a32 - b32) / 2) / (2 * math.cosh(a32 / 2) * math.cosh(b32 / 2)))
+        r = oracle.verify_batch(tgt, dft, np.array([2]), np.array([0, 1]),
+                                np.array([0.5], np.float32), np.array([0.5], np.float32),
+                                1.0, 0, 1, "f32")
+        res = r.requests[0]
+        assert r.num_accepted[0] == 0 and res.probs.mode == "resid"
+        assert not res.err & ERR_ZFALLBACK
+        assert abs(float(res.probs.W_resid) - exact) <= 1e-8 * exact
+        assert res.emitted == [1]                     # a > b: the residual lives on token 1

@@ -225,6 +225,26 @@ def test_branch_switch_takes_the_second_sibling():
     assert r.path == [1] and r.emitted == [1, 1] and r.tried == [0, 1]
 
 
+def test_tiny_residual_continues_the_sibling_chain():
+    # the residual after a rejected child is the next sibling's target distribution however
+    # small its mass; only a residual of exactly 0 stops the walk with a draw from the
+    # distribution the child was tested against (flagged). Root children: node 0 proposes
+    # token 2 (P = Q = 0, rejected), node 1 proposes token 0
+    from oracle.verify import ERR_ZFALLBACK
+    q = [F(1, 2), F(1, 2), F(0)]
+    rows_q = [q, q, q]
+    for d in (F(0), F(1, 2 ** 40), F(1, 4)):
+        p = [F(1, 2) + d, F(1, 2) - d, F(0)]
+        r = tree_verify_probs([p, p, p], rows_q, [-1, -1], [2, 0], [F(1, 2), F(1, 2)], F(1, 3))
+        if d == 0:
+            assert r.flags & ERR_ZFALLBACK and r.path == [] and r.emitted == [0]
+            assert r.tried == [0]
+        else:
+            # the residual (d, 0, 0) normalizes to (1, 0, 0): node 1's token 0 has P = 1,
+            # Q = 1/2 and is accepted for every u
+            assert not r.flags & ERR_ZFALLBACK and r.path == [1] and r.tried == [0, 1]
+
+
 def test_batch_errors():
     from rejection_sampling_verify_specdec_amd import synth
     vin = synth.make_verify("tiny", seed=3, B=3, V=50, k=3)
