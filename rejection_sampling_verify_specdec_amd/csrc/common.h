@@ -9,10 +9,10 @@
 
 namespace sd {
 
-// A residual mass at or below 2^-20 counts as zero: the draw after a rejection then takes
-// p instead (the residual is undefined without mass). Target and draft rows that agree in
-// exact arithmetic leave only rounding noise in p - q, and the fp32 exponentials carry up
-// to ~2^-22 relative error per token, so a smaller mass cannot be told from zero.
+// The tree walk's clamp on a residual mass (its residual chain is formed from fp32
+// exponentials): at or below 2^-20 the replacement is drawn from the distribution the
+// child was tested against, flagged. Target and draft rows that agree leave only rounding
+// noise in p - q, about 2^-22 of p per token there, so a smaller mass is not resolved.
 constexpr double kResidFloor = 0x1p-20;
 
 constexpr int kWave = 64;

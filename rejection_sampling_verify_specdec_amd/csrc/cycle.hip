@@ -336,6 +336,8 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
     sa.nch = p.nch;
     sa.topk = p.filter;
     sa.c = c;
+    sa.T = temperature;
+    sa.temps = pr_t ? per_request->temperature : nullptr;
     sa.eos = per_request ? per_request->eos_token : nullptr;
     sa.cap = per_request ? per_request->max_emit : nullptr;
     sa.early = early ? 1 : 0;

@@ -17,7 +17,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kNT = 256;        // threads per workgroup of the streaming kernels
 constexpr int kVPT = 8;         // 16-byte vectors per thread per chunk
 
-enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_BONUS = 2 };
+// MODE_PRECISE: a residual draw whose streaming mass came out below kPreciseBelow; the
+// pick launch re-derives it with the precise arithmetic (precise_draw)
+enum : int { MODE_NONE = 0, MODE_RESID = 1, MODE_BONUS = 2, MODE_PRECISE = 3 };
 
 // Partial statistics of one row chunk (or of a whole row for top-k rows).
 struct alignas(16) RowPartial {
@@ -1146,16 +1148,18 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Decision and sampling, fused: one workgroup of 1024 threads per request.
-//   1. combine the row partials in fp64, evaluate p_i(y_i), q_i(y_i) and the accept test
-//      left to right, find the first rejection, publish the accepted tokens;
-//   2. stream the one row pair (or bonus row) still to be sampled in 8192-element chunks
-//      (four chunks in flight per thread) and keep per-chunk weight sums in LDS;
-//   3. W = sum of the chunk sums, t = u * W, locate the chunk holding t and scan it in
-//      ascending token order (each thread owns 8 consecutive tokens) for the smallest x
-//      with C(x) > t.
-// Nothing crosses workgroups, so no device-scope fence is needed; rows after the first
-// rejection are never read.
+// Decision and sampling, in three launches with kernel boundaries as the only
+// synchronization:
+//   1. decision: one workgroup per request combines its rows' partials in fp64, evaluates
+//      p_i(y_i), q_i(y_i) and the accept test left to right, finds the first rejection and
+//      publishes the accepted tokens;
+//   2. chunk sums: one workgroup per (request, 8192-token chunk) of the row pair (or bonus
+//      row) still to be sampled writes the chunk's four sub-chunk sums of the weights;
+//   3. pick: one workgroup per request forms W from the sub-chunk sums, locates the
+//      sub-chunk holding t = u * W and scans it in ascending token order for the smallest x
+//      with C(x) > t. A residual whose mass comes out below kPreciseBelow is re-derived
+//      there first with the precise arithmetic (precise_draw).
+// Rows after the first rejection are never read.
 // ---------------------------------------------------------------------------------------
 constexpr int kDecideNT = 256;             // threads of a decision workgroup (>= 2*64+1 rows)
 constexpr int kPartNT = 256;               // threads of a chunk-sum workgroup
@@ -1167,12 +1171,13 @@ constexpr int kSMaxChunks = 256;           // V <= kSChunk * kSMaxChunks
 static_assert(kSChunk * kSMaxChunks == SPECDEC_MAX_V, "sampling chunks cover the largest V");
 
 struct Decision {
-    int flags, err, a, k, mode, row_t, row_d, pad;
+    int flags, err, a, k, mode, row_t, row_d;
+    float T;                 // the request's temperature
     float mc_t, mc_d, thr_t, thr_d;
     double al_t, al_d;
     float u;
     float c;                 // log2(e) / T of the request
-    int pad3, pad4;
+    float mt, md;            // max kept logit of the target / draft row of the draw
 };
 
 struct SampleArgs {
@@ -1187,6 +1192,8 @@ struct SampleArgs {
     int topk;                // 1 when rows carry a top-k threshold
     int nch;                 // sampling chunks per row
     float c;
+    float T;                 // the scalar temperature (per-request arrays: temps)
+    const float* temps;      // [B] per-request temperatures, or null
     const RowParams* rpar;   // per-request parameters: [rows] each row's, else null
     const RowPartial* part;
     const float* row_thr;
@@ -1454,12 +1461,14 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
             d.err = err;
             d.a = j;
             d.k = k;
-            d.pad = d.pad3 = d.pad4 = 0;
+            d.T = a.temps ? a.temps[b] : a.T;
             d.c = cf;
             d.mode = (err || stop) ? MODE_NONE : (j < k ? MODE_RESID : MODE_BONUS);
             d.row_t = lo + b + j;
             d.row_d = j < k ? lo + j : 0;
             const float mt = s_m[j];
+            d.mt = mt;
+            d.md = j < k ? s_m[k + 1 + j] : 0.f;
             d.mc_t = mt * cf;
             d.al_t = exp2(-(double)fmaf(mt, cf, -d.mc_t)) / s_S[j];
             d.thr_t = s_thr[j];
@@ -1486,10 +1495,12 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
             q.mode = err ? MODE_NONE : MODE_RESID;
             q.row_t = lo + b + lane;
             q.row_d = lo + lane;
-            q.pad = q.pad3 = q.pad4 = 0;
+            q.T = a.temps ? a.temps[b] : a.T;
             q.c = cf;
             q.u = 0.f;
             const float mt = s_m[lane], md = s_m[k + 1 + lane];
+            q.mt = mt;
+            q.md = md;
             q.mc_t = mt * cf;
             q.al_t = exp2(-(double)fmaf(mt, cf, -q.mc_t)) / s_S[lane];
             q.thr_t = s_thr[lane];
@@ -1688,6 +1699,135 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
                               a.rpar);
 }
 
+// ---------------------------------------------------------------------------------------
+// Precise residual draw. The streaming draw forms max(0, p - q) from fp32 exponentials of
+// each row, normalized by each row's exp-sum, so the difference carries an absolute error
+// of about 1e-7 of p: harmless while the residual mass W is large, not once W is small
+// (close distributions) or zero (distributions that agree). A draw whose streaming mass
+// comes out below kPreciseBelow is re-derived by its pick workgroup without that
+// cancellation:
+//   a(x)     = exp((z_t(x) - m_t) / T)                 target weight (fp32 exponential)
+//   delta(x) = ((z_d(x) - m_d) - (z_t(x) - m_t)) / T   exact differences, one fp64 rounding
+//   q(x) / p(x) = exp(delta(x) - lambda),   lambda = log(S_d / S_t)
+//   S_d / S_t - 1 = (sum_both a expm1(delta) + sum_draft-only e_d - sum_target-only a) / A
+//   w(x) = a(x) max(0, -expm1(delta(x) - lambda))      kept on both sides
+//        = a(x)                                        kept by the target only
+// with A the sum of a over the target's kept tokens and every sum in fp64. S_d / S_t is a
+// weighted mean of exp(delta) under the same a values that weight the tokens, so an error
+// in a(x) moves lambda only through the spread of delta, and rows that agree (equal kept
+// sets, delta = 0 on every kept token) give lambda = 0 and w = 0 everywhere: W = 0 exactly,
+// as the definition has it. Each weight then carries the relative error of a(x), about
+// 1e-7, whatever the size of W.
+// ---------------------------------------------------------------------------------------
+constexpr double kPreciseBelow = 0.25;
+
+struct PreciseRow {
+    double mt, md;      // max kept logit of the target / draft row
+    double invT;        // 1 / T
+    double l2T;         // log2(e) / T, for the fp32 exponentials of the weights
+    double lam;         // log(S_d / S_t)
+    float thr_t, thr_d;
+};
+
+SD_DEV double precise_a(double dz, const PreciseRow& P) {
+    return (double)__builtin_amdgcn_exp2f((float)(dz * P.l2T));
+}
+
+// Pass 1 terms of one token: A += a(x) for a kept target token, N += its share of
+// S_d - S_t (in units of the target's max-normalized exp-sum).
+SD_DEV void precise_terms(float zt, float zd, const PreciseRow& P, double& A, double& N) {
+    const bool kt = zt >= P.thr_t && zt > -INFINITY;
+    const bool kd = zd >= P.thr_d && zd > -INFINITY;
+    const double dt = (double)zt - P.mt;
+    if (kt) {
+        const double a = precise_a(dt, P);
+        A += a;
+        N += kd ? a * expm1((((double)zd - P.md) - dt) * P.invT) : -a;
+    } else if (kd) {
+        N += precise_a((double)zd - P.md, P);
+    }
+}
+
+// The precise draw's weight of one token: the residual (RESID) or p, both unnormalized
+// (in units of A).
+SD_DEV double precise_weight(float zt, float zd, const PreciseRow& P, bool resid) {
+    if (!(zt >= P.thr_t && zt > -INFINITY)) return 0.0;
+    const double dt = (double)zt - P.mt;
+    const double a = precise_a(dt, P);
+    if (!resid || !(zd >= P.thr_d && zd > -INFINITY)) return a;
+    const double ell = (((double)zd - P.md) - dt) * P.invT - P.lam;
+    return a * fmax(0.0, -expm1(ell));
+}
+
+// One chunk of the row pair, kSSub groups of 8 tokens per thread with every load in flight
+// (group g of every thread lies in sub-chunk g, as in chunk_weight_sums_t).
+template <bool BF16, bool VEC, int NT>
+SD_DEV void precise_load(const uint8_t* trow, const uint8_t* drow, int V, int chunk, bool pair,
+                         float (&zt)[kSSub][8], float (&zd)[kSSub][8]) {
+    static_assert(NT * 8 * kSSub == kSChunk, "group g of every thread is sub-chunk g");
+#pragma unroll
+    for (int g = 0; g < kSSub; ++g) {
+        const int i0 = chunk * kSChunk + (g * NT + threadIdx.x) * 8;
+        load8<BF16, VEC>(trow, V, i0, zt[g]);
+        if (pair) {
+            load8<BF16, VEC>(drow, V, i0, zd[g]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zd[g][e] = -INFINITY;
+        }
+    }
+}
+
+// Pass 1 over the row pair: A and lambda (every thread gets both). `red` holds NT / 64
+// doubles.
+template <bool BF16, bool VEC, int NT>
+SD_DEV double precise_lambda(const uint8_t* trow, const uint8_t* drow, int V, int nch,
+                             PreciseRow& P, double* red) {
+    double A = 0.0, N = 0.0;
+    for (int ch = 0; ch < nch; ++ch) {
+        float zt[kSSub][8], zd[kSSub][8];
+        precise_load<BF16, VEC, NT>(trow, drow, V, ch, true, zt, zd);
+#pragma unroll
+        for (int g = 0; g < kSSub; ++g) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) precise_terms(zt[g][e], zd[g][e], P, A, N);
+        }
+    }
+    A = block_sum<NT>(A, red);
+    N = block_sum<NT>(N, red);
+    P.lam = log1p(N / A);
+    return A;
+}
+
+// Pass 2: the sub-chunk sums of the precise weights into out[0 .. nch * kSSub), fixed
+// reduction order (lanes, then waves in index order). `red` holds kSSub * NT / 64 doubles.
+template <bool BF16, bool VEC, int NT>
+SD_DEV void precise_sums(const uint8_t* trow, const uint8_t* drow, int V, int nch,
+                         const PreciseRow& P, bool resid, double* red, double* out) {
+    constexpr int NW = NT / kWave;
+    const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+    for (int ch = 0; ch < nch; ++ch) {
+        float zt[kSSub][8], zd[kSSub][8];
+        precise_load<BF16, VEC, NT>(trow, drow, V, ch, resid, zt, zd);
+#pragma unroll
+        for (int g = 0; g < kSSub; ++g) {
+            double acc = 0.0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += precise_weight(zt[g][e], zd[g][e], P, resid);
+            acc = wave_sum(acc);
+            if (l == 0) red[g * NW + w] = acc;
+        }
+        __syncthreads();
+        if (tid < kSSub) {
+            double sum = 0.0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) sum += red[tid * NW + i];
+            out[ch * kSSub + tid] = sum;
+        }
+        __syncthreads();
+    }
+}
+
 // Draw from the target row's kept-token list (bf16 top-k rows). Tokens outside the list
 // have p = 0 and so weight 0 in both the residual and the bonus draw, so scanning the list
 // in ascending token order finds the same smallest x with C(x) > u * W as scanning the
@@ -1704,7 +1844,7 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
     const uint32_t* tok = a.ktok + (size_t)r.row_t * kKeptCap;
     const uint16_t* key = a.kkey + (size_t)r.row_t * kKeptCap;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * (BF16 ? 2 : 4);
-    bool resid = r.mode == MODE_RESID;
+    const bool resid = r.mode == MODE_RESID;
     int x[EPT];
     float zt[EPT], zd[EPT];
 #pragma unroll
@@ -1726,18 +1866,12 @@ SD_DEV void listed_pick_body(const SampleArgs& a, int b, Decision r, int n) {
         run += w[e];
     }
     double C = block_excl_scan_d<NT>(run, redd, &W);
-    if (resid && !(W > kResidFloor)) {
-        // residual mass 0 after a rejection: draw the replacement from p_j instead
-        resid = false;
-        r.flags |= SPECDEC_ERR_ZFALLBACK;
-        run = 0.0;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            w[e] = x[e] >= 0 ? weight(zt[e], zd[e], r, r.c, false) : 0.0;
-            run += w[e];
-        }
-        C = block_excl_scan_d<NT>(run, redd, &W);
-        if (tid == 0) atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
+    if (resid && !(W >= kPreciseBelow)) {
+        // a small (or zero) residual: the pick launch re-derives it with the precise
+        // arithmetic over the whole row pair (the draft's kept tokens outside the list
+        // enter its normalization)
+        if (tid == 0) a.rec[b].mode = MODE_PRECISE;
+        return;
     }
     const double t = (double)r.u * W;
     int mine = 0x7fffffff, lastpos = -1;
@@ -1798,7 +1932,9 @@ SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
 // Sampling, part 2: workgroup b turns the sub-chunk sums into W, finds the sub-chunk holding
 // t = u * W and scans it in ascending token order (each thread owns 8 consecutive tokens,
 // an exclusive scan over threads gives each its running sum) for the smallest x with
-// C(x) > t.
+// C(x) > t. A residual of streaming mass below kPreciseBelow (or one the kept-token list
+// handed over as MODE_PRECISE) is re-derived first with the precise arithmetic; a precise
+// residual of mass 0 falls back to p (flagged).
 template <bool BF16, bool VEC, int NT>
 SD_DEV void pick_body(const SampleArgs& a, int b) {
     using Lt = Layout<BF16, VEC>;
@@ -1813,34 +1949,57 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
     if constexpr (BF16) {
-        if (a.kn && a.kn[r.row_t] >= 0) return;   // drawn from the kept-token list
+        // drawn from the kept-token list, unless the list handed the draw over
+        if (r.mode != MODE_PRECISE && a.kn && a.kn[r.row_t] >= 0) return;
     }
-    bool resid = r.mode == MODE_RESID;
+    bool resid = r.mode != MODE_BONUS;
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
     const int nch = a.nch, nsub = nch * kSSub;
-    for (int q = tid; q < nsub; q += NT) s_cs[q] = a.wsum[(size_t)b * nsub + q];
-    __syncthreads();
-    if (tid == 0) {
-        double W = 0.0;
-        for (int q = 0; q < nsub; ++q) W += s_cs[q];
-        s_W = W;
-    }
-    __syncthreads();
-    if (resid && !(s_W > kResidFloor)) {
-        // residual mass 0 after a rejection: draw the replacement from p_j instead
-        resid = false;
-        r.flags |= SPECDEC_ERR_ZFALLBACK;
-        for (int q = 0; q < nch; ++q)
-            chunk_weight_sums<BF16, VEC, NT>(trow, drow, a.V, q, r, r.c, false, a.topk != 0, red,
-                                             s_cs + q * kSSub);
+    bool precise = r.mode == MODE_PRECISE;
+    if (!precise) {
+        for (int q = tid; q < nsub; q += NT) s_cs[q] = a.wsum[(size_t)b * nsub + q];
+        __syncthreads();
         if (tid == 0) {
             double W = 0.0;
             for (int q = 0; q < nsub; ++q) W += s_cs[q];
             s_W = W;
-            atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
         }
         __syncthreads();
+        precise = resid && !(s_W >= kPreciseBelow);
+    }
+    PreciseRow P;
+    double wscale = 1.0;      // reported W = the sum of the weights times wscale
+    if (precise) {
+        P.mt = (double)r.mt;
+        P.md = (double)r.md;
+        P.invT = 1.0 / (double)r.T;
+        P.l2T = 1.4426950408889634074 * P.invT;
+        P.thr_t = r.thr_t;
+        P.thr_d = r.thr_d;
+        P.lam = 0.0;
+        const double A = precise_lambda<BF16, VEC, NT>(trow, drow, a.V, nch, P, red);
+        wscale = 1.0 / A;
+        precise_sums<BF16, VEC, NT>(trow, drow, a.V, nch, P, true, red, s_cs);
+        if (tid == 0) {
+            double W = 0.0;
+            for (int q = 0; q < nsub; ++q) W += s_cs[q];
+            s_W = W;
+        }
+        __syncthreads();
+        if (!(s_W > 0.0)) {
+            // the rows agree: no residual mass, draw the replacement from p_j instead
+            resid = false;
+            r.flags |= SPECDEC_ERR_ZFALLBACK;
+            precise_sums<BF16, VEC, NT>(trow, drow, a.V, nch, P, false, red, s_cs);
+            if (tid == 0) {
+                double W = 0.0;
+                for (int q = 0; q < nsub; ++q) W += s_cs[q];
+                s_W = W;
+                atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
+            }
+            __syncthreads();
+        }
     }
     const double W = s_W;
     const double t = (double)r.u * W;
@@ -1869,7 +2028,8 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     double run = 0.0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        w[e] = weight(t8[e], resid ? d8[e] : -INFINITY, r, r.c, resid);
+        const float zd = resid ? d8[e] : -INFINITY;
+        w[e] = precise ? precise_weight(t8[e], zd, P, resid) : weight(t8[e], zd, r, r.c, resid);
         run += w[e];
     }
     double tot;
@@ -1898,7 +2058,7 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     __syncthreads();
     if (tid == 0) {
         a.out_tokens[a.cu[b] + b + r.a] = found;
-        if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W;
+        if (a.dbg.resid_mass) a.dbg.resid_mass[b] = W * wscale;
         if (a.dbg.picked_prob) a.dbg.picked_prob[b] = s_wpick / W;
         if (a.dbg.req_flags) a.dbg.req_flags[b] = r.flags;
     }

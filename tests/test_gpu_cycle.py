@@ -42,12 +42,12 @@ def test_cycle(wl, mode):
     g = g_v.result()
     rep = compare_verify(vin, g, o)
     log(f"[cycle] {wl}: {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     # the oracle cache follows the GPU's accepted counts (identical unless flagged)
     o_kv = oracle_kv(kv)
     o_kv.append(kv.k_new, kv.v_new, kv.cu_new)
     o_kv.rollback(g.num_accepted, vin.cu_draft)
-    errs = compare_kv_meta(o_kv, g_kv.meta(), wl) + compare_kv_data(o_kv, g_kv.pool)
+    errs = compare_kv_meta(o_kv, g_kv.meta(), wl) + compare_kv_data(o_kv, g_kv.pool, kv)
     assert not errs, "\n".join(errs)
     o_kv.check_invariants()
     if kv.block_size and wl == "c3":

@@ -1,18 +1,19 @@
 """The early-exit cycle (specdec_cycle_early_exit: row statistics position by position,
-no row read past a request's first rejection) against the full cycle, on twin inputs and
-caches: accepted counts, emitted tokens, error word, request flags, the draw's W and
-picked probability, cache metadata and pool bits are equal bit for bit; p(y), q(y) and
-the row statistics of the positions it read are equal too, and those of the positions it
-did not read are NaN. The full cycle is itself checked against the oracle elsewhere, so
-this carries the oracle parity over ("Speculative decoding: accelerate LLM generation
-without changing its answers" §2-3: nothing after the first rejection is looked at).
+no row read past a request's first rejection) against the oracle and against the full
+cycle, on twin inputs and caches. Against the oracle: the flagged-margin rule of every
+verification test, with the debug values of rows past the GPU's accepted count allowed to
+be NaN ("Speculative decoding: accelerate LLM generation without changing its answers"
+§2-3: nothing after the first rejection is looked at). Against the full cycle: accepted
+counts, emitted tokens, error word, request flags, the draw's W and picked probability,
+cache metadata and pool bits are equal bit for bit; p(y), q(y) and the row statistics of
+the positions it read are equal too, and those of the positions it did not read are NaN.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_harness import KVOnDevice, VerifyOnDevice, log
+from gpu_harness import KVOnDevice, VerifyOnDevice, compare_verify, log, oracle_verify
 from rejection_sampling_verify_specdec_amd import binding, synth
 
 pytestmark = pytest.mark.gpu
@@ -104,9 +105,23 @@ def _compare(vin, full, early, u, y):
     return read, 2 * vin.K + vin.B
 
 
+def _against_oracle(vin, e, top_k=None, eos=None, max_emit=None, temps=None):
+    """The early-exit outputs against the oracle on the same inputs."""
+    T = vin.T if temps is None else temps
+    o = oracle_verify(vin, top_k=top_k, T=T, eos=eos, max_emit=max_emit)
+    rep = compare_verify(vin, e, o, T=T, top_k=top_k, eos=eos, max_emit=max_emit,
+                         early_exit=True)
+    log(f"[early-exit]   against the oracle: {rep}")
+    rep.check()
+
+
 def _both(vin, kv, **kw):
     full = _run(vin, kv, False, **kw)
     early = _run(vin, kv, True, **kw)
+    if kw.get("cu") is None and kw.get("plant") is None:
+        # offsets or device inputs changed after upload have no oracle counterpart here
+        _against_oracle(vin, early[0], top_k=kw.get("top_k"), eos=kw.get("eos"),
+                        max_emit=kw.get("max_emit"), temps=kw.get("temps"))
     read, rows = _compare(vin, full[:3], early[:3], *full[3:])
     acc = full[0].num_accepted
     log(f"[early-exit]   rows read {read} of {rows}; accepted {int(acc[acc >= 0].sum())}, "
@@ -286,5 +301,6 @@ def test_verify_early_exit_equals_specdec_verify(wl, dtype, V, k_range, per_requ
     read, rows = _compare(vin, (f, None, None), (e, None, None), full.u_acc.cpu().numpy(),
                           full.tokens.cpu().numpy())
     log(f"[verify-early-exit] {wl} {dtype} V={V}: rows read {read} of {rows}")
+    _against_oracle(vin, e, temps=kw.get("temps"))
     if per_request:
         assert f.req_flags[2] & binding.ERR_PARAM

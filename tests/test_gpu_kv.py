@@ -79,7 +79,7 @@ def _rollback(g, o, k, a):
 def _assert_same(g, o, what, data=True):
     errs = compare_kv_meta(o, g.meta(), what)
     if data:
-        errs += compare_kv_data(o, g.pool)
+        errs += compare_kv_data(o, g.pool, g.kv)
     assert not errs, "\n".join(errs)
 
 

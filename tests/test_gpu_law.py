@@ -1,0 +1,167 @@
+"""The law of what the device emits ("Speculative decoding: accelerate LLM generation without
+changing its answers", section 3: accepting with probability min(1, p/q) and drawing the
+correction from normalize(max(0, p - q)) leaves the output distributed exactly as the
+target; section 6 asks to compare empirical token frequencies on a controlled small
+vocabulary).
+
+Setup: V = 8, k = 3, fixed rows with rational probabilities (multiples of 1/64, every token
+positive), the same at every request: target rows p_0..p_3 for positions 0..3 and draft
+rows q_0..q_2, which depend on the position only. Proposals y_i are drawn from q_i and all
+uniforms are seeded. Each request's emitted tokens (the accepted proposals and the
+replacement or bonus token, 1 to 4 of them) are completed to four tokens by drawing the
+missing positions t from p_t, as autoregressive sampling from the target would go on. The
+completed sequences must then follow prod_t p_t(x_t); the first emitted token alone must
+follow p_0. Both are chi-square tests with a fixed seed, cells of expected count below 5
+pooled, and a p-value threshold of 1e-4. 2^20 requests go through specdec_verify in 16
+calls of 65536.
+
+The same statistic run on the CPU over the oracle detects a planted mistake (the
+correction drawn from p instead of the residual) and accepts the oracle itself, so the
+test has the power to see what it is for.
+"""
+
+import math
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import scipy.stats
+
+import oracle
+
+V, K = 8, 3
+CALLS, BATCH = 16, 65536
+P_VALUE = 1e-4
+
+
+def _rows():
+    """Target rows p_0..p_3 and draft rows q_0..q_2 in 64ths (every entry positive)."""
+    p = [[12, 4, 9, 3, 14, 6, 10, 6], [5, 15, 7, 9, 4, 8, 10, 6],
+         [20, 3, 5, 8, 6, 9, 4, 9], [7, 7, 11, 5, 9, 13, 6, 6]]
+    q = [[6, 10, 9, 7, 8, 9, 8, 7], [9, 8, 5, 12, 3, 11, 10, 6], [10, 5, 9, 6, 12, 4, 9, 9]]
+    for r in p + q:
+        assert sum(r) == 64 and min(r) > 0
+    return [[F(x, 64) for x in r] for r in p], [[F(x, 64) for x in r] for r in q]
+
+
+def _draw(rng, probs, n):
+    """n draws from a probability vector, by inverse CDF of seeded uniforms."""
+    c = np.cumsum([float(x) for x in probs])
+    return np.minimum(np.searchsorted(c, rng.random(n), side="right"), len(probs) - 1)
+
+
+def _complete(rng, emitted, n_emitted, p):
+    """Rows of 4 tokens: each request's emitted tokens, then draws from p_t."""
+    n = emitted.shape[0]
+    out = np.empty((n, K + 1), np.int64)
+    for t in range(K + 1):
+        fill = _draw(rng, p[t], n)
+        out[:, t] = np.where(t < n_emitted, emitted[:, t], fill)
+    return out
+
+
+def _chi2(counts, probs):
+    """Chi-square p-value of counts against exact cell probabilities (cells of expected
+    count below 5 pooled into one)."""
+    n = counts.sum()
+    exp = n * probs
+    small = exp < 5
+    obs = np.concatenate([counts[~small], [counts[small].sum()]]) if small.any() else counts
+    ex = np.concatenate([exp[~small], [exp[small].sum()]]) if small.any() else exp
+    stat = float(((obs - ex) ** 2 / ex).sum())
+    return float(scipy.stats.chi2.sf(stat, len(ex) - 1)), stat
+
+
+def _law_pvalues(seqs, first, p):
+    joint = np.array([float(p[0][a] * p[1][b] * p[2][c] * p[3][d])
+                      for a in range(V) for b in range(V) for c in range(V) for d in range(V)])
+    idx = ((seqs[:, 0] * V + seqs[:, 1]) * V + seqs[:, 2]) * V + seqs[:, 3]
+    pj, _ = _chi2(np.bincount(idx, minlength=V ** 4).astype(np.float64), joint)
+    pf, _ = _chi2(np.bincount(first, minlength=V).astype(np.float64),
+                  np.array([float(x) for x in p[0]]))
+    return pj, pf
+
+
+def _oracle_sample(n, seed, plant=False):
+    """n requests through the oracle (plant: the correction drawn from p instead)."""
+    p, q = _rows()
+    rng = np.random.default_rng(seed)
+    pf = [np.array([float(x) for x in r]) for r in p]
+    qf = [np.array([float(x) for x in r]) for r in q]
+    ys = np.stack([_draw(rng, q[i], n) for i in range(K)], axis=1)
+    ua = rng.random((n, K)).astype(np.float32)
+    us = rng.random(n).astype(np.float32)
+    em = np.zeros((n, K + 1), np.int64)
+    ne = np.zeros(n, np.int64)
+    resid = oracle.verify.residual_weights
+    try:
+        if plant:
+            oracle.verify.residual_weights = lambda pp, qq: pp
+        for j in range(n):
+            r = oracle.verify_probs(pf, qf, ys[j].tolist(), [float(u) for u in ua[j]],
+                                    float(us[j]))
+            em[j, :len(r.emitted)] = r.emitted
+            ne[j] = len(r.emitted)
+    finally:
+        oracle.verify.residual_weights = resid
+    return _complete(rng, em, ne, p), em[:, 0]
+
+
+def test_law_statistic_sees_a_planted_mistake():
+    # CPU: the oracle passes, the oracle with the correction drawn from p fails
+    p, _ = _rows()
+    ok = _law_pvalues(*_oracle_sample(30000, 5), p)
+    bad = _law_pvalues(*_oracle_sample(30000, 5, plant=True), p)
+    assert min(ok) > P_VALUE, ok
+    assert min(bad) < 1e-12, bad
+
+
+@pytest.mark.gpu
+def test_emitted_sequences_follow_the_target_law():
+    import torch
+    from gpu_harness import log
+    from rejection_sampling_verify_specdec_amd import binding
+
+    p, q = _rows()
+    d = torch.device("cuda:0")
+    rng = np.random.default_rng(2024)
+    # logits ln p: the kernels' softmax gives the rows back to fp32 rounding
+    lp = np.log(np.array([[float(x) for x in r] for r in p], np.float64)).astype(np.float32)
+    lq = np.log(np.array([[float(x) for x in r] for r in q], np.float64)).astype(np.float32)
+    B = BATCH
+    tgt = torch.from_numpy(np.tile(lp, (B, 1))).to(d)          # rows of b: 4b .. 4b + 3
+    dft = torch.from_numpy(np.tile(lq, (B, 1))).to(d)          # rows of b: 3b .. 3b + 2
+    cu = torch.arange(0, K * B + 1, K, dtype=torch.int32, device=d)
+    out = torch.empty(K * B + B, dtype=torch.int32, device=d)
+    nacc = torch.empty(B, dtype=torch.int32, device=d)
+    nemit = torch.empty(B, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    ws = torch.empty(binding.specdec_verify_workspace_size(B, K * B, V, binding.SPECDEC_F32, 0),
+                     dtype=torch.uint8, device=d)
+    seqs, firsts, accepted = [], [], 0
+    for call in range(CALLS):
+        ys = np.stack([_draw(rng, q[i], B) for i in range(K)], axis=1).astype(np.int32)
+        ua = rng.random((B, K), dtype=np.float32)
+        us = rng.random(B, dtype=np.float32)
+        binding.specdec_verify(tgt, dft, torch.from_numpy(ys.reshape(-1)).to(d), cu,
+                               torch.from_numpy(ua.reshape(-1)).to(d), torch.from_numpy(us).to(d),
+                               max_k=K, temperature=1.0, top_k=0, out_tokens=out,
+                               num_accepted=nacc, num_emitted=nemit, err_word=err, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        o = out.cpu().numpy().reshape(B, K + 1).astype(np.int64)
+        ne = nemit.cpu().numpy().astype(np.int64)
+        na = nacc.cpu().numpy()
+        assert (ne == na + 1).all() and (na >= 0).all()
+        # the accepted proposals are emitted as drawn
+        for i in range(K):
+            sel = na > i
+            assert np.array_equal(o[sel, i], ys[sel, i])
+        accepted += int(na.sum())
+        seqs.append(_complete(rng, o, ne, p))
+        firsts.append(o[:, 0])
+    seqs, firsts = np.concatenate(seqs), np.concatenate(firsts)
+    pj, pf = _law_pvalues(seqs, firsts, p)
+    log(f"[law] {CALLS * B} requests, mean accepted {accepted / (CALLS * B):.3f}: "
+        f"joint law p-value {pj:.3g}, first-token p-value {pf:.3g}")
+    assert pj > P_VALUE and pf > P_VALUE

@@ -73,8 +73,11 @@ class Caches:
                     free_count=int(c.free_count.item()), state=int(c.state.item()))
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_target_and_draft_caches_over_rounds(seed):
+@pytest.mark.parametrize("seed,repeat", [(0, False), (1, False), (2, True)])
+def test_target_and_draft_caches_over_rounds(seed, repeat):
+    # repeat: every proposal of a round repeats the request's pending token id ("Keep cache
+    # validity aligned with the committed token history", paragraph 6): the caches hold
+    # one state per position, whatever the ids
     B, NB, MBR, V, rounds = 8, 600, 64, 64, 12
     rng = np.random.default_rng(200 + seed)
     tgt = Caches(B, NB, MBR, 300 + seed)
@@ -83,6 +86,9 @@ def test_target_and_draft_caches_over_rounds(seed):
     for rnd in range(rounds):
         vin = synth.make_verify("c1", seed=1000 * seed + rnd, B=B, V=V, k_range=(0, 5))
         cu = [int(x) for x in vin.cu_draft]
+        if repeat:
+            for b in range(B):
+                vin.draft_tokens[cu[b]:cu[b + 1]] = hist[b][-1]
         y = [[int(t) for t in vin.draft_tokens[cu[b]:cu[b + 1]]] for b in range(B)]
         log(f"[loop] seed {seed} round {rnd}: k_b = {[len(t) for t in y]}")
         # drafting: the draft processes its pending tokens, then y_1 .. y_{k-1}

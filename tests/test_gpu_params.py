@@ -50,7 +50,7 @@ def _check(vin, Ts, ks, ps, top_k_max=None, requests=None, redraw=True, seed=0):
                       top_k_max=top_k_max if top_k_max is not None else int(max(ks.max(), 0)))
     rep = compare_verify(vin, g, o, requests=requests, T=Ts, top_k=ks, top_p=ps)
     log(f"[params]   {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     return g, o
 
 
@@ -184,7 +184,7 @@ def test_fused_cycle_equals_three_calls_per_request(wl, temps_only):
     o = oracle_verify(vin, T=Ts, top_k=ok_, top_p=op_, top_k_max=2000)
     rep = compare_verify(vin, a[0], o, T=Ts, top_k=ok_, top_p=op_)
     log(f"[params-fused]   {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     o_kv = oracle_kv(kv)
     o_kv.append(kv.k_new, kv.v_new, kv.cu_new)
     o_kv.rollback(a[0].num_accepted, vin.cu_draft)

@@ -23,7 +23,7 @@ def _check(vin, requests=None):
     o = oracle_verify(vin, requests=requests)
     rep = compare_verify(vin, g, o, requests=requests)
     log(f"[topk]   {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     return g, o
 
 

@@ -37,7 +37,9 @@ def _redraw(vin, top_p, seed, requests=None):
     return vin
 
 
-def _check(vin, top_p, requests=None, min_checked=1):
+def _check(vin, top_p, requests=None, min_checked=None):
+    """min_checked: requests that must be held to the full rule (default: half of them;
+    the flagged count depends on the oracle's margins only, so it is fixed per case)."""
     log(f"[topp] B={vin.B} K={vin.K} V={vin.V} {vin.dtype} T={vin.T} top_k={vin.top_k} "
         f"top_p={top_p} requests={'all' if requests is None else len(requests)}")
     v = VerifyOnDevice(vin, top_p=top_p)
@@ -46,9 +48,9 @@ def _check(vin, top_p, requests=None, min_checked=1):
     o = oracle_verify(vin, requests=requests, top_p=top_p)
     rep = compare_verify(vin, g, o, requests=requests, top_p=top_p)
     log(f"[topp]   {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     n = vin.B if requests is None else len(requests)
-    assert n - rep.flagged_nucleus >= min_checked
+    assert n - rep.flagged_nucleus >= (min_checked if min_checked is not None else (n + 1) // 2)
     return g, o
 
 

@@ -24,7 +24,7 @@ def _check(vin, requests=None, **kw):
     o = oracle_verify(vin, requests=requests)
     rep = compare_verify(vin, g, o, requests=requests)
     log(f"[verify]   {rep}")
-    assert not rep.errors, "\n".join(rep.errors)
+    rep.check()
     return g, o, rep
 
 
@@ -104,6 +104,21 @@ def test_forced_rejection_positions_and_bonus():
     g, o, _ = _check(vin)
     assert list(g.num_accepted) == [0, 2, 4, 5]
     assert list(g.num_emitted) == [1, 3, 5, 6]
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20000), ("f32", 4000)])
+def test_repeated_proposal_ids(dtype, V):
+    # "Keep cache validity aligned with the committed token history", paragraph 6: repeated
+    # token ids. Every proposal of a request is one id: the argmax of its first draft row
+    # (accepted often, then judged again at later positions against their own rows), or
+    # token 0 for every request of the batch
+    vin = synth.make_verify("c2", seed=24, B=10, V=V, dtype=dtype)
+    dft = (synth.bf16_bits_to_f32(vin.draft) if dtype == "bf16" else vin.draft).reshape(vin.K, V)
+    for b in range(vin.B):
+        lo, hi = int(vin.cu_draft[b]), int(vin.cu_draft[b + 1])
+        vin.draft_tokens[lo:hi] = int(np.argmax(dft[lo])) if b % 2 == 0 else 0
+    g, o, _ = _check(vin)
+    assert (g.num_accepted[::2] >= 1).any()
 
 
 def test_draft_zero_probability_proposal_is_accepted_and_flagged():

@@ -537,3 +537,26 @@ def test_two_token_residual_matches_closed_form(gap):
         assert not res.err & ERR_ZFALLBACK
         assert abs(float(res.probs.W_resid) - exact) <= 1e-8 * exact
         assert res.emitted == [1]                     # a > b: the residual lives on token 1
+
+
+def test_repeated_proposal_ids_use_each_positions_rows():
+    # "Keep cache validity aligned with the committed token history", paragraph 6 lists
+    # repeated token ids among the cases to test: the same id proposed at several positions
+    # is judged each time against that position's own rows (section 2: p_i, q_i per
+    # position). Token 1 three times: position 0 has p(1) = q(1) (ratio 1, accepted for any
+    # u), position 1 has p(1) = 1/4 against q(1) = 1/2 (ratio 1/2), position 2 would accept
+    P0 = [F(1, 4), F(1, 2), F(1, 4)]
+    P1 = [F(1, 2), F(1, 4), F(1, 4)]
+    P2 = [F(0), F(1), F(0)]
+    Q = [F(1, 4), F(1, 2), F(1, 4)]
+    rows_p = [P0, P1, P2, [F(1, 3)] * 3]
+    for u1, a in ((F(1, 3), 3), (F(3, 4), 1)):
+        r = verify_probs(rows_p, [Q, Q, Q], [1, 1, 1], [F(9, 10), u1, F(1, 2)], F(1, 2))
+        assert r.a == a and r.emitted[:a] == [1] * a
+        assert r.P == [F(1, 2), F(1, 4), F(1)] and r.Q == [F(1, 2)] * 3
+        if a == 1:
+            # the residual of position 1: max(0, P1 - Q) = (1/4, 0, 0) -> token 0
+            assert r.mode == "resid" and r.W == F(1, 4) and r.emitted[1] == 0
+        else:
+            # position 2: P2(1) = 1 >= Q(1): accepted; the bonus comes from the last row
+            assert r.mode == "bonus"
