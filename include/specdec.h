@@ -48,6 +48,8 @@ extern "C" {
 #define SPECDEC_EINVAL     (-1)   /* a host-visible argument is invalid; nothing enqueued */
 #define SPECDEC_EHIP       (-3)   /* a HIP launch / runtime call failed                    */
 #define SPECDEC_EWORKSPACE (-4)   /* workspace missing, misaligned or too small            */
+#define SPECDEC_ESCRATCH   (-5)   /* specdec_cycle_static: the call needs more scratch than
+                                     SPECDEC_STATIC_SCRATCH_BYTES; nothing enqueued       */
 
 /* ---- logits element type ----------------------------------------------------------- */
 #define SPECDEC_F32  0
@@ -358,6 +360,33 @@ int specdec_cycle(const kv_paged_cache* cache, const void* k_new, const void* v_
                   int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                   int32_t* err_word, const specdec_debug* dbg,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * specdec_cycle_static - specdec_cycle without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Its scratch is one array of
+ * SPECDEC_STATIC_SCRATCH_BYTES in the library's device image: each GPU the library runs
+ * on holds its own copy until the process ends; the library takes its address once per
+ * device on the first call there. The call allocates nothing and frees nothing. Arguments,
+ * layouts, ownership, host checks and results: as specdec_cycle with a workspace of that
+ * size, bit for bit. A call whose workspace (specdec_cycle_workspace_size with the same
+ * arguments) exceeds the array returns SPECDEC_ESCRATCH before anything is enqueued
+ * (temperature-only cycles fit up to several hundred requests at V = 152064; top-k and
+ * top-p candidate lists do not fit past small batches). Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (other streams, other threads) race and must
+ * be serialized by the caller. Nothing in the array must start at zero (every launch
+ * writes what it reads).
+ */
+#define SPECDEC_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+int specdec_cycle_static(const kv_paged_cache* cache, const void* k_new, const void* v_new,
+                         const void* target_logits, const void* draft_logits, int32_t dtype,
+                         const int32_t* draft_tokens, const int32_t* cu_draft,
+                         const float* u_accept, const float* u_sample,
+                         int32_t B, int32_t K, int32_t max_k, int32_t V,
+                         float temperature, int32_t top_k, float top_p,
+                         const specdec_params* per_request,
+                         int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
+                         int32_t* err_word, const specdec_debug* dbg, hipStream_t stream);
 
 /* specdec_cycle_early_exit: the same cycle, reading no logit row past a request's first
  * rejection. "Speculative decoding: accelerate LLM generation without changing its

@@ -22,6 +22,8 @@ SPECDEC_OK = 0
 SPECDEC_EINVAL = -1
 SPECDEC_EHIP = -3
 SPECDEC_EWORKSPACE = -4
+SPECDEC_ESCRATCH = -5
+STATIC_SCRATCH_BYTES = 8 << 20
 SPECDEC_F32 = 0
 SPECDEC_BF16 = 1
 
@@ -50,6 +52,7 @@ EXPORTED = [
     "specdec_verify_early_exit",
     "kv_paged_append_workspace_size", "kv_paged_append", "kv_rollback", "kv_rollback_draft",
     "specdec_cycle_workspace_size", "specdec_cycle", "specdec_cycle_early_exit",
+    "specdec_cycle_static",
     "specdec_tree_verify_workspace_size",
     "specdec_tree_verify", "kv_tree_commit",
     "kv_contig_append", "kv_contig_rollback",
@@ -166,6 +169,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                        i32, i32, i32, i32, f32, i32, f32, pp, vp, vp, vp, vp,
                        ctypes.POINTER(SpecdecDebug), vp, sz, vp]
         fn.restype = ctypes.c_int
+    lib.specdec_cycle_static.argtypes = [ctypes.POINTER(KvPagedCacheStruct), vp, vp, vp, vp, i32,
+                                         vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, f32, pp,
+                                         vp, vp, vp, vp, ctypes.POINTER(SpecdecDebug), vp]
+    lib.specdec_cycle_static.restype = ctypes.c_int
     lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32]
     lib.specdec_tree_verify_workspace_size.restype = sz
     lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
@@ -347,22 +354,11 @@ def specdec_cycle_workspace_size(B: int, K: int, V: int, dtype: int, top_k: int,
                                                            _pref(params)))
 
 
-def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
-                  target_logits: torch.Tensor, draft_logits: torch.Tensor,
-                  draft_tokens: torch.Tensor, cu_draft: torch.Tensor,
-                  u_accept: torch.Tensor, u_sample: torch.Tensor, *, max_k: int,
-                  temperature: float, top_k: int, out_tokens: torch.Tensor,
-                  num_accepted: torch.Tensor, num_emitted: torch.Tensor,
-                  err_word: torch.Tensor, workspace: torch.Tensor,
-                  debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
-                  temperatures: Optional[torch.Tensor] = None,
-                  top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
-                  top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
-                  max_emit: Optional[torch.Tensor] = None, early_exit: bool = False) -> None:
-    """Enqueue append -> verify -> rollback of one cycle as fused launches. With
-    ``early_exit`` (specdec_cycle_early_exit) the row statistics run position by position and
-    no row past a request's first rejection is read."""
-    lib = load_library()
+def _cycle_args(cache, k_new, v_new, target_logits, draft_logits, draft_tokens, cu_draft,
+                u_accept, u_sample, max_k, temperature, top_k, out_tokens, num_accepted,
+                num_emitted, err_word, debug, top_p, temperatures, top_ks, top_ps, top_k_max,
+                eos_tokens, max_emit):
+    """Checked C arguments of a cycle call, up to (not including) the workspace."""
     dev = target_logits.device
     dtype = _logits_dtype(target_logits)
     if target_logits.dim() != 2:
@@ -386,18 +382,64 @@ def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
     _check(num_accepted, "num_accepted", torch.int32, B, dev)
     _check(num_emitted, "num_emitted", torch.int32, B, dev)
     _check(err_word, "err_word", torch.int32, 1, dev)
-    _check(workspace, "workspace", torch.uint8, None, dev)
     prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
+    args = (ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
+            dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K,
+            max_k, V, float(temperature), int(top_k), float(top_p), _pref(prm), _ptr(out_tokens),
+            _ptr(num_accepted), _ptr(num_emitted), _ptr(err_word),
+            ctypes.byref(debug) if debug is not None else None)
+    return args, prm, dev
+
+
+def specdec_cycle(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                  target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                  draft_tokens: torch.Tensor, cu_draft: torch.Tensor,
+                  u_accept: torch.Tensor, u_sample: torch.Tensor, *, max_k: int,
+                  temperature: float, top_k: int, out_tokens: torch.Tensor,
+                  num_accepted: torch.Tensor, num_emitted: torch.Tensor,
+                  err_word: torch.Tensor, workspace: torch.Tensor,
+                  debug: Optional[SpecdecDebug] = None, top_p: float = 1.0,
+                  temperatures: Optional[torch.Tensor] = None,
+                  top_ks: Optional[torch.Tensor] = None, top_ps: Optional[torch.Tensor] = None,
+                  top_k_max: Optional[int] = None, eos_tokens: Optional[torch.Tensor] = None,
+                  max_emit: Optional[torch.Tensor] = None, early_exit: bool = False) -> None:
+    """Enqueue append -> verify -> rollback of one cycle as fused launches. With
+    ``early_exit`` (specdec_cycle_early_exit) the row statistics run position by position and
+    no row past a request's first rejection is read."""
+    lib = load_library()
+    args, prm, dev = _cycle_args(cache, k_new, v_new, target_logits, draft_logits, draft_tokens,
+                                 cu_draft, u_accept, u_sample, max_k, temperature, top_k,
+                                 out_tokens, num_accepted, num_emitted, err_word, debug, top_p,
+                                 temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
+    _check(workspace, "workspace", torch.uint8, None, dev)
     name = "specdec_cycle_early_exit" if early_exit else "specdec_cycle"
-    st = getattr(lib, name)(
-        ctypes.byref(s), _ptr(k_new), _ptr(v_new), _ptr(target_logits), _ptr(draft_logits),
-        dtype, _ptr(draft_tokens), _ptr(cu_draft), _ptr(u_accept), _ptr(u_sample), B, K, max_k,
-        V, float(temperature), int(top_k), float(top_p), _pref(prm), _ptr(out_tokens),
-        _ptr(num_accepted),
-        _ptr(num_emitted), _ptr(err_word), ctypes.byref(debug) if debug is not None else None,
-        _ptr(workspace), workspace.numel(), _stream(dev))
+    st = getattr(lib, name)(*args, _ptr(workspace), workspace.numel(), _stream(dev))
     if st != SPECDEC_OK:
         raise SpecdecError(name, st)
+
+
+def specdec_cycle_static(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.Tensor,
+                         target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                         draft_tokens: torch.Tensor, cu_draft: torch.Tensor,
+                         u_accept: torch.Tensor, u_sample: torch.Tensor, *, max_k: int,
+                         temperature: float, top_k: int, out_tokens: torch.Tensor,
+                         num_accepted: torch.Tensor, num_emitted: torch.Tensor,
+                         err_word: torch.Tensor, debug: Optional[SpecdecDebug] = None,
+                         top_p: float = 1.0, temperatures: Optional[torch.Tensor] = None,
+                         top_ks: Optional[torch.Tensor] = None,
+                         top_ps: Optional[torch.Tensor] = None, top_k_max: Optional[int] = None,
+                         eos_tokens: Optional[torch.Tensor] = None,
+                         max_emit: Optional[torch.Tensor] = None) -> None:
+    """specdec_cycle over the library's static scratch array (no workspace argument, nothing
+    allocated); calls that overlap on one GPU race."""
+    lib = load_library()
+    args, prm, dev = _cycle_args(cache, k_new, v_new, target_logits, draft_logits, draft_tokens,
+                                 cu_draft, u_accept, u_sample, max_k, temperature, top_k,
+                                 out_tokens, num_accepted, num_emitted, err_word, debug, top_p,
+                                 temperatures, top_ks, top_ps, top_k_max, eos_tokens, max_emit)
+    st = lib.specdec_cycle_static(*args, _stream(dev))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_cycle_static", st)
 
 
 # --- HIP events and stream waits through the runtime (timing, cross-stream ordering) -----

@@ -21,6 +21,9 @@
 // entry t of request b is row cu_draft[b] + b + t of k_new / v_new), then verified, then
 // rolled back to the pending token plus the accepted proposals.
 
+#include <atomic>
+#include <mutex>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -412,4 +415,58 @@ extern "C" int specdec_cycle_early_exit(const kv_paged_cache* cache, const void*
                        draft_tokens, cu_draft, u_accept, u_sample, B, K, max_k, V, temperature,
                        top_k, top_p, per_request, out_tokens, num_accepted, num_emitted, err_word,
                        dbg, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// specdec_cycle_static: the cycle over a scratch array in the device image instead of a
+// caller workspace. The array's host-side name is only a stand-in for the symbol; the
+// kernels get the device address that hipGetSymbolAddress returns, taken once per device
+// (under a lock) with that device current, and kept.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+__device__ __align__(256) uint8_t scratch[SPECDEC_STATIC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_lock;
+
+// the calling thread's current device's copy of the array, or null
+void* scratch_of_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> guard(g_scratch_lock);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        void* q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+        p = q;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+}  // namespace
+
+extern "C" int specdec_cycle_static(const kv_paged_cache* cache, const void* k_new,
+                                    const void* v_new, const void* target_logits,
+                                    const void* draft_logits, int32_t dtype,
+                                    const int32_t* draft_tokens, const int32_t* cu_draft,
+                                    const float* u_accept, const float* u_sample, int32_t B,
+                                    int32_t K, int32_t max_k, int32_t V, float temperature,
+                                    int32_t top_k, float top_p, const specdec_params* per_request,
+                                    int32_t* out_tokens, int32_t* num_accepted,
+                                    int32_t* num_emitted, int32_t* err_word,
+                                    const specdec_debug* dbg, hipStream_t stream) {
+    // the size check first: an oversized call never takes the array's address
+    const size_t need = specdec_cycle_workspace_size(B, K, V, dtype, top_k, top_p, per_request);
+    if (need > SPECDEC_STATIC_SCRATCH_BYTES) return SPECDEC_ESCRATCH;
+    void* ws = scratch_of_current_device();
+    if (!ws) return SPECDEC_EHIP;
+    return cycle_entry(false, cache, k_new, v_new, target_logits, draft_logits, dtype,
+                       draft_tokens, cu_draft, u_accept, u_sample, B, K, max_k, V, temperature,
+                       top_k, top_p, per_request, out_tokens, num_accepted, num_emitted, err_word,
+                       dbg, ws, SPECDEC_STATIC_SCRATCH_BYTES, stream);
 }

@@ -332,6 +332,9 @@ extern "C" const char* specdec_status_string(int status) {
         case SPECDEC_EINVAL: return "invalid argument";
         case SPECDEC_EHIP: return "HIP runtime error";
         case SPECDEC_EWORKSPACE: return "workspace missing, misaligned or too small";
+        case SPECDEC_ESCRATCH:
+            return "the call needs more scratch than the static array holds; use the entry "
+                   "point that takes a workspace";
         default: return "unknown status";
     }
 }

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -3, -4, 12345):
+    for st in (0, -1, -3, -4, -5, 12345):
         assert isinstance(binding.status_string(st), str) and binding.status_string(st)
 
 
@@ -204,3 +204,15 @@ def test_verify_early_exit_host_validation_without_gpu(lib):
         assert call(full, **kw) == binding.SPECDEC_EWORKSPACE, kw
     for kw in (dict(), dict(top_k=1000), dict(pr=binding.SpecdecParams(16, None, None, 0))):
         assert call(ee, **kw) == binding.SPECDEC_EWORKSPACE, kw
+
+
+def test_static_cycle_refuses_calls_larger_than_its_scratch(lib):
+    # the size check comes before anything touches a device: a full top-k batch needs more
+    # than the static array and is refused with SPECDEC_ESCRATCH, here without a GPU
+    need = binding.specdec_cycle_workspace_size(128, 1024, 128256, binding.SPECDEC_BF16, 64)
+    assert need > binding.STATIC_SCRATCH_BYTES
+    st = lib.specdec_cycle_static(None, None, None, None, None, binding.SPECDEC_BF16, None, None,
+                                  None, None, 128, 1024, 8, 128256, 0.8, 64, 1.0, None, None,
+                                  None, None, None, None, None)
+    assert st == binding.SPECDEC_ESCRATCH
+    assert "static" in binding.status_string(st)
