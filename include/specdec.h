@@ -84,6 +84,9 @@ extern "C" {
 #define SPECDEC_MAX_TREE   64         /* nodes of one request's draft tree               */
 #define SPECDEC_MAX_KV_BATCH 4096
 #define SPECDEC_MAX_V      2097152
+/* positions the early-exit calls read one launch at a time before one launch reads the
+ * rest of every request still live */
+#define SPECDEC_EARLY_EXIT_SEQUENTIAL 2
 
 /* Short English text for a return code. Never NULL. */
 const char* specdec_status_string(int status);
@@ -212,11 +215,15 @@ int specdec_verify(const void* target_logits, const void* draft_logits, int32_t 
                    int32_t* err_word, const specdec_debug* dbg,
                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* specdec_verify_early_exit: specdec_verify reading no logit row past a request's first
+/* specdec_verify_early_exit: specdec_verify without the rows past a request's first
  * rejection ("Speculative decoding: accelerate LLM generation without changing its
  * answers" §2-3: nothing after the first rejected proposal decides anything). The row
- * statistics run as max_k + 1 launches, one per position, each reading the rows of the
- * requests whose earlier proposals were all accepted; the decision and the draw follow.
+ * statistics of positions 0 .. SPECDEC_EARLY_EXIT_SEQUENTIAL - 1 run one launch per
+ * position, each reading the rows of the requests whose earlier proposals were all
+ * accepted; one more launch reads every later row of the requests still live then (ahead
+ * of their decisions: few requests get that far, and one launch costs less than one per
+ * position). A request rejected at an earlier position reads none of them. The decision
+ * and the draw follow.
  * Arguments, layouts, ownership and workspace (specdec_verify_workspace_size with the same
  * arguments): as specdec_verify, and the same results bit for bit for every request whose
  * read rows are finite. A non-finite row past the first rejection is not reported; debug
@@ -388,7 +395,7 @@ int specdec_cycle_static(const kv_paged_cache* cache, const void* k_new, const v
                          int32_t* out_tokens, int32_t* num_accepted, int32_t* num_emitted,
                          int32_t* err_word, const specdec_debug* dbg, hipStream_t stream);
 
-/* specdec_cycle_early_exit: the same cycle, reading no logit row past a request's first
+/* specdec_cycle_early_exit: the same cycle without the rows past a request's first
  * rejection. "Speculative decoding: accelerate LLM generation without changing its
  * answers" §2-3: once proposal i is rejected, nothing after it is looked at; the accepted
  * count, the emitted tokens, the draw and the cache step depend only on the rows of
@@ -397,8 +404,11 @@ int specdec_cycle_static(const kv_paged_cache* cache, const void* k_new, const v
  * Arguments, layouts, ownership, workspace (specdec_cycle_workspace_size with the same
  * arguments) and results: as specdec_cycle, bit for bit, for every request whose rows are
  * finite. Differences, all from the rows that are not read:
- *   - the row statistics run as max_k + 1 launches, one per position p, each reading the
- *     rows of position p of the requests whose proposals before p were all accepted;
+ *   - the row statistics of positions 0 .. SPECDEC_EARLY_EXIT_SEQUENTIAL - 1 run one launch
+ *     per position p, each reading the rows of position p of the requests whose proposals
+ *     before p were all accepted; one more launch reads every later row of the requests
+ *     live at SPECDEC_EARLY_EXIT_SEQUENTIAL (ahead of their decisions); the K/V scatter
+ *     is spread over the launches after the first;
  *   - SPECDEC_ERR_NONFINITE covers the rows read (a non-finite row after the first
  *     rejection is not seen);
  *   - debug p_y / q_y after the first rejection, and row_max / row_sum / row_thr of rows

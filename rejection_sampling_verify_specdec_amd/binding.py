@@ -44,6 +44,9 @@ KV_ERR_ROLLBACK = 256
 KV_APPEND_REJECTED = 1 << 16
 
 MAX_K = 64
+# positions the early-exit calls read one launch at a time before one launch reads the rest
+# of every request still live (SPECDEC_EARLY_EXIT_SEQUENTIAL)
+EARLY_EXIT_SEQUENTIAL = 2
 MAX_KV_BATCH = 4096
 MAX_V = 2097152
 

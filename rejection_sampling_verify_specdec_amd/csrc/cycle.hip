@@ -7,12 +7,18 @@
 //                   destination rows) while every other workgroup streams logit rows
 //                   (row statistics; with top-k or top-p, k_cycle_topk gathers chunk
 //                   candidates and a short per-row merge launch follows);
-//   k_cycle_decide  K/V scatter workgroups, then one workgroup per request for its
-//                   accept / reject decisions;
+//   k_cycle_decide  one workgroup per request for its accept / reject decisions, then
+//                   most of the K/V scatter;
 //   k_cycle_part    workgroup 0 truncates every request to its committed prefix (up to 512
 //                   requests; beyond that k_cycle_rollback runs after the pick) while the
-//                   others sum the sampling weights chunk by chunk;
-//   k_cycle_pick    one workgroup per request draws its replacement / bonus token.
+//                   others sum the sampling weights chunk by chunk, then a share of the
+//                   scatter;
+//   k_cycle_pick    one workgroup per request draws its replacement / bonus token, then the
+//                   rest of the scatter.
+// The scatter (bandwidth-bound, independent of the decisions: every candidate is appended)
+// is spread over the three launches after the statistics so that its copy fills the
+// memory time the latency-bound decision, chunk-sum and pick workgroups leave idle. The
+// early-exit cycle spreads it over its position launches instead.
 //
 // The cycle is the one the pages describe ("Walk through KV-cache updates when
 // speculative decoding rejects some draft tokens": K/V for the candidates are appended by
@@ -21,6 +27,7 @@
 // entry t of request b is row cu_draft[b] + b + t of k_new / v_new), then verified, then
 // rolled back to the pending token plus the accepted proposals.
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -32,6 +39,7 @@
 
 #include "kv_dev.h"
 #include "verify_dev.h"
+
 
 namespace sd {
 
@@ -63,13 +71,40 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1, rpar);
 }
 
+// One launch's share of the K/V scatter: scatter workgroups s0 .. s0 + ns - 1 of the
+// ntiles * L * 2 (tile, layer / K-V plane) workgroups; each copies its tile's rows, and the
+// copy-on-write copies are spread over all of them by global index.
+struct ScatterShare {
+    KvArgs kv;
+    const uint8_t* knew;
+    const uint8_t* vnew;
+    const uint8_t* aws;
+    int B, N, tpw, ntiles, s0, ns;
+};
+
+SD_DEV void scatter_share(const ScatterShare& sc, int i) {
+    const int planes = sc.kv.L * 2;
+    const int s = sc.s0 + i;
+    scatter_body<kCycScatterPPT>(sc.kv, sc.knew, sc.vnew, sc.B, sc.N, sc.tpw, sc.aws, s / planes,
+                                 s % planes, s, sc.ntiles * planes, kScNT);
+}
+
+// Of the n workgroups i = 0 .. n-1 of a launch, the last ns run the scatter: returns i's
+// scatter index, or -1 with *work set to i (the launch's own work first in dispatch order).
+SD_DEV int scatter_index(unsigned i, unsigned n, unsigned ns, int* work) {
+    if (i >= n - ns) return (int)(i - (n - ns));
+    *work = (int)i;
+    return -1;
+}
+
 // Early-exit statistics: launch p holds the statistics of position p's rows (workgroup 0
-// of launch 0 allocates the cycle's blocks first, as k_cycle_stats does).
+// of launch 0 allocates the cycle's blocks first, as k_cycle_stats does); the launches
+// after the first also carry a share of the K/V scatter (the allocation is done by then).
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kNT) void k_cycle_pass(KvArgs kv, const int* __restrict__ cu,
                                                     int B, int N, uint8_t* __restrict__ aws,
                                                     SampleArgs sa, RowPartial* __restrict__ part,
-                                                    int p) {
+                                                    int p, int nwg, ScatterShare sc) {
     if (p == 0) {
         if (blockIdx.x == 0) {
             alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
@@ -77,8 +112,20 @@ __global__ __launch_bounds__(kNT) void k_cycle_pass(KvArgs kv, const int* __rest
         }
         pass_body<BF16, VEC>(sa, part, 0, blockIdx.x - 1);
     } else {
-        pass_body<BF16, VEC>(sa, part, p, blockIdx.x);
+        int w = 0;
+        const int si = scatter_index(blockIdx.x, gridDim.x, sc.ns, &w);
+        if (si >= 0) scatter_share(sc, si);
+        else pass_body<BF16, VEC>(sa, part, p, w);
     }
+}
+
+// The early-exit cycle's last statistics launch (position p, every later row of each live
+// request), with a share of the K/V scatter.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_cycle_tail(SampleArgs sa, RowPartial* __restrict__ part,
+                                                    int p, int nwg, ScatterShare sc) {
+    if (blockIdx.x < (unsigned)nwg) tail_body<BF16, VEC>(sa, part, p, blockIdx.x);
+    else scatter_share(sc, blockIdx.x - nwg);
 }
 
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
@@ -109,26 +156,19 @@ __global__ __launch_bounds__(256) void k_cycle_row_params(ParamArgs a, int rows)
     if (r < rows) row_params_one(a, r);
 }
 
-static_assert(kDecideNT == kScNT, "decision and scatter workgroups share one launch");
+static_assert(kDecideNT == kScNT && kPartNT == kScNT && kPickNT == kScNT && kNT == kScNT,
+              "scatter workgroups share the decision, chunk-sum, pick and position launches");
 
 template <bool BF16>
-__global__ __launch_bounds__(kDecideNT) void k_cycle_decide(SampleArgs sa, KvArgs kv,
-                                                            const uint8_t* __restrict__ knew,
-                                                            const uint8_t* __restrict__ vnew,
-                                                            int N, int tpw, int ntiles,
-                                                            const uint8_t* __restrict__ aws) {
-    // scatter workgroups are dispatched first; the short decision workgroups come last and
-    // finish in the scatter's tail
-    const int planes = kv.L * 2;
-    const int nscat = ntiles * planes;
+__global__ __launch_bounds__(kDecideNT) void k_cycle_decide(SampleArgs sa, ScatterShare sc) {
+    // the decision workgroups first: the launch that follows waits for them, not for the
+    // scatter's tail
     const int bid = blockIdx.x;
-    if (bid >= nscat) {
-        decide_kernel_body<BF16, kDecideNT>(sa, bid - nscat);
+    if (bid < sa.B) {
+        decide_kernel_body<BF16, kDecideNT>(sa, bid);
         return;
     }
-    const int s = bid;
-    scatter_body<kCycScatterPPT>(kv, knew, vnew, sa.B, N, tpw, aws, s / planes, s % planes, s,
-                                 ntiles * planes, kScNT);
+    scatter_share(sc, bid - sa.B);
 }
 
 // Up to kCycRbMaxB requests the rollback runs as workgroup 0 of the chunk-sum launch (its
@@ -137,38 +177,94 @@ constexpr int kCycRbMaxB = 512;
 constexpr int kCycRbEv = 512;
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa, KvArgs kv, int rb) {
+__global__ __launch_bounds__(kPartNT) void k_cycle_part(SampleArgs sa, KvArgs kv, int rb,
+                                                        ScatterShare sc) {
     if (rb && blockIdx.x == 0) {
         rollback_body<kPartNT, kCycRbMaxB, kCycRbEv>(kv, sa.num_acc, sa.cu, sa.B);
         return;
     }
-    const int w = blockIdx.x - rb;
+    int w = 0;
+    const int si = scatter_index(blockIdx.x - rb, gridDim.x - rb, sc.ns, &w);
+    if (si >= 0) {
+        scatter_share(sc, si);
+        return;
+    }
     part_body<BF16, VEC, kPartNT>(sa, w / sa.nch, w % sa.nch);
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa) {
-    pick_body<BF16, VEC, kPickNT>(sa, blockIdx.x);
+__global__ __launch_bounds__(kPickNT) void k_cycle_pick(SampleArgs sa, ScatterShare sc) {
+    int w = 0;
+    const int si = scatter_index(blockIdx.x, gridDim.x, sc.ns, &w);
+    if (si >= 0) {
+        scatter_share(sc, si);
+        return;
+    }
+    pick_body<BF16, VEC, kPickNT>(sa, w);
 }
 
 __global__ __launch_bounds__(kKvNT) void k_cycle_rollback(SampleArgs sa, KvArgs kv) {
     rollback_body(kv, sa.num_acc, sa.cu, sa.B);
 }
 
-// decision (with the K/V scatter), draw, rollback; analytics when asked
+// How a cycle spreads the K/V scatter (percent of its workgroups) over the launches that
+// follow the allocation. The fused cycle puts it beside the decisions (its chunk sums and
+// picks gain nothing from more company, measured); the early-exit cycle, whose statistics
+// launches past position 0 hold few rows, spreads it over them and the sampling launches.
+struct ScatterSplit {
+    int pass_pct;      // beside position 1's statistics (early exit)
+    int tail_pct;      // beside the last statistics launch (early exit)
+    int part_pct;      // beside the chunk sums
+    int pick_pct;      // beside the picks; the rest beside the decisions
+};
+constexpr ScatterSplit kFusedSplit = {0, 0, 0, 0};
+constexpr ScatterSplit kEarlySplit = {30, 30, 10, 10};
+
+static int pct_of(int n, int pct) { return (int)(((long long)n * pct) / 100); }
+
+static ScatterShare scatter_plan(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
+                                 const uint8_t* aws, int B, int N) {
+    ScatterShare sc;
+    sc.kv = kv;
+    sc.knew = knew;
+    sc.vnew = vnew;
+    sc.aws = aws;
+    sc.B = B;
+    sc.N = N;
+    sc.tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);
+    sc.ntiles = (N + sc.tpw - 1) / sc.tpw;
+    sc.s0 = 0;
+    sc.ns = sc.ntiles * kv.L * 2;
+    return sc;
+}
+
+// sc's workgroups [from, from + n)
+static ScatterShare scatter_slice(ScatterShare sc, int from, int n) {
+    sc.s0 = from;
+    sc.ns = n;
+    return sc;
+}
+
+// decision, draw, rollback, with the scatter workgroups `sc` holds (whatever the position
+// launches left) spread over them; analytics when asked
 template <bool BF16, bool VEC>
-static void launch_cycle_tail(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew, int B,
-                              int K, const WsPlan& p, uint8_t* aws, const SampleArgs& sa,
-                              hipStream_t st) {
-    const int N = K + B;
-    const int tpw = scatter_tokens_per_wg(kv, kScNT, kCycScatterPPT);
-    const int ntiles = (N + tpw - 1) / tpw;
-    hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)ntiles * kv.L * 2),
-                       dim3(kDecideNT), 0, st, sa, kv, knew, vnew, N, tpw, ntiles, aws);
+static void launch_cycle_tail(const KvArgs& kv, int B, int K, const WsPlan& p,
+                              const SampleArgs& sa, const ScatterShare& sc,
+                              const ScatterSplit& split, hipStream_t st) {
+    const int total = sc.s0 + sc.ns;          // the whole scatter; sc holds what is left
+    const int n_pick = std::min(sc.ns, pct_of(total, split.pick_pct));
+    const int n_part = std::min(sc.ns - n_pick, pct_of(total, split.part_pct));
+    const int n_dec = sc.ns - n_pick - n_part;
+    const ScatterShare s_dec = scatter_slice(sc, sc.s0, n_dec);
+    const ScatterShare s_part = scatter_slice(sc, sc.s0 + n_dec, n_part);
+    const ScatterShare s_pick = scatter_slice(sc, sc.s0 + n_dec + n_part, n_pick);
+    hipLaunchKernelGGL((k_cycle_decide<BF16>), dim3((unsigned)B + (unsigned)n_dec), dim3(kDecideNT),
+                       0, st, sa, s_dec);
     const int rb = B <= kCycRbMaxB;
-    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb), dim3(kPartNT), 0,
-                       st, sa, kv, rb);
-    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3(B), dim3(kPickNT), 0, st, sa);
+    hipLaunchKernelGGL((k_cycle_part<BF16, VEC>), dim3((unsigned)B * p.nch + rb + (unsigned)n_part),
+                       dim3(kPartNT), 0, st, sa, kv, rb, s_part);
+    hipLaunchKernelGGL((k_cycle_pick<BF16, VEC>), dim3((unsigned)B + (unsigned)n_pick), dim3(kPickNT),
+                       0, st, sa, s_pick);
     if (sa.prec && K > 0) {
         // acceptance analytics: residual mass of every proposal position, then beta and E[A]
         hipLaunchKernelGGL((k_accept_part<BF16, VEC>), dim3((unsigned)K * p.nch), dim3(kPartNT), 0,
@@ -230,11 +326,14 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
                               p.nchunks, c, part, (const RowParams*)nullptr);
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
-    launch_cycle_tail<BF16, VEC>(kv, knew, vnew, B, K, p, aws, sa, st);
+    launch_cycle_tail<BF16, VEC>(kv, B, K, p, sa, scatter_plan(kv, knew, vnew, aws, B, N),
+                                 kFusedSplit, st);
 }
 
-// The early-exit cycle: one statistics launch per position (temperature only, scalar or
-// per request), then the same decision, draw and cache launches.
+// The early-exit cycle (temperature only, scalar or per request): one statistics launch
+// for each of positions 0 .. kEarlyCut - 1, then one for every later row of the requests
+// still live, with the K/V scatter spread over the launches after the first; then the same
+// decision, draw and cache launches.
 template <bool BF16, bool VEC>
 static void launch_cycle_early(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
                                const int* cu, int B, int K, int max_k, const WsPlan& p,
@@ -247,13 +346,28 @@ static void launch_cycle_early(const KvArgs& kv, const uint8_t* knew, const uint
                            pa, rows);
     }
     const unsigned nwg = (unsigned)B * 2u * (unsigned)p.nchunks;
+    const ScatterShare sc = scatter_plan(kv, knew, vnew, aws, B, K + B);
     if (dbg && dbg->ev_stats_begin) (void)hipEventRecord(dbg->ev_stats_begin, st);
-    for (int q = 0; q <= max_k; ++q)
-        hipLaunchKernelGGL((k_cycle_pass<BF16, VEC>), dim3(nwg + (q == 0 ? 1u : 0u)), dim3(kNT), 0,
-                           st, kv, cu, B, K + B, aws, sa, part, q);
+    int done = 0;
+    for (int q = 0; q <= max_k && q < kEarlyCut; ++q) {
+        const int share = q == 1 ? std::min(sc.ns, pct_of(sc.ns, kEarlySplit.pass_pct)) : 0;
+        hipLaunchKernelGGL((k_cycle_pass<BF16, VEC>),
+                           dim3(nwg + (q == 0 ? 1u : 0u) + (unsigned)share), dim3(kNT), 0, st, kv,
+                           cu, B, K + B, aws, sa, part, q, (int)nwg,
+                           scatter_slice(sc, done, share));
+        done += share;
+    }
+    if (max_k >= kEarlyCut) {
+        const unsigned tw = (unsigned)B * (unsigned)p.nchunks;
+        const int share = std::min(sc.ns - done, pct_of(sc.ns, kEarlySplit.tail_pct));
+        hipLaunchKernelGGL((k_cycle_tail<BF16, VEC>), dim3(tw + (unsigned)share), dim3(kNT), 0, st,
+                           sa, part, kEarlyCut, (int)tw, scatter_slice(sc, done, share));
+        done += share;
+    }
     if (dbg && dbg->ev_stats_end) (void)hipEventRecord(dbg->ev_stats_end, st);
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
-    launch_cycle_tail<BF16, VEC>(kv, knew, vnew, B, K, p, aws, sa, st);
+    launch_cycle_tail<BF16, VEC>(kv, B, K, p, sa, scatter_slice(sc, done, sc.ns - done),
+                                 kEarlySplit, st);
 }
 
 }  // namespace sd

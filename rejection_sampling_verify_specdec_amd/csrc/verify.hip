@@ -108,6 +108,13 @@ __global__ __launch_bounds__(kNT) void k_pass(SampleArgs a, RowPartial* __restri
     pass_body<BF16, VEC>(a, part, p, blockIdx.x);
 }
 
+// Early exit, the last statistics launch: every row from position p on of the requests
+// still live at p
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_tail(SampleArgs a, RowPartial* __restrict__ part, int p) {
+    tail_body<BF16, VEC>(a, part, p, blockIdx.x);
+}
+
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
                        float top_p, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
@@ -119,14 +126,18 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (early) {
-        // one launch per position; the events bracket them all
+        // one launch per position up to kEarlyCut, then one for the rest; the events
+        // bracket them all
         if (p.pr_plain)
             hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
                                pa, rows);
         if (e0) (void)hipEventRecord(e0, st);
-        for (int q = 0; q <= max_k; ++q)
+        for (int q = 0; q <= max_k && q < kEarlyCut; ++q)
             hipLaunchKernelGGL((k_pass<BF16, VEC>), dim3((unsigned)B * 2u * (unsigned)p.nchunks),
                                dim3(kNT), 0, st, sa, part, q);
+        if (max_k >= kEarlyCut)
+            hipLaunchKernelGGL((k_tail<BF16, VEC>), dim3((unsigned)B * (unsigned)p.nchunks),
+                               dim3(kNT), 0, st, sa, part, kEarlyCut);
         if (e1) (void)hipEventRecord(e1, st);
     } else if (p.pr_plain) {
         hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,

@@ -1256,19 +1256,20 @@ SD_DEV double kept_prob(float z, float m, double S, float thr, double cd) {
 }
 
 // Weight of token x for the draw: max(0, p(x) - q(x)) after a rejection (RESID), p(x)
-// for the bonus; p and q in fp64 from fp32 exponentials of the same form the statistics
-// used. TOPK masks tokens below the rows' thresholds.
+// for the bonus; p and q from fp32 exponentials of the form the statistics used, scaled
+// by the rows' normalizers, in fp32 (about 2e-7 relative to p; a residual mass this path
+// cannot resolve goes to the precise draw). TOPK masks tokens below the rows' thresholds.
 template <bool RESID, bool TOPK>
-SD_DEV double weight_t(float zt, float zd, const Decision& r, float c) {
-    double pt = (double)__builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * r.al_t;
-    if (TOPK && !(zt >= r.thr_t)) pt = 0.0;
+SD_DEV float weight_t(float zt, float zd, const Decision& r, float c) {
+    float pt = __builtin_amdgcn_exp2f(fmaf(zt, c, -r.mc_t)) * (float)r.al_t;
+    if (TOPK && !(zt >= r.thr_t)) pt = 0.f;
     if (!RESID) return pt;
-    double pd = (double)__builtin_amdgcn_exp2f(fmaf(zd, c, -r.mc_d)) * r.al_d;
-    if (TOPK && !(zd >= r.thr_d)) pd = 0.0;
-    return fmax(pt - pd, 0.0);
+    float pd = __builtin_amdgcn_exp2f(fmaf(zd, c, -r.mc_d)) * (float)r.al_d;
+    if (TOPK && !(zd >= r.thr_d)) pd = 0.f;
+    return fmaxf(pt - pd, 0.f);
 }
 
-SD_DEV double weight(float zt, float zd, const Decision& r, float c, bool resid) {
+SD_DEV float weight(float zt, float zd, const Decision& r, float c, bool resid) {
     if (resid) return weight_t<true, true>(zt, zd, r, c);
     return weight_t<false, true>(zt, zd, r, c);
 }
@@ -1557,14 +1558,14 @@ SD_DEV void chunk_weight_sums_t(const uint8_t* trow, const uint8_t* drow, int V,
                 qd[2] = rd[g].z;
                 qd[3] = rd[g].w;
             }
-            double acc = 0.0;
+            float acc = 0.f;               // the thread's 8 weights in fp32, in order
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 acc += weight_t<RESID, TOPK>(bf16_lo(qt[j]), bf16_lo(qd[j]), r, c);
                 acc += weight_t<RESID, TOPK>(bf16_hi(qt[j]), bf16_hi(qd[j]), r, c);
             }
-            acc = wave_sum(acc);
-            if (l == 0) red[g * NW + w] = acc;
+            const double sum = wave_sum((double)acc);
+            if (l == 0) red[g * NW + w] = sum;
         }
     } else {
         float zt[kSSub][8], zd[kSSub][8];
@@ -1585,11 +1586,11 @@ SD_DEV void chunk_weight_sums_t(const uint8_t* trow, const uint8_t* drow, int V,
         }
 #pragma unroll
         for (int g = 0; g < kSSub; ++g) {
-            double acc = 0.0;
+            float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc += weight_t<RESID, TOPK>(zt[g][e], zd[g][e], r, c);
-            acc = wave_sum(acc);
-            if (l == 0) red[g * NW + w] = acc;
+            const double sum = wave_sum((double)acc);
+            if (l == 0) red[g * NW + w] = sum;
         }
     }
     __syncthreads();
@@ -1625,19 +1626,59 @@ SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Early exit (an opt-in cycle): the statistics run position by position, one launch per
-// position p = 0..max_k. Workgroup (b, side, chunk) of launch p reads its chunk of request
-// b's target row p (side 0) or draft row p (side 1, only while p < k_b) if every proposal
-// before p passed the accept test with a valid uniform and token. That test is evaluated
-// again here from the partials the earlier launches wrote, with the decision's own
-// arithmetic (combine_partials, kept_prob, u * Q < P), so both agree on the rows that
-// were read. Rows past a request's first rejection are never read; the decision, the
-// draw and the cache steps then run as in the full cycle. Temperature only, scalar or per
-// request (no top-k / top-p): partials are per chunk.
+// Early exit (an opt-in cycle): the statistics of the first positions run one launch per
+// position, then one more launch reads every remaining row of each request still live.
+// Workgroup (b, side, chunk) of position launch p reads its chunk of request b's target
+// row p (side 0) or draft row p (side 1, only while p < k_b) if every proposal before p
+// passed the accept test with a valid uniform and token. That test is evaluated again here
+// from the partials the earlier launches wrote, with the decision's own arithmetic
+// (combine_partials, kept_prob, u * Q < P), so both agree on the rows that were read. The
+// last launch (tail_body) does the same test at its position and then reads the chunk of
+// every later row of the request, ahead of knowing whether the decision needs them: one
+// launch instead of one per position, for the few requests still live. No row past a
+// rejection at an earlier position is read; the decision, the draw and the cache steps
+// then run as in the full cycle. Temperature only, scalar or per request (no top-k /
+// top-p): partials are per chunk.
 // ---------------------------------------------------------------------------------------
+
+// positions 0 .. kEarlyCut - 1 one launch each, then one launch for every later row of the
+// requests still live
+constexpr int kEarlyCut = SPECDEC_EARLY_EXIT_SEQUENTIAL;
+static_assert(kEarlyCut >= 1, "position 0 is read for every request first");
+
+// Whether request b (first proposal lo, k_b = k) is live at position p >= 1, given that it
+// was live at p - 1 (the flag the launch for p - 1 left) and p <= k: proposal p - 1 has a
+// valid uniform and token and passes u * Q < P. Threads 0 and 1 of the workgroup call:
+// thread 0 evaluates the target row, thread 1 the draft row; thread 0's result counts.
+template <bool BF16>
+SD_DEV bool live_test(const SampleArgs& a, const RowPartial* part, int p, int b, int lo) {
+    using Lt = Layout<BF16, true>;
+    const int lane = threadIdx.x;
+    const int nchunks = a.nparts;
+    const int rows_t = a.K + a.B;
+    const int i = lo + p - 1;
+    const int y = a.tokens[i];
+    const double u = (double)a.u_acc[i];
+    bool live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
+    if (live) {
+        // the request's log2(e) / T, as the decision takes it
+        const double cd = (double)(a.rpar ? a.rpar[lo + b].c : a.c);
+        const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
+        const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
+                                        : a.dft + (size_t)i * a.V * Lt::ES;
+        float m;
+        double S;
+        int nk;
+        combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
+        const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
+        const double Q = __shfl(pr, 1, kWave);
+        live = u * Q < pr;                           // lane 0's: P = its own
+    }
+    return live;
+}
+
 template <bool BF16, bool VEC>
 SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
-    using Lt = Layout<BF16, true>;
     __shared__ int s_live;
     const int nchunks = a.nparts;
     const int b = w / (2 * nchunks);
@@ -1653,11 +1694,6 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
         return;
     }
     if (threadIdx.x < 2) {
-        // lane 0 takes the target row of proposal p-1, lane 1 its draft row
-        const int lane = threadIdx.x;
-        // live at p: proposals 0..p-1 all passed. The previous launch left the flag for
-        // 0..p-2 (live[(p-1) & 1], 0 also for malformed offsets or invalid parameters);
-        // proposal p-1 is tested here from its rows' partials.
         bool live;
         if (p == 0) {
             live = !(a.cu[0] != 0 || a.cu[a.B] != a.K || k < 0 || k > a.max_k || lo < 0 ||
@@ -1665,27 +1701,9 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
             // a request with invalid parameters fails in the decision without its rows
             if (live && a.rpar) live = !(a.rpar[lo + b].flags & kRpBad);
         } else {
-            // live through proposal p-2 and p <= k (checked above): test proposal p-1
-            const int i = lo + p - 1;
-            const int y = a.tokens[i];
-            const double u = (double)a.u_acc[i];
-            live = u >= 0.0 && u < 1.0 && y >= 0 && y < a.V;
-            if (live) {
-                // the request's log2(e) / T, as the decision takes it
-                const double cd = (double)(a.rpar ? a.rpar[lo + b].c : a.c);
-                const size_t prow = lane == 0 ? (size_t)(i + b) : (size_t)(rows_t + i);
-                const uint8_t* zrow = lane == 0 ? a.tgt + (size_t)(i + b) * a.V * Lt::ES
-                                                : a.dft + (size_t)i * a.V * Lt::ES;
-                float m;
-                double S;
-                int nk;
-                combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
-                const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
-                const double Q = __shfl(pr, 1, kWave);
-                live = u * Q < pr;                   // lane 0's: P = its own
-            }
+            live = live_test<BF16>(a, part, p, b, lo);
         }
-        if (lane == 0) {
+        if (threadIdx.x == 0) {
             // one workgroup per request leaves the flag for the next launch (every launch
             // writes every request's flag, so none is stale)
             if (side == 0 && chunk == 0) a.live[(p & 1) * a.B + b] = live ? 1 : 0;
@@ -1697,6 +1715,33 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
     const int row = side == 0 ? lo + b + p : rows_t + lo + p;
     row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part, row * nchunks + chunk,
                               a.rpar);
+}
+
+// The last statistics launch, at position p >= 1: workgroup (b, chunk) reads its chunk of
+// every target row p .. k_b and draft row p .. k_b - 1 of request b if b is live at p.
+template <bool BF16, bool VEC>
+SD_DEV void tail_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+    __shared__ int s_live;
+    const int nchunks = a.nparts;
+    const int b = w / nchunks;
+    const int chunk = w - b * nchunks;
+    const int rows_t = a.K + a.B;
+    const int lo = a.cu[b], hi = a.cu[b + 1];
+    const int k = hi - lo;
+    if (p > k || a.live[((p - 1) & 1) * a.B + b] == 0) return;
+    if (threadIdx.x < 2) {
+        const bool live = live_test<BF16>(a, part, p, b, lo);
+        if (threadIdx.x == 0) s_live = live;
+    }
+    __syncthreads();
+    if (!s_live) return;
+    for (int i = p; i <= k; ++i) {
+        row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part,
+                                  (lo + b + i) * nchunks + chunk, a.rpar);
+        if (i < k)
+            row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part,
+                                      (rows_t + lo + i) * nchunks + chunk, a.rpar);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1929,6 +1974,68 @@ SD_DEV void part_body(const SampleArgs& a, int b, int chunk) {
                                      a.wsum + ((size_t)b * a.nch + chunk) * kSSub);
 }
 
+// The sub-chunk sums s[0 .. n) of a draw (n <= 4 * NT, thread i owning entries 4i .. 4i+3):
+// their total W, then the sub-chunk q holding t = u * W, the first whose running sum
+// through it exceeds t (the last non-empty one if rounding leaves none), and the running
+// sum before it. Fixed association order; every thread gets the results. `red` holds
+// NT / 64 doubles, `redi` NT / 64 ints.
+template <int NT>
+SD_DEV double subchunk_total(const double* s, int n, double* red) {
+    double v = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int q = threadIdx.x * 4 + j;
+        if (q < n) v += s[q];
+    }
+    return block_sum<NT>(v, red);
+}
+
+template <int NT>
+SD_DEV int subchunk_locate(const double* s, int n, double t, double* red, int* redi,
+                           double* base_out) {
+    __shared__ double s_base;
+    double v[4], run = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int q = threadIdx.x * 4 + j;
+        v[j] = q < n ? s[q] : 0.0;
+        run += v[j];
+    }
+    double tot;
+    double C = block_excl_scan_d<NT>(run, red, &tot);
+    int mine = 0x7fffffff, lastpos = -1;
+    double cmine = 0.0, clast = 0.0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int q = threadIdx.x * 4 + j;
+        if (mine == 0x7fffffff && C + v[j] > t) {
+            mine = q;
+            cmine = C;
+        }
+        if (v[j] > 0.0) {
+            lastpos = q;
+            clast = C;
+        }
+        C += v[j];
+    }
+    int q = block_min_i<NT>(mine, redi);
+    if (q != 0x7fffffff) {
+        if (mine == q) s_base = cmine;
+    } else {
+        q = block_max_i<NT>(lastpos, redi);
+        if (q < 0) {
+            q = 0;
+            if (threadIdx.x == 0) s_base = 0.0;
+        } else if (lastpos == q) {
+            s_base = clast;
+        }
+    }
+    __syncthreads();
+    *base_out = s_base;
+    __syncthreads();
+    return q;
+}
+
 // Sampling, part 2: workgroup b turns the sub-chunk sums into W, finds the sub-chunk holding
 // t = u * W and scans it in ascending token order (each thread owns 8 consecutive tokens,
 // an exclusive scan over threads gives each its running sum) for the smallest x with
@@ -1943,8 +2050,7 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     __shared__ double red[kSSub * NW];
     __shared__ int redi[NW];
     __shared__ double s_cs[kSMaxChunks * kSSub];
-    __shared__ double s_W, s_base, s_wpick;
-    __shared__ int s_sub;
+    __shared__ double s_wpick;
     const int tid = threadIdx.x;
     Decision r = a.rec[b];
     if (r.mode == MODE_NONE) return;
@@ -1956,17 +2062,14 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
     const uint8_t* trow = a.tgt + (size_t)r.row_t * a.V * Lt::ES;
     const uint8_t* drow = a.dft + (size_t)r.row_d * a.V * Lt::ES;
     const int nch = a.nch, nsub = nch * kSSub;
+    static_assert(kSMaxChunks * kSSub <= 4 * NT, "four sub-chunk sums per thread");
     bool precise = r.mode == MODE_PRECISE;
+    double W = 0.0;
     if (!precise) {
         for (int q = tid; q < nsub; q += NT) s_cs[q] = a.wsum[(size_t)b * nsub + q];
         __syncthreads();
-        if (tid == 0) {
-            double W = 0.0;
-            for (int q = 0; q < nsub; ++q) W += s_cs[q];
-            s_W = W;
-        }
-        __syncthreads();
-        precise = resid && !(s_W >= kPreciseBelow);
+        W = subchunk_total<NT>(s_cs, nsub, red);
+        precise = resid && !(W >= kPreciseBelow);
     }
     PreciseRow P;
     double wscale = 1.0;      // reported W = the sum of the weights times wscale
@@ -1981,59 +2084,43 @@ SD_DEV void pick_body(const SampleArgs& a, int b) {
         const double A = precise_lambda<BF16, VEC, NT>(trow, drow, a.V, nch, P, red);
         wscale = 1.0 / A;
         precise_sums<BF16, VEC, NT>(trow, drow, a.V, nch, P, true, red, s_cs);
-        if (tid == 0) {
-            double W = 0.0;
-            for (int q = 0; q < nsub; ++q) W += s_cs[q];
-            s_W = W;
-        }
-        __syncthreads();
-        if (!(s_W > 0.0)) {
+        W = subchunk_total<NT>(s_cs, nsub, red);
+        if (!(W > 0.0)) {
             // the rows agree: no residual mass, draw the replacement from p_j instead
             resid = false;
             r.flags |= SPECDEC_ERR_ZFALLBACK;
             precise_sums<BF16, VEC, NT>(trow, drow, a.V, nch, P, false, red, s_cs);
-            if (tid == 0) {
-                double W = 0.0;
-                for (int q = 0; q < nsub; ++q) W += s_cs[q];
-                s_W = W;
-                atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
-            }
-            __syncthreads();
+            W = subchunk_total<NT>(s_cs, nsub, red);
+            if (tid == 0) atomicOr(a.err_word, SPECDEC_ERR_ZFALLBACK);
         }
     }
-    const double W = s_W;
     const double t = (double)r.u * W;
-    if (tid == 0) {
-        double C = 0.0;
-        int q = 0;
-        for (; q < nsub; ++q) {
-            if (C + s_cs[q] > t) break;
-            C += s_cs[q];
-        }
-        if (q == nsub) {   // unreachable while t < W; keep the last non-empty sub-chunk
-            q = nsub - 1;
-            while (q > 0 && !(s_cs[q] > 0.0)) --q;
-            C = 0.0;
-            for (int i = 0; i < q; ++i) C += s_cs[i];
-        }
-        s_sub = q;
-        s_base = C;
-    }
-    __syncthreads();
-    const int i0 = s_sub * kSSubLen + tid * 8;
+    double base;
+    const int sub = subchunk_locate<NT>(s_cs, nsub, t, red, redi, &base);
+    const int i0 = sub * kSSubLen + tid * 8;
     float t8[8], d8[8];
     load8<BF16, VEC>(trow, a.V, i0, t8);
     if (resid) load8<BF16, VEC>(drow, a.V, i0, d8);
     double w[8];
     double run = 0.0;
+    if (precise) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float zd = resid ? d8[e] : -INFINITY;
-        w[e] = precise ? precise_weight(t8[e], zd, P, resid) : weight(t8[e], zd, r, r.c, resid);
-        run += w[e];
+        for (int e = 0; e < 8; ++e) {
+            w[e] = precise_weight(t8[e], resid ? d8[e] : -INFINITY, P, resid);
+            run += w[e];
+        }
+    } else {
+        float run32 = 0.f;         // the thread's 8 weights as the chunk sums added them
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float wf = weight(t8[e], resid ? d8[e] : -INFINITY, r, r.c, resid);
+            w[e] = (double)wf;
+            run32 += wf;
+        }
+        run = (double)run32;
     }
     double tot;
-    double C = s_base + block_excl_scan_d<NT>(run, red, &tot);
+    double C = base + block_excl_scan_d<NT>(run, red, &tot);
     int mine = 0x7fffffff, lastpos = -1;
     double wmine = 0.0, wlast = 0.0;
 #pragma unroll
