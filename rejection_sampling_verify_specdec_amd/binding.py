@@ -137,11 +137,14 @@ class KvContigCacheStruct(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the HIP library once; raise if it was not built."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the HIP library once; raise if it was not built. The path defaults to the in-tree
+    build; SPECDEC_LIBRARY names another build of the same sources (the host-sanitized one
+    the CPU tests load)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("SPECDEC_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build it with `python -m rejection_sampling_verify_specdec_amd.build`")

@@ -216,3 +216,12 @@ def test_static_cycle_refuses_calls_larger_than_its_scratch(lib):
                                   None, None, None, None, None)
     assert st == binding.SPECDEC_ESCRATCH
     assert "static" in binding.status_string(st)
+
+
+def test_the_library_loaded_is_the_one_asked_for(lib):
+    # under the host-sanitizer test, SPECDEC_LIBRARY names the sanitized build
+    want = os.environ.get("SPECDEC_LIBRARY")
+    if want:
+        assert os.path.samefile(lib._name, want)
+        data = open(want, "rb").read().decode("latin-1")
+        assert "__asan_init" in data and "__ubsan_handle" in data
