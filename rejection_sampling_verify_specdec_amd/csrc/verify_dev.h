@@ -428,6 +428,17 @@ SD_DEV uint32_t reg_min(uint32_t a, uint32_t b) {
     else
         return a < b ? a : b;
 }
+// the inverse of reg_keys: the raw bits of one register's two bf16 (or one fp32) back from
+// their keys (a key with its top bit set is a non-negative value)
+template <bool BF16>
+SD_DEV uint32_t reg_raw(uint32_t k) {
+    if constexpr (BF16) {
+        const sd_i16x2 s = __builtin_bit_cast(sd_i16x2, k) >> (sd_i16x2){15, 15};
+        return k ^ (~__builtin_bit_cast(uint32_t, s) | 0x80008000u);
+    } else {
+        return k ^ (~uint32_t((int)k >> 31) | 0x80000000u);
+    }
+}
 template <bool BF16>
 SD_DEV float key_to_float(uint32_t k) {
     if constexpr (BF16) {
@@ -584,13 +595,16 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk, const ChunkSe
             for (int g = 0; g < 4; ++g) {
                 float e[NR / 4 * EPR];
 #pragma unroll
-                for (int w = 0; w < NR / 4; ++w)
+                for (int w = 0; w < NR / 4; ++w) {
+                    // the values back from the keys, both halves of a register at once
+                    const uint32_t raw = reg_raw<BF16>(r[g * (NR / 4) + w]);
 #pragma unroll
                     for (int h = 0; h < EPR; ++h) {
-                        const uint32_t k = (r[g * (NR / 4) + w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
-                        e[w * EPR + h] =
-                            __builtin_amdgcn_exp2f(fmaf(key_to_float<BF16>(k), sel.c, -mc));
+                        const float z = __uint_as_float(
+                            BF16 ? (h ? raw & 0xffff0000u : raw << 16) : raw);
+                        e[w * EPR + h] = __builtin_amdgcn_exp2f(fmaf(z, sel.c, -mc));
                     }
+                }
                 gs[g] = tree_sum(e);
             }
             sw = wave_sum((double)tree_sum(gs)) * exp2(-(double)emc);
@@ -623,7 +637,6 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk, const ChunkSe
 
     // 3. candidates (key >= t0): each wave appends to its own list, ballot-compacted in
     //    LDS, then copied out with coalesced stores
-    const uint64_t below_me = __lanemask_lt();
     uint32_t* lst = s_list + wv * a.wcap;
     int woff = 0;
 #pragma unroll
@@ -634,7 +647,9 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk, const ChunkSe
             const bool f = k >= t0;
             const uint64_t bal = __ballot(f);
             if (bal) {
-                const int pos = woff + __popcll(bal & below_me);
+                const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                           uint32_t(bal >> 32),
+                                           __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u));
                 if (f && pos < a.wcap)
                     lst[pos] = BF16 ? (k << 16) | (uint32_t)(token(w, h) - c0) : k;
                 woff += __popcll(bal);
