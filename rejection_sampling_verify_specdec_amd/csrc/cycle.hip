@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __re
 }
 
 template <bool BF16, bool PR, int NT>
-__global__ __launch_bounds__(NT) void k_cycle_topk_merge(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_cycle_topk_merge(TopkArgs a) {
     if constexpr (PR) merge_pr_body<BF16, NT>(a, blockIdx.x);
     else topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
 }
@@ -299,12 +299,8 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
                            pa, rows);
         hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 2>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kTkNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
-        if (p.wide_merge)
-            hipLaunchKernelGGL((k_cycle_topk_merge<BF16, true, kMergeNTp>), dim3(rows),
-                               dim3(kMergeNTp), 0, st, ta);
-        else
-            hipLaunchKernelGGL((k_cycle_topk_merge<BF16, true, kMergeNT>), dim3(rows),
-                               dim3(kMergeNT), 0, st, ta);
+        hipLaunchKernelGGL((k_cycle_topk_merge<BF16, true, kMergeNT>), dim3(rows),
+                           dim3(kMergeNT), 0, st, ta);
     } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         const unsigned nchunk_wg = ta.generic ? 0u : (unsigned)rows * p.nchunks;
@@ -314,12 +310,8 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
         else
             hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 0>), dim3(nchunk_wg + 1), dim3(kTkNT),
                                   0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
-        if (p.wide_merge)
-            hipLaunchKernelGGL((k_cycle_topk_merge<BF16, false, kMergeNTp>), dim3(rows),
-                               dim3(kMergeNTp), 0, st, ta);
-        else
-            hipLaunchKernelGGL((k_cycle_topk_merge<BF16, false, kMergeNT>), dim3(rows),
-                               dim3(kMergeNT), 0, st, ta);
+        hipLaunchKernelGGL((k_cycle_topk_merge<BF16, false, kMergeNT>), dim3(rows),
+                           dim3(kMergeNT), 0, st, ta);
     } else {
         hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,

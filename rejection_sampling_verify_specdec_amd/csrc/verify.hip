@@ -16,9 +16,11 @@
 //                 that can be in the row's top-k set (a bound from its per-thread maxima);
 //                 for top-p alone, the chunk's top k_c tokens plus its max and exp-sum.
 //   k_topk_merge  one workgroup per row: exact top-k threshold over the chunks'
-//                 candidates, then the nucleus boundary (top-p) from fixed-point mass
-//                 histograms, max, kept count and kept-set sum; rows the candidates do not
-//                 cover take full passes over the row.
+//                 candidates, then the nucleus boundary (top-p) in fixed-point mass, both
+//                 from the token count on each key when the candidates' keys span fewer
+//                 than 1024 values (bf16 rows), else from digit histograms; max, kept
+//                 count and kept-set sum; rows the candidates do not cover take full passes
+//                 over the row.
 //   k_decide      one workgroup per request: combines the row partials in fp64, evaluates
 //                 p_i(y_i), q_i(y_i) in fp64 and the accept test u * q < p left to right,
 //                 finds the first rejection, publishes the accepted tokens and stores the
@@ -67,7 +69,7 @@ __global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
 }
 
 template <bool BF16, int NT>
-__global__ __launch_bounds__(NT) void k_topk_merge(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_topk_merge(TopkArgs a) {
     topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
 }
 
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kTkNT) void k_chunks_pr(TopkArgs a) {
 }
 
 template <bool BF16, int NT>
-__global__ __launch_bounds__(NT) void k_merge_pr(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_merge_pr(TopkArgs a) {
     merge_pr_body<BF16, NT>(a, blockIdx.x);
 }
 
@@ -151,10 +153,7 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                            rows);
         hipExtLaunchKernelGGL((k_chunks_pr<BF16, VEC>), dim3((unsigned)rows * p.nchunks),
                               dim3(kTkNT), 0, st, e0, e1, 0, ta);
-        if (p.wide_merge)
-            hipLaunchKernelGGL((k_merge_pr<BF16, kMergeNTp>), dim3(rows), dim3(kMergeNTp), 0, st, ta);
-        else
-            hipLaunchKernelGGL((k_merge_pr<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st, ta);
+        hipLaunchKernelGGL((k_merge_pr<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st, ta);
     } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         if (!ta.generic) {
@@ -168,12 +167,8 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
                                       0, ta);
             e0 = e1 = nullptr;
         }
-        if (p.wide_merge)
-            hipExtLaunchKernelGGL((k_topk_merge<BF16, kMergeNTp>), dim3(rows), dim3(kMergeNTp), 0,
-                                  st, e0, e1, 0, ta);
-        else
-            hipExtLaunchKernelGGL((k_topk_merge<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st,
-                                  e0, e1, 0, ta);
+        hipExtLaunchKernelGGL((k_topk_merge<BF16, kMergeNT>), dim3(rows), dim3(kMergeNT), 0, st,
+                              e0, e1, 0, ta);
     } else {
         hipExtLaunchKernelGGL((k_row_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks), dim3(kNT),
                               0, st, e0, e1, 0, tgt, dft, K + B, V, p.nchunks, c, part,

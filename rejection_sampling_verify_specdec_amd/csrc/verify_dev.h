@@ -229,12 +229,12 @@ SD_DEV float key2f(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// (hist: 256 u32 of LDS)
 template <bool BF16, int NT>
 SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __restrict__ dft,
                            int rows_t, int V, int top_k, float c, RowPartial* __restrict__ part,
-                           float* __restrict__ row_thr, int row) {
+                           float* __restrict__ row_thr, int row, unsigned* hist) {
     constexpr int ES = BF16 ? 2 : 4;
-    __shared__ unsigned hist[256];
     __shared__ float redf[NT / kWave];
     __shared__ double redd[NT / kWave];
     __shared__ int redi[NT / kWave];
@@ -332,8 +332,7 @@ SD_DEV void topk_rows_body(const uint8_t* __restrict__ tgt, const uint8_t* __res
 // ---------------------------------------------------------------------------------------
 constexpr int kTkNT = kNT;         // threads of a chunk workgroup
 constexpr int kTkRegs = kVPT * 4;  // key registers per thread (the chunk's 16-byte vectors)
-constexpr int kMergeNT = 128;      // threads of a merge workgroup (candidates only)
-constexpr int kMergeNTp = 256;     // with top-p alone: rows may need passes over the row
+constexpr int kMergeNT = 128;      // threads of a merge workgroup
 constexpr int kTkMaxK = 4 * kTkNT; // largest top_k of the chunked select
 constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
@@ -803,22 +802,72 @@ SD_DEV void topp_rows_body(const TopkArgs& a, int row, float m, float thr_lo, fl
     }
 }
 
+// Bins 0 .. NB-1 of token counts in descending key order, bin i weighing wt(i, count) (an
+// exact integer: the count itself, or the count times the fixed-point mass of the bin's
+// key): the first bin at which the running weight reaches need (frac > 0: frac times the
+// total weight). Returns NB when the total falls short. All NT threads call; red holds
+// NT / 64 u64 of LDS; the caller synchronizes before it writes cnt again.
+template <int NT, int NB, class Wt>
+SD_DEV int first_bin_reaching(const unsigned* cnt, Wt wt, double frac, double need,
+                              unsigned long long* red, int* s_bin) {
+    constexpr int BPT = NB / NT;
+    static_assert(BPT * NT == NB, "whole bins per thread");
+    const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
+    unsigned long long own = 0ull, bm[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const unsigned n = cnt[tid * BPT + j];
+        bm[j] = n ? wt(tid * BPT + j, n) : 0ull;
+        own += bm[j];
+    }
+    unsigned long long x = own;                          // inclusive scan over the threads
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long y = __shfl_up(x, o, kWave);
+        if (l >= o) x += y;
+    }
+    if (l == kWave - 1) red[w] = x;
+    if (tid == 0) *s_bin = NB;
+    __syncthreads();
+    unsigned long long before = x - own, total = 0ull;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+        before += i < w ? red[i] : 0ull;
+        total += red[i];
+    }
+    const double nd = frac > 0.0 ? frac * (double)total : need;
+    if ((double)(before + own) >= nd && (double)before < nd) {
+        unsigned long long acc = before;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            acc += bm[j];
+            if ((double)acc >= nd) {
+                *s_bin = tid * BPT + j;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    return *s_bin;
+}
+
 // Top-p alone, bf16, when the candidates' complete upper set (keys >= lo) is short of the
 // nucleus: every bf16 key is one logit value, so one pass that counts the row's tokens on
 // each of the 1024 keys below lo finds the boundary exactly, each key's mass being its
 // count times one exponential (the same fixed-point mass the per-token sums use), and the
 // kept sum follows from the counts without another pass. keys[0 .. total) are the row's
 // candidate entries (key << 16 | offset); need is the nucleus mass in fixed point, in
-// units of exp2(z c - mc). Returns false, having written nothing, when the boundary lies
-// further below (the caller then runs the full-row passes).
+// units of exp2(z c - mc); s_cnt: kToppBelow u32 of LDS (bin i: key lo - 1 - i). Returns
+// false, having written nothing, when the boundary lies further below (the caller then runs
+// the full-row passes).
 constexpr int kToppBelow = 1024;
 template <int NT>
 SD_DEV bool topp_below_bf16(const TopkArgs& a, int row, float m, float mc, float emc, float c,
-                            uint32_t lo, double need, const uint32_t* keys, int total) {
+                            uint32_t lo, double need, const uint32_t* keys, int total,
+                            unsigned* s_cnt) {
     using Kt = TopkKeys<true>;
     constexpr int BPT = kToppBelow / NT;
     static_assert(BPT * NT == kToppBelow, "whole bins per thread");
-    __shared__ unsigned s_cnt[kToppBelow];              // bin i: key lo - 1 - i
     __shared__ unsigned long long s_red[NT / kWave];
     __shared__ double redd[NT / kWave];
     __shared__ int redi[NT / kWave];
@@ -923,20 +972,25 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
     constexpr int LPT = kTkMaxChunks > NT ? kTkMaxChunks / NT : 1;   // lists per thread
     constexpr int UNR = 8;                              // candidate loads in flight per thread
     using Kt = TopkKeys<BF16>;
-    static_assert(kKeptCap >= 256, "the histogram and the kept-token list share LDS");
-    __shared__ __attribute__((aligned(16))) uint32_t s_u32[kKeptCap];   // histograms, then
-                                                                       // the kept tokens
-    unsigned* hist = s_u32;
-    uint32_t* s_ktok = s_u32;
+    // 4 KB of LDS for one use at a time: per-key token counts, the digit histograms, the
+    // count bins below the candidates, then the kept tokens and their keys
+    constexpr int kRangeBins = 1024;
+    __shared__ __attribute__((aligned(16))) uint32_t s_work[kRangeBins];
+    static_assert(kKeptCap * 6 <= kRangeBins * 4 && kToppBelow <= kRangeBins &&
+                      256 * 8 <= kRangeBins * 4, "the uses of the work area fit");
+    unsigned* hist = s_work;
+    uint32_t* s_ktok = s_work;
+    uint16_t* s_kkey = reinterpret_cast<uint16_t*>(s_work + kKeptCap);
     __shared__ int s_off[kTkMaxChunks + 1];
     __shared__ __attribute__((aligned(16))) uint32_t keys[kMergeCap];   // entries as the chunks
                                                                      // wrote them
     static_assert(kMergeCap * 4 >= kToppRowBins * 8, "the full-row nucleus histogram fits");
-    __shared__ uint16_t s_kkey[BF16 ? kKeptCap : 1];
+    static_assert(kMergeCap >= 2 * kTkMaxChunks, "the chunks' run bounds fit over the candidates");
     __shared__ int redi[NT / kWave];
     __shared__ double redd[2 * (NT / kWave)];
-    __shared__ int s_dig, s_krem, s_nk;
-    __shared__ unsigned s_kmax;
+    __shared__ unsigned long long s_red64[NT / kWave];
+    __shared__ int s_dig, s_krem, s_bin;
+    __shared__ unsigned s_kmax, s_kmin;
     // an entry's key
     auto key_of = [](uint32_t e) { return BF16 ? e >> 16 : e; };
     const bool listed = BF16 && a.kn && row < a.rows_t;
@@ -957,7 +1011,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
     if (tid == 0) {
         s_krem = sel.top_k;
         s_kmax = 0u;
-        s_nk = 0;
+        s_kmin = ~0u;
     }
     int total;
     int off = block_excl_scan_i<NT>(mine, redi, &total);
@@ -965,7 +1019,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
         if (listed && tid == 0) a.kn[row] = -1;
         // generic select (all of the row's finite tokens for top-p alone), then the nucleus
         topk_rows_body<BF16, NT>(a.tgt, a.dft, a.rows_t, a.V, sel.topp_mode == 2 ? a.V : sel.top_k,
-                                 sel.c, a.part, a.row_thr, row);
+                                 sel.c, a.part, a.row_thr, row, s_work);
         if (sel.topp_mode) {
             // the row max and validity as the select left them (tid 0 wrote them)
             if (tid == 0) {
@@ -1005,7 +1059,7 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
         }
         return lo;
     };
-    uint32_t kmax = 0u;
+    uint32_t kmax = 0u, kmin = ~0u;
     for (int e0 = 0; e0 < total; e0 += UNR * NT) {
         uint32_t v[UNR];
 #pragma unroll
@@ -1023,30 +1077,54 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
             if (e < total) {
                 keys[e] = v[u];
                 kmax = max(kmax, key_of(v[u]));
+                kmin = min(kmin, key_of(v[u]));
             }
         }
     }
-    if (kmax) atomicMax(&s_kmax, kmax);
+    // the candidates' key range (wave reductions, then one LDS atomic per wave)
+    kmax = uint32_t(wave_max_i(int(kmax ^ 0x80000000u))) ^ 0x80000000u;
+    kmin = uint32_t(wave_min_i(int(kmin ^ 0x80000000u))) ^ 0x80000000u;
+    if (tid % kWave == 0) {
+        if (kmax) atomicMax(&s_kmax, kmax);
+        atomicMin(&s_kmin, kmin);
+    }
     __syncthreads();
+    const uint32_t khi = s_kmax, klo = s_kmin;
 
-    // exact top_k-th largest candidate key, one 8-bit digit at a time (no top-k: none)
+    // exact top_k-th largest candidate key (no top-k: none). Candidates cluster on a few
+    // high digits, so histograms of digits funnel their adds into a few bins; when the
+    // candidates' keys span fewer than kRangeBins values (the rule for bf16 rows) one pass
+    // counts the tokens on each key and the key follows from the counts; else one 8-bit
+    // digit at a time
     uint32_t prefix = 0u;
+    if (sel.topp_mode != 2 && khi >= klo && khi - klo < (uint32_t)kRangeBins) {
+        for (int i = tid; i < kRangeBins; i += NT) hist[i] = 0u;
+        __syncthreads();
+        for (int i = tid; i < total; i += NT) atomicAdd(&hist[khi - key_of(keys[i])], 1u);
+        __syncthreads();
+        const int bin = first_bin_reaching<NT, kRangeBins>(
+            hist, [](int, unsigned n) { return (unsigned long long)n; }, 0.0, (double)sel.top_k,
+            s_red64, &s_bin);
+        prefix = bin < kRangeBins ? khi - (uint32_t)bin : Kt::KEY_NINF;
+        __syncthreads();
+    } else if (sel.topp_mode != 2) {
 #pragma unroll
-    for (int shift = Kt::KBITS - 8; shift >= 0 && sel.topp_mode != 2; shift -= 8) {
-        const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
-        for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-        __syncthreads();
-        for (int i = tid; i < total; i += NT) {
-            const uint32_t k = key_of(keys[i]);
-            if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+        for (int shift = Kt::KBITS - 8; shift >= 0; shift -= 8) {
+            const uint32_t hmask = shift + 8 >= Kt::KBITS ? 0u : ~0u << (shift + 8);
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < total; i += NT) {
+                const uint32_t k = key_of(keys[i]);
+                if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 0xffu], 1u);
+            }
+            __syncthreads();
+            if (tid < kWave) hist_select(hist, &s_dig, &s_krem);
+            __syncthreads();
+            prefix |= (uint32_t)s_dig << shift;
         }
-        __syncthreads();
-        if (tid < kWave) hist_select(hist, &s_dig, &s_krem);
-        __syncthreads();
-        prefix |= (uint32_t)s_dig << shift;
     }
     float thr = sel.topp_mode == 2 ? -INFINITY : key_to_float<BF16>(prefix);
-    const float m = key_to_float<BF16>(s_kmax);
+    const float m = key_to_float<BF16>(khi);
     const float mc = m * sel.c;
     const float emc = fmaf(m, sel.c, -mc);
     if (sel.topp_mode && m > -INFINITY) {
@@ -1080,23 +1158,47 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
             lo = max(lo, Kt::KEY_NINF + 1u);
             need = (double)sel.top_p * S * exp2((double)emc) * kMassFix;
         }
-        unsigned long long* h64 = reinterpret_cast<unsigned long long*>(s_u32);
         uint32_t K = lo;
-        const bool ok = nucleus_key<NT, Kt::KBITS, 8, 256>(
-            [&](auto f) {
-                for (int i = tid; i < total; i += NT) {
-                    const uint32_t k = canon(key_of(keys[i]));
-                    f(k, key_to_float<BF16>(k));
-                }
-            },
-            lo, sel.c, mc, frac, need, h64, &K);
+        bool ok = false;
+        const uint32_t chi = canon(khi);
+        if (chi >= lo && chi - lo < (uint32_t)kRangeBins) {
+            // every key is one value: the tokens on each key >= lo, then each bin's mass as
+            // its count times one exponential (the fixed-point mass of its key)
+            for (int i = tid; i < kRangeBins; i += NT) hist[i] = 0u;
+            __syncthreads();
+            for (int i = tid; i < total; i += NT) {
+                const uint32_t k = canon(key_of(keys[i]));
+                if (k >= lo) atomicAdd(&hist[chi - k], 1u);
+            }
+            __syncthreads();
+            const int bin = first_bin_reaching<NT, kRangeBins>(
+                hist,
+                [&](int i, unsigned n) {
+                    const float z = key_to_float<BF16>(chi - (uint32_t)i);
+                    return (unsigned long long)n *
+                           mass_fix(__builtin_amdgcn_exp2f(fmaf(z, sel.c, -mc)));
+                },
+                frac, need, s_red64, &s_bin);
+            ok = bin < kRangeBins;
+            K = chi - (uint32_t)bin;
+        } else if (chi >= lo) {
+            ok = nucleus_key<NT, Kt::KBITS, 8, 256>(
+                [&](auto f) {
+                    for (int i = tid; i < total; i += NT) {
+                        const uint32_t k = canon(key_of(keys[i]));
+                        f(k, key_to_float<BF16>(k));
+                    }
+                },
+                lo, sel.c, mc, frac, need, reinterpret_cast<unsigned long long*>(s_work), &K);
+        }
         if (!ok && sel.topp_mode == 2) {
             // the nucleus reaches below the candidates: for bf16 first one counting pass
             // over the keys just below them, else (or when it reaches further) full passes
             if (listed && tid == 0) a.kn[row] = -1;
             __syncthreads();
             if constexpr (BF16) {
-                if (topp_below_bf16<NT>(a, row, m, mc, emc, sel.c, lo, need, keys, total)) return;
+                if (topp_below_bf16<NT>(a, row, m, mc, emc, sel.c, lo, need, keys, total, s_work))
+                    return;
             }
             topp_rows_body<BF16, NT>(a, row, m, -INFINITY, sel.c, sel.top_p,
                                      reinterpret_cast<unsigned long long*>(keys));
@@ -1105,35 +1207,81 @@ SD_DEV void topk_merge_body(const TopkArgs& a, int row, const RowSel& sel) {
         thr = key_to_float<BF16>(ok ? max(K, lo) : lo);
         __syncthreads();                    // the histogram memory holds kept tokens next
     }
+    // kept count and exp-sum; thread t takes the candidates [t q, t q + q), so that a
+    // workgroup scan of the kept counts lists the kept tokens in candidate order
+    const int q = (total + NT - 1) / NT;
+    const int i0 = min(tid * q, total), i1 = min(i0 + q, total);
+    auto is_kept = [&](float z) { return z >= thr && z > -INFINITY; };
+    constexpr int KU = 4;                   // candidate reads in flight per thread
     float acc = 0.f;
     int kept = 0;
-    for (int i = tid; i < total; i += NT) {
-        const uint32_t k = key_of(keys[i]);
-        const float z = key_to_float<BF16>(k);
-        if (z >= thr && z > -INFINITY) {
-            acc += __builtin_amdgcn_exp2f(fmaf(z, sel.c, -mc));
-            ++kept;
-            if (listed) {
-                const int pos = atomicAdd(&s_nk, 1);
-                if (pos < kKeptCap) {
-                    s_ktok[pos] = (uint32_t)list_of(i) * (uint32_t)Layout<BF16, true>::CH +
-                                  (keys[i] & 0xffffu);
-                    s_kkey[pos] = (uint16_t)k;
-                }
+    for (int i = i0; i < i1; i += KU) {
+        uint32_t e[KU];
+#pragma unroll
+        for (int u = 0; u < KU; ++u) e[u] = i + u < i1 ? keys[i + u] : 0u;
+#pragma unroll
+        for (int u = 0; u < KU; ++u) {
+            const float z = key_to_float<BF16>(key_of(e[u]));
+            if (i + u < i1 && is_kept(z)) {
+                acc += __builtin_amdgcn_exp2f(fmaf(z, sel.c, -mc));
+                ++kept;
             }
         }
     }
     if (listed) {
-        // the kept tokens in ascending order: each one's rank among them
-        __syncthreads();
-        const int nk = s_nk;
+        // the kept tokens in ascending order. Candidate order is chunk order, so the kept
+        // tokens of one chunk form one run and the runs ascend: a token's rank is the start
+        // of its chunk's run plus its rank within the run
+        constexpr uint32_t CH = Layout<BF16, true>::CH;
+        int nk;
+        int pos = block_excl_scan_i<NT>(kept, redi, &nk);
         if (nk <= kKeptCap) {
-            for (int i = tid; i < nk; i += NT) {
-                const uint32_t x = s_ktok[i];
-                int rank = 0;
-                for (int j = 0; j < nk; ++j) rank += s_ktok[j] < x;
+            for (int i = i0; i < i1; i += KU) {
+                uint32_t e[KU];
+#pragma unroll
+                for (int u = 0; u < KU; ++u) e[u] = i + u < i1 ? keys[i + u] : 0u;
+#pragma unroll
+                for (int u = 0; u < KU; ++u) {
+                    const uint32_t k = key_of(e[u]);
+                    if (i + u < i1 && is_kept(key_to_float<BF16>(k))) {
+                        s_ktok[pos] = (uint32_t)list_of(i + u) * CH + (e[u] & 0xffffu);
+                        s_kkey[pos] = (uint16_t)k;
+                        ++pos;
+                    }
+                }
+            }
+        }
+        __syncthreads();                    // the candidates are no longer read
+        if (nk <= kKeptCap) {
+            int* run_lo = reinterpret_cast<int*>(keys);         // per chunk: its run's bounds
+            int* run_hi = run_lo + kTkMaxChunks;
+            for (int p = tid; p < nk; p += NT) {
+                const uint32_t c = s_ktok[p] / CH;
+                if (p == 0 || s_ktok[p - 1] / CH != c) run_lo[c] = p;
+                if (p == nk - 1 || s_ktok[p + 1] / CH != c) run_hi[c] = p + 1;
+            }
+            __syncthreads();
+            for (int p = tid; p < nk; p += NT) {
+                const uint32_t x = s_ktok[p];
+                const int lo = run_lo[x / CH], hi = run_hi[x / CH];
+                int rank = lo, j = lo;
+                for (; j < hi && (j & 3); ++j) rank += s_ktok[j] < x;
+                for (; j + 16 <= hi; j += 16) {         // four 16-byte reads in flight
+                    uint32_t t[16];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const uint4 v = *reinterpret_cast<const uint4*>(s_ktok + j + 4 * g);
+                        t[4 * g] = v.x;
+                        t[4 * g + 1] = v.y;
+                        t[4 * g + 2] = v.z;
+                        t[4 * g + 3] = v.w;
+                    }
+#pragma unroll
+                    for (int g = 0; g < 16; ++g) rank += t[g] < x;
+                }
+                for (; j < hi; ++j) rank += s_ktok[j] < x;
                 a.ktok[(size_t)row * kKeptCap + rank] = x;
-                a.kkey[(size_t)row * kKeptCap + rank] = s_kkey[i];
+                a.kkey[(size_t)row * kKeptCap + rank] = s_kkey[p];
             }
         }
         if (tid == 0) a.kn[row] = nk <= kKeptCap ? nk : -1;
@@ -2376,7 +2524,6 @@ struct WsPlan {
         rpar, prec, wacc, total;
     int nparts, nchunks, nch, tk_wcap, tk_listed, filter, topp_mode, sel_k, sel_generic;
     int pr;                  // per-request parameters: every row through the chunk select
-    int wide_merge;          // top-p on: the wider merge workgroups (rows may need passes)
     int pr_plain;            // per-request temperatures only: plain statistics, per-row c
     int kc;                  // the chunk k of a top-p-alone row
 };
@@ -2428,14 +2575,12 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         p.topp_mode = 0;
         p.sel_k = 0;
         p.sel_generic = 0;
-        p.wide_merge = 0;
     } else if (p.pr) {
         // lists sized for the largest chunk k any row may use
         int kmax = 0;
         if (prm->top_k) kmax = prm->top_k_max < kTkMaxK ? prm->top_k_max : kTkMaxK;
         else if (topk_active(top_k, V) && !topk_generic(top_k)) kmax = top_k;
         if (prm->top_p || topp_active(top_p)) kmax = kmax > p.kc ? kmax : p.kc;
-        p.wide_merge = (prm->top_p || topp_active(top_p)) ? 1 : 0;
         p.filter = 1;
         p.topp_mode = -1;               // per row
         p.sel_k = kmax > 0 ? kmax : 1;
@@ -2445,9 +2590,6 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         p.topp_mode = topp_mode(top_k, top_p, V);
         p.sel_k = select_k(top_k, top_p, V, p.nchunks);
         p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
-        // whenever top-p is on (with or without top-k), as for per-request arrays, so the
-        // two paths keep identical sums
-        p.wide_merge = p.topp_mode != 0 ? 1 : 0;
     }
     p.nparts = p.filter ? 1 : p.nchunks;
     const size_t rows = (size_t)2 * K + B;
