@@ -338,6 +338,8 @@ constexpr int kTkMaxChunks = 256; // statistics chunks per row at the largest V
 constexpr int kTkWaves = kTkNT / kWave;          // candidate lists per chunk
 constexpr int kMergeCap = 3072;  // candidates of a row the merge holds in LDS
 constexpr int kTkWcapMax = kTkMaxK;   // list capacity at the largest top_k
+constexpr int kTkLaneSlots = 7;        // candidates a lane stages before they are listed
+constexpr int kTkColumns = (kTkLaneSlots + 1) * kWave;   // a wave's staging (and spill) slots
 constexpr int kKeptCap = 512;   // kept tokens of a bf16 target row listed for the draw
 
 struct TopkArgs {
@@ -634,26 +636,63 @@ SD_DEV void topk_chunk_body(const TopkArgs& a, int row, int chunk, const ChunkSe
         a.ctc[ci] = t0;
     }
 
-    // 3. candidates (key >= t0): each wave appends to its own list, ballot-compacted in
-    //    LDS, then copied out with coalesced stores
+    // 3. candidates (key >= t0): each wave fills its own list, then copies it out with
+    //    coalesced stores. Candidates are few, so each lane first stages its own in a column
+    //    of kTkLaneSlots LDS slots (slot-major: a wave's column writes hit distinct banks)
+    //    and a wave scan of the lane counts places them; a wave with a fuller lane, or lists
+    //    too long to leave room for the columns, compacts with one ballot per element
     uint32_t* lst = s_list + wv * a.wcap;
+    auto entry = [&](uint32_t k, int w, int h) {
+        return BF16 ? (k << 16) | (uint32_t)(token(w, h) - c0) : k;
+    };
     int woff = 0;
+    bool staged = kTkWaves * (a.wcap + kTkColumns) <= kTkWaves * kTkWcapMax;
+    if (staged) {
+        uint32_t* col = s_list + kTkWaves * a.wcap + wv * kTkColumns + lane;
+        int ns = 0;                                      // this lane's staged candidates
 #pragma unroll
-    for (int w = 0; w < NR; ++w)
+        for (int w = 0; w < NR; ++w)
 #pragma unroll
-        for (int h = 0; h < EPR; ++h) {
-            const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
-            const bool f = k >= t0;
-            const uint64_t bal = __ballot(f);
-            if (bal) {
-                const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
-                                           uint32_t(bal >> 32),
-                                           __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u));
-                if (f && pos < a.wcap)
-                    lst[pos] = BF16 ? (k << 16) | (uint32_t)(token(w, h) - c0) : k;
-                woff += __popcll(bal);
+            for (int h = 0; h < EPR; ++h) {
+                const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+                if (k >= t0) {
+                    col[min(ns, kTkLaneSlots) * kWave] = entry(k, w, h);   // slot 7: spill
+                    ++ns;
+                }
             }
+        staged = __ballot(ns > kTkLaneSlots) == 0ull;
+        if (staged) {
+            int p = ns;                                  // exclusive scan of the lane counts
+#pragma unroll
+            for (int o = 1; o < kWave; o <<= 1) {
+                const int y = __shfl_up(p, o, kWave);
+                if (lane >= o) p += y;
+            }
+            woff = __shfl(p, kWave - 1, kWave);
+            p -= ns;
+#pragma unroll
+            for (int j = 0; j < kTkLaneSlots; ++j)
+                if (j < ns && p + j < a.wcap) lst[p + j] = col[j * kWave];
         }
+    }
+    if (!staged) {
+        woff = 0;
+#pragma unroll
+        for (int w = 0; w < NR; ++w)
+#pragma unroll
+            for (int h = 0; h < EPR; ++h) {
+                const uint32_t k = (r[w] >> (16 * h)) & (BF16 ? 0xffffu : ~0u);
+                const bool f = k >= t0;
+                const uint64_t bal = __ballot(f);
+                if (bal) {
+                    const int pos = woff + (int)__builtin_amdgcn_mbcnt_hi(
+                                               uint32_t(bal >> 32),
+                                               __builtin_amdgcn_mbcnt_lo(uint32_t(bal), 0u));
+                    if (f && pos < a.wcap) lst[pos] = entry(k, w, h);
+                    woff += __popcll(bal);
+                }
+            }
+    }
     if (lane == 0) s_wn[wv] = wbad ? -1 : woff;
     __syncthreads();
     int before = 0, total = 0, bad = 0, over = 0;
