@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-early-exit-compare", action="store_true",
                    help="skip timing specdec_cycle_early_exit beside the fused cycle")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="skip the read / copy bandwidth probes after the timed region")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="run one plain device-to-device copy of this many MiB before timing "
                         "(a known-size reference for HBM traffic counters)")
@@ -80,6 +82,39 @@ def parse():
     p.add_argument("--cpu-workers", type=int, default=0,
                    help="processes for the n-core oracle baseline (0: min(16, available))")
     return p.parse_args()
+
+
+def probe_ceilings(binding, torch, d, srcs, copy_mib: int, reps: int = 20):
+    """This device's read and copy ceilings from the library's bandwidth probes, measured
+    after the timed region: the tensors in srcs streamed reps times with the statistics
+    launches' access pattern, and a copy_mib MiB buffer copied reps times with the fastest
+    copy shape measured on this part; events around each group of launches."""
+    sink = torch.zeros(1, dtype=torch.int32, device=d)
+    # whole 16-byte vectors of each tensor (the probes' unit)
+    srcs = [t.reshape(-1).view(torch.uint8) for t in srcs]
+    srcs = [t[: t.numel() // 16 * 16] for t in srcs]
+    nb_read = sum(t.numel() for t in srcs)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_read = timed(lambda: [binding.specdec_probe_read(t, sink) for t in srcs])
+    a = torch.empty(copy_mib << 20, dtype=torch.uint8, device=d).fill_(1)
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: binding.specdec_probe_copy(b, a))
+    nb_copy = 2 * a.numel()
+    del a, b
+    return {"read_gbps": nb_read / t_read / 1e9, "read_bytes": nb_read,
+            "copy_gbps": nb_copy / t_copy / 1e9, "copy_bytes_read_and_written": nb_copy,
+            "kernels": "k_probe_read, k_probe_copy", "reps": reps}
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -622,6 +657,7 @@ def main():
         del g
     acceptance = acceptance_stats(binding, torch, d, vin, tgt, dft, tokens, cu, u_acc, u_smp,
                                   out, nacc, nemit, err, ws, top_p, pr, ms_per_step)
+    ceilings = None if args.no_ceilings else probe_ceilings(binding, torch, d, [tgt, dft], 512)
     es = 2 if vin.dtype == "bf16" else 4
     rows = 2 * K + B
     logit_bytes = rows * V * es
@@ -694,6 +730,15 @@ def main():
         res["per_call"] = {"append_ms": ap, "append_gbps": kv_bytes / (ap / 1e3) / 1e9,
                            "verify_ms": ve, "verify_gbps": logit_bytes / (ve / 1e3) / 1e9,
                            "rollback_ms": rb}
+    if ceilings is not None:
+        # the cycle's compulsory bytes at this device's measured ceilings: every logit row
+        # read at the read probe's rate, the new K/V read and written at the copy probe's
+        at = read_bytes / (ceilings["read_gbps"] * 1e9) + kv_bytes / (ceilings["copy_gbps"] * 1e9)
+        ceilings["compulsory_ms_at_ceilings"] = at * 1e3
+        ceilings["pct_peak_hbm_at_ceilings"] = 100.0 * cycle_bytes / at / 1e9 / PEAK_GBPS
+        ceilings["cycle_vs_ceilings"] = at * 1e3 / ms_per_step
+        res["ceilings"] = ceilings
+        res["roofline"]["frac_of_read_ceiling"] = achieved / ceilings["read_gbps"]
     if generic:
         res["roofline"] = None
     seq_bytes = seq_rows * V * es + kv_bytes + small

@@ -542,6 +542,21 @@ int kv_tree_commit(const kv_paged_cache* cache, int32_t B, const int32_t* num_ac
                    const int32_t* accepted_nodes, const int32_t* cu_nodes, int32_t N,
                    hipStream_t stream);
 
+/*
+ * Bandwidth probes (measurement only, not part of the verification path): the ceilings
+ * against which the launches above are read. specdec_probe_read streams `bytes` from `src`
+ * once with the statistics launches' access pattern (256-thread workgroups, eight 16-byte
+ * non-temporal loads in flight per thread, one 32 KB span per workgroup) and stores into
+ * *sink only when the data fold to one particular word. specdec_probe_copy copies `bytes`
+ * from `src` to `dst` with non-temporal 16-byte loads and stores, four in flight per thread
+ * (the fastest copy shape measured on MI355X). Device pointers, 16-byte aligned, `bytes` a
+ * positive multiple of 16,
+ * buffers not overlapping; EINVAL otherwise, before anything is enqueued. One launch on
+ * `stream`.
+ */
+int specdec_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+int specdec_probe_copy(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,7 @@ EXPORTED = [
     "specdec_tree_verify_workspace_size",
     "specdec_tree_verify", "kv_tree_commit",
     "kv_contig_append", "kv_contig_rollback",
+    "specdec_probe_read", "specdec_probe_copy",
 ]
 
 
@@ -190,6 +191,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kv_contig_append.restype = ctypes.c_int
     lib.kv_contig_rollback.argtypes = [ctypes.POINTER(KvContigCacheStruct), i32, vp, vp, i32, vp]
     lib.kv_contig_rollback.restype = ctypes.c_int
+    lib.specdec_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.specdec_probe_read.restype = ctypes.c_int
+    lib.specdec_probe_copy.argtypes = [vp, vp, sz, vp]
+    lib.specdec_probe_copy.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -446,6 +451,26 @@ def specdec_cycle_static(cache: PagedKVCache, k_new: torch.Tensor, v_new: torch.
     st = lib.specdec_cycle_static(*args, _stream(dev))
     if st != SPECDEC_OK:
         raise SpecdecError("specdec_cycle_static", st)
+
+
+def specdec_probe_read(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Stream src once with the statistics launches' access pattern (bandwidth probe)."""
+    lib = load_library()
+    st = lib.specdec_probe_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                _stream(src.device))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_probe_read", st)
+
+
+def specdec_probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Copy src into dst with the K/V scatter's loads and stores (bandwidth probe)."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("specdec_probe_copy: dst is smaller than src")
+    st = lib.specdec_probe_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device))
+    if st != SPECDEC_OK:
+        raise SpecdecError("specdec_probe_copy", st)
 
 
 # --- HIP events and stream waits through the runtime (timing, cross-stream ordering) -----

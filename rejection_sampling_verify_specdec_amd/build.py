@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecdec.so")
-SOURCES = ["verify.hip", "kv.hip", "cycle.hip", "tree.hip"]
+SOURCES = ["verify.hip", "kv.hip", "cycle.hip", "tree.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -13,7 +13,7 @@ namespace sd {
 
 constexpr int kKvNT = 1024;      // rollback workgroup (and the standalone allocation)
 constexpr int kScNT = 256;       // standalone scatter workgroup
-constexpr int kScPPT = 8;        // token rows per scatter thread in flight
+constexpr int kScPPT = 2;        // token rows per scatter thread in flight
 constexpr int kEvCap = 2048;     // rollback events per window
 constexpr int kTreeGatherNT = 128;   // tree commit gather workgroup
 

@@ -225,3 +225,18 @@ def test_the_library_loaded_is_the_one_asked_for(lib):
         assert os.path.samefile(lib._name, want)
         data = open(want, "rb").read().decode("latin-1")
         assert "__asan_init" in data and "__ubsan_handle" in data
+
+
+def test_probe_host_validation_without_gpu(lib):
+    # the bandwidth probes refuse null, misaligned, empty, ragged and overlapping buffers
+    # before anything is enqueued
+    E = binding.SPECDEC_EINVAL
+    assert lib.specdec_probe_read(None, 1 << 20, 4096, None) == E
+    assert lib.specdec_probe_read(4096, 1 << 20, None, None) == E
+    assert lib.specdec_probe_read(4100, 1 << 20, 8, None) == E
+    assert lib.specdec_probe_read(4096, 0, 8, None) == E
+    assert lib.specdec_probe_read(4096, 1000, 8, None) == E
+    assert lib.specdec_probe_copy(1 << 30, 4096, 0, None) == E
+    assert lib.specdec_probe_copy(4096 + (1 << 19), 4096, 1 << 20, None) == E
+    assert lib.specdec_probe_copy(4096, 4096 + (1 << 19), 1 << 20, None) == E
+    assert lib.specdec_probe_copy(4104, 1 << 30, 1 << 20, None) == E
