@@ -86,13 +86,17 @@ def parse():
 
 def probe_ceilings(binding, torch, d, srcs, copy_mib: int, reps: int = 20):
     """This device's read and copy ceilings from the library's bandwidth probes, measured
-    after the timed region: the tensors in srcs streamed reps times with the statistics
-    launches' access pattern, and a copy_mib MiB buffer copied reps times with the fastest
-    copy shape measured on this part; events around each group of launches."""
+    after the timed region: the tensors in srcs (the logit rows; at least copy_mib MiB)
+    streamed reps times with the statistics launches' access pattern, and a copy_mib MiB
+    buffer copied reps times with the fastest copy shape measured on this part; events
+    around each group of launches."""
     sink = torch.zeros(1, dtype=torch.int32, device=d)
-    # whole 16-byte vectors of each tensor (the probes' unit)
+    # whole 16-byte vectors of each tensor (the probes' unit); small batches' rows are too
+    # few to keep the device busy, so below copy_mib MiB a buffer of that size is read
     srcs = [t.reshape(-1).view(torch.uint8) for t in srcs]
     srcs = [t[: t.numel() // 16 * 16] for t in srcs]
+    if sum(t.numel() for t in srcs) < copy_mib << 20:
+        srcs = [torch.ones(copy_mib << 20, dtype=torch.uint8, device=d)]
     nb_read = sum(t.numel() for t in srcs)
 
     def timed(fn):
