@@ -436,10 +436,9 @@ def main():
     vin = synth.make_verify(wl, seed=args.seed, B=args.batch,
                             **({} if args.top_k is None else {"top_k": args.top_k}))
     top_p = args.top_p
-    # the fused cycle with temperature only is also timed in its early-exit form, on the
-    # same batch and cache, after the timed region
-    compare_early = (args.schedule == "fused" and not args.no_early_exit_compare and
-                     not 0 < vin.top_k < vin.V and not 0.0 < top_p < 1.0)
+    # the fused cycle is also timed in its early-exit form, on the same batch and cache,
+    # after the timed region
+    compare_early = args.schedule == "fused" and not args.no_early_exit_compare
     # the pool holds the warm-up, the timed cycles and twice as many again for the
     # percentiles (without and with a cache flush before each cycle), and the early-exit
     # comparison's cycles
@@ -473,9 +472,6 @@ def main():
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
-    if args.schedule == "early-exit" and (0 < vin.top_k < V or 0.0 < top_p < 1.0):
-        raise SystemExit("--schedule early-exit takes temperature only (scalar or per "
-                         "request; no top-k or top-p)")
     pr = {}
     if args.per_request:
         pr["temperatures"] = torch.full((B,), vin.T, dtype=torch.float32, device=d)
@@ -687,8 +683,8 @@ def main():
     # streams the rows once
     generic = 0 < vin.top_k < V and vin.top_k > 1024
     # per-request arrays hold temperatures only when no top-k / top-p is on: plain statistics
-    if early:                          # max_k + 1 launches, timed as one span
-        stats_kernel = "k_cycle_pass"
+    if early:                          # the position launches, timed as one span
+        stats_kernel = "k_cycle_fpass" if filtered else "k_cycle_pass"
     elif filtered:                     # the chunk launch streams the rows
         stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
     else:

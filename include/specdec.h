@@ -222,16 +222,17 @@ int specdec_verify(const void* target_logits, const void* draft_logits, int32_t 
  * position, each reading the rows of the requests whose earlier proposals were all
  * accepted; one more launch reads every later row of the requests still live then (ahead
  * of their decisions: few requests get that far, and one launch costs less than one per
- * position). A request rejected at an earlier position reads none of them. The decision
- * and the draw follow.
+ * position). A request rejected at an earlier position reads none of them. With a top-k /
+ * top-p transform (scalar or per request) each of these is a chunk-select launch followed
+ * by a merge launch over the rows it selected. The decision and the draw follow.
  * Arguments, layouts, ownership and workspace (specdec_verify_workspace_size with the same
  * arguments): as specdec_verify, and the same results bit for bit for every request whose
  * read rows are finite. A non-finite row past the first rejection is not reported; debug
  * p_y / q_y past the first rejection and row_max / row_sum / row_thr of rows not read are
  * NaN (row_nkept -1); ev_stats_begin / ev_stats_end bracket all the statistics launches.
- * Temperature only, scalar or per request. Host: every specdec_verify check, and also
- * EINVAL, before anything is enqueued, for top-k (0 < top_k < V), top-p (0 < top_p < 1),
- * per_request top_k or top_p arrays, or the acceptance analytics in dbg.
+ * Every transform specdec_verify takes (temperature, top-k, top-p, scalar or per request).
+ * Host: every specdec_verify check, and also EINVAL, before anything is enqueued, when dbg
+ * asks for the acceptance analytics (they need every row).
  */
 int specdec_verify_early_exit(const void* target_logits, const void* draft_logits, int32_t dtype,
                               const int32_t* draft_tokens, const int32_t* cu_draft,
@@ -407,19 +408,20 @@ int specdec_cycle_static(const kv_paged_cache* cache, const void* k_new, const v
  *   - the row statistics of positions 0 .. SPECDEC_EARLY_EXIT_SEQUENTIAL - 1 run one launch
  *     per position p, each reading the rows of position p of the requests whose proposals
  *     before p were all accepted; one more launch reads every later row of the requests
- *     live at SPECDEC_EARLY_EXIT_SEQUENTIAL (ahead of their decisions); the K/V scatter
- *     is spread over the launches after the first;
+ *     live at SPECDEC_EARLY_EXIT_SEQUENTIAL (ahead of their decisions); with a top-k /
+ *     top-p transform each of these is a chunk-select launch followed by a merge launch
+ *     over the rows it selected; the K/V scatter is spread over the launches after the
+ *     first;
  *   - SPECDEC_ERR_NONFINITE covers the rows read (a non-finite row after the first
  *     rejection is not seen);
  *   - debug p_y / q_y after the first rejection, and row_max / row_sum / row_thr of rows
  *     not read, are NaN (row_nkept -1);
  *   - events: ev_stats_begin / ev_stats_end bracket all the statistics launches.
- * Temperature only: scalar, or per request (per_request->temperature; a request with an
- * invalid temperature reads no row and fails with SPECDEC_ERR_PARAM as in specdec_cycle).
- * Host: every specdec_cycle check, and also EINVAL, before anything is enqueued, when top-k
- * (0 < top_k < V) or top-p (0 < top_p < 1) is on, when per_request carries top_k or top_p
- * arrays (temperature, eos_token and max_emit are allowed), or when dbg asks for the
- * acceptance analytics (accept_prob, expected_emitted: they need every row).
+ * Every transform specdec_cycle takes: temperature, top-k and top-p, scalar or per request
+ * (a request with invalid parameters reads no row and fails with SPECDEC_ERR_PARAM as in
+ * specdec_cycle). Host: every specdec_cycle check, and also EINVAL, before anything is
+ * enqueued, when dbg asks for the acceptance analytics (accept_prob, expected_emitted:
+ * they need every row).
  */
 int specdec_cycle_early_exit(const kv_paged_cache* cache, const void* k_new, const void* v_new,
                              const void* target_logits, const void* draft_logits, int32_t dtype,

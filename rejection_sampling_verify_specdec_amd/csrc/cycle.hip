@@ -130,6 +130,43 @@ __global__ __launch_bounds__(kNT) void k_cycle_tail(SampleArgs sa, RowPartial* _
 
 static_assert(kTkNT == kCycAllocNT, "allocation and top-k chunk workgroups share one launch");
 
+// Early exit with a top-k / top-p transform: launch p runs the chunk select of position p's
+// rows of the live requests (workgroup 0 of launch 0 allocates the cycle's blocks first;
+// later launches carry a share of the K/V scatter); the tail launch every later row of the
+// requests still live; a merge launch follows each (P2: 0 top-k, 1 top-p alone, 2
+// per-request parameters).
+template <bool BF16, bool VEC, int P2>
+__global__ __launch_bounds__(kTkNT) void k_cycle_fpass(KvArgs kv, const int* __restrict__ cu,
+                                                     int B, int N, uint8_t* __restrict__ aws,
+                                                     SampleArgs sa, TopkArgs ta, int p,
+                                                     ScatterShare sc) {
+    if (p == 0) {
+        if (blockIdx.x == 0) {
+            alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
+            return;
+        }
+        fpass_body<BF16, VEC, P2>(sa, ta, 0, blockIdx.x - 1);
+    } else {
+        int w = 0;
+        const int si = scatter_index(blockIdx.x, gridDim.x, sc.ns, &w);
+        if (si >= 0) scatter_share(sc, si);
+        else fpass_body<BF16, VEC, P2>(sa, ta, p, w);
+    }
+}
+
+template <bool BF16, bool VEC, int P2>
+__global__ __launch_bounds__(kTkNT) void k_cycle_ftail(SampleArgs sa, TopkArgs ta, int p,
+                                                     int nwg, ScatterShare sc) {
+    if (blockIdx.x < (unsigned)nwg) ftail_body<BF16, VEC, P2>(sa, ta, p, blockIdx.x);
+    else scatter_share(sc, blockIdx.x - nwg);
+}
+
+template <bool BF16, bool PR>
+__global__ __launch_bounds__(kMergeNT) __attribute__((amdgpu_waves_per_eu(5))) void
+k_cycle_fmerge(SampleArgs sa, TopkArgs ta, int p, int tail) {
+    fmerge_body<BF16, kMergeNT, PR>(sa, ta, p, blockIdx.x, tail != 0);
+}
+
 // P2: 0 top-k, 1 top-p alone, 2 per-request parameters
 template <bool BF16, bool VEC, int P2>
 __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __restrict__ cu,
@@ -322,15 +359,71 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
                                  kFusedSplit, st);
 }
 
-// The early-exit cycle (temperature only, scalar or per request): one statistics launch
-// for each of positions 0 .. kEarlyCut - 1, then one for every later row of the requests
-// still live, with the K/V scatter spread over the launches after the first; then the same
-// decision, draw and cache launches.
+// The early-exit cycle: one statistics launch for each of positions 0 .. kEarlyCut - 1,
+// then one for every later row of the requests still live, with the K/V scatter spread over
+// the launches after the first; then the same decision, draw and cache launches. With a
+// top-k / top-p transform each statistics launch is a chunk-select launch followed by a
+// merge launch over the rows it selected.
+template <bool BF16, bool VEC, int P2>
+static void launch_cycle_early_filtered(const KvArgs& kv, const uint8_t* knew,
+                                        const uint8_t* vnew, const int* cu, int B, int K,
+                                        int max_k, const WsPlan& p, const TopkArgs& ta,
+                                        const SampleArgs& sa, const ParamArgs& pa,
+                                        uint8_t* aws, const specdec_debug* dbg, hipStream_t st) {
+    constexpr bool PR = P2 == 2;
+    if (PR) {                   // each row's parameters first
+        const int rows = 2 * K + B;
+        hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
+                           pa, rows);
+    }
+    const unsigned nwg = (unsigned)B * 2u * (unsigned)ta.nchunks;
+    const ScatterShare sc = scatter_plan(kv, knew, vnew, aws, B, K + B);
+    if (dbg && dbg->ev_stats_begin) (void)hipEventRecord(dbg->ev_stats_begin, st);
+    int done = 0;
+    for (int q = 0; q <= max_k && q < kEarlyCut; ++q) {
+        const int share = q == 1 ? std::min(sc.ns, pct_of(sc.ns, kEarlySplit.pass_pct)) : 0;
+        hipLaunchKernelGGL((k_cycle_fpass<BF16, VEC, P2>),
+                           dim3(nwg + (q == 0 ? 1u : 0u) + (unsigned)share), dim3(kTkNT), 0, st,
+                           kv, cu, B, K + B, aws, sa, ta, q, scatter_slice(sc, done, share));
+        done += share;
+        hipLaunchKernelGGL((k_cycle_fmerge<BF16, PR>), dim3((unsigned)B * 2u), dim3(kMergeNT), 0,
+                           st, sa, ta, q, 0);
+    }
+    if (max_k >= kEarlyCut) {
+        const unsigned per = (unsigned)early_tail_slots(max_k, kEarlyCut);
+        const unsigned tw = (unsigned)B * per * (unsigned)ta.nchunks;
+        const int share = std::min(sc.ns - done, pct_of(sc.ns, kEarlySplit.tail_pct));
+        hipLaunchKernelGGL((k_cycle_ftail<BF16, VEC, P2>), dim3(tw + (unsigned)share), dim3(kTkNT),
+                           0, st, sa, ta, kEarlyCut, (int)tw, scatter_slice(sc, done, share));
+        done += share;
+        hipLaunchKernelGGL((k_cycle_fmerge<BF16, PR>), dim3((unsigned)B * per), dim3(kMergeNT), 0,
+                           st, sa, ta, kEarlyCut, 1);
+    }
+    if (dbg && dbg->ev_stats_end) (void)hipEventRecord(dbg->ev_stats_end, st);
+    if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
+    launch_cycle_tail<BF16, VEC>(kv, B, K, p, sa, scatter_slice(sc, done, sc.ns - done),
+                                 kEarlySplit, st);
+}
+
 template <bool BF16, bool VEC>
 static void launch_cycle_early(const KvArgs& kv, const uint8_t* knew, const uint8_t* vnew,
-                               const int* cu, int B, int K, int max_k, const WsPlan& p,
+                               const uint8_t* tgt, const uint8_t* dft, const int* cu, int B,
+                               int K, int max_k, int V, float top_p, float c, const WsPlan& p,
                                uint8_t* vws, uint8_t* aws, const SampleArgs& sa,
                                const ParamArgs& pa, const specdec_debug* dbg, hipStream_t st) {
+    if (p.filter) {
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
+        if (p.pr)
+            launch_cycle_early_filtered<BF16, VEC, 2>(kv, knew, vnew, cu, B, K, max_k, p, ta, sa,
+                                                      pa, aws, dbg, st);
+        else if (p.topp_mode == 2)
+            launch_cycle_early_filtered<BF16, VEC, 1>(kv, knew, vnew, cu, B, K, max_k, p, ta, sa,
+                                                      pa, aws, dbg, st);
+        else
+            launch_cycle_early_filtered<BF16, VEC, 0>(kv, knew, vnew, cu, B, K, max_k, p, ta, sa,
+                                                      pa, aws, dbg, st);
+        return;
+    }
     RowPartial* part = reinterpret_cast<RowPartial*>(vws + p.part);
     if (p.pr_plain) {          // per-request temperatures: each row's log2(e) / T first
         const int rows = 2 * K + B;
@@ -385,12 +478,8 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
                        const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
     using namespace sd;
-    // early exit: temperature only (scalar or per request), no analytics (they need every
-    // row)
-    if (early && (topk_active(top_k, V) || topp_active(top_p) ||
-                  (per_request && (per_request->top_k || per_request->top_p)) ||
-                  (dbg && (dbg->accept_prob || dbg->expected_emitted))))
-        return SPECDEC_EINVAL;
+    // early exit: no analytics (they need every row)
+    if (early && dbg && (dbg->accept_prob || dbg->expected_emitted)) return SPECDEC_EINVAL;
     // verification arguments: the same checks as specdec_verify
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
@@ -410,7 +499,9 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
         return SPECDEC_EINVAL;
     const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks + 1 > 0x7fffffffu ||
-        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V)
+        (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V ||
+        (early && max_k >= kEarlyCut &&
+         (size_t)B * early_tail_slots(max_k, kEarlyCut) * p.nchunks > 0x7fffffffu))
         return SPECDEC_EINVAL;
     const size_t vbytes = align256(p.total);
     if (!workspace || workspace_bytes < vbytes + append_ws_bytes(B, K + B) ||
@@ -474,11 +565,11 @@ static int cycle_entry(bool early, const kv_paged_cache* cache, const void* k_ne
     (void)hipGetLastError();
     if (early) {
         if (dtype == SPECDEC_BF16) {
-            if (vec) launch_cycle_early<true, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
-            else launch_cycle_early<true, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
+            if (vec) launch_cycle_early<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, max_k, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
+            else launch_cycle_early<true, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, max_k, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
         } else {
-            if (vec) launch_cycle_early<false, true>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
-            else launch_cycle_early<false, false>(kv, knew, vnew, cu_draft, B, K, max_k, p, vws, aws, sa, pa, dbg, stream);
+            if (vec) launch_cycle_early<false, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, max_k, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
+            else launch_cycle_early<false, false>(kv, knew, vnew, tgt, dft, cu_draft, B, K, max_k, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);
         }
     } else if (dtype == SPECDEC_BF16) {
         if (vec) launch_cycle<true, true>(kv, knew, vnew, tgt, dft, cu_draft, B, K, V, top_p, c, p, vws, aws, sa, pa, dbg, stream);

@@ -117,6 +117,48 @@ __global__ __launch_bounds__(kNT) void k_tail(SampleArgs a, RowPartial* __restri
     tail_body<BF16, VEC>(a, part, p, blockIdx.x);
 }
 
+// Early exit with a top-k / top-p transform: the chunk select of position p's rows (of every
+// later row for the tail launch) of the live requests, then their merge
+template <bool BF16, bool VEC, int P2>
+__global__ __launch_bounds__(kTkNT) void k_fpass(SampleArgs a, TopkArgs ta, int p) {
+    fpass_body<BF16, VEC, P2>(a, ta, p, blockIdx.x);
+}
+
+template <bool BF16, bool VEC, int P2>
+__global__ __launch_bounds__(kTkNT) void k_ftail(SampleArgs a, TopkArgs ta, int p) {
+    ftail_body<BF16, VEC, P2>(a, ta, p, blockIdx.x);
+}
+
+template <bool BF16, bool PR>
+__global__ __launch_bounds__(kMergeNT) __attribute__((amdgpu_waves_per_eu(5))) void k_fmerge(
+    SampleArgs a, TopkArgs ta, int p, int tail) {
+    fmerge_body<BF16, kMergeNT, PR>(a, ta, p, blockIdx.x, tail != 0);
+}
+
+template <bool BF16, bool VEC, int P2>
+static void launch_early_filtered(int B, int K, int max_k, const TopkArgs& ta,
+                                  const SampleArgs& sa, const ParamArgs& pa, hipStream_t st) {
+    constexpr bool PR = P2 == 2;
+    if (PR) {
+        const int rows = 2 * K + B;
+        hipLaunchKernelGGL(k_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st, pa,
+                           rows);
+    }
+    for (int q = 0; q <= max_k && q < kEarlyCut; ++q) {
+        hipLaunchKernelGGL((k_fpass<BF16, VEC, P2>), dim3((unsigned)B * 2u * (unsigned)ta.nchunks),
+                           dim3(kTkNT), 0, st, sa, ta, q);
+        hipLaunchKernelGGL((k_fmerge<BF16, PR>), dim3((unsigned)B * 2u), dim3(kMergeNT), 0, st,
+                           sa, ta, q, 0);
+    }
+    if (max_k >= kEarlyCut) {
+        const unsigned per = (unsigned)early_tail_slots(max_k, kEarlyCut);
+        hipLaunchKernelGGL((k_ftail<BF16, VEC, P2>), dim3((unsigned)B * per * (unsigned)ta.nchunks),
+                           dim3(kTkNT), 0, st, sa, ta, kEarlyCut);
+        hipLaunchKernelGGL((k_fmerge<BF16, PR>), dim3((unsigned)B * per), dim3(kMergeNT), 0, st,
+                           sa, ta, kEarlyCut, 1);
+    }
+}
+
 template <bool BF16, bool VEC>
 static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int V,
                        float top_p, float c, const WsPlan& p, uint8_t* ws, SampleArgs sa,
@@ -127,7 +169,15 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     // optional timing events are attached to the statistics launch itself
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
-    if (early) {
+    if (early && p.filter) {
+        // the same positions, each a chunk-select and a merge launch
+        const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
+        if (e0) (void)hipEventRecord(e0, st);
+        if (p.pr) launch_early_filtered<BF16, VEC, 2>(B, K, max_k, ta, sa, pa, st);
+        else if (p.topp_mode == 2) launch_early_filtered<BF16, VEC, 1>(B, K, max_k, ta, sa, pa, st);
+        else launch_early_filtered<BF16, VEC, 0>(B, K, max_k, ta, sa, pa, st);
+        if (e1) (void)hipEventRecord(e1, st);
+    } else if (early) {
         // one launch per position up to kEarlyCut, then one for the rest; the events
         // bracket them all
         if (p.pr_plain)
@@ -209,12 +259,8 @@ static int verify_entry(bool early, const void* target_logits, const void* draft
                         const specdec_debug* dbg, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
     using namespace sd;
-    // early exit: temperature only (scalar or per request), no analytics (they need every
-    // row)
-    if (early && (topk_active(top_k, V) || topp_active(top_p) ||
-                  (per_request && (per_request->top_k || per_request->top_p)) ||
-                  (dbg && (dbg->accept_prob || dbg->expected_emitted))))
-        return SPECDEC_EINVAL;
+    // early exit: no analytics (they need every row)
+    if (early && dbg && (dbg->accept_prob || dbg->expected_emitted)) return SPECDEC_EINVAL;
     if (B < 1 || K < 0 || V < 1 || max_k < 0 || max_k > SPECDEC_MAX_K) return SPECDEC_EINVAL;
     if ((long long)K > (long long)B * max_k) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
@@ -230,7 +276,9 @@ static int verify_entry(bool early, const void* target_logits, const void* draft
     const WsPlan p = plan_ws(B, K, V, dtype, top_k, top_p, per_request);
     if ((size_t)(2 * (size_t)K + B) * p.nchunks > 0x7fffffffu ||
         (size_t)K * p.nch > 0x7fffffffu || V > SPECDEC_MAX_V ||
-        (early && (size_t)2 * B * p.nchunks > 0x7fffffffu))
+        (early && (size_t)2 * B * p.nchunks > 0x7fffffffu) ||
+        (early && max_k >= kEarlyCut &&
+         (size_t)B * early_tail_slots(max_k, kEarlyCut) * p.nchunks > 0x7fffffffu))
         return SPECDEC_EINVAL;
     if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace & 15))
         return SPECDEC_EWORKSPACE;

@@ -1526,6 +1526,7 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
     __shared__ float s_thr[kMaxRows];
     __shared__ int s_rowbad;
     __shared__ int s_bad[kMaxRows];     // early exit: each row's validity
+    __shared__ int s_nk[kMaxRows];      // early exit: each row's kept count
     __shared__ int s_vis;               // early exit: the last visited position
     const int tid = threadIdx.x, lane = tid % kWave;
     const int rows_t = a.K + a.B;
@@ -1572,8 +1573,12 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         s_S[r] = S;
         s_thr[r] = thr;
         const bool rbad = !(S > 0.0 && S < INFINITY && m > -INFINITY);
-        if (a.early) s_bad[r] = rbad;
-        else if (rbad) atomicOr(&s_rowbad, 1);
+        if (a.early) {
+            s_bad[r] = rbad;
+            s_nk[r] = a.topk ? nk : -1;
+        } else if (rbad) {
+            atomicOr(&s_rowbad, 1);
+        }
         if (publish && !a.early) {
             if (a.dbg.row_max) a.dbg.row_max[prow] = m;
             if (a.dbg.row_sum) a.dbg.row_sum[prow] = S;
@@ -1721,7 +1726,7 @@ SD_DEV void decide_body(const SampleArgs& a, int b, bool publish, Decision& D) {
         if (a.dbg.row_max) a.dbg.row_max[prow] = seen ? s_m[tid] : NAN;
         if (a.dbg.row_sum) a.dbg.row_sum[prow] = seen ? s_S[tid] : NAN;
         if (a.dbg.row_thr) a.dbg.row_thr[prow] = seen ? s_thr[tid] : NAN;
-        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = -1;
+        if (a.dbg.row_nkept) a.dbg.row_nkept[prow] = seen ? s_nk[tid] : -1;
     }
 }
 
@@ -1847,11 +1852,16 @@ SD_DEV void decide_kernel_body(const SampleArgs& a, int b) {
 // requests still live
 constexpr int kEarlyCut = SPECDEC_EARLY_EXIT_SEQUENTIAL;
 static_assert(kEarlyCut >= 1, "position 0 is read for every request first");
+// rows from position p on of a request with k_b <= max_k: target rows p .. k_b and draft
+// rows p .. k_b - 1, at most 2 (max_k - p) + 1
+__host__ __device__ inline int early_tail_slots(int max_k, int p) { return 2 * (max_k - p) + 1; }
 
 // Whether request b (first proposal lo, k_b = k) is live at position p >= 1, given that it
 // was live at p - 1 (the flag the launch for p - 1 left) and p <= k: proposal p - 1 has a
-// valid uniform and token and passes u * Q < P. Threads 0 and 1 of the workgroup call:
-// thread 0 evaluates the target row, thread 1 the draft row; thread 0's result counts.
+// valid uniform and token and passes u * Q < P, with P and Q formed as the decision forms
+// them (the rows' combined partials, and their thresholds when a top-k / top-p transform
+// is on). Threads 0 and 1 of the workgroup call: thread 0 evaluates the target row, thread
+// 1 the draft row; thread 0's result counts.
 template <bool BF16>
 SD_DEV bool live_test(const SampleArgs& a, const RowPartial* part, int p, int b, int lo) {
     using Lt = Layout<BF16, true>;
@@ -1872,17 +1882,30 @@ SD_DEV bool live_test(const SampleArgs& a, const RowPartial* part, int p, int b,
         double S;
         int nk;
         combine_partials(part + prow * nchunks, nchunks, cd, &m, &S, &nk);
-        const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, -INFINITY, cd);
+        const float thr = a.topk ? a.row_thr[prow] : -INFINITY;
+        const double pr = kept_prob(load_elem(zrow, y, BF16), m, S, thr, cd);
         const double Q = __shfl(pr, 1, kWave);
         live = u * Q < pr;                           // lane 0's: P = its own
     }
     return live;
 }
 
-template <bool BF16, bool VEC>
-SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+// The early-exit grids. pass_grid: workgroup w of a (request, side, chunk) grid at
+// position p; the liveness chain (p = 0: the request's offsets and parameters are valid;
+// p >= 1: live at p - 1 and proposal p - 1 accepted), the flag for the next launch, then
+// work(row, chunk) for the row of this side at p if the request is live and has it.
+// tail_grid: if the request is live at p >= 1, work(row, chunk) for its target rows
+// p .. k_b and draft rows p .. k_b - 1, and (with `flag`) the liveness at p left for a
+// later launch. SLOTS: workgroup w of a (request, row slot, chunk) grid with
+// early_tail_slots(max_k, p) slots per request (slots 0 .. k_b - p the target rows, the
+// slots after them the draft rows), one row each: the chunk select, several times the
+// work of the plain statistics, keeps the few live requests' rows side by side; else
+// workgroup w of a (request, chunk) grid takes the chunk of every row in turn, which for
+// the plain statistics costs less than one liveness test per row. nchunks: the grid's
+// chunks per row.
+template <bool BF16, class Work>
+SD_DEV void pass_grid(const SampleArgs& a, int nchunks, int p, int w, Work&& work) {
     __shared__ int s_live;
-    const int nchunks = a.nparts;
     const int b = w / (2 * nchunks);
     const int side = (w / nchunks) & 1;
     const int chunk = w - (w / nchunks) * nchunks;
@@ -1903,7 +1926,7 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
             // a request with invalid parameters fails in the decision without its rows
             if (live && a.rpar) live = !(a.rpar[lo + b].flags & kRpBad);
         } else {
-            live = live_test<BF16>(a, part, p, b, lo);
+            live = live_test<BF16>(a, a.part, p, b, lo);
         }
         if (threadIdx.x == 0) {
             // one workgroup per request leaves the flag for the next launch (every launch
@@ -1914,36 +1937,71 @@ SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p,
     }
     __syncthreads();
     if (!s_live) return;
-    const int row = side == 0 ? lo + b + p : rows_t + lo + p;
-    row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part, row * nchunks + chunk,
-                              a.rpar);
+    work(side == 0 ? lo + b + p : rows_t + lo + p, chunk);
 }
 
-// The last statistics launch, at position p >= 1: workgroup (b, chunk) reads its chunk of
-// every target row p .. k_b and draft row p .. k_b - 1 of request b if b is live at p.
-template <bool BF16, bool VEC>
-SD_DEV void tail_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+template <bool BF16, bool SLOTS, class Work>
+SD_DEV void tail_grid(const SampleArgs& a, int nchunks, int p, int w, bool flag, Work&& work) {
     __shared__ int s_live;
-    const int nchunks = a.nparts;
-    const int b = w / nchunks;
-    const int chunk = w - b * nchunks;
+    const int per = SLOTS ? early_tail_slots(a.max_k, p) : 1;
+    const int chunk = w % nchunks;
+    const int b = w / nchunks / per;
+    const int j = w / nchunks - b * per;
     const int rows_t = a.K + a.B;
     const int lo = a.cu[b], hi = a.cu[b + 1];
     const int k = hi - lo;
-    if (p > k || a.live[((p - 1) & 1) * a.B + b] == 0) return;
+    const bool first = j == 0 && chunk == 0;         // leaves the flag
+    if (p > k || a.live[((p - 1) & 1) * a.B + b] == 0) {
+        if (flag && first && threadIdx.x == 0) a.live[(p & 1) * a.B + b] = 0;
+        return;
+    }
+    int row = 0;
+    if (SLOTS) {
+        if (j <= k - p) {
+            row = lo + b + p + j;                      // target rows p .. k
+        } else {
+            const int i = p + (j - (k - p + 1));       // draft rows p .. k - 1
+            row = i < k ? rows_t + lo + i : -1;
+        }
+        if (row < 0 && !(flag && first)) return;
+    }
     if (threadIdx.x < 2) {
-        const bool live = live_test<BF16>(a, part, p, b, lo);
-        if (threadIdx.x == 0) s_live = live;
+        const bool live = live_test<BF16>(a, a.part, p, b, lo);
+        if (threadIdx.x == 0) {
+            if (flag && first) a.live[(p & 1) * a.B + b] = live ? 1 : 0;
+            s_live = live && row >= 0;
+        }
     }
     __syncthreads();
     if (!s_live) return;
-    for (int i = p; i <= k; ++i) {
-        row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part,
-                                  (lo + b + i) * nchunks + chunk, a.rpar);
-        if (i < k)
-            row_stats_body<BF16, VEC>(a.tgt, a.dft, rows_t, a.V, nchunks, a.c, part,
-                                      (rows_t + lo + i) * nchunks + chunk, a.rpar);
+    if (SLOTS) {
+        work(row, chunk);
+    } else {
+        for (int i = p; i <= k; ++i) {
+            work(lo + b + i, chunk);
+            if (i < k) work(rows_t + lo + i, chunk);
+        }
     }
+}
+
+// Early exit with the plain statistics (temperature only): launch p reads position p's
+// rows of the requests live at p; the last launch every later row of those still live.
+template <bool BF16, bool VEC>
+SD_DEV void pass_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+    const int nchunks = a.nparts;
+    pass_grid<BF16>(a, nchunks, p, w, [&](int row, int chunk) {
+        row_stats_body<BF16, VEC>(a.tgt, a.dft, a.K + a.B, a.V, nchunks, a.c, part,
+                                  row * nchunks + chunk, a.rpar);
+    });
+}
+
+template <bool BF16, bool VEC>
+SD_DEV void tail_body(const SampleArgs& a, RowPartial* __restrict__ part, int p, int w) {
+    const int nchunks = a.nparts;
+    tail_grid<BF16, false>(a, nchunks, p, w, false, [&](int row, int chunk) {
+        row_stats_body<BF16, VEC>(a.tgt, a.dft, a.K + a.B, a.V, nchunks, a.c, part,
+                                  row * nchunks + chunk, a.rpar);
+    });
 }
 
 // ---------------------------------------------------------------------------------------
@@ -2557,6 +2615,63 @@ SD_DEV void merge_pr_body(const TopkArgs& a, int row) {
 // Host side.
 // ---------------------------------------------------------------------------------------
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Early exit with a top-k / top-p transform (scalar or per request). The position
+// launches run the chunk select of the rows of live requests instead of their plain
+// statistics (P2: 0 top-k, 1 top-p alone, 2 per-request parameters; the generic select of
+// very large top_k has no chunk work), and a merge launch after each finishes those rows:
+// the liveness test of the next launch reads the merged rows (one partial and a threshold
+// per row), exactly what the decision reads.
+template <bool BF16, bool VEC, int P2>
+SD_DEV void chunk_of(const TopkArgs& ta, int row, int chunk) {
+    if constexpr (P2 == 2) {
+        chunk_pr_body<BF16, VEC>(ta, row, chunk);
+    } else {
+        if (ta.generic) return;
+        topk_chunk_body<BF16, VEC, P2>(ta, row, chunk, ChunkSel{ta.top_k, ta.c, P2 == 1});
+    }
+}
+
+template <bool BF16, bool VEC, int P2>
+SD_DEV void fpass_body(const SampleArgs& a, const TopkArgs& ta, int p, int w) {
+    pass_grid<BF16>(a, ta.nchunks, p, w,
+                    [&](int row, int chunk) { chunk_of<BF16, VEC, P2>(ta, row, chunk); });
+}
+
+template <bool BF16, bool VEC, int P2>
+SD_DEV void ftail_body(const SampleArgs& a, const TopkArgs& ta, int p, int w) {
+    tail_grid<BF16, true>(a, ta.nchunks, p, w, true,
+                    [&](int row, int chunk) { chunk_of<BF16, VEC, P2>(ta, row, chunk); });
+}
+
+// The merge of one row the launch before selected: at a position launch p < the tail's,
+// workgroup w is (request w / 2, side w % 2) at p; after the tail launch at p, workgroup w
+// is (request w / per, slot w % per) over the target rows p .. k_b (slots 0 .. k_b - p) and
+// the draft rows p .. k_b - 1 (the slots after), per = 2 (max_k - p) + 1. Requests not
+// live at p (the flag the launch before left) merge nothing.
+template <bool BF16, int NT, bool PR>
+SD_DEV void fmerge_body(const SampleArgs& a, const TopkArgs& ta, int p, int w, bool tail) {
+    const int rows_t = a.K + a.B;
+    const int per = tail ? early_tail_slots(a.max_k, p) : 2;
+    const int b = w / per;
+    const int j = w - b * per;
+    const int lo = a.cu[b], hi = a.cu[b + 1];
+    const int k = hi - lo;
+    if (p > k || a.live[(p & 1) * a.B + b] == 0) return;
+    int row;
+    if (!tail) {
+        if (j == 1 && p >= k) return;
+        row = j == 0 ? lo + b + p : rows_t + lo + p;
+    } else if (j <= k - p) {
+        row = lo + b + p + j;                          // target rows p .. k
+    } else {
+        const int i = p + (j - (k - p + 1));           // draft rows p .. k - 1
+        if (i >= k) return;
+        row = rows_t + lo + i;
+    }
+    if constexpr (PR) merge_pr_body<BF16, NT>(ta, row);
+    else topk_merge_body<BF16, NT>(ta, row, RowSel{ta.top_k, ta.topp_mode, ta.top_p, ta.c});
+}
 
 struct WsPlan {
     size_t part, thr, rec, wsum, live, tk_cnt, tk_cand, tk_kn, tk_ktok, tk_kkey, tk_cpart, tk_ctc,

@@ -157,9 +157,8 @@ def test_tree_workspace_and_host_validation_without_gpu(lib):
 
 
 def test_early_exit_host_validation_without_gpu(lib):
-    # the early-exit cycle takes temperature only (scalar or per request): top-k, top-p,
-    # their per-request arrays and the acceptance analytics are EINVAL before anything is
-    # enqueued; allowed
+    # the early-exit cycle takes every transform (temperature, top-k, top-p, scalar or per
+    # request); the acceptance analytics are EINVAL before anything is enqueued; allowed
     # arguments go on to the workspace check (8 bytes: EWORKSPACE), as specdec_cycle does
     c = binding.KvPagedCacheStruct(16, 2, 2, 8, 16, 64, 8, 16, 16, 16, 16, 16, 16)
 
@@ -172,13 +171,13 @@ def test_early_exit_host_validation_without_gpu(lib):
     analytics = binding.SpecdecDebug()
     analytics.accept_prob = 16
     eos_only = binding.SpecdecParams(None, None, None, 0, 16, 16)
-    for kw in (dict(top_k=10), dict(top_p=0.9), dict(top_p=0.5, top_k=999),
-               dict(pr=binding.SpecdecParams(None, 16, None, 4)),
-               dict(pr=binding.SpecdecParams(None, None, 16, 0)), dict(dbg=analytics)):
-        assert call(ee, **kw) == binding.SPECDEC_EINVAL, kw
-        assert call(full, **kw) == binding.SPECDEC_EWORKSPACE, kw
+    assert call(ee, dbg=analytics) == binding.SPECDEC_EINVAL
+    assert call(full, dbg=analytics) == binding.SPECDEC_EWORKSPACE
     for kw in (dict(), dict(top_k=1000), dict(top_k=0, top_p=1.0, pr=eos_only),
                dict(pr=binding.SpecdecParams(16, None, None, 0)),   # temperature array
+               dict(top_k=10), dict(top_p=0.9), dict(top_p=0.5, top_k=999),
+               dict(pr=binding.SpecdecParams(None, 16, None, 4)),
+               dict(pr=binding.SpecdecParams(None, None, 16, 0)),
                dict(dbg=binding.SpecdecDebug())):
         assert call(ee, **kw) == binding.SPECDEC_EWORKSPACE, kw
     # the checks both entry points share
@@ -188,7 +187,7 @@ def test_early_exit_host_validation_without_gpu(lib):
 
 
 def test_verify_early_exit_host_validation_without_gpu(lib):
-    # as the cycle's: temperature only, no analytics; allowed arguments reach the workspace
+    # as the cycle's: every transform, no analytics; allowed arguments reach the workspace
     # check
     def call(fn, top_k=0, top_p=1.0, pr=None, dbg=None):
         return fn(16, 16, 1, 16, 16, 16, 16, 4, 8, 2, 1000, 1.0, top_k, top_p,
@@ -198,11 +197,11 @@ def test_verify_early_exit_host_validation_without_gpu(lib):
     ee, full = lib.specdec_verify_early_exit, lib.specdec_verify
     analytics = binding.SpecdecDebug()
     analytics.expected_emitted = 16
-    for kw in (dict(top_k=10), dict(top_p=0.9), dict(pr=binding.SpecdecParams(None, None, 16, 0)),
-               dict(pr=binding.SpecdecParams(None, 16, None, 4)), dict(dbg=analytics)):
-        assert call(ee, **kw) == binding.SPECDEC_EINVAL, kw
-        assert call(full, **kw) == binding.SPECDEC_EWORKSPACE, kw
-    for kw in (dict(), dict(top_k=1000), dict(pr=binding.SpecdecParams(16, None, None, 0))):
+    assert call(ee, dbg=analytics) == binding.SPECDEC_EINVAL
+    assert call(full, dbg=analytics) == binding.SPECDEC_EWORKSPACE
+    for kw in (dict(), dict(top_k=1000), dict(pr=binding.SpecdecParams(16, None, None, 0)),
+               dict(top_k=10), dict(top_p=0.9), dict(pr=binding.SpecdecParams(None, None, 16, 0)),
+               dict(pr=binding.SpecdecParams(None, 16, None, 4))):
         assert call(ee, **kw) == binding.SPECDEC_EWORKSPACE, kw
 
 

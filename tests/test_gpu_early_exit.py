@@ -1,6 +1,7 @@
 """The early-exit cycle (specdec_cycle_early_exit: row statistics position by position,
-no row read past a request's first rejection) against the oracle and against the full
-cycle, on twin inputs and caches. Against the oracle: the flagged-margin rule of every
+no row read past a request's first rejection; with a top-k / top-p transform a chunk
+select and a merge per position) against the oracle and against the full cycle, on twin
+inputs and caches. Against the oracle: the flagged-margin rule of every
 verification test, with the debug values of rows past the GPU's accepted count allowed to
 be NaN ("Speculative decoding: accelerate LLM generation without changing its answers"
 §2-3: nothing after the first rejection is looked at). Against the full cycle: accepted
@@ -20,18 +21,19 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(vin, kv, early, top_k=None, eos=None, max_emit=None, cu=None, free_count=None,
-         plant=None, temps=None):
+         plant=None, temps=None, top_p=1.0, top_ks=None, top_ps=None, top_k_max=None):
     g_kv = KVOnDevice(kv, vin.B)
     if free_count is not None:
         g_kv.cache.free_count.fill_(free_count)
-    g_v = VerifyOnDevice(vin, top_k=top_k, eos=eos, max_emit=max_emit, temps=temps)
+    g_v = VerifyOnDevice(vin, top_k=top_k, eos=eos, max_emit=max_emit, temps=temps, top_p=top_p,
+                         top_ks=top_ks, top_ps=top_ps, top_k_max=top_k_max)
     if cu is not None:
         g_v.cu.copy_(torch.tensor(cu, dtype=torch.int32))
     if plant is not None:
         plant(g_v)
     dt = binding.SPECDEC_BF16 if vin.dtype == "bf16" else binding.SPECDEC_F32
     ws = torch.empty(binding.specdec_cycle_workspace_size(vin.B, vin.K, vin.V, dt, g_v.top_k,
-                                                          1.0, g_v.params),
+                                                          g_v.top_p, g_v.params),
                      dtype=torch.uint8, device=g_v.tgt.device)
     ws.fill_(0x5A if early else 0xA5)      # stale partials must not matter
     binding.specdec_cycle(g_kv.cache, g_kv.k_new, g_kv.v_new, g_v.tgt, g_v.dft, g_v.tokens,
@@ -39,7 +41,8 @@ def _run(vin, kv, early, top_k=None, eos=None, max_emit=None, cu=None, free_coun
                           top_k=g_v.top_k, out_tokens=g_v.out_tokens, num_accepted=g_v.num_acc,
                           num_emitted=g_v.num_emit, err_word=g_v.err, workspace=ws,
                           debug=g_v.dbg, eos_tokens=g_v.eos, max_emit=g_v.max_emit,
-                          temperatures=g_v.temps, early_exit=early)
+                          temperatures=g_v.temps, top_p=g_v.top_p, top_ks=g_v.top_ks,
+                          top_ps=g_v.top_ps, top_k_max=g_v.top_k_max, early_exit=early)
     r = g_v.result()
     u = g_v.u_acc.cpu().numpy()
     y = g_v.tokens.cpu().numpy()
@@ -105,11 +108,15 @@ def _compare(vin, full, early, u, y):
     return read, 2 * vin.K + vin.B
 
 
-def _against_oracle(vin, e, top_k=None, eos=None, max_emit=None, temps=None):
+def _against_oracle(vin, e, top_k=None, eos=None, max_emit=None, temps=None, top_p=1.0,
+                    top_ks=None, top_ps=None, top_k_max=None):
     """The early-exit outputs against the oracle on the same inputs."""
     T = vin.T if temps is None else temps
-    o = oracle_verify(vin, top_k=top_k, T=T, eos=eos, max_emit=max_emit)
-    rep = compare_verify(vin, e, o, T=T, top_k=top_k, eos=eos, max_emit=max_emit,
+    k = (vin.top_k if top_k is None else top_k) if top_ks is None else top_ks
+    pp = top_p if top_ps is None else top_ps
+    o = oracle_verify(vin, top_k=k, T=T, top_p=pp, top_k_max=top_k_max, eos=eos,
+                      max_emit=max_emit)
+    rep = compare_verify(vin, e, o, T=T, top_k=k, top_p=pp, eos=eos, max_emit=max_emit,
                          early_exit=True)
     log(f"[early-exit]   against the oracle: {rep}")
     rep.check()
@@ -121,7 +128,9 @@ def _both(vin, kv, **kw):
     if kw.get("cu") is None and kw.get("plant") is None:
         # offsets or device inputs changed after upload have no oracle counterpart here
         _against_oracle(vin, early[0], top_k=kw.get("top_k"), eos=kw.get("eos"),
-                        max_emit=kw.get("max_emit"), temps=kw.get("temps"))
+                        max_emit=kw.get("max_emit"), temps=kw.get("temps"),
+                        top_p=kw.get("top_p", 1.0), top_ks=kw.get("top_ks"),
+                        top_ps=kw.get("top_ps"), top_k_max=kw.get("top_k_max"))
     read, rows = _compare(vin, full[:3], early[:3], *full[3:])
     acc = full[0].num_accepted
     log(f"[early-exit]   rows read {read} of {rows}; accepted {int(acc[acc >= 0].sum())}, "
@@ -304,3 +313,76 @@ def test_verify_early_exit_equals_specdec_verify(wl, dtype, V, k_range, per_requ
     _against_oracle(vin, e, temps=kw.get("temps"))
     if per_request:
         assert f.req_flags[2] & binding.ERR_PARAM
+
+
+@pytest.mark.parametrize("case", ["topk64", "topk8_f32", "topp090", "topk_topp", "topp_f32",
+                                  "generic", "c4_full"])
+def test_early_exit_with_top_k_and_top_p(case):
+    # every position launch a chunk select plus a merge: top-k 64 (bf16, listed draws),
+    # top-k on fp32 rows, top-p alone (chunk exp-sums and bounds), top-p inside top-k, a
+    # top_k above the chunked select's limit (generic full-row select in the merge), and
+    # the benchmark's top-k workload at its full vocabulary
+    kw, over = {}, {}
+    wl, seed, B, V = "c4", 170, 16, 20000
+    if case == "topk64":
+        over = dict(top_k=64)
+    elif case == "topk8_f32":
+        wl, V, over = "c1", 5003, dict(top_k=8, k_range=(0, 6), k=6)
+    elif case == "topp090":
+        over, kw = dict(top_k=0), dict(top_p=0.9)
+    elif case == "topk_topp":
+        over, kw = dict(top_k=50), dict(top_p=0.8)
+    elif case == "topp_f32":
+        wl, V, over, kw = "c1", 4000, dict(top_k=0), dict(top_p=0.95)
+    elif case == "generic":
+        V, over = 6000, dict(top_k=2000)
+    else:
+        B, V = 40, None                      # the workload's vocabulary and transform
+    args = dict(seed=seed, B=B, **over)
+    if V is not None:
+        args.update(V=V)
+    vin = synth.make_verify(wl, **args)
+    kv = _small_kv(wl, vin, seed)
+    log(f"[early-exit] {case}: {vin.dtype} B={vin.B} V={vin.V} top_k={vin.top_k} {kw}")
+    _both(vin, kv, top_k=vin.top_k, **kw)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 20000), ("f32", 4001)])
+def test_early_exit_per_request_transforms(dtype, V):
+    # per-request top_k and top_p arrays (with an invalid temperature and an out-of-bound
+    # top_k failing only their requests)
+    vin = synth.make_verify("c4", seed=171, B=20, V=V, dtype=dtype, top_k=0)
+    kv = _small_kv("c4", vin, 171)
+    r = np.random.default_rng(171)
+    temps = r.choice([0.5, 0.8, 1.2], vin.B).astype(np.float32)
+    ks = r.choice([0, 4, 64, vin.V], vin.B).astype(np.int32)
+    ps = r.choice([1.0, 0.7, 0.95], vin.B).astype(np.float32)
+    temps[2] = 0.0
+    ks[5] = 100                       # above top_k_max
+    log(f"[early-exit] per-request top_k / top_p arrays, {dtype} V={V}")
+    f = _both(vin, kv, temps=temps, top_ks=ks, top_ps=ps, top_k_max=64)
+    assert f.req_flags[2] & binding.ERR_PARAM and f.req_flags[5] & binding.ERR_PARAM
+
+
+@pytest.mark.parametrize("case", ["topk", "topp", "per_request"])
+def test_verify_early_exit_with_transforms(case):
+    # specdec_verify_early_exit with a transform against specdec_verify and the oracle
+    vin = synth.make_verify("c4", seed=172, B=24, V=20000, top_k=64 if case == "topk" else 0)
+    kw = {}
+    if case == "topp":
+        kw = dict(top_p=0.9)
+    elif case == "per_request":
+        r = np.random.default_rng(172)
+        kw = dict(top_ks=r.choice([0, 8, 64], vin.B).astype(np.int32),
+                  top_ps=r.choice([1.0, 0.8], vin.B).astype(np.float32), top_k_max=64)
+    full = VerifyOnDevice(vin, **kw)
+    full.run()
+    early = VerifyOnDevice(vin, **kw)
+    early.ws.fill_(0x5A)
+    early.run(early_exit=True)
+    f, e = full.result(), early.result()
+    read, rows = _compare(vin, (f, None, None), (e, None, None), full.u_acc.cpu().numpy(),
+                          full.tokens.cpu().numpy())
+    log(f"[verify-early-exit] {case}: rows read {read} of {rows}")
+    _against_oracle(vin, e, top_k=vin.top_k, top_p=kw.get("top_p", 1.0), top_ks=kw.get("top_ks"),
+                    top_ps=kw.get("top_ps"), top_k_max=kw.get("top_k_max"))
