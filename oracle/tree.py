@@ -119,12 +119,17 @@ class TreeRequestResult:
     emitted: List[int]
     err: int
     res: Optional[TreeResult]
+    # top-p: the smallest nucleus margin of the rows the walk read (inf when off)
+    nucleus_margin: float = math.inf
 
 
 def tree_verify_request(t_rows, d_rows, parent, tokens, u_accept, u_sample, T: float,
-                        V: int) -> TreeRequestResult:
-    """One request from logits (fp64 rows by position); temperature transform, stable
-    softmax, rows transformed only where the walk reads them."""
+                        V: int, top_k: int = 0, top_p: float = 1.0) -> TreeRequestResult:
+    """One request from logits (fp64 rows by position); the decoding transform (temperature,
+    then top-k, then top-p) applied alike to every target and draft row ("Speculative
+    decoding: accelerate LLM generation without changing its answers", section 3's closing
+    paragraph and section 4: p and q must come from the same transform), stable softmax,
+    rows transformed only where the walk reads them."""
     n = len(tokens)
     err = 0
     if any(not (-1 <= int(pa) < j) for j, pa in enumerate(parent)):
@@ -137,11 +142,13 @@ def tree_verify_request(t_rows, d_rows, parent, tokens, u_accept, u_sample, T: f
         return TreeRequestResult(-1, [], [], err, None)
     cache = {}
     bad = []
+    margin = [math.inf]
 
     def row(which, v):
         key = (which, v)
         if key not in cache:
-            t = transform((t_rows if which == 0 else d_rows)[v], T, 0)
+            t = transform((t_rows if which == 0 else d_rows)[v], T, top_k, top_p)
+            margin[0] = min(margin[0], t.nucleus_margin)
             if not t.valid:
                 bad.append(v)
                 t = None
@@ -155,8 +162,8 @@ def tree_verify_request(t_rows, d_rows, parent, tokens, u_accept, u_sample, T: f
         res = tree_verify_probs(None, None, parent, tokens, u_accept, u_sample,
                                 P_of=lambda v: row(0, v), Q_of=lambda v: row(1, v))
     except _BadRow:
-        return TreeRequestResult(-1, [], [], ERR_NONFINITE, None)
-    return TreeRequestResult(len(res.path), res.path, res.emitted, res.flags, res)
+        return TreeRequestResult(-1, [], [], ERR_NONFINITE, None, margin[0])
+    return TreeRequestResult(len(res.path), res.path, res.emitted, res.flags, res, margin[0])
 
 
 class _BadRow(Exception):
@@ -175,9 +182,11 @@ class TreeBatchResult:
 
 def tree_verify_batch(target, draft, tree_tokens, tree_parent, cu_nodes, u_accept, u_sample,
                       T: float, max_nodes: int, dtype: str,
-                      requests: Optional[Sequence[int]] = None) -> TreeBatchResult:
+                      requests: Optional[Sequence[int]] = None, top_k: int = 0,
+                      top_p: float = 1.0) -> TreeBatchResult:
     """Packed trees: request b owns nodes cu[b] .. cu[b+1] - 1 and the target / draft rows
-    cu[b] + b + v for its positions v = 0 .. n_b (draft rows of leaves are not read)."""
+    cu[b] + b + v for its positions v = 0 .. n_b (draft rows of leaves are not read).
+    top_k (0 or >= V: off) and top_p (>= 1 or <= 0: off) apply to every row read."""
     cu = np.asarray(cu_nodes, dtype=np.int64)
     B = cu.shape[0] - 1
     N = int(np.asarray(tree_tokens).shape[0])
@@ -200,7 +209,8 @@ def tree_verify_batch(target, draft, tree_tokens, tree_parent, cu_nodes, u_accep
         d_rows = _decode_rows(draft[lo + b: hi + b + 1], dtype)
         r = tree_verify_request(t_rows, d_rows, [int(x) for x in tree_parent[lo:hi]],
                                 [int(x) for x in tree_tokens[lo:hi]],
-                                [float(u) for u in u_accept[lo:hi]], float(u_sample[b]), T, V)
+                                [float(u) for u in u_accept[lo:hi]], float(u_sample[b]), T, V,
+                                int(top_k), float(np.float32(top_p)))
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

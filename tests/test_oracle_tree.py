@@ -11,6 +11,11 @@
   an accepted node.
 * The cache keeps exactly the pending token and the accepted path, in path order; a chain
   with a path of its first a nodes leaves the cache as the linear rollback does.
+* Transforms (section 3's closing paragraph and section 4: the same temperature / top-k /
+  top-p on p and q): a chain under top-k, top-p or both gives what the linear oracle gives
+  on the same logits; top-k 1 (or a nucleus of one token) makes p and q point masses, and
+  the walk becomes greedy on the target: the first child carrying the target's argmax is
+  followed, and where none does (or at a leaf) that argmax is emitted.
 """
 
 import itertools
@@ -25,7 +30,7 @@ import pytest
 import oracle
 from oracle.tree import (ERR_TREE, children_of, tree_commit, tree_verify_batch,
                          tree_verify_probs)
-from oracle.verify import residual_weights, verify_probs
+from oracle.verify import residual_weights, verify_batch, verify_probs
 
 
 def _rand_dist(rng, V, den):
@@ -340,3 +345,85 @@ def test_commit_rejects_bad_paths():
     # request 0: path not increasing; request 1: a > n
     err = tree_commit(c, [2, 3], np.array([2, 1, -1, 0, 1]), cu)
     assert err & oracle.KV_ERR_ROLLBACK and c.seq_lens == before
+
+
+def _logit_tree(seed, B, V, n_lo, n_hi, branch):
+    rng = np.random.default_rng(seed)
+    n_b = rng.integers(n_lo, n_hi + 1, size=B)
+    cu = np.zeros(B + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(n_b)
+    N = int(cu[-1])
+    parent = np.zeros(N, dtype=np.int64)
+    for b in range(B):
+        for j in range(int(n_b[b])):
+            parent[cu[b] + j] = -1 if j == 0 else (
+                int(rng.integers(-1, j)) if rng.random() < branch else j - 1)
+    tgt = (rng.standard_normal((N + B, V)) * 2.0).astype(np.float32)
+    dft = (tgt + rng.standard_normal((N + B, V)) * 0.7).astype(np.float32)
+    return rng, cu, N, parent, tgt, dft
+
+
+@pytest.mark.parametrize("top_k,top_p", [(5, 1.0), (0, 0.8), (12, 0.9), (1, 1.0)])
+def test_chain_with_transforms_is_the_linear_rule(top_k, top_p):
+    B, V = 24, 40
+    rng, cu, N, parent, tgt, dft = _logit_tree(31 + top_k, B, V, 0, 6, 0.0)
+    # chains: every node the child of the previous one; tokens drawn from the transformed q
+    tokens = np.zeros(N, dtype=np.int64)
+    for b in range(B):
+        for j in range(int(cu[b + 1] - cu[b])):
+            q = oracle.verify.transform(dft[cu[b] + b + j].astype(np.float64), 0.9, top_k, top_p).p
+            tokens[cu[b] + j] = int(rng.choice(V, p=q / q.sum()))
+    u_acc = rng.random(N).astype(np.float32)
+    u_smp = rng.random(B).astype(np.float32)
+    tr = tree_verify_batch(tgt, dft, tokens, parent, cu, u_acc, u_smp, 0.9, 64, "f32",
+                           top_k=top_k, top_p=top_p)
+    # the linear layout: draft row of proposal i of request b at cu[b] + i
+    lin_d = np.concatenate([dft[cu[b] + b: cu[b + 1] + b] for b in range(B)]) if N else \
+        np.zeros((0, V), np.float32)
+    lin = verify_batch(tgt, lin_d, tokens, cu, u_acc, u_smp, 0.9, top_k, 64, "f32", top_p=top_p)
+    assert np.array_equal(tr.num_accepted, lin.num_accepted)
+    assert np.array_equal(tr.num_emitted, lin.num_emitted)
+    assert np.array_equal(tr.out_tokens, lin.out_tokens)
+    assert np.array_equal(tr.err, lin.err)
+    if 0 < top_p < 1:
+        for b in range(B):
+            m = min([r.nucleus_margin for r in lin.requests[b].rows_t[:int(tr.num_accepted[b]) + 1]] +
+                    [r.nucleus_margin for r in lin.requests[b].rows_d[:int(tr.num_accepted[b]) + 1]])
+            assert tr.requests[b].nucleus_margin >= m
+
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (0, 1e-6), (3, 1e-6)])
+def test_point_mass_transforms_make_the_walk_greedy(top_k, top_p):
+    B, V = 40, 30
+    rng, cu, N, parent, tgt, dft = _logit_tree(77, B, V, 0, 12, 0.6)
+    # distinct logits, and the draft's argmax never the target's at any position
+    for r in range(N + B):
+        tgt[r] = rng.permutation(V).astype(np.float32) * 0.25
+        dft[r] = rng.permutation(V).astype(np.float32) * 0.25
+        if np.argmax(dft[r]) == np.argmax(tgt[r]):
+            dft[r] = np.roll(dft[r], 1)
+    at = np.argmax(tgt, axis=1)
+    tokens = np.zeros(N, dtype=np.int64)
+    for b in range(B):
+        for j in range(int(cu[b + 1] - cu[b])):
+            pos = cu[b] + b + int(parent[cu[b] + j]) + 1
+            tokens[cu[b] + j] = at[pos] if rng.random() < 0.5 else int(rng.integers(0, V))
+    u_acc = rng.random(N).astype(np.float32)
+    u_smp = rng.random(B).astype(np.float32)
+    res = tree_verify_batch(tgt, dft, tokens, parent, cu, u_acc, u_smp, 1.3, 64, "f32",
+                            top_k=top_k, top_p=top_p)
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        kids = children_of([int(x) for x in parent[lo:hi]])
+        v, path, emitted = 0, [], []
+        while True:
+            a = int(at[lo + b + v])
+            nxt = next((j for j in kids[v] if int(tokens[lo + j]) == a), None)
+            if nxt is None:
+                emitted.append(a)
+                break
+            path.append(nxt)
+            emitted.append(a)
+            v = nxt + 1
+        r = res.requests[b]
+        assert r.path == path and r.emitted == emitted, (b, r.path, path, r.emitted, emitted)
