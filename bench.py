@@ -56,8 +56,7 @@ def parse():
                         "rollback as three calls on one stream; overlap: the three calls with "
                         "the append on a second stream after the logit rows are streamed; "
                         "early-exit: specdec_cycle_early_exit (row statistics position by "
-                        "position, no row read past a request's first rejection; temperature "
-                        "only)")
+                        "position, no row read past a request's first rejection)")
     p.add_argument("--timing-every", type=int, default=4,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
@@ -285,9 +284,13 @@ def tree_main(args):
         _b.build()
     binding.load_library()
     d = torch.device("cuda:0")
-    cfg = synth.TREE_WORKLOADS[args.workload]
+    cfg = dict(synth.TREE_WORKLOADS[args.workload])
+    top_k = args.top_k or 0
+    top_p = args.top_p
+    if args.batch:
+        cfg["B"] = args.batch
     print(f"# {args.workload}: drawing the synthetic trees", file=sys.stderr, flush=True)
-    tin = synth.make_tree(seed=args.seed, **cfg)
+    tin = synth.make_tree(seed=args.seed, top_k=top_k, **cfg)
     kv = synth.make_kv("c2", tin, seed=args.seed, cycles=args.warmup + args.steps + 2)
     print(f"# {args.workload}: inputs ready, timing", file=sys.stderr, flush=True)
     B, N, V = tin.B, tin.N, tin.V
@@ -316,8 +319,9 @@ def tree_main(args):
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
     kws = torch.empty(binding.kv_paged_append_workspace_size(B, N + B), dtype=torch.uint8, device=d)
-    tws = torch.empty(binding.specdec_tree_verify_workspace_size(B, N, tin.V), dtype=torch.uint8,
-                      device=d)
+    tws = torch.empty(binding.specdec_tree_verify_workspace_size(B, N, tin.V, binding.SPECDEC_BF16,
+                                                                 top_k, top_p),
+                      dtype=torch.uint8, device=d)
     n = args.warmup + args.steps
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in range(args.warmup, n)}
 
@@ -331,7 +335,8 @@ def tree_main(args):
         binding.specdec_tree_verify(tgt, dft, tokens, parent, cu, u_acc, u_smp,
                                     max_nodes=tin.max_nodes, temperature=tin.T, out_tokens=out,
                                     accepted_nodes=nodes, num_accepted=nacc, num_emitted=nemit,
-                                    err_word=err, workspace=tws, team=args.team)
+                                    err_word=err, workspace=tws, team=args.team, top_k=top_k,
+                                    top_p=top_p)
         if e:
             e[2].record()
         binding.kv_tree_commit(cache, nacc, nodes, cu)
@@ -368,7 +373,11 @@ def tree_main(args):
     a = nacc.cpu().numpy()
     path = nodes.cpu().numpy()
     row = V * 2
-    walk = 0
+    filt = 0 < top_k < V or 0 < top_p < 1
+    # top-k / top-p: the select reads every target and draft row once, and the walk takes
+    # each position's statistics from it instead of its own pass
+    walk = 2 * (N + B) * row if filt else 0
+    stats = 0 if filt else 1
     for b in range(B):
         lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
         par = tin.parent[lo:hi]
@@ -379,9 +388,9 @@ def tree_main(args):
         steps = list(path[lo: lo + max(int(a[b]), 0)]) + [None]
         for nxt in steps:
             if not kids[v]:
-                walk += 2 * row                                   # stats + bonus pass
+                walk += (stats + 1) * row                         # stats + bonus pass
                 break
-            walk += 2 * row                                       # target + draft stats
+            walk += stats * 2 * row                               # target + draft stats
             rej = kids[v].index(nxt) if nxt is not None else len(kids[v])
             walk += rej * 2 * row                                 # residual passes
             if nxt is None:
@@ -397,7 +406,9 @@ def tree_main(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": (f"{args.workload}: B={B} trees of U{{{cfg['n_range'][0]}.."
-                                f"{cfg['n_range'][1]}}} nodes (N={N}), V={V} bf16 T={tin.T:g}; "
+                                f"{cfg['n_range'][1]}}} nodes (N={N}), V={V} bf16 T={tin.T:g}"
+                                + (f" top_k={top_k}" if 0 < top_k < V else "")
+                                + (f" top_p={top_p:g}" if 0 < top_p < 1 else "") + "; "
                                 f"paged KV {kv.L}x{kv.H}x{kv.D} bf16, block {kv.block_size}"),
                    "global_batch": B, "parallelism": "single GPU"},
         "tree": {"team": args.team or "auto", "append_ms": append_ms, "verify_ms": verify_ms,

@@ -180,10 +180,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, f32, pp,
                                          vp, vp, vp, vp, ctypes.POINTER(SpecdecDebug), vp]
     lib.specdec_cycle_static.restype = ctypes.c_int
-    lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32]
+    lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
     lib.specdec_tree_verify_workspace_size.restype = sz
     lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                        vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+                                        i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.specdec_tree_verify.restype = ctypes.c_int
     lib.kv_tree_commit.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32, vp]
     lib.kv_tree_commit.restype = ctypes.c_int
@@ -548,8 +548,10 @@ class HipEvent:
             pass
 
 
-def specdec_tree_verify_workspace_size(B: int, N: int, V: int) -> int:
-    return int(load_library().specdec_tree_verify_workspace_size(B, N, V))
+def specdec_tree_verify_workspace_size(B: int, N: int, V: int, dtype: int = SPECDEC_BF16,
+                                       top_k: int = 0, top_p: float = 1.0) -> int:
+    return int(load_library().specdec_tree_verify_workspace_size(B, N, V, dtype, top_k,
+                                                                 float(top_p)))
 
 
 def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
@@ -559,7 +561,7 @@ def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                         accepted_nodes: torch.Tensor, num_accepted: torch.Tensor,
                         num_emitted: torch.Tensor, err_word: torch.Tensor,
                         workspace: torch.Tensor, req_flags: Optional[torch.Tensor] = None,
-                        team: int = 0) -> None:
+                        team: int = 0, top_k: int = 0, top_p: float = 1.0) -> None:
     """Enqueue the verification of one draft tree per request (shapes as in the header);
     ``team`` workgroups share each request's walk (0: automatic)."""
     lib = load_library()
@@ -588,7 +590,8 @@ def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     st = lib.specdec_tree_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(tree_tokens), _ptr(tree_parent),
         _ptr(cu_nodes), _ptr(u_accept), _ptr(u_sample), B, N, max_nodes, V, float(temperature),
-        _ptr(out_tokens), _ptr(accepted_nodes) if N else None, _ptr(num_accepted),
+        int(top_k), float(top_p), _ptr(out_tokens), _ptr(accepted_nodes) if N else None,
+        _ptr(num_accepted),
         _ptr(num_emitted),
         _ptr(err_word), _ptr(req_flags) if req_flags is not None else None, int(team),
         _ptr(workspace), workspace.numel(), _stream(dev))

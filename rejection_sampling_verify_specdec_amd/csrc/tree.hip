@@ -1,6 +1,9 @@
 // Verification of draft trees for gfx950: a team of 1024-thread workgroups walks each
-// request's tree, sharing every pass over a row (tree_dev.h). The cache step that keeps
-// the accepted path is kv_tree_commit (kv.hip).
+// request's tree, sharing every pass over a row (tree_dev.h). With top-k or top-p, the
+// linear path's chunk select and merge first give every target and draft row its
+// threshold and the max and exp-sum of its kept tokens, which the walk reads in place of
+// its own statistics passes. The cache step that keeps the accepted path is kv_tree_commit
+// (kv.hip).
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -29,27 +32,54 @@ __global__ void k_tree_reset(int* ctr, int n) {
     if (i < n) ctr[i] = 0;
 }
 
+// the select of every row (target rows first, then draft rows), as in the linear path
+template <bool BF16, bool VEC, bool P2>
+__global__ __launch_bounds__(kTkNT) void k_tree_select(TopkArgs a) {
+    topk_chunk_body<BF16, VEC, P2 ? 1 : 0>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks,
+                                          ChunkSel{a.top_k, a.c, P2});
+}
+
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge(TopkArgs a) {
+    topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
+}
+
 struct TreeWs {
     size_t ctr_bytes, ring_bytes, total;
     int nchunk, nsub, slot;
+    WsPlan sel;                         // top-k / top-p: offsets from the workspace start
 };
 
-static bool tree_ws(int32_t B, int32_t N, int32_t V, TreeWs* w) {
+static bool tree_ws(int32_t B, int32_t N, int32_t V, int32_t dtype, int32_t top_k, float top_p,
+                    TreeWs* w) {
     if (B < 1 || N < 0 || V < 1 || V > SPECDEC_MAX_V) return false;
+    if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return false;
+    if (top_p != top_p) return false;
     w->nchunk = (V + kTreeChunk - 1) / kTreeChunk;
     w->nsub = (V + kTreeSub - 1) / kTreeSub;
     w->slot = 64 * w->nchunk;           // >= 4 * nsub (weights); 4 per wave-chunk (stats)
     w->ctr_bytes = ((size_t)B * kTreeCtrStride * sizeof(int) + 255) & ~(size_t)255;
     w->ring_bytes = ((size_t)N + 2 * (size_t)B) * w->slot * sizeof(double);
-    w->total = w->ctr_bytes + w->ring_bytes;
+    size_t off = align256(w->ctr_bytes + w->ring_bytes);
+    w->sel = plan_transform(V, dtype, top_k, top_p, nullptr);
+    if (w->sel.filter) {
+        const size_t rows = 2 * ((size_t)N + B);
+        w->sel.part = off;
+        off = align256(off + rows * sizeof(RowPartial));
+        w->sel.thr = off;
+        off = align256(off + rows * sizeof(float));
+        off = plan_select(w->sel, off, rows, (size_t)N + B, dtype, false);
+    }
+    w->total = off;
     return true;
 }
 
 }  // namespace sd
 
-extern "C" size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V) {
+extern "C" size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V,
+                                                     int32_t dtype, int32_t top_k, float top_p) {
     sd::TreeWs w;
-    return sd::tree_ws(B, N, V, &w) ? w.total : 0;
+    return sd::tree_ws(B, N, V, dtype, top_k, top_p, &w) ? w.total : 0;
 }
 
 extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_logits,
@@ -57,7 +87,7 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
                                    const int32_t* tree_parent, const int32_t* cu_nodes,
                                    const float* u_accept, const float* u_sample, int32_t B,
                                    int32_t N, int32_t max_nodes, int32_t V, float temperature,
-                                   int32_t* out_tokens, int32_t* accepted_nodes,
+                                   int32_t top_k, float top_p, int32_t* out_tokens, int32_t* accepted_nodes,
                                    int32_t* num_accepted, int32_t* num_emitted,
                                    int32_t* err_word, int32_t* req_flags, int32_t team,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -68,6 +98,7 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     if ((long long)N > (long long)B * max_nodes) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
     if (!(temperature > 0.0f) || !isfinite(temperature)) return SPECDEC_EINVAL;
+    if (top_p != top_p) return SPECDEC_EINVAL;
     if (!target_logits || !draft_logits || !cu_nodes || !u_sample || !out_tokens ||
         !num_accepted || !num_emitted || !err_word)
         return SPECDEC_EINVAL;
@@ -77,7 +108,9 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
     if (team < 0 || team > kTreeMaxTeam) return SPECDEC_EINVAL;
     TreeWs w;
-    if (!tree_ws(B, N, V, &w)) return SPECDEC_EINVAL;
+    if (!tree_ws(B, N, V, dtype, top_k, top_p, &w)) return SPECDEC_EINVAL;
+    const size_t rows = 2 * ((size_t)N + B);
+    if (w.sel.filter && rows * w.sel.nchunks > 0x7fffffffu) return SPECDEC_EINVAL;
     if (!workspace || ((uintptr_t)workspace & 15) != 0 || workspace_bytes < w.total)
         return SPECDEC_EWORKSPACE;
     int G = team;
@@ -121,6 +154,9 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     a.team = G;
     // testing only: a smaller bound on the team's wait forces SPECDEC_ERR_TEAM from the host
     a.spin_limit = kTreeSpinLimit;
+    a.thr = w.sel.filter ? reinterpret_cast<const float*>(ws + w.sel.thr) : nullptr;
+    a.part = w.sel.filter ? reinterpret_cast<const RowPartial*>(ws + w.sel.part) : nullptr;
+    a.rows = N + B;
     if (const char* lim = getenv("SPECDEC_TREE_SPIN_LIMIT")) {
         char* end = nullptr;
         const long v = strtol(lim, &end, 10);
@@ -130,6 +166,34 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     const int grid = (B + 7) / 8 * 8 * G;
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_tree_reset, dim3((nctr + 255) / 256), dim3(256), 0, stream, a.ctr, nctr);
+    if (w.sel.filter) {
+        const TopkArgs ta = topk_args(a.tgt, a.dft, N + B, V, top_p, c, w.sel, ws);
+        const dim3 g((unsigned)(rows * w.sel.nchunks));
+        if (!ta.generic) {
+            const bool p2 = w.sel.topp_mode == 2;
+            if (dtype == SPECDEC_BF16) {
+                if (vec) {
+                    if (p2) hipLaunchKernelGGL((k_tree_select<true, true, true>), g, dim3(kTkNT), 0, stream, ta);
+                    else hipLaunchKernelGGL((k_tree_select<true, true, false>), g, dim3(kTkNT), 0, stream, ta);
+                } else {
+                    if (p2) hipLaunchKernelGGL((k_tree_select<true, false, true>), g, dim3(kTkNT), 0, stream, ta);
+                    else hipLaunchKernelGGL((k_tree_select<true, false, false>), g, dim3(kTkNT), 0, stream, ta);
+                }
+            } else {
+                if (vec) {
+                    if (p2) hipLaunchKernelGGL((k_tree_select<false, true, true>), g, dim3(kTkNT), 0, stream, ta);
+                    else hipLaunchKernelGGL((k_tree_select<false, true, false>), g, dim3(kTkNT), 0, stream, ta);
+                } else {
+                    if (p2) hipLaunchKernelGGL((k_tree_select<false, false, true>), g, dim3(kTkNT), 0, stream, ta);
+                    else hipLaunchKernelGGL((k_tree_select<false, false, false>), g, dim3(kTkNT), 0, stream, ta);
+                }
+            }
+        }
+        if (dtype == SPECDEC_BF16)
+            hipLaunchKernelGGL((k_tree_merge<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+        else
+            hipLaunchKernelGGL((k_tree_merge<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+    }
     if (dtype == SPECDEC_BF16) {
         if (vec) hipLaunchKernelGGL((k_tree_verify<true, true>), dim3(grid), dim3(kTreeNT), 0, stream, a);
         else hipLaunchKernelGGL((k_tree_verify<true, false>), dim3(grid), dim3(kTreeNT), 0, stream, a);

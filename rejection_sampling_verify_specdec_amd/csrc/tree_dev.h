@@ -58,6 +58,12 @@ struct TreeArgs {
     int slot;                // doubles per pass: 64 * nchunk (4 per wave and chunk)
     int team;                // workgroups per request
     int spin_limit;          // polls a member waits for the others before it gives up
+    // top-k / top-p: every row's threshold and its kept tokens' max and exp-sum, from the
+    // select launches (target row r at r, draft row r at rows + r); null with temperature
+    // alone, where the walk takes each position's statistics itself
+    const float* thr;
+    const RowPartial* part;
+    int rows;                // N + B
 };
 
 // Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
@@ -104,9 +110,19 @@ SD_DEV Tok8<BF16> load8r(const uint8_t* __restrict__ row, int V, int i0) {
     return t;
 }
 
-// The exponential form of the linear path: p(x) = exp2(z c - mc) * al, 0 for z = -inf.
-SD_DEV double tree_prob(float z, float c, float mc, double al) {
-    return z > -INFINITY ? (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al : 0.0;
+// A position's two rows as the walk weighs them: p(x) = exp2(z c - mct) * alt for a target
+// logit z >= tt, 0 below it; q(x) likewise from the draft row (tt = td = -inf without top-k
+// or top-p).
+struct RowNorm {
+    float mct, mcd, tt, td;
+    double alt, ald;
+};
+
+// The exponential form of the linear path: p(x) = exp2(z c - mc) * al, 0 for z = -inf or
+// below the row's threshold.
+SD_DEV double tree_prob(float z, float c, float mc, double al, float thr) {
+    return (z > -INFINITY && z >= thr) ? (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al
+                                       : 0.0;
 }
 
 // Residual chain: f_0 = p, f_{s+1} = max(0, f_s - q) / W_s, with Winv[s] = 1 / W_s.
@@ -120,11 +136,11 @@ enum : int { TW_P = 0, TW_RESID = 1, TW_TESTED = 2 };
 
 // Weight of a token for the draw or the residual mass: TW_P p (bonus), TW_RESID
 // max(0, f_{t-1} - q) (the residual after t rejections, unnormalized), TW_TESTED f_t.
-SD_DEV double tree_weight(float zt, float zd, int kind, int t, float c, float mct, double alt,
-                          float mcd, double ald, const double* W) {
-    const double p = tree_prob(zt, c, mct, alt);
+SD_DEV double tree_weight(float zt, float zd, int kind, int t, float c, const RowNorm& r,
+                          const double* W) {
+    const double p = tree_prob(zt, c, r.mct, r.alt, r.tt);
     if (kind == TW_P) return p;
-    const double q = tree_prob(zd, c, mcd, ald);
+    const double q = tree_prob(zd, c, r.mcd, r.ald, r.td);
     if (kind == TW_TESTED) return tree_chain(p, q, W, t);
     return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
 }
@@ -156,10 +172,14 @@ struct TeamLds {
 };
 
 // The ring and the counters are shared by workgroups on different XCDs, whose L2 caches
-// are not coherent with each other: every access to them is an agent-scope atomic (the
-// hardware keeps those coherent without writing back or invalidating whole caches). A
-// writer waits for its ring stores to complete before the workgroup barrier that precedes
-// the done count; a reader loads the ring only after it has seen the count.
+// are not coherent with each other. Every ring access is an agent-scope atomic, and the
+// pass is published by release / acquire at agent scope: the waves' ring stores precede
+// the workgroup barrier, after which one thread adds the member's chunks to the done count
+// with release order; the waiting thread polls the count with relaxed loads, then issues
+// an agent-scope acquire fence before the barrier that lets its workgroup read the ring.
+// Happens-before thus runs writer waves -> barrier -> release -> acquire -> barrier ->
+// reader waves, each link at a scope that holds both ends. (On gfx950 the release writes
+// back and the acquire invalidates the XCD's L2: measured 8% of the walk at 128 requests.)
 // A team of one (solo) shares nothing: plain stores and loads, ordered by the workgroup
 // barrier.
 SD_DEV void ring_put(double* p, double x, bool solo) {
@@ -199,15 +219,16 @@ SD_DEV void wave_stats2(const T8& za, const T8& zb, float c, double* m_out, doub
     *s_out = wave_sum((double)acc);
 }
 
-// Weight of a token in a pass (tree_weight without the -inf tests: exp2 of -inf is 0).
-SD_DEV double team_prob(float z, float c, float mc, double al) {
-    return (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al;
+// Weight of a token in a pass (tree_weight without the -inf tests: exp2 of -inf is 0, and
+// -inf >= -inf holds).
+SD_DEV double team_prob(float z, float c, float mc, double al, float thr) {
+    return z >= thr ? (double)__builtin_amdgcn_exp2f(fmaf(z, c, -mc)) * al : 0.0;
 }
-SD_DEV double team_weight(float zt, float zd, int kind, int t, float c, float mct, double alt,
-                          float mcd, double ald, const double* W) {
-    const double p = team_prob(zt, c, mct, alt);
+SD_DEV double team_weight(float zt, float zd, int kind, int t, float c, const RowNorm& r,
+                          const double* W) {
+    const double p = team_prob(zt, c, r.mct, r.alt, r.tt);
     if (kind == TW_P) return p;
-    const double q = team_prob(zd, c, mcd, ald);
+    const double q = team_prob(zd, c, r.mcd, r.ald, r.td);
     if (kind == TW_TESTED) return tree_chain(p, q, W, t);
     return fmax(tree_chain(p, q, W, t - 1) - q, 0.0);
 }
@@ -266,8 +287,7 @@ enum : int { KC_STATS = 0, KC_P = 1, KC_RESID1 = 2, KC_CHAIN = 3 };
 // slot[wc] = the wave's sum (sub-chunk q, 2048 tokens, is entries 2q and 2q + 1).
 template <bool BF16, int KC>
 SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kind, bool both,
-                         int t, float mct, double alt, float mcd, double ald, const double* W,
-                         double* slot) {
+                         int t, const RowNorm& r, const double* W, double* slot) {
     const int tid = threadIdx.x, w = tid / kWave, l = tid % kWave;
     const int wc = ch * (kTreeNT / kWave) + w;
     const bool solo = a.team == 1;
@@ -289,23 +309,23 @@ SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kin
         double s0 = 0.0, s1 = 0.0;
         if constexpr (KC == KC_P) {              // the bonus: p alone
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s0 += team_prob(q.t0.get(e), a.c, mct, alt);
+            for (int e = 0; e < 8; ++e) s0 += team_prob(q.t0.get(e), a.c, r.mct, r.alt, r.tt);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s1 += team_prob(q.t1.get(e), a.c, mct, alt);
+            for (int e = 0; e < 8; ++e) s1 += team_prob(q.t1.get(e), a.c, r.mct, r.alt, r.tt);
         } else if constexpr (KC == KC_RESID1) {  // the first residual, max(0, p - q)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s0 += fmax(team_prob(q.t0.get(e), a.c, mct, alt) -
-                           team_prob(q.d0.get(e), a.c, mcd, ald), 0.0);
+                s0 += fmax(team_prob(q.t0.get(e), a.c, r.mct, r.alt, r.tt) -
+                           team_prob(q.d0.get(e), a.c, r.mcd, r.ald, r.td), 0.0);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                s1 += fmax(team_prob(q.t1.get(e), a.c, mct, alt) -
-                           team_prob(q.d1.get(e), a.c, mcd, ald), 0.0);
+                s1 += fmax(team_prob(q.t1.get(e), a.c, r.mct, r.alt, r.tt) -
+                           team_prob(q.d1.get(e), a.c, r.mcd, r.ald, r.td), 0.0);
         } else {                                 // longer residual chains, tested weights
 #pragma unroll 2
             for (int e = 0; e < 8; ++e) {
-                s0 += team_weight(q.t0.get(e), q.d0.get(e), kind, t, a.c, mct, alt, mcd, ald, W);
-                s1 += team_weight(q.t1.get(e), q.d1.get(e), kind, t, a.c, mct, alt, mcd, ald, W);
+                s0 += team_weight(q.t0.get(e), q.d0.get(e), kind, t, a.c, r, W);
+                s1 += team_weight(q.t1.get(e), q.d1.get(e), kind, t, a.c, r, W);
             }
         }
         const double sw = wave_sum(s0 + s1);
@@ -318,8 +338,8 @@ SD_DEV void team_compute(const TreeArgs& a, const Quad<BF16>& q, int ch, int kin
 // bounds-tested loads.
 template <bool BF16, bool VEC, bool DR, int KC>
 SD_DEV void team_slice(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int c0,
-                       int c1, int kind, bool both, int t, float mct, double alt, float mcd,
-                       double ald, const double* W, double* slot) {
+                       int c1, int kind, bool both, int t, const RowNorm& r, const double* W,
+                       double* slot) {
     constexpr bool PIPE = KC != KC_CHAIN;
     const int cfull = VEC ? min(c1, a.V / kTreeChunk) : c0;
     if (c0 < cfull) {
@@ -327,20 +347,20 @@ SD_DEV void team_slice(const TreeArgs& a, const uint8_t* trow, const uint8_t* dr
             Quad<BF16> cur = team_load<BF16, VEC, DR, true>(a, trow, drow, c0);
             for (int ch = c0; ch + 1 < cfull; ++ch) {
                 const Quad<BF16> nxt = team_load<BF16, VEC, DR, true>(a, trow, drow, ch + 1);
-                team_compute<BF16, KC>(a, cur, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+                team_compute<BF16, KC>(a, cur, ch, kind, both, t, r, W, slot);
                 cur = nxt;
             }
-            team_compute<BF16, KC>(a, cur, cfull - 1, kind, both, t, mct, alt, mcd, ald, W, slot);
+            team_compute<BF16, KC>(a, cur, cfull - 1, kind, both, t, r, W, slot);
         } else {
             for (int ch = c0; ch < cfull; ++ch) {
                 const Quad<BF16> q = team_load<BF16, VEC, DR, true>(a, trow, drow, ch);
-                team_compute<BF16, KC>(a, q, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+                team_compute<BF16, KC>(a, q, ch, kind, both, t, r, W, slot);
             }
         }
     }
     for (int ch = max(c0, cfull); ch < c1; ++ch) {
         const Quad<BF16> q = team_load<BF16, VEC, DR, false>(a, trow, drow, ch);
-        team_compute<BF16, KC>(a, q, ch, kind, both, t, mct, alt, mcd, ald, W, slot);
+        team_compute<BF16, KC>(a, q, ch, kind, both, t, r, W, slot);
     }
 }
 
@@ -352,9 +372,8 @@ SD_DEV void team_slice(const TreeArgs& a, const uint8_t* trow, const uint8_t* dr
 // bound.
 template <bool BF16, bool VEC>
 SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int k,
-                      int kind, bool both, int t, float mct, double alt, float mcd, double ald,
-                      const double* W, double* slot, int* claim, int* done, TeamLds& s,
-                      int& par) {
+                      int kind, bool both, int t, const RowNorm& r, const double* W, double* slot,
+                      int* claim, int* done, TeamLds& s, int& par) {
     const int tid = threadIdx.x, l = tid % kWave;
     const int C = a.nchunk, S = (C + a.team - 1) / a.team, NS = (C + S - 1) / S;
     const bool solo = a.team == 1;
@@ -368,20 +387,18 @@ SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* dro
         const int c0 = (tk - k * NS) * S, c1 = min(C, c0 + S);
         if (kind == TK_STATS) {
             if (both)
-                team_slice<BF16, VEC, true, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, mct,
-                                                      alt, mcd, ald, W, slot);
+                team_slice<BF16, VEC, true, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, r, W,
+                                                      slot);
             else
-                team_slice<BF16, VEC, false, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, mct,
-                                                       alt, mcd, ald, W, slot);
+                team_slice<BF16, VEC, false, KC_STATS>(a, trow, drow, c0, c1, kind, both, t, r, W,
+                                                       slot);
         } else if (kind == TW_P) {
-            team_slice<BF16, VEC, false, KC_P>(a, trow, drow, c0, c1, kind, both, t, mct, alt,
-                                               mcd, ald, W, slot);
+            team_slice<BF16, VEC, false, KC_P>(a, trow, drow, c0, c1, kind, both, t, r, W, slot);
         } else if (kind == TW_RESID && t == 1) {
-            team_slice<BF16, VEC, true, KC_RESID1>(a, trow, drow, c0, c1, kind, both, t, mct,
-                                                   alt, mcd, ald, W, slot);
+            team_slice<BF16, VEC, true, KC_RESID1>(a, trow, drow, c0, c1, kind, both, t, r, W,
+                                                   slot);
         } else {
-            team_slice<BF16, VEC, true, KC_CHAIN>(a, trow, drow, c0, c1, kind, both, t, mct, alt,
-                                                  mcd, ald, W, slot);
+            team_slice<BF16, VEC, true, KC_CHAIN>(a, trow, drow, c0, c1, kind, both, t, r, W, slot);
         }
         mine += c1 - c0;
         if (solo) break;
@@ -394,10 +411,9 @@ SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* dro
         __syncthreads();                              // the partials are visible to the WG
         return true;
     }
-    if (l == 0) __builtin_amdgcn_s_waitcnt(0);        // this wave's ring stores completed
     __syncthreads();
     if (tid == 0) {
-        if (mine) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (mine) __hip_atomic_fetch_add(done, mine, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         int it = 0, to = 0;
         while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (k + 1) * C) {
             if (++it > a.spin_limit) {
@@ -406,6 +422,7 @@ SD_DEV bool team_pass(const TreeArgs& a, const uint8_t* trow, const uint8_t* dro
             }
             __builtin_amdgcn_s_sleep(2);
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         s.timeout = to;
     }
     __syncthreads();
@@ -503,8 +520,8 @@ SD_DEV double team_weight_total(const TreeArgs& a, const double* slot, double* r
 // last x with positive weight if rounding leaves none.
 template <bool BF16, bool VEC>
 SD_DEV int tree_draw(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow, int kind,
-                     int t, float mct, double alt, float mcd, double ald, const double* W,
-                     const double* sub, float u, double* red, int* redi) {
+                     int t, const RowNorm& r, const double* W, const double* sub, float u,
+                     double* red, int* redi) {
     const int tid = threadIdx.x;
     const int nsub = (a.V + kTreeSub - 1) / kTreeSub;
     // the sub-chunk holding t: exclusive prefix of the sub-chunk sums, fixed order
@@ -535,8 +552,7 @@ SD_DEV int tree_draw(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow
         if (kind != TW_P) load8<BF16, VEC>(drow, a.V, i0, zd);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            wv[e] = tree_weight(zt[e], kind != TW_P ? zd[e] : -INFINITY, kind, t, a.c, mct, alt,
-                                mcd, ald, W);
+            wv[e] = tree_weight(zt[e], kind != TW_P ? zd[e] : -INFINITY, kind, t, a.c, r, W);
             run += wv[e];
         }
     } else {
@@ -618,8 +634,8 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
         int par = 0;                                 // tl.tk[par]: the current ticket
         int k = 0;      // passes so far: at most n + 2 (ring slots), checked before each
         int wslot = -1, kind = TW_RESID, t = 0;      // the final draw's slot, kind, residual
-        float mct = 0.f, mcd = 0.f;
-        double alt = 0.0, ald = 0.0;
+        RowNorm rn{0.f, 0.f, -INFINITY, -INFINITY, 0.0, 0.0};
+        const RowNorm none{0.f, 0.f, -INFINITY, -INFINITY, 0.0, 0.0};
         const uint8_t* trow = nullptr;
         const uint8_t* drow = nullptr;
         int v = 0;                                   // position: 0 root, 1 + j node j
@@ -640,34 +656,49 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
             }
             __syncthreads();
             unsigned long long kids = s_kids;
-            if (k > n + 1 ||
-                !team_pass<BF16, VEC>(a, trow, drow, k, TK_STATS, kids != 0, 0, 0.f, 0.0, 0.f,
-                                      0.0, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
-                flags |= SPECDEC_ERR_TEAM;
-                break;
+            float mt, md = 0.f;
+            double St, Sd = 1.0;
+            if (a.part) {
+                // top-k / top-p: the select launches' statistics of the kept tokens
+                const int rt = lo + b + v;
+                const RowPartial pt = a.part[rt];
+                mt = pt.m;
+                St = pt.s;
+                rn.tt = a.thr[rt];
+                if (kids) {
+                    const RowPartial pd = a.part[a.rows + rt];
+                    md = pd.m;
+                    Sd = pd.s;
+                    rn.td = a.thr[a.rows + rt];
+                }
+            } else {
+                if (k > n + 1 ||
+                    !team_pass<BF16, VEC>(a, trow, drow, k, TK_STATS, kids != 0, 0, none, sW,
+                                          ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                    flags |= SPECDEC_ERR_TEAM;
+                    break;
+                }
+                team_stats_final(a, ring + (size_t)k * a.slot, kids != 0, &mt, &St, &md, &Sd,
+                                 red2, redf2, redi);
+                if (!kids) {
+                    md = 0.f;
+                    Sd = 1.0;
+                }
+                ++k;
             }
-            float mt, md;
-            double St, Sd;
-            team_stats_final(a, ring + (size_t)k * a.slot, kids != 0, &mt, &St, &md, &Sd, red2,
-                             redf2, redi);
-            if (!kids) {
-                md = 0.f;
-                Sd = 1.0;
-            }
-            ++k;
             if (!(St > 0.0 && St < INFINITY && mt > -INFINITY) ||
                 (kids && !(Sd > 0.0 && Sd < INFINITY && md > -INFINITY))) {
                 flags |= SPECDEC_ERR_NONFINITE;
                 break;
             }
-            mct = mt * a.c;
-            mcd = md * a.c;
-            alt = exp2(-(double)fmaf(mt, a.c, -mct)) / St;
-            ald = kids ? exp2(-(double)fmaf(md, a.c, -mcd)) / Sd : 0.0;
+            rn.mct = mt * a.c;
+            rn.mcd = md * a.c;
+            rn.alt = exp2(-(double)fmaf(mt, a.c, -rn.mct)) / St;
+            rn.ald = kids ? exp2(-(double)fmaf(md, a.c, -rn.mcd)) / Sd : 0.0;
             if (!kids) {                             // bonus from p at a leaf
                 if (k > n + 1 ||
-                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_P, false, 0, mct, alt, mcd, ald,
-                                          sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_P, false, 0, rn, sW,
+                                          ring + (size_t)k * a.slot, claim, done, tl, par)) {
                     flags |= SPECDEC_ERR_TEAM;
                     break;
                 }
@@ -684,8 +715,8 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 kids &= kids - 1;
                 if (tid == 0) {
                     const float zt = s_zt[j], zd = s_zd[j];
-                    const double q = tree_prob(zd, a.c, mcd, ald);
-                    const double P = tree_chain(tree_prob(zt, a.c, mct, alt), q, sW, t);
+                    const double q = tree_prob(zd, a.c, rn.mcd, rn.ald, rn.td);
+                    const double P = tree_chain(tree_prob(zt, a.c, rn.mct, rn.alt, rn.tt), q, sW, t);
                     if (q == 0.0) s_flags |= SPECDEC_ERR_QZERO;
                     s_next = ((double)a.u_acc[lo + j] * q < P) ? j : -1;
                 }
@@ -695,8 +726,8 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 if (next >= 0) break;
                 // rejected: the residual mass after t + 1 rejections
                 if (k > n + 1 ||
-                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_RESID, true, t + 1, mct, alt, mcd,
-                                          ald, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_RESID, true, t + 1, rn, sW,
+                                          ring + (size_t)k * a.slot, claim, done, tl, par)) {
                     flags |= SPECDEC_ERR_TEAM;
                     break;
                 }
@@ -708,8 +739,8 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                     flags |= SPECDEC_ERR_ZFALLBACK;
                     kind = TW_TESTED;
                     if (k > n + 1 ||
-                        !team_pass<BF16, VEC>(a, trow, drow, k, TW_TESTED, true, t, mct, alt, mcd,
-                                              ald, sW, ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                        !team_pass<BF16, VEC>(a, trow, drow, k, TW_TESTED, true, t, rn, sW,
+                                              ring + (size_t)k * a.slot, claim, done, tl, par)) {
                         flags |= SPECDEC_ERR_TEAM;
                         break;
                     }
@@ -735,7 +766,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
             const double* sl = ring + (size_t)wslot * a.slot;
             for (int q = tid; q < a.nsub; q += kTreeNT) sub[q] = team_weight_sub(sl, q, a.team == 1);
             __syncthreads();
-            x = tree_draw<BF16, VEC>(a, trow, drow, kind, t, mct, alt, mcd, ald, sW, sub,
+            x = tree_draw<BF16, VEC>(a, trow, drow, kind, t, rn, sW, sub,
                                      a.u_smp[b], red, redi);
         }
         __syncthreads();

@@ -2712,8 +2712,9 @@ static inline bool select_generic(int top_k, float top_p, int V, int nchunks) {
     return topk_generic(k) || k >= V;
 }
 
-static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float top_p,
-                             const specdec_params* prm) {
+// The transform's mode and the chunk select's k (no offsets yet).
+static inline WsPlan plan_transform(int V, int dtype, int top_k, float top_p,
+                                    const specdec_params* prm) {
     WsPlan p{};
     // the vector and scalar layouts use the same chunk length
     const int ch = dtype == SPECDEC_BF16 ? Layout<true, true>::CH : Layout<false, true>::CH;
@@ -2746,19 +2747,14 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
         p.sel_generic = select_generic(top_k, top_p, V, p.nchunks);
     }
     p.nparts = p.filter ? 1 : p.nchunks;
-    const size_t rows = (size_t)2 * K + B;
-    size_t off = 0;
-    p.part = off;
-    off = align256(off + rows * p.nparts * sizeof(RowPartial));
-    p.thr = off;
-    off = align256(off + rows * sizeof(float));
     p.nch = (V + kSChunk - 1) / kSChunk;
-    p.rec = off;
-    off = align256(off + (size_t)B * sizeof(Decision));
-    p.wsum = off;
-    off = align256(off + (size_t)B * p.nch * kSSub * sizeof(double));
-    p.live = off;                          // early-exit liveness flags
-    off = align256(off + (size_t)2 * B * sizeof(int));
+    return p;
+}
+
+// The chunk select's lists from `off` for `rows` rows, the first rows_t of them target rows
+// (listed: their kept tokens too, bf16 only); returns the end.
+static inline size_t plan_select(WsPlan& p, size_t off, size_t rows, size_t rows_t, int dtype,
+                                 bool listed) {
     p.tk_cnt = p.tk_cand = p.tk_cpart = p.tk_ctc = off;
     if (p.filter && !p.sel_generic) {
         p.tk_wcap = topk_wcap(p.sel_k);
@@ -2772,8 +2768,7 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
             p.tk_ctc = off;
             off = align256(off + lists * sizeof(uint32_t));
         }
-        if (dtype == SPECDEC_BF16) {       // kept-token lists of the target rows
-            const size_t rows_t = (size_t)K + B;
+        if (listed && dtype == SPECDEC_BF16) {   // kept-token lists of the target rows
             p.tk_listed = 1;
             p.tk_kn = off;
             off = align256(off + rows_t * sizeof(int));
@@ -2783,6 +2778,25 @@ static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float to
             off = align256(off + rows_t * kKeptCap * sizeof(uint16_t));
         }
     }
+    return off;
+}
+
+static inline WsPlan plan_ws(int B, int K, int V, int dtype, int top_k, float top_p,
+                             const specdec_params* prm) {
+    WsPlan p = plan_transform(V, dtype, top_k, top_p, prm);
+    const size_t rows = (size_t)2 * K + B;
+    size_t off = 0;
+    p.part = off;
+    off = align256(off + rows * p.nparts * sizeof(RowPartial));
+    p.thr = off;
+    off = align256(off + rows * sizeof(float));
+    p.rec = off;
+    off = align256(off + (size_t)B * sizeof(Decision));
+    p.wsum = off;
+    off = align256(off + (size_t)B * p.nch * kSSub * sizeof(double));
+    p.live = off;                          // early-exit liveness flags
+    off = align256(off + (size_t)2 * B * sizeof(int));
+    off = plan_select(p, off, rows, (size_t)K + B, dtype, true);
     p.rpar = off;
     if (p.pr) off = align256(off + rows * sizeof(RowParams));
     // acceptance analytics: a record and the sub-chunk residual sums of every position

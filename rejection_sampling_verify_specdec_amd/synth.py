@@ -351,12 +351,13 @@ class TreeInputs:
 
 def make_tree(seed: int = 0, B: int = 16, V: int = 32000, dtype: str = "bf16", T: float = 0.7,
               n_range=(1, 16), target_std: float = 3.0, noise_std: float = 1.5,
-              branch: float = 0.5, max_nodes: int = 64) -> TreeInputs:
+              branch: float = 0.5, max_nodes: int = 64, top_k: int = 0) -> TreeInputs:
     """Seeded trees: node j's parent is j - 1 (the chain goes on) or, with probability
     ``branch``, a uniform pick among the root and the earlier nodes. Target rows N(0,
     target_std) per position, draft rows the target row plus N(0, noise_std); each node's
     token is a Gumbel-max draw from the draft row of its parent's position (siblings are
-    independent draws), standing in for the draft model."""
+    independent draws; within the row's top_k when given), standing in for the draft
+    model."""
     rng = np.random.default_rng(seed)
     n_b = rng.integers(n_range[0], n_range[1] + 1, size=B)
     cu = np.zeros(B + 1, dtype=np.int32)
@@ -381,7 +382,7 @@ def make_tree(seed: int = 0, B: int = 16, V: int = 32000, dtype: str = "bf16", T
     # the draft row each node was drawn from: its parent's position
     req = np.repeat(np.arange(B), n_b)
     rows = cu[req] + req + parent + 1
-    tokens = _gumbel_sample(dvals[rows], float(np.float32(T)), 0, rng) if N else \
+    tokens = _gumbel_sample(dvals[rows], float(np.float32(T)), top_k, rng) if N else \
         np.zeros(0, dtype=np.int32)
     u_accept = rng.random(N, dtype=np.float32)
     u_sample = rng.random(B, dtype=np.float32)

@@ -139,21 +139,37 @@ def test_tree_workspace_and_host_validation_without_gpu(lib):
     assert n >= (2071 + 256) * 4 * 63 * 8 + 128 * 64 * 4
     assert binding.specdec_tree_verify_workspace_size(0, 0, 100) == 0
     assert binding.specdec_tree_verify_workspace_size(1, 0, binding.MAX_V + 1) == 0
+    assert binding.specdec_tree_verify_workspace_size(1, 0, 100, dtype=7) == 0
+    assert binding.specdec_tree_verify_workspace_size(1, 0, 100, top_p=float("nan")) == 0
+    # top-k / top-p add every row's statistics, threshold and select lists
+    R = 2 * (2071 + 128)
+    for tk, tp in ((64, 1.0), (0, 0.9), (50, 0.9), (2000, 1.0)):
+        m = binding.specdec_tree_verify_workspace_size(128, 2071, 128256, binding.SPECDEC_BF16,
+                                                       tk, tp)
+        assert m >= n + R * (16 + 4)
+    # off: top_k 0 or >= V, top_p >= 1 or <= 0
+    for tk, tp in ((0, 1.0), (128256, 1.0), (0, 0.0), (-3, 1.5)):
+        assert binding.specdec_tree_verify_workspace_size(128, 2071, 128256,
+                                                          binding.SPECDEC_BF16, tk, tp) == n
     vp = None
 
-    def call(team=0, ws=16, nbytes=1 << 30, T=1.0, B=1, N=1, max_nodes=4, V=1000):
+    def call(team=0, ws=16, nbytes=1 << 30, T=1.0, B=1, N=1, max_nodes=4, V=1000, top_k=0,
+             top_p=1.0):
         return lib.specdec_tree_verify(16, 16, binding.SPECDEC_BF16, 16, 16, 16, 16, 16, B, N,
-                                       max_nodes, V, T, 16, 16, 16, 16, 16, vp, team, ws, nbytes,
-                                       vp)
+                                       max_nodes, V, T, top_k, top_p, 16, 16, 16, 16, 16, vp,
+                                       team, ws, nbytes, vp)
     assert call(team=-1) == binding.SPECDEC_EINVAL
     assert call(team=binding.MAX_TREE_TEAM + 1) == binding.SPECDEC_EINVAL
     assert call(T=0.0) == binding.SPECDEC_EINVAL
+    assert call(top_p=float("nan")) == binding.SPECDEC_EINVAL
     assert call(max_nodes=binding.MAX_TREE + 1) == binding.SPECDEC_EINVAL
     assert call(N=5, max_nodes=4) == binding.SPECDEC_EINVAL
     assert call(ws=None) == binding.SPECDEC_EWORKSPACE
     assert call(ws=17) == binding.SPECDEC_EWORKSPACE
     assert call(nbytes=binding.specdec_tree_verify_workspace_size(1, 1, 1000) - 1,
                 team=1) == binding.SPECDEC_EWORKSPACE
+    need = binding.specdec_tree_verify_workspace_size(1, 1, 1000, binding.SPECDEC_BF16, 8, 0.9)
+    assert call(nbytes=need - 1, team=1, top_k=8, top_p=0.9) == binding.SPECDEC_EWORKSPACE
 
 
 def test_early_exit_host_validation_without_gpu(lib):

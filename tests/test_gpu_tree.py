@@ -5,8 +5,9 @@ validity aligned with the committed token history", paragraphs 3 and 6).
 
 Rule: accepted paths, emitted tokens and flags equal the oracle's, except requests whose
 walk met a decision within 1e-6 of its threshold (|u - P/Q| of a tried node, or the draw's
-distance to a CDF edge as a fraction of W), and requests whose walk formed a residual mass
-below 4 * 2^-20: the device's residual chain is built from fp32 exponentials and clamps a
+distance to a CDF edge as a fraction of W), or read a row whose nucleus (top-p) decision
+lies within 2e-6 of top_p, and requests whose walk formed a residual mass below
+4 * 2^-20: the device's residual chain is built from fp32 exponentials and clamps a
 mass at or below 2^-20 to zero (drawing from the distribution the child was tested
 against), so near that clamp its fallback decision is rounding's. Both classes are counted
 and checked for validity only: the path is a root-to-node chain whose tokens were emitted,
@@ -19,7 +20,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_harness import compare_kv_data, compare_kv_meta, dev, log, pool_tensor
+from gpu_harness import (NUCLEUS_MARGIN, _nucleus_floor, compare_kv_data, compare_kv_meta, dev,
+                         log, pool_tensor)
 import oracle
 from rejection_sampling_verify_specdec_amd import binding, synth
 
@@ -39,9 +41,10 @@ def _logits(x, dtype, d):
 
 
 class TreeOnDevice:
-    def __init__(self, tin, team: int = 0, ws_fill: int = 0):
+    def __init__(self, tin, team: int = 0, ws_fill: int = 0, top_k: int = 0, top_p: float = 1.0):
         d = dev()
         self.team = team
+        self.top_k, self.top_p = top_k, top_p
         self.tin = tin
         self.tgt = _logits(tin.target, tin.dtype, d)
         self.dft = _logits(tin.draft, tin.dtype, d)
@@ -56,8 +59,10 @@ class TreeOnDevice:
         self.err = torch.zeros(1, dtype=torch.int32, device=d)
         self.flags = torch.full((B,), -1, dtype=torch.int32, device=d)
         # the call resets what it needs: start from arbitrary contents
-        self.ws = torch.full((binding.specdec_tree_verify_workspace_size(B, N, tin.V),), ws_fill,
-                             dtype=torch.uint8, device=d)
+        dt = binding.SPECDEC_BF16 if tin.dtype == "bf16" else binding.SPECDEC_F32
+        self.ws = torch.full((binding.specdec_tree_verify_workspace_size(B, N, tin.V, dt, top_k,
+                                                                         top_p),),
+                             ws_fill, dtype=torch.uint8, device=d)
 
     def run(self):
         binding.specdec_tree_verify(self.tgt, self.dft, self.tokens, self.parent, self.cu,
@@ -65,7 +70,8 @@ class TreeOnDevice:
                                     temperature=self.tin.T, out_tokens=self.out,
                                     accepted_nodes=self.nodes, num_accepted=self.num_acc,
                                     num_emitted=self.num_emit, err_word=self.err,
-                                    workspace=self.ws, req_flags=self.flags, team=self.team)
+                                    workspace=self.ws, req_flags=self.flags, team=self.team,
+                                    top_k=self.top_k, top_p=self.top_p)
         torch.cuda.synchronize()
         c = lambda x: x.cpu().numpy()
         return dict(a=c(self.num_acc), n=c(self.num_emit), out=c(self.out), nodes=c(self.nodes),
@@ -83,15 +89,20 @@ def _flagged(res):
                                                         r.sample_margin < MARGIN)
 
 
+def _nucleus_close(res):
+    return res is not None and res.nucleus_margin < NUCLEUS_MARGIN
+
+
 def _near_clamp(res):
     """The walk formed a residual mass within a factor of 4 of the device's clamp."""
     return res is not None and res.res is not None and \
         any(0 < float(W) < 4 * TREE_CLAMP for W in res.res.resid_W)
 
 
-def _valid(tin, g, b, ga):
+def _valid(tin, g, b, ga, top_k=0, top_p=1.0):
     """A valid walk result: a root-to-node chain, its tokens emitted in order, one more
-    token drawn with positive target probability at the position the path ends."""
+    token drawn with positive target probability at the position the path ends (inside
+    the row's top-k set, and its nucleus decided either way)."""
     errs = []
     lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
     path = [int(j) for j in g["nodes"][lo: lo + ga]]
@@ -110,19 +121,22 @@ def _valid(tin, g, b, ga):
     pos = 0 if not path else path[-1] + 1
     z = oracle.verify._decode_rows(tin.target[lo + b + pos: lo + b + pos + 1], tin.dtype)[0]
     x = got[ga] if len(got) > ga else -1
-    if not (0 <= x < tin.V and z[x] > -np.inf):
+    floor = _nucleus_floor(z, tin.T, top_k, top_p) if (0 < top_k < tin.V or 0 < top_p < 1) \
+        else -np.inf
+    if not (0 <= x < tin.V and z[x] > -np.inf and z[x] >= floor):
         errs.append(f"req {b}: drawn token {x} has no target probability")
     return errs
 
 
-def compare_tree(tin, g, o):
-    """errors, flagged requests (margin or clamp), flagged mismatches; asserts the bound."""
+def compare_tree(tin, g, o, top_k=0, top_p=1.0):
+    """errors, flagged requests (margin, nucleus or clamp), flagged mismatches; the caller
+    asserts that there are no errors (the bound on mismatches is one of them)."""
     flagged = mism = decisions = 0
     errs = []
     for b in range(tin.B):
         oa, ga = int(o.num_accepted[b]), int(g["a"][b])
         r = o.requests[b]
-        fl = _flagged(r) or _near_clamp(r)
+        fl = _flagged(r) or _near_clamp(r) or _nucleus_close(r)
         if int(o.err[b]) != int(g["flags"][b]) and not fl:
             errs.append(f"req {b}: flags oracle {o.err[b]} gpu {g['flags'][b]}")
         if oa < 0 or ga < 0:
@@ -134,7 +148,7 @@ def compare_tree(tin, g, o):
         got = list(g["out"][lo + b: lo + b + ga + 1])
         path = list(g["nodes"][lo: lo + ga])
         flagged += fl
-        errs += _valid(tin, g, b, ga)
+        errs += _valid(tin, g, b, ga, top_k, top_p)
         if oa != ga or got != r.emitted or path != r.path:
             if fl:
                 mism += 1
@@ -145,12 +159,14 @@ def compare_tree(tin, g, o):
     return errs, flagged, mism
 
 
-def _check(tin):
-    log(f"[tree] B={tin.B} N={tin.N} V={tin.V} {tin.dtype} T={tin.T}")
-    g = TreeOnDevice(tin).run()
+def _check(tin, top_k=0, top_p=1.0, team=0):
+    log(f"[tree] B={tin.B} N={tin.N} V={tin.V} {tin.dtype} T={tin.T} top_k={top_k} "
+        f"top_p={top_p} team={team}")
+    g = TreeOnDevice(tin, top_k=top_k, top_p=top_p, team=team).run()
     o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
-                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype)
-    errs, fl, mism = compare_tree(tin, g, o)
+                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype,
+                                 top_k=top_k, top_p=top_p)
+    errs, fl, mism = compare_tree(tin, g, o, top_k, top_p)
     log(f"[tree]   accepted mean {np.mean(g['a'][g['a'] >= 0]) if (g['a'] >= 0).any() else 0:.2f}, "
         f"flagged {fl}, flagged mismatches {mism}")
     assert not errs, "\n".join(errs[:20])
@@ -217,6 +233,66 @@ def test_tree_deterministic():
     outs = [TreeOnDevice(tin).run() for _ in range(3)]
     for o in outs[1:]:
         assert all(np.array_equal(outs[0][k], o[k]) for k in ("a", "out", "nodes", "flags"))
+
+
+@pytest.mark.parametrize("dtype,V,top_k,top_p", [
+    ("bf16", 128256, 64, 1.0),       # top-k 64, as the linear top-k workload
+    ("bf16", 128256, 0, 0.9),        # top-p alone
+    ("f32", 32000, 50, 0.9),         # top-k, then top-p inside it
+    ("bf16", 20000, 2000, 1.0),      # top-k past the chunk select's limit: the generic select
+    ("bf16", 4001, 16, 0.95),        # rows that are not whole 16-byte vectors
+])
+def test_tree_with_transforms(dtype, V, top_k, top_p):
+    # the transform applies alike to every target and draft row the walk reads; the nodes
+    # are drawn within the draft rows' top-k set
+    _check(synth.make_tree(seed=130, B=10, V=V, dtype=dtype, n_range=(1, 20), noise_std=0.5,
+                           top_k=top_k), top_k, top_p)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (0, 1e-6)])
+def test_tree_point_mass_transform_is_greedy(top_k, top_p):
+    # top-k 1 (or a one-token nucleus) makes p and q point masses: the walk follows the
+    # first child carrying the target row's argmax and emits that argmax where no child
+    # does; distinct fp32 logits, the draft's argmax never the target's
+    tin = synth.make_tree(seed=131, B=16, V=3000, dtype="f32", n_range=(0, 12), branch=0.6)
+    rng = np.random.default_rng(5)
+    R = tin.N + tin.B
+    tin.target[:] = np.stack([rng.permutation(tin.V) for _ in range(R)]).astype(np.float32) * 0.01
+    tin.draft[:] = np.stack([rng.permutation(tin.V) for _ in range(R)]).astype(np.float32) * 0.01
+    at = np.argmax(tin.target, axis=1)
+    clash = np.argmax(tin.draft, axis=1) == at
+    tin.draft[clash] = np.roll(tin.draft[clash], 1, axis=1)
+    for b in range(tin.B):
+        lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
+        for j in range(hi - lo):
+            if rng.random() < 0.5:
+                tin.tokens[lo + j] = at[lo + b + int(tin.parent[lo + j]) + 1]
+    g, o = _check(tin, top_k, top_p)
+    for b in range(tin.B):
+        lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
+        kids = oracle.tree.children_of([int(x) for x in tin.parent[lo:hi]])
+        v, want = 0, []
+        while True:
+            a = int(at[lo + b + v])
+            want.append(a)
+            nxt = next((j for j in kids[v] if int(tin.tokens[lo + j]) == a), None)
+            if nxt is None:
+                break
+            v = nxt + 1
+        got = [int(x) for x in g["out"][lo + b: lo + b + int(g["n"][b])]]
+        assert got == want, (b, got, want)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(64, 1.0), (0, 0.9)])
+def test_team_sizes_with_transforms(top_k, top_p):
+    tin = synth.make_tree(seed=132, B=6, V=128256, dtype="bf16", n_range=(5, 30),
+                          noise_std=0.5, top_k=top_k)
+    ref, _ = _check(tin, top_k, top_p, team=1)
+    for team in (2, 7, 16):
+        log(f"[tree-team]   team {team}, top_k {top_k}, top_p {top_p}")
+        g = TreeOnDevice(tin, team=team, ws_fill=0xCD, top_k=top_k, top_p=top_p).run()
+        for key in ("a", "n", "out", "nodes", "flags"):
+            assert np.array_equal(g[key], ref[key]), (team, key)
 
 
 def _cycle(tin, seed):
