@@ -2,7 +2,8 @@
 // request's tree, sharing every pass over a row (tree_dev.h). With top-k or top-p, the
 // linear path's chunk select and merge first give every target and draft row its
 // threshold and the max and exp-sum of its kept tokens, which the walk reads in place of
-// its own statistics passes. The cache step that keeps the accepted path is kv_tree_commit
+// its own statistics passes; a bf16 target row's kept tokens are also listed (up to
+// kKeptCap), and the walk's passes and draw over such a row read the list alone. The cache step that keeps the accepted path is kv_tree_commit
 // (kv.hip).
 
 #include <hip/hip_runtime.h>
@@ -68,7 +69,7 @@ static bool tree_ws(int32_t B, int32_t N, int32_t V, int32_t dtype, int32_t top_
         off = align256(off + rows * sizeof(RowPartial));
         w->sel.thr = off;
         off = align256(off + rows * sizeof(float));
-        off = plan_select(w->sel, off, rows, (size_t)N + B, dtype, false);
+        off = plan_select(w->sel, off, rows, (size_t)N + B, dtype, true);
     }
     w->total = off;
     return true;
@@ -157,6 +158,10 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     a.thr = w.sel.filter ? reinterpret_cast<const float*>(ws + w.sel.thr) : nullptr;
     a.part = w.sel.filter ? reinterpret_cast<const RowPartial*>(ws + w.sel.part) : nullptr;
     a.rows = N + B;
+    const bool listed = w.sel.filter && w.sel.tk_listed;
+    a.kn = listed ? reinterpret_cast<const int*>(ws + w.sel.tk_kn) : nullptr;
+    a.ktok = listed ? reinterpret_cast<const uint32_t*>(ws + w.sel.tk_ktok) : nullptr;
+    a.kkey = listed ? reinterpret_cast<const uint16_t*>(ws + w.sel.tk_kkey) : nullptr;
     if (const char* lim = getenv("SPECDEC_TREE_SPIN_LIMIT")) {
         char* end = nullptr;
         const long v = strtol(lim, &end, 10);

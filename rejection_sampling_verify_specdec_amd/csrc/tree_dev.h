@@ -64,6 +64,11 @@ struct TreeArgs {
     const float* thr;
     const RowPartial* part;
     int rows;                // N + B
+    // bf16 with top-k / top-p: each target row's kept tokens listed in ascending order
+    // ([N+B] counts, -1 when not listed; [N+B][kKeptCap] tokens and their keys), else null
+    const int* kn;
+    const uint32_t* ktok;
+    const uint16_t* kkey;
 };
 
 // Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
@@ -574,6 +579,38 @@ SD_DEV int tree_draw(const TreeArgs& a, const uint8_t* trow, const uint8_t* drow
     return x;
 }
 
+// A target row whose kept tokens are listed: every weight off the list is 0 (p = 0 there),
+// so a pass is a sum over at most kKeptCap entries, which each member of a team takes by
+// itself (same entries, same order, same result) with no ring and no wait. Thread i takes
+// entry i; *tok is its token (-1 past the list).
+static_assert(kKeptCap <= kTreeNT, "one listed token per thread");
+SD_DEV double listed_weight(const TreeArgs& a, int rt, const uint8_t* drow, int nl, int kind,
+                            int t, const RowNorm& r, const double* W, int* tok) {
+    const int i = threadIdx.x;
+    *tok = -1;
+    if (i >= nl) return 0.0;
+    const int x = (int)a.ktok[(size_t)rt * kKeptCap + i];
+    const float zt = key_to_float<true>(a.kkey[(size_t)rt * kKeptCap + i]);
+    const float zd = kind != TW_P ? load_elem(drow, x, true) : -INFINITY;
+    *tok = x;
+    return tree_weight(zt, zd, kind, t, a.c, r, W);
+}
+
+// Inverse CDF over a listed row (ascending ids): the smallest listed x with C(x) > u * W,
+// or the last with positive weight if rounding leaves none; -1 when nothing has weight.
+SD_DEV int listed_draw(const TreeArgs& a, int rt, const uint8_t* drow, int nl, int kind, int t,
+                       const RowNorm& r, const double* W, float u, double* red, int* redi) {
+    int x;
+    const double w = listed_weight(a, rt, drow, nl, kind, t, r, W, &x);
+    double tot;
+    const double C = block_excl_scan_d<kTreeNT>(w, red, &tot);
+    const double tt = (double)u * tot;
+    const bool pos = x >= 0 && w > 0.0;
+    int i = block_min_i<kTreeNT>(pos && C + w > tt ? (int)threadIdx.x : 0x7fffffff, redi);
+    if (i == 0x7fffffff) i = block_max_i<kTreeNT>(pos ? (int)threadIdx.x : -1, redi);
+    return i < 0 ? -1 : (int)a.ktok[(size_t)rt * kKeptCap + i];
+}
+
 // The walk of request b by member `mem` of its team; member 0 draws and writes the outputs.
 template <bool BF16, bool VEC>
 SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
@@ -634,6 +671,8 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
         int par = 0;                                 // tl.tk[par]: the current ticket
         int k = 0;      // passes so far: at most n + 2 (ring slots), checked before each
         int wslot = -1, kind = TW_RESID, t = 0;      // the final draw's slot, kind, residual
+        bool ldraw = false;                          // the final draw is over a listed row
+        int nl = -1, rt = 0;                         // the position's listed tokens, its row
         RowNorm rn{0.f, 0.f, -INFINITY, -INFINITY, 0.0, 0.0};
         const RowNorm none{0.f, 0.f, -INFINITY, -INFINITY, 0.0, 0.0};
         const uint8_t* trow = nullptr;
@@ -658,9 +697,9 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
             unsigned long long kids = s_kids;
             float mt, md = 0.f;
             double St, Sd = 1.0;
+            rt = lo + b + v;
             if (a.part) {
                 // top-k / top-p: the select launches' statistics of the kept tokens
-                const int rt = lo + b + v;
                 const RowPartial pt = a.part[rt];
                 mt = pt.m;
                 St = pt.s;
@@ -691,10 +730,17 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 flags |= SPECDEC_ERR_NONFINITE;
                 break;
             }
+            nl = a.kn ? a.kn[rt] : -1;
             rn.mct = mt * a.c;
             rn.mcd = md * a.c;
             rn.alt = exp2(-(double)fmaf(mt, a.c, -rn.mct)) / St;
             rn.ald = kids ? exp2(-(double)fmaf(md, a.c, -rn.mcd)) / Sd : 0.0;
+            if (!kids && nl >= 0) {                  // bonus from a listed p
+                ldraw = true;
+                kind = TW_P;
+                t = 0;
+                break;
+            }
             if (!kids) {                             // bonus from p at a leaf
                 if (k > n + 1 ||
                     !team_pass<BF16, VEC>(a, trow, drow, k, TW_P, false, 0, rn, sW,
@@ -703,6 +749,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                     break;
                 }
                 wslot = k++;
+                ldraw = false;
                 kind = TW_P;
                 t = 0;
                 break;
@@ -725,19 +772,29 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
                 __syncthreads();
                 if (next >= 0) break;
                 // rejected: the residual mass after t + 1 rejections
-                if (k > n + 1 ||
-                    !team_pass<BF16, VEC>(a, trow, drow, k, TW_RESID, true, t + 1, rn, sW,
-                                          ring + (size_t)k * a.slot, claim, done, tl, par)) {
-                    flags |= SPECDEC_ERR_TEAM;
-                    break;
+                double Wn;
+                if (nl >= 0) {
+                    int x_;
+                    Wn = block_sum<kTreeNT>(
+                        listed_weight(a, rt, drow, nl, TW_RESID, t + 1, rn, sW, &x_), red);
+                    ldraw = true;
+                } else {
+                    if (k > n + 1 ||
+                        !team_pass<BF16, VEC>(a, trow, drow, k, TW_RESID, true, t + 1, rn, sW,
+                                              ring + (size_t)k * a.slot, claim, done, tl, par)) {
+                        flags |= SPECDEC_ERR_TEAM;
+                        break;
+                    }
+                    Wn = team_weight_total(a, ring + (size_t)k * a.slot, red);
+                    wslot = k++;
+                    ldraw = false;
                 }
-                const double Wn = team_weight_total(a, ring + (size_t)k * a.slot, red);
-                wslot = k++;
                 if (!(Wn > kResidFloor)) {
                     // no residual mass (not possible in exact arithmetic): draw from the
                     // distribution the child was tested against
                     flags |= SPECDEC_ERR_ZFALLBACK;
                     kind = TW_TESTED;
+                    if (ldraw) break;
                     if (k > n + 1 ||
                         !team_pass<BF16, VEC>(a, trow, drow, k, TW_TESTED, true, t, rn, sW,
                                               ring + (size_t)k * a.slot, claim, done, tl, par)) {
@@ -762,7 +819,10 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
         }
         // the replacement (from the last residual, or the tested distribution after a zero
         // residual) or the bonus: member 0 rescans one sub-chunk
-        if (mem == 0 && wslot >= 0 && !(flags & (SPECDEC_ERR_NONFINITE | SPECDEC_ERR_TEAM))) {
+        if (mem == 0 && ldraw && !(flags & (SPECDEC_ERR_NONFINITE | SPECDEC_ERR_TEAM))) {
+            x = listed_draw(a, rt, drow, nl, kind, t, rn, sW, a.u_smp[b], red, redi);
+        } else if (mem == 0 && wslot >= 0 &&
+                   !(flags & (SPECDEC_ERR_NONFINITE | SPECDEC_ERR_TEAM))) {
             const double* sl = ring + (size_t)wslot * a.slot;
             for (int q = tid; q < a.nsub; q += kTreeNT) sub[q] = team_weight_sub(sl, q, a.team == 1);
             __syncthreads();

@@ -235,33 +235,44 @@ def test_tree_deterministic():
         assert all(np.array_equal(outs[0][k], o[k]) for k in ("a", "out", "nodes", "flags"))
 
 
-@pytest.mark.parametrize("dtype,V,top_k,top_p", [
-    ("bf16", 128256, 64, 1.0),       # top-k 64, as the linear top-k workload
-    ("bf16", 128256, 0, 0.9),        # top-p alone
-    ("f32", 32000, 50, 0.9),         # top-k, then top-p inside it
-    ("bf16", 20000, 2000, 1.0),      # top-k past the chunk select's limit: the generic select
-    ("bf16", 4001, 16, 0.95),        # rows that are not whole 16-byte vectors
+@pytest.mark.parametrize("dtype,V,top_k,top_p,std", [
+    ("bf16", 128256, 64, 1.0, 3.0),       # top-k 64, as the linear top-k workload (listed)
+    ("bf16", 128256, 0, 0.9, 3.0),        # top-p alone
+    ("bf16", 128256, 0, 0.99, 1.0),       # a nucleus too large to list: full-row passes
+    ("f32", 32000, 50, 0.9, 3.0),         # top-k, then top-p inside it (fp32: never listed)
+    ("bf16", 20000, 2000, 1.0, 3.0),      # top-k past the chunk select's limit: generic
+    ("bf16", 4001, 16, 0.95, 3.0),        # rows that are not whole 16-byte vectors
 ])
-def test_tree_with_transforms(dtype, V, top_k, top_p):
+def test_tree_with_transforms(dtype, V, top_k, top_p, std):
     # the transform applies alike to every target and draft row the walk reads; the nodes
-    # are drawn within the draft rows' top-k set
+    # are drawn within the draft rows' top-k set. bf16 target rows whose kept tokens fit the
+    # list are walked over the list alone, the others (and fp32) with masked full-row passes
     _check(synth.make_tree(seed=130, B=10, V=V, dtype=dtype, n_range=(1, 20), noise_std=0.5,
-                           top_k=top_k), top_k, top_p)
+                           target_std=std, top_k=top_k), top_k, top_p)
 
 
+@pytest.mark.parametrize("dtype,V,step", [("f32", 3000, 0.01), ("bf16", 200, 0.25)])
 @pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (0, 1e-6)])
-def test_tree_point_mass_transform_is_greedy(top_k, top_p):
+def test_tree_point_mass_transform_is_greedy(top_k, top_p, dtype, V, step):
     # top-k 1 (or a one-token nucleus) makes p and q point masses: the walk follows the
     # first child carrying the target row's argmax and emits that argmax where no child
-    # does; distinct fp32 logits, the draft's argmax never the target's
-    tin = synth.make_tree(seed=131, B=16, V=3000, dtype="f32", n_range=(0, 12), branch=0.6)
+    # does; distinct logits (exact in bf16 at V = 200), the draft's argmax never the
+    # target's
+    tin = synth.make_tree(seed=131, B=16, V=V, dtype=dtype, n_range=(0, 12), branch=0.6)
     rng = np.random.default_rng(5)
     R = tin.N + tin.B
-    tin.target[:] = np.stack([rng.permutation(tin.V) for _ in range(R)]).astype(np.float32) * 0.01
-    tin.draft[:] = np.stack([rng.permutation(tin.V) for _ in range(R)]).astype(np.float32) * 0.01
-    at = np.argmax(tin.target, axis=1)
-    clash = np.argmax(tin.draft, axis=1) == at
-    tin.draft[clash] = np.roll(tin.draft[clash], 1, axis=1)
+    tz = np.stack([rng.permutation(V) for _ in range(R)]).astype(np.float32) * np.float32(step)
+    dz = np.stack([rng.permutation(V) for _ in range(R)]).astype(np.float32) * np.float32(step)
+    at = np.argmax(tz, axis=1)
+    clash = np.argmax(dz, axis=1) == at
+    dz[clash] = np.roll(dz[clash], 1, axis=1)
+    if dtype == "bf16":
+        tin.target[:] = synth.f32_to_bf16_bits(tz)
+        tin.draft[:] = synth.f32_to_bf16_bits(dz)
+        assert np.array_equal(synth.bf16_bits_to_f32(tin.target), tz)
+    else:
+        tin.target[:] = tz
+        tin.draft[:] = dz
     for b in range(tin.B):
         lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
         for j in range(hi - lo):
