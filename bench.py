@@ -732,6 +732,13 @@ def main():
                      "algorithmic_bytes": read_bytes,
                      "avg_launch_us": stats_avg_s * 1e6},
     }
+    if early:
+        # the events bracket every position launch (with top-k / top-p, their merge
+        # launches too), and those launches also carry shares of the K/V scatter whose
+        # bytes are not counted here: a span, not one launch at its roofline
+        res["roofline"]["span"] = ("every statistics launch of the early-exit schedule, "
+                                   "merges and K/V scatter shares included; "
+                                   "algorithmic_bytes counts the logit rows read only")
     if args.schedule == "serial":
         # each call's time from events around it on the timing steps, and the bytes it must
         # move: the append reads and writes the new K/V, the verify reads every logit row
