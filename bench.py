@@ -417,6 +417,12 @@ def tree_main(args):
                  "walk_gbps": walk / (verify_ms / 1e3) / 1e9,
                  "walk_frac_of_peak": walk / (verify_ms / 1e3) / 1e9 / PEAK_GBPS},
     }
+    if filt:
+        res["tree"]["select_bytes"] = 2 * (N + B) * row
+        res["tree"]["walk_bytes_note"] = (
+            "select_bytes plus a full row pair per rejected child and a row per bonus: an "
+            "upper bound, since a bf16 target row whose kept tokens are listed (up to 512) "
+            "is summed over the list instead of re-read")
     if int(cache.state.item()):
         print(f"# warning: cache state word {int(cache.state.item()):#x}", file=sys.stderr)
     print(json.dumps(res))
