@@ -251,6 +251,37 @@ def test_tree_with_transforms(dtype, V, top_k, top_p, std):
                            target_std=std, top_k=top_k), top_k, top_p)
 
 
+def test_tree_transforms_with_ties_and_bad_rows():
+    # bf16 rows with a block of equal logits at the top-k boundary (ties are kept), and
+    # NaN planted in one request's root target row (the walk reads it: an error) and in
+    # another's unvisited leaf draft row (never read: no error)
+    tin = synth.make_tree(seed=133, B=12, V=30000, dtype="bf16", n_range=(2, 10),
+                          noise_std=0.5, top_k=32)
+    z = synth.bf16_bits_to_f32(tin.target)
+    for r in range(tin.N + tin.B):
+        top = np.argsort(z[r])[::-1]
+        z[r, top[28:40]] = z[r, top[28]]          # 12 equal values across the 32nd place
+    tin.target[:] = synth.f32_to_bf16_bits(z)
+    lo1 = int(tin.cu_nodes[1])
+    tin.target[lo1 + 1, 5] = 0x7fc0               # NaN in request 1's root target row
+    lo2, hi2 = int(tin.cu_nodes[2]), int(tin.cu_nodes[3])
+    leaf = max(j for j in range(hi2 - lo2) if j not in set(tin.parent[lo2:hi2]))
+    tin.draft[lo2 + 2 + 1 + leaf, 7] = 0x7fc0     # NaN in a leaf's draft row (not read)
+    g, o = _check(tin, 32, 1.0)
+    assert g["flags"][1] & binding.ERR_NONFINITE and g["a"][1] == -1
+    assert g["a"][2] >= 0
+
+
+@pytest.mark.parametrize("top_k,top_p", [(30000, 1.0), (0, 0.0), (0, 1.0)])
+def test_tree_transforms_that_are_off(top_k, top_p):
+    # top_k >= V, top_p <= 0 or >= 1: no filter, the same outputs as temperature alone
+    tin = synth.make_tree(seed=134, B=6, V=30000, dtype="bf16", n_range=(2, 12))
+    ref = TreeOnDevice(tin).run()
+    g = TreeOnDevice(tin, top_k=top_k, top_p=top_p).run()
+    for key in ("a", "n", "out", "nodes", "flags"):
+        assert np.array_equal(g[key], ref[key]), key
+
+
 @pytest.mark.parametrize("dtype,V,step", [("f32", 3000, 0.01), ("bf16", 200, 0.25)])
 @pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (0, 1e-6)])
 def test_tree_point_mass_transform_is_greedy(top_k, top_p, dtype, V, step):
