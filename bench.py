@@ -57,7 +57,7 @@ def parse():
                         "the append on a second stream after the logit rows are streamed; "
                         "early-exit: specdec_cycle_early_exit (row statistics position by "
                         "position, no row read past a request's first rejection)")
-    p.add_argument("--timing-every", type=int, default=4,
+    p.add_argument("--timing-every", type=int, default=10,
                    help="attach HIP timing events to the row-statistics launch of every "
                         "n-th step (they add a few microseconds to those steps)")
     p.add_argument("--team", type=int, default=0,
