@@ -107,9 +107,9 @@ def test_random_fused_cycles_equal_three_calls(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_trees_match_the_oracle_for_any_team(seed):
-    # random tree batches (sizes, vocabulary, dtype, temperature, branching, draft noise,
-    # empty trees) with a random team size: checked against the oracle, and bit for bit
-    # against a team of one
+    # random tree batches (sizes, vocabulary, dtype, temperature, top-k, top-p, branching,
+    # draft noise, empty trees) with a random team size: checked against the oracle, and
+    # bit for bit against a team of one
     from test_gpu_tree import TreeOnDevice, compare_tree
     import oracle
     r = np.random.default_rng(2000 + seed)
@@ -119,37 +119,44 @@ def test_random_trees_match_the_oracle_for_any_team(seed):
               n_range=(nlo, nlo + int(r.integers(0, 30))), branch=float(r.choice([0.0, 0.5, 1.0])),
               noise_std=float(r.choice([0.1, 0.5, 2.0])), target_std=float(r.choice([1.0, 3.0])))
     team = int(r.choice([0, 2, 3, 7, 16]))
-    tin = synth.make_tree(seed=3000 + seed, **kw)
-    log(f"[random-tree] seed {seed}: {kw} N={tin.N} team {team}")
-    g = TreeOnDevice(tin, team=team, ws_fill=0x5A).run()
+    top_k = int(r.choice([0, 0, 1, 8, 64, 300, 2000]))
+    top_p = float(r.choice([1.0, 1.0, 0.5, 0.9, 0.99]))
+    tin = synth.make_tree(seed=3000 + seed, top_k=top_k, **kw)
+    log(f"[random-tree] seed {seed}: {kw} N={tin.N} team {team} top_k {top_k} top_p {top_p}")
+    g = TreeOnDevice(tin, team=team, ws_fill=0x5A, top_k=top_k, top_p=top_p).run()
     o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
-                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype)
-    errs, fl, mism = compare_tree(tin, g, o)
+                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype,
+                                 top_k=top_k, top_p=top_p)
+    errs, fl, mism = compare_tree(tin, g, o, top_k, top_p)
     log(f"[random-tree]   flagged {fl}, flagged mismatches {mism}")
     assert not errs, f"seed {seed} {kw} team {team}\n" + "\n".join(errs[:20])
-    solo = TreeOnDevice(tin, team=1).run()
+    solo = TreeOnDevice(tin, team=1, top_k=top_k, top_p=top_p).run()
     for key in ("a", "n", "out", "nodes", "flags"):
         assert np.array_equal(g[key], solo[key]), key
 
 
 @pytest.mark.parametrize("seed", range(12))
 def test_random_early_exit_cycles_equal_the_full_cycle(seed):
-    # the early-exit cycle on random temperature-only batches (dtype, V, B, ragged and empty
-    # k_b, scalar or per-request temperatures with an invalid one now and then, EOS / caps,
-    # draft noise): bit for bit against the full cycle on twin caches
+    # the early-exit cycle on random batches (dtype, V, B, ragged and empty k_b, top-k,
+    # top-p, scalar or per-request parameters with an invalid temperature now and then,
+    # EOS / caps, draft noise): against the oracle, and bit for bit against the full cycle
+    # on twin caches
     from test_gpu_early_exit import _both
     opts, r = _case(200 + seed)
-    opts.update(top_k=0, top_p=1.0)
     vin = _inputs(opts, 200 + seed)
     rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=10, prefix_hi=200, share_group=2,
                          share_blocks=1)
     kv = synth.make_kv("c1", vin, seed=seed, recipe=rec)
-    kw = {}
+    kw = dict(top_p=opts["top_p"])
     if opts["per_request"]:
         temps = r.choice([0.4, 0.8, 1.2], vin.B).astype(np.float32)
         if r.random() < 0.5:
             temps[int(r.integers(0, vin.B))] = 0.0
         kw["temps"] = temps
+        if r.random() < 0.5:
+            kw.update(top_ks=r.choice([0, 4, 50, vin.V], vin.B).astype(np.int32),
+                      top_ps=r.choice([1.0, 0.8, 0.95], vin.B).astype(np.float32),
+                      top_k_max=64)
     if opts["stop"]:
         eos = r.integers(0, vin.V, vin.B).astype(np.int32)
         for b in range(vin.B):
