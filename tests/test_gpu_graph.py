@@ -1,7 +1,9 @@
 """The fused cycle captured once in a HIP graph and replayed: each replay is the next cycle
 (the launches read their sizes and pointers from arguments or device memory), so replays
 equal eager cycles on a twin cache bit for bit, with the program's own eager work and
-synchronizations between the replays. The library records no memset or allocation."""
+synchronizations between the replays. The library records no memset or allocation. The
+tree verification likewise: its counters are cleared by a launch of its own, so every
+replay equals the eager call."""
 
 import numpy as np
 import pytest
@@ -23,7 +25,8 @@ def _cycle(g_kv, g_v, vin, ws, early=False):
 
 @pytest.mark.parametrize("wl,top_p,early", [("c4", 1.0, False), ("c2", 0.9, False),
                                             ("c1", 1.0, False), ("c2", 1.0, True),
-                                            ("c1", 1.0, True)])
+                                            ("c1", 1.0, True), ("c4", 1.0, True),
+                                            ("c2", 0.9, True)])
 def test_graph_replays_equal_eager_cycles(wl, top_p, early):
     # early: the early-exit cycle (its liveness flags live in the workspace and are
     # rewritten by every replay's first launch)
@@ -63,3 +66,44 @@ def test_graph_replays_equal_eager_cycles(wl, top_p, early):
         log(f"[graph]   cycle {it}: accepted {int(a.num_accepted.sum())}, "
             f"seq_lens sum {int(ma['seq_lens'].sum())}")
     assert int(ma["seq_lens"].sum()) > int(kv.seq_lens.sum())   # the cache did grow
+
+
+@pytest.mark.parametrize("top_k,top_p,team", [(0, 1.0, 0), (64, 1.0, 0), (0, 0.9, 3)])
+def test_graph_replays_of_tree_verification(top_k, top_p, team):
+    from test_gpu_tree import TreeOnDevice
+    tin = synth.make_tree(seed=141, B=6, V=40000, dtype="bf16", n_range=(3, 20),
+                          noise_std=0.5, top_k=top_k)
+    ref = TreeOnDevice(tin, team=team, top_k=top_k, top_p=top_p).run()
+    t = TreeOnDevice(tin, team=team, ws_fill=0x33, top_k=top_k, top_p=top_p)
+    log(f"[graph] tree top_k={top_k} top_p={top_p} team={team}: capture")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        binding.specdec_tree_verify(t.tgt, t.dft, t.tokens, t.parent, t.cu, t.u_acc, t.u_smp,
+                                    max_nodes=tin.max_nodes, temperature=tin.T,
+                                    out_tokens=t.out, accepted_nodes=t.nodes,
+                                    num_accepted=t.num_acc, num_emitted=t.num_emit,
+                                    err_word=t.err, workspace=t.ws, req_flags=t.flags,
+                                    team=team, top_k=top_k, top_p=top_p)
+    torch.cuda.synchronize()
+    x = torch.randn(256, 256, device=t.tgt.device)
+    for it in range(3):
+        # the fills the reference call started from (entries past a path stay as they were)
+        t.out.fill_(-7)
+        t.nodes.fill_(-7)
+        t.num_acc.fill_(-9)
+        t.num_emit.fill_(-9)
+        t.flags.fill_(-1)
+        t.err.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        x = (x @ x.T).tanh()              # the program's own work between replays
+        torch.cuda.synchronize()
+        c = lambda v: v.cpu().numpy()
+        got = dict(a=c(t.num_acc), n=c(t.num_emit), out=c(t.out), nodes=c(t.nodes),
+                   flags=c(t.flags))
+        for key in ("a", "n", "out", "nodes", "flags"):
+            assert np.array_equal(got[key], ref[key]), (it, key)
+        assert int(t.err.item()) == ref["err"], it
