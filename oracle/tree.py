@@ -33,12 +33,13 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 from .kv import KV_APPEND_REJECTED, KV_ERR_ROLLBACK, PagedKV
-from .verify import (ERR_K, ERR_NONFINITE, ERR_QZERO, ERR_TOKEN, ERR_UNIFORM, ERR_ZFALLBACK,
-                     _decode_rows, _icdf, _u_ok, accept, residual_weights, transform)
+from .verify import (ERR_K, ERR_NONFINITE, ERR_PARAM, ERR_QZERO, ERR_TOKEN, ERR_UNIFORM,
+                     ERR_ZFALLBACK, _decode_rows, _icdf, _u_ok, accept, params_ok,
+                     residual_weights, transform)
 
 ERR_TREE = 128          # a parent index outside {-1, .., j-1}
 
-ERROR_BITS_TREE = ERR_TOKEN | ERR_K | ERR_NONFINITE | ERR_UNIFORM | ERR_TREE
+ERROR_BITS_TREE = ERR_TOKEN | ERR_K | ERR_NONFINITE | ERR_UNIFORM | ERR_TREE | ERR_PARAM
 
 
 def children_of(parent: Sequence[int]) -> List[List[int]]:
@@ -124,14 +125,19 @@ class TreeRequestResult:
 
 
 def tree_verify_request(t_rows, d_rows, parent, tokens, u_accept, u_sample, T: float,
-                        V: int, top_k: int = 0, top_p: float = 1.0) -> TreeRequestResult:
+                        V: int, top_k: int = 0, top_p: float = 1.0,
+                        top_k_max=None) -> TreeRequestResult:
     """One request from logits (fp64 rows by position); the decoding transform (temperature,
     then top-k, then top-p) applied alike to every target and draft row ("Speculative
     decoding: accelerate LLM generation without changing its answers", section 3's closing
     paragraph and section 4: p and q must come from the same transform), stable softmax,
-    rows transformed only where the walk reads them."""
+    rows transformed only where the walk reads them. Invalid parameters (as for the linear
+    rule: T not positive and finite, top_p NaN, an active top_k above top_k_max) fail the
+    request with ERR_PARAM."""
     n = len(tokens)
     err = 0
+    if not params_ok(T, top_k, top_p, V, top_k_max):
+        err |= ERR_PARAM
     if any(not (-1 <= int(pa) < j) for j, pa in enumerate(parent)):
         err |= ERR_TREE
     if any(not 0 <= int(y) < V for y in tokens):
@@ -181,17 +187,22 @@ class TreeBatchResult:
 
 
 def tree_verify_batch(target, draft, tree_tokens, tree_parent, cu_nodes, u_accept, u_sample,
-                      T: float, max_nodes: int, dtype: str,
-                      requests: Optional[Sequence[int]] = None, top_k: int = 0,
-                      top_p: float = 1.0) -> TreeBatchResult:
+                      T, max_nodes: int, dtype: str,
+                      requests: Optional[Sequence[int]] = None, top_k=0,
+                      top_p=1.0, top_k_max=None) -> TreeBatchResult:
     """Packed trees: request b owns nodes cu[b] .. cu[b+1] - 1 and the target / draft rows
     cu[b] + b + v for its positions v = 0 .. n_b (draft rows of leaves are not read).
-    top_k (0 or >= V: off) and top_p (>= 1 or <= 0: off) apply to every row read."""
+    T, top_k (0 or >= V: off) and top_p (>= 1 or <= 0: off) apply to every row a request
+    reads: one value for every request, or one per request (T and top_p rounded to fp32);
+    top_k_max bounds the active per-request top_k values, if given."""
     cu = np.asarray(cu_nodes, dtype=np.int64)
     B = cu.shape[0] - 1
     N = int(np.asarray(tree_tokens).shape[0])
     V = int(target.shape[1])
-    T = float(np.float32(T))
+    per = lambda x, f: [f(v) for v in np.broadcast_to(np.asarray(x), (B,))]
+    Ts = per(T, lambda v: float(np.float32(v)))
+    ks = per(top_k, int)
+    ps = per(top_p, lambda v: float(np.float32(v)))
     num_acc = np.full(B, -1, dtype=np.int32)
     num_emit = np.zeros(B, dtype=np.int32)
     out = np.full(N + B, -1, dtype=np.int32)
@@ -209,8 +220,8 @@ def tree_verify_batch(target, draft, tree_tokens, tree_parent, cu_nodes, u_accep
         d_rows = _decode_rows(draft[lo + b: hi + b + 1], dtype)
         r = tree_verify_request(t_rows, d_rows, [int(x) for x in tree_parent[lo:hi]],
                                 [int(x) for x in tree_tokens[lo:hi]],
-                                [float(u) for u in u_accept[lo:hi]], float(u_sample[b]), T, V,
-                                int(top_k), float(np.float32(top_p)))
+                                [float(u) for u in u_accept[lo:hi]], float(u_sample[b]), Ts[b],
+                                V, ks[b], ps[b], top_k_max)
         results[b] = r
         errs[b] = r.err
         if r.a >= 0:

@@ -427,3 +427,30 @@ def test_point_mass_transforms_make_the_walk_greedy(top_k, top_p):
             v = nxt + 1
         r = res.requests[b]
         assert r.path == path and r.emitted == emitted, (b, r.path, path, r.emitted, emitted)
+
+
+def test_per_request_transforms_are_each_requests_own():
+    # per-request T / top_k / top_p: every request gives what a call with its values as
+    # scalars gives; invalid values (T <= 0, NaN top_p, an active top_k above the bound)
+    # fail that request alone with ERR_PARAM
+    B, V = 10, 50
+    rng, cu, N, parent, tgt, dft = _logit_tree(91, B, V, 0, 8, 0.5)
+    tokens = rng.integers(0, V, N)
+    u_acc = rng.random(N).astype(np.float32)
+    u_smp = rng.random(B).astype(np.float32)
+    Ts = np.array([0.5, 1.0, 1.7, 0.0, 1.0, 0.8, 1.2, 0.9, 1.0, 0.6], np.float32)
+    ks = np.array([0, 5, 12, 3, 40, 1, 0, 60, 49, 50], np.int32)
+    ps = np.array([1.0, 0.9, 0.5, 1.0, np.nan, 1.0, 0.3, 0.95, 1.0, 0.99], np.float32)
+    res = tree_verify_batch(tgt, dft, tokens, parent, cu, u_acc, u_smp, Ts, 64, "f32",
+                            top_k=ks, top_p=ps, top_k_max=45)
+    for b in range(B):
+        one = tree_verify_batch(tgt, dft, tokens, parent, cu, u_acc, u_smp, float(Ts[b]), 64,
+                                "f32", requests=[b], top_k=int(ks[b]), top_p=float(ps[b]),
+                                top_k_max=45)
+        bad = not (Ts[b] > 0) or np.isnan(ps[b]) or 45 < ks[b] < V
+        assert bool(res.err[b] & oracle.ERR_PARAM) == bad, b
+        assert res.err[b] == one.err[b] and res.num_accepted[b] == one.num_accepted[b], b
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        assert np.array_equal(res.out_tokens[lo + b: hi + b + 1], one.out_tokens[lo + b: hi + b + 1])
+        if bad:
+            assert res.num_accepted[b] == -1
