@@ -500,7 +500,10 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * in specdec_verify: temperature, then top_k (0 or >= V: off; ties at the k-th value
  * kept), then top_p (<= 0 or >= 1: off; the nucleus of the top-k set, ties kept); with
  * either filter on, the call first selects over every row (draft rows of leaves
- * included) and the walk reads the kept tokens' statistics from there.
+ * included) and the walk reads the kept tokens' statistics from there. per_request (or
+ * NULL) replaces any of the three scalars by [B] arrays as in specdec_verify (a request
+ * whose values are invalid fails with SPECDEC_ERR_PARAM alone); its stopping arrays
+ * (eos_token, max_emit) are not taken on trees (EINVAL).
  * Outputs (device): num_accepted [B] = the accepted path's length (-1 on error),
  * num_emitted [B] = that + 1; out_tokens [N+B]: request b writes the path's tokens then
  * the drawn token at cu_nodes[b] + b; accepted_nodes [N]: the path's local node indices,
@@ -510,25 +513,30 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * them); 0 picks min(16, max(1, CUs / B)), otherwise 1..16. The outputs do not depend on
  * it: partial sums are combined in a fixed order.
  * workspace: device, 16-byte aligned, >= specdec_tree_verify_workspace_size(B, N, V,
- * dtype, top_k, top_p) bytes, owned by the caller, contents need not be initialized (the
- * call resets its counters first); not used by other calls while this one runs.
+ * dtype, top_k, top_p, per_request) bytes, owned by the caller, contents need not be
+ * initialized (the call resets its counters first); not used by other calls while this
+ * one runs.
  * Host: B >= 1, N = cu_nodes[B], 0 <= max_nodes <= SPECDEC_MAX_TREE, 1 <= V <=
- * SPECDEC_MAX_V, temperature > 0 and finite, top_p not NaN, 0 <= team <= 16; EINVAL
+ * SPECDEC_MAX_V, temperature > 0 and finite and top_p not NaN (unless replaced per
+ * request), per_request->top_k_max >= 0 with a top_k array, 0 <= team <= 16; EINVAL
  * otherwise, EWORKSPACE for a missing / small / misaligned workspace, before anything is
  * enqueued. Two launches on `stream` (counter reset, walk), two more before the walk with
- * top-k / top-p (the chunk select, the per-row merge; one with top_k above 1024). Testing only: the environment variable
+ * top-k / top-p (the chunk select, the per-row merge; one with top_k above 1024), one
+ * more with per-request arrays (each row's parameters). Testing only: the environment variable
  * SPECDEC_TREE_SPIN_LIMIT (a decimal integer in [0, 2^20], read at each call; anything
  * else is ignored) lowers the bound on the polls a member makes while it waits for the
  * rest of its team (default 2^20); a member that reaches the bound gives up, and its
  * request fails with SPECDEC_ERR_TEAM (the other requests are unaffected).
  */
 size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V, int32_t dtype,
-                                          int32_t top_k, float top_p);
+                                          int32_t top_k, float top_p,
+                                          const specdec_params* per_request);
 int specdec_tree_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
                         const int32_t* tree_tokens, const int32_t* tree_parent,
                         const int32_t* cu_nodes, const float* u_accept, const float* u_sample,
                         int32_t B, int32_t N, int32_t max_nodes, int32_t V, float temperature,
-                        int32_t top_k, float top_p, int32_t* out_tokens, int32_t* accepted_nodes, int32_t* num_accepted,
+                        int32_t top_k, float top_p, const specdec_params* per_request,
+                        int32_t* out_tokens, int32_t* accepted_nodes, int32_t* num_accepted,
                         int32_t* num_emitted, int32_t* err_word, int32_t* req_flags,
                         int32_t team, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);

@@ -180,10 +180,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                          vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, f32, pp,
                                          vp, vp, vp, vp, ctypes.POINTER(SpecdecDebug), vp]
     lib.specdec_cycle_static.restype = ctypes.c_int
-    lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32]
+    lib.specdec_tree_verify_workspace_size.argtypes = [i32, i32, i32, i32, i32, f32, pp]
     lib.specdec_tree_verify_workspace_size.restype = sz
     lib.specdec_tree_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32,
-                                        i32, f32, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
+                                        i32, f32, pp, vp, vp, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.specdec_tree_verify.restype = ctypes.c_int
     lib.kv_tree_commit.argtypes = [ctypes.POINTER(KvPagedCacheStruct), i32, vp, vp, vp, i32, vp]
     lib.kv_tree_commit.restype = ctypes.c_int
@@ -549,9 +549,10 @@ class HipEvent:
 
 
 def specdec_tree_verify_workspace_size(B: int, N: int, V: int, dtype: int = SPECDEC_BF16,
-                                       top_k: int = 0, top_p: float = 1.0) -> int:
+                                       top_k: int = 0, top_p: float = 1.0,
+                                       params: Optional[SpecdecParams] = None) -> int:
     return int(load_library().specdec_tree_verify_workspace_size(B, N, V, dtype, top_k,
-                                                                 float(top_p)))
+                                                                 float(top_p), _pref(params)))
 
 
 def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
@@ -561,9 +562,14 @@ def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                         accepted_nodes: torch.Tensor, num_accepted: torch.Tensor,
                         num_emitted: torch.Tensor, err_word: torch.Tensor,
                         workspace: torch.Tensor, req_flags: Optional[torch.Tensor] = None,
-                        team: int = 0, top_k: int = 0, top_p: float = 1.0) -> None:
+                        team: int = 0, top_k: int = 0, top_p: float = 1.0,
+                        temperatures: Optional[torch.Tensor] = None,
+                        top_ks: Optional[torch.Tensor] = None,
+                        top_ps: Optional[torch.Tensor] = None,
+                        top_k_max: Optional[int] = None) -> None:
     """Enqueue the verification of one draft tree per request (shapes as in the header);
-    ``team`` workgroups share each request's walk (0: automatic)."""
+    ``team`` workgroups share each request's walk (0: automatic); temperatures / top_ks /
+    top_ps: optional per-request [B] device tensors replacing the scalars."""
     lib = load_library()
     dev = target_logits.device
     dtype = _logits_dtype(target_logits)
@@ -587,10 +593,12 @@ def specdec_tree_verify(target_logits: torch.Tensor, draft_logits: torch.Tensor,
     if req_flags is not None:
         _check(req_flags, "req_flags", torch.int32, B, dev)
     _check(workspace, "workspace", torch.uint8, device=dev)
+    prm = _params(B, dev, temperatures, top_ks, top_ps, top_k_max)
     st = lib.specdec_tree_verify(
         _ptr(target_logits), _ptr(draft_logits), dtype, _ptr(tree_tokens), _ptr(tree_parent),
         _ptr(cu_nodes), _ptr(u_accept), _ptr(u_sample), B, N, max_nodes, V, float(temperature),
-        int(top_k), float(top_p), _ptr(out_tokens), _ptr(accepted_nodes) if N else None,
+        int(top_k), float(top_p), _pref(prm), _ptr(out_tokens),
+        _ptr(accepted_nodes) if N else None,
         _ptr(num_accepted),
         _ptr(num_emitted),
         _ptr(err_word), _ptr(req_flags) if req_flags is not None else None, int(team),

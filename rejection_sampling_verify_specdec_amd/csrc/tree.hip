@@ -45,6 +45,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_
     topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
 }
 
+// per-request transforms: each row's parameters, then its chunks and merge (the linear
+// path's per-request bodies over the tree's rows)
+__global__ __launch_bounds__(256) void k_tree_params(ParamArgs a, int rows) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < rows) row_params_one(a, r);
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kTkNT) void k_tree_select_pr(TopkArgs a) {
+    chunk_pr_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+}
+
+template <bool BF16, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge_pr(TopkArgs a) {
+    merge_pr_body<BF16, NT>(a, blockIdx.x);
+}
+
 struct TreeWs {
     size_t ctr_bytes, ring_bytes, total;
     int nchunk, nsub, slot;
@@ -52,19 +69,25 @@ struct TreeWs {
 };
 
 static bool tree_ws(int32_t B, int32_t N, int32_t V, int32_t dtype, int32_t top_k, float top_p,
-                    TreeWs* w) {
+                    const specdec_params* prm, TreeWs* w) {
     if (B < 1 || N < 0 || V < 1 || V > SPECDEC_MAX_V) return false;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return false;
-    if (top_p != top_p) return false;
+    if (top_p != top_p && !(prm && prm->top_p)) return false;
+    if (prm && (prm->eos_token || prm->max_emit)) return false;   // no stopping on trees
+    if (prm && prm->top_k && prm->top_k_max < 0) return false;
     w->nchunk = (V + kTreeChunk - 1) / kTreeChunk;
     w->nsub = (V + kTreeSub - 1) / kTreeSub;
     w->slot = 64 * w->nchunk;           // >= 4 * nsub (weights); 4 per wave-chunk (stats)
     w->ctr_bytes = ((size_t)B * kTreeCtrStride * sizeof(int) + 255) & ~(size_t)255;
     w->ring_bytes = ((size_t)N + 2 * (size_t)B) * w->slot * sizeof(double);
     size_t off = align256(w->ctr_bytes + w->ring_bytes);
-    w->sel = plan_transform(V, dtype, top_k, top_p, nullptr);
+    w->sel = plan_transform(V, dtype, top_k, top_p, prm);
+    const size_t rows = 2 * ((size_t)N + B);
+    if (w->sel.pr) {
+        w->sel.rpar = off;
+        off = align256(off + rows * sizeof(RowParams));
+    }
     if (w->sel.filter) {
-        const size_t rows = 2 * ((size_t)N + B);
         w->sel.part = off;
         off = align256(off + rows * sizeof(RowPartial));
         w->sel.thr = off;
@@ -78,9 +101,10 @@ static bool tree_ws(int32_t B, int32_t N, int32_t V, int32_t dtype, int32_t top_
 }  // namespace sd
 
 extern "C" size_t specdec_tree_verify_workspace_size(int32_t B, int32_t N, int32_t V,
-                                                     int32_t dtype, int32_t top_k, float top_p) {
+                                                     int32_t dtype, int32_t top_k, float top_p,
+                                                     const specdec_params* per_request) {
     sd::TreeWs w;
-    return sd::tree_ws(B, N, V, dtype, top_k, top_p, &w) ? w.total : 0;
+    return sd::tree_ws(B, N, V, dtype, top_k, top_p, per_request, &w) ? w.total : 0;
 }
 
 extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_logits,
@@ -88,7 +112,8 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
                                    const int32_t* tree_parent, const int32_t* cu_nodes,
                                    const float* u_accept, const float* u_sample, int32_t B,
                                    int32_t N, int32_t max_nodes, int32_t V, float temperature,
-                                   int32_t top_k, float top_p, int32_t* out_tokens, int32_t* accepted_nodes,
+                                   int32_t top_k, float top_p, const specdec_params* per_request,
+                                   int32_t* out_tokens, int32_t* accepted_nodes,
                                    int32_t* num_accepted, int32_t* num_emitted,
                                    int32_t* err_word, int32_t* req_flags, int32_t team,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -98,18 +123,20 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
         return SPECDEC_EINVAL;
     if ((long long)N > (long long)B * max_nodes) return SPECDEC_EINVAL;
     if (dtype != SPECDEC_F32 && dtype != SPECDEC_BF16) return SPECDEC_EINVAL;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SPECDEC_EINVAL;
-    if (top_p != top_p) return SPECDEC_EINVAL;
+    const bool pr_t = per_request && per_request->temperature;
+    if (!pr_t && (!(temperature > 0.0f) || !isfinite(temperature))) return SPECDEC_EINVAL;
+    if (top_p != top_p && !(per_request && per_request->top_p)) return SPECDEC_EINVAL;
     if (!target_logits || !draft_logits || !cu_nodes || !u_sample || !out_tokens ||
         !num_accepted || !num_emitted || !err_word)
         return SPECDEC_EINVAL;
     if (N > 0 && (!tree_tokens || !tree_parent || !u_accept || !accepted_nodes))
         return SPECDEC_EINVAL;
-    const float c = (float)(1.4426950408889634074 / (double)temperature);   // log2(e) / T
+    // log2(e) / T (per-request temperatures: each row's own, from the parameter launch)
+    const float c = pr_t ? 1.0f : (float)(1.4426950408889634074 / (double)temperature);
     if (!(c > 0.0f) || !isfinite(c)) return SPECDEC_EINVAL;
     if (team < 0 || team > kTreeMaxTeam) return SPECDEC_EINVAL;
     TreeWs w;
-    if (!tree_ws(B, N, V, dtype, top_k, top_p, &w)) return SPECDEC_EINVAL;
+    if (!tree_ws(B, N, V, dtype, top_k, top_p, per_request, &w)) return SPECDEC_EINVAL;
     const size_t rows = 2 * ((size_t)N + B);
     if (w.sel.filter && rows * w.sel.nchunks > 0x7fffffffu) return SPECDEC_EINVAL;
     if (!workspace || ((uintptr_t)workspace & 15) != 0 || workspace_bytes < w.total)
@@ -162,6 +189,7 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     a.kn = listed ? reinterpret_cast<const int*>(ws + w.sel.tk_kn) : nullptr;
     a.ktok = listed ? reinterpret_cast<const uint32_t*>(ws + w.sel.tk_ktok) : nullptr;
     a.kkey = listed ? reinterpret_cast<const uint16_t*>(ws + w.sel.tk_kkey) : nullptr;
+    a.rpar = w.sel.pr ? reinterpret_cast<const RowParams*>(ws + w.sel.rpar) : nullptr;
     if (const char* lim = getenv("SPECDEC_TREE_SPIN_LIMIT")) {
         char* end = nullptr;
         const long v = strtol(lim, &end, 10);
@@ -171,7 +199,38 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     const int grid = (B + 7) / 8 * 8 * G;
     (void)hipGetLastError();
     hipLaunchKernelGGL(k_tree_reset, dim3((nctr + 255) / 256), dim3(256), 0, stream, a.ctr, nctr);
-    if (w.sel.filter) {
+    if (w.sel.pr) {
+        ParamArgs pa{};
+        pa.cu = cu_nodes;
+        pa.B = B;
+        pa.K = N;
+        pa.V = V;
+        pa.temp = per_request->temperature;
+        pa.topk = per_request->top_k;
+        pa.topp = per_request->top_p;
+        pa.T = temperature;
+        pa.top_k = top_k;
+        pa.top_p = top_p;
+        pa.top_k_max = per_request->top_k ? per_request->top_k_max : top_k;
+        pa.kc = w.sel.kc;
+        pa.tree = 1;
+        pa.out = reinterpret_cast<RowParams*>(ws + w.sel.rpar);
+        hipLaunchKernelGGL(k_tree_params, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                           pa, (int)rows);
+    }
+    if (w.sel.filter && w.sel.pr) {
+        const TopkArgs ta = topk_args(a.tgt, a.dft, N + B, V, top_p, c, w.sel, ws);
+        const dim3 g((unsigned)(rows * w.sel.nchunks));
+        if (dtype == SPECDEC_BF16) {
+            if (vec) hipLaunchKernelGGL((k_tree_select_pr<true, true>), g, dim3(kTkNT), 0, stream, ta);
+            else hipLaunchKernelGGL((k_tree_select_pr<true, false>), g, dim3(kTkNT), 0, stream, ta);
+            hipLaunchKernelGGL((k_tree_merge_pr<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+        } else {
+            if (vec) hipLaunchKernelGGL((k_tree_select_pr<false, true>), g, dim3(kTkNT), 0, stream, ta);
+            else hipLaunchKernelGGL((k_tree_select_pr<false, false>), g, dim3(kTkNT), 0, stream, ta);
+            hipLaunchKernelGGL((k_tree_merge_pr<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+        }
+    } else if (w.sel.filter) {
         const TopkArgs ta = topk_args(a.tgt, a.dft, N + B, V, top_p, c, w.sel, ws);
         const dim3 g((unsigned)(rows * w.sel.nchunks));
         if (!ta.generic) {

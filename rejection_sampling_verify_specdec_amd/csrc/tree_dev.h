@@ -69,6 +69,9 @@ struct TreeArgs {
     const int* kn;
     const uint32_t* ktok;
     const uint16_t* kkey;
+    // per-request transforms: every row's parameters ([N+B] target rows, then draft rows),
+    // the request's log2(e) / T read from its root row; null with scalars
+    const RowParams* rpar;
 };
 
 // Eight consecutive tokens of a row kept as loaded (bf16 stays packed: 4 VGPRs); tokens at
@@ -613,7 +616,8 @@ SD_DEV int listed_draw(const TreeArgs& a, int rt, const uint8_t* drow, int nl, i
 
 // The walk of request b by member `mem` of its team; member 0 draws and writes the outputs.
 template <bool BF16, bool VEC>
-SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
+SD_DEV void tree_walk_body(const TreeArgs& args, int b, int mem) {
+    TreeArgs a = args;           // with per-request transforms a.c becomes the request's own
     using Lt = Layout<BF16, VEC>;
     __shared__ double red[kTreeNT / kWave + 1];
     __shared__ int redi[kTreeNT / kWave];
@@ -640,7 +644,9 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
         }
         return;
     }
-    // validity of the tree, its tokens and uniforms (wave 0, a lane per node)
+    const bool bad_param = a.rpar && (a.rpar[lo + b].flags & kRpBad);
+    if (a.rpar) a.c = a.rpar[lo + b].c;
+    // validity of the tree, its tokens, uniforms and parameters (wave 0, a lane per node)
     if (tid < kWave) {
         int f = 0;
         if (lane < n) {
@@ -653,6 +659,7 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
         if (lane == 0) {
             const float us = a.u_smp[b];
             if (!(us >= 0.0f && us < 1.0f)) f |= SPECDEC_ERR_UNIFORM;
+            if (bad_param) f |= SPECDEC_ERR_PARAM;
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o, kWave);
@@ -834,10 +841,10 @@ SD_DEV void tree_walk_body(const TreeArgs& a, int b, int mem) {
     }
     if (mem != 0) return;
     if (x < 0 && !(flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_TREE |
-                            SPECDEC_ERR_TEAM)))
+                            SPECDEC_ERR_TEAM | SPECDEC_ERR_PARAM)))
         flags |= SPECDEC_ERR_NONFINITE;          // nothing to draw from
     const bool err = (flags & (SPECDEC_ERR_TOKEN | SPECDEC_ERR_UNIFORM | SPECDEC_ERR_NONFINITE |
-                               SPECDEC_ERR_TREE | SPECDEC_ERR_TEAM)) != 0;
+                               SPECDEC_ERR_TREE | SPECDEC_ERR_TEAM | SPECDEC_ERR_PARAM)) != 0;
     if (tid < na && !err) {
         a.nodes_out[lo + tid] = s_path[tid];
         a.out_tokens[lo + b + tid] = a.tokens[lo + s_path[tid]];

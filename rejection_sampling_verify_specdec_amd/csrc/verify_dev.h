@@ -2510,7 +2510,8 @@ struct ParamArgs {
     float top_p;
     int top_k_max;           // requests with an active top_k above it fail
     int kc;                  // the chunk k of a top-p-alone row
-    RowParams* out;          // [2K+B]
+    int tree;                // 1: draft rows laid out like target rows (trees: [K+B] each)
+    RowParams* out;          // [2K+B], trees [2(K+B)]
 };
 
 SD_DEV void row_params_one(const ParamArgs& a, int r) {
@@ -2520,7 +2521,7 @@ SD_DEV void row_params_one(const ParamArgs& a, int r) {
     int lo = 0, hi = a.B;                       // largest b with start(b) <= x
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (a.cu[mid] + (tgt ? mid : 0) <= x) lo = mid;
+        if (a.cu[mid] + ((tgt || a.tree) ? mid : 0) <= x) lo = mid;
         else hi = mid;
     }
     const int b = lo;
@@ -2824,6 +2825,7 @@ static inline ParamArgs param_args(const int* cu, int B, int K, int V, float T, 
     a.top_p = top_p;
     a.top_k_max = prm->top_k ? prm->top_k_max : top_k;
     a.kc = p.kc;
+    a.tree = 0;
     a.out = reinterpret_cast<RowParams*>(ws + p.rpar);
     return a;
 }

@@ -154,10 +154,11 @@ def test_tree_workspace_and_host_validation_without_gpu(lib):
     vp = None
 
     def call(team=0, ws=16, nbytes=1 << 30, T=1.0, B=1, N=1, max_nodes=4, V=1000, top_k=0,
-             top_p=1.0):
+             top_p=1.0, pr=None):
         return lib.specdec_tree_verify(16, 16, binding.SPECDEC_BF16, 16, 16, 16, 16, 16, B, N,
-                                       max_nodes, V, T, top_k, top_p, 16, 16, 16, 16, 16, vp,
-                                       team, ws, nbytes, vp)
+                                       max_nodes, V, T, top_k, top_p,
+                                       ctypes.byref(pr) if pr is not None else None, 16, 16,
+                                       16, 16, 16, vp, team, ws, nbytes, vp)
     assert call(team=-1) == binding.SPECDEC_EINVAL
     assert call(team=binding.MAX_TREE_TEAM + 1) == binding.SPECDEC_EINVAL
     assert call(T=0.0) == binding.SPECDEC_EINVAL
@@ -170,6 +171,22 @@ def test_tree_workspace_and_host_validation_without_gpu(lib):
                 team=1) == binding.SPECDEC_EWORKSPACE
     need = binding.specdec_tree_verify_workspace_size(1, 1, 1000, binding.SPECDEC_BF16, 8, 0.9)
     assert call(nbytes=need - 1, team=1, top_k=8, top_p=0.9) == binding.SPECDEC_EWORKSPACE
+    # per-request arrays: they replace the scalars (a bad scalar is then not checked);
+    # stopping arrays are not taken on trees; a top_k array needs top_k_max >= 0
+    P = binding.SpecdecParams
+    temps = P(16, None, None, 0, None, None)
+    assert call(T=0.0, pr=temps, nbytes=8, team=1) == binding.SPECDEC_EWORKSPACE
+    assert call(top_p=float("nan"), pr=P(None, None, 16, 0, None, None), nbytes=8,
+                team=1) == binding.SPECDEC_EWORKSPACE
+    assert call(pr=P(None, None, None, 0, 16, None)) == binding.SPECDEC_EINVAL
+    assert call(pr=P(None, None, None, 0, None, 16)) == binding.SPECDEC_EINVAL
+    assert call(pr=P(None, 16, None, -1, None, None)) == binding.SPECDEC_EINVAL
+    size = lambda pr: lib.specdec_tree_verify_workspace_size(128, 2071, 128256,
+                                                             binding.SPECDEC_BF16, 0, 1.0,
+                                                             ctypes.byref(pr))
+    assert size(temps) > n                          # each row's parameters
+    assert size(P(None, 16, None, 64, None, None)) > size(temps)   # and the select
+    assert size(P(None, None, None, 0, 16, None)) == 0
 
 
 def test_early_exit_host_validation_without_gpu(lib):

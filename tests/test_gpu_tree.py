@@ -41,10 +41,14 @@ def _logits(x, dtype, d):
 
 
 class TreeOnDevice:
-    def __init__(self, tin, team: int = 0, ws_fill: int = 0, top_k: int = 0, top_p: float = 1.0):
+    def __init__(self, tin, team: int = 0, ws_fill: int = 0, top_k: int = 0, top_p: float = 1.0,
+                 temps=None, top_ks=None, top_ps=None, top_k_max=None):
         d = dev()
         self.team = team
         self.top_k, self.top_p = top_k, top_p
+        opt = lambda x: None if x is None else _t(np.asarray(x), d)
+        self.temps, self.top_ks, self.top_ps = opt(temps), opt(top_ks), opt(top_ps)
+        self.top_k_max = top_k_max
         self.tin = tin
         self.tgt = _logits(tin.target, tin.dtype, d)
         self.dft = _logits(tin.draft, tin.dtype, d)
@@ -60,8 +64,9 @@ class TreeOnDevice:
         self.flags = torch.full((B,), -1, dtype=torch.int32, device=d)
         # the call resets what it needs: start from arbitrary contents
         dt = binding.SPECDEC_BF16 if tin.dtype == "bf16" else binding.SPECDEC_F32
+        prm = binding._params(B, d, self.temps, self.top_ks, self.top_ps, top_k_max)
         self.ws = torch.full((binding.specdec_tree_verify_workspace_size(B, N, tin.V, dt, top_k,
-                                                                         top_p),),
+                                                                         top_p, prm),),
                              ws_fill, dtype=torch.uint8, device=d)
 
     def run(self):
@@ -71,7 +76,9 @@ class TreeOnDevice:
                                     accepted_nodes=self.nodes, num_accepted=self.num_acc,
                                     num_emitted=self.num_emit, err_word=self.err,
                                     workspace=self.ws, req_flags=self.flags, team=self.team,
-                                    top_k=self.top_k, top_p=self.top_p)
+                                    top_k=self.top_k, top_p=self.top_p, temperatures=self.temps,
+                                    top_ks=self.top_ks, top_ps=self.top_ps,
+                                    top_k_max=self.top_k_max)
         torch.cuda.synchronize()
         c = lambda x: x.cpu().numpy()
         return dict(a=c(self.num_acc), n=c(self.num_emit), out=c(self.out), nodes=c(self.nodes),
@@ -99,7 +106,7 @@ def _near_clamp(res):
         any(0 < float(W) < 4 * TREE_CLAMP for W in res.res.resid_W)
 
 
-def _valid(tin, g, b, ga, top_k=0, top_p=1.0):
+def _valid(tin, g, b, ga, top_k=0, top_p=1.0, T=None):
     """A valid walk result: a root-to-node chain, its tokens emitted in order, one more
     token drawn with positive target probability at the position the path ends (inside
     the row's top-k set, and its nucleus decided either way)."""
@@ -121,18 +128,23 @@ def _valid(tin, g, b, ga, top_k=0, top_p=1.0):
     pos = 0 if not path else path[-1] + 1
     z = oracle.verify._decode_rows(tin.target[lo + b + pos: lo + b + pos + 1], tin.dtype)[0]
     x = got[ga] if len(got) > ga else -1
-    floor = _nucleus_floor(z, tin.T, top_k, top_p) if (0 < top_k < tin.V or 0 < top_p < 1) \
-        else -np.inf
+    floor = _nucleus_floor(z, tin.T if T is None else T, top_k, top_p) \
+        if (0 < top_k < tin.V or 0 < top_p < 1) else -np.inf
     if not (0 <= x < tin.V and z[x] > -np.inf and z[x] >= floor):
         errs.append(f"req {b}: drawn token {x} has no target probability")
     return errs
 
 
-def compare_tree(tin, g, o, top_k=0, top_p=1.0):
+def compare_tree(tin, g, o, top_k=0, top_p=1.0, T=None):
     """errors, flagged requests (margin, nucleus or clamp), flagged mismatches; the caller
-    asserts that there are no errors (the bound on mismatches is one of them)."""
+    asserts that there are no errors (the bound on mismatches is one of them). T, top_k,
+    top_p: scalars or per-request arrays."""
     flagged = mism = decisions = 0
     errs = []
+    per = lambda x, f: [f(v) for v in np.broadcast_to(np.asarray(x), (tin.B,))]
+    Ts = per(tin.T if T is None else T, lambda v: float(np.float32(v)))
+    ks = per(top_k, int)
+    ps = per(top_p, lambda v: float(np.float32(v)))
     for b in range(tin.B):
         oa, ga = int(o.num_accepted[b]), int(g["a"][b])
         r = o.requests[b]
@@ -148,7 +160,7 @@ def compare_tree(tin, g, o, top_k=0, top_p=1.0):
         got = list(g["out"][lo + b: lo + b + ga + 1])
         path = list(g["nodes"][lo: lo + ga])
         flagged += fl
-        errs += _valid(tin, g, b, ga, top_k, top_p)
+        errs += _valid(tin, g, b, ga, ks[b], ps[b], Ts[b])
         if oa != ga or got != r.emitted or path != r.path:
             if fl:
                 mism += 1
@@ -159,14 +171,19 @@ def compare_tree(tin, g, o, top_k=0, top_p=1.0):
     return errs, flagged, mism
 
 
-def _check(tin, top_k=0, top_p=1.0, team=0):
+def _check(tin, top_k=0, top_p=1.0, team=0, temps=None, top_ks=None, top_ps=None,
+           top_k_max=None):
     log(f"[tree] B={tin.B} N={tin.N} V={tin.V} {tin.dtype} T={tin.T} top_k={top_k} "
-        f"top_p={top_p} team={team}")
-    g = TreeOnDevice(tin, top_k=top_k, top_p=top_p, team=team).run()
+        f"top_p={top_p} team={team} per-request={temps is not None or top_ks is not None or top_ps is not None}")
+    g = TreeOnDevice(tin, top_k=top_k, top_p=top_p, team=team, temps=temps, top_ks=top_ks,
+                     top_ps=top_ps, top_k_max=top_k_max).run()
+    T = tin.T if temps is None else temps
+    k = top_k if top_ks is None else top_ks
+    p = top_p if top_ps is None else top_ps
     o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
-                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype,
-                                 top_k=top_k, top_p=top_p)
-    errs, fl, mism = compare_tree(tin, g, o, top_k, top_p)
+                                 tin.u_accept, tin.u_sample, T, tin.max_nodes, tin.dtype,
+                                 top_k=k, top_p=p, top_k_max=top_k_max)
+    errs, fl, mism = compare_tree(tin, g, o, k, p, T)
     log(f"[tree]   accepted mean {np.mean(g['a'][g['a'] >= 0]) if (g['a'] >= 0).any() else 0:.2f}, "
         f"flagged {fl}, flagged mismatches {mism}")
     assert not errs, "\n".join(errs[:20])
@@ -335,6 +352,35 @@ def test_team_sizes_with_transforms(top_k, top_p):
         g = TreeOnDevice(tin, team=team, ws_fill=0xCD, top_k=top_k, top_p=top_p).run()
         for key in ("a", "n", "out", "nodes", "flags"):
             assert np.array_equal(g[key], ref[key]), (team, key)
+
+
+@pytest.mark.parametrize("dtype,V", [("bf16", 128256), ("f32", 32000)])
+def test_tree_per_request_transforms(dtype, V):
+    # per-request temperature, top-k and top-p (each request its own transform on its p and
+    # q rows), with an invalid temperature and a NaN top_p failing their requests alone
+    tin = synth.make_tree(seed=135, B=14, V=V, dtype=dtype, n_range=(1, 16), noise_std=0.5)
+    r = np.random.default_rng(9)
+    temps = r.choice([0.5, 0.8, 1.2], tin.B).astype(np.float32)
+    ks = r.choice([0, 8, 64, V], tin.B).astype(np.int32)
+    ps = r.choice([1.0, 0.9, 0.5], tin.B).astype(np.float32)
+    temps[3] = 0.0
+    ps[7] = np.nan
+    g, o = _check(tin, temps=temps, top_ks=ks, top_ps=ps, top_k_max=64)
+    assert g["flags"][3] & binding.ERR_PARAM and g["flags"][7] & binding.ERR_PARAM
+    assert g["a"][3] == -1 and g["a"][7] == -1
+    assert sum(int(x) >= 0 for x in g["a"]) == tin.B - 2
+
+
+def test_tree_per_request_temperatures_alone():
+    # temperatures alone: no select, the walk takes each request's own statistics; equal
+    # values give the scalar call's results bit for bit
+    tin = synth.make_tree(seed=136, B=10, V=50000, dtype="bf16", n_range=(2, 18))
+    temps = np.array([0.4, 0.7, 1.0, 1.5, 0.7, 2.0, 0.9, 0.7, 1.1, 0.6], np.float32)
+    _check(tin, temps=temps)
+    same = TreeOnDevice(tin, temps=np.full(tin.B, tin.T, np.float32)).run()
+    ref = TreeOnDevice(tin).run()
+    for key in ("a", "n", "out", "nodes", "flags"):
+        assert np.array_equal(same[key], ref[key]), key
 
 
 def _cycle(tin, seed):
