@@ -122,15 +122,25 @@ def test_random_trees_match_the_oracle_for_any_team(seed):
     top_k = int(r.choice([0, 0, 1, 8, 64, 300, 2000]))
     top_p = float(r.choice([1.0, 1.0, 0.5, 0.9, 0.99]))
     tin = synth.make_tree(seed=3000 + seed, top_k=top_k, **kw)
-    log(f"[random-tree] seed {seed}: {kw} N={tin.N} team {team} top_k {top_k} top_p {top_p}")
-    g = TreeOnDevice(tin, team=team, ws_fill=0x5A, top_k=top_k, top_p=top_p).run()
+    pr = {}
+    if r.random() < 0.4:              # per-request arrays (some requests the multi-pass select)
+        B = tin.B
+        pr = dict(temps=r.choice([0.5, 1.0, 1.5], B).astype(np.float32),
+                  top_ks=r.choice([0, 8, 64, 2000, kw["V"]], B).astype(np.int32),
+                  top_ps=r.choice([1.0, 0.9, 0.5], B).astype(np.float32), top_k_max=2000)
+    log(f"[random-tree] seed {seed}: {kw} N={tin.N} team {team} top_k {top_k} top_p {top_p} "
+        f"per-request {bool(pr)}")
+    g = TreeOnDevice(tin, team=team, ws_fill=0x5A, top_k=top_k, top_p=top_p, **pr).run()
+    T = pr.get("temps", tin.T)
+    k = pr.get("top_ks", top_k)
+    p = pr.get("top_ps", top_p)
     o = oracle.tree_verify_batch(tin.target, tin.draft, tin.tokens, tin.parent, tin.cu_nodes,
-                                 tin.u_accept, tin.u_sample, tin.T, tin.max_nodes, tin.dtype,
-                                 top_k=top_k, top_p=top_p)
-    errs, fl, mism = compare_tree(tin, g, o, top_k, top_p)
+                                 tin.u_accept, tin.u_sample, T, tin.max_nodes, tin.dtype,
+                                 top_k=k, top_p=p, top_k_max=pr.get("top_k_max"))
+    errs, fl, mism = compare_tree(tin, g, o, k, p, T)
     log(f"[random-tree]   flagged {fl}, flagged mismatches {mism}")
     assert not errs, f"seed {seed} {kw} team {team}\n" + "\n".join(errs[:20])
-    solo = TreeOnDevice(tin, team=1, top_k=top_k, top_p=top_p).run()
+    solo = TreeOnDevice(tin, team=1, top_k=top_k, top_p=top_p, **pr).run()
     for key in ("a", "n", "out", "nodes", "flags"):
         assert np.array_equal(g[key], solo[key]), key
 
