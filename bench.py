@@ -374,9 +374,13 @@ def tree_main(args):
     path = nodes.cpu().numpy()
     row = V * 2
     filt = 0 < top_k < V or 0 < top_p < 1
-    # top-k / top-p: the select reads every target and draft row once, and the walk takes
-    # each position's statistics from it instead of its own pass
-    walk = 2 * (N + B) * row if filt else 0
+    # top-k / top-p: the select reads every target row and the draft row of every position
+    # with children once, and the walk takes each position's statistics from it instead of
+    # its own pass
+    inner = sum(len({int(x) for x in tin.parent[int(tin.cu_nodes[b]):int(tin.cu_nodes[b + 1])]})
+                for b in range(B))
+    select_bytes = (N + B + inner) * row
+    walk = select_bytes if filt else 0
     stats = 0 if filt else 1
     for b in range(B):
         lo, hi = int(tin.cu_nodes[b]), int(tin.cu_nodes[b + 1])
@@ -418,7 +422,7 @@ def tree_main(args):
                  "walk_frac_of_peak": walk / (verify_ms / 1e3) / 1e9 / PEAK_GBPS},
     }
     if filt:
-        res["tree"]["select_bytes"] = 2 * (N + B) * row
+        res["tree"]["select_bytes"] = select_bytes
         res["tree"]["walk_bytes_note"] = (
             "select_bytes plus a full row pair per rejected child and a row per bonus: an "
             "upper bound, since a bf16 target row whose kept tokens are listed (up to 512) "

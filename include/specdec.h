@@ -499,8 +499,9 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * (ascending ids). Every target and draft row the walk reads takes the same transform as
  * in specdec_verify: temperature, then top_k (0 or >= V: off; ties at the k-th value
  * kept), then top_p (<= 0 or >= 1: off; the nucleus of the top-k set, ties kept); with
- * either filter on, the call first selects over every row (draft rows of leaves
- * included) and the walk reads the kept tokens' statistics from there. per_request (or
+ * either filter on, the call first selects over every target row and the draft row of
+ * every position with children (the draft rows of leaves are never read) and the walk
+ * reads the kept tokens' statistics from there. per_request (or
  * NULL) replaces any of the three scalars by [B] arrays as in specdec_verify (a request
  * whose values are invalid fails with SPECDEC_ERR_PARAM alone); its stopping arrays
  * (eos_token, max_emit) are not taken on trees (EINVAL).
@@ -520,9 +521,10 @@ int kv_contig_rollback(const kv_contig_cache* cache, int32_t B, const int32_t* n
  * SPECDEC_MAX_V, temperature > 0 and finite and top_p not NaN (unless replaced per
  * request), per_request->top_k_max >= 0 with a top_k array, 0 <= team <= 16; EINVAL
  * otherwise, EWORKSPACE for a missing / small / misaligned workspace, before anything is
- * enqueued. Two launches on `stream` (counter reset, walk), two more before the walk with
- * top-k / top-p (the chunk select, the per-row merge; one with top_k above 1024), one
- * more with per-request arrays (each row's parameters). Testing only: the environment variable
+ * enqueued. Two launches on `stream` (counter reset, walk), three more before the walk
+ * with top-k / top-p (the marking of the draft rows read, the chunk select, the per-row
+ * merge; no chunk select with top_k above 1024), one more with per-request arrays (each
+ * row's parameters). Testing only: the environment variable
  * SPECDEC_TREE_SPIN_LIMIT (a decimal integer in [0, 2^20], read at each call; anything
  * else is ignored) lowers the bound on the polls a member makes while it waits for the
  * rest of its team (default 2^20); a member that reaches the bound gives up, and its

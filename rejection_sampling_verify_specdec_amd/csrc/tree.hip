@@ -28,20 +28,47 @@ __global__ __launch_bounds__(kTreeNT) void k_tree_verify(TreeArgs a) {
     tree_walk_body<BF16, VEC>(a, b, mem);
 }
 
-__global__ void k_tree_reset(int* ctr, int n) {
+// the team counters and (with top-k / top-p) the draft rows' marks start at zero
+__global__ void k_tree_reset(int* ctr, int n, int* need, int nn) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) ctr[i] = 0;
+    if (i < nn) need[i] = 0;
+}
+
+// With top-k / top-p only positions with children have their draft rows read: node i
+// marks its parent's position (bounds-checked; a malformed tree fails in the walk).
+__global__ void k_tree_mark(const int* __restrict__ cu, const int* __restrict__ parent, int B,
+                            int N, int* __restrict__ need) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    int lo = 0, hi = B;                         // largest b with cu[b] <= i
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= i) lo = mid;
+        else hi = mid;
+    }
+    const int j = i - cu[lo], pa = parent[i];
+    const long long row = (long long)cu[lo] + lo + pa + 1;
+    if (j >= 0 && pa >= -1 && pa < j && row >= 0 && row < (long long)N + B) need[row] = 1;
+}
+
+// a draft row no walk reads (the position of a leaf) is skipped
+SD_DEV bool tree_row_skipped(const TopkArgs& a, const int* need, int row) {
+    return row >= a.rows_t && need[row - a.rows_t] == 0;
 }
 
 // the select of every row (target rows first, then draft rows), as in the linear path
 template <bool BF16, bool VEC, bool P2>
-__global__ __launch_bounds__(kTkNT) void k_tree_select(TopkArgs a) {
-    topk_chunk_body<BF16, VEC, P2 ? 1 : 0>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks,
+__global__ __launch_bounds__(kTkNT) void k_tree_select(TopkArgs a, const int* need) {
+    const int row = blockIdx.x / a.nchunks;
+    if (tree_row_skipped(a, need, row)) return;
+    topk_chunk_body<BF16, VEC, P2 ? 1 : 0>(a, row, blockIdx.x % a.nchunks,
                                           ChunkSel{a.top_k, a.c, P2});
 }
 
 template <bool BF16, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge(TopkArgs a, const int* need) {
+    if (tree_row_skipped(a, need, blockIdx.x)) return;
     topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
 }
 
@@ -53,17 +80,20 @@ __global__ __launch_bounds__(256) void k_tree_params(ParamArgs a, int rows) {
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kTkNT) void k_tree_select_pr(TopkArgs a) {
-    chunk_pr_body<BF16, VEC>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks);
+__global__ __launch_bounds__(kTkNT) void k_tree_select_pr(TopkArgs a, const int* need) {
+    const int row = blockIdx.x / a.nchunks;
+    if (tree_row_skipped(a, need, row)) return;
+    chunk_pr_body<BF16, VEC>(a, row, blockIdx.x % a.nchunks);
 }
 
 template <bool BF16, int NT>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge_pr(TopkArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge_pr(TopkArgs a, const int* need) {
+    if (tree_row_skipped(a, need, blockIdx.x)) return;
     merge_pr_body<BF16, NT>(a, blockIdx.x);
 }
 
 struct TreeWs {
-    size_t ctr_bytes, ring_bytes, total;
+    size_t ctr_bytes, ring_bytes, total, need;
     int nchunk, nsub, slot;
     WsPlan sel;                         // top-k / top-p: offsets from the workspace start
 };
@@ -87,7 +117,9 @@ static bool tree_ws(int32_t B, int32_t N, int32_t V, int32_t dtype, int32_t top_
         w->sel.rpar = off;
         off = align256(off + rows * sizeof(RowParams));
     }
+    w->need = off;
     if (w->sel.filter) {
+        off = align256(off + ((size_t)N + B) * sizeof(int));     // draft rows read
         w->sel.part = off;
         off = align256(off + rows * sizeof(RowPartial));
         w->sel.thr = off;
@@ -198,7 +230,14 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
     const int nctr = B * kTreeCtrStride;
     const int grid = (B + 7) / 8 * 8 * G;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(k_tree_reset, dim3((nctr + 255) / 256), dim3(256), 0, stream, a.ctr, nctr);
+    int* need = reinterpret_cast<int*>(ws + w.need);
+    const int nneed = w.sel.filter ? N + B : 0;
+    const int nreset = nctr > nneed ? nctr : nneed;
+    hipLaunchKernelGGL(k_tree_reset, dim3((nreset + 255) / 256), dim3(256), 0, stream, a.ctr, nctr,
+                       need, nneed);
+    if (w.sel.filter && N > 0)
+        hipLaunchKernelGGL(k_tree_mark, dim3((N + 255) / 256), dim3(256), 0, stream, cu_nodes,
+                           tree_parent, B, N, need);
     if (w.sel.pr) {
         ParamArgs pa{};
         pa.cu = cu_nodes;
@@ -222,13 +261,13 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
         const TopkArgs ta = topk_args(a.tgt, a.dft, N + B, V, top_p, c, w.sel, ws);
         const dim3 g((unsigned)(rows * w.sel.nchunks));
         if (dtype == SPECDEC_BF16) {
-            if (vec) hipLaunchKernelGGL((k_tree_select_pr<true, true>), g, dim3(kTkNT), 0, stream, ta);
-            else hipLaunchKernelGGL((k_tree_select_pr<true, false>), g, dim3(kTkNT), 0, stream, ta);
-            hipLaunchKernelGGL((k_tree_merge_pr<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+            if (vec) hipLaunchKernelGGL((k_tree_select_pr<true, true>), g, dim3(kTkNT), 0, stream, ta, need);
+            else hipLaunchKernelGGL((k_tree_select_pr<true, false>), g, dim3(kTkNT), 0, stream, ta, need);
+            hipLaunchKernelGGL((k_tree_merge_pr<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta, need);
         } else {
-            if (vec) hipLaunchKernelGGL((k_tree_select_pr<false, true>), g, dim3(kTkNT), 0, stream, ta);
-            else hipLaunchKernelGGL((k_tree_select_pr<false, false>), g, dim3(kTkNT), 0, stream, ta);
-            hipLaunchKernelGGL((k_tree_merge_pr<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+            if (vec) hipLaunchKernelGGL((k_tree_select_pr<false, true>), g, dim3(kTkNT), 0, stream, ta, need);
+            else hipLaunchKernelGGL((k_tree_select_pr<false, false>), g, dim3(kTkNT), 0, stream, ta, need);
+            hipLaunchKernelGGL((k_tree_merge_pr<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta, need);
         }
     } else if (w.sel.filter) {
         const TopkArgs ta = topk_args(a.tgt, a.dft, N + B, V, top_p, c, w.sel, ws);
@@ -237,26 +276,26 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
             const bool p2 = w.sel.topp_mode == 2;
             if (dtype == SPECDEC_BF16) {
                 if (vec) {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<true, true, true>), g, dim3(kTkNT), 0, stream, ta);
-                    else hipLaunchKernelGGL((k_tree_select<true, true, false>), g, dim3(kTkNT), 0, stream, ta);
+                    if (p2) hipLaunchKernelGGL((k_tree_select<true, true, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    else hipLaunchKernelGGL((k_tree_select<true, true, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 } else {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<true, false, true>), g, dim3(kTkNT), 0, stream, ta);
-                    else hipLaunchKernelGGL((k_tree_select<true, false, false>), g, dim3(kTkNT), 0, stream, ta);
+                    if (p2) hipLaunchKernelGGL((k_tree_select<true, false, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    else hipLaunchKernelGGL((k_tree_select<true, false, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 }
             } else {
                 if (vec) {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<false, true, true>), g, dim3(kTkNT), 0, stream, ta);
-                    else hipLaunchKernelGGL((k_tree_select<false, true, false>), g, dim3(kTkNT), 0, stream, ta);
+                    if (p2) hipLaunchKernelGGL((k_tree_select<false, true, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    else hipLaunchKernelGGL((k_tree_select<false, true, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 } else {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<false, false, true>), g, dim3(kTkNT), 0, stream, ta);
-                    else hipLaunchKernelGGL((k_tree_select<false, false, false>), g, dim3(kTkNT), 0, stream, ta);
+                    if (p2) hipLaunchKernelGGL((k_tree_select<false, false, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    else hipLaunchKernelGGL((k_tree_select<false, false, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 }
             }
         }
         if (dtype == SPECDEC_BF16)
-            hipLaunchKernelGGL((k_tree_merge<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+            hipLaunchKernelGGL((k_tree_merge<true, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta, need);
         else
-            hipLaunchKernelGGL((k_tree_merge<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta);
+            hipLaunchKernelGGL((k_tree_merge<false, kMergeNT>), dim3((unsigned)rows), dim3(kMergeNT), 0, stream, ta, need);
     }
     if (dtype == SPECDEC_BF16) {
         if (vec) hipLaunchKernelGGL((k_tree_verify<true, true>), dim3(grid), dim3(kTreeNT), 0, stream, a);
