@@ -165,3 +165,125 @@ def test_emitted_sequences_follow_the_target_law():
     log(f"[law] {CALLS * B} requests, mean accepted {accepted / (CALLS * B):.3f}: "
         f"joint law p-value {pj:.3g}, first-token p-value {pf:.3g}")
     assert pj > P_VALUE and pf > P_VALUE
+
+
+# Draft trees: every request's tree is a root with three children (tokens i.i.d. from q_0),
+# the first of which has two children and the second one (tokens from q_1), so the walk
+# meets sibling residual chains at depths 1 and 2. Rows depend on the depth only: target
+# p_0 at the root, p_1 at depth 1, p_2 at depth 2; draft q_0 at the root, q_1 at depth 1.
+# The emitted path and draw, completed to three tokens from p_t, must follow
+# p_0(x_0) p_1(x_1) p_2(x_2), and the first token alone p_0.
+TREE_PARENT = [-1, -1, -1, 0, 0, 1]
+TREE_DEPTH_POS = [0, 1, 1, 1, 2, 2, 2]          # depth of positions 0 (root), 1 + j
+TREE_T = 3
+
+
+def _tree_pvalues(seqs, first, p):
+    joint = np.array([float(p[0][a] * p[1][b] * p[2][c])
+                      for a in range(V) for b in range(V) for c in range(V)])
+    idx = (seqs[:, 0] * V + seqs[:, 1]) * V + seqs[:, 2]
+    pj, _ = _chi2(np.bincount(idx, minlength=V ** 3).astype(np.float64), joint)
+    pf, _ = _chi2(np.bincount(first, minlength=V).astype(np.float64),
+                  np.array([float(x) for x in p[0]]))
+    return pj, pf
+
+
+def _tree_tokens(rng, q, n):
+    """n requests' node tokens: nodes 0-2 from q_0, nodes 3-5 from q_1."""
+    cols = [_draw(rng, q[0], n) for _ in range(3)] + [_draw(rng, q[1], n) for _ in range(3)]
+    return np.stack(cols, axis=1)
+
+
+def _complete_tree(rng, emitted, n_emitted, p):
+    n = emitted.shape[0]
+    out = np.empty((n, TREE_T), np.int64)
+    for t in range(TREE_T):
+        out[:, t] = np.where(t < n_emitted, emitted[:, t], _draw(rng, p[t], n))
+    return out
+
+
+def _oracle_tree_sample(n, seed, plant=False):
+    p, q = _rows()
+    rng = np.random.default_rng(seed)
+    P = [np.array([float(x) for x in p[d]]) for d in TREE_DEPTH_POS]
+    Q = [np.array([float(x) for x in q[min(d, 1)]]) for d in TREE_DEPTH_POS]
+    ys = _tree_tokens(rng, q, n)
+    ua = rng.random((n, 6)).astype(np.float32)
+    us = rng.random(n).astype(np.float32)
+    em = np.zeros((n, TREE_T), np.int64)
+    ne = np.zeros(n, np.int64)
+    resid = oracle.tree.residual_weights
+    try:
+        if plant:
+            oracle.tree.residual_weights = lambda pp, qq: pp
+        for j in range(n):
+            r = oracle.tree.tree_verify_probs(P, Q, TREE_PARENT, ys[j].tolist(),
+                                              [float(u) for u in ua[j]], float(us[j]))
+            em[j, :len(r.emitted)] = r.emitted
+            ne[j] = len(r.emitted)
+    finally:
+        oracle.tree.residual_weights = resid
+    return _complete_tree(rng, em, ne, p), em[:, 0]
+
+
+def test_tree_law_statistic_sees_a_planted_mistake():
+    # CPU: the tree oracle passes, the tree oracle with the residual replaced by p fails
+    p, _ = _rows()
+    ok = _tree_pvalues(*_oracle_tree_sample(20000, 6), p)
+    bad = _tree_pvalues(*_oracle_tree_sample(20000, 6, plant=True), p)
+    assert min(ok) > P_VALUE, ok
+    assert min(bad) < 1e-12, bad
+
+
+@pytest.mark.gpu
+def test_tree_emitted_sequences_follow_the_target_law():
+    import torch
+    from gpu_harness import log
+    from rejection_sampling_verify_specdec_amd import binding
+
+    p, q = _rows()
+    d = torch.device("cuda:0")
+    rng = np.random.default_rng(2025)
+    lp = np.log(np.array([[float(x) for x in p[dd]] for dd in TREE_DEPTH_POS])).astype(np.float32)
+    lq = np.log(np.array([[float(x) for x in q[min(dd, 1)]] for dd in TREE_DEPTH_POS])).astype(np.float32)
+    B, n = BATCH, len(TREE_PARENT)
+    tgt = torch.from_numpy(np.tile(lp, (B, 1))).to(d)          # rows of b: 7b .. 7b + 6
+    dft = torch.from_numpy(np.tile(lq, (B, 1))).to(d)
+    cu = torch.arange(0, n * B + 1, n, dtype=torch.int32, device=d)
+    parent = torch.tensor(np.tile(TREE_PARENT, B), dtype=torch.int32, device=d)
+    out = torch.empty(n * B + B, dtype=torch.int32, device=d)
+    nodes = torch.empty(n * B, dtype=torch.int32, device=d)
+    nacc = torch.empty(B, dtype=torch.int32, device=d)
+    nemit = torch.empty(B, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    ws = torch.empty(binding.specdec_tree_verify_workspace_size(B, n * B, V, binding.SPECDEC_F32),
+                     dtype=torch.uint8, device=d)
+    seqs, firsts, accepted = [], [], 0
+    for call in range(CALLS):
+        ys = _tree_tokens(rng, q, B).astype(np.int32)
+        ua = rng.random((B, n), dtype=np.float32)
+        us = rng.random(B, dtype=np.float32)
+        binding.specdec_tree_verify(tgt, dft, torch.from_numpy(ys.reshape(-1)).to(d), parent, cu,
+                                    torch.from_numpy(ua.reshape(-1)).to(d),
+                                    torch.from_numpy(us).to(d), max_nodes=n, temperature=1.0,
+                                    out_tokens=out, accepted_nodes=nodes, num_accepted=nacc,
+                                    num_emitted=nemit, err_word=err, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        o = out.cpu().numpy().reshape(B, n + 1).astype(np.int64)
+        ne = nemit.cpu().numpy().astype(np.int64)
+        na = nacc.cpu().numpy()
+        assert (ne == na + 1).all() and (na >= 0).all() and (na <= 2).all()
+        # the path's tokens are the accepted nodes' tokens
+        nd = nodes.cpu().numpy().reshape(B, n)
+        for i in range(2):
+            sel = na > i
+            assert np.array_equal(o[sel, i], ys[sel, :][np.arange(sel.sum()), nd[sel, i]])
+        accepted += int(na.sum())
+        seqs.append(_complete_tree(rng, o, ne, p))
+        firsts.append(o[:, 0])
+    seqs, firsts = np.concatenate(seqs), np.concatenate(firsts)
+    pj, pf = _tree_pvalues(seqs, firsts, p)
+    log(f"[law] trees: {CALLS * B} requests, mean path {accepted / (CALLS * B):.3f}: "
+        f"joint law p-value {pj:.3g}, first-token p-value {pf:.3g}")
+    assert pj > P_VALUE and pf > P_VALUE
