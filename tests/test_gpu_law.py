@@ -61,8 +61,11 @@ def _complete(rng, emitted, n_emitted, p):
 
 
 def _chi2(counts, probs):
-    """Chi-square p-value of counts against exact cell probabilities (cells of expected
-    count below 5 pooled into one)."""
+    """Chi-square p-value of counts against exact cell probabilities (cells of probability 0
+    must be empty and are left out; cells of expected count below 5 pooled into one)."""
+    zero = probs == 0
+    assert counts[zero].sum() == 0, "a sequence of probability 0 was emitted"
+    counts, probs = counts[~zero], probs[~zero]
     n = counts.sum()
     exp = n * probs
     small = exp < 5
@@ -116,8 +119,20 @@ def test_law_statistic_sees_a_planted_mistake():
     assert min(bad) < 1e-12, bad
 
 
+def _transformed(rows, logits, top_k, top_p):
+    """The rows after the decoding transform of their fp32 logits (the oracle's, which its
+    own pins tie to the pages; the identity when both filters are off)."""
+    if top_k == 0 and top_p >= 1.0:
+        return rows
+    return [list(oracle.verify.transform(z.astype(np.float64), 1.0, top_k, top_p).p)
+            for z in logits]
+
+
 @pytest.mark.gpu
-def test_emitted_sequences_follow_the_target_law():
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (5, 1.0), (0, 0.8)])
+def test_emitted_sequences_follow_the_target_law(top_k, top_p):
+    # with top-k / top-p the output must follow the transformed target (the proposals are
+    # drawn from the transformed q)
     import torch
     from gpu_harness import log
     from rejection_sampling_verify_specdec_amd import binding
@@ -128,6 +143,7 @@ def test_emitted_sequences_follow_the_target_law():
     # logits ln p: the kernels' softmax gives the rows back to fp32 rounding
     lp = np.log(np.array([[float(x) for x in r] for r in p], np.float64)).astype(np.float32)
     lq = np.log(np.array([[float(x) for x in r] for r in q], np.float64)).astype(np.float32)
+    p, q = _transformed(p, lp, top_k, top_p), _transformed(q, lq, top_k, top_p)
     B = BATCH
     tgt = torch.from_numpy(np.tile(lp, (B, 1))).to(d)          # rows of b: 4b .. 4b + 3
     dft = torch.from_numpy(np.tile(lq, (B, 1))).to(d)          # rows of b: 3b .. 3b + 2
@@ -136,7 +152,8 @@ def test_emitted_sequences_follow_the_target_law():
     nacc = torch.empty(B, dtype=torch.int32, device=d)
     nemit = torch.empty(B, dtype=torch.int32, device=d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
-    ws = torch.empty(binding.specdec_verify_workspace_size(B, K * B, V, binding.SPECDEC_F32, 0),
+    ws = torch.empty(binding.specdec_verify_workspace_size(B, K * B, V, binding.SPECDEC_F32,
+                                                           top_k, top_p),
                      dtype=torch.uint8, device=d)
     seqs, firsts, accepted = [], [], 0
     for call in range(CALLS):
@@ -145,8 +162,9 @@ def test_emitted_sequences_follow_the_target_law():
         us = rng.random(B, dtype=np.float32)
         binding.specdec_verify(tgt, dft, torch.from_numpy(ys.reshape(-1)).to(d), cu,
                                torch.from_numpy(ua.reshape(-1)).to(d), torch.from_numpy(us).to(d),
-                               max_k=K, temperature=1.0, top_k=0, out_tokens=out,
-                               num_accepted=nacc, num_emitted=nemit, err_word=err, workspace=ws)
+                               max_k=K, temperature=1.0, top_k=top_k, out_tokens=out,
+                               num_accepted=nacc, num_emitted=nemit, err_word=err, workspace=ws,
+                               top_p=top_p)
         torch.cuda.synchronize()
         assert int(err.item()) == 0
         o = out.cpu().numpy().reshape(B, K + 1).astype(np.int64)
@@ -162,7 +180,8 @@ def test_emitted_sequences_follow_the_target_law():
         firsts.append(o[:, 0])
     seqs, firsts = np.concatenate(seqs), np.concatenate(firsts)
     pj, pf = _law_pvalues(seqs, firsts, p)
-    log(f"[law] {CALLS * B} requests, mean accepted {accepted / (CALLS * B):.3f}: "
+    log(f"[law] top_k {top_k} top_p {top_p}: {CALLS * B} requests, mean accepted "
+        f"{accepted / (CALLS * B):.3f}: "
         f"joint law p-value {pj:.3g}, first-token p-value {pf:.3g}")
     assert pj > P_VALUE and pf > P_VALUE
 
