@@ -245,16 +245,19 @@ __global__ __launch_bounds__(kKvNT) void k_cycle_rollback(SampleArgs sa, KvArgs 
 }
 
 // How a cycle spreads the K/V scatter (percent of its workgroups) over the launches that
-// follow the allocation. The fused cycle puts it beside the decisions (its chunk sums and
-// picks gain nothing from more company, measured); the early-exit cycle, whose statistics
-// launches past position 0 hold few rows, spreads it over them and the sampling launches.
+// follow the allocation. The fused cycle puts most of it beside the decisions, and without
+// top-k / top-p a fifth beside the chunk sums and the picks (measured: -0.9% at the
+// headline workload; with top-k the merges' rows change the balance and the split costs
+// 1-2%); the early-exit cycle, whose statistics launches past position 0 hold few rows,
+// spreads it over them and the sampling launches.
 struct ScatterSplit {
     int pass_pct;      // beside position 1's statistics (early exit)
     int tail_pct;      // beside the last statistics launch (early exit)
     int part_pct;      // beside the chunk sums
     int pick_pct;      // beside the picks; the rest beside the decisions
 };
-constexpr ScatterSplit kFusedSplit = {0, 0, 0, 0};
+constexpr ScatterSplit kFusedSplit = {0, 0, 15, 5};
+constexpr ScatterSplit kFusedFilteredSplit = {0, 0, 0, 0};
 constexpr ScatterSplit kEarlySplit = {30, 30, 10, 10};
 
 static int pct_of(int n, int pct) { return (int)(((long long)n * pct) / 100); }
@@ -356,7 +359,7 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     }
     if (dbg && dbg->ev_stats_done) (void)hipEventRecord(dbg->ev_stats_done, st);
     launch_cycle_tail<BF16, VEC>(kv, B, K, p, sa, scatter_plan(kv, knew, vnew, aws, B, N),
-                                 kFusedSplit, st);
+                                 p.filter ? kFusedFilteredSplit : kFusedSplit, st);
 }
 
 // The early-exit cycle: one statistics launch for each of positions 0 .. kEarlyCut - 1,
