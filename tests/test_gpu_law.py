@@ -156,6 +156,7 @@ def test_emitted_sequences_follow_the_target_law(top_k, top_p):
                                                            top_k, top_p),
                      dtype=torch.uint8, device=d)
     seqs, firsts, accepted = [], [], 0
+    reached, passed = np.zeros(K, np.int64), np.zeros(K, np.int64)
     for call in range(CALLS):
         ys = np.stack([_draw(rng, q[i], B) for i in range(K)], axis=1).astype(np.int32)
         ua = rng.random((B, K), dtype=np.float32)
@@ -176,10 +177,21 @@ def test_emitted_sequences_follow_the_target_law(top_k, top_p):
             sel = na > i
             assert np.array_equal(o[sel, i], ys[sel, i])
         accepted += int(na.sum())
+        for i in range(K):
+            reached[i] += int((na >= i).sum())
+            passed[i] += int((na >= i + 1).sum())
         seqs.append(_complete(rng, o, ne, p))
         firsts.append(o[:, 0])
     seqs, firsts = np.concatenate(seqs), np.concatenate(firsts)
     pj, pf = _law_pvalues(seqs, firsts, p)
+    # acceptance rate at each position against beta_i = sum_x min(p_i(x), q_i(x)), the
+    # complement of the residual mass ("Speculative decoding ...", section 3)
+    for i in range(K):
+        beta = float(sum(min(a, b) for a, b in zip(p[i], q[i])))
+        pb = scipy.stats.binomtest(int(passed[i]), int(reached[i]), beta).pvalue
+        log(f"[law]   position {i}: accepted {passed[i]} of {reached[i]} "
+            f"({passed[i] / reached[i]:.5f} against beta {beta:.5f}), p-value {pb:.3g}")
+        assert pb > P_VALUE, (i, passed[i], reached[i], beta)
     log(f"[law] top_k {top_k} top_p {top_p}: {CALLS * B} requests, mean accepted "
         f"{accepted / (CALLS * B):.3f}: "
         f"joint law p-value {pj:.3g}, first-token p-value {pf:.3g}")
