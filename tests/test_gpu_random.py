@@ -6,6 +6,8 @@ same launch where no nucleus boundary is too close to call; and the fused cycle 
 three calls bit for bit on a further set. A failure prints the case's seed and options.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -15,6 +17,16 @@ from test_gpu_analytics import _compare as compare_analytics
 from test_gpu_cycle import _run_mode
 
 pytestmark = pytest.mark.gpu
+
+
+def _seeds(n):
+    """The committed seeds 0 .. n-1, or SPECDEC_RANDOM_SEEDS="start:count" for a longer sweep
+    (every case reproducible from its seed)."""
+    spec = os.environ.get("SPECDEC_RANDOM_SEEDS")
+    if not spec:
+        return list(range(n))
+    start, count = (int(x) for x in spec.split(":"))
+    return list(range(start, start + count))
 
 
 def _case(seed):
@@ -43,7 +55,7 @@ def _inputs(opts, seed):
     return synth.make_verify(wl, seed=seed, B=opts["B"], V=opts["V"], **over)
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", _seeds(64))
 def test_random_batches_match_the_oracle(seed):
     opts, r = _case(seed)
     vin = _inputs(opts, seed)
@@ -105,7 +117,7 @@ def test_random_fused_cycles_equal_three_calls(seed):
     assert np.array_equal(a[2], b[2])
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", _seeds(16))
 def test_random_trees_match_the_oracle_for_any_team(seed):
     # random tree batches (sizes, vocabulary, dtype, temperature, top-k, top-p, branching,
     # draft noise, empty trees) with a random team size: checked against the oracle, and
@@ -145,7 +157,7 @@ def test_random_trees_match_the_oracle_for_any_team(seed):
         assert np.array_equal(g[key], solo[key]), key
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", _seeds(12))
 def test_random_early_exit_cycles_equal_the_full_cycle(seed):
     # the early-exit cycle on random batches (dtype, V, B, ragged and empty k_b, top-k,
     # top-p, scalar or per-request parameters with an invalid temperature now and then,
