@@ -71,6 +71,33 @@ __global__ __launch_bounds__(kNT) void k_cycle_stats(KvArgs kv, const int* __res
     row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, c, part, blockIdx.x - 1, rpar);
 }
 
+// Per-request temperatures alone: the same launch, each workgroup deriving its row's
+// parameters from its request's values (the first chunk's workgroup also records them for
+// the launches that follow), so no parameter launch runs first.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kNT) void k_cycle_stats_pr(KvArgs kv, const int* __restrict__ cu,
+                                                        int B, int N, uint8_t* __restrict__ aws,
+                                                        const uint8_t* __restrict__ tgt,
+                                                        const uint8_t* __restrict__ dft,
+                                                        int rows_t, int V, int nchunks,
+                                                        RowPartial* __restrict__ part,
+                                                        ParamArgs pa) {
+    __shared__ float s_c;
+    if (blockIdx.x == 0) {
+        alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
+        return;
+    }
+    const int bid = blockIdx.x - 1, row = bid / nchunks;
+    if (threadIdx.x == 0) {
+        const RowParams rp = row_params_of(pa, row);
+        if (bid == row * nchunks) pa.out[row] = rp;
+        s_c = rp.c;
+    }
+    __syncthreads();
+    row_stats_body<BF16, VEC>(tgt, dft, rows_t, V, nchunks, s_c, part, bid,
+                              (const RowParams*)nullptr);
+}
+
 // One launch's share of the K/V scatter: scatter workgroups s0 .. s0 + ns - 1 of the
 // ntiles * L * 2 (tile, layer / K-V plane) workgroups; each copies its tile's rows, and the
 // copy-on-write copies are spread over all of them by global index.
@@ -328,11 +355,9 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     hipEvent_t e0 = dbg ? dbg->ev_stats_begin : nullptr;
     hipEvent_t e1 = dbg ? dbg->ev_stats_end : nullptr;
     if (p.pr_plain) {
-        hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,
-                           pa, rows);
-        hipExtLaunchKernelGGL((k_cycle_stats<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
+        hipExtLaunchKernelGGL((k_cycle_stats_pr<BF16, VEC>), dim3((unsigned)rows * p.nchunks + 1),
                               dim3(kNT), 0, st, e0, e1, 0, kv, cu, B, N, aws, tgt, dft, K + B, V,
-                              p.nchunks, c, part, reinterpret_cast<const RowParams*>(vws + p.rpar));
+                              p.nchunks, part, pa);
     } else if (p.pr) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         hipLaunchKernelGGL(k_cycle_row_params, dim3((unsigned)(rows + 255) / 256), dim3(256), 0, st,

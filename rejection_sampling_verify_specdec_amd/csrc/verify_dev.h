@@ -2514,7 +2514,7 @@ struct ParamArgs {
     RowParams* out;          // [2K+B], trees [2(K+B)]
 };
 
-SD_DEV void row_params_one(const ParamArgs& a, int r) {
+SD_DEV RowParams row_params_of(const ParamArgs& a, int r) {
     const int rows_t = a.K + a.B;
     const bool tgt = r < rows_t;
     const int x = tgt ? r : r - rows_t;
@@ -2547,8 +2547,10 @@ SD_DEV void row_params_one(const ParamArgs& a, int r) {
         const bool generic = (mode == 1 && k > kTkMaxK) || (mode == 2 && a.kc >= a.V);
         rp.flags = mode | (generic ? kRpGeneric : 0);
     }
-    a.out[r] = rp;
+    return rp;
 }
+
+SD_DEV void row_params_one(const ParamArgs& a, int r) { a.out[r] = row_params_of(a, r); }
 
 // One chunk of one row under per-request parameters: plain statistics into cpart for an
 // unfiltered row, the candidate select otherwise (nothing for a row that takes the
