@@ -707,9 +707,13 @@ def main():
     if early:                          # the position launches, timed as one span
         stats_kernel = "k_cycle_fpass" if filtered else "k_cycle_pass"
     elif filtered:                     # the chunk launch streams the rows
-        stats_kernel = "k_cycle_topk" if args.schedule == "fused" else "k_topk_chunks"
+        # top-p alone (scalar) has a launch of its own in the fused cycle
+        topp_alone = not args.per_request and not 0 < vin.top_k < V
+        stats_kernel = (("k_cycle_topp" if topp_alone else "k_cycle_topk")
+                        if args.schedule == "fused" else "k_topk_chunks")
     else:
-        stats_kernel = "k_cycle_stats" if args.schedule == "fused" else "k_row_stats"
+        stats_kernel = (("k_cycle_stats_pr" if args.per_request else "k_cycle_stats")
+                        if args.schedule == "fused" else "k_row_stats")
     res = {
         "metric": METRIC,
         "value": positions_per_s,

@@ -209,6 +209,22 @@ __global__ __launch_bounds__(kTkNT) void k_cycle_topk(KvArgs kv, const int* __re
                                         ChunkSel{a.top_k, a.c, P2 == 1});
 }
 
+// Top-p alone over 16-byte loads: the same launch held to 64 VGPRs, so that eight waves
+// share each SIMD (the launch issues more instructions per byte than any other and hides
+// its loads with waves; the scalar-load form would spill at this bound)
+template <bool BF16>
+__global__ __launch_bounds__(kTkNT) __attribute__((amdgpu_waves_per_eu(8))) void
+k_cycle_topp(KvArgs kv, const int* __restrict__ cu, int B, int N, uint8_t* __restrict__ aws,
+             TopkArgs a) {
+    if (blockIdx.x == 0) {
+        alloc_body<kCycAllocNT>(kv, cu, 1, B, N, aws);
+        return;
+    }
+    const int w = blockIdx.x - 1;
+    topk_chunk_body<BF16, true, 1>(a, w / a.nchunks, w % a.nchunks,
+                                   ChunkSel{a.top_k, a.c, true});
+}
+
 template <bool BF16, bool PR, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_cycle_topk_merge(TopkArgs a) {
     if constexpr (PR) merge_pr_body<BF16, NT>(a, blockIdx.x);
@@ -369,7 +385,10 @@ static void launch_cycle(const KvArgs& kv, const uint8_t* knew, const uint8_t* v
     } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, vws);
         const unsigned nchunk_wg = ta.generic ? 0u : (unsigned)rows * p.nchunks;
-        if (p.topp_mode == 2)
+        if (p.topp_mode == 2 && VEC)
+            hipExtLaunchKernelGGL((k_cycle_topp<BF16>), dim3(nchunk_wg + 1), dim3(kTkNT), 0, st,
+                                  e0, e1, 0, kv, cu, B, N, aws, ta);
+        else if (p.topp_mode == 2)
             hipExtLaunchKernelGGL((k_cycle_topk<BF16, VEC, 1>), dim3(nchunk_wg + 1), dim3(kTkNT),
                                   0, st, e0, e1, 0, kv, cu, B, N, aws, ta);
         else
