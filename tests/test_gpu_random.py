@@ -98,7 +98,7 @@ def test_random_batches_match_the_oracle(seed):
                           top_k_max=okw.get("top_k_max"))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", _seeds(12))
 def test_random_fused_cycles_equal_three_calls(seed):
     opts, _ = _case(100 + seed)
     opts["V"] = max(opts["V"], 1000)
