@@ -66,6 +66,16 @@ __global__ __launch_bounds__(kTkNT) void k_tree_select(TopkArgs a, const int* ne
                                           ChunkSel{a.top_k, a.c, P2});
 }
 
+// top-p alone over 16-byte loads, held to 64 VGPRs (eight waves per SIMD)
+template <bool BF16>
+__global__ __launch_bounds__(kTkNT) __attribute__((amdgpu_waves_per_eu(8))) void
+k_tree_topp(TopkArgs a, const int* need) {
+    const int row = blockIdx.x / a.nchunks;
+    if (tree_row_skipped(a, need, row)) return;
+    topk_chunk_body<BF16, true, 1>(a, row, blockIdx.x % a.nchunks,
+                                   ChunkSel{a.top_k, a.c, true});
+}
+
 template <bool BF16, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_tree_merge(TopkArgs a, const int* need) {
     if (tree_row_skipped(a, need, blockIdx.x)) return;
@@ -276,7 +286,7 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
             const bool p2 = w.sel.topp_mode == 2;
             if (dtype == SPECDEC_BF16) {
                 if (vec) {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<true, true, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    if (p2) hipLaunchKernelGGL((k_tree_topp<true>), g, dim3(kTkNT), 0, stream, ta, need);
                     else hipLaunchKernelGGL((k_tree_select<true, true, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 } else {
                     if (p2) hipLaunchKernelGGL((k_tree_select<true, false, true>), g, dim3(kTkNT), 0, stream, ta, need);
@@ -284,7 +294,7 @@ extern "C" int specdec_tree_verify(const void* target_logits, const void* draft_
                 }
             } else {
                 if (vec) {
-                    if (p2) hipLaunchKernelGGL((k_tree_select<false, true, true>), g, dim3(kTkNT), 0, stream, ta, need);
+                    if (p2) hipLaunchKernelGGL((k_tree_topp<false>), g, dim3(kTkNT), 0, stream, ta, need);
                     else hipLaunchKernelGGL((k_tree_select<false, true, false>), g, dim3(kTkNT), 0, stream, ta, need);
                 } else {
                     if (p2) hipLaunchKernelGGL((k_tree_select<false, false, true>), g, dim3(kTkNT), 0, stream, ta, need);

@@ -68,6 +68,15 @@ __global__ __launch_bounds__(kTkNT) void k_topk_chunks(TopkArgs a) {
                                           ChunkSel{a.top_k, a.c, P2});
 }
 
+// top-p alone over 16-byte loads, held to 64 VGPRs: eight waves per SIMD hide its loads
+// better than the fewer instructions of a larger register budget would pay
+template <bool BF16>
+__global__ __launch_bounds__(kTkNT) __attribute__((amdgpu_waves_per_eu(8))) void
+k_topp_chunks(TopkArgs a) {
+    topk_chunk_body<BF16, true, 1>(a, blockIdx.x / a.nchunks, blockIdx.x % a.nchunks,
+                                   ChunkSel{a.top_k, a.c, true});
+}
+
 template <bool BF16, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(5))) void k_topk_merge(TopkArgs a) {
     topk_merge_body<BF16, NT>(a, blockIdx.x, RowSel{a.top_k, a.topp_mode, a.top_p, a.c});
@@ -207,7 +216,10 @@ static void launch_all(const uint8_t* tgt, const uint8_t* dft, int B, int K, int
     } else if (p.filter) {
         const TopkArgs ta = topk_args(tgt, dft, K + B, V, top_p, c, p, ws);
         if (!ta.generic) {
-            if (p.topp_mode == 2)
+            if (p.topp_mode == 2 && VEC)
+                hipExtLaunchKernelGGL((k_topp_chunks<BF16>), dim3((unsigned)rows * p.nchunks),
+                                      dim3(kTkNT), 0, st, e0, e1, 0, ta);
+            else if (p.topp_mode == 2)
                 hipExtLaunchKernelGGL((k_topk_chunks<BF16, VEC, true>),
                                       dim3((unsigned)rows * p.nchunks), dim3(kTkNT), 0, st, e0, e1,
                                       0, ta);
