@@ -6,7 +6,8 @@
 //   k_cycle_stats   workgroup 0 allocates the cycle's blocks (copy-on-write, LIFO pops,
 //                   destination rows) while every other workgroup streams logit rows
 //                   (row statistics; with top-k or top-p, k_cycle_topk gathers chunk
-//                   candidates and a short per-row merge launch follows);
+//                   candidates, k_cycle_topp for top-p alone, and a short per-row merge
+//                   launch follows);
 //   k_cycle_decide  one workgroup per request for its accept / reject decisions, then
 //                   most of the K/V scatter;
 //   k_cycle_part    workgroup 0 truncates every request to its committed prefix (up to 512

@@ -14,7 +14,8 @@
 //   k_topk_chunks (top-k or top-p, replaces k_row_stats) the same chunks, held in
 //                 registers as order-preserving keys: each workgroup writes the few tokens
 //                 that can be in the row's top-k set (a bound from its per-thread maxima);
-//                 for top-p alone, the chunk's top k_c tokens plus its max and exp-sum.
+//                 for top-p alone, the chunk's top k_c tokens plus its max and exp-sum
+//                 (k_topp_chunks, the same body at eight waves per SIMD).
 //   k_topk_merge  one workgroup per row: exact top-k threshold over the chunks'
 //                 candidates, then the nucleus boundary (top-p) in fixed-point mass, both
 //                 from the token count on each key when the candidates' keys span fewer
