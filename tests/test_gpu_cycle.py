@@ -115,6 +115,51 @@ def test_fused_cycle_equals_three_calls(case):
         assert a[1]["state"] & binding.KV_ERR_APPEND and (a[0].num_accepted == -1).all()
 
 
+@pytest.mark.parametrize("case", ["plateau", "close"])
+def test_fused_cycle_unlisted_and_handed_over_draws(case):
+    # bf16 top-k within the kept-token list's capacity, where most draws scan a row's list:
+    # "plateau": half the requests' target rows put 600 tokens on their maximum, more than
+    # a list holds, so those rows are drawn over the whole row (five sampling chunks);
+    # "close": drafts a little off the target and uniforms that reject wherever p < q, so
+    # the lists hand small residuals over to the precise arithmetic. Bit for bit against
+    # the three calls, and against the oracle.
+    if case == "plateau":
+        vin = synth.make_verify("c4", seed=37, B=12, V=40000, top_k=8)
+        rng = np.random.default_rng(37)
+        t32 = synth.bf16_bits_to_f32(vin.target).copy()
+        for b in range(0, vin.B, 2):
+            for r in range(int(vin.cu_draft[b]) + b, int(vin.cu_draft[b + 1]) + b + 1):
+                t32[r, rng.choice(vin.V, 600, replace=False)] = np.float32(t32[r].max() + 1.0)
+        vin.target = synth.f32_to_bf16_bits(t32)
+    else:
+        vin = synth.make_verify("c4", seed=38, B=12, V=20000, top_k=64, T=0.8,
+                                classes=((1.0, "noise", 0.02),))
+        vin.u_accept[:] = np.float32(1.0 - 2.0 ** -24)
+    rec = synth.KVRecipe(L=2, H=2, D=8, prefix_lo=60, prefix_hi=300, share_group=3,
+                         share_blocks=2)
+    kv = synth.make_kv("c4", vin, seed=37, recipe=rec)
+    log(f"[fused-unlisted] {case}: B={vin.B} K={vin.K} V={vin.V} top_k={vin.top_k}")
+    a = _run_mode(vin, kv, "calls")
+    b = _run_mode(vin, kv, "fused")
+    for f in ("num_accepted", "num_emitted", "out_tokens", "err_word", "p_y", "q_y", "row_sum",
+              "row_thr", "row_nkept", "resid_mass", "picked_prob", "req_flags"):
+        assert np.array_equal(np.asarray(getattr(a[0], f)), np.asarray(getattr(b[0], f))), f
+    for f in ("tables", "seq_lens", "refcount", "free_list", "free_count", "state"):
+        assert np.array_equal(np.asarray(a[1][f]), np.asarray(b[1][f])), f
+    assert np.array_equal(a[2], b[2])
+    o = oracle_verify(vin, keep_probs=False)
+    rep = compare_verify(vin, b[0], o)
+    log(f"[fused-unlisted]   {rep}")
+    rep.check()
+    drawn = [r for r in range(vin.B) if o.requests[r].probs.mode == "resid"]
+    if case == "plateau":
+        # unlisted rows were drawn from (kept sets past the list's capacity)
+        assert any(b[0].row_nkept[int(vin.cu_draft[r]) + r + int(b[0].num_accepted[r])] > 512
+                   for r in drawn)
+    else:
+        assert drawn and max(o.requests[r].probs.W_resid for r in drawn) < 0.25
+
+
 @pytest.mark.parametrize("B,k", [(600, 3), (300, 40)])
 def test_fused_cycle_batch_shapes(B, k):
     # 600 requests: the truncation runs in the pick launch; 300 requests x 40 proposals with
