@@ -32,7 +32,7 @@ PEAK_GBPS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30,
                    help="untimed cycles before the timed ones")
     p.add_argument("--settle-ms", type=float, default=150.0,
