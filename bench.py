@@ -479,6 +479,12 @@ def main():
     tgt, dft = logits(vin.target), logits(vin.draft)
     tokens, cu = t(vin.draft_tokens), t(vin.cu_draft)
     u_acc, u_smp = t(vin.u_accept), t(vin.u_sample)
+    pool_bytes = kv.L * 2 * kv.num_blocks * kv.block_size * kv.H * kv.D * 2
+    free_bytes = torch.cuda.mem_get_info(d)[0]
+    if pool_bytes > free_bytes:
+        sys.exit(f"bench.py: the paged pool for {args.warmup} warm-up and {args.steps} timed cycles "
+                 f"needs {pool_bytes / 2**30:.0f} GiB (every cycle's entries stay in the cache) "
+                 f"and {free_bytes / 2**30:.0f} GiB are free; use fewer --steps")
     pool = torch.empty((kv.L, 2, kv.num_blocks, kv.block_size, kv.H, kv.D), dtype=torch.bfloat16, device=d)
     if kv.blocks:
         ids = sorted(kv.blocks)
